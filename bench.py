@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused fp32 convolutions on one MI355X.
+
+One step = one call of each fused kernel on its full-size workload, inputs
+already resident in HBM:
+  * fconv2d_pool_sigmoid_sum on x[128,8,384,384], Conv2d 8->64 k3, AvgPool 4
+  * dwsep_conv1d on x[32,256,4096], depthwise k9 pad 4, pointwise 256->512
+Prints one JSON line (driver contract) with whole-step GFLOP/s, per-kernel
+ms/call and GFLOP/s, the roofline fraction of the dominant kernel, and the CPU
+oracle timed on a bounded sample of the same workloads.
+
+FLOPs are algorithmic, 2 per multiply-add: the conv outputs that feed the pool,
+s*s*Cin*K*K MACs per (co, pooled output); the separable conv1d, C*K + O*C MACs
+per time step (not the dense fused form).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fconv_inputs as fi  # noqa: E402
+
+METRIC = "fp32 GFLOP/s + ms/call per fused conv; fraction of MI355X fp32 roofline"
+PEAK_FP32_TFLOPS = 157.3  # MI355X dense fp32 (matrix cores), published
+PEAK_HBM_GBPS = 8000.0
+
+CONV = "conv2d_full"
+DW = "dwsep_full"
+
+
+def conv2d_flops(cfg):
+    Hc, Wc = cfg["H"] - cfg["K"] + 1, cfg["W"] - cfg["K"] + 1
+    s = cfg["pool"]
+    PH, PW = Hc // s, Wc // s
+    return 2 * cfg["B"] * cfg["Cout"] * PH * PW * s * s * cfg["Cin"] * cfg["K"] ** 2
+
+
+def conv2d_bytes(cfg):
+    return 4 * (cfg["B"] * cfg["Cin"] * cfg["H"] * cfg["W"] + cfg["Cout"] * cfg["Cin"] * cfg["K"] ** 2
+                + cfg["Cout"] + cfg["B"])
+
+
+def dwsep_flops(cfg):
+    Tout = cfg["T"] + 2 * cfg["pad"] - cfg["K"] + 1
+    return 2 * cfg["B"] * Tout * cfg["C"] * (cfg["K"] + cfg["O"])
+
+
+def dwsep_bytes(cfg):
+    Tout = cfg["T"] + 2 * cfg["pad"] - cfg["K"] + 1
+    return 4 * (cfg["B"] * cfg["C"] * cfg["T"] + cfg["C"] * cfg["K"] + cfg["O"] * cfg["C"] + cfg["O"]
+                + cfg["B"] * cfg["O"] * Tout)
+
+
+def cpu_baseline(conv_in, dw_in, conv_gpu, dw_gpu, conv_items, dw_items):
+    """Times the oracle (as it stands) on a bounded sample and checks the GPU
+    results on that sample against it."""
+    import oracle
+
+    oracle.load()
+    threads = oracle.oracle._threads(None)
+    cc, dc = fi.WORKLOADS[CONV], fi.WORKLOADS[DW]
+    x, w, b = conv_in
+    idx = list(range(0, cc["B"], max(1, cc["B"] // conv_items)))[:conv_items]
+    t0 = time.perf_counter()
+    want_out = oracle.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], batch_idx=idx, nthreads=threads)
+    t_conv = time.perf_counter() - t0
+    xd, wdw, wpw, bpw = dw_in
+    didx = list(range(0, dc["B"], max(1, dc["B"] // dw_items)))[:dw_items]
+    t0 = time.perf_counter()
+    want_y = oracle.dwsep_conv1d(xd, wdw, wpw, bpw, dc["pad"], batch_idx=didx, nthreads=threads)
+    t_dw = time.perf_counter() - t0
+    f_conv = conv2d_flops(cc) * len(idx) / cc["B"]
+    f_dw = dwsep_flops(dc) * len(didx) / dc["B"]
+    err_conv = np.abs(conv_gpu[idx] - want_out) / (1e-4 + 1e-4 * np.abs(want_out))
+    err_dw = np.abs(dw_gpu[didx] - want_y) / (1e-4 + 1e-4 * np.abs(want_y))
+    parity = {"conv2d_items": len(idx), "dwsep_items": len(didx),
+              "conv2d_worst_err_over_tol": float(err_conv.max()),
+              "dwsep_worst_err_over_tol": float(err_dw.max()),
+              "ok": bool(err_conv.max() <= 1.0 and err_dw.max() <= 1.0)}
+    return {
+        "value": round((f_conv + f_dw) / (t_conv + t_dw) / 1e9, 3),
+        "unit": "GFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"literal float64 oracle on {len(idx)} of {cc['B']} batch items of {CONV} "
+                   f"({t_conv:.1f} s) and {len(didx)} of {dc['B']} of {DW} ({t_dw:.1f} s), same inputs"),
+        "conv2d_gflops": round(f_conv / t_conv / 1e9, 3),
+        "dwsep_gflops": round(f_dw / t_dw / 1e9, 3),
+    }, parity
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--cpu-conv-items", type=int, default=128, help="conv2d batch items in the oracle sample")
+    ap.add_argument("--cpu-dw-items", type=int, default=32, help="dwsep batch items in the oracle sample")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="run one device copy of this many MiB first (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every kernel here runs on a single device and the "
+              "multi-GPU sharding is a design note, not an implementation. Run with --gpus 1.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import fp32_convolution_amd as fc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cc, dc = fi.WORKLOADS[CONV], fi.WORKLOADS[DW]
+    conv_in = fi.make(CONV, seed=args.seed)
+    dw_in = fi.make(DW, seed=args.seed)
+    x, w, b = (torch.from_numpy(a).to(dev) for a in conv_in)
+    xd, wdw, wpw, bpw = (torch.from_numpy(a).to(dev) for a in dw_in)
+    out = torch.empty(cc["B"], device=dev)
+    Tout = fc.dwsep_out_len(dc["T"], dc["K"], dc["pad"])
+    y = torch.empty((dc["B"], dc["O"], Tout), device=dev)
+
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def conv_call():
+        fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=out)
+
+    def dw_call():
+        fc.dwsep_conv1d(xd, wdw, wpw, bpw, dc["pad"], out=y)
+
+    for _ in range(args.warmup):
+        conv_call()
+        dw_call()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for e in ev:
+        e[0].record(stream)
+        conv_call()
+        e[1].record(stream)
+        dw_call()
+        e[2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    ms_conv = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    ms_dw = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    f_conv, f_dw = conv2d_flops(cc), dwsep_flops(dc)
+    b_conv, b_dw = conv2d_bytes(cc), dwsep_bytes(dc)
+
+    def kstats(ms, flops, nbytes):
+        m = float(ms.mean())
+        return {"ms_mean": round(m, 4), "ms_median": round(float(np.median(ms)), 4),
+                "ms_p10": round(float(np.percentile(ms, 10)), 4), "ms_p90": round(float(np.percentile(ms, 90)), 4),
+                "gflops": round(flops / (m * 1e-3) / 1e9, 1),
+                "frac_fp32_peak": round(flops / (m * 1e-3) / (PEAK_FP32_TFLOPS * 1e12), 4),
+                "hbm_gbps_algorithmic": round(nbytes / (m * 1e-3) / 1e9, 1),
+                "algorithmic_gflop": round(flops / 1e9, 3), "algorithmic_bytes": nbytes}
+
+    k_conv = kstats(ms_conv, f_conv, b_conv)
+    k_dw = kstats(ms_dw, f_dw, b_dw)
+    achieved = f_conv / (k_conv["ms_mean"] * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round((f_conv + f_dw) / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded: x ~ N(0,1), weights and biases ~ U(+-1/sqrt(fan_in)))",
+        "config": {
+            "workload": f"{CONV} + {DW} (one call each per step)",
+            CONV: "x[128,8,384,384] Conv2d 8->64 k3 -> AvgPool2d 4 -> sigmoid -> sum",
+            DW: "x[32,256,4096] depthwise k9 pad4 -> pointwise 256->512 + bias",
+            "parallelism": "single GPU",
+        },
+        "kernels": {"fconv2d_pool_sigmoid_sum": k_conv, "dwsep_conv1d": k_dw},
+        "roofline": {
+            "kernel": "fconv2d_pool_sigmoid_sum (conv2d_pool_mfma_kernel) on " + CONV,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+            "traffic": None,
+        },
+        "wall_s_timed_region": round(t_wall, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline(conv_in, dw_in, out.cpu().numpy().astype(np.float64),
+                                    y.cpu().numpy().astype(np.float64), args.cpu_conv_items, args.cpu_dw_items)
+        result["cpu_baseline"] = base
+        result["parity_sample"] = parity
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+"""fp32_convolution_amd: Python binding of libfconv (fused fp32 convolutions, MI355X / gfx950).
+
+Argument marshalling only: every function checks dtype, device and layout,
+then calls the C ABI of ``libfconv.so`` (declared in ``include/fconv.h``) with
+raw device pointers and torch's current HIP stream.  All arithmetic runs in
+the library's HIP kernels.  There is no fallback: if the library is missing,
+importing this package raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfconv.so")
+
+FCONV_OK = 0
+FCONV_EINVAL = -1
+FCONV_EUNSUPPORTED = -2
+FCONV_EHIP = -3
+
+ALGO_AUTO = 0
+ALGO_DIRECT_MFMA = 1
+ALGO_DIRECT_SIMPLE = 2
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libfconv.so not found at {LIB_PATH}; build it first with `python -m fp32_convolution_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_SIGS = {
+    "fconv2d_pool_sigmoid_sum": ([_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _vp], ctypes.c_int),
+    "fconv2d_pool_sigmoid_sum_algo": (
+        [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
+    "fconv2d_pool_map": (
+        [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
+    "fconv2d_pool_out_size": ([_i64, _i64, _i64, _i64, _i64p, _i64p], ctypes.c_int),
+    "fconv2d_select_algo": ([_i64, _i64, _i64, _i64], ctypes.c_int),
+    "dwsep_conv1d": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp], ctypes.c_int),
+    "dwsep_conv1d_out_len": ([_i64, _i64, _i64], ctypes.c_int64),
+    "fconv_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "fconv_version": ([], ctypes.c_int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+class FconvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib.fconv_strerror(status).decode()} ({status})")
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != FCONV_OK:
+        raise FconvError(rc, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_f32(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def version() -> int:
+    return lib.fconv_version()
+
+
+def conv2d_out_size(H: int, W: int, K: int, pool: int):
+    ph, pw = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.fconv2d_pool_out_size(H, W, K, pool, ctypes.byref(ph), ctypes.byref(pw)), "fconv2d_pool_out_size")
+    return ph.value, pw.value
+
+
+def conv2d_select_algo(Cin: int, Cout: int, K: int, pool: int) -> int:
+    return lib.fconv2d_select_algo(Cin, Cout, K, pool)
+
+
+def _conv2d_args(x, w, b):
+    _dev_f32(x, "x")
+    _dev_f32(w, "w")
+    if b is not None:
+        _dev_f32(b, "bias")
+    if x.dim() != 4 or w.dim() != 4 or w.shape[2] != w.shape[3] or w.shape[1] != x.shape[1]:
+        raise ValueError(f"expected x[B,Cin,H,W] and w[Cout,Cin,K,K], got {tuple(x.shape)} and {tuple(w.shape)}")
+    if b is not None and tuple(b.shape) != (w.shape[0],):
+        raise ValueError(f"bias must be [Cout]={w.shape[0]}, got {tuple(b.shape)}")
+    if x.device != w.device or (b is not None and b.device != x.device):
+        raise ValueError("x, w and bias must be on the same device")
+
+
+def conv2d_pool_sigmoid_sum(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO):
+    """Conv2d(stride 1, no pad) -> AvgPool2d(pool, floor) -> sigmoid -> sum over (C,H,W): out[B]."""
+    _conv2d_args(x, w, b)
+    B, Cin, H, W = x.shape
+    Cout, _, K, _ = w.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.float32, device=x.device)
+    else:
+        _dev_f32(out, "out")
+        if tuple(out.shape) != (B,) or out.device != x.device:
+            raise ValueError("out must be [B] on x's device")
+    rc = lib.fconv2d_pool_sigmoid_sum_algo(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
+                                           _ptr(out), _stream(x))
+    _check(rc, "fconv2d_pool_sigmoid_sum")
+    return out
+
+
+def conv2d_pool_map(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO):
+    """Pre-sigmoid pooled map [B,Cout,PH,PW] of the same fused computation."""
+    _conv2d_args(x, w, b)
+    B, Cin, H, W = x.shape
+    Cout, _, K, _ = w.shape
+    PH, PW = conv2d_out_size(H, W, K, pool)
+    if out is None:
+        out = torch.empty((B, Cout, PH, PW), dtype=torch.float32, device=x.device)
+    else:
+        _dev_f32(out, "out")
+        if tuple(out.shape) != (B, Cout, PH, PW) or out.device != x.device:
+            raise ValueError("out must be [B,Cout,PH,PW] on x's device")
+    rc = lib.fconv2d_pool_map(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo, _ptr(out), _stream(x))
+    _check(rc, "fconv2d_pool_map")
+    return out
+
+
+def dwsep_out_len(T: int, K: int, pad: int) -> int:
+    return int(lib.dwsep_conv1d_out_len(T, K, pad))
+
+
+def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None):
+    """Depthwise Conv1d(K, pad) -> pointwise 1x1 Conv1d + bias: y[B,O,Tout].
+
+    w_dw may be [C,K] or PyTorch's [C,1,K]; w_pw [O,C] or [O,C,1].
+    """
+    _dev_f32(x, "x")
+    _dev_f32(w_dw, "w_dw")
+    _dev_f32(w_pw, "w_pw")
+    if b_pw is not None:
+        _dev_f32(b_pw, "b_pw")
+    if w_dw.dim() == 3 and w_dw.shape[1] == 1:
+        w_dw = w_dw.view(w_dw.shape[0], w_dw.shape[2])
+    if w_pw.dim() == 3 and w_pw.shape[2] == 1:
+        w_pw = w_pw.view(w_pw.shape[0], w_pw.shape[1])
+    if x.dim() != 3 or w_dw.dim() != 2 or w_pw.dim() != 2 or w_dw.shape[0] != x.shape[1] or \
+            w_pw.shape[1] != x.shape[1]:
+        raise ValueError(f"expected x[B,C,T], w_dw[C,K], w_pw[O,C]; got {tuple(x.shape)}, "
+                         f"{tuple(w_dw.shape)}, {tuple(w_pw.shape)}")
+    B, C, T = x.shape
+    K = w_dw.shape[1]
+    O = w_pw.shape[0]
+    if b_pw is not None and tuple(b_pw.shape) != (O,):
+        raise ValueError(f"b_pw must be [O]={O}")
+    for t in (w_dw, w_pw, b_pw, out):
+        if t is not None and t.device != x.device:
+            raise ValueError("all tensors must be on x's device")
+    Tout = dwsep_out_len(T, K, pad)
+    if Tout < 1:
+        raise FconvError(FCONV_EINVAL, "dwsep_conv1d")
+    if out is None:
+        out = torch.empty((B, O, Tout), dtype=torch.float32, device=x.device)
+    else:
+        _dev_f32(out, "out")
+        if tuple(out.shape) != (B, O, Tout):
+            raise ValueError(f"out must be [B,O,Tout]=({B},{O},{Tout})")
+    rc = lib.dwsep_conv1d(_ptr(x), B, C, T, _ptr(w_dw), K, _ptr(w_pw), O, _ptr(b_pw), pad, _ptr(out), _stream(x))
+    _check(rc, "dwsep_conv1d")
+    return out

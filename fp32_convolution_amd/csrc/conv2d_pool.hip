@@ -1,0 +1,325 @@
+// conv2d_pool.hip -- Conv2d (stride 1, no pad) -> AvgPool2d(k = s, floor) -> sigmoid -> sum,
+// fused so that neither the conv map nor the pooled map reaches HBM.
+//
+// Method: POPCORNBENCH reasoning trace "Kimi-K2.6 l2_p65" (Conv2d -> AvgPool2d ->
+// Sigmoid -> Sum).  Its fused per-pooled-output formula is used as written:
+// a pooled output of channel co is
+//     bias[co] + (1/s^2) * sum_{dy,dx < s} sum_{ic,ky,kx} x[ic, ph*s+dy+ky, pw*s+dx+kx] * w[co,ic,ky,kx]
+// (the bias factors out of the window average, as the trace notes when it
+// accumulates all s*s conv outputs into one running sum).  Because the pool's
+// stride equals its kernel, windows do not overlap and every conv output that
+// feeds the pool is computed exactly once: s*s*Cin*K*K multiply-adds per
+// (co, pooled output).
+//
+// gfx950 design (not the trace's H100 tiling):
+//  * The whole (dy, dx, ic, ky, kx) reduction is one fp32 matrix-core
+//    contraction: M = output channels, N = pooled positions,
+//    k = Cin*K*K*s*s.  The pool is folded into the reduction, so the
+//    accumulators hold window sums directly and no conv value is ever
+//    materialised, not even in registers.
+//  * v_mfma_f32_16x16x4_f32: the 4 k-slots of an instruction are 4 channel
+//    groups (lane group g = l/16 reads channel g*CINQ + q), so every operand
+//    address is a per-lane base plus a compile-time immediate: no address
+//    arithmetic in the inner loop.
+//  * The input tile (all channels, tile + K-1 halo) sits in LDS with its
+//    columns split by phase (column c stored at phase c%s, slot c/s), so the
+//    16 lanes of a group that read 16 horizontally adjacent pooled positions
+//    (stride s in x) hit 16 consecutive LDS words.
+//  * Weights stream from L2/L1 straight into registers (they are 18-200 KB).
+//  * Epilogue: scale by 1/s^2, add bias, sigmoid, lane sum, wave + LDS
+//    reduction, one float atomic per workgroup into out[b].
+#include "fconv_device.hpp"
+#include "fconv_internal.hpp"
+
+namespace fconv {
+
+// ---------------------------------------------------------------- MFMA direct conv
+
+// Compile-time tiling of one instance.
+//   K, S      conv kernel and pool size
+//   CB        16-channel output blocks per wave
+//   P         16-position pooled blocks per wave
+//   WCO,WPOS  waves along output channels / along pooled positions
+//   TPH,TPW   pooled tile of the workgroup (TPH*TPW = 16*P*WPOS)
+template <int K_, int S_, int CB_, int P_, int WCO_, int WPOS_, int TPH_, int TPW_>
+struct DirectCfg {
+    static constexpr int K = K_, S = S_, CB = CB_, P = P_, WCO = WCO_, WPOS = WPOS_, TPH = TPH_, TPW = TPW_;
+    static constexpr int NW = WCO * WPOS;
+    static constexpr int NT = 64 * NW;
+    static constexpr int IH = TPH * S + K - 1;  // input rows of the tile
+    static constexpr int IW = TPW * S + K - 1;  // input columns of the tile
+    static constexpr int QP = (IW + S - 1) / S; // LDS slots per phase
+    static constexpr int RP = S * QP;           // LDS floats per input row
+    static constexpr int NBV = S + K - 1;       // distinct input offsets per axis inside a window
+    static constexpr int CO_RANGE = 16 * CB * WCO;
+    static_assert(TPH * TPW == 16 * P * WPOS, "tile must hold the waves' position blocks");
+};
+
+template <class Cfg, bool MAP>
+__global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane,
+    int tiles_w) {
+    constexpr int K = Cfg::K, S = Cfg::S, CB = Cfg::CB, P = Cfg::P, WCO = Cfg::WCO;
+    constexpr int TPH = Cfg::TPH, TPW = Cfg::TPW, IH = Cfg::IH, IW = Cfg::IW;
+    constexpr int QP = Cfg::QP, RP = Cfg::RP, NBV = Cfg::NBV, NT = Cfg::NT;
+
+    extern __shared__ float lds[];
+    __shared__ float red[Cfg::NW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wco = wave % WCO;
+    const int wpos = wave / WCO;
+    const int tile_y = blockIdx.x / tiles_w;
+    const int tile_x = blockIdx.x - tile_y * tiles_w;
+    const int b = blockIdx.z;
+    const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
+
+    // Stage the input tile: channel ic at ic*plane, row r at r*RP, column c at
+    // phase (c % S)*QP + slot c/S.  Zero outside the image and for ic >= Cin.
+    const float* xb = x + (size_t)b * Cin * H * W;
+    const int nload = 4 * CINQ * IH * IW;
+    for (int i = tid; i < nload; i += NT) {
+        const int ic = i / (IH * IW);
+        const int rem = i - ic * (IH * IW);
+        const int r = rem / IW;
+        const int c = rem - r * IW;
+        const int gy = y0 + r, gx = x0 + c;
+        float v = 0.f;
+        if (ic < Cin && gy < H && gx < W) v = xb[(ic * H + gy) * W + gx];
+        lds[ic * plane + r * RP + (c % S) * QP + c / S] = v;
+    }
+    __syncthreads();
+
+    const int g = lane >> 4;   // k-slot of the MFMA: channel group
+    const int l16 = lane & 15; // row of A / column of B
+    int pbase[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int j = (wpos * P + p) * 16 + l16;
+        const int py = j / TPW, px = j - (j / TPW) * TPW;
+        pbase[p] = g * CINQ * plane + py * S * RP + px;
+    }
+    const int co0 = blockIdx.y * Cfg::CO_RANGE + wco * 16 * CB;
+
+    floatx4 acc[CB][P];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int p = 0; p < P; ++p) acc[cb][p] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (int q = 0; q < CINQ; ++q) {
+        const int ic = g * CINQ + q;
+        const int lq = q * plane;
+        const float* wq[CB];
+        bool wok[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int co = co0 + cb * 16 + l16;
+            wok[cb] = (co < Cout) && (ic < Cin);
+            wq[cb] = w + ((size_t)(wok[cb] ? co : 0) * Cin + (wok[cb] ? ic : 0)) * (K * K);
+        }
+#pragma unroll
+        for (int ky = 0; ky < K; ++ky) {
+            float a[CB][K];
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int kx = 0; kx < K; ++kx) a[cb][kx] = wok[cb] ? wq[cb][ky * K + kx] : 0.f;
+#pragma unroll
+            for (int dy = 0; dy < S; ++dy) {
+                const int rr = ky + dy;
+                float bv[P][NBV];
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+#pragma unroll
+                    for (int cc = 0; cc < NBV; ++cc)
+                        bv[p][cc] = lds[pbase[p] + lq + rr * RP + (cc % S) * QP + cc / S];
+#pragma unroll
+                for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+                    for (int dx = 0; dx < S; ++dx)
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                            for (int p = 0; p < P; ++p)
+                                acc[cb][p] = mfma_16x16x4(a[cb][kx], bv[p][dx + kx], acc[cb][p]);
+            }
+        }
+    }
+
+    // Epilogue.  Lane (g, l16) holds, for block (cb, p) and r = 0..3, the
+    // window sum of output channel co0 + cb*16 + 4g + r at pooled position
+    // j = (wpos*P + p)*16 + l16 of the tile.
+    const float inv = 1.0f / (float)(S * S);
+    const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
+    float lsum = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int co = co0 + cb * 16 + 4 * g + r;
+            const bool cok = co < Cout;
+            const float bco = (cok && bias) ? bias[co] : 0.f;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int j = (wpos * P + p) * 16 + l16;
+                const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
+                if (cok && ph < PH && pw < PW) {
+                    const float avg = acc[cb][p][r] * inv + bco;
+                    if constexpr (MAP)
+                        dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
+                    else
+                        lsum += logistic(avg);
+                }
+            }
+        }
+    if constexpr (!MAP) {
+        const float s = block_sum<Cfg::NW>(lsum, red);
+        if (tid == 0) atomicAdd(dst + b, s);
+    }
+}
+
+// Instances.  (3,4): 8x16 pooled tile, 4 waves side by side along positions,
+// each wave all 64 channels of its range.  (5,3): 4x12 tile (84 = 21*4 = 7*12,
+// no ragged tiles on 84x84 maps), 4 waves side by side along channels.
+using CfgK3S4 = DirectCfg<3, 4, 4, 2, 1, 4, 8, 16>;
+using CfgK5S3 = DirectCfg<5, 3, 2, 3, 4, 1, 4, 12>;
+using CfgK3S2 = DirectCfg<3, 2, 4, 2, 1, 4, 8, 16>;
+using CfgK3S3 = DirectCfg<3, 3, 4, 2, 1, 4, 8, 16>;
+
+template <class Cfg>
+static int plane_floats(int CINQ) {
+    // Pad each channel plane so that the 4 lane groups (which read planes
+    // g*CINQ*plane apart) fall on different LDS banks where possible.
+    const int base = Cfg::IH * Cfg::RP;
+    for (int pad = 0; pad < 32; ++pad)
+        if (((long)CINQ * (base + pad)) % 32 == 16) return base + pad;
+    return base;
+}
+
+template <class Cfg>
+static size_t lds_bytes_for(int Cin) {
+    const int CINQ = (Cin + 3) / 4;
+    return (size_t)4 * CINQ * plane_floats<Cfg>(CINQ) * sizeof(float);
+}
+
+static constexpr size_t kMaxLds = 160 * 1024 - 256;  // dynamic share; the rest holds the reduction slots
+
+bool conv2d_mfma_supported(int Cin, int K, int S, size_t* lds_bytes) {
+    size_t bytes = 0;
+    if (K == 3 && S == 4) bytes = lds_bytes_for<CfgK3S4>(Cin);
+    else if (K == 5 && S == 3) bytes = lds_bytes_for<CfgK5S3>(Cin);
+    else if (K == 3 && S == 2) bytes = lds_bytes_for<CfgK3S2>(Cin);
+    else if (K == 3 && S == 3) bytes = lds_bytes_for<CfgK3S3>(Cin);
+    else return false;
+    if (lds_bytes) *lds_bytes = bytes;
+    return bytes <= kMaxLds;
+}
+
+template <class Cfg>
+static hipError_t launch_direct(const Conv2dShape& s, const float* x, const float* w, const float* bias,
+                                float* dst, bool map, hipStream_t stream) {
+    const int CINQ = (s.Cin + 3) / 4;
+    const int plane = plane_floats<Cfg>(CINQ);
+    const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
+    const int tiles_h = (s.PH + Cfg::TPH - 1) / Cfg::TPH;
+    const int tiles_w = (s.PW + Cfg::TPW - 1) / Cfg::TPW;
+    const int co_ranges = (s.Cout + Cfg::CO_RANGE - 1) / Cfg::CO_RANGE;
+    dim3 grid(tiles_h * tiles_w, co_ranges, s.B);
+    dim3 block(Cfg::NT);
+    hipError_t e;
+    if (map) {
+        e = hipFuncSetAttribute((const void*)conv2d_pool_mfma_kernel<Cfg, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((conv2d_pool_mfma_kernel<Cfg, true>), grid, block, lds, stream, x, w, bias, dst,
+                           s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, tiles_w);
+    } else {
+        e = hipFuncSetAttribute((const void*)conv2d_pool_mfma_kernel<Cfg, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((conv2d_pool_mfma_kernel<Cfg, false>), grid, block, lds, stream, x, w, bias, dst,
+                           s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, tiles_w);
+    }
+    return hipGetLastError();
+}
+
+hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
+                              float* dst, bool map, hipStream_t stream) {
+    if (s.K == 3 && s.S == 4) return launch_direct<CfgK3S4>(s, x, w, bias, dst, map, stream);
+    if (s.K == 5 && s.S == 3) return launch_direct<CfgK5S3>(s, x, w, bias, dst, map, stream);
+    if (s.K == 3 && s.S == 2) return launch_direct<CfgK3S2>(s, x, w, bias, dst, map, stream);
+    if (s.K == 3 && s.S == 3) return launch_direct<CfgK3S3>(s, x, w, bias, dst, map, stream);
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- simple direct conv (any K, s)
+
+// One thread per (co, ph, pw) of one batch item: the window's s*s conv
+// outputs are summed straight from global memory.  The general fallback.
+template <bool MAP>
+__global__ __launch_bounds__(256) void conv2d_pool_simple_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ dst, int Cin, int H, int W, int Cout, int K, int S, int PH, int PW) {
+    __shared__ float red[4];
+    const int b = blockIdx.y;
+    const int n = Cout * PH * PW;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    float v = 0.f;
+    if (idx < n) {
+        const int co = idx / (PH * PW);
+        const int rem = idx - co * (PH * PW);
+        const int ph = rem / PW, pw = rem - (rem / PW) * PW;
+        const float* xb = x + (size_t)b * Cin * H * W;
+        const float* wc = w + (size_t)co * Cin * K * K;
+        float acc = 0.f;
+        for (int dy = 0; dy < S; ++dy)
+            for (int dx = 0; dx < S; ++dx)
+                for (int ic = 0; ic < Cin; ++ic)
+                    for (int ky = 0; ky < K; ++ky) {
+                        const float* xr = xb + (ic * H + ph * S + dy + ky) * W + pw * S + dx;
+                        const float* wr = wc + (ic * K + ky) * K;
+                        for (int kx = 0; kx < K; ++kx) acc += xr[kx] * wr[kx];
+                    }
+        const float avg = acc / (float)(S * S) + (bias ? bias[co] : 0.f);
+        if constexpr (MAP)
+            dst[(size_t)b * n + idx] = avg;
+        else
+            v = logistic(avg);
+    }
+    if constexpr (!MAP) {
+        const float s = block_sum<4>(v, red);
+        if (threadIdx.x == 0) atomicAdd(dst + b, s);
+    }
+}
+
+hipError_t conv2d_simple_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
+                                float* dst, bool map, hipStream_t stream) {
+    const int n = s.Cout * s.PH * s.PW;
+    dim3 grid((n + 255) / 256, s.B);
+    if (map)
+        hipLaunchKernelGGL((conv2d_pool_simple_kernel<true>), grid, dim3(256), 0, stream, x, w, bias, dst, s.Cin,
+                           s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW);
+    else
+        hipLaunchKernelGGL((conv2d_pool_simple_kernel<false>), grid, dim3(256), 0, stream, x, w, bias, dst, s.Cin,
+                           s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- zero fill
+
+__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+hipError_t fill_zero(float* p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace fconv

@@ -1,0 +1,168 @@
+// fconv_api.hip -- the C ABI of libfconv (declared in include/fconv.h): argument
+// checks, algorithm choice and kernel dispatch.  Host code only.
+#include <limits.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <stdio.h>
+
+#include "../../include/fconv.h"
+#include "fconv_internal.hpp"
+
+namespace {
+
+using fconv::Conv2dShape;
+using fconv::DwsepShape;
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *r = a * b;
+    return true;
+}
+
+bool fits_i32(int64_t v) { return v >= 0 && v <= INT32_MAX; }
+
+bool log_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char* e = getenv("FCONV_LOG");
+        on = (e && e[0] && e[0] != '0') ? 1 : 0;
+    }
+    return on == 1;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FCONV_OK : FCONV_EHIP; }
+
+// Validates a Conv2d call.  Returns FCONV_OK and fills `s`, or an error.
+// Element counts per batch item must fit int32 (kernel offsets are 32-bit
+// inside one batch item); larger shapes are FCONV_EUNSUPPORTED.
+int check_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
+                 int64_t K, int64_t pool, const void* dst, Conv2dShape* s) {
+    if (!x || !w || !dst) return FCONV_EINVAL;
+    if (B < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || K < 1 || pool < 1) return FCONV_EINVAL;
+    if (H < K || W < K) return FCONV_EINVAL;
+    int64_t t, per_item_x, nx, nw;
+    if (!mul_ok(Cin, H, &t) || !mul_ok(t, W, &per_item_x) || !mul_ok(per_item_x, B, &nx)) return FCONV_EINVAL;
+    if (!mul_ok(Cout, Cin, &t) || !mul_ok(t, K, &t) || !mul_ok(t, K, &nw)) return FCONV_EINVAL;
+    const int64_t PH = (H - K + 1) / pool, PW = (W - K + 1) / pool;
+    int64_t per_item_map, nmap;
+    if (!mul_ok(Cout, PH, &t) || !mul_ok(t, PW, &per_item_map) || !mul_ok(per_item_map, B, &nmap))
+        return FCONV_EINVAL;
+    if (!fits_i32(per_item_x) || !fits_i32(nw) || !fits_i32(per_item_map) || B > 65535 || pool > 4096 ||
+        K > 4096 || Cout > (1 << 20))
+        return FCONV_EUNSUPPORTED;
+    s->B = (int)B; s->Cin = (int)Cin; s->H = (int)H; s->W = (int)W; s->Cout = (int)Cout;
+    s->K = (int)K; s->S = (int)pool; s->PH = (int)PH; s->PW = (int)PW;
+    return FCONV_OK;
+}
+
+int pick_conv2d_algo(const Conv2dShape& s, int algo) {
+    if (algo == FCONV_ALGO_AUTO)
+        return fconv::conv2d_mfma_supported(s.Cin, s.K, s.S, nullptr) ? FCONV_ALGO_DIRECT_MFMA
+                                                                       : FCONV_ALGO_DIRECT_SIMPLE;
+    if (algo == FCONV_ALGO_DIRECT_MFMA)
+        return fconv::conv2d_mfma_supported(s.Cin, s.K, s.S, nullptr) ? algo : FCONV_EUNSUPPORTED;
+    if (algo == FCONV_ALGO_DIRECT_SIMPLE) return algo;
+    return FCONV_EINVAL;
+}
+
+int run_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
+               int64_t K, const float* bias, int64_t pool, int algo, float* dst, bool map, void* stream) {
+    Conv2dShape s;
+    int rc = check_conv2d(x, B, Cin, H, W, w, Cout, K, pool, dst, &s);
+    if (rc != FCONV_OK) return rc;
+    const int a = pick_conv2d_algo(s, algo);
+    if (a < 0) return a;
+    hipStream_t st = (hipStream_t)stream;
+    if (log_enabled())
+        fprintf(stderr, "[fconv] conv2d%s B=%d Cin=%d H=%d W=%d Cout=%d K=%d pool=%d -> algo %d\n",
+                map ? "_map" : "", s.B, s.Cin, s.H, s.W, s.Cout, s.K, s.S, a);
+    if (s.PH == 0 || s.PW == 0) {
+        // Empty pooled map: the sum is 0 and the map has no elements.
+        return map ? FCONV_OK : status_of(fconv::fill_zero(dst, s.B, st));
+    }
+    if (!map) {
+        hipError_t e = fconv::fill_zero(dst, s.B, st);
+        if (e != hipSuccess) return FCONV_EHIP;
+    }
+    hipError_t e = (a == FCONV_ALGO_DIRECT_MFMA) ? fconv::conv2d_mfma_launch(s, x, w, bias, dst, map, st)
+                                                 : fconv::conv2d_simple_launch(s, x, w, bias, dst, map, st);
+    return status_of(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fconv2d_pool_sigmoid_sum(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w,
+                             int64_t Cout, int64_t K, const float* bias, int64_t pool, float* out, void* stream) {
+    return run_conv2d(x, B, Cin, H, W, w, Cout, K, bias, pool, FCONV_ALGO_AUTO, out, false, stream);
+}
+
+int fconv2d_pool_sigmoid_sum_algo(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w,
+                                  int64_t Cout, int64_t K, const float* bias, int64_t pool, int algo, float* out,
+                                  void* stream) {
+    return run_conv2d(x, B, Cin, H, W, w, Cout, K, bias, pool, algo, out, false, stream);
+}
+
+int fconv2d_pool_map(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
+                     int64_t K, const float* bias, int64_t pool, int algo, float* pooled, void* stream) {
+    return run_conv2d(x, B, Cin, H, W, w, Cout, K, bias, pool, algo, pooled, true, stream);
+}
+
+int fconv2d_pool_out_size(int64_t H, int64_t W, int64_t K, int64_t pool, int64_t* PH, int64_t* PW) {
+    if (!PH || !PW || H < 1 || W < 1 || K < 1 || pool < 1 || H < K || W < K) return FCONV_EINVAL;
+    *PH = (H - K + 1) / pool;
+    *PW = (W - K + 1) / pool;
+    return FCONV_OK;
+}
+
+int fconv2d_select_algo(int64_t Cin, int64_t Cout, int64_t K, int64_t pool) {
+    if (Cin < 1 || Cout < 1 || K < 1 || pool < 1 || Cin > INT32_MAX || K > 4096 || pool > 4096)
+        return FCONV_EINVAL;
+    return fconv::conv2d_mfma_supported((int)Cin, (int)K, (int)pool, nullptr) ? FCONV_ALGO_DIRECT_MFMA
+                                                                              : FCONV_ALGO_DIRECT_SIMPLE;
+}
+
+int64_t dwsep_conv1d_out_len(int64_t T, int64_t K, int64_t pad) {
+    if (T < 1 || K < 1 || pad < 0 || pad > INT32_MAX) return -1;
+    const int64_t tout = T + 2 * pad - K + 1;
+    return tout >= 1 ? tout : -1;
+}
+
+int dwsep_conv1d(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
+                 const float* w_pw, int64_t O, const float* b_pw, int64_t pad, float* y, void* stream) {
+    if (!x || !w_dw || !w_pw || !y) return FCONV_EINVAL;
+    if (B < 1 || C < 1 || T < 1 || O < 1 || K < 1 || pad < 0) return FCONV_EINVAL;
+    const int64_t Tout = dwsep_conv1d_out_len(T, K, pad);
+    if (Tout < 1) return FCONV_EINVAL;
+    int64_t per_item_x, per_item_y, t, n;
+    if (!mul_ok(C, T, &per_item_x) || !mul_ok(per_item_x, B, &n)) return FCONV_EINVAL;
+    if (!mul_ok(O, Tout, &per_item_y) || !mul_ok(per_item_y, B, &n)) return FCONV_EINVAL;
+    if (!mul_ok(O, C, &t) || !mul_ok(C, K, &n)) return FCONV_EINVAL;
+    if (!fits_i32(per_item_x) || !fits_i32(per_item_y) || !fits_i32(t) || !fits_i32(n) || B > 65535 || K > 8192 ||
+        O > (1 << 20))
+        return FCONV_EUNSUPPORTED;
+    if (!fconv::dwsep_supported((int)K, (int)O)) return FCONV_EUNSUPPORTED;
+    DwsepShape s{(int)B, (int)C, (int)T, (int)K, (int)O, (int)pad, (int)Tout};
+    if (log_enabled())
+        fprintf(stderr, "[fconv] dwsep B=%d C=%d T=%d K=%d O=%d pad=%d Tout=%d\n", s.B, s.C, s.T, s.K, s.O, s.pad,
+                s.Tout);
+    return status_of(fconv::dwsep_launch(s, x, w_dw, w_pw, b_pw, y, (hipStream_t)stream));
+}
+
+const char* fconv_strerror(int status) {
+    switch (status) {
+        case FCONV_OK: return "success";
+        case FCONV_EINVAL: return "invalid argument";
+        case FCONV_EUNSUPPORTED: return "shape not supported by the requested algorithm";
+        case FCONV_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int fconv_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// fconv_device.hpp -- device helpers shared by the libfconv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fconv {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// One fp32 matrix-core step: D(16x16) = A(16x4) * B(4x16) + C, all fp32
+// (v_mfma_f32_16x16x4_f32).  Operand layout per lane l of the wave:
+//   A: row l%16, k-index l/16        B: k-index l/16, column l%16
+//   C/D element r (0..3): row 4*(l/16) + r, column l%16
+__device__ __forceinline__ floatx4 mfma_16x16x4(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sums v over the workgroup; the result is valid in thread 0 only.
+template <int NWAVES>
+__device__ __forceinline__ float block_sum(float v, float* red /* NWAVES floats of LDS */) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float s = 0.f;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 0; i < NWAVES; ++i) s += red[i];
+    }
+    return s;
+}
+
+__device__ __forceinline__ float logistic(float a) { return 1.0f / (1.0f + expf(-a)); }
+
+}  // namespace fconv

@@ -1,0 +1,153 @@
+/*
+ * fconv.h -- C ABI of libfconv: fused fp32 convolutions for AMD MI355X (gfx950).
+ *
+ * Two operations, each one call that keeps its intermediate out of HBM:
+ *
+ *   fconv2d_pool_sigmoid_sum   Conv2d (stride 1, no padding) -> AvgPool2d
+ *                              (kernel = stride = pool, floor) -> sigmoid ->
+ *                              sum over channels and space: one scalar per
+ *                              batch item.  Defined by the POPCORNBENCH
+ *                              reasoning trace "Kimi-K2.6 l2_p65"
+ *                              (Conv2d -> AvgPool2d -> Sigmoid -> Sum): its
+ *                              opening problem statement and the fused
+ *                              per-pooled-output formula that follows it.
+ *
+ *   dwsep_conv1d               depthwise Conv1d (kernel K, zero padding pad,
+ *                              stride 1) -> pointwise 1x1 Conv1d + bias.
+ *                              Defined by the POPCORNBENCH reasoning trace
+ *                              "Kimi-K2.6 l2_p7" (depthwise-separable Conv1d):
+ *                              its opening problem statement (output length)
+ *                              and the per-output formula
+ *                              out[b,o,t] = sum_c (sum_k in[b,c,t+k-pad] *
+ *                              dw[c,k]) * pw[o,c] + bias[o].
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, contiguous, row-major fp32 in DEVICE memory
+ *     (hipMalloc'd or equivalent), owned by the caller.  Only 4-byte
+ *     alignment is required.  Input buffers are never written.
+ *   - The library allocates no memory and keeps no state between calls; it
+ *     is reentrant.  Calls on different streams may run concurrently as
+ *     long as their output buffers do not overlap.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Every call is asynchronous with respect to the host: it enqueues its
+ *     kernels on `stream` and returns.  Outputs are valid once the stream
+ *     has reached that point.
+ *   - Sizes are int64_t.  Argument checks happen on the host before any
+ *     device work; a failed check returns FCONV_EINVAL and enqueues nothing.
+ *   - A HIP launch error is returned as FCONV_EHIP (from hipGetLastError).
+ *   - The sums inside a call are fp32.  fconv2d_pool_sigmoid_sum combines
+ *     partial sums with floating-point atomics, so its last bits may differ
+ *     from call to call.
+ */
+#ifndef FCONV_H
+#define FCONV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define FCONV_OK 0
+#define FCONV_EINVAL (-1)      /* an argument failed a check; nothing was enqueued */
+#define FCONV_EUNSUPPORTED (-2) /* the requested algorithm cannot run this shape   */
+#define FCONV_EHIP (-3)        /* the HIP runtime reported an error              */
+
+/* Algorithms for the Conv2d path.  AUTO picks the fastest one that supports
+ * the shape. */
+#define FCONV_ALGO_AUTO 0
+#define FCONV_ALGO_DIRECT_MFMA 1   /* direct conv on fp32 matrix cores (templated K, pool) */
+#define FCONV_ALGO_DIRECT_SIMPLE 2 /* direct conv, one thread per pooled output, any shape */
+
+/*
+ * fconv2d_pool_sigmoid_sum
+ *
+ *   out[b] = sum_{co < Cout} sum_{ph < PH} sum_{pw < PW}
+ *              sigmoid( (1/pool^2) * sum_{dy,dx < pool} conv[b,co,ph*pool+dy,pw*pool+dx] )
+ *   conv[b,co,y,x] = bias[co] + sum_{ic,ky,kx} x[b,ic,y+ky,x+kx] * w[co,ic,ky,kx]
+ *   Hc = H-K+1, Wc = W-K+1, PH = floor(Hc/pool), PW = floor(Wc/pool);
+ *   sigmoid(a) = 1/(1+exp(-a)).  Conv rows/columns at or beyond PH*pool
+ *   (PW*pool) feed no pooled output (floor mode).
+ *
+ *   x    [B, Cin, H, W]
+ *   w    [Cout, Cin, K, K]   (cross-correlation, as PyTorch's Conv2d)
+ *   bias [Cout], or NULL for no bias
+ *   out  [B], fully overwritten (the call zeroes it on `stream` first)
+ *
+ * FCONV_EINVAL when: x, w or out is NULL; any of B, Cin, Cout, H, W, K, pool
+ * is < 1; H < K or W < K; an element count overflows int64.  A shape with
+ * PH = 0 or PW = 0 is valid and gives out = 0.
+ * FCONV_EUNSUPPORTED when one batch item's input (Cin*H*W), the weight or one
+ * batch item's pooled map (Cout*PH*PW) exceeds 2^31-1 elements, B > 65535,
+ * Cout > 2^20, or K or pool > 4096.
+ */
+int fconv2d_pool_sigmoid_sum(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
+                             const float* w, int64_t Cout, int64_t K, const float* bias,
+                             int64_t pool, float* out, void* stream);
+
+/* As fconv2d_pool_sigmoid_sum, with an explicit algorithm (FCONV_ALGO_*).
+ * FCONV_EUNSUPPORTED if that algorithm has no instance for (K, pool). */
+int fconv2d_pool_sigmoid_sum_algo(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
+                                  const float* w, int64_t Cout, int64_t K, const float* bias,
+                                  int64_t pool, int algo, float* out, void* stream);
+
+/*
+ * fconv2d_pool_map -- the pre-sigmoid pooled map of the same computation,
+ *   pooled[b,co,ph,pw] = bias[co] + (1/pool^2) * sum_{dy,dx} (conv - bias)
+ * written for every (b, co, ph, pw) of [B, Cout, PH, PW], computed by the
+ * same kernels (same tiling and accumulation order) as the fused call.
+ * This is the elementwise view the fused scalar hides; it exists for
+ * verification and costs an extra HBM write of B*Cout*PH*PW floats.
+ * Errors as fconv2d_pool_sigmoid_sum_algo; with PH or PW = 0 nothing is
+ * written.
+ */
+int fconv2d_pool_map(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
+                     const float* w, int64_t Cout, int64_t K, const float* bias, int64_t pool,
+                     int algo, float* pooled, void* stream);
+
+/* Output size of the pooled map: PH, PW (either may be 0).  Pure host
+ * arithmetic, no device access.  FCONV_EINVAL on sizes < 1, H < K, W < K. */
+int fconv2d_pool_out_size(int64_t H, int64_t W, int64_t K, int64_t pool, int64_t* PH, int64_t* PW);
+
+/* The algorithm FCONV_ALGO_AUTO would run for this shape (a FCONV_ALGO_*
+ * value), or FCONV_EINVAL.  Pure host logic, no device access. */
+int fconv2d_select_algo(int64_t Cin, int64_t Cout, int64_t K, int64_t pool);
+
+/*
+ * dwsep_conv1d
+ *
+ *   y[b,o,t] = b_pw[o] + sum_{c < C} w_pw[o,c] * D[b,c,t]
+ *   D[b,c,t] = sum_{k < K} w_dw[c,k] * x[b,c,t+k-pad]   (x read as 0 outside [0,T))
+ *   Tout = T + 2*pad - K + 1, t < Tout.  No depthwise bias.
+ *
+ *   x     [B, C, T]
+ *   w_dw  [C, K]     (PyTorch's depthwise weight [C,1,K])
+ *   w_pw  [O, C]     (PyTorch's pointwise weight [O,C,1])
+ *   b_pw  [O], or NULL for no bias
+ *   y     [B, O, Tout], fully overwritten
+ *
+ * FCONV_EINVAL when: x, w_dw, w_pw or y is NULL; any of B, C, T, O, K is
+ * < 1; pad < 0; Tout < 1; an element count overflows int64.
+ * FCONV_EUNSUPPORTED when C*T, O*Tout, O*C or C*K exceeds 2^31-1, B > 65535,
+ * O > 2^20, or K is so wide that the depthwise window does not fit the
+ * kernel's LDS tile (K above roughly 500).
+ */
+int dwsep_conv1d(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
+                 const float* w_pw, int64_t O, const float* b_pw, int64_t pad, float* y,
+                 void* stream);
+
+/* Tout for dwsep_conv1d, or -1 if the arguments are invalid.  Host only. */
+int64_t dwsep_conv1d_out_len(int64_t T, int64_t K, int64_t pad);
+
+/* Static description of a status code (never NULL). */
+const char* fconv_strerror(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fconv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FCONV_H */

@@ -1,0 +1,145 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/fconv.h declares, and
+reject bad arguments with the documented status codes before any device
+work.  No call here reaches a kernel launch: every argument set fails a
+host check first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fconv.h")
+LIB = os.path.join(ROOT, "fp32_convolution_amd", "libfconv.so")
+
+EINVAL, EUNSUP = -1, -2
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails a host check first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libfconv.so is not built (python -m fp32_convolution_amd.build)")
+    import fp32_convolution_amd as fc
+
+    return fc.lib
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ["fconv2d_pool_sigmoid_sum", "dwsep_conv1d", "fconv2d_pool_map", "fconv_strerror",
+                 "fconv_version", "fconv2d_pool_sigmoid_sum_algo", "fconv2d_pool_out_size",
+                 "fconv2d_select_algo", "dwsep_conv1d_out_len"]:
+        assert must in names, must
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in fconv.h but not exported"
+
+
+def test_version_and_strerror(lib):
+    assert lib.fconv_version() >= 100
+    for code in [0, -1, -2, -3, 7]:
+        assert isinstance(lib.fconv_strerror(code), bytes) and lib.fconv_strerror(code)
+    assert lib.fconv_strerror(0) == b"success"
+
+
+def test_out_size(lib):
+    import fp32_convolution_amd as fc
+
+    assert fc.conv2d_out_size(384, 384, 3, 4) == (95, 95)
+    assert fc.conv2d_out_size(257, 257, 5, 3) == (84, 84)
+    assert fc.conv2d_out_size(16, 16, 3, 4) == (3, 3)
+    assert fc.conv2d_out_size(5, 6, 3, 4) == (0, 1)
+    ph, pw = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.fconv2d_pool_out_size(2, 5, 3, 1, ctypes.byref(ph), ctypes.byref(pw)) == EINVAL
+    assert lib.fconv2d_pool_out_size(5, 5, 3, 0, ctypes.byref(ph), ctypes.byref(pw)) == EINVAL
+    assert lib.fconv2d_pool_out_size(5, 5, 3, 1, None, ctypes.byref(pw)) == EINVAL
+
+
+def test_dwsep_out_len(lib):
+    assert lib.dwsep_conv1d_out_len(4096, 9, 4) == 4096
+    assert lib.dwsep_conv1d_out_len(256, 9, 4) == 256
+    assert lib.dwsep_conv1d_out_len(10, 3, 0) == 8
+    assert lib.dwsep_conv1d_out_len(4, 9, 0) == -1
+    assert lib.dwsep_conv1d_out_len(4, 9, -1) == -1
+    assert lib.dwsep_conv1d_out_len(0, 1, 0) == -1
+
+
+def test_select_algo(lib):
+    assert lib.fconv2d_select_algo(8, 64, 3, 4) == 1   # direct MFMA instance
+    assert lib.fconv2d_select_algo(16, 128, 5, 3) == 1
+    assert lib.fconv2d_select_algo(3, 4, 3, 4) == 1
+    assert lib.fconv2d_select_algo(3, 4, 7, 2) == 2    # no MFMA instance for K=7 -> simple path
+    assert lib.fconv2d_select_algo(512, 4, 3, 4) == 2  # LDS tile too large -> simple path
+    assert lib.fconv2d_select_algo(0, 4, 3, 4) == EINVAL
+
+
+def conv(lib, x=FAKE, B=1, Cin=1, H=8, W=8, w=FAKE, Cout=1, K=3, b=None, pool=2, algo=0, out=FAKE):
+    return lib.fconv2d_pool_sigmoid_sum_algo(x, B, Cin, H, W, w, Cout, K, b, pool, algo, out, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(w=None), dict(out=None),
+    dict(B=0), dict(Cin=0), dict(H=0), dict(W=-1), dict(Cout=0), dict(K=0), dict(pool=0),
+    dict(H=2, K=3), dict(W=2, K=3),
+    dict(B=2**40, Cin=2**30),       # element count overflows int64
+    dict(algo=9),                   # unknown algorithm
+])
+def test_conv2d_einval(lib, kw):
+    assert conv(lib, **kw) == EINVAL
+
+
+def test_conv2d_unsupported(lib):
+    assert conv(lib, K=7, algo=1) == EUNSUP            # no MFMA instance for K=7
+    assert conv(lib, Cin=2**16, H=2**8, W=2**8) == EUNSUP  # per-item elements beyond int32
+    assert conv(lib, B=70000) == EUNSUP
+
+
+def test_conv2d_entry_points_share_checks(lib):
+    assert lib.fconv2d_pool_sigmoid_sum(None, 1, 1, 8, 8, FAKE, 1, 3, None, 2, FAKE, None) == EINVAL
+    assert lib.fconv2d_pool_map(FAKE, 1, 1, 8, 8, FAKE, 1, 3, None, 0, 0, FAKE, None) == EINVAL
+    assert lib.fconv2d_pool_map(FAKE, 1, 1, 8, 8, FAKE, 1, 9, None, 2, 1, FAKE, None) == EINVAL  # H < K
+
+
+def dw(lib, x=FAKE, B=1, C=4, T=16, wd=FAKE, K=3, wp=FAKE, O=4, b=None, pad=1, y=FAKE):
+    return lib.dwsep_conv1d(x, B, C, T, wd, K, wp, O, b, pad, y, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(wd=None), dict(wp=None), dict(y=None),
+    dict(B=0), dict(C=0), dict(T=0), dict(K=0), dict(O=0), dict(pad=-1),
+    dict(T=4, K=9, pad=0),              # Tout < 1
+    dict(B=2**40, C=2**30),             # overflow
+])
+def test_dwsep_einval(lib, kw):
+    assert dw(lib, **kw) == EINVAL
+
+
+def test_dwsep_unsupported(lib):
+    assert dw(lib, C=2**16, T=2**16) == EUNSUP
+    assert dw(lib, K=4000, T=5000) == EUNSUP   # depthwise window too wide for the LDS tile
+    assert dw(lib, B=70000) == EUNSUP
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    import fp32_convolution_amd as fc
+
+    x = torch.zeros(1, 1, 8, 8)
+    with pytest.raises(ValueError):
+        fc.conv2d_pool_sigmoid_sum(x, torch.zeros(1, 1, 3, 3), None, 2)
+    with pytest.raises(TypeError):
+        fc.dwsep_conv1d(torch.zeros(1, 2, 8, dtype=torch.float64), torch.zeros(2, 3), torch.zeros(2, 2), None, 1)

@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar (spec tolerance for fp32): |gpu - oracle| <= 1e-4 + 1e-4*|oracle|
+element by element, with the oracle in float64.  For the fused Conv2d sum the
+elementwise check runs on the pre-sigmoid pooled map, which the same kernels
+write; the scalar sums are checked as well.  Full-size workloads compare
+sampled outputs that the oracle computes one by one, plus whole batch items.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import fconv_inputs as fi
+import oracle
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+RTOL = ATOL = 1e-4
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp32_convolution_amd as fc
+
+    return fc
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def assert_close(got, want, what):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    err = np.abs(got - want)
+    bound = ATOL + RTOL * np.abs(want)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst at {i}: "
+                             f"gpu={got[i]!r} oracle={want[i]!r}")
+
+
+# ------------------------------------------------------------------ Conv2d path
+
+SMALL_CONV = [
+    # B, Cin, H, W, Cout, K, s
+    (2, 3, 16, 16, 4, 3, 4),        # the tiny workload
+    (2, 8, 70, 75, 64, 3, 4),       # several 8x16 tiles, ragged in both directions
+    (1, 16, 60, 50, 128, 5, 3),     # K5/s3 instance: several 4x12 tiles, ragged
+    (2, 5, 41, 37, 20, 3, 4),       # odd Cin, Cout not a multiple of 16
+    (1, 8, 40, 40, 70, 3, 4),       # Cout > 64: two channel ranges
+    (1, 3, 37, 41, 7, 3, 2),        # K3/s2 instance
+    (2, 4, 30, 28, 9, 3, 3),        # K3/s3 instance
+    (1, 2, 23, 19, 5, 7, 2),        # no MFMA instance (K=7): simple path
+    (1, 3, 9, 9, 4, 5, 3),          # PH = PW = 1
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_CONV)
+@pytest.mark.parametrize("algo", [0, 2])
+def test_conv2d_small(fc, shape, algo):
+    B, Cin, H, W, Cout, K, s = shape
+    announce(f"conv2d small {shape} algo={algo}")
+    x, w, b = fi.conv2d_inputs(B, Cin, H, W, Cout, K, seed=1)
+    want_out, want_map = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, want_pooled=True)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    got_map = fc.conv2d_pool_map(xd, wd, bd, s, algo=algo).cpu().numpy()
+    got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=algo).cpu().numpy()
+    assert_close(got_map, want_map, f"pooled map {shape}")
+    assert_close(got_out, want_out, f"out {shape}")
+
+
+def test_conv2d_no_bias(fc):
+    announce("conv2d no bias")
+    x, w, _ = fi.conv2d_inputs(2, 8, 40, 44, 64, 3, seed=2)
+    want = oracle.conv2d_pool_sigmoid_sum(x, w, None, 4)
+    got = fc.conv2d_pool_sigmoid_sum(dev(x), dev(w), None, 4).cpu().numpy()
+    assert_close(got, want, "out, bias=None")
+
+
+def test_conv2d_empty_pool_gives_zero(fc):
+    announce("conv2d empty pooled map")
+    x, w, b = fi.conv2d_inputs(3, 2, 5, 9, 4, 3, seed=3)   # Hc = 3 < pool 4 -> PH = 0
+    out = torch.full((3,), 7.0, device="cuda")
+    fc.conv2d_pool_sigmoid_sum(dev(x), dev(w), dev(b), 4, out=out)
+    assert out.cpu().numpy().tolist() == [0.0, 0.0, 0.0]
+
+
+def test_conv2d_repeat_calls_overwrite(fc):
+    announce("conv2d repeated calls")
+    x, w, b = fi.conv2d_inputs(2, 8, 40, 40, 64, 3, seed=4)
+    want = oracle.conv2d_pool_sigmoid_sum(x, w, b, 4)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    out = torch.full((2,), 1e6, device="cuda")
+    for _ in range(3):
+        fc.conv2d_pool_sigmoid_sum(xd, wd, bd, 4, out=out)
+    assert_close(out.cpu().numpy(), want, "out after 3 calls")
+
+
+FULL_CONV = {
+    "conv2d_full": [0, 1, 63, 64, 126, 127],
+    "conv2d_tail": [0, 31, 62, 63],
+}
+
+
+@pytest.fixture(scope="module")
+def full_conv_inputs():
+    return {name: fi.make(name, seed=0) for name in FULL_CONV}
+
+
+@pytest.mark.parametrize("name", list(FULL_CONV))
+def test_conv2d_full_size(fc, full_conv_inputs, name):
+    cfg = fi.WORKLOADS[name]
+    s = cfg["pool"]
+    x, w, b = full_conv_inputs[name]
+    announce(f"conv2d full size {name}")
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s).cpu().numpy()
+    got_map = fc.conv2d_pool_map(xd, wd, bd, s).cpu().numpy()
+    # whole batch items through the literal oracle
+    idx = FULL_CONV[name]
+    want_out = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, batch_idx=idx)
+    assert_close(got_out[idx], want_out, f"{name} out[{idx}]")
+    # the sum over the pooled map the kernels wrote equals the fused sums
+    sig = (1.0 / (1.0 + np.exp(-got_map.astype(np.float64)))).sum(axis=(1, 2, 3))
+    assert_close(got_out, sig, f"{name} fused sum vs sigmoid(map) sum")
+    # sampled pooled values: random, plus every corner / edge / tile seam
+    B, Cout, PH, PW = got_map.shape
+    rng = np.random.default_rng(5)
+    n = 20000
+    samp = np.stack([rng.integers(0, B, n), rng.integers(0, Cout, n), rng.integers(0, PH, n),
+                     rng.integers(0, PW, n)], axis=1)
+    edge = [0, 1, 3, 4, 7, 8, 11, 12, 15, 16, PH - 2, PH - 1]
+    extra = [(bb, co, ph, pw) for bb in (0, B - 1) for co in (0, Cout - 1)
+             for ph in edge for pw in edge if ph < PH and pw < PW]
+    samp = np.concatenate([samp, np.array(extra)], axis=0)
+    want = oracle.conv2d_pooled_at(x, w, b, s, samp)
+    assert_close(got_map[tuple(samp.T)], want, f"{name} sampled pooled map")
+
+
+@pytest.mark.parametrize("name", list(FULL_CONV))
+def test_conv2d_full_size_closed_forms(fc, full_conv_inputs, name):
+    cfg = fi.WORKLOADS[name]
+    s = cfg["pool"]
+    x, w, b = full_conv_inputs[name]
+    announce(f"conv2d full size closed forms {name}")
+    B, Cin, H, W = x.shape
+    Cout = w.shape[0]
+    PH, PW = fc.conv2d_out_size(H, W, w.shape[2], s)
+    xd = dev(x)
+    # zero weights and bias: sigmoid(0) = 1/2 everywhere, exactly representable sums
+    z = fc.conv2d_pool_sigmoid_sum(xd, torch.zeros_like(dev(w)), torch.zeros(Cout, device="cuda"), s)
+    assert (z.cpu().numpy() == Cout * PH * PW / 2.0).all()
+    # sigma symmetry: negating w and b gives Cout*PH*PW - out
+    wd, bd = dev(w), dev(b)
+    pos = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s).cpu().numpy().astype(np.float64)
+    neg = fc.conv2d_pool_sigmoid_sum(xd, -wd, -bd, s).cpu().numpy().astype(np.float64)
+    assert_close(pos + neg, np.full(B, float(Cout * PH * PW)), f"{name} sigma symmetry")
+
+
+# ------------------------------------------------------------------ depthwise-separable path
+
+SMALL_DW = [
+    # B, C, T, O, K, pad
+    (4, 16, 256, 32, 9, 4),     # the small workload
+    (2, 256, 300, 512, 9, 4),   # big instance, ragged T
+    (2, 64, 200, 200, 9, 4),    # mid instance, O not a multiple of 16
+    (3, 10, 77, 33, 9, 4),      # C not a multiple of 4 (scalar weight loads)
+    (1, 48, 70, 300, 5, 0),     # no padding, big instance with masked channels
+    (2, 20, 40, 24, 3, 7),      # pad > K: Tout > T
+    (1, 8, 5, 16, 9, 4),        # T < K
+    (2, 100, 129, 70, 1, 0),    # 1-tap depthwise (pure GEMM), C not a multiple of 16
+    (1, 300, 64, 64, 9, 4),     # C spans several chunks with a partial last chunk
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_DW)
+def test_dwsep_small(fc, shape):
+    B, C, T, O, K, pad = shape
+    announce(f"dwsep small {shape}")
+    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=7)
+    want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad)
+    got = fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad).cpu().numpy()
+    assert_close(got, want, f"y {shape}")
+
+
+def test_dwsep_no_bias_and_torch_shapes(fc):
+    announce("dwsep no bias, [C,1,K] and [O,C,1] weights")
+    x, w_dw, w_pw, _ = fi.dwsep_inputs(2, 32, 100, 48, 9, seed=8)
+    want = oracle.dwsep_conv1d(x, w_dw, w_pw, None, 4)
+    got = fc.dwsep_conv1d(dev(x), dev(w_dw[:, None, :]), dev(w_pw[:, :, None]), None, 4).cpu().numpy()
+    assert_close(got, want, "y no bias")
+
+
+def test_dwsep_unaligned_weights(fc):
+    # w_pw starting 4 bytes past a 16-byte boundary takes the scalar weight path.
+    announce("dwsep unaligned w_pw")
+    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(1, 32, 64, 32, 9, seed=9)
+    want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, 4)
+    buf = torch.zeros(w_pw.size + 1, device="cuda")
+    buf[1:] = dev(w_pw).reshape(-1)
+    wp = buf[1:].view(32, 32)
+    got = fc.dwsep_conv1d(dev(x), dev(w_dw), wp, dev(b_pw), 4).cpu().numpy()
+    assert_close(got, want, "y unaligned")
+
+
+def test_dwsep_full_size(fc):
+    name = "dwsep_full"
+    cfg = fi.WORKLOADS[name]
+    announce(f"dwsep full size {name}")
+    x, w_dw, w_pw, b_pw = fi.make(name, seed=0)
+    got = fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), cfg["pad"]).cpu().numpy()
+    # whole batch items
+    for bi in (0, 31):
+        want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, cfg["pad"], batch_idx=[bi])[0]
+        assert_close(got[bi], want, f"{name} y[{bi}]")
+    # sampled outputs over all items, with the padded edges
+    B, O, Tout = got.shape
+    rng = np.random.default_rng(6)
+    n = 30000
+    samp = np.stack([rng.integers(0, B, n), rng.integers(0, O, n), rng.integers(0, Tout, n)], axis=1)
+    edge = np.array([(bb, o, t) for bb in range(0, B, 5) for o in (0, 255, 511) for t in (0, 1, 3, 4, 63, 64,
+                                                                                         Tout - 5, Tout - 1)])
+    samp = np.concatenate([samp, edge])
+    want = oracle.dwsep_conv1d_at(x, w_dw, w_pw, b_pw, cfg["pad"], samp)
+    assert_close(got[tuple(samp.T)], want, f"{name} sampled")
+
+
+def test_dwsep_full_size_linearity(fc):
+    announce("dwsep full size linearity")
+    cfg = fi.WORKLOADS["dwsep_full"]
+    x, w_dw, w_pw, b_pw = fi.make("dwsep_full", seed=0)
+    x2 = fi.normal(x.shape, 17, 0)
+    wd, wp = dev(w_dw), dev(w_pw)
+    y1 = fc.dwsep_conv1d(dev(x), wd, wp, None, cfg["pad"])
+    y2 = fc.dwsep_conv1d(dev(x2), wd, wp, None, cfg["pad"])
+    ys = fc.dwsep_conv1d(dev(x) * 0.5 - dev(x2) * 2.0, wd, wp, None, cfg["pad"])
+    diff = (ys - (0.5 * y1 - 2.0 * y2)).abs().max().item()
+    scale = ys.abs().max().item()
+    assert diff <= 1e-4 * max(1.0, scale), (diff, scale)
