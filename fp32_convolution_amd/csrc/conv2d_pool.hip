@@ -63,6 +63,7 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
     constexpr int K = Cfg::K, S = Cfg::S, CB = Cfg::CB, P = Cfg::P, WCO = Cfg::WCO;
     constexpr int TPH = Cfg::TPH, TPW = Cfg::TPW, IH = Cfg::IH, IW = Cfg::IW;
     constexpr int QP = Cfg::QP, RP = Cfg::RP, NBV = Cfg::NBV, NT = Cfg::NT;
+    constexpr int NR = S + K - 1;  // input rows a pooled row's windows touch
 
     extern __shared__ float lds[];
     __shared__ float red[Cfg::NW];
@@ -76,25 +77,74 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
     const int tile_x = blockIdx.x - tile_y * tiles_w;
     const int b = blockIdx.z;
     const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
+    const int g = lane >> 4;   // k-slot of the MFMA: channel group
+    const int l16 = lane & 15; // row of A / column of B
+    const int co0 = blockIdx.y * Cfg::CO_RANGE + wco * 16 * CB;
+
+    const buf_rsrc rx = make_rsrc(x + (size_t)b * Cin * H * W, Cin * H * W * 4);
+    const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
+
+    // Weights of channel quad q for this lane: a[ky][cb][kx] =
+    // w[co0 + cb*16 + l16, g*CINQ + q, ky, kx], 0 where co or ic is out of range.
+    auto load_a = [&](float (&a)[K][CB][K], int q) {
+        const int ic = g * CINQ + q;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int co = co0 + cb * 16 + l16;
+            const bool ok = (co < Cout) && (ic < Cin) && (q < CINQ);
+            const int base = ok ? (co * Cin + ic) * (K * K * 4) : kBufOOB;
+#pragma unroll
+            for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+                for (int kx = 0; kx < K; ++kx) a[ky][cb][kx] = buf_load_f32(rw, base + (ky * K + kx) * 4);
+        }
+    };
+    float a_cur[K][CB][K], a_nxt[K][CB][K];
+    load_a(a_cur, 0);  // in flight while the tile is staged
+
+    // Biases of this lane's output channels co0 + cb*16 + 4g + r (0 where
+    // co >= Cout or bias is NULL: the resource is then empty).
+    const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
+    float bco[CB][4];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int co = co0 + cb * 16 + 4 * g + r;
+            bco[cb][r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
+        }
 
     // Stage the input tile: channel ic at ic*plane, row r at r*RP, column c at
-    // phase (c % S)*QP + slot c/S.  Zero outside the image and for ic >= Cin.
-    const float* xb = x + (size_t)b * Cin * H * W;
+    // phase (c % S)*QP + slot c/S.  Out-of-image elements and channels
+    // >= Cin load as 0 through the buffer bounds check.  STAGE_U loads per
+    // thread are in flight before their LDS writes.
     const int nload = 4 * CINQ * IH * IW;
-    for (int i = tid; i < nload; i += NT) {
-        const int ic = i / (IH * IW);
-        const int rem = i - ic * (IH * IW);
-        const int r = rem / IW;
-        const int c = rem - r * IW;
-        const int gy = y0 + r, gx = x0 + c;
-        float v = 0.f;
-        if (ic < Cin && gy < H && gx < W) v = xb[(ic * H + gy) * W + gx];
-        lds[ic * plane + r * RP + (c % S) * QP + c / S] = v;
+    constexpr int STAGE_U = 8;
+    for (int base = 0; base < nload; base += NT * STAGE_U) {
+        float v[STAGE_U];
+#pragma unroll
+        for (int u = 0; u < STAGE_U; ++u) {
+            const int i = base + u * NT + tid;
+            const int ic = i / (IH * IW);
+            const int rem = i - ic * (IH * IW);
+            const int r = rem / IW;
+            const int c = rem - r * IW;
+            const int gy = y0 + r, gx = x0 + c;
+            const bool ok = (ic < Cin) && (gy < H) && (gx < W);
+            v[u] = buf_load_f32(rx, ok ? ((ic * H + gy) * W + gx) * 4 : kBufOOB);
+        }
+#pragma unroll
+        for (int u = 0; u < STAGE_U; ++u) {
+            const int i = base + u * NT + tid;
+            const int ic = i / (IH * IW);
+            const int rem = i - ic * (IH * IW);
+            const int r = rem / IW;
+            const int c = rem - r * IW;
+            if (i < nload) lds[ic * plane + r * RP + (c % S) * QP + c / S] = v[u];
+        }
     }
     __syncthreads();
 
-    const int g = lane >> 4;   // k-slot of the MFMA: channel group
-    const int l16 = lane & 15; // row of A / column of B
     int pbase[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -102,7 +152,6 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
         const int py = j / TPW, px = j - (j / TPW) * TPW;
         pbase[p] = g * CINQ * plane + py * S * RP + px;
     }
-    const int co0 = blockIdx.y * Cfg::CO_RANGE + wco * 16 * CB;
 
     floatx4 acc[CB][P];
 #pragma unroll
@@ -110,33 +159,29 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
 #pragma unroll
         for (int p = 0; p < P; ++p) acc[cb][p] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // Input row rr of a window (0 <= rr < S+K-1) is shared by every (ky, dy)
+    // with ky + dy = rr: it is read from LDS once and multiplied by each of
+    // those weight rows.  The next row (and the next quad's weights) load
+    // while the current row's matrix instructions run.
+    auto load_row = [&](float (&bv)[P][NBV], int lq, int rr) {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int cc = 0; cc < NBV; ++cc) bv[p][cc] = lds[pbase[p] + lq + rr * RP + (cc % S) * QP + cc / S];
+    };
+
     for (int q = 0; q < CINQ; ++q) {
-        const int ic = g * CINQ + q;
         const int lq = q * plane;
-        const float* wq[CB];
-        bool wok[CB];
+        load_a(a_nxt, q + 1);  // zeros past the last quad
+        float bcur[P][NBV], bnxt[P][NBV];
+        load_row(bcur, lq, 0);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int co = co0 + cb * 16 + l16;
-            wok[cb] = (co < Cout) && (ic < Cin);
-            wq[cb] = w + ((size_t)(wok[cb] ? co : 0) * Cin + (wok[cb] ? ic : 0)) * (K * K);
-        }
+        for (int rr = 0; rr < NR; ++rr) {
+            if (rr + 1 < NR) load_row(bnxt, lq, rr + 1);
 #pragma unroll
-        for (int ky = 0; ky < K; ++ky) {
-            float a[CB][K];
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                for (int kx = 0; kx < K; ++kx) a[cb][kx] = wok[cb] ? wq[cb][ky * K + kx] : 0.f;
-#pragma unroll
-            for (int dy = 0; dy < S; ++dy) {
-                const int rr = ky + dy;
-                float bv[P][NBV];
-#pragma unroll
-                for (int p = 0; p < P; ++p)
-#pragma unroll
-                    for (int cc = 0; cc < NBV; ++cc)
-                        bv[p][cc] = lds[pbase[p] + lq + rr * RP + (cc % S) * QP + cc / S];
+            for (int ky = 0; ky < K; ++ky) {
+                const int dy = rr - ky;
+                if (dy < 0 || dy >= S) continue;
 #pragma unroll
                 for (int kx = 0; kx < K; ++kx)
 #pragma unroll
@@ -145,9 +190,21 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
                         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                             for (int p = 0; p < P; ++p)
-                                acc[cb][p] = mfma_16x16x4(a[cb][kx], bv[p][dx + kx], acc[cb][p]);
+                                acc[cb][p] = mfma_16x16x4(a_cur[ky][cb][kx], bcur[p][dx + kx], acc[cb][p]);
+            }
+            if (rr + 1 < NR) {
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+#pragma unroll
+                    for (int cc = 0; cc < NBV; ++cc) bcur[p][cc] = bnxt[p][cc];
             }
         }
+#pragma unroll
+        for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int kx = 0; kx < K; ++kx) a_cur[ky][cb][kx] = a_nxt[ky][cb][kx];
     }
 
     // Epilogue.  Lane (g, l16) holds, for block (cb, p) and r = 0..3, the
@@ -162,13 +219,12 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
         for (int r = 0; r < 4; ++r) {
             const int co = co0 + cb * 16 + 4 * g + r;
             const bool cok = co < Cout;
-            const float bco = (cok && bias) ? bias[co] : 0.f;
 #pragma unroll
             for (int p = 0; p < P; ++p) {
                 const int j = (wpos * P + p) * 16 + l16;
                 const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
                 if (cok && ph < PH && pw < PW) {
-                    const float avg = acc[cb][p][r] * inv + bco;
+                    const float avg = acc[cb][p][r] * inv + bco[cb][r];
                     if constexpr (MAP)
                         dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
                     else
@@ -185,8 +241,15 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
 // Instances.  (3,4): 8x16 pooled tile, 4 waves side by side along positions,
 // each wave all 64 channels of its range.  (5,3): 4x12 tile (84 = 21*4 = 7*12,
 // no ragged tiles on 84x84 maps), 4 waves side by side along channels.
-using CfgK3S4 = DirectCfg<3, 4, 4, 2, 1, 4, 8, 16>;
-using CfgK5S3 = DirectCfg<5, 3, 2, 3, 4, 1, 4, 12>;
+// The FCONV_CFG_* macros let a build override an instance's tiling.
+#ifndef FCONV_CFG_K3S4
+#define FCONV_CFG_K3S4 3, 4, 2, 2, 2, 2, 4, 16
+#endif
+#ifndef FCONV_CFG_K5S3
+#define FCONV_CFG_K5S3 5, 3, 2, 3, 4, 1, 4, 12
+#endif
+using CfgK3S4 = DirectCfg<FCONV_CFG_K3S4>;
+using CfgK5S3 = DirectCfg<FCONV_CFG_K5S3>;
 using CfgK3S2 = DirectCfg<3, 2, 4, 2, 1, 4, 8, 16>;
 using CfgK3S3 = DirectCfg<3, 3, 4, 2, 1, 4, 8, 16>;
 

@@ -50,7 +50,9 @@ int check_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, c
     int64_t per_item_map, nmap;
     if (!mul_ok(Cout, PH, &t) || !mul_ok(t, PW, &per_item_map) || !mul_ok(per_item_map, B, &nmap))
         return FCONV_EINVAL;
-    if (!fits_i32(per_item_x) || !fits_i32(nw) || !fits_i32(per_item_map) || B > 65535 || pool > 4096 ||
+    // Kernels address one batch item's input and the weight through buffer
+    // resources (< 2^31 bytes each); other offsets are 32-bit.
+    if (per_item_x >= (1 << 29) || nw >= (1 << 29) || !fits_i32(per_item_map) || B > 65535 || pool > 4096 ||
         K > 4096 || Cout > (1 << 20))
         return FCONV_EUNSUPPORTED;
     s->B = (int)B; s->Cin = (int)Cin; s->H = (int)H; s->W = (int)W; s->Cout = (int)Cout;

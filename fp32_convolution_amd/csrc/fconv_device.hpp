@@ -16,6 +16,23 @@ __device__ __forceinline__ floatx4 mfma_16x16x4(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Raw buffer loads.  A buffer resource covers [base, base + bytes); a load
+// whose byte offset is at or beyond `bytes` returns 0 without touching
+// memory, so zero padding and masking need no branch.  Offsets are unsigned
+// 32-bit; kBufOOB is past the end of every resource the library builds
+// (each covers < 2^31 bytes).  0x00020000 is the gfx9-family descriptor word
+// for 32-bit data.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+constexpr int kBufOOB = (int)0x80000000u;
+
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ float buf_load_f32(buf_rsrc r, int byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -37,6 +54,9 @@ __device__ __forceinline__ float block_sum(float v, float* red /* NWAVES floats 
     return s;
 }
 
-__device__ __forceinline__ float logistic(float a) { return 1.0f / (1.0f + expf(-a)); }
+// Logistic sigmoid 1/(1+e^-a) with the hardware exp2 (v_exp_f32) and
+// reciprocal: relative error a few ulp for |a| < 80, exactly 1/2 at a = 0,
+// saturating to 0 or 1 (never NaN) for large |a|.
+__device__ __forceinline__ float logistic(float a) { return __frcp_rn(1.0f + __expf(-a)); }
 
 }  // namespace fconv

@@ -78,9 +78,10 @@ extern "C" {
  * FCONV_EINVAL when: x, w or out is NULL; any of B, Cin, Cout, H, W, K, pool
  * is < 1; H < K or W < K; an element count overflows int64.  A shape with
  * PH = 0 or PW = 0 is valid and gives out = 0.
- * FCONV_EUNSUPPORTED when one batch item's input (Cin*H*W), the weight or one
- * batch item's pooled map (Cout*PH*PW) exceeds 2^31-1 elements, B > 65535,
- * Cout > 2^20, or K or pool > 4096.
+ * FCONV_EUNSUPPORTED when one batch item's input (Cin*H*W) or the weight
+ * (Cout*Cin*K*K) has 2^29 elements or more, one batch item's pooled map
+ * (Cout*PH*PW) exceeds 2^31-1 elements, B > 65535, Cout > 2^20, or K or
+ * pool > 4096.
  */
 int fconv2d_pool_sigmoid_sum(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
                              const float* w, int64_t Cout, int64_t K, const float* bias,
