@@ -115,32 +115,46 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
         }
 
     // Stage the input tile: channel ic at ic*plane, row r at r*RP, column c at
-    // phase (c % S)*QP + slot c/S.  Out-of-image elements and channels
-    // >= Cin load as 0 through the buffer bounds check.  STAGE_U loads per
-    // thread are in flight before their LDS writes.
-    const int nload = 4 * CINQ * IH * IW;
-    constexpr int STAGE_U = 8;
-    for (int base = 0; base < nload; base += NT * STAGE_U) {
-        float v[STAGE_U];
+    // phase (c % S)*QP + slot c/S.  Each wave copies whole rows: the row's
+    // address and bounds live in a buffer resource built in scalar registers
+    // (empty for rows outside the image and channels >= Cin, so they load
+    // as 0), and each lane's column offset is fixed for the whole tile, so a
+    // row costs its loads, one address add and its LDS writes.
+    {
+        constexpr int NCH = (IW + 63) / 64;  // 64-column chunks per row
+        constexpr int UR = 4;                // rows in flight per wave
+        int voff[NCH], loff[NCH];
 #pragma unroll
-        for (int u = 0; u < STAGE_U; ++u) {
-            const int i = base + u * NT + tid;
-            const int ic = i / (IH * IW);
-            const int rem = i - ic * (IH * IW);
-            const int r = rem / IW;
-            const int c = rem - r * IW;
-            const int gy = y0 + r, gx = x0 + c;
-            const bool ok = (ic < Cin) && (gy < H) && (gx < W);
-            v[u] = buf_load_f32(rx, ok ? ((ic * H + gy) * W + gx) * 4 : kBufOOB);
+        for (int k = 0; k < NCH; ++k) {
+            const int c = lane + 64 * k;
+            voff[k] = (c < IW && x0 + c < W) ? (x0 + c) * 4 : kBufOOB;
+            loff[k] = (c < IW) ? (c % S) * QP + c / S : -1;
         }
+        const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+        const int nrows = 4 * CINQ * IH;
+        const float* xb = x + (size_t)b * Cin * H * W;
+        for (int row0 = wave_s; row0 < nrows; row0 += Cfg::NW * UR) {
+            float v[UR][NCH];
 #pragma unroll
-        for (int u = 0; u < STAGE_U; ++u) {
-            const int i = base + u * NT + tid;
-            const int ic = i / (IH * IW);
-            const int rem = i - ic * (IH * IW);
-            const int r = rem / IW;
-            const int c = rem - r * IW;
-            if (i < nload) lds[ic * plane + r * RP + (c % S) * QP + c / S] = v[u];
+            for (int u = 0; u < UR; ++u) {
+                const int row = row0 + u * Cfg::NW;
+                const int ic = row / IH, r = row - (row / IH) * IH;
+                const bool ok = (row < nrows) && (ic < Cin) && (y0 + r < H);
+                const buf_rsrc rrow = make_rsrc(xb + (ok ? (ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) v[u][k] = buf_load_f32(rrow, voff[k]);
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int row = row0 + u * Cfg::NW;
+                if (row < nrows) {
+                    const int ic = row / IH, r = row - (row / IH) * IH;
+                    float* lrow = lds + ic * plane + r * RP;
+#pragma unroll
+                    for (int k = 0; k < NCH; ++k)
+                        if (loff[k] >= 0) lrow[loff[k]] = v[u][k];
+                }
+            }
         }
     }
     __syncthreads();
@@ -238,20 +252,21 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
     }
 }
 
-// Instances.  (3,4): 8x16 pooled tile, 4 waves side by side along positions,
-// each wave all 64 channels of its range.  (5,3): 4x12 tile (84 = 21*4 = 7*12,
-// no ragged tiles on 84x84 maps), 4 waves side by side along channels.
+// Instances (tilings measured on MI355X).  K3/s4 and the other K3 pools: a
+// 4x16 pooled tile, 4 waves each owning 16 output channels of a 64-channel
+// range and all 64 positions.  K5/s3: a 4x12 tile (84 = 21*4 = 7*12, so an
+// 84x84 map has no ragged tiles), 8 waves of 16 channels each.
 // The FCONV_CFG_* macros let a build override an instance's tiling.
 #ifndef FCONV_CFG_K3S4
-#define FCONV_CFG_K3S4 3, 4, 2, 2, 2, 2, 4, 16
+#define FCONV_CFG_K3S4 3, 4, 1, 4, 4, 1, 4, 16
 #endif
 #ifndef FCONV_CFG_K5S3
-#define FCONV_CFG_K5S3 5, 3, 2, 3, 4, 1, 4, 12
+#define FCONV_CFG_K5S3 5, 3, 1, 3, 8, 1, 4, 12
 #endif
 using CfgK3S4 = DirectCfg<FCONV_CFG_K3S4>;
 using CfgK5S3 = DirectCfg<FCONV_CFG_K5S3>;
-using CfgK3S2 = DirectCfg<3, 2, 4, 2, 1, 4, 8, 16>;
-using CfgK3S3 = DirectCfg<3, 3, 4, 2, 1, 4, 8, 16>;
+using CfgK3S2 = DirectCfg<3, 2, 1, 4, 4, 1, 4, 16>;
+using CfgK3S3 = DirectCfg<3, 3, 1, 4, 4, 1, 4, 16>;
 
 template <class Cfg>
 static int plane_floats(int CINQ) {

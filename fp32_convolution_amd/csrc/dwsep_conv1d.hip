@@ -13,76 +13,59 @@
 //
 // Workgroup: one batch item, a tile of OT output channels x TT time steps,
 // all C input channels in chunks of CC:
-//   1. x[c0:c0+CC, t0-pad : t0+TT+K-1-pad] and w_dw[c0:c0+CC, :] -> LDS
-//      (coalesced, zero padded)
-//   2. D[t][c] for the chunk -> LDS (row pitch CC+4 floats).  A thread makes
-//      4 channels x TPT consecutive steps from a register window of the input.
+//   1. x[c0:c0+CC, t0-pad : t0+TT+K-1-pad] -> LDS.  Each wave copies whole
+//      rows through a per-row buffer resource (scalar registers); the
+//      hardware bounds check supplies the zero padding.
+//   2. Depthwise stage -> D[t][c] in LDS (row pitch CC+4 floats).  Each wave
+//      owns CC/NW channels, so their taps are wave-uniform scalar loads, and
+//      lane l makes step t = l (consecutive LDS words, no bank conflicts).
 //   3. v_mfma_f32_16x16x4_f32 over the chunk.  Within each group of 16
 //      channels, lane group g holds channels 4g..4g+3 for 4 consecutive
-//      MFMA steps, so one 16-byte global load gives a lane its 4 weights
-//      (w_pw rows are contiguous in c) and one 16-byte LDS read its 4 D
-//      values.  The weight loads run one 16-channel group ahead of the
-//      matrix instructions that use them.
+//      MFMA steps, so one 16-byte load gives a lane its 4 weights (w_pw rows
+//      are contiguous in c) and one 16-byte LDS read its 4 D values.  The
+//      weight loads run one 16-channel group ahead of the matrix
+//      instructions that use them; the group index is a scalar offset.
 //   4. + bias, store.
-// Out-of-range output channels read a clamped (valid) weight row and are
-// never stored; channels >= C have D = 0, so their clamped weights add 0.
+// Out-of-range output rows read a clamped (valid) weight row and are never
+// stored.  Channels >= C have D = 0, so whatever weights pair with them
+// (the next row's, or 0 past the end of w_pw) add nothing.
 #include "fconv_device.hpp"
 #include "fconv_internal.hpp"
 
 namespace fconv {
 
 // OB, TB: 16x16 output blocks per wave along o and t; WO, WT: waves along o
-// and t; CC: channel chunk; TPT: time steps per thread in the depthwise
-// stage; KC: compile-time depthwise taps (0 = runtime K); MINW: waves per
-// SIMD the register budget must allow.
-template <int OB_, int TB_, int WO_, int WT_, int CC_, int TPT_, int KC_, int MINW_>
+// and t; CC: channel chunk; KC: compile-time depthwise taps (0 = runtime K);
+// MINW: waves per SIMD the register budget must allow.
+template <int OB_, int TB_, int WO_, int WT_, int CC_, int KC_, int MINW_>
 struct DwsepCfg {
-    static constexpr int OB = OB_, TB = TB_, WO = WO_, WT = WT_, CC = CC_, TPT = TPT_, KC = KC_, MINW = MINW_;
+    static constexpr int OB = OB_, TB = TB_, WO = WO_, WT = WT_, CC = CC_, KC = KC_, MINW = MINW_;
     static constexpr int NW = WO * WT;
     static constexpr int NT = 64 * NW;
     static constexpr int OT = 16 * OB * WO;
     static constexpr int TT = 16 * TB * WT;
     static constexpr int CCP = CC + 4;  // D row pitch in floats
+    static constexpr int CPW = CC / NW; // depthwise channels per wave
     static_assert(CC % 16 == 0, "channel chunk must be whole 16-channel groups");
-    static_assert(TT % TPT == 0, "time tile must split into per-thread runs");
+    static_assert(CC % NW == 0 && CPW % 4 == 0, "each wave makes whole 4-channel groups of D");
 };
-
-template <class Cfg>
-__device__ __forceinline__ void load_pw(floatx4 (&a)[Cfg::OB], const float* __restrict__ w_pw, int o_first, int O,
-                                        int c, int C, bool vec) {
-    // Weights of output rows o_first + ob*16 (clamped to O-1) and channels
-    // c..c+3 (clamped to C-1).  Clamped entries multiply D = 0 or feed an
-    // output that is not stored.
-#pragma unroll
-    for (int ob = 0; ob < Cfg::OB; ++ob) {
-        const int o = min(o_first + ob * 16, O - 1);
-        const float* row = w_pw + (size_t)o * C;
-        if (vec) {
-            a[ob] = *reinterpret_cast<const floatx4*>(row + min(c, C - 4));
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) a[ob][j] = row[min(c + j, C - 1)];
-        }
-    }
-}
 
 template <class Cfg, bool VEC>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
     const float* __restrict__ x, const float* __restrict__ w_dw, const float* __restrict__ w_pw,
     const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int Kr, int O, int pad, int Tout) {
-    constexpr int OB = Cfg::OB, TB = Cfg::TB, WO = Cfg::WO, CC = Cfg::CC, CCP = Cfg::CCP, TPT = Cfg::TPT;
-    constexpr int TT = Cfg::TT, NT = Cfg::NT, NW = Cfg::NW;
+    constexpr int OB = Cfg::OB, TB = Cfg::TB, WO = Cfg::WO, CC = Cfg::CC, CCP = Cfg::CCP, CPW = Cfg::CPW;
+    constexpr int TT = Cfg::TT, NW = Cfg::NW;
     const int K = Cfg::KC > 0 ? Cfg::KC : Kr;
 
     extern __shared__ float lds[];
-    float* Ds = lds;                    // [TT][CCP]
-    float* wsm = lds + TT * CCP;        // [CC][K]
-    float* xs = wsm + CC * K;           // [CC][XW]
+    float* Ds = lds;             // [TT][CCP]
+    float* xs = lds + TT * CCP;  // [CC][XW]
     const int XW = TT + K - 1;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wo = wave % WO;
     const int wt = wave / WO;
     const int g = lane >> 4;
@@ -93,6 +76,28 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
     const float* xb = x + (size_t)b * C * T;
     const int NG = (C + 15) / 16;  // 16-channel groups
 
+    // Pointwise weights: lane (g, l16) of block ob reads row min(o, O-1) at
+    // channel 16*grp + 4g.  The group moves the resource's base (scalar
+    // arithmetic), so the per-lane offsets stay fixed and the bounds check
+    // still covers every byte read: loads past the end of w_pw return 0.
+    int woff[OB];
+#pragma unroll
+    for (int ob = 0; ob < OB; ++ob) woff[ob] = (min(o0 + ob * 16 + l16, O - 1) * C + 4 * g) * 4;
+    auto load_pw = [&](floatx4 (&a)[OB], int grp) {
+        const buf_rsrc rw = make_rsrc(w_pw + 16 * grp, (O * C - 16 * grp) * 4);
+#pragma unroll
+        for (int ob = 0; ob < OB; ++ob) {
+            if constexpr (VEC) {
+                a[ob] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[ob], 0, 0));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    a[ob][j] =
+                        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, woff[ob] + 4 * j, 0, 0));
+            }
+        }
+    };
+
     floatx4 acc[OB][TB];
 #pragma unroll
     for (int i = 0; i < OB; ++i)
@@ -100,76 +105,55 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
         for (int j = 0; j < TB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     floatx4 a_next[OB];
-    load_pw<Cfg>(a_next, w_pw, o0 + l16, O, 4 * g, C, VEC);
+    load_pw(a_next, 0);
 
+    constexpr int UR = 4;  // rows in flight per wave while staging
+    const int nch = (XW + 63) / 64;
     for (int c0 = 0; c0 < C; c0 += CC) {
         __syncthreads();  // the previous chunk's LDS data is no longer read
-        // 1. input chunk with halo, and the chunk's depthwise weights.  Loads
-        //    are branch-free (clamped address, value selected to 0) and issued
-        //    STAGE_U at a time so they overlap.
-        {
-            constexpr int STAGE_U = 8;
-            const int nx = CC * XW;
-            for (int base = 0; base < nx; base += NT * STAGE_U) {
-                float v[STAGE_U];
+        // 1. input rows c0..c0+CC-1, steps t0-pad .. t0-pad+XW-1
+        for (int ch = 0; ch < nch; ++ch) {
+            const int u = ch * 64 + lane;
+            const int src = t0 - pad + u;
+            const int voff = (u < XW && src >= 0) ? src * 4 : kBufOOB;  // src >= T: past the row's end
+            for (int r0 = wave; r0 < CC; r0 += NW * UR) {
+                float v[UR];
 #pragma unroll
-                for (int u = 0; u < STAGE_U; ++u) {
-                    const int i = base + u * NT + tid;
-                    const int c = i / XW;
-                    const int src = t0 - pad + (i - c * XW);
-                    const bool ok = (i < nx) && (c0 + c < C) && (src >= 0) && (src < T);
-                    const float val = xb[(size_t)(ok ? c0 + c : 0) * T + (ok ? src : 0)];
-                    v[u] = ok ? val : 0.f;
+                for (int uu = 0; uu < UR; ++uu) {
+                    const int row = r0 + uu * NW;
+                    const bool ok = (row < CC) && (c0 + row < C);
+                    const buf_rsrc rrow = make_rsrc(xb + (ok ? (size_t)(c0 + row) * T : 0), ok ? T * 4 : 0);
+                    v[uu] = buf_load_f32(rrow, voff);
                 }
 #pragma unroll
-                for (int u = 0; u < STAGE_U; ++u) {
-                    const int i = base + u * NT + tid;
-                    if (i < nx) xs[i] = v[u];
+                for (int uu = 0; uu < UR; ++uu) {
+                    const int row = r0 + uu * NW;
+                    if (row < CC && u < XW) xs[row * XW + u] = v[uu];
                 }
-            }
-            const int nw_valid = min(CC, C - c0) * K;
-            for (int i = tid; i < CC * K; i += NT) {
-                const float val = w_dw[(size_t)c0 * K + min(i, nw_valid - 1)];
-                wsm[i] = i < nw_valid ? val : 0.f;
             }
         }
         __syncthreads();
-        // 2. depthwise stage: 4 channels x TPT steps per thread
-        for (int i = tid; i < (CC / 4) * (TT / TPT); i += NT) {
-            const int tq = i % (TT / TPT);
-            const int c4 = (i / (TT / TPT)) * 4;
-            const int t = tq * TPT;
-            float d[TPT][4];
+        // 2. depthwise stage: wave owns channels wave*CPW .. +CPW-1 of the chunk
+        for (int t = lane; t < TT; t += 64) {
+            float d[CPW];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float* xr = xs + (c4 + j) * XW + t;
-                const float* wr = wsm + (c4 + j) * K;
+            for (int cc = 0; cc < CPW; ++cc) {
+                const int c = wave * CPW + cc;
+                const float* wr = w_dw + (size_t)min(c0 + c, C - 1) * K;  // rows >= C: x is 0 there
+                const float* xr = xs + c * XW + t;
+                float s = 0.f;
                 if constexpr (Cfg::KC > 0) {
-                    float win[TPT + Cfg::KC - 1];
 #pragma unroll
-                    for (int u = 0; u < TPT + Cfg::KC - 1; ++u) win[u] = xr[u];
-                    float wk[Cfg::KC];
-#pragma unroll
-                    for (int k = 0; k < Cfg::KC; ++k) wk[k] = wr[k];
-#pragma unroll
-                    for (int tt = 0; tt < TPT; ++tt) {
-                        float s = 0.f;
-#pragma unroll
-                        for (int k = 0; k < Cfg::KC; ++k) s += wk[k] * win[tt + k];
-                        d[tt][j] = s;
-                    }
+                    for (int k = 0; k < Cfg::KC; ++k) s += wr[k] * xr[k];
                 } else {
-#pragma unroll
-                    for (int tt = 0; tt < TPT; ++tt) {
-                        float s = 0.f;
-                        for (int k = 0; k < K; ++k) s += wr[k] * xr[tt + k];
-                        d[tt][j] = s;
-                    }
+                    for (int k = 0; k < K; ++k) s += wr[k] * xr[k];
                 }
+                d[cc] = s;
             }
 #pragma unroll
-            for (int tt = 0; tt < TPT; ++tt)
-                *reinterpret_cast<floatx4*>(Ds + (t + tt) * CCP + c4) = floatx4{d[tt][0], d[tt][1], d[tt][2], d[tt][3]};
+            for (int c4 = 0; c4 < CPW; c4 += 4)
+                *reinterpret_cast<floatx4*>(Ds + t * CCP + wave * CPW + c4) =
+                    floatx4{d[c4], d[c4 + 1], d[c4 + 2], d[c4 + 3]};
         }
         __syncthreads();
         // 3. pointwise GEMM over this chunk, weights one group ahead
@@ -180,7 +164,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
                 floatx4 a[OB];
 #pragma unroll
                 for (int ob = 0; ob < OB; ++ob) a[ob] = a_next[ob];
-                if (grp + 1 < NG) load_pw<Cfg>(a_next, w_pw, o0 + l16, O, (grp + 1) * 16 + 4 * g, C, VEC);
+                if (grp + 1 < NG) load_pw(a_next, grp + 1);
                 floatx4 bq[TB];
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
@@ -198,14 +182,15 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
     }
 
     // 4. epilogue: lane (g, l16) holds y[o0 + ob*16 + 4g + r, t0 + (wt*TB + tb)*16 + l16]
+    const buf_rsrc rb = make_rsrc(b_pw, b_pw ? O * 4 : 0);
     float* yb = y + (size_t)b * O * Tout;
 #pragma unroll
     for (int ob = 0; ob < OB; ++ob)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int o = o0 + ob * 16 + 4 * g + r;
+            const float bo = buf_load_f32(rb, o < O ? o * 4 : kBufOOB);
             if (o >= O) continue;
-            const float bo = b_pw ? b_pw[o] : 0.f;
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
                 const int t = t0 + (wt * TB + tb) * 16 + l16;
@@ -214,21 +199,19 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
         }
 }
 
-// Instances.  Wide (O > 64): 256 x 64 tile, 4 waves of 64 x 64, register
-// budget for 3 waves per SIMD so three workgroups share a CU and one's load
-// and depthwise phases overlap the others' matrix work.  Small: 32 x 32.
+// Instances.  Wide (O > 64): 256 x 64 tile, 8 waves of 32 x 64, register
+// budget for 4 waves per SIMD.  Small: 32 x 32.
 // FCONV_CFG_DW9 lets a build override the K = 9 instance's tiling.
 #ifndef FCONV_CFG_DW9
-#define FCONV_CFG_DW9 2, 4, 8, 1, 64, 2, 9, 4
+#define FCONV_CFG_DW9 2, 4, 8, 1, 64, 9, 4
 #endif
 using DwWide9 = DwsepCfg<FCONV_CFG_DW9>;
-using DwWideK = DwsepCfg<4, 4, 4, 1, 64, 4, 0, 3>;
-using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 2, 0, 2>;
+using DwWideK = DwsepCfg<2, 4, 8, 1, 64, 0, 4>;
+using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 
 template <class Cfg>
 static size_t dw_lds_bytes(int K) {
-    return ((size_t)Cfg::TT * Cfg::CCP + (size_t)Cfg::CC * K + (size_t)Cfg::CC * (Cfg::TT + K - 1)) *
-           sizeof(float);
+    return ((size_t)Cfg::TT * Cfg::CCP + (size_t)Cfg::CC * (Cfg::TT + K - 1)) * sizeof(float);
 }
 
 template <class Cfg>

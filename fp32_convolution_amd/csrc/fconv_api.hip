@@ -144,8 +144,10 @@ int dwsep_conv1d(const float* x, int64_t B, int64_t C, int64_t T, const float* w
     if (!mul_ok(C, T, &per_item_x) || !mul_ok(per_item_x, B, &n)) return FCONV_EINVAL;
     if (!mul_ok(O, Tout, &per_item_y) || !mul_ok(per_item_y, B, &n)) return FCONV_EINVAL;
     if (!mul_ok(O, C, &t) || !mul_ok(C, K, &n)) return FCONV_EINVAL;
-    if (!fits_i32(per_item_x) || !fits_i32(per_item_y) || !fits_i32(t) || !fits_i32(n) || B > 65535 || K > 8192 ||
-        O > (1 << 20))
+    // The kernel reads x rows (T floats) and w_pw (O*C floats) through buffer
+    // resources of < 2^31 bytes; other offsets are 32-bit per batch item.
+    if (!fits_i32(per_item_x) || !fits_i32(per_item_y) || t >= (1 << 29) || T >= (1 << 29) || !fits_i32(n) ||
+        B > 65535 || K > 8192 || O > (1 << 20))
         return FCONV_EUNSUPPORTED;
     if (!fconv::dwsep_supported((int)K, (int)O)) return FCONV_EUNSUPPORTED;
     DwsepShape s{(int)B, (int)C, (int)T, (int)K, (int)O, (int)pad, (int)Tout};

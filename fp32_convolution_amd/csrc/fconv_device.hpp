@@ -57,6 +57,6 @@ __device__ __forceinline__ float block_sum(float v, float* red /* NWAVES floats 
 // Logistic sigmoid 1/(1+e^-a) with the hardware exp2 (v_exp_f32) and
 // reciprocal: relative error a few ulp for |a| < 80, exactly 1/2 at a = 0,
 // saturating to 0 or 1 (never NaN) for large |a|.
-__device__ __forceinline__ float logistic(float a) { return __frcp_rn(1.0f + __expf(-a)); }
+__device__ __forceinline__ float logistic(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 }  // namespace fconv

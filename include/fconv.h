@@ -130,9 +130,9 @@ int fconv2d_select_algo(int64_t Cin, int64_t Cout, int64_t K, int64_t pool);
  *
  * FCONV_EINVAL when: x, w_dw, w_pw or y is NULL; any of B, C, T, O, K is
  * < 1; pad < 0; Tout < 1; an element count overflows int64.
- * FCONV_EUNSUPPORTED when C*T, O*Tout, O*C or C*K exceeds 2^31-1, B > 65535,
- * O > 2^20, or K is so wide that the depthwise window does not fit the
- * kernel's LDS tile (K above roughly 500).
+ * FCONV_EUNSUPPORTED when C*T, O*Tout or C*K exceeds 2^31-1, O*C or T is
+ * 2^29 or more, B > 65535, O > 2^20, or K is so wide that the depthwise
+ * window does not fit the kernel's LDS tile (K above roughly 500).
  */
 int dwsep_conv1d(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
                  const float* w_pw, int64_t O, const float* b_pw, int64_t pad, float* y,
