@@ -36,6 +36,86 @@ PEAK_HBM_GBPS = 8000.0
 CONV = "conv2d_full"
 DW = "dwsep_full"
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+# Sources that define the timed kernels; measured HBM traffic is reported
+# only while their hash matches the one recorded with the counters.
+KERNEL_SOURCES = {
+    "conv2d_pool_mfma_kernel": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
+                                "fp32_convolution_amd/csrc/fconv_device.hpp"],
+    "dwsep_mfma_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
+                          "fp32_convolution_amd/csrc/fconv_device.hpp"],
+}
+
+
+def sources_sha256(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the recorded counters, or None if the record
+    is missing or the kernel's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_sha256(kernel):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def ingest_counters(fetch_csv, write_csv, copy_mb, command):
+    """Writes TRAFFIC_FILE from two rocprofv3 --pmc runs of this script with
+    --copy-calibration-mb: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of each
+    timed kernel, scaled by what the same counters read for the calibration
+    copy of copy_mb MiB (which reads and writes exactly that many bytes)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = copy_mb * 1024.0
+    cal_f = [v for k, vs in fetch.items() if "copyBuffer" in k for v in vs if v > 0.25 * copy_kib]
+    cal_w = [v for k, vs in write.items() if "copyBuffer" in k for v in vs if v > 0.25 * copy_kib]
+    if not cal_f or not cal_w:
+        raise SystemExit("calibration copy not found in the counter files")
+    f_scale, w_scale = copy_kib / max(cal_f), copy_kib / max(cal_w)
+    out = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "calibration": f"device copy of {copy_mb} MiB: FETCH_SIZE {max(cal_f):.1f} KiB, "
+                          f"WRITE_SIZE {max(cal_w):.1f} KiB",
+           "command": command, "kernels": {}}
+    for kernel in KERNEL_SOURCES:
+        fk = [v for k, vs in fetch.items() if kernel in k for v in vs]
+        wk = [v for k, vs in write.items() if kernel in k for v in vs]
+        if not fk or not wk:
+            continue
+        fb = sum(fk) / len(fk) * 1024 * f_scale
+        wb = sum(wk) / len(wk) * 1024 * w_scale
+        name = next(k for k in fetch if kernel in k)
+        out["kernels"][kernel] = {"kernel_name": name, "dispatches": len(fk),
+                                  "fetch_kib_raw": round(sum(fk) / len(fk), 1),
+                                  "write_kib_raw": round(sum(wk) / len(wk), 1),
+                                  "hbm_read_bytes_per_launch": int(fb), "hbm_write_bytes_per_launch": int(wb),
+                                  "hbm_bytes_per_launch": int(fb + wb),
+                                  "sources_sha256": sources_sha256(kernel)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
 
 def conv2d_flops(cfg):
     Hc, Wc = cfg["H"] - cfg["K"] + 1, cfg["W"] - cfg["K"] + 1
@@ -109,7 +189,15 @@ def main():
     ap.add_argument("--cpu-dw-items", type=int, default=32, help="dwsep batch items in the oracle sample")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one device copy of this many MiB first (reference for HBM byte counters)")
+    ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MB"),
+                    help="write profiles/hbm_traffic.json from rocprofv3 counter files and exit")
+    ap.add_argument("--ingest-command", default="", help="the profiling command, recorded with the counters")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        fetch_csv, write_csv, copy_mb = args.ingest_counters
+        ingest_counters(fetch_csv, write_csv, int(copy_mb), args.ingest_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every kernel here runs on a single device and the "
@@ -189,6 +277,8 @@ def main():
 
     k_conv = kstats(ms_conv, f_conv, b_conv)
     k_dw = kstats(ms_dw, f_dw, b_dw)
+    k_conv["hbm_bytes_measured"] = measured_traffic("conv2d_pool_mfma_kernel")
+    k_dw["hbm_bytes_measured"] = measured_traffic("dwsep_mfma_kernel")
     achieved = f_conv / (k_conv["ms_mean"] * 1e-3) / 1e12
 
     result = {
@@ -218,7 +308,8 @@ def main():
             "peak": PEAK_FP32_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("conv2d_pool_mfma_kernel"),
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         },
         "wall_s_timed_region": round(t_wall, 3),
     }

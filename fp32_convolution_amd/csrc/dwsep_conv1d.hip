@@ -107,28 +107,64 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
     floatx4 a_next[OB];
     load_pw(a_next, 0);
 
-    constexpr int UR = 4;  // rows in flight per wave while staging
+    // 1. Input rows c0..c0+CC-1, steps t0-pad .. t0-pad+XW-1, copied into
+    //    LDS a row per wave at a time through per-row buffer resources.  With
+    //    a compile-time K each lane's column offsets are fixed and the next
+    //    chunk's rows are loaded into registers while this chunk computes.
+    constexpr int UR = 4;  // rows in flight per wave (runtime-K path)
     const int nch = (XW + 63) / 64;
+    constexpr int NCHC = Cfg::KC > 0 ? (TT + Cfg::KC - 1 + 63) / 64 : 1;
+    constexpr int RPW = CC / NW;  // rows per wave
+    int voffc[NCHC];
+#pragma unroll
+    for (int ch = 0; ch < NCHC; ++ch) {
+        const int u = ch * 64 + lane;
+        const int src = t0 - pad + u;
+        voffc[ch] = (u < XW && src >= 0) ? src * 4 : kBufOOB;  // src >= T: past the row's end
+    }
+    float xv[Cfg::KC > 0 ? RPW : 1][NCHC];
+    auto load_rows = [&](int c0) {
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+            const int row = wave + rr * NW;
+            const bool ok = c0 + row < C;
+            const buf_rsrc rrow = make_rsrc(xb + (ok ? (size_t)(c0 + row) * T : 0), ok ? T * 4 : 0);
+#pragma unroll
+            for (int ch = 0; ch < NCHC; ++ch) xv[rr][ch] = buf_load_f32(rrow, voffc[ch]);
+        }
+    };
+    if constexpr (Cfg::KC > 0) load_rows(0);
+
     for (int c0 = 0; c0 < C; c0 += CC) {
         __syncthreads();  // the previous chunk's LDS data is no longer read
-        // 1. input rows c0..c0+CC-1, steps t0-pad .. t0-pad+XW-1
-        for (int ch = 0; ch < nch; ++ch) {
-            const int u = ch * 64 + lane;
-            const int src = t0 - pad + u;
-            const int voff = (u < XW && src >= 0) ? src * 4 : kBufOOB;  // src >= T: past the row's end
-            for (int r0 = wave; r0 < CC; r0 += NW * UR) {
-                float v[UR];
+        if constexpr (Cfg::KC > 0) {
 #pragma unroll
-                for (int uu = 0; uu < UR; ++uu) {
-                    const int row = r0 + uu * NW;
-                    const bool ok = (row < CC) && (c0 + row < C);
-                    const buf_rsrc rrow = make_rsrc(xb + (ok ? (size_t)(c0 + row) * T : 0), ok ? T * 4 : 0);
-                    v[uu] = buf_load_f32(rrow, voff);
+            for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+                for (int ch = 0; ch < NCHC; ++ch) {
+                    const int u = ch * 64 + lane;
+                    if (u < XW) xs[(wave + rr * NW) * XW + u] = xv[rr][ch];
                 }
+            if (c0 + CC < C) load_rows(c0 + CC);
+        } else {
+            for (int ch = 0; ch < nch; ++ch) {
+                const int u = ch * 64 + lane;
+                const int src = t0 - pad + u;
+                const int voff = (u < XW && src >= 0) ? src * 4 : kBufOOB;
+                for (int r0 = wave; r0 < CC; r0 += NW * UR) {
+                    float v[UR];
 #pragma unroll
-                for (int uu = 0; uu < UR; ++uu) {
-                    const int row = r0 + uu * NW;
-                    if (row < CC && u < XW) xs[row * XW + u] = v[uu];
+                    for (int uu = 0; uu < UR; ++uu) {
+                        const int row = r0 + uu * NW;
+                        const bool ok = (row < CC) && (c0 + row < C);
+                        const buf_rsrc rrow = make_rsrc(xb + (ok ? (size_t)(c0 + row) * T : 0), ok ? T * 4 : 0);
+                        v[uu] = buf_load_f32(rrow, voff);
+                    }
+#pragma unroll
+                    for (int uu = 0; uu < UR; ++uu) {
+                        const int row = r0 + uu * NW;
+                        if (row < CC && u < XW) xs[row * XW + u] = v[uu];
+                    }
                 }
             }
         }
