@@ -124,6 +124,14 @@ def conv2d_flops(cfg):
     return 2 * cfg["B"] * cfg["Cout"] * PH * PW * s * s * cfg["Cin"] * cfg["K"] ** 2
 
 
+def conv2d_boxsum_flops(cfg):
+    """Work of the box-sum form: Cin*K*K MACs per (co, pooled output)."""
+    Hc, Wc = cfg["H"] - cfg["K"] + 1, cfg["W"] - cfg["K"] + 1
+    s = cfg["pool"]
+    PH, PW = Hc // s, Wc // s
+    return 2 * cfg["B"] * cfg["Cout"] * PH * PW * cfg["Cin"] * cfg["K"] ** 2
+
+
 def conv2d_bytes(cfg):
     return 4 * (cfg["B"] * cfg["Cin"] * cfg["H"] * cfg["W"] + cfg["Cout"] * cfg["Cin"] * cfg["K"] ** 2
                 + cfg["Cout"] + cfg["B"])
@@ -233,7 +241,7 @@ def main():
         del src, dst
 
     def conv_call():
-        fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=out)
+        fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=out, algo=fc.ALGO_DIRECT_MFMA)
 
     def dw_call():
         fc.dwsep_conv1d(xd, wdw, wpw, bpw, dc["pad"], out=y)
@@ -259,6 +267,22 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
 
+    # The box-sum variant of the Conv2d call (pool before convolving), timed
+    # on its own after the step loop and measured against its own work: Cin*K*K
+    # MACs per (co, pooled output) and the same compulsory bytes (HBM-bound).
+    out_box = torch.empty_like(out)
+    ms_box = []
+    for _ in range(args.warmup):
+        fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=out_box, algo=fc.ALGO_BOXSUM)
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=out_box, algo=fc.ALGO_BOXSUM)
+        e1.record(stream)
+        ms_box.append((e0, e1))
+    torch.cuda.synchronize()
+    ms_box = np.array([e0.elapsed_time(e1) for e0, e1 in ms_box])
+
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
     ms_conv = np.array([e[0].elapsed_time(e[1]) for e in ev])
@@ -280,6 +304,17 @@ def main():
     k_conv["hbm_bytes_measured"] = measured_traffic("conv2d_pool_mfma_kernel")
     k_dw["hbm_bytes_measured"] = measured_traffic("dwsep_mfma_kernel")
     achieved = f_conv / (k_conv["ms_mean"] * 1e-3) / 1e12
+    f_box = conv2d_boxsum_flops(cc)
+    mb = float(ms_box.mean())
+    k_box = {"algorithm": "box-sum (FCONV_ALGO_BOXSUM)", "ms_mean": round(mb, 4),
+             "ms_median": round(float(np.median(ms_box)), 4),
+             "gflops_own": round(f_box / (mb * 1e-3) / 1e9, 1), "algorithmic_gflop_own": round(f_box / 1e9, 3),
+             "hbm_gbps_algorithmic": round(b_conv / (mb * 1e-3) / 1e9, 1),
+             "roofline": {"bound": "hbm", "achieved": round(b_conv / (mb * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                          "unit": "GB/s", "frac": round(b_conv / (mb * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+             "speedup_vs_direct": round(k_conv["ms_mean"] / mb, 2),
+             "matches_direct_within_tol": bool(
+                 ((out_box - out).abs() <= 1e-4 + 1e-4 * out.abs()).all().item())}
 
     result = {
         "metric": METRIC,
@@ -301,6 +336,7 @@ def main():
             "parallelism": "single GPU",
         },
         "kernels": {"fconv2d_pool_sigmoid_sum": k_conv, "dwsep_conv1d": k_dw},
+        "variants": {"fconv2d_pool_sigmoid_sum_boxsum": k_box},
         "roofline": {
             "kernel": "fconv2d_pool_sigmoid_sum (conv2d_pool_mfma_kernel) on " + CONV,
             "bound": "mfma",

@@ -25,6 +25,7 @@ FCONV_EHIP = -3
 ALGO_AUTO = 0
 ALGO_DIRECT_MFMA = 1
 ALGO_DIRECT_SIMPLE = 2
+ALGO_BOXSUM = 3
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

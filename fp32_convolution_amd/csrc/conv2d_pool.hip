@@ -334,6 +334,283 @@ hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float*
     return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------- box-sum variant
+
+// Pooling commutes with the convolution: the window sum of conv outputs is
+//     sum_{dy,dx<s} conv[ph*s+dy, pw*s+dx] - s^2*bias
+//   = sum_{ic,ky,kx} w[co,ic,ky,kx] * Sx[ic, ph*s+ky, pw*s+kx],
+//     Sx[ic,y,x] = sum_{dy,dx<s} x[ic, y+dy, x+dx],
+// (the linearity behind the trace's bias factoring, applied to the whole
+// sum), so after s x s box sums of the input each (co, pooled output) needs
+// Cin*K*K multiply-adds instead of s^2*Cin*K*K.  The result equals the
+// direct form up to rounding.
+//
+// Workgroup: one batch item, a TPH x TPW pooled tile, all WCO*16*CB output
+// channels of a range, every wave covering all positions (WPOS must be 1).
+//  1. Each wave loads all IH rows of a channel's tile into registers (many
+//     loads in flight: the kernel is HBM-bound), adds s consecutive rows in
+//     registers and writes those vertical sums V[ic][r][c] to LDS.
+//  2. Sx[ic][r][c] = sum_{dx<s} V[ic][r][c+dx] into a phase-split buffer
+//     (column c at phase c % s, slot c/s, as the direct kernel's tile).
+//  3. MFMA contraction over (ic, ky, kx) with the direct kernel's channel
+//     grouping of the 4 k-slots.  Same epilogue.
+// Blocks are numbered so that consecutive tiles land on the same XCD (blocks
+// are dealt to the 8 XCDs round-robin), where they share halo lines in L2.
+template <class Cfg>
+struct BoxLayout {
+    static constexpr int K = Cfg::K, S = Cfg::S;
+    static constexpr int RS = (Cfg::TPH - 1) * S + K;  // rows of Sx the tile needs
+    static constexpr int CS = (Cfg::TPW - 1) * S + K;  // columns of Sx the tile needs
+    static constexpr int VP = Cfg::IW;                  // V row pitch (floats)
+    static constexpr int QS = (CS + S - 1) / S;         // Sx slots per phase
+    static constexpr int RSS = S * QS;                  // Sx floats per row
+    static constexpr int VPLANE = RS * VP;
+    static constexpr int SPLANE = RS * RSS;
+    static_assert(Cfg::WPOS == 1, "box-sum waves split output channels only");
+};
+
+__device__ __forceinline__ int xcd_spread(int bid, int n) {
+    // Inverse of the round-robin deal of block ids to 8 XCDs: XCD k's blocks
+    // (bid % 8 == k) get the k-th contiguous share of the logical ids.
+    const int per = n / 8, rem = n % 8;
+    const int xcd = bid % 8, idx = bid / 8;
+    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+template <class Cfg, bool MAP>
+__global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int tiles_w,
+    int tiles_per_item, int co_ranges, int nblocks) {
+    using L = BoxLayout<Cfg>;
+    constexpr int K = Cfg::K, S = Cfg::S, CB = Cfg::CB, P = Cfg::P, NW = Cfg::NW;
+    constexpr int TPH = Cfg::TPH, TPW = Cfg::TPW, IH = Cfg::IH, IW = Cfg::IW;
+    constexpr int RS = L::RS, CS = L::CS, VP = L::VP, QS = L::QS, RSS = L::RSS;
+    constexpr int NT = Cfg::NT;
+
+    extern __shared__ float lds[];
+    __shared__ float red[NW];
+    const int CinP = 4 * CINQ;
+    float* Vb = lds;                      // [CinP][RS][VP]
+    float* Sb = lds + CinP * L::VPLANE;   // [CinP][RS][RSS] phase-split
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lid = xcd_spread(blockIdx.x, nblocks);
+    const int tile = lid % tiles_per_item;
+    const int cr = (lid / tiles_per_item) % co_ranges;
+    const int b = lid / (tiles_per_item * co_ranges);
+    const int tile_y = tile / tiles_w, tile_x = tile - (tile / tiles_w) * tiles_w;
+    const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
+    const int g = lane >> 4, l16 = lane & 15;
+    const int co0 = cr * Cfg::CO_RANGE + wave * 16 * CB;
+
+    const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
+    auto load_a = [&](float (&a)[K * K][CB], int q) {
+        const int ic = g * CINQ + q;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int co = co0 + cb * 16 + l16;
+            const bool ok = (co < Cout) && (ic < Cin) && (q < CINQ);
+            const int base = ok ? (co * Cin + ic) * (K * K * 4) : kBufOOB;
+#pragma unroll
+            for (int kk = 0; kk < K * K; ++kk) a[kk][cb] = buf_load_f32(rw, base + kk * 4);
+        }
+    };
+    float a_cur[K * K][CB], a_nxt[K * K][CB];
+    load_a(a_cur, 0);
+    const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
+    float bco[CB][4];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int co = co0 + cb * 16 + 4 * g + r;
+            bco[cb][r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
+        }
+
+    // 1. vertical sums of s rows, per channel, from registers
+    {
+        constexpr int NCH = (IW + 63) / 64;
+        int voff[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int c = lane + 64 * k;
+            voff[k] = (c < IW && x0 + c < W) ? (x0 + c) * 4 : kBufOOB;
+        }
+        const float* xb = x + (size_t)b * Cin * H * W;
+        for (int ic = wave; ic < CinP; ic += NW) {
+            float v[IH][NCH];
+#pragma unroll
+            for (int r = 0; r < IH; ++r) {
+                const bool ok = (ic < Cin) && (y0 + r < H);
+                const buf_rsrc rrow = make_rsrc(xb + (ok ? (ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) v[r][k] = buf_load_f32(rrow, voff[k]);
+            }
+            float* vplane = Vb + ic * L::VPLANE;
+#pragma unroll
+            for (int r = 0; r < RS; ++r)
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) {
+                    const int c = lane + 64 * k;
+                    float sum = v[r][k];
+#pragma unroll
+                    for (int dy = 1; dy < S; ++dy) sum += v[r + dy][k];
+                    if (c < IW) vplane[r * VP + c] = sum;
+                }
+        }
+    }
+    __syncthreads();
+    // 2. horizontal sums of s columns into the phase-split Sx buffer
+    {
+        const int n = CinP * RS * CS;
+        for (int i = tid; i < n; i += NT) {
+            const int ic = i / (RS * CS);
+            const int rem = i - ic * (RS * CS);
+            const int r = rem / CS, c = rem - (rem / CS) * CS;
+            const float* vr = Vb + ic * L::VPLANE + r * VP + c;
+            float sum = vr[0];
+#pragma unroll
+            for (int dx = 1; dx < S; ++dx) sum += vr[dx];
+            Sb[ic * L::SPLANE + r * RSS + (c % S) * QS + c / S] = sum;
+        }
+    }
+    __syncthreads();
+
+    // 3. contraction: B for lane (g, l16), block p, tap (ky, kx) is
+    //    Sx[g*CINQ + q][py*S + ky][px*S + kx] for position j = p*16 + l16.
+    int pbase[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int j = p * 16 + l16;
+        const int py = j / TPW, px = j - (j / TPW) * TPW;
+        pbase[p] = g * CINQ * L::SPLANE + py * S * RSS + px;
+    }
+    floatx4 acc[CB][P];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int p = 0; p < P; ++p) acc[cb][p] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < CINQ; ++q) {
+        const int lq = q * L::SPLANE;
+        load_a(a_nxt, q + 1);
+#pragma unroll
+        for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+            for (int kx = 0; kx < K; ++kx) {
+                float bv[P];
+#pragma unroll
+                for (int p = 0; p < P; ++p) bv[p] = Sb[pbase[p] + lq + ky * RSS + (kx % S) * QS + kx / S];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int p = 0; p < P; ++p) acc[cb][p] = mfma_16x16x4(a_cur[ky * K + kx][cb], bv[p], acc[cb][p]);
+            }
+#pragma unroll
+        for (int kk = 0; kk < K * K; ++kk)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) a_cur[kk][cb] = a_nxt[kk][cb];
+    }
+
+    // Epilogue (as the direct kernel): window sum / s^2 + bias.
+    const float inv = 1.0f / (float)(S * S);
+    const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
+    float lsum = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int co = co0 + cb * 16 + 4 * g + r;
+            const bool cok = co < Cout;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int j = p * 16 + l16;
+                const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
+                if (cok && ph < PH && pw < PW) {
+                    const float avg = acc[cb][p][r] * inv + bco[cb][r];
+                    if constexpr (MAP)
+                        dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
+                    else
+                        lsum += logistic(avg);
+                }
+            }
+        }
+    if constexpr (!MAP) {
+        const float s = block_sum<NW>(lsum, red);
+        if (tid == 0) atomicAdd(dst + b, s);
+    }
+}
+
+// Instances: K3/s4 4x16 tile with 4 waves x 16 channels; K5/s3 4x12 tile
+// with 8 waves x 16 channels.
+#ifndef FCONV_CFG_BOX_K3S4
+#define FCONV_CFG_BOX_K3S4 3, 4, 1, 4, 4, 1, 4, 16
+#endif
+#ifndef FCONV_CFG_BOX_K5S3
+#define FCONV_CFG_BOX_K5S3 5, 3, 1, 3, 8, 1, 4, 12
+#endif
+using BoxK3S4 = DirectCfg<FCONV_CFG_BOX_K3S4>;
+using BoxK5S3 = DirectCfg<FCONV_CFG_BOX_K5S3>;
+using BoxK3S2 = DirectCfg<3, 2, 1, 4, 4, 1, 4, 16>;
+using BoxK3S3 = DirectCfg<3, 3, 1, 4, 4, 1, 4, 16>;
+
+template <class Cfg>
+static size_t box_lds_bytes(int Cin) {
+    using L = BoxLayout<Cfg>;
+    const int CinP = 4 * ((Cin + 3) / 4);
+    return (size_t)CinP * (L::VPLANE + L::SPLANE) * sizeof(float);
+}
+
+bool conv2d_boxsum_supported(int Cin, int K, int S) {
+    size_t bytes = 0;
+    if (K == 3 && S == 4) bytes = box_lds_bytes<BoxK3S4>(Cin);
+    else if (K == 5 && S == 3) bytes = box_lds_bytes<BoxK5S3>(Cin);
+    else if (K == 3 && S == 2) bytes = box_lds_bytes<BoxK3S2>(Cin);
+    else if (K == 3 && S == 3) bytes = box_lds_bytes<BoxK3S3>(Cin);
+    else return false;
+    return bytes <= kMaxLds;
+}
+
+template <class Cfg>
+static hipError_t launch_box(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                             bool map, hipStream_t stream) {
+    const int CINQ = (s.Cin + 3) / 4;
+    const size_t lds = box_lds_bytes<Cfg>(s.Cin);
+    const int tiles_h = (s.PH + Cfg::TPH - 1) / Cfg::TPH;
+    const int tiles_w = (s.PW + Cfg::TPW - 1) / Cfg::TPW;
+    const int tiles = tiles_h * tiles_w;
+    const int co_ranges = (s.Cout + Cfg::CO_RANGE - 1) / Cfg::CO_RANGE;
+    const long nblocks_l = (long)tiles * co_ranges * s.B;
+    if (nblocks_l > INT32_MAX) return hipErrorInvalidValue;
+    const int nblocks = (int)nblocks_l;
+    hipError_t e;
+    if (map) {
+        e = hipFuncSetAttribute((const void*)conv2d_pool_boxsum_kernel<Cfg, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((conv2d_pool_boxsum_kernel<Cfg, true>), dim3(nblocks), dim3(Cfg::NT), lds, stream, x, w,
+                           bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
+    } else {
+        e = hipFuncSetAttribute((const void*)conv2d_pool_boxsum_kernel<Cfg, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((conv2d_pool_boxsum_kernel<Cfg, false>), dim3(nblocks), dim3(Cfg::NT), lds, stream, x, w,
+                           bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
+    }
+    return hipGetLastError();
+}
+
+hipError_t conv2d_boxsum_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
+                                float* dst, bool map, hipStream_t stream) {
+    if (s.K == 3 && s.S == 4) return launch_box<BoxK3S4>(s, x, w, bias, dst, map, stream);
+    if (s.K == 5 && s.S == 3) return launch_box<BoxK5S3>(s, x, w, bias, dst, map, stream);
+    if (s.K == 3 && s.S == 2) return launch_box<BoxK3S2>(s, x, w, bias, dst, map, stream);
+    if (s.K == 3 && s.S == 3) return launch_box<BoxK3S3>(s, x, w, bias, dst, map, stream);
+    return hipErrorInvalidValue;
+}
+
 // ---------------------------------------------------------------- simple direct conv (any K, s)
 
 // One thread per (co, ph, pw) of one batch item: the window's s*s conv

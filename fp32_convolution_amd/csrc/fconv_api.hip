@@ -60,12 +60,18 @@ int check_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, c
     return FCONV_OK;
 }
 
+int auto_conv2d_algo(int Cin, int K, int S) {
+    if (fconv::conv2d_boxsum_supported(Cin, K, S)) return FCONV_ALGO_BOXSUM;
+    if (fconv::conv2d_mfma_supported(Cin, K, S, nullptr)) return FCONV_ALGO_DIRECT_MFMA;
+    return FCONV_ALGO_DIRECT_SIMPLE;
+}
+
 int pick_conv2d_algo(const Conv2dShape& s, int algo) {
-    if (algo == FCONV_ALGO_AUTO)
-        return fconv::conv2d_mfma_supported(s.Cin, s.K, s.S, nullptr) ? FCONV_ALGO_DIRECT_MFMA
-                                                                       : FCONV_ALGO_DIRECT_SIMPLE;
+    if (algo == FCONV_ALGO_AUTO) return auto_conv2d_algo(s.Cin, s.K, s.S);
     if (algo == FCONV_ALGO_DIRECT_MFMA)
         return fconv::conv2d_mfma_supported(s.Cin, s.K, s.S, nullptr) ? algo : FCONV_EUNSUPPORTED;
+    if (algo == FCONV_ALGO_BOXSUM)
+        return fconv::conv2d_boxsum_supported(s.Cin, s.K, s.S) ? algo : FCONV_EUNSUPPORTED;
     if (algo == FCONV_ALGO_DIRECT_SIMPLE) return algo;
     return FCONV_EINVAL;
 }
@@ -90,7 +96,8 @@ int run_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, con
         if (e != hipSuccess) return FCONV_EHIP;
     }
     hipError_t e = (a == FCONV_ALGO_DIRECT_MFMA) ? fconv::conv2d_mfma_launch(s, x, w, bias, dst, map, st)
-                                                 : fconv::conv2d_simple_launch(s, x, w, bias, dst, map, st);
+                   : (a == FCONV_ALGO_BOXSUM)     ? fconv::conv2d_boxsum_launch(s, x, w, bias, dst, map, st)
+                                                  : fconv::conv2d_simple_launch(s, x, w, bias, dst, map, st);
     return status_of(e);
 }
 
@@ -124,8 +131,7 @@ int fconv2d_pool_out_size(int64_t H, int64_t W, int64_t K, int64_t pool, int64_t
 int fconv2d_select_algo(int64_t Cin, int64_t Cout, int64_t K, int64_t pool) {
     if (Cin < 1 || Cout < 1 || K < 1 || pool < 1 || Cin > INT32_MAX || K > 4096 || pool > 4096)
         return FCONV_EINVAL;
-    return fconv::conv2d_mfma_supported((int)Cin, (int)K, (int)pool, nullptr) ? FCONV_ALGO_DIRECT_MFMA
-                                                                              : FCONV_ALGO_DIRECT_SIMPLE;
+    return auto_conv2d_algo((int)Cin, (int)K, (int)pool);
 }
 
 int64_t dwsep_conv1d_out_len(int64_t T, int64_t K, int64_t pad) {

@@ -23,6 +23,10 @@ bool conv2d_mfma_supported(int Cin, int K, int S, size_t* lds_bytes);
 // pooled-map output (pooled[B,Cout,PH,PW]) instead of the fused sum (out[B]).
 hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
                               float* dst, bool map, hipStream_t stream);
+// Box-sum variant: true if it has an instance for (K, S) and its LDS fits.
+bool conv2d_boxsum_supported(int Cin, int K, int S);
+hipError_t conv2d_boxsum_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
+                                float* dst, bool map, hipStream_t stream);
 hipError_t conv2d_simple_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
                                 float* dst, bool map, hipStream_t stream);
 hipError_t fill_zero(float* p, int64_t n, hipStream_t stream);

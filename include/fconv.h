@@ -54,11 +54,19 @@ extern "C" {
 #define FCONV_EUNSUPPORTED (-2) /* the requested algorithm cannot run this shape   */
 #define FCONV_EHIP (-3)        /* the HIP runtime reported an error              */
 
-/* Algorithms for the Conv2d path.  AUTO picks the fastest one that supports
- * the shape. */
+/* Algorithms for the Conv2d path.  All compute the same result up to fp32
+ * rounding.  AUTO picks the fastest one that supports the shape: BOXSUM,
+ * else DIRECT_MFMA, else DIRECT_SIMPLE. */
 #define FCONV_ALGO_AUTO 0
-#define FCONV_ALGO_DIRECT_MFMA 1   /* direct conv on fp32 matrix cores (templated K, pool) */
+#define FCONV_ALGO_DIRECT_MFMA 1   /* direct conv on fp32 matrix cores: s*s*Cin*K*K MACs per
+                                      (co, pooled output); instances for K=3 with pool 2,3,4
+                                      and K=5 with pool 3 */
 #define FCONV_ALGO_DIRECT_SIMPLE 2 /* direct conv, one thread per pooled output, any shape */
+#define FCONV_ALGO_BOXSUM 3        /* pool-then-convolve: s x s box sums of the input, then
+                                      Cin*K*K MACs per (co, pooled output) on matrix cores;
+                                      same instances as DIRECT_MFMA.  Pooling commutes with the
+                                      convolution (both are linear), so the result is the
+                                      same function of the inputs. */
 
 /*
  * fconv2d_pool_sigmoid_sum

@@ -78,11 +78,12 @@ def test_dwsep_out_len(lib):
 
 
 def test_select_algo(lib):
-    assert lib.fconv2d_select_algo(8, 64, 3, 4) == 1   # direct MFMA instance
-    assert lib.fconv2d_select_algo(16, 128, 5, 3) == 1
-    assert lib.fconv2d_select_algo(3, 4, 3, 4) == 1
-    assert lib.fconv2d_select_algo(3, 4, 7, 2) == 2    # no MFMA instance for K=7 -> simple path
+    assert lib.fconv2d_select_algo(8, 64, 3, 4) == 3   # box-sum instance
+    assert lib.fconv2d_select_algo(16, 128, 5, 3) == 3
+    assert lib.fconv2d_select_algo(3, 4, 3, 4) == 3
+    assert lib.fconv2d_select_algo(3, 4, 7, 2) == 2    # no matrix-core instance for K=7 -> simple path
     assert lib.fconv2d_select_algo(512, 4, 3, 4) == 2  # LDS tile too large -> simple path
+    assert lib.fconv2d_select_algo(32, 4, 3, 4) == 1   # box-sum buffers too large, direct tile fits
     assert lib.fconv2d_select_algo(0, 4, 3, 4) == EINVAL
 
 
@@ -103,6 +104,7 @@ def test_conv2d_einval(lib, kw):
 
 def test_conv2d_unsupported(lib):
     assert conv(lib, K=7, algo=1) == EUNSUP            # no MFMA instance for K=7
+    assert conv(lib, K=7, algo=3) == EUNSUP            # nor a box-sum one
     assert conv(lib, Cin=2**16, H=2**8, W=2**8) == EUNSUP  # per-item elements beyond int32
     assert conv(lib, B=70000) == EUNSUP
 

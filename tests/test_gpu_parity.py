@@ -1,6 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Bar (spec tolerance for fp32): |gpu - oracle| <= 1e-4 + 1e-4*|oracle|
+Bar (the specified fp32 tolerance): |gpu - oracle| <= 1e-4 + 1e-4*|oracle|
 element by element, with the oracle in float64.  For the fused Conv2d sum the
 elementwise check runs on the pre-sigmoid pooled map, which the same kernels
 write; the scalar sums are checked as well.  Full-size workloads compare
@@ -58,8 +58,8 @@ def assert_close(got, want, what):
 SMALL_CONV = [
     # B, Cin, H, W, Cout, K, s
     (2, 3, 16, 16, 4, 3, 4),        # the tiny workload
-    (2, 8, 70, 75, 64, 3, 4),       # several 8x16 tiles, ragged in both directions
-    (1, 16, 60, 50, 128, 5, 3),     # K5/s3 instance: several 4x12 tiles, ragged
+    (2, 8, 70, 75, 64, 3, 4),       # several tiles, ragged in both directions
+    (1, 16, 60, 50, 128, 5, 3),     # K5/s3 instance: several tiles, ragged
     (2, 5, 41, 37, 20, 3, 4),       # odd Cin, Cout not a multiple of 16
     (1, 8, 40, 40, 70, 3, 4),       # Cout > 64: two channel ranges
     (1, 3, 37, 41, 7, 3, 2),        # K3/s2 instance
@@ -69,25 +69,34 @@ SMALL_CONV = [
 ]
 
 
+ALGOS = [0, 1, 2, 3]  # auto, direct MFMA, direct simple, box-sum
+
+
 @pytest.mark.parametrize("shape", SMALL_CONV)
-@pytest.mark.parametrize("algo", [0, 2])
+@pytest.mark.parametrize("algo", ALGOS)
 def test_conv2d_small(fc, shape, algo):
     B, Cin, H, W, Cout, K, s = shape
     announce(f"conv2d small {shape} algo={algo}")
     x, w, b = fi.conv2d_inputs(B, Cin, H, W, Cout, K, seed=1)
-    want_out, want_map = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, want_pooled=True)
     xd, wd, bd = dev(x), dev(w), dev(b)
+    if algo in (1, 3) and fc.conv2d_select_algo(Cin, Cout, K, s) == 2:
+        with pytest.raises(fc.FconvError) as err:
+            fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=algo)
+        assert err.value.status == fc.FCONV_EUNSUPPORTED
+        return
+    want_out, want_map = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, want_pooled=True)
     got_map = fc.conv2d_pool_map(xd, wd, bd, s, algo=algo).cpu().numpy()
     got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=algo).cpu().numpy()
     assert_close(got_map, want_map, f"pooled map {shape}")
     assert_close(got_out, want_out, f"out {shape}")
 
 
-def test_conv2d_no_bias(fc):
-    announce("conv2d no bias")
+@pytest.mark.parametrize("algo", [1, 3])
+def test_conv2d_no_bias(fc, algo):
+    announce(f"conv2d no bias algo={algo}")
     x, w, _ = fi.conv2d_inputs(2, 8, 40, 44, 64, 3, seed=2)
     want = oracle.conv2d_pool_sigmoid_sum(x, w, None, 4)
-    got = fc.conv2d_pool_sigmoid_sum(dev(x), dev(w), None, 4).cpu().numpy()
+    got = fc.conv2d_pool_sigmoid_sum(dev(x), dev(w), None, 4, algo=algo).cpu().numpy()
     assert_close(got, want, "out, bias=None")
 
 
@@ -121,15 +130,16 @@ def full_conv_inputs():
     return {name: fi.make(name, seed=0) for name in FULL_CONV}
 
 
+@pytest.mark.parametrize("algo", [1, 3])
 @pytest.mark.parametrize("name", list(FULL_CONV))
-def test_conv2d_full_size(fc, full_conv_inputs, name):
+def test_conv2d_full_size(fc, full_conv_inputs, name, algo):
     cfg = fi.WORKLOADS[name]
     s = cfg["pool"]
     x, w, b = full_conv_inputs[name]
-    announce(f"conv2d full size {name}")
+    announce(f"conv2d full size {name} algo={algo}")
     xd, wd, bd = dev(x), dev(w), dev(b)
-    got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s).cpu().numpy()
-    got_map = fc.conv2d_pool_map(xd, wd, bd, s).cpu().numpy()
+    got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=algo).cpu().numpy()
+    got_map = fc.conv2d_pool_map(xd, wd, bd, s, algo=algo).cpu().numpy()
     # whole batch items through the literal oracle
     idx = FULL_CONV[name]
     want_out = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, batch_idx=idx)
@@ -151,23 +161,24 @@ def test_conv2d_full_size(fc, full_conv_inputs, name):
     assert_close(got_map[tuple(samp.T)], want, f"{name} sampled pooled map")
 
 
+@pytest.mark.parametrize("algo", [1, 3])
 @pytest.mark.parametrize("name", list(FULL_CONV))
-def test_conv2d_full_size_closed_forms(fc, full_conv_inputs, name):
+def test_conv2d_full_size_closed_forms(fc, full_conv_inputs, name, algo):
     cfg = fi.WORKLOADS[name]
     s = cfg["pool"]
     x, w, b = full_conv_inputs[name]
-    announce(f"conv2d full size closed forms {name}")
+    announce(f"conv2d full size closed forms {name} algo={algo}")
     B, Cin, H, W = x.shape
     Cout = w.shape[0]
     PH, PW = fc.conv2d_out_size(H, W, w.shape[2], s)
     xd = dev(x)
     # zero weights and bias: sigmoid(0) = 1/2 everywhere, exactly representable sums
-    z = fc.conv2d_pool_sigmoid_sum(xd, torch.zeros_like(dev(w)), torch.zeros(Cout, device="cuda"), s)
+    z = fc.conv2d_pool_sigmoid_sum(xd, torch.zeros_like(dev(w)), torch.zeros(Cout, device="cuda"), s, algo=algo)
     assert (z.cpu().numpy() == Cout * PH * PW / 2.0).all()
     # sigma symmetry: negating w and b gives Cout*PH*PW - out
     wd, bd = dev(w), dev(b)
-    pos = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s).cpu().numpy().astype(np.float64)
-    neg = fc.conv2d_pool_sigmoid_sum(xd, -wd, -bd, s).cpu().numpy().astype(np.float64)
+    pos = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=algo).cpu().numpy().astype(np.float64)
+    neg = fc.conv2d_pool_sigmoid_sum(xd, -wd, -bd, s, algo=algo).cpu().numpy().astype(np.float64)
     assert_close(pos + neg, np.full(B, float(Cout * PH * PW)), f"{name} sigma symmetry")
 
 
