@@ -42,6 +42,11 @@ _SIGS = {
         [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
     "fconv2d_pool_map": (
         [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
+    "fconv2d_pool_sigmoid_sum_det": (
+        [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, ctypes.c_size_t, _vp, _vp],
+        ctypes.c_int),
+    "fconv2d_pool_sigmoid_sum_det_workspace": (
+        [_i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "fconv2d_pool_out_size": ([_i64, _i64, _i64, _i64, _i64p, _i64p], ctypes.c_int),
     "fconv2d_select_algo": ([_i64, _i64, _i64, _i64], ctypes.c_int),
     "dwsep_conv1d": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp], ctypes.c_int),
@@ -127,6 +132,40 @@ def conv2d_pool_sigmoid_sum(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO)
     rc = lib.fconv2d_pool_sigmoid_sum_algo(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
                                            _ptr(out), _stream(x))
     _check(rc, "fconv2d_pool_sigmoid_sum")
+    return out
+
+
+def conv2d_det_workspace_bytes(B, Cin, H, W, Cout, K, pool, algo: int = ALGO_AUTO) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.fconv2d_pool_sigmoid_sum_det_workspace(B, Cin, H, W, Cout, K, pool, algo, ctypes.byref(n)),
+           "fconv2d_pool_sigmoid_sum_det_workspace")
+    return n.value
+
+
+def conv2d_pool_sigmoid_sum_det(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO, workspace=None):
+    """Bitwise-reproducible form of conv2d_pool_sigmoid_sum (partials + fixed-order reduction).
+
+    workspace: a device tensor of at least conv2d_det_workspace_bytes() bytes,
+    or None to allocate one here.
+    """
+    _conv2d_args(x, w, b)
+    B, Cin, H, W = x.shape
+    Cout, _, K, _ = w.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.float32, device=x.device)
+    else:
+        _dev_f32(out, "out")
+        if tuple(out.shape) != (B,) or out.device != x.device:
+            raise ValueError("out must be [B] on x's device")
+    need = conv2d_det_workspace_bytes(B, Cin, H, W, Cout, K, pool, algo)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=x.device)
+    if workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on x's device")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib.fconv2d_pool_sigmoid_sum_det(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
+                                          _ptr(workspace), nbytes, _ptr(out), _stream(x))
+    _check(rc, "fconv2d_pool_sigmoid_sum_det")
     return out
 
 

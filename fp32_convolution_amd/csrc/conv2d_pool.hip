@@ -55,14 +55,14 @@ struct DirectCfg {
     static_assert(TPH * TPW == 16 * P * WPOS, "tile must hold the waves' position blocks");
 };
 
-template <class Cfg, bool MAP>
+template <class Cfg, int MODE>
 __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane,
     int tiles_w) {
     constexpr int K = Cfg::K, S = Cfg::S, CB = Cfg::CB, P = Cfg::P, WCO = Cfg::WCO;
     constexpr int TPH = Cfg::TPH, TPW = Cfg::TPW, IH = Cfg::IH, IW = Cfg::IW;
-    constexpr int QP = Cfg::QP, RP = Cfg::RP, NBV = Cfg::NBV, NT = Cfg::NT;
+    constexpr int QP = Cfg::QP, RP = Cfg::RP, NBV = Cfg::NBV;
     constexpr int NR = S + K - 1;  // input rows a pooled row's windows touch
 
     extern __shared__ float lds[];
@@ -81,7 +81,6 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
     const int l16 = lane & 15; // row of A / column of B
     const int co0 = blockIdx.y * Cfg::CO_RANGE + wco * 16 * CB;
 
-    const buf_rsrc rx = make_rsrc(x + (size_t)b * Cin * H * W, Cin * H * W * 4);
     const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
 
     // Weights of channel quad q for this lane: a[ky][cb][kx] =
@@ -239,16 +238,21 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
                 const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
                 if (cok && ph < PH && pw < PW) {
                     const float avg = acc[cb][p][r] * inv + bco[cb][r];
-                    if constexpr (MAP)
+                    if constexpr (MODE == OUT_MAP)
                         dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
                     else
                         lsum += logistic(avg);
                 }
             }
         }
-    if constexpr (!MAP) {
+    if constexpr (MODE != OUT_MAP) {
         const float s = block_sum<Cfg::NW>(lsum, red);
-        if (tid == 0) atomicAdd(dst + b, s);
+        if (tid == 0) {
+            if constexpr (MODE == OUT_SUM_ATOMIC)
+                atomicAdd(dst + b, s);
+            else
+                dst[(size_t)b * (gridDim.x * gridDim.y) + blockIdx.y * gridDim.x + blockIdx.x] = s;
+        }
     }
 }
 
@@ -297,41 +301,69 @@ bool conv2d_mfma_supported(int Cin, int K, int S, size_t* lds_bytes) {
     return bytes <= kMaxLds;
 }
 
+// Instantiates a kernel template for the three output modes and launches
+// the one `mode` asks for, raising the dynamic LDS limit first.
+#define FCONV_LAUNCH_MODES(KERNEL, GRID, BLOCK, LDS, STREAM, ...)                                            \
+    do {                                                                                                 \
+        const void* fn = mode == OUT_MAP       ? (const void*)KERNEL<OUT_MAP>                            \
+                         : mode == OUT_PARTIAL ? (const void*)KERNEL<OUT_PARTIAL>                        \
+                                               : (const void*)KERNEL<OUT_SUM_ATOMIC>;                    \
+        if ((LDS) > 0) {                                                                                 \
+            hipError_t ea = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(LDS)); \
+            if (ea != hipSuccess) return ea;                                                             \
+        }                                                                                                \
+        if (mode == OUT_MAP)                                                                             \
+            hipLaunchKernelGGL((KERNEL<OUT_MAP>), GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                \
+        else if (mode == OUT_PARTIAL)                                                                    \
+            hipLaunchKernelGGL((KERNEL<OUT_PARTIAL>), GRID, BLOCK, LDS, STREAM, __VA_ARGS__);            \
+        else                                                                                             \
+            hipLaunchKernelGGL((KERNEL<OUT_SUM_ATOMIC>), GRID, BLOCK, LDS, STREAM, __VA_ARGS__);         \
+        return hipGetLastError();                                                                        \
+    } while (0)
+
 template <class Cfg>
-static hipError_t launch_direct(const Conv2dShape& s, const float* x, const float* w, const float* bias,
-                                float* dst, bool map, hipStream_t stream) {
-    const int CINQ = (s.Cin + 3) / 4;
-    const int plane = plane_floats<Cfg>(CINQ);
-    const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
+struct DirectLaunch {
+    template <int MODE>
+    static constexpr auto kernel = conv2d_pool_mfma_kernel<Cfg, MODE>;
+};
+
+template <class Cfg>
+static dim3 direct_grid(const Conv2dShape& s) {
     const int tiles_h = (s.PH + Cfg::TPH - 1) / Cfg::TPH;
     const int tiles_w = (s.PW + Cfg::TPW - 1) / Cfg::TPW;
     const int co_ranges = (s.Cout + Cfg::CO_RANGE - 1) / Cfg::CO_RANGE;
-    dim3 grid(tiles_h * tiles_w, co_ranges, s.B);
-    dim3 block(Cfg::NT);
-    hipError_t e;
-    if (map) {
-        e = hipFuncSetAttribute((const void*)conv2d_pool_mfma_kernel<Cfg, true>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((conv2d_pool_mfma_kernel<Cfg, true>), grid, block, lds, stream, x, w, bias, dst,
-                           s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, tiles_w);
-    } else {
-        e = hipFuncSetAttribute((const void*)conv2d_pool_mfma_kernel<Cfg, false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((conv2d_pool_mfma_kernel<Cfg, false>), grid, block, lds, stream, x, w, bias, dst,
-                           s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, tiles_w);
-    }
-    return hipGetLastError();
+    return dim3(tiles_h * tiles_w, co_ranges, s.B);
+}
+
+template <class Cfg>
+static hipError_t launch_direct(const Conv2dShape& s, const float* x, const float* w, const float* bias,
+                                float* dst, int mode, hipStream_t stream) {
+    const int CINQ = (s.Cin + 3) / 4;
+    const int plane = plane_floats<Cfg>(CINQ);
+    const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
+    const int tiles_w = (s.PW + Cfg::TPW - 1) / Cfg::TPW;
+    const dim3 grid = direct_grid<Cfg>(s);
+    FCONV_LAUNCH_MODES(DirectLaunch<Cfg>::template kernel, grid, dim3(Cfg::NT), lds, stream, x, w, bias, dst, s.Cin,
+                       s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, tiles_w);
 }
 
 hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
-                              float* dst, bool map, hipStream_t stream) {
-    if (s.K == 3 && s.S == 4) return launch_direct<CfgK3S4>(s, x, w, bias, dst, map, stream);
-    if (s.K == 5 && s.S == 3) return launch_direct<CfgK5S3>(s, x, w, bias, dst, map, stream);
-    if (s.K == 3 && s.S == 2) return launch_direct<CfgK3S2>(s, x, w, bias, dst, map, stream);
-    if (s.K == 3 && s.S == 3) return launch_direct<CfgK3S3>(s, x, w, bias, dst, map, stream);
+                              float* dst, int mode, hipStream_t stream) {
+    if (s.K == 3 && s.S == 4) return launch_direct<CfgK3S4>(s, x, w, bias, dst, mode, stream);
+    if (s.K == 5 && s.S == 3) return launch_direct<CfgK5S3>(s, x, w, bias, dst, mode, stream);
+    if (s.K == 3 && s.S == 2) return launch_direct<CfgK3S2>(s, x, w, bias, dst, mode, stream);
+    if (s.K == 3 && s.S == 3) return launch_direct<CfgK3S3>(s, x, w, bias, dst, mode, stream);
     return hipErrorInvalidValue;
+}
+
+int64_t conv2d_mfma_parts(const Conv2dShape& s) {
+    dim3 g;
+    if (s.K == 3 && s.S == 4) g = direct_grid<CfgK3S4>(s);
+    else if (s.K == 5 && s.S == 3) g = direct_grid<CfgK5S3>(s);
+    else if (s.K == 3 && s.S == 2) g = direct_grid<CfgK3S2>(s);
+    else if (s.K == 3 && s.S == 3) g = direct_grid<CfgK3S3>(s);
+    else return -1;
+    return (int64_t)g.x * g.y;
 }
 
 // ---------------------------------------------------------------- box-sum variant
@@ -361,11 +393,12 @@ struct BoxLayout {
     static constexpr int K = Cfg::K, S = Cfg::S;
     static constexpr int RS = (Cfg::TPH - 1) * S + K;  // rows of Sx the tile needs
     static constexpr int CS = (Cfg::TPW - 1) * S + K;  // columns of Sx the tile needs
-    static constexpr int VP = Cfg::IW;                  // V row pitch (floats)
+    static constexpr int NCH = (Cfg::IW + 63) / 64;     // 64-column chunks of an input row
+    static constexpr int NCS = (CS + 63) / 64;          // 64-column chunks of an Sx row
     static constexpr int QS = (CS + S - 1) / S;         // Sx slots per phase
     static constexpr int RSS = S * QS;                  // Sx floats per row
-    static constexpr int VPLANE = RS * VP;
     static constexpr int SPLANE = RS * RSS;
+    static constexpr int SCRATCH = NCH * 64;            // one vertical-sum row per wave
     static_assert(Cfg::WPOS == 1, "box-sum waves split output channels only");
 };
 
@@ -377,7 +410,7 @@ __device__ __forceinline__ int xcd_spread(int bid, int n) {
     return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
-template <class Cfg, bool MAP>
+template <class Cfg, int MODE>
 __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int tiles_w,
@@ -385,14 +418,13 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
     using L = BoxLayout<Cfg>;
     constexpr int K = Cfg::K, S = Cfg::S, CB = Cfg::CB, P = Cfg::P, NW = Cfg::NW;
     constexpr int TPH = Cfg::TPH, TPW = Cfg::TPW, IH = Cfg::IH, IW = Cfg::IW;
-    constexpr int RS = L::RS, CS = L::CS, VP = L::VP, QS = L::QS, RSS = L::RSS;
-    constexpr int NT = Cfg::NT;
+    constexpr int RS = L::RS, CS = L::CS, QS = L::QS, RSS = L::RSS;
 
     extern __shared__ float lds[];
     __shared__ float red[NW];
     const int CinP = 4 * CINQ;
-    float* Vb = lds;                      // [CinP][RS][VP]
-    float* Sb = lds + CinP * L::VPLANE;   // [CinP][RS][RSS] phase-split
+    float* Sb = lds;                                        // [CinP][RS][RSS] phase-split
+    float* scratch = lds + CinP * L::SPLANE;                // [NW][SCRATCH]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -430,51 +462,79 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
             bco[cb][r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
         }
 
-    // 1. vertical sums of s rows, per channel, from registers
+    // 1-2. Box sums, one channel per wave at a time.  All IH rows of the
+    //      channel's tile are loaded into registers (the next channel's rows
+    //      load while this one is summed); s rows are added in registers;
+    //      each vertical-sum row goes through the wave's own LDS scratch row
+    //      and comes back shifted by 0..s-1 columns for the horizontal sum.
+    //      LDS operations of one wave complete in order, so the scratch row
+    //      needs no workgroup barrier, only compiler fences.
     {
-        constexpr int NCH = (IW + 63) / 64;
+        constexpr int NCH = L::NCH, NCS = L::NCS;
         int voff[NCH];
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             const int c = lane + 64 * k;
             voff[k] = (c < IW && x0 + c < W) ? (x0 + c) * 4 : kBufOOB;
         }
+        int soff[NCS];
+#pragma unroll
+        for (int k = 0; k < NCS; ++k) {
+            const int c = lane + 64 * k;
+            soff[k] = c < CS ? (c % S) * QS + c / S : -1;
+        }
         const float* xb = x + (size_t)b * Cin * H * W;
-        for (int ic = wave; ic < CinP; ic += NW) {
-            float v[IH][NCH];
+        float* srow = scratch + wave * L::SCRATCH;
+        auto load_rows = [&](float (&vv)[IH][NCH], int ic) {
 #pragma unroll
             for (int r = 0; r < IH; ++r) {
                 const bool ok = (ic < Cin) && (y0 + r < H);
                 const buf_rsrc rrow = make_rsrc(xb + (ok ? (ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
 #pragma unroll
-                for (int k = 0; k < NCH; ++k) v[r][k] = buf_load_f32(rrow, voff[k]);
+                for (int k = 0; k < NCH; ++k) vv[r][k] = buf_load_f32(rrow, voff[k]);
             }
-            float* vplane = Vb + ic * L::VPLANE;
+        };
+        auto sum_rows = [&](float (&vv)[IH][NCH], int ic) {
+            float* splane = Sb + ic * L::SPLANE;
 #pragma unroll
-            for (int r = 0; r < RS; ++r)
+            for (int r = 0; r < RS; ++r) {
+                // The fences keep the compiler from moving this row's reads
+                // above its writes (or the next row's writes above these
+                // reads): other lanes' values are exchanged through srow.
+                __builtin_amdgcn_wave_barrier();
 #pragma unroll
                 for (int k = 0; k < NCH; ++k) {
-                    const int c = lane + 64 * k;
-                    float sum = v[r][k];
+                    float sum = vv[r][k];
 #pragma unroll
-                    for (int dy = 1; dy < S; ++dy) sum += v[r + dy][k];
-                    if (c < IW) vplane[r * VP + c] = sum;
+                    for (int dy = 1; dy < S; ++dy) sum += vv[r + dy][k];
+                    srow[lane + 64 * k] = sum;
                 }
-        }
-    }
-    __syncthreads();
-    // 2. horizontal sums of s columns into the phase-split Sx buffer
-    {
-        const int n = CinP * RS * CS;
-        for (int i = tid; i < n; i += NT) {
-            const int ic = i / (RS * CS);
-            const int rem = i - ic * (RS * CS);
-            const int r = rem / CS, c = rem - (rem / CS) * CS;
-            const float* vr = Vb + ic * L::VPLANE + r * VP + c;
-            float sum = vr[0];
+                __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int dx = 1; dx < S; ++dx) sum += vr[dx];
-            Sb[ic * L::SPLANE + r * RSS + (c % S) * QS + c / S] = sum;
+                for (int k = 0; k < NCS; ++k) {
+                    const int c = lane + 64 * k;
+                    if (c < CS) {
+                        float sum = srow[c];
+#pragma unroll
+                        for (int dx = 1; dx < S; ++dx) sum += srow[c + dx];
+                        splane[r * RSS + soff[k]] = sum;
+                    }
+                }
+            }
+        };
+        // Channels wave, wave+NW, ...; two register buffers alternate (the
+        // loop is unrolled by two so that neither is indexed at run time).
+        const int nmine = (CinP - wave + NW - 1) / NW;
+        float va[IH][NCH], vb[IH][NCH];
+        if (nmine > 0) load_rows(va, wave);
+        for (int m = 0; m < nmine; m += 2) {
+            const int ic = wave + m * NW;
+            if (m + 1 < nmine) load_rows(vb, ic + NW);
+            sum_rows(va, ic);
+            if (m + 1 < nmine) {
+                if (m + 2 < nmine) load_rows(va, ic + 2 * NW);
+                sum_rows(vb, ic + NW);
+            }
         }
     }
     __syncthreads();
@@ -530,16 +590,21 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
                 const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
                 if (cok && ph < PH && pw < PW) {
                     const float avg = acc[cb][p][r] * inv + bco[cb][r];
-                    if constexpr (MAP)
+                    if constexpr (MODE == OUT_MAP)
                         dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
                     else
                         lsum += logistic(avg);
                 }
             }
         }
-    if constexpr (!MAP) {
+    if constexpr (MODE != OUT_MAP) {
         const float s = block_sum<NW>(lsum, red);
-        if (tid == 0) atomicAdd(dst + b, s);
+        if (tid == 0) {
+            if constexpr (MODE == OUT_SUM_ATOMIC)
+                atomicAdd(dst + b, s);
+            else
+                dst[(size_t)b * (tiles_per_item * co_ranges) + cr * tiles_per_item + tile] = s;
+        }
     }
 }
 
@@ -560,7 +625,7 @@ template <class Cfg>
 static size_t box_lds_bytes(int Cin) {
     using L = BoxLayout<Cfg>;
     const int CinP = 4 * ((Cin + 3) / 4);
-    return (size_t)CinP * (L::VPLANE + L::SPLANE) * sizeof(float);
+    return ((size_t)CinP * L::SPLANE + (size_t)Cfg::NW * L::SCRATCH) * sizeof(float);
 }
 
 bool conv2d_boxsum_supported(int Cin, int K, int S) {
@@ -574,48 +639,55 @@ bool conv2d_boxsum_supported(int Cin, int K, int S) {
 }
 
 template <class Cfg>
+struct BoxLaunch {
+    template <int MODE>
+    static constexpr auto kernel = conv2d_pool_boxsum_kernel<Cfg, MODE>;
+};
+
+template <class Cfg>
+static int64_t box_parts(const Conv2dShape& s) {
+    const int tiles = ((s.PH + Cfg::TPH - 1) / Cfg::TPH) * ((s.PW + Cfg::TPW - 1) / Cfg::TPW);
+    const int co_ranges = (s.Cout + Cfg::CO_RANGE - 1) / Cfg::CO_RANGE;
+    return (int64_t)tiles * co_ranges;
+}
+
+template <class Cfg>
 static hipError_t launch_box(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
-                             bool map, hipStream_t stream) {
+                             int mode, hipStream_t stream) {
     const int CINQ = (s.Cin + 3) / 4;
     const size_t lds = box_lds_bytes<Cfg>(s.Cin);
-    const int tiles_h = (s.PH + Cfg::TPH - 1) / Cfg::TPH;
     const int tiles_w = (s.PW + Cfg::TPW - 1) / Cfg::TPW;
-    const int tiles = tiles_h * tiles_w;
+    const int tiles = ((s.PH + Cfg::TPH - 1) / Cfg::TPH) * tiles_w;
     const int co_ranges = (s.Cout + Cfg::CO_RANGE - 1) / Cfg::CO_RANGE;
     const long nblocks_l = (long)tiles * co_ranges * s.B;
     if (nblocks_l > INT32_MAX) return hipErrorInvalidValue;
     const int nblocks = (int)nblocks_l;
-    hipError_t e;
-    if (map) {
-        e = hipFuncSetAttribute((const void*)conv2d_pool_boxsum_kernel<Cfg, true>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((conv2d_pool_boxsum_kernel<Cfg, true>), dim3(nblocks), dim3(Cfg::NT), lds, stream, x, w,
-                           bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
-    } else {
-        e = hipFuncSetAttribute((const void*)conv2d_pool_boxsum_kernel<Cfg, false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((conv2d_pool_boxsum_kernel<Cfg, false>), dim3(nblocks), dim3(Cfg::NT), lds, stream, x, w,
-                           bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
-    }
-    return hipGetLastError();
+    FCONV_LAUNCH_MODES(BoxLaunch<Cfg>::template kernel, dim3(nblocks), dim3(Cfg::NT), lds, stream, x, w, bias, dst,
+                       s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
 }
 
 hipError_t conv2d_boxsum_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
-                                float* dst, bool map, hipStream_t stream) {
-    if (s.K == 3 && s.S == 4) return launch_box<BoxK3S4>(s, x, w, bias, dst, map, stream);
-    if (s.K == 5 && s.S == 3) return launch_box<BoxK5S3>(s, x, w, bias, dst, map, stream);
-    if (s.K == 3 && s.S == 2) return launch_box<BoxK3S2>(s, x, w, bias, dst, map, stream);
-    if (s.K == 3 && s.S == 3) return launch_box<BoxK3S3>(s, x, w, bias, dst, map, stream);
+                                float* dst, int mode, hipStream_t stream) {
+    if (s.K == 3 && s.S == 4) return launch_box<BoxK3S4>(s, x, w, bias, dst, mode, stream);
+    if (s.K == 5 && s.S == 3) return launch_box<BoxK5S3>(s, x, w, bias, dst, mode, stream);
+    if (s.K == 3 && s.S == 2) return launch_box<BoxK3S2>(s, x, w, bias, dst, mode, stream);
+    if (s.K == 3 && s.S == 3) return launch_box<BoxK3S3>(s, x, w, bias, dst, mode, stream);
     return hipErrorInvalidValue;
+}
+
+int64_t conv2d_boxsum_parts(const Conv2dShape& s) {
+    if (s.K == 3 && s.S == 4) return box_parts<BoxK3S4>(s);
+    if (s.K == 5 && s.S == 3) return box_parts<BoxK5S3>(s);
+    if (s.K == 3 && s.S == 2) return box_parts<BoxK3S2>(s);
+    if (s.K == 3 && s.S == 3) return box_parts<BoxK3S3>(s);
+    return -1;
 }
 
 // ---------------------------------------------------------------- simple direct conv (any K, s)
 
 // One thread per (co, ph, pw) of one batch item: the window's s*s conv
 // outputs are summed straight from global memory.  The general fallback.
-template <bool MAP>
+template <int MODE>
 __global__ __launch_bounds__(256) void conv2d_pool_simple_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int K, int S, int PH, int PW) {
@@ -640,27 +712,52 @@ __global__ __launch_bounds__(256) void conv2d_pool_simple_kernel(
                         for (int kx = 0; kx < K; ++kx) acc += xr[kx] * wr[kx];
                     }
         const float avg = acc / (float)(S * S) + (bias ? bias[co] : 0.f);
-        if constexpr (MAP)
+        if constexpr (MODE == OUT_MAP)
             dst[(size_t)b * n + idx] = avg;
         else
             v = logistic(avg);
     }
-    if constexpr (!MAP) {
+    if constexpr (MODE != OUT_MAP) {
         const float s = block_sum<4>(v, red);
-        if (threadIdx.x == 0) atomicAdd(dst + b, s);
+        if (threadIdx.x == 0) {
+            if constexpr (MODE == OUT_SUM_ATOMIC)
+                atomicAdd(dst + b, s);
+            else
+                dst[(size_t)b * gridDim.x + blockIdx.x] = s;
+        }
     }
 }
 
+struct SimpleLaunch {
+    template <int MODE>
+    static constexpr auto kernel = conv2d_pool_simple_kernel<MODE>;
+};
+
+int64_t conv2d_simple_parts(const Conv2dShape& s) { return ((int64_t)s.Cout * s.PH * s.PW + 255) / 256; }
+
 hipError_t conv2d_simple_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
-                                float* dst, bool map, hipStream_t stream) {
-    const int n = s.Cout * s.PH * s.PW;
-    dim3 grid((n + 255) / 256, s.B);
-    if (map)
-        hipLaunchKernelGGL((conv2d_pool_simple_kernel<true>), grid, dim3(256), 0, stream, x, w, bias, dst, s.Cin,
-                           s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW);
-    else
-        hipLaunchKernelGGL((conv2d_pool_simple_kernel<false>), grid, dim3(256), 0, stream, x, w, bias, dst, s.Cin,
-                           s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW);
+                                float* dst, int mode, hipStream_t stream) {
+    const dim3 grid((unsigned)conv2d_simple_parts(s), s.B);
+    FCONV_LAUNCH_MODES(SimpleLaunch::template kernel, grid, dim3(256), 0, stream, x, w, bias, dst, s.Cin, s.H, s.W,
+                       s.Cout, s.K, s.S, s.PH, s.PW);
+}
+
+// ---------------------------------------------------------------- fixed-order reduction of partial sums
+
+// out[b] = sum over p of ws[b*parts + p]: thread t adds p = t, t+256, ... in
+// order, then the workgroup tree (fixed shuffle pattern, fixed wave order).
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ ws, int64_t parts,
+                                                              float* __restrict__ out) {
+    __shared__ float red[4];
+    const float* row = ws + (size_t)blockIdx.x * parts;
+    float v = 0.f;
+    for (int64_t p = threadIdx.x; p < parts; p += 256) v += row[p];
+    const float s = block_sum<4>(v, red);
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
+hipError_t reduce_partials(const float* ws, int64_t parts, int B, float* out, hipStream_t stream) {
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3(B), dim3(256), 0, stream, ws, parts, out);
     return hipGetLastError();
 }
 

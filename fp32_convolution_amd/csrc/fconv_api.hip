@@ -76,6 +76,19 @@ int pick_conv2d_algo(const Conv2dShape& s, int algo) {
     return FCONV_EINVAL;
 }
 
+hipError_t launch_conv2d(int algo, const Conv2dShape& s, const float* x, const float* w, const float* bias,
+                         float* dst, int mode, hipStream_t st) {
+    if (algo == FCONV_ALGO_DIRECT_MFMA) return fconv::conv2d_mfma_launch(s, x, w, bias, dst, mode, st);
+    if (algo == FCONV_ALGO_BOXSUM) return fconv::conv2d_boxsum_launch(s, x, w, bias, dst, mode, st);
+    return fconv::conv2d_simple_launch(s, x, w, bias, dst, mode, st);
+}
+
+int64_t conv2d_parts(int algo, const Conv2dShape& s) {
+    if (algo == FCONV_ALGO_DIRECT_MFMA) return fconv::conv2d_mfma_parts(s);
+    if (algo == FCONV_ALGO_BOXSUM) return fconv::conv2d_boxsum_parts(s);
+    return fconv::conv2d_simple_parts(s);
+}
+
 int run_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
                int64_t K, const float* bias, int64_t pool, int algo, float* dst, bool map, void* stream) {
     Conv2dShape s;
@@ -95,10 +108,20 @@ int run_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, con
         hipError_t e = fconv::fill_zero(dst, s.B, st);
         if (e != hipSuccess) return FCONV_EHIP;
     }
-    hipError_t e = (a == FCONV_ALGO_DIRECT_MFMA) ? fconv::conv2d_mfma_launch(s, x, w, bias, dst, map, st)
-                   : (a == FCONV_ALGO_BOXSUM)     ? fconv::conv2d_boxsum_launch(s, x, w, bias, dst, map, st)
-                                                  : fconv::conv2d_simple_launch(s, x, w, bias, dst, map, st);
-    return status_of(e);
+    return status_of(launch_conv2d(a, s, x, w, bias, dst, map ? fconv::OUT_MAP : fconv::OUT_SUM_ATOMIC, st));
+}
+
+// Shape/algorithm checks shared by the deterministic entry point and its
+// workspace query.  w and out may be placeholders for the query.
+int det_plan(int64_t B, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t K, int64_t pool, int algo,
+             Conv2dShape* s, int* a, int64_t* parts) {
+    static const float placeholder = 0.f;
+    int rc = check_conv2d(&placeholder, B, Cin, H, W, &placeholder, Cout, K, pool, &placeholder, s);
+    if (rc != FCONV_OK) return rc;
+    *a = pick_conv2d_algo(*s, algo);
+    if (*a < 0) return *a;
+    *parts = (s->PH == 0 || s->PW == 0) ? 0 : conv2d_parts(*a, *s);
+    return *parts < 0 ? FCONV_EUNSUPPORTED : FCONV_OK;
 }
 
 }  // namespace
@@ -119,6 +142,36 @@ int fconv2d_pool_sigmoid_sum_algo(const float* x, int64_t B, int64_t Cin, int64_
 int fconv2d_pool_map(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
                      int64_t K, const float* bias, int64_t pool, int algo, float* pooled, void* stream) {
     return run_conv2d(x, B, Cin, H, W, w, Cout, K, bias, pool, algo, pooled, true, stream);
+}
+
+int fconv2d_pool_sigmoid_sum_det_workspace(int64_t B, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t K,
+                                            int64_t pool, int algo, size_t* bytes) {
+    if (!bytes) return FCONV_EINVAL;
+    Conv2dShape s;
+    int a;
+    int64_t parts;
+    int rc = det_plan(B, Cin, H, W, Cout, K, pool, algo, &s, &a, &parts);
+    if (rc != FCONV_OK) return rc;
+    *bytes = (size_t)parts * (size_t)s.B * sizeof(float);
+    return FCONV_OK;
+}
+
+int fconv2d_pool_sigmoid_sum_det(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w,
+                                 int64_t Cout, int64_t K, const float* bias, int64_t pool, int algo, void* workspace,
+                                 size_t workspace_bytes, float* out, void* stream) {
+    if (!x || !w || !out) return FCONV_EINVAL;
+    Conv2dShape s;
+    int a;
+    int64_t parts;
+    int rc = det_plan(B, Cin, H, W, Cout, K, pool, algo, &s, &a, &parts);
+    if (rc != FCONV_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (parts == 0) return status_of(fconv::fill_zero(out, s.B, st));
+    if (!workspace || workspace_bytes < (size_t)parts * (size_t)s.B * sizeof(float)) return FCONV_EINVAL;
+    float* ws = (float*)workspace;
+    hipError_t e = launch_conv2d(a, s, x, w, bias, ws, fconv::OUT_PARTIAL, st);
+    if (e != hipSuccess) return FCONV_EHIP;
+    return status_of(fconv::reduce_partials(ws, parts, s.B, out, st));
 }
 
 int fconv2d_pool_out_size(int64_t H, int64_t W, int64_t K, int64_t pool, int64_t* PH, int64_t* PW) {

@@ -15,20 +15,31 @@ struct DwsepShape {
     int B, C, T, K, O, pad, Tout;
 };
 
+// What a Conv2d kernel writes: the fused sums (one float atomic per
+// workgroup into out[b]), the pre-sigmoid pooled map, or one partial sum per
+// workgroup into ws[b * parts_per_item + part] for a fixed-order reduction.
+enum OutMode { OUT_SUM_ATOMIC = 0, OUT_MAP = 1, OUT_PARTIAL = 2 };
+
 // Returns true (and fills lds_bytes) if the MFMA direct-conv kernel has an
 // instance for (K, S) and its LDS tile for Cin channels fits one workgroup.
 bool conv2d_mfma_supported(int Cin, int K, int S, size_t* lds_bytes);
 
-// Enqueue kernels; return hipSuccess or the launch error.  `map` selects the
-// pooled-map output (pooled[B,Cout,PH,PW]) instead of the fused sum (out[B]).
+// Enqueue kernels; return hipSuccess or the launch error.  `mode` is an
+// OutMode; dst is out[B], pooled[B,Cout,PH,PW] or ws[B * parts_per_item].
 hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
-                              float* dst, bool map, hipStream_t stream);
+                              float* dst, int mode, hipStream_t stream);
 // Box-sum variant: true if it has an instance for (K, S) and its LDS fits.
 bool conv2d_boxsum_supported(int Cin, int K, int S);
 hipError_t conv2d_boxsum_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
-                                float* dst, bool map, hipStream_t stream);
+                                float* dst, int mode, hipStream_t stream);
 hipError_t conv2d_simple_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
-                                float* dst, bool map, hipStream_t stream);
+                                float* dst, int mode, hipStream_t stream);
+// Workgroups (= partial sums) per batch item of each algorithm's launch.
+int64_t conv2d_mfma_parts(const Conv2dShape& s);
+int64_t conv2d_boxsum_parts(const Conv2dShape& s);
+int64_t conv2d_simple_parts(const Conv2dShape& s);
+// out[b] = sum of ws[b*parts .. b*parts+parts-1], in a fixed order.
+hipError_t reduce_partials(const float* ws, int64_t parts, int B, float* out, hipStream_t stream);
 hipError_t fill_zero(float* p, int64_t n, hipStream_t stream);
 
 // True if the fused depthwise-separable kernel's LDS tile fits for this K.

@@ -42,6 +42,7 @@
 #ifndef FCONV_H
 #define FCONV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -100,6 +101,34 @@ int fconv2d_pool_sigmoid_sum(const float* x, int64_t B, int64_t Cin, int64_t H, 
 int fconv2d_pool_sigmoid_sum_algo(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
                                   const float* w, int64_t Cout, int64_t K, const float* bias,
                                   int64_t pool, int algo, float* out, void* stream);
+
+/*
+ * fconv2d_pool_sigmoid_sum_det -- the same result, bitwise reproducible.
+ *   Each workgroup writes its partial sum to its own slot of `workspace`
+ *   (no atomics); a second kernel then adds each batch item's slots in a
+ *   fixed order into out[b].  Repeated calls with the same inputs, algorithm
+ *   and device give identical bits.  This is the two-pass alternative to the
+ *   per-block atomics that the l2_p65 trace weighs in its atomic-contention
+ *   discussion.
+ *   workspace        device memory of at least the size that
+ *                    fconv2d_pool_sigmoid_sum_det_workspace reports, owned by
+ *                    the caller; its contents on entry are ignored and on
+ *                    return are unspecified.  Calls that share a workspace
+ *                    must be ordered (same stream).
+ *   workspace_bytes  its size; FCONV_EINVAL if too small (or NULL with a
+ *                    non-empty pooled map).
+ * Other arguments and errors as fconv2d_pool_sigmoid_sum_algo.
+ */
+int fconv2d_pool_sigmoid_sum_det(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
+                                 const float* w, int64_t Cout, int64_t K, const float* bias,
+                                 int64_t pool, int algo, void* workspace, size_t workspace_bytes,
+                                 float* out, void* stream);
+
+/* Workspace bytes fconv2d_pool_sigmoid_sum_det needs for this shape and
+ * algorithm (B * workgroups per batch item * 4; 0 if the pooled map is
+ * empty).  Host only.  Errors as the call itself (NULL bytes: EINVAL). */
+int fconv2d_pool_sigmoid_sum_det_workspace(int64_t B, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                                           int64_t K, int64_t pool, int algo, size_t* bytes);
 
 /*
  * fconv2d_pool_map -- the pre-sigmoid pooled map of the same computation,

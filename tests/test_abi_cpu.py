@@ -83,8 +83,32 @@ def test_select_algo(lib):
     assert lib.fconv2d_select_algo(3, 4, 3, 4) == 3
     assert lib.fconv2d_select_algo(3, 4, 7, 2) == 2    # no matrix-core instance for K=7 -> simple path
     assert lib.fconv2d_select_algo(512, 4, 3, 4) == 2  # LDS tile too large -> simple path
-    assert lib.fconv2d_select_algo(32, 4, 3, 4) == 1   # box-sum buffers too large, direct tile fits
+    assert lib.fconv2d_select_algo(40, 4, 3, 4) == 3   # box-sum buffers fit where the direct tile does not
+    assert lib.fconv2d_select_algo(44, 4, 3, 4) == 2   # neither fits: simple path
     assert lib.fconv2d_select_algo(0, 4, 3, 4) == EINVAL
+
+
+def test_det_workspace_query(lib):
+    import fp32_convolution_amd as fc
+
+    # direct MFMA on x[128,8,384,384], 4x16 pooled tiles of a 95x95 map: 24*6 workgroups per item
+    assert fc.conv2d_det_workspace_bytes(128, 8, 384, 384, 64, 3, 4, algo=1) == 128 * 24 * 6 * 4
+    # box-sum uses the same tiles; the simple path one workgroup per 256 pooled values of an item
+    assert fc.conv2d_det_workspace_bytes(128, 8, 384, 384, 64, 3, 4, algo=3) == 128 * 24 * 6 * 4
+    assert fc.conv2d_det_workspace_bytes(2, 3, 16, 16, 4, 3, 4, algo=2) == 2 * 1 * 4
+    assert fc.conv2d_det_workspace_bytes(3, 2, 5, 9, 4, 3, 4) == 0          # empty pooled map
+    n = ctypes.c_size_t()
+    assert lib.fconv2d_pool_sigmoid_sum_det_workspace(1, 1, 8, 8, 1, 3, 2, 0, None) == EINVAL
+    assert lib.fconv2d_pool_sigmoid_sum_det_workspace(1, 1, 2, 8, 1, 3, 2, 0, ctypes.byref(n)) == EINVAL
+    assert lib.fconv2d_pool_sigmoid_sum_det_workspace(1, 1, 8, 8, 1, 7, 2, 1, ctypes.byref(n)) == EUNSUP
+
+
+def test_det_rejects_small_workspace(lib):
+    # checked on the host before any launch
+    args = (FAKE, 2, 3, 16, 16, FAKE, 4, 3, None, 4, 2)
+    assert lib.fconv2d_pool_sigmoid_sum_det(*args, FAKE, 7, FAKE, None) == EINVAL
+    assert lib.fconv2d_pool_sigmoid_sum_det(*args, None, 8, FAKE, None) == EINVAL
+    assert lib.fconv2d_pool_sigmoid_sum_det(None, *args[1:], FAKE, 8, FAKE, None) == EINVAL
 
 
 def conv(lib, x=FAKE, B=1, Cin=1, H=8, W=8, w=FAKE, Cout=1, K=3, b=None, pool=2, algo=0, out=FAKE):

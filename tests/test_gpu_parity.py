@@ -119,6 +119,21 @@ def test_conv2d_repeat_calls_overwrite(fc):
     assert_close(out.cpu().numpy(), want, "out after 3 calls")
 
 
+@pytest.mark.parametrize("algo", [1, 2, 3])
+def test_conv2d_deterministic(fc, algo):
+    announce(f"conv2d deterministic algo={algo}")
+    x, w, b = fi.conv2d_inputs(3, 8, 70, 75, 64, 3, seed=6)
+    want = oracle.conv2d_pool_sigmoid_sum(x, w, b, 4)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    first = fc.conv2d_pool_sigmoid_sum_det(xd, wd, bd, 4, algo=algo).cpu().numpy()
+    ws = torch.full((fc.conv2d_det_workspace_bytes(3, 8, 70, 75, 64, 3, 4, algo) // 4,), float("nan"),
+                    device="cuda")
+    for _ in range(3):
+        again = fc.conv2d_pool_sigmoid_sum_det(xd, wd, bd, 4, algo=algo, workspace=ws).cpu().numpy()
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+    assert_close(first, want, f"deterministic out algo={algo}")
+
+
 FULL_CONV = {
     "conv2d_full": [0, 1, 63, 64, 126, 127],
     "conv2d_tail": [0, 31, 62, 63],
@@ -180,6 +195,11 @@ def test_conv2d_full_size_closed_forms(fc, full_conv_inputs, name, algo):
     pos = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=algo).cpu().numpy().astype(np.float64)
     neg = fc.conv2d_pool_sigmoid_sum(xd, -wd, -bd, s, algo=algo).cpu().numpy().astype(np.float64)
     assert_close(pos + neg, np.full(B, float(Cout * PH * PW)), f"{name} sigma symmetry")
+    # the deterministic form agrees with the atomic one and repeats bit for bit
+    d1 = fc.conv2d_pool_sigmoid_sum_det(xd, wd, bd, s, algo=algo).cpu().numpy()
+    d2 = fc.conv2d_pool_sigmoid_sum_det(xd, wd, bd, s, algo=algo).cpu().numpy()
+    assert np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
+    assert_close(d1, pos, f"{name} deterministic vs atomic")
 
 
 # ------------------------------------------------------------------ depthwise-separable path
