@@ -243,22 +243,29 @@ int oracle_conv2d_pooled_at(const float *x, long B, long Cin, long H, long W, co
 
 /* ------------------------------------ depthwise Conv1d -> pointwise 1x1 Conv1d + bias */
 
-/* [P7] opening problem statement: T_out = (T + 2*pad - K)/stride + 1, stride 1. */
-long oracle_dwsep_tout(long T, long K, long pad) {
-    if (T < 1 || K < 1 || pad < 0) return -1;
-    return T + 2 * pad - K + 1;
+/* [P7] opening problem statement: T_out = (T + 2*pad - K)/stride + 1.  With
+ * a dilation d the filter spans d*(K-1)+1 steps (PyTorch's Conv1d), so
+ * T_out = floor((T + 2*pad - d*(K-1) - 1)/stride) + 1; -1 if that is < 1. */
+long oracle_dwsep_tout_ex(long T, long K, long pad, long stride, long dilation) {
+    if (T < 1 || K < 1 || pad < 0 || stride < 1 || dilation < 1) return -1;
+    const long span = T + 2 * pad - dilation * (K - 1) - 1;
+    if (span < 0) return -1;
+    return span / stride + 1;
 }
+
+long oracle_dwsep_tout(long T, long K, long pad) { return oracle_dwsep_tout_ex(T, K, pad, 1, 1); }
 
 typedef struct {
     const float *x, *w_dw, *w_pw, *b_pw;
-    long B, C, T, K, O, pad, Tout;
+    long B, C, T, K, O, pad, stride, dilation, Tout;
     long b;
     double *D; /* [C][Tout] */
     double *y; /* [O][Tout] for the current batch item */
 } dwsep_ctx;
 
-/* Depthwise stage, one channel: D[c,t] = sum_k w_dw[c,k] * x[b,c,t+k-pad],
- * reading 0 outside [0, T).  [P7] per-output formula, inner sum. */
+/* Depthwise stage, one channel: D[c,t] = sum_k w_dw[c,k] * x[b,c,t*stride+k*dilation-pad],
+ * reading 0 outside [0, T).  [P7] per-output formula, inner sum (its
+ * in[b, c, t*stride + k - padding]; the dilation spaces the taps). */
 static void dw_channel(void *vctx, long c, double *unused) {
     (void)unused;
     dwsep_ctx *d = (dwsep_ctx *)vctx;
@@ -268,7 +275,7 @@ static void dw_channel(void *vctx, long c, double *unused) {
     for (long t = 0; t < d->Tout; ++t) {
         double acc = 0.0;
         for (long k = 0; k < d->K; ++k) {
-            const long src = t + k - d->pad;
+            const long src = t * d->stride + k * d->dilation - d->pad;
             const double xv = (src >= 0 && src < d->T) ? (double)xr[src] : 0.0;
             acc += (double)wr[k] * xv;
         }
@@ -298,12 +305,12 @@ static void pw_channel(void *vctx, long o, double *unused) {
  * batch_idx[i] (NULL: i = 0..nb-1); y is [nb, O, Tout] doubles.  b_pw may
  * be NULL (zero).
  */
-int oracle_dwsep_conv1d(const float *x, long B, long C, long T, const float *w_dw, long K, const float *w_pw,
-                        long O, const float *b_pw, long pad, const long *batch_idx, long nb, double *y,
-                        int nthreads) {
+int oracle_dwsep_conv1d_ex(const float *x, long B, long C, long T, const float *w_dw, long K, const float *w_pw,
+                           long O, const float *b_pw, long pad, long stride, long dilation, const long *batch_idx,
+                           long nb, double *y, int nthreads) {
     dwsep_ctx d;
     if (!x || !w_dw || !w_pw || !y || B < 1 || C < 1 || O < 1 || nb < 0) return ORACLE_EINVAL;
-    d.Tout = oracle_dwsep_tout(T, K, pad);
+    d.Tout = oracle_dwsep_tout_ex(T, K, pad, stride, dilation);
     if (d.Tout < 1) return ORACLE_EINVAL;
     if (batch_idx) {
         for (long i = 0; i < nb; ++i)
@@ -312,7 +319,7 @@ int oracle_dwsep_conv1d(const float *x, long B, long C, long T, const float *w_d
         return ORACLE_EINVAL;
     }
     d.x = x; d.w_dw = w_dw; d.w_pw = w_pw; d.b_pw = b_pw;
-    d.B = B; d.C = C; d.T = T; d.K = K; d.O = O; d.pad = pad;
+    d.B = B; d.C = C; d.T = T; d.K = K; d.O = O; d.pad = pad; d.stride = stride; d.dilation = dilation;
     d.D = (double *)malloc((size_t)(C * d.Tout) * sizeof(double));
     if (!d.D) return ORACLE_ENOMEM;
     int rc = ORACLE_OK;
@@ -326,12 +333,18 @@ int oracle_dwsep_conv1d(const float *x, long B, long C, long T, const float *w_d
     return rc;
 }
 
+int oracle_dwsep_conv1d(const float *x, long B, long C, long T, const float *w_dw, long K, const float *w_pw,
+                        long O, const float *b_pw, long pad, const long *batch_idx, long nb, double *y,
+                        int nthreads) {
+    return oracle_dwsep_conv1d_ex(x, B, C, T, w_dw, K, w_pw, O, b_pw, pad, 1, 1, batch_idx, nb, y, nthreads);
+}
+
 /* y at n chosen positions idx[3*i..3*i+2] = (b, o, t), each from the
  * definition (the depthwise values are recomputed per position). */
-int oracle_dwsep_conv1d_at(const float *x, long B, long C, long T, const float *w_dw, long K,
-                           const float *w_pw, long O, const float *b_pw, long pad, const long *idx, long n,
-                           double *y) {
-    const long Tout = oracle_dwsep_tout(T, K, pad);
+int oracle_dwsep_conv1d_at_ex(const float *x, long B, long C, long T, const float *w_dw, long K,
+                              const float *w_pw, long O, const float *b_pw, long pad, long stride, long dilation,
+                              const long *idx, long n, double *y) {
+    const long Tout = oracle_dwsep_tout_ex(T, K, pad, stride, dilation);
     if (!x || !w_dw || !w_pw || !y || (n > 0 && !idx) || Tout < 1) return ORACLE_EINVAL;
     for (long i = 0; i < n; ++i) {
         const long b = idx[3 * i], o = idx[3 * i + 1], t = idx[3 * i + 2];
@@ -340,7 +353,7 @@ int oracle_dwsep_conv1d_at(const float *x, long B, long C, long T, const float *
         for (long c = 0; c < C; ++c) {
             double dv = 0.0;
             for (long k = 0; k < K; ++k) {
-                const long src = t + k - pad;
+                const long src = t * stride + k * dilation - pad;
                 const double xv = (src >= 0 && src < T) ? (double)x[(b * C + c) * T + src] : 0.0;
                 dv += (double)w_dw[c * K + k] * xv;
             }
@@ -349,4 +362,10 @@ int oracle_dwsep_conv1d_at(const float *x, long B, long C, long T, const float *
         y[i] = acc + (b_pw ? (double)b_pw[o] : 0.0);
     }
     return ORACLE_OK;
+}
+
+int oracle_dwsep_conv1d_at(const float *x, long B, long C, long T, const float *w_dw, long K,
+                           const float *w_pw, long O, const float *b_pw, long pad, const long *idx, long n,
+                           double *y) {
+    return oracle_dwsep_conv1d_at_ex(x, B, C, T, w_dw, K, w_pw, O, b_pw, pad, 1, 1, idx, n, y);
 }

@@ -42,6 +42,14 @@ def load():
     lib.oracle_conv2d_pooled_at.restype = ctypes.c_int
     lib.oracle_dwsep_tout.argtypes = [_L, _L, _L]
     lib.oracle_dwsep_tout.restype = _L
+    lib.oracle_dwsep_tout_ex.argtypes = [_L, _L, _L, _L, _L]
+    lib.oracle_dwsep_tout_ex.restype = _L
+    lib.oracle_dwsep_conv1d_ex.argtypes = [
+        _f32p, _L, _L, _L, _f32p, _L, _f32p, _L, _f32p, _L, _L, _L, _i64p, _L, _f64p, ctypes.c_int]
+    lib.oracle_dwsep_conv1d_ex.restype = ctypes.c_int
+    lib.oracle_dwsep_conv1d_at_ex.argtypes = [
+        _f32p, _L, _L, _L, _f32p, _L, _f32p, _L, _f32p, _L, _L, _L, _i64p, _L, _f64p]
+    lib.oracle_dwsep_conv1d_at_ex.restype = ctypes.c_int
     lib.oracle_dwsep_conv1d.argtypes = [
         _f32p, _L, _L, _L, _f32p, _L, _f32p, _L, _f32p, _L, _i64p, _L, _f64p, ctypes.c_int]
     lib.oracle_dwsep_conv1d.restype = ctypes.c_int
@@ -137,12 +145,12 @@ def conv2d_pooled_at(x, w, b, pool, idx):
     return out
 
 
-def dwsep_tout(T, K, pad):
-    return int(load().oracle_dwsep_tout(T, K, pad))
+def dwsep_tout(T, K, pad, stride=1, dilation=1):
+    return int(load().oracle_dwsep_tout_ex(T, K, pad, stride, dilation))
 
 
-def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad, batch_idx=None, nthreads=None):
-    """Literal depthwise Conv1d(K, pad) -> pointwise 1x1 Conv1d + bias; y [nb,O,Tout] float64."""
+def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad, batch_idx=None, nthreads=None, stride=1, dilation=1):
+    """Literal depthwise Conv1d(K, pad, stride, dilation) -> pointwise 1x1 Conv1d + bias; y [nb,O,Tout] float64."""
     lib = load()
     x, w_dw, w_pw = _f32(x), _f32(w_dw), _f32(w_pw)
     b_pw = None if b_pw is None else _f32(b_pw)
@@ -151,7 +159,7 @@ def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad, batch_idx=None, nthreads=None):
     O, C3 = w_pw.shape
     if C2 != C or C3 != C or (b_pw is not None and b_pw.shape != (O,)):
         raise ValueError("shape mismatch")
-    Tout = dwsep_tout(T, K, pad)
+    Tout = dwsep_tout(T, K, pad, stride, dilation)
     if Tout < 1:
         raise ValueError("empty output")
     if batch_idx is None:
@@ -160,14 +168,14 @@ def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad, batch_idx=None, nthreads=None):
         idx = np.ascontiguousarray(batch_idx, dtype=np.int64)
         nb = idx.size
     y = np.zeros((nb, O, Tout), dtype=np.float64)
-    rc = lib.oracle_dwsep_conv1d(_fp(x), B, C, T, _fp(w_dw), K, _fp(w_pw), O, _fp(b_pw), pad,
-                                 None if idx is None else idx.ctypes.data_as(_i64p), nb,
-                                 y.ctypes.data_as(_f64p), _threads(nthreads))
+    rc = lib.oracle_dwsep_conv1d_ex(_fp(x), B, C, T, _fp(w_dw), K, _fp(w_pw), O, _fp(b_pw), pad, stride, dilation,
+                                    None if idx is None else idx.ctypes.data_as(_i64p), nb,
+                                    y.ctypes.data_as(_f64p), _threads(nthreads))
     _check(rc, "dwsep_conv1d")
     return y
 
 
-def dwsep_conv1d_at(x, w_dw, w_pw, b_pw, pad, idx):
+def dwsep_conv1d_at(x, w_dw, w_pw, b_pw, pad, idx, stride=1, dilation=1):
     """y at positions idx [n,3] = (b, o, t), each from the definition."""
     lib = load()
     x, w_dw, w_pw = _f32(x), _f32(w_dw), _f32(w_pw)
@@ -177,7 +185,7 @@ def dwsep_conv1d_at(x, w_dw, w_pw, b_pw, pad, idx):
     O, _ = w_pw.shape
     idx = np.ascontiguousarray(idx, dtype=np.int64).reshape(-1, 3)
     y = np.zeros(idx.shape[0], dtype=np.float64)
-    rc = lib.oracle_dwsep_conv1d_at(_fp(x), B, C, T, _fp(w_dw), K, _fp(w_pw), O, _fp(b_pw), pad,
-                                    idx.ctypes.data_as(_i64p), idx.shape[0], y.ctypes.data_as(_f64p))
+    rc = lib.oracle_dwsep_conv1d_at_ex(_fp(x), B, C, T, _fp(w_dw), K, _fp(w_pw), O, _fp(b_pw), pad, stride,
+                                       dilation, idx.ctypes.data_as(_i64p), idx.shape[0], y.ctypes.data_as(_f64p))
     _check(rc, "dwsep_conv1d_at")
     return y

@@ -176,3 +176,66 @@ def test_page_figures():
     assert g["C"] * g["K"] == g["dense_macs_per_output"]
     assert g["B"] * g["C"] * g["T_out"] * g["K"] == g["depthwise_macs"]
     assert g["B"] * g["O"] * g["T_out"] * g["C"] == g["pointwise_macs"]
+
+
+def torch_reference_ex(x, w_dw, w_pw, b_pw, pad, stride, dilation):
+    xt = torch.from_numpy(x.astype(np.float64))
+    C, K = w_dw.shape
+    d = F.conv1d(xt, torch.from_numpy(w_dw.astype(np.float64)).reshape(C, 1, K), padding=pad, groups=C,
+                 stride=stride, dilation=dilation)
+    bt = None if b_pw is None else torch.from_numpy(b_pw.astype(np.float64))
+    return F.conv1d(d, torch.from_numpy(w_pw.astype(np.float64))[:, :, None], bt).numpy()
+
+
+STRIDED = [
+    # B, C, T, O, K, pad, stride, dilation
+    (2, 6, 50, 8, 9, 4, 2, 1),
+    (1, 5, 47, 3, 9, 4, 3, 1),
+    (2, 4, 40, 6, 3, 2, 1, 2),
+    (1, 3, 33, 4, 5, 0, 2, 3),
+    (2, 7, 64, 9, 9, 8, 4, 2),
+    (1, 2, 9, 2, 3, 0, 5, 4),    # one output step
+]
+
+
+@pytest.mark.parametrize("shape", STRIDED)
+def test_strided_dilated_match_torch_float64(shape):
+    B, C, T, O, K, pad, stride, dil = shape
+    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=93)
+    want = torch_reference_ex(x, w_dw, w_pw, b_pw, pad, stride, dil)
+    got = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad, stride=stride, dilation=dil)
+    assert got.shape == want.shape
+    assert oracle.dwsep_tout(T, K, pad, stride, dil) == want.shape[2]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    rng = np.random.default_rng(2)
+    idx = np.stack([rng.integers(0, n, 40) for n in got.shape], axis=1)
+    np.testing.assert_allclose(oracle.dwsep_conv1d_at(x, w_dw, w_pw, b_pw, pad, idx, stride=stride, dilation=dil),
+                               got[tuple(idx.T)], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("stride,dil", [(2, 1), (3, 2), (1, 3)])
+def test_strided_delta_input(stride, dil):
+    # x = e(c0, t0): y[o,t] - b[o] = w_pw[o,c0] * sum of w_dw[c0,k] over taps k with
+    # t*stride + k*dil - pad == t0.
+    B, C, T, O, K, pad = 1, 3, 40, 4, 5, 3
+    _, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=97)
+    c0 = 1
+    for t0 in (0, 7, T - 1):
+        x = np.zeros((B, C, T), np.float32)
+        x[0, c0, t0] = 1.0
+        y = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad, stride=stride, dilation=dil)[0]
+        y -= b_pw.astype(np.float64)[:, None]
+        want = np.zeros_like(y)
+        for t in range(y.shape[1]):
+            tap = sum(float(w_dw[c0, k]) for k in range(K) if t * stride + k * dil - pad == t0)
+            want[:, t] = w_pw[:, c0].astype(np.float64) * tap
+        np.testing.assert_allclose(y, want, rtol=0, atol=1e-15)
+
+
+def test_output_length_formula():
+    # [P7]: T_out = (T + 2*pad - K)/stride + 1; a dilation d makes the filter span d*(K-1)+1.
+    assert oracle.dwsep_tout(4096, 9, 4, 1, 1) == 4096
+    assert oracle.dwsep_tout(10, 3, 1, 2, 1) == 5
+    assert oracle.dwsep_tout(10, 3, 0, 1, 2) == 6
+    assert oracle.dwsep_tout(9, 3, 0, 5, 4) == 1
+    assert oracle.dwsep_tout(8, 3, 0, 1, 4) == -1
