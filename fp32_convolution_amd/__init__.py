@@ -29,7 +29,7 @@ ALGO_BOXSUM = 3
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"libfconv.so not found at {LIB_PATH}; build it first with `python -m fp32_convolution_amd.build`")
+        f"libfconv.so not found at {LIB_PATH}; build it first with `python fp32_convolution_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -51,6 +51,9 @@ _SIGS = {
     "fconv2d_select_algo": ([_i64, _i64, _i64, _i64], ctypes.c_int),
     "dwsep_conv1d": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp], ctypes.c_int),
     "dwsep_conv1d_out_len": ([_i64, _i64, _i64], ctypes.c_int64),
+    "dwsep_conv1d_ex": (
+        [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "dwsep_conv1d_out_len_ex": ([_i64, _i64, _i64, _i64, _i64], ctypes.c_int64),
     "fconv_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "fconv_version": ([], ctypes.c_int),
 }
@@ -186,12 +189,12 @@ def conv2d_pool_map(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO):
     return out
 
 
-def dwsep_out_len(T: int, K: int, pad: int) -> int:
-    return int(lib.dwsep_conv1d_out_len(T, K, pad))
+def dwsep_out_len(T: int, K: int, pad: int, stride: int = 1, dilation: int = 1) -> int:
+    return int(lib.dwsep_conv1d_out_len_ex(T, K, pad, stride, dilation))
 
 
-def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None):
-    """Depthwise Conv1d(K, pad) -> pointwise 1x1 Conv1d + bias: y[B,O,Tout].
+def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None, stride: int = 1, dilation: int = 1):
+    """Depthwise Conv1d(K, pad, stride, dilation) -> pointwise 1x1 Conv1d + bias: y[B,O,Tout].
 
     w_dw may be [C,K] or PyTorch's [C,1,K]; w_pw [O,C] or [O,C,1].
     """
@@ -216,7 +219,7 @@ def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None):
     for t in (w_dw, w_pw, b_pw, out):
         if t is not None and t.device != x.device:
             raise ValueError("all tensors must be on x's device")
-    Tout = dwsep_out_len(T, K, pad)
+    Tout = dwsep_out_len(T, K, pad, stride, dilation)
     if Tout < 1:
         raise FconvError(FCONV_EINVAL, "dwsep_conv1d")
     if out is None:
@@ -225,6 +228,7 @@ def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None):
         _dev_f32(out, "out")
         if tuple(out.shape) != (B, O, Tout):
             raise ValueError(f"out must be [B,O,Tout]=({B},{O},{Tout})")
-    rc = lib.dwsep_conv1d(_ptr(x), B, C, T, _ptr(w_dw), K, _ptr(w_pw), O, _ptr(b_pw), pad, _ptr(out), _stream(x))
+    rc = lib.dwsep_conv1d_ex(_ptr(x), B, C, T, _ptr(w_dw), K, _ptr(w_pw), O, _ptr(b_pw), pad, stride, dilation,
+                             _ptr(out), _stream(x))
     _check(rc, "dwsep_conv1d")
     return out

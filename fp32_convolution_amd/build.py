@@ -1,6 +1,7 @@
 """Builds libfconv.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m fp32_convolution_amd.build [-v]
+Usage: python fp32_convolution_amd/build.py [-v]   (run by path: importing the
+package would load the library being rebuilt)
 
 Flags: -O3 for gfx950 only; -munsafe-fp-atomics so float atomicAdd is the
 native global_atomic_add_f32; packed-FP32 VALU instructions disabled

@@ -53,7 +53,8 @@ struct DwsepCfg {
 template <class Cfg, bool VEC>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
     const float* __restrict__ x, const float* __restrict__ w_dw, const float* __restrict__ w_pw,
-    const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int Kr, int O, int pad, int Tout) {
+    const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int Kr, int O, int pad, int Tout,
+    int stride, int dil) {
     constexpr int OB = Cfg::OB, TB = Cfg::TB, WO = Cfg::WO, CC = Cfg::CC, CCP = Cfg::CCP, CPW = Cfg::CPW;
     constexpr int TT = Cfg::TT, NW = Cfg::NW;
     const int K = Cfg::KC > 0 ? Cfg::KC : Kr;
@@ -61,7 +62,9 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
     extern __shared__ float lds[];
     float* Ds = lds;             // [TT][CCP]
     float* xs = lds + TT * CCP;  // [CC][XW]
-    const int XW = TT + K - 1;
+    // input steps a time tile reads; the compile-time-K instances run only
+    // with stride = dilation = 1
+    const int XW = Cfg::KC > 0 ? TT + K - 1 : (TT - 1) * stride + (K - 1) * dil + 1;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
         } else {
             for (int ch = 0; ch < nch; ++ch) {
                 const int u = ch * 64 + lane;
-                const int src = t0 - pad + u;
+                const int src = t0 * stride - pad + u;
                 const int voff = (u < XW && src >= 0) ? src * 4 : kBufOOB;
                 for (int r0 = wave; r0 < CC; r0 += NW * UR) {
                     float v[UR];
@@ -176,13 +179,13 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
             for (int cc = 0; cc < CPW; ++cc) {
                 const int c = wave * CPW + cc;
                 const float* wr = w_dw + (size_t)min(c0 + c, C - 1) * K;  // rows >= C: x is 0 there
-                const float* xr = xs + c * XW + t;
+                const float* xr = xs + c * XW + (Cfg::KC > 0 ? t : t * stride);
                 float s = 0.f;
                 if constexpr (Cfg::KC > 0) {
 #pragma unroll
                     for (int k = 0; k < Cfg::KC; ++k) s += wr[k] * xr[k];
                 } else {
-                    for (int k = 0; k < K; ++k) s += wr[k] * xr[k];
+                    for (int k = 0; k < K; ++k) s += wr[k] * xr[k * dil];
                 }
                 d[cc] = s;
             }
@@ -236,24 +239,29 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_mfma_kernel(
 }
 
 // Instances.  Wide (O > 64): 256 x 64 tile, 8 waves of 32 x 64, register
-// budget for 4 waves per SIMD.  Small: 32 x 32.
+// budget for 4 waves per SIMD.  Small: 32 x 32.  Narrow: 256 x 16, for
+// strides/dilations whose 64-step input window would not fit in LDS.
 // FCONV_CFG_DW9 lets a build override the K = 9 instance's tiling.
 #ifndef FCONV_CFG_DW9
 #define FCONV_CFG_DW9 2, 4, 8, 1, 64, 9, 4
 #endif
 using DwWide9 = DwsepCfg<FCONV_CFG_DW9>;
 using DwWideK = DwsepCfg<2, 4, 8, 1, 64, 0, 4>;
+using DwNarrowK = DwsepCfg<2, 1, 8, 1, 32, 0, 4>;
 using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 
 template <class Cfg>
-static size_t dw_lds_bytes(int K) {
-    return ((size_t)Cfg::TT * Cfg::CCP + (size_t)Cfg::CC * (Cfg::TT + K - 1)) * sizeof(float);
+static size_t dw_lds_bytes(const DwsepShape& s) {
+    const long xw = Cfg::KC > 0 ? Cfg::TT + Cfg::KC - 1 : (long)(Cfg::TT - 1) * s.stride + (long)(s.K - 1) * s.dil + 1;
+    return ((size_t)Cfg::TT * Cfg::CCP + (size_t)Cfg::CC * xw) * sizeof(float);
 }
+
+static constexpr size_t kDwLdsLimit = 160 * 1024;
 
 template <class Cfg>
 static hipError_t launch_dw(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                             const float* b_pw, float* y, hipStream_t stream) {
-    const size_t lds = dw_lds_bytes<Cfg>(s.K);
+    const size_t lds = dw_lds_bytes<Cfg>(s);
     dim3 grid((s.Tout + Cfg::TT - 1) / Cfg::TT, (s.O + Cfg::OT - 1) / Cfg::OT, s.B);
     const bool vec = (s.C % 4 == 0) && ((uintptr_t)w_pw % 16 == 0);
     hipError_t e;
@@ -262,29 +270,43 @@ static hipError_t launch_dw(const DwsepShape& s, const float* x, const float* w_
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((dwsep_mfma_kernel<Cfg, true>), grid, dim3(Cfg::NT), lds, stream, x, w_dw, w_pw, b_pw,
-                           y, s.C, s.T, s.K, s.O, s.pad, s.Tout);
+                           y, s.C, s.T, s.K, s.O, s.pad, s.Tout, s.stride, s.dil);
     } else {
         e = hipFuncSetAttribute((const void*)dwsep_mfma_kernel<Cfg, false>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((dwsep_mfma_kernel<Cfg, false>), grid, dim3(Cfg::NT), lds, stream, x, w_dw, w_pw, b_pw,
-                           y, s.C, s.T, s.K, s.O, s.pad, s.Tout);
+                           y, s.C, s.T, s.K, s.O, s.pad, s.Tout, s.stride, s.dil);
     }
     return hipGetLastError();
 }
 
-bool dwsep_supported(int K, int O) {
-    const size_t limit = 160 * 1024;
-    if (O > 64) return dw_lds_bytes<DwWideK>(K) <= limit;
-    return dw_lds_bytes<DwSmallK>(K) <= limit;
+// The instance a shape runs on: 0 = none fits, 1 = wide K=9, 2 = wide
+// runtime-K, 3 = narrow runtime-K, 4 = small runtime-K.
+static int pick_dw(const DwsepShape& s) {
+    const bool unit = s.stride == 1 && s.dil == 1;
+    if (s.O > 64) {
+        if (unit && s.K == 9) return 1;
+        if (dw_lds_bytes<DwWideK>(s) <= kDwLdsLimit) return 2;
+        if (dw_lds_bytes<DwNarrowK>(s) <= kDwLdsLimit) return 3;
+        return 0;
+    }
+    if (dw_lds_bytes<DwSmallK>(s) <= kDwLdsLimit) return 4;
+    if (dw_lds_bytes<DwNarrowK>(s) <= kDwLdsLimit) return 3;
+    return 0;
 }
+
+bool dwsep_supported(const DwsepShape& s) { return pick_dw(s) != 0; }
 
 hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                         const float* b_pw, float* y, hipStream_t stream) {
-    if (s.O > 64)
-        return s.K == 9 ? launch_dw<DwWide9>(s, x, w_dw, w_pw, b_pw, y, stream)
-                        : launch_dw<DwWideK>(s, x, w_dw, w_pw, b_pw, y, stream);
-    return launch_dw<DwSmallK>(s, x, w_dw, w_pw, b_pw, y, stream);
+    switch (pick_dw(s)) {
+        case 1: return launch_dw<DwWide9>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 2: return launch_dw<DwWideK>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 3: return launch_dw<DwNarrowK>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 4: return launch_dw<DwSmallK>(s, x, w_dw, w_pw, b_pw, y, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace fconv

@@ -187,17 +187,21 @@ int fconv2d_select_algo(int64_t Cin, int64_t Cout, int64_t K, int64_t pool) {
     return auto_conv2d_algo((int)Cin, (int)K, (int)pool);
 }
 
-int64_t dwsep_conv1d_out_len(int64_t T, int64_t K, int64_t pad) {
-    if (T < 1 || K < 1 || pad < 0 || pad > INT32_MAX) return -1;
-    const int64_t tout = T + 2 * pad - K + 1;
-    return tout >= 1 ? tout : -1;
+int64_t dwsep_conv1d_out_len_ex(int64_t T, int64_t K, int64_t pad, int64_t stride, int64_t dilation) {
+    if (T < 1 || K < 1 || pad < 0 || stride < 1 || dilation < 1) return -1;
+    if (pad > (INT64_MAX / 4) || K > (INT64_MAX / 4) / dilation || T > INT64_MAX / 4) return -1;
+    const int64_t span = T + 2 * pad - dilation * (K - 1) - 1;
+    return span < 0 ? -1 : span / stride + 1;
 }
 
-int dwsep_conv1d(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
-                 const float* w_pw, int64_t O, const float* b_pw, int64_t pad, float* y, void* stream) {
+int64_t dwsep_conv1d_out_len(int64_t T, int64_t K, int64_t pad) { return dwsep_conv1d_out_len_ex(T, K, pad, 1, 1); }
+
+int dwsep_conv1d_ex(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
+                    const float* w_pw, int64_t O, const float* b_pw, int64_t pad, int64_t stride, int64_t dilation,
+                    float* y, void* stream) {
     if (!x || !w_dw || !w_pw || !y) return FCONV_EINVAL;
-    if (B < 1 || C < 1 || T < 1 || O < 1 || K < 1 || pad < 0) return FCONV_EINVAL;
-    const int64_t Tout = dwsep_conv1d_out_len(T, K, pad);
+    if (B < 1 || C < 1 || T < 1 || O < 1 || K < 1 || pad < 0 || stride < 1 || dilation < 1) return FCONV_EINVAL;
+    const int64_t Tout = dwsep_conv1d_out_len_ex(T, K, pad, stride, dilation);
     if (Tout < 1) return FCONV_EINVAL;
     int64_t per_item_x, per_item_y, t, n;
     if (!mul_ok(C, T, &per_item_x) || !mul_ok(per_item_x, B, &n)) return FCONV_EINVAL;
@@ -205,15 +209,21 @@ int dwsep_conv1d(const float* x, int64_t B, int64_t C, int64_t T, const float* w
     if (!mul_ok(O, C, &t) || !mul_ok(C, K, &n)) return FCONV_EINVAL;
     // The kernel reads x rows (T floats) and w_pw (O*C floats) through buffer
     // resources of < 2^31 bytes; other offsets are 32-bit per batch item.
-    if (!fits_i32(per_item_x) || !fits_i32(per_item_y) || t >= (1 << 29) || T >= (1 << 29) || !fits_i32(n) ||
-        B > 65535 || K > 8192 || O > (1 << 20))
+    const int64_t lim = (int64_t)1 << 29;
+    if (!fits_i32(per_item_x) || !fits_i32(per_item_y) || t >= lim || T >= lim || !fits_i32(n) || B > 65535 ||
+        K > 8192 || O > (1 << 20) || pad >= lim || stride >= lim || dilation * (K - 1) >= lim)
         return FCONV_EUNSUPPORTED;
-    if (!fconv::dwsep_supported((int)K, (int)O)) return FCONV_EUNSUPPORTED;
-    DwsepShape s{(int)B, (int)C, (int)T, (int)K, (int)O, (int)pad, (int)Tout};
+    DwsepShape s{(int)B, (int)C, (int)T, (int)K, (int)O, (int)pad, (int)Tout, (int)stride, (int)dilation};
+    if (!fconv::dwsep_supported(s)) return FCONV_EUNSUPPORTED;
     if (log_enabled())
-        fprintf(stderr, "[fconv] dwsep B=%d C=%d T=%d K=%d O=%d pad=%d Tout=%d\n", s.B, s.C, s.T, s.K, s.O, s.pad,
-                s.Tout);
+        fprintf(stderr, "[fconv] dwsep B=%d C=%d T=%d K=%d O=%d pad=%d stride=%d dil=%d Tout=%d\n", s.B, s.C, s.T,
+                s.K, s.O, s.pad, s.stride, s.dil, s.Tout);
     return status_of(fconv::dwsep_launch(s, x, w_dw, w_pw, b_pw, y, (hipStream_t)stream));
+}
+
+int dwsep_conv1d(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
+                 const float* w_pw, int64_t O, const float* b_pw, int64_t pad, float* y, void* stream) {
+    return dwsep_conv1d_ex(x, B, C, T, w_dw, K, w_pw, O, b_pw, pad, 1, 1, y, stream);
 }
 
 const char* fconv_strerror(int status) {

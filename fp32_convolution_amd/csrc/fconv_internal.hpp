@@ -12,7 +12,7 @@ struct Conv2dShape {
 };
 
 struct DwsepShape {
-    int B, C, T, K, O, pad, Tout;
+    int B, C, T, K, O, pad, Tout, stride, dil;
 };
 
 // What a Conv2d kernel writes: the fused sums (one float atomic per
@@ -42,8 +42,8 @@ int64_t conv2d_simple_parts(const Conv2dShape& s);
 hipError_t reduce_partials(const float* ws, int64_t parts, int B, float* out, hipStream_t stream);
 hipError_t fill_zero(float* p, int64_t n, hipStream_t stream);
 
-// True if the fused depthwise-separable kernel's LDS tile fits for this K.
-bool dwsep_supported(int K, int O);
+// True if a fused depthwise-separable instance's LDS tile fits this shape.
+bool dwsep_supported(const DwsepShape& s);
 hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                         const float* b_pw, float* y, hipStream_t stream);
 

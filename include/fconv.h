@@ -178,6 +178,24 @@ int dwsep_conv1d(const float* x, int64_t B, int64_t C, int64_t T, const float* w
 /* Tout for dwsep_conv1d, or -1 if the arguments are invalid.  Host only. */
 int64_t dwsep_conv1d_out_len(int64_t T, int64_t K, int64_t pad);
 
+/*
+ * dwsep_conv1d_ex -- dwsep_conv1d with a depthwise stride and dilation
+ * (PyTorch Conv1d semantics; the l2_p7 trace parametrises the stride):
+ *   D[b,c,t] = sum_{k < K} w_dw[c,k] * x[b,c, t*stride + k*dilation - pad]
+ *   Tout = floor((T + 2*pad - dilation*(K-1) - 1) / stride) + 1
+ * The pointwise stage and the bias are as in dwsep_conv1d.  stride = dilation
+ * = 1 is exactly dwsep_conv1d.  FCONV_EINVAL additionally for stride < 1 or
+ * dilation < 1; FCONV_EUNSUPPORTED additionally when pad, stride or
+ * dilation*(K-1) is 2^29 or more, or the strided input window of even the
+ * narrowest time tile does not fit in LDS.
+ */
+int dwsep_conv1d_ex(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
+                    const float* w_pw, int64_t O, const float* b_pw, int64_t pad, int64_t stride,
+                    int64_t dilation, float* y, void* stream);
+
+/* Tout for dwsep_conv1d_ex, or -1 if the arguments are invalid.  Host only. */
+int64_t dwsep_conv1d_out_len_ex(int64_t T, int64_t K, int64_t pad, int64_t stride, int64_t dilation);
+
 /* Static description of a status code (never NULL). */
 const char* fconv_strerror(int status);
 

@@ -159,6 +159,22 @@ def test_dwsep_unsupported(lib):
     assert dw(lib, B=70000) == EUNSUP
 
 
+def test_dwsep_ex_checks(lib):
+    def dwx(stride=1, dil=1, K=3, T=16, pad=1, C=4):
+        return lib.dwsep_conv1d_ex(FAKE, 1, C, T, FAKE, K, FAKE, 4, None, pad, stride, dil, FAKE, None)
+    assert dwx(stride=0) == EINVAL
+    assert dwx(dil=0) == EINVAL
+    assert dwx(K=9, T=8, pad=0, dil=2) == EINVAL          # dilated filter longer than the padded input
+    assert dwx(stride=2**30) == EUNSUP
+    assert dwx(K=3, dil=2**29, T=2**28, pad=2**29) == EUNSUP
+    assert dwx(stride=4000, T=2**20, C=16) == EUNSUP      # strided window does not fit in LDS
+    assert lib.dwsep_conv1d_out_len_ex(4096, 9, 4, 1, 1) == 4096
+    assert lib.dwsep_conv1d_out_len_ex(10, 3, 1, 2, 1) == 5
+    assert lib.dwsep_conv1d_out_len_ex(10, 3, 0, 1, 2) == 6
+    assert lib.dwsep_conv1d_out_len_ex(8, 3, 0, 1, 4) == -1
+    assert lib.dwsep_conv1d_out_len_ex(8, 3, 0, 0, 1) == -1
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
 

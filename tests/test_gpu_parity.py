@@ -228,6 +228,26 @@ def test_dwsep_small(fc, shape):
     assert_close(got, want, f"y {shape}")
 
 
+STRIDED_DW = [
+    # B, C, T, O, K, pad, stride, dilation
+    (2, 64, 300, 300, 9, 4, 2, 1),     # wide runtime-K instance, stride 2
+    (1, 48, 257, 512, 9, 8, 1, 2),     # dilation 2
+    (2, 20, 100, 40, 5, 3, 3, 2),      # small instance
+    (1, 16, 2000, 128, 9, 4, 16, 1),   # window too wide for 64 steps: narrow instance
+    (1, 32, 40, 64, 3, 0, 5, 4),       # few output steps
+]
+
+
+@pytest.mark.parametrize("shape", STRIDED_DW)
+def test_dwsep_strided_dilated(fc, shape):
+    B, C, T, O, K, pad, stride, dil = shape
+    announce(f"dwsep strided/dilated {shape}")
+    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=11)
+    want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad, stride=stride, dilation=dil)
+    got = fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad, stride=stride, dilation=dil).cpu().numpy()
+    assert_close(got, want, f"y {shape}")
+
+
 def test_dwsep_no_bias_and_torch_shapes(fc):
     announce("dwsep no bias, [C,1,K] and [O,C,1] weights")
     x, w_dw, w_pw, _ = fi.dwsep_inputs(2, 32, 100, 48, 9, seed=8)
