@@ -142,6 +142,12 @@ def dwsep_flops(cfg):
     return 2 * cfg["B"] * Tout * cfg["C"] * (cfg["K"] + cfg["O"])
 
 
+def dwsep_dense_flops(cfg):
+    """Work of the dense-fused form: C*K*O MACs per output step."""
+    Tout = cfg["T"] + 2 * cfg["pad"] - cfg["K"] + 1
+    return 2 * cfg["B"] * Tout * cfg["C"] * cfg["K"] * cfg["O"]
+
+
 def dwsep_bytes(cfg):
     Tout = cfg["T"] + 2 * cfg["pad"] - cfg["K"] + 1
     return 4 * (cfg["B"] * cfg["C"] * cfg["T"] + cfg["C"] * cfg["K"] + cfg["O"] * cfg["C"] + cfg["O"]
@@ -267,21 +273,33 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
 
-    # The box-sum variant of the Conv2d call (pool before convolving), timed
-    # on its own after the step loop and measured against its own work: Cin*K*K
-    # MACs per (co, pooled output) and the same compulsory bytes (HBM-bound).
+    def time_calls(fn):
+        for _ in range(args.warmup):
+            fn()
+        evs = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+
+    # Variants, each timed on its own after the step loop and measured against
+    # its own work.  Box-sum (pool before convolving): Cin*K*K MACs per (co,
+    # pooled output), the same compulsory bytes (HBM-bound).  Deterministic
+    # Conv2d: the direct kernel writing per-workgroup partials plus a
+    # fixed-order reduction.  Dense-fused dwsep: C*K*O MACs per step.
     out_box = torch.empty_like(out)
-    ms_box = []
-    for _ in range(args.warmup):
-        fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=out_box, algo=fc.ALGO_BOXSUM)
-    for _ in range(args.steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=out_box, algo=fc.ALGO_BOXSUM)
-        e1.record(stream)
-        ms_box.append((e0, e1))
-    torch.cuda.synchronize()
-    ms_box = np.array([e0.elapsed_time(e1) for e0, e1 in ms_box])
+    ms_box = time_calls(lambda: fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=out_box, algo=fc.ALGO_BOXSUM))
+    out_det = torch.empty_like(out)
+    ws_det = torch.empty(fc.conv2d_det_workspace_bytes(cc["B"], cc["Cin"], cc["H"], cc["W"], cc["Cout"], cc["K"],
+                                                       cc["pool"], fc.ALGO_DIRECT_MFMA) // 4, device=dev)
+    ms_det = time_calls(lambda: fc.conv2d_pool_sigmoid_sum_det(x, w, b, cc["pool"], out=out_det,
+                                                               algo=fc.ALGO_DIRECT_MFMA, workspace=ws_det))
+    y_dense = torch.empty_like(y)
+    ms_dense = time_calls(lambda: fc.dwsep_conv1d(xd, wdw, wpw, bpw, dc["pad"], out=y_dense, algo=fc.DWSEP_DENSE))
 
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
@@ -315,6 +333,13 @@ def main():
              "speedup_vs_direct": round(k_conv["ms_mean"] / mb, 2),
              "matches_direct_within_tol": bool(
                  ((out_box - out).abs() <= 1e-4 + 1e-4 * out.abs()).all().item())}
+    k_det = kstats(ms_det, f_conv, b_conv)
+    k_det["algorithm"] = "direct MFMA, deterministic (partials + fixed-order reduction)"
+    k_det["matches_atomic_within_tol"] = bool(((out_det - out).abs() <= 1e-4 + 1e-4 * out.abs()).all().item())
+    f_dense = dwsep_dense_flops(dc)
+    k_dense = kstats(ms_dense, f_dense, b_dw)
+    k_dense["algorithm"] = "dense-fused combined weight (FCONV_DWSEP_DENSE), own FLOPs C*K*O per step"
+    k_dense["matches_separable_within_tol"] = bool(((y_dense - y).abs() <= 1e-4 + 1e-4 * y.abs()).all().item())
 
     result = {
         "metric": METRIC,
@@ -336,7 +361,8 @@ def main():
             "parallelism": "single GPU",
         },
         "kernels": {"fconv2d_pool_sigmoid_sum": k_conv, "dwsep_conv1d": k_dw},
-        "variants": {"fconv2d_pool_sigmoid_sum_boxsum": k_box},
+        "variants": {"fconv2d_pool_sigmoid_sum_boxsum": k_box, "fconv2d_pool_sigmoid_sum_det": k_det,
+                     "dwsep_conv1d_dense": k_dense},
         "roofline": {
             "kernel": "fconv2d_pool_sigmoid_sum (conv2d_pool_mfma_kernel) on " + CONV,
             "bound": "mfma",

@@ -27,6 +27,10 @@ ALGO_DIRECT_MFMA = 1
 ALGO_DIRECT_SIMPLE = 2
 ALGO_BOXSUM = 3
 
+DWSEP_AUTO = 0
+DWSEP_SEPARABLE = 1
+DWSEP_DENSE = 2
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libfconv.so not found at {LIB_PATH}; build it first with `python fp32_convolution_amd/build.py`")
@@ -54,6 +58,8 @@ _SIGS = {
     "dwsep_conv1d_ex": (
         [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
     "dwsep_conv1d_out_len_ex": ([_i64, _i64, _i64, _i64, _i64], ctypes.c_int64),
+    "dwsep_conv1d_algo": (
+        [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
     "fconv_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "fconv_version": ([], ctypes.c_int),
 }
@@ -193,7 +199,8 @@ def dwsep_out_len(T: int, K: int, pad: int, stride: int = 1, dilation: int = 1) 
     return int(lib.dwsep_conv1d_out_len_ex(T, K, pad, stride, dilation))
 
 
-def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None, stride: int = 1, dilation: int = 1):
+def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None, stride: int = 1, dilation: int = 1,
+                 algo: int = DWSEP_AUTO):
     """Depthwise Conv1d(K, pad, stride, dilation) -> pointwise 1x1 Conv1d + bias: y[B,O,Tout].
 
     w_dw may be [C,K] or PyTorch's [C,1,K]; w_pw [O,C] or [O,C,1].
@@ -228,7 +235,7 @@ def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None, stride: int = 1, dilat
         _dev_f32(out, "out")
         if tuple(out.shape) != (B, O, Tout):
             raise ValueError(f"out must be [B,O,Tout]=({B},{O},{Tout})")
-    rc = lib.dwsep_conv1d_ex(_ptr(x), B, C, T, _ptr(w_dw), K, _ptr(w_pw), O, _ptr(b_pw), pad, stride, dilation,
-                             _ptr(out), _stream(x))
+    rc = lib.dwsep_conv1d_algo(_ptr(x), B, C, T, _ptr(w_dw), K, _ptr(w_pw), O, _ptr(b_pw), pad, stride, dilation,
+                               algo, _ptr(out), _stream(x))
     _check(rc, "dwsep_conv1d")
     return out

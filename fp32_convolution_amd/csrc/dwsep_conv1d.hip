@@ -250,6 +250,145 @@ using DwWideK = DwsepCfg<2, 4, 8, 1, 64, 0, 4>;
 using DwNarrowK = DwsepCfg<2, 1, 8, 1, 32, 0, 4>;
 using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 
+// ---------------------------------------------------------------- dense-fused variant
+
+// The l2_p7 trace's dense-fused form: one convolution with the combined
+// weight W[o,c,k] = w_pw[o,c] * w_dw[c,k] (equal to the separable result up
+// to rounding, with C*K*O instead of C*(K+O) multiply-adds per step).  Kept
+// as a second, independently arranged path and a comparison point.
+//   Per 16-channel group and tap k the MFMA k-slots hold channels 4g..4g+3
+//   (as in the separable kernel); A = w_pw[o, c] * w_dw[c, k] is formed in
+//   registers (one multiply per weight fragment and tap), B is the staged
+//   input x[c, t*stride + k*dilation - pad] read straight from LDS.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_dense_kernel(
+    const float* __restrict__ x, const float* __restrict__ w_dw, const float* __restrict__ w_pw,
+    const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int K, int O, int pad, int Tout,
+    int stride, int dil) {
+    constexpr int OB = Cfg::OB, TB = Cfg::TB, WO = Cfg::WO, CC = Cfg::CC, TT = Cfg::TT, NW = Cfg::NW, NT = Cfg::NT;
+    static_assert(Cfg::KC == 0, "the dense kernel takes K at run time");
+
+    extern __shared__ float lds[];
+    const int XW = (TT - 1) * stride + (K - 1) * dil + 1;
+    float* xs = lds;             // [CC][XW]
+    float* wsm = lds + CC * XW;  // [CC][K] depthwise taps of the chunk
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wo = wave % WO;
+    const int wt = wave / WO;
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int t0 = blockIdx.x * TT;
+    const int o0 = blockIdx.y * Cfg::OT + wo * 16 * OB;
+    const int b = blockIdx.z;
+    const float* xb = x + (size_t)b * C * T;
+
+    int woff[OB];
+#pragma unroll
+    for (int ob = 0; ob < OB; ++ob) woff[ob] = (min(o0 + ob * 16 + l16, O - 1) * C + 4 * g) * 4;
+
+    floatx4 acc[OB][TB];
+#pragma unroll
+    for (int i = 0; i < OB; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int nch = (XW + 63) / 64;
+    for (int c0 = 0; c0 < C; c0 += CC) {
+        __syncthreads();
+        for (int ch = 0; ch < nch; ++ch) {
+            const int u = ch * 64 + lane;
+            const int src = t0 * stride - pad + u;
+            const int voff = (u < XW && src >= 0) ? src * 4 : kBufOOB;
+            for (int row = wave; row < CC; row += NW) {
+                const bool ok = c0 + row < C;
+                const buf_rsrc rrow = make_rsrc(xb + (ok ? (size_t)(c0 + row) * T : 0), ok ? T * 4 : 0);
+                const float v = buf_load_f32(rrow, voff);
+                if (u < XW) xs[row * XW + u] = v;
+            }
+        }
+        const int nw_valid = min(CC, C - c0) * K;
+        for (int i = tid; i < CC * K; i += NT) {
+            const float v = w_dw[(size_t)c0 * K + min(i, nw_valid - 1)];
+            wsm[i] = i < nw_valid ? v : 0.f;
+        }
+        __syncthreads();
+        for (int s16 = 0; s16 < CC; s16 += 16) {
+            const int grp = (c0 + s16) / 16;
+            if (c0 + s16 >= C) break;
+            // pointwise weights of channels 16*grp + 4g .. +3 (past the end of
+            // w_pw: 0; past C: the next row's, multiplied by x = 0)
+            const buf_rsrc rw = make_rsrc(w_pw + 16 * grp, (O * C - 16 * grp) * 4);
+            floatx4 apw[OB];
+#pragma unroll
+            for (int ob = 0; ob < OB; ++ob)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    apw[ob][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, woff[ob] + 4 * j,
+                                                                                              0, 0));
+            for (int k = 0; k < K; ++k) {
+                float bv[TB][4];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const int tl = (wt * TB + tb) * 16 + l16;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bv[tb][j] = xs[(s16 + 4 * g + j) * XW + tl * stride + k * dil];
+                }
+                float wk[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wk[j] = wsm[(s16 + 4 * g + j) * K + k];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int ob = 0; ob < OB; ++ob) {
+                        const float a = apw[ob][j] * wk[j];
+#pragma unroll
+                        for (int tb = 0; tb < TB; ++tb) acc[ob][tb] = mfma_16x16x4(a, bv[tb][j], acc[ob][tb]);
+                    }
+            }
+        }
+    }
+
+    const buf_rsrc rb = make_rsrc(b_pw, b_pw ? O * 4 : 0);
+    float* yb = y + (size_t)b * O * Tout;
+#pragma unroll
+    for (int ob = 0; ob < OB; ++ob)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int o = o0 + ob * 16 + 4 * g + r;
+            const float bo = buf_load_f32(rb, o < O ? o * 4 : kBufOOB);
+            if (o >= O) continue;
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int t = t0 + (wt * TB + tb) * 16 + l16;
+                if (t < Tout) yb[(size_t)o * Tout + t] = acc[ob][tb][r] + bo;
+            }
+        }
+}
+
+using DwDense = DwsepCfg<2, 4, 8, 1, 64, 0, 4>;
+
+static size_t dense_lds_bytes(const DwsepShape& s) {
+    const long xw = (long)(DwDense::TT - 1) * s.stride + (long)(s.K - 1) * s.dil + 1;
+    return ((size_t)DwDense::CC * xw + (size_t)DwDense::CC * s.K) * sizeof(float);
+}
+
+bool dwsep_dense_supported(const DwsepShape& s) { return dense_lds_bytes(s) <= 160 * 1024; }
+
+hipError_t dwsep_dense_launch(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
+                              const float* b_pw, float* y, hipStream_t stream) {
+    const size_t lds = dense_lds_bytes(s);
+    hipError_t e = hipFuncSetAttribute((const void*)dwsep_dense_kernel<DwDense>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    dim3 grid((s.Tout + DwDense::TT - 1) / DwDense::TT, (s.O + DwDense::OT - 1) / DwDense::OT, s.B);
+    hipLaunchKernelGGL(dwsep_dense_kernel<DwDense>, grid, dim3(DwDense::NT), lds, stream, x, w_dw, w_pw, b_pw, y, s.C,
+                       s.T, s.K, s.O, s.pad, s.Tout, s.stride, s.dil);
+    return hipGetLastError();
+}
+
 template <class Cfg>
 static size_t dw_lds_bytes(const DwsepShape& s) {
     const long xw = Cfg::KC > 0 ? Cfg::TT + Cfg::KC - 1 : (long)(Cfg::TT - 1) * s.stride + (long)(s.K - 1) * s.dil + 1;

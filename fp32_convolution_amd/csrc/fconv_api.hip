@@ -196,9 +196,11 @@ int64_t dwsep_conv1d_out_len_ex(int64_t T, int64_t K, int64_t pad, int64_t strid
 
 int64_t dwsep_conv1d_out_len(int64_t T, int64_t K, int64_t pad) { return dwsep_conv1d_out_len_ex(T, K, pad, 1, 1); }
 
-int dwsep_conv1d_ex(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
-                    const float* w_pw, int64_t O, const float* b_pw, int64_t pad, int64_t stride, int64_t dilation,
-                    float* y, void* stream) {
+int dwsep_conv1d_algo(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
+                      const float* w_pw, int64_t O, const float* b_pw, int64_t pad, int64_t stride,
+                      int64_t dilation, int algo, float* y, void* stream) {
+    if (algo != FCONV_DWSEP_AUTO && algo != FCONV_DWSEP_SEPARABLE && algo != FCONV_DWSEP_DENSE)
+        return FCONV_EINVAL;
     if (!x || !w_dw || !w_pw || !y) return FCONV_EINVAL;
     if (B < 1 || C < 1 || T < 1 || O < 1 || K < 1 || pad < 0 || stride < 1 || dilation < 1) return FCONV_EINVAL;
     const int64_t Tout = dwsep_conv1d_out_len_ex(T, K, pad, stride, dilation);
@@ -214,11 +216,21 @@ int dwsep_conv1d_ex(const float* x, int64_t B, int64_t C, int64_t T, const float
         K > 8192 || O > (1 << 20) || pad >= lim || stride >= lim || dilation * (K - 1) >= lim)
         return FCONV_EUNSUPPORTED;
     DwsepShape s{(int)B, (int)C, (int)T, (int)K, (int)O, (int)pad, (int)Tout, (int)stride, (int)dilation};
-    if (!fconv::dwsep_supported(s)) return FCONV_EUNSUPPORTED;
+    const bool dense = algo == FCONV_DWSEP_DENSE;
+    if (dense ? !fconv::dwsep_dense_supported(s) : !fconv::dwsep_supported(s)) return FCONV_EUNSUPPORTED;
     if (log_enabled())
-        fprintf(stderr, "[fconv] dwsep B=%d C=%d T=%d K=%d O=%d pad=%d stride=%d dil=%d Tout=%d\n", s.B, s.C, s.T,
-                s.K, s.O, s.pad, s.stride, s.dil, s.Tout);
-    return status_of(fconv::dwsep_launch(s, x, w_dw, w_pw, b_pw, y, (hipStream_t)stream));
+        fprintf(stderr, "[fconv] dwsep%s B=%d C=%d T=%d K=%d O=%d pad=%d stride=%d dil=%d Tout=%d\n",
+                dense ? "_dense" : "", s.B, s.C, s.T, s.K, s.O, s.pad, s.stride, s.dil, s.Tout);
+    hipStream_t st = (hipStream_t)stream;
+    return status_of(dense ? fconv::dwsep_dense_launch(s, x, w_dw, w_pw, b_pw, y, st)
+                           : fconv::dwsep_launch(s, x, w_dw, w_pw, b_pw, y, st));
+}
+
+int dwsep_conv1d_ex(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
+                    const float* w_pw, int64_t O, const float* b_pw, int64_t pad, int64_t stride, int64_t dilation,
+                    float* y, void* stream) {
+    return dwsep_conv1d_algo(x, B, C, T, w_dw, K, w_pw, O, b_pw, pad, stride, dilation, FCONV_DWSEP_AUTO, y,
+                             stream);
 }
 
 int dwsep_conv1d(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,

@@ -46,5 +46,9 @@ hipError_t fill_zero(float* p, int64_t n, hipStream_t stream);
 bool dwsep_supported(const DwsepShape& s);
 hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                         const float* b_pw, float* y, hipStream_t stream);
+// The dense-fused (combined 9-tap weight) variant.
+bool dwsep_dense_supported(const DwsepShape& s);
+hipError_t dwsep_dense_launch(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
+                              const float* b_pw, float* y, hipStream_t stream);
 
 }  // namespace fconv

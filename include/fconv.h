@@ -196,6 +196,19 @@ int dwsep_conv1d_ex(const float* x, int64_t B, int64_t C, int64_t T, const float
 /* Tout for dwsep_conv1d_ex, or -1 if the arguments are invalid.  Host only. */
 int64_t dwsep_conv1d_out_len_ex(int64_t T, int64_t K, int64_t pad, int64_t stride, int64_t dilation);
 
+/* Algorithms for the depthwise-separable path (same result up to rounding). */
+#define FCONV_DWSEP_AUTO 0      /* = SEPARABLE */
+#define FCONV_DWSEP_SEPARABLE 1 /* depthwise into LDS, pointwise GEMM: C*(K+O) MACs per step */
+#define FCONV_DWSEP_DENSE 2     /* one convolution with the combined weight
+                                   W[o,c,k] = w_pw[o,c]*w_dw[c,k] (the l2_p7 trace's dense-fused
+                                   form): C*K*O MACs per step; a comparison path */
+
+/* dwsep_conv1d_ex with an explicit algorithm (FCONV_DWSEP_*).  FCONV_EINVAL
+ * for an unknown algorithm; otherwise as dwsep_conv1d_ex. */
+int dwsep_conv1d_algo(const float* x, int64_t B, int64_t C, int64_t T, const float* w_dw, int64_t K,
+                      const float* w_pw, int64_t O, const float* b_pw, int64_t pad, int64_t stride,
+                      int64_t dilation, int algo, float* y, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fconv_strerror(int status);
 

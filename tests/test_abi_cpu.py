@@ -175,6 +175,14 @@ def test_dwsep_ex_checks(lib):
     assert lib.dwsep_conv1d_out_len_ex(8, 3, 0, 0, 1) == -1
 
 
+def test_dwsep_algo_checks(lib):
+    args = (FAKE, 1, 4, 16, FAKE, 3, FAKE, 4, None, 1, 1, 1)
+    assert lib.dwsep_conv1d_algo(*args, 3, FAKE, None) == EINVAL      # unknown algorithm
+    assert lib.dwsep_conv1d_algo(*args, -1, FAKE, None) == EINVAL
+    assert lib.dwsep_conv1d_algo(FAKE, 1, 4, 16, FAKE, 3, FAKE, 4, None, 1, 0, 1, 2, FAKE, None) == EINVAL
+    assert lib.dwsep_conv1d_algo(FAKE, 1, 16, 2**20, FAKE, 3, FAKE, 4, None, 1, 5000, 1, 2, FAKE, None) == EUNSUP
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
 

@@ -248,6 +248,38 @@ def test_dwsep_strided_dilated(fc, shape):
     assert_close(got, want, f"y {shape}")
 
 
+DENSE_DW = [
+    # B, C, T, O, K, pad, stride, dilation
+    (4, 16, 256, 32, 9, 4, 1, 1),      # the small workload
+    (2, 100, 150, 70, 9, 4, 1, 1),     # C not a multiple of 16, O ragged
+    (1, 64, 200, 300, 5, 2, 2, 2),     # strided and dilated
+]
+
+
+@pytest.mark.parametrize("shape", DENSE_DW)
+def test_dwsep_dense_variant(fc, shape):
+    B, C, T, O, K, pad, stride, dil = shape
+    announce(f"dwsep dense {shape}")
+    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=12)
+    want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad, stride=stride, dilation=dil)
+    args = (dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad)
+    dense = fc.dwsep_conv1d(*args, stride=stride, dilation=dil, algo=fc.DWSEP_DENSE).cpu().numpy()
+    sep = fc.dwsep_conv1d(*args, stride=stride, dilation=dil, algo=fc.DWSEP_SEPARABLE).cpu().numpy()
+    assert_close(dense, want, f"dense y {shape}")
+    assert_close(dense, sep, f"dense vs separable {shape}")
+
+
+def test_dwsep_dense_full_size_sampled(fc):
+    announce("dwsep dense full size")
+    cfg = fi.WORKLOADS["dwsep_full"]
+    x, w_dw, w_pw, b_pw = fi.make("dwsep_full", seed=0)
+    got = fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), cfg["pad"], algo=fc.DWSEP_DENSE).cpu().numpy()
+    rng = np.random.default_rng(8)
+    samp = np.stack([rng.integers(0, n, 5000) for n in got.shape], axis=1)
+    want = oracle.dwsep_conv1d_at(x, w_dw, w_pw, b_pw, cfg["pad"], samp)
+    assert_close(got[tuple(samp.T)], want, "dense sampled")
+
+
 def test_dwsep_no_bias_and_torch_shapes(fc):
     announce("dwsep no bias, [C,1,K] and [O,C,1] weights")
     x, w_dw, w_pw, _ = fi.dwsep_inputs(2, 32, 100, 48, 9, seed=8)
