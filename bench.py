@@ -44,6 +44,10 @@ KERNEL_SOURCES = {
                                 "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_mfma_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                           "fp32_convolution_amd/csrc/fconv_device.hpp"],
+    "conv2d_pool_boxsum_kernel": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
+                                  "fp32_convolution_amd/csrc/fconv_device.hpp"],
+    "dwsep_dense_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
+                           "fp32_convolution_amd/csrc/fconv_device.hpp"],
 }
 
 
@@ -329,7 +333,8 @@ def main():
              "gflops_own": round(f_box / (mb * 1e-3) / 1e9, 1), "algorithmic_gflop_own": round(f_box / 1e9, 3),
              "hbm_gbps_algorithmic": round(b_conv / (mb * 1e-3) / 1e9, 1),
              "roofline": {"bound": "hbm", "achieved": round(b_conv / (mb * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
-                          "unit": "GB/s", "frac": round(b_conv / (mb * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+                          "unit": "GB/s", "frac": round(b_conv / (mb * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                          "traffic": measured_traffic("conv2d_pool_boxsum_kernel")},
              "speedup_vs_direct": round(k_conv["ms_mean"] / mb, 2),
              "matches_direct_within_tol": bool(
                  ((out_box - out).abs() <= 1e-4 + 1e-4 * out.abs()).all().item())}
@@ -339,6 +344,7 @@ def main():
     f_dense = dwsep_dense_flops(dc)
     k_dense = kstats(ms_dense, f_dense, b_dw)
     k_dense["algorithm"] = "dense-fused combined weight (FCONV_DWSEP_DENSE), own FLOPs C*K*O per step"
+    k_dense["hbm_bytes_measured"] = measured_traffic("dwsep_dense_kernel")
     k_dense["matches_separable_within_tol"] = bool(((y_dense - y).abs() <= 1e-4 + 1e-4 * y.abs()).all().item())
 
     result = {
