@@ -42,7 +42,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "conv2d_pool_mfma_kernel": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
                                 "fp32_convolution_amd/csrc/fconv_device.hpp"],
-    "dwsep_mfma_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
+    "dwsep_tall_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                           "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "conv2d_pool_boxsum_kernel": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
                                   "fp32_convolution_amd/csrc/fconv_device.hpp"],
@@ -324,7 +324,7 @@ def main():
     k_conv = kstats(ms_conv, f_conv, b_conv)
     k_dw = kstats(ms_dw, f_dw, b_dw)
     k_conv["hbm_bytes_measured"] = measured_traffic("conv2d_pool_mfma_kernel")
-    k_dw["hbm_bytes_measured"] = measured_traffic("dwsep_mfma_kernel")
+    k_dw["hbm_bytes_measured"] = measured_traffic("dwsep_tall_kernel")
     achieved = f_conv / (k_conv["ms_mean"] * 1e-3) / 1e12
     f_box = conv2d_boxsum_flops(cc)
     mb = float(ms_box.mean())

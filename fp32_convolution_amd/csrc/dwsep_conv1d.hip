@@ -29,6 +29,8 @@
 // Out-of-range output rows read a clamped (valid) weight row and are never
 // stored.  Channels >= C have D = 0, so whatever weights pair with them
 // (the next row's, or 0 past the end of w_pw) add nothing.
+#include <type_traits>
+
 #include "fconv_device.hpp"
 #include "fconv_internal.hpp"
 
@@ -250,6 +252,254 @@ using DwWideK = DwsepCfg<2, 4, 8, 1, 64, 0, 4>;
 using DwNarrowK = DwsepCfg<2, 1, 8, 1, 32, 0, 4>;
 using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 
+// ---------------------------------------------------------------- tall-tile variant
+
+// Stride 1, dilation 1, O > 256: a 512 x 64 tile (8 waves of 64 x 64), so
+// each depthwise value is made once per time tile instead of once per 256
+// output channels, and the matrix cores see twice the work per depthwise
+// instruction.  The extra accumulator registers are paid for by staging x,
+// the depthwise taps and the bias with LDS-direct buffer loads
+// (buffer_load_dword ... lds: memory to LDS with no register round trip),
+// which also lets the next chunk's rows stream in while the current chunk's
+// GEMM runs.
+//
+// Per chunk of CC channels (every chunk has CC/16 groups; in a last,
+// partial chunk the channels >= C are staged as 0, so their depthwise value
+// is 0, and their pointwise weights load as 0):
+//   wait for this wave's LDS-direct loads; barrier (xs holds chunk i, Ds is free)
+//   depthwise xs -> Ds; barrier (Ds ready, xs free)
+//   LDS-direct loads of chunk i+1 into xs
+//   GEMM over the chunk's 16-channel groups
+// The accumulators start at the bias.  Epilogue: each wave transposes its
+// 64 x 64 block through LDS, 16 rows at a time, and writes rows of 64 steps
+// with 16-byte stores; ragged tiles store element by element.
+// Depthwise (K = 9 instance): lane (dc, dj) makes steps 8dj .. 8dj+7 of the
+// wave's channel dc from 16 staged steps (four 16-byte LDS reads) and the
+// channel's 9 taps (staged in LDS too, so the stage needs no scalar loads,
+// whose out-of-order return would serialize the LDS reads): 8 independent
+// multiply-add chains per lane.  The runtime-K instance has lane t make
+// step t of each of the wave's channels.
+// LDS: xs [CC][128], then Ds: [64][CC+4] for the GEMM operand and
+// 8 x [16][68] in the epilogue, then the bias [512] and the taps [CC][9]
+// (71.8 KB, two workgroups per CU).  Row r of xs holds input steps
+// t0-pad .. t0-pad+127 (two 64-lane runs; steps past the K-1 halo or
+// outside [0, T) load as 0), so K <= 65.
+// Pointwise weights: lane (g, l16) of block ob keeps channels 4g..4g+3 of
+// the current group; the registers of block ob are refilled with the next
+// group's weights as soon as its 16 matrix instructions are issued.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
+    const float* __restrict__ x, const float* __restrict__ w_dw, const float* __restrict__ w_pw,
+    const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int Kr, int O, int pad, int Tout,
+    int vec_out) {
+    constexpr int OB = Cfg::OB, TB = Cfg::TB, CC = Cfg::CC, CCP = Cfg::CCP, CPW = Cfg::CPW;
+    constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = 128, OP = 68;
+    constexpr int DSF = TT * CCP > NW * 16 * OP ? TT * CCP : NW * 16 * OP;
+    static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && OB == 4 && TB == 4, "8 waves of 64 x 64");
+    static_assert(CC % NW == 0 && CC % 16 == 0, "whole rows per wave, whole groups per chunk");
+    const int K = Cfg::KC > 0 ? Cfg::KC : Kr;
+    const int XW = TT + K - 1;  // input steps the tile reads (<= XP)
+
+    // xs first: the depthwise reads then fit the short LDS offset fields
+    extern __shared__ float lds[];
+    float* xs = lds;            // [CC][XP]
+    float* Ds = lds + CC * XP;  // [TT][CCP]; epilogue: [NW][16][OP]
+    float* bs = Ds + DSF;       // [NW][64]: each wave's 64 bias values
+    float* ws = bs + NW * 64;   // [CC][9]: the chunk's depthwise taps (K = 9 instance)
+    auto* xs3 = (__attribute__((address_space(3))) float*)xs;
+    auto* bs3 = (__attribute__((address_space(3))) float*)bs;
+    auto* ws3 = (__attribute__((address_space(3))) float*)ws;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int t0 = blockIdx.x * TT;
+    const int o0 = blockIdx.y * Cfg::OT + wave * 16 * OB;  // this wave's first output channel
+    const float* xb = x + (size_t)blockIdx.z * C * T;
+
+    // 1. staging: per row two LDS-direct loads of 64 consecutive steps; rows
+    //    >= C get an empty resource and load 0
+    int voff[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int u = 64 * r + lane;
+        const int src = t0 - pad + u;
+        voff[r] = (u < XW && src >= 0) ? src * 4 : kBufOOB;
+    }
+    auto stage = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < CC / NW; ++i) {
+            const int row = c0 + wave + i * NW;
+            const buf_rsrc rr = make_rsrc(xb + (size_t)min(row, C - 1) * T, row < C ? T * 4 : 0);
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, xs3 + (wave + i * NW) * XP + 64 * r, 4, voff[r], 0, 0,
+                                                         0);
+        }
+        if constexpr (Cfg::KC == 9) {
+            // the chunk's taps w_dw[c0 .. c0+CC-1][0..8] are contiguous: 9 runs
+            // of 64 floats (0 past channel C-1)
+            const int n = min(CC, C - c0) * 9;
+            const buf_rsrc rt = make_rsrc(w_dw + (size_t)c0 * 9, n * 4);
+            for (int q = wave; q < 9 * CC / 64; q += NW)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, ws3 + 64 * q, 4, (64 * q + lane) * 4, 0, 0, 0);
+        }
+    };
+
+    // Pointwise weights.  rw[ob] covers rows o0 + 16*ob .. O-1 of w_pw (none
+    // past O), so lanes whose row is >= O load 0; lane (g, l16) reads row
+    // 16*ob + l16 of it at channels cb + 4g .. +3, with the channel offset
+    // cb*4 in the scalar offset field.  A lane in range stays inside its
+    // row, so the loads are in bounds whether or not the scalar offset
+    // enters the hardware range check.  Lanes whose channels are all >= C
+    // (C is a multiple of 4) take an out-of-range offset and load 0.
+    const int woff = (l16 * C + 4 * g) * 4;
+    buf_rsrc rw[OB];
+#pragma unroll
+    for (int ob = 0; ob < OB; ++ob) {
+        const int rows = O - (o0 + 16 * ob);
+        rw[ob] = make_rsrc(w_pw + (size_t)(rows > 0 ? o0 + 16 * ob : 0) * C, rows > 0 ? rows * C * 4 : 0);
+    }
+    auto load_pw = [&](int ob, int cb) {
+        const int off = cb + 4 * g < C ? woff : kBufOOB;
+        return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rw[ob], off, cb * 4, 0));
+    };
+
+    floatx4 acc[OB][TB];
+    floatx4 a[OB];
+#pragma unroll
+    for (int ob = 0; ob < OB; ++ob) a[ob] = load_pw(ob, 0);
+    stage(0);
+    {
+        // this wave's 64 bias values (0 past O or without a bias)
+        const int rows = O - o0;
+        const buf_rsrc rb = make_rsrc(b_pw + (rows > 0 ? o0 : 0), b_pw && rows > 0 ? rows * 4 : 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, bs3 + wave * 64, 4, lane * 4, 0, 0, 0);
+    }
+
+    for (int c0 = 0; c0 < C; c0 += CC) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's LDS-direct loads have landed
+        __syncthreads();
+        if (c0 == 0) {
+            // the accumulators start at the bias
+#pragma unroll
+            for (int ob = 0; ob < OB; ++ob) {
+                const floatx4 bo = *reinterpret_cast<const floatx4*>(bs + wave * 64 + 16 * ob + 4 * g);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) acc[ob][tb] = bo;
+            }
+        }
+        // 2. depthwise -> Ds[t][c] for the wave's CPW channels (channels >= C
+        //    read the zero rows staged for them, so their D is 0)
+        if constexpr (Cfg::KC == 9) {
+            static_assert(CPW == 8 && 9 * CC % 64 == 0, "8 channels x 8 groups of 8 steps per wave");
+            const int dc = lane & 7, dj = lane >> 3;
+            const int c = wave * CPW + dc;
+            float xv[16], wv[9];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const floatx4 v = *reinterpret_cast<const floatx4*>(xs + c * XP + 8 * dj + 4 * q);
+                xv[4 * q] = v[0];
+                xv[4 * q + 1] = v[1];
+                xv[4 * q + 2] = v[2];
+                xv[4 * q + 3] = v[3];
+            }
+#pragma unroll
+            for (int k = 0; k < 9; ++k) wv[k] = ws[c * 9 + k];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float s = 0.f;
+#pragma unroll
+                for (int k = 0; k < 9; ++k) s += wv[k] * xv[i + k];
+                Ds[(8 * dj + i) * CCP + c] = s;
+            }
+        } else {
+            float d[CPW];
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc) {
+                const float* wr = w_dw + (size_t)min(c0 + wave * CPW + cc, C - 1) * K;
+                const float* xr = xs + (wave * CPW + cc) * XP + lane;
+                float s = 0.f;
+                for (int k = 0; k < K; ++k) s += wr[k] * xr[k];
+                d[cc] = s;
+            }
+#pragma unroll
+            for (int c4 = 0; c4 < CPW; c4 += 4)
+                *reinterpret_cast<floatx4*>(Ds + lane * CCP + wave * CPW + c4) =
+                    floatx4{d[c4], d[c4 + 1], d[c4 + 2], d[c4 + 3]};
+        }
+        __syncthreads();
+        if (c0 + CC < C) stage(c0 + CC);
+        // 3. pointwise GEMM over the chunk's 16-channel groups; block ob's
+        //    registers take the next group's weights once its products are
+        //    issued (past the last group these load 0)
+#pragma unroll
+        for (int s16 = 0; s16 < CC; s16 += 16) {
+            floatx4 bq[TB];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+                bq[tb] = *reinterpret_cast<const floatx4*>(Ds + (tb * 16 + l16) * CCP + s16 + 4 * g);
+#pragma unroll
+            for (int ob = 0; ob < OB; ++ob) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) acc[ob][tb] = mfma_16x16x4(a[ob][j], bq[tb][j], acc[ob][tb]);
+                a[ob] = load_pw(ob, c0 + s16 + 16);
+            }
+        }
+    }
+
+    // 4. epilogue: lane (g, l16) holds y[o0 + 16*ob + 4g + r, t0 + 16*tb + l16]
+    float* yb = y + (size_t)blockIdx.z * O * Tout;
+    __syncthreads();  // every wave is done reading Ds (outside the branch: o0 differs per wave)
+    if (vec_out && o0 + 16 * OB <= O && t0 + TT <= Tout) {
+        float* ow = Ds + wave * 16 * OP;
+#pragma unroll
+        for (int ob = 0; ob < OB; ++ob) {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ow[(4 * g + r) * OP + 16 * tb + l16] = acc[ob][tb][r];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const floatx4 v = *reinterpret_cast<const floatx4*>(ow + (4 * i + g) * OP + 4 * l16);
+                *reinterpret_cast<floatx4*>(yb + (size_t)(o0 + 16 * ob + 4 * i + g) * Tout + t0 + 4 * l16) = v;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    } else {
+#pragma unroll
+        for (int ob = 0; ob < OB; ++ob)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = o0 + ob * 16 + 4 * g + r;
+                if (o >= O) continue;
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const int t = t0 + tb * 16 + l16;
+                    if (t < Tout) yb[(size_t)o * Tout + t] = acc[ob][tb][r];
+                }
+            }
+    }
+}
+
+#ifndef FCONV_CFG_TALL
+#define FCONV_CFG_TALL 4, 4, 8, 1, 64, 9, 4
+#endif
+using DwTall9 = DwsepCfg<FCONV_CFG_TALL>;
+using DwTallK = DwsepCfg<4, 4, 8, 1, 64, 0, 4>;
+
+static constexpr size_t kTallLds =
+    ((size_t)DwTall9::CC * 128 +
+     (size_t)(DwTall9::TT * DwTall9::CCP > DwTall9::NW * 16 * 68 ? DwTall9::TT * DwTall9::CCP
+                                                                 : DwTall9::NW * 16 * 68) +
+     (size_t)DwTall9::NW * 64 + (size_t)DwTall9::CC * 9) *
+    sizeof(float);
+
 // ---------------------------------------------------------------- dense-fused variant
 
 // The l2_p7 trace's dense-fused form: one convolution with the combined
@@ -420,10 +670,28 @@ static hipError_t launch_dw(const DwsepShape& s, const float* x, const float* w_
     return hipGetLastError();
 }
 
+template <class Cfg>
+static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
+                              const float* b_pw, float* y, hipStream_t stream) {
+    hipError_t e = hipFuncSetAttribute((const void*)dwsep_tall_kernel<Cfg>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTallLds);
+    if (e != hipSuccess) return e;
+    dim3 grid((s.Tout + Cfg::TT - 1) / Cfg::TT, (s.O + Cfg::OT - 1) / Cfg::OT, s.B);
+    const int vec_out = (s.Tout % 4 == 0) && ((uintptr_t)y % 16 == 0);
+    hipLaunchKernelGGL(dwsep_tall_kernel<Cfg>, grid, dim3(Cfg::NT), kTallLds, stream, x, w_dw, w_pw, b_pw, y, s.C,
+                       s.T, s.K, s.O, s.pad, s.Tout, vec_out);
+    return hipGetLastError();
+}
+
 // The instance a shape runs on: 0 = none fits, 1 = wide K=9, 2 = wide
-// runtime-K, 3 = narrow runtime-K, 4 = small runtime-K.
-static int pick_dw(const DwsepShape& s) {
+// runtime-K, 3 = narrow runtime-K, 4 = small runtime-K, 5 = tall K=9,
+// 6 = tall runtime-K.  The tall tile needs 16-byte weight loads (C a
+// multiple of 4 and an aligned w_pw), which the caller states in vec_ok.
+static int pick_dw(const DwsepShape& s, bool vec_ok) {
     const bool unit = s.stride == 1 && s.dil == 1;
+#ifndef FCONV_DW_NO_TALL
+    if (unit && vec_ok && s.O > 256 && s.K <= 65 && s.C % 4 == 0) return s.K == 9 ? 5 : 6;
+#endif
     if (s.O > 64) {
         if (unit && s.K == 9) return 1;
         if (dw_lds_bytes<DwWideK>(s) <= kDwLdsLimit) return 2;
@@ -435,15 +703,17 @@ static int pick_dw(const DwsepShape& s) {
     return 0;
 }
 
-bool dwsep_supported(const DwsepShape& s) { return pick_dw(s) != 0; }
+bool dwsep_supported(const DwsepShape& s) { return pick_dw(s, false) != 0; }
 
 hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                         const float* b_pw, float* y, hipStream_t stream) {
-    switch (pick_dw(s)) {
+    switch (pick_dw(s, (uintptr_t)w_pw % 16 == 0)) {
         case 1: return launch_dw<DwWide9>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 2: return launch_dw<DwWideK>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 3: return launch_dw<DwNarrowK>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 4: return launch_dw<DwSmallK>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 5: return launch_tall<DwTall9>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 6: return launch_tall<DwTallK>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

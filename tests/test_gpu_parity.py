@@ -228,6 +228,42 @@ def test_dwsep_small(fc, shape):
     assert_close(got, want, f"y {shape}")
 
 
+TALL_DW = [
+    # B, C, T, O, K, pad: O > 256 at stride 1 runs the 512 x 64 tile
+    (2, 200, 130, 520, 9, 4),    # 3 full chunks + an 8-channel chunk (half a group), 2 output tiles
+    (1, 68, 64, 257, 33, 16),    # runtime K, a 4-channel last chunk, one valid row in the 2nd block
+    (1, 64, 100, 300, 65, 32),   # the widest window the tile stages (K = 65)
+    (2, 16, 50, 512, 9, 0),      # a single partial chunk, T < 64, no padding
+    (1, 32, 70, 300, 1, 0),      # 1-tap depthwise
+    (1, 44, 200, 1100, 3, 1),    # three output tiles, C not a multiple of 16
+]
+
+
+@pytest.mark.parametrize("shape", TALL_DW)
+def test_dwsep_tall_tile(fc, shape):
+    B, C, T, O, K, pad = shape
+    announce(f"dwsep tall tile {shape}")
+    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=13)
+    want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad)
+    got = fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad).cpu().numpy()
+    assert_close(got, want, f"y {shape}")
+
+
+def test_dwsep_tall_tile_inf_in_next_row(fc):
+    # Padded channels of a partial group must form no product: an infinite
+    # weight in row o+1 may not reach row o.
+    announce("dwsep tall tile, inf weight next to a partial group")
+    B, C, T, O, K, pad = 1, 36, 64, 300, 9, 4
+    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=14)
+    w_pw = w_pw.copy()
+    w_pw[101, 0] = np.inf
+    got = fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad).cpu().numpy()
+    rows = [o for o in range(O) if o != 101]
+    want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad)
+    assert np.isfinite(got[:, rows]).all()
+    assert_close(got[:, rows], want[:, rows], "finite rows")
+
+
 STRIDED_DW = [
     # B, C, T, O, K, pad, stride, dilation
     (2, 64, 300, 300, 9, 4, 2, 1),     # wide runtime-K instance, stride 2
@@ -288,14 +324,15 @@ def test_dwsep_no_bias_and_torch_shapes(fc):
     assert_close(got, want, "y no bias")
 
 
-def test_dwsep_unaligned_weights(fc):
+@pytest.mark.parametrize("O", [32, 300])
+def test_dwsep_unaligned_weights(fc, O):
     # w_pw starting 4 bytes past a 16-byte boundary takes the scalar weight path.
-    announce("dwsep unaligned w_pw")
-    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(1, 32, 64, 32, 9, seed=9)
+    announce(f"dwsep unaligned w_pw, O={O}")
+    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(1, 32, 64, O, 9, seed=9)
     want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, 4)
     buf = torch.zeros(w_pw.size + 1, device="cuda")
     buf[1:] = dev(w_pw).reshape(-1)
-    wp = buf[1:].view(32, 32)
+    wp = buf[1:].view(O, 32)
     got = fc.dwsep_conv1d(dev(x), dev(w_dw), wp, dev(b_pw), 4).cpu().numpy()
     assert_close(got, want, "y unaligned")
 
