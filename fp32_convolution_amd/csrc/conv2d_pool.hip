@@ -402,14 +402,6 @@ struct BoxLayout {
     static_assert(Cfg::WPOS == 1, "box-sum waves split output channels only");
 };
 
-__device__ __forceinline__ int xcd_spread(int bid, int n) {
-    // Inverse of the round-robin deal of block ids to 8 XCDs: XCD k's blocks
-    // (bid % 8 == k) get the k-th contiguous share of the logical ids.
-    const int per = n / 8, rem = n % 8;
-    const int xcd = bid % 8, idx = bid / 8;
-    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-}
-
 template <class Cfg, int MODE>
 __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,

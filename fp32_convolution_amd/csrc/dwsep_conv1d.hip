@@ -273,15 +273,15 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 // The accumulators start at the bias.  Epilogue: each wave transposes its
 // 64 x 64 block through LDS, 16 rows at a time, and writes rows of 64 steps
 // with 16-byte stores; ragged tiles store element by element.
-// Depthwise (K = 9 instance): lane (dc, dj) makes steps 8dj .. 8dj+7 of the
-// wave's channel dc from 16 staged steps (four 16-byte LDS reads) and the
+// Depthwise (K = 9 instance): lane (dc, dj) = (lane/8, lane%8) makes steps
+// 8dj .. 8dj+7 of the wave's channel dc from 16 staged steps (four 16-byte LDS reads) and the
 // channel's 9 taps (staged in LDS too, so the stage needs no scalar loads,
 // whose out-of-order return would serialize the LDS reads): 8 independent
 // multiply-add chains per lane.  The runtime-K instance has lane t make
 // step t of each of the wave's channels.
-// LDS: xs [CC][128], then Ds: [64][CC+4] for the GEMM operand and
+// LDS: xs [CC][132], then Ds: [64][CC+4] for the GEMM operand and
 // 8 x [16][68] in the epilogue, then the bias [512] and the taps [CC][9]
-// (71.8 KB, two workgroups per CU).  Row r of xs holds input steps
+// (72.9 KB, two workgroups per CU).  Row r of xs holds input steps
 // t0-pad .. t0-pad+127 (two 64-lane runs; steps past the K-1 halo or
 // outside [0, T) load as 0), so K <= 65.
 // Pointwise weights: lane (g, l16) of block ob keeps channels 4g..4g+3 of
@@ -290,12 +290,14 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     const float* __restrict__ x, const float* __restrict__ w_dw, const float* __restrict__ w_pw,
-    const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int Kr, int O, int pad, int Tout,
-    int vec_out) {
+    const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int Kr, int O, int pad, int Tout, int n_tt,
+    int n_ot, int vec_out) {
     constexpr int OB = Cfg::OB, TB = Cfg::TB, CC = Cfg::CC, CCP = Cfg::CCP, CPW = Cfg::CPW;
-    constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = 128, OP = 68;
+    // xs row pitch: 128 staged steps + 4, so that rows of consecutive
+    // channels start 16 bytes apart on the LDS banks
+    constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = 132, OP = 68;
     constexpr int DSF = TT * CCP > NW * 16 * OP ? TT * CCP : NW * 16 * OP;
-    static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && OB == 4 && TB == 4, "8 waves of 64 x 64");
+    static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && OB == 4 && TB == 4, "waves of 64 x 64 along o");
     static_assert(CC % NW == 0 && CC % 16 == 0, "whole rows per wave, whole groups per chunk");
     const int K = Cfg::KC > 0 ? Cfg::KC : Kr;
     const int XW = TT + K - 1;  // input steps the tile reads (<= XP)
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     float* xs = lds;            // [CC][XP]
     float* Ds = lds + CC * XP;  // [TT][CCP]; epilogue: [NW][16][OP]
     float* bs = Ds + DSF;       // [NW][64]: each wave's 64 bias values
-    float* ws = bs + NW * 64;   // [CC][9]: the chunk's depthwise taps (K = 9 instance)
+    float* ws = bs + NW * 64;   // [CC][9], rounded up to whole 64-float runs: the chunk's taps (K = 9)
     auto* xs3 = (__attribute__((address_space(3))) float*)xs;
     auto* bs3 = (__attribute__((address_space(3))) float*)bs;
     auto* ws3 = (__attribute__((address_space(3))) float*)ws;
@@ -315,9 +317,15 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
     const int l16 = lane & 15;
-    const int t0 = blockIdx.x * TT;
-    const int o0 = blockIdx.y * Cfg::OT + wave * 16 * OB;  // this wave's first output channel
-    const float* xb = x + (size_t)blockIdx.z * C * T;
+    // tile = (b * n_ot + ot) * n_tt + tt in launch order.  (Dealing the
+    // tiles to the XCDs in contiguous runs, so that neighbouring time tiles
+    // share an L2 for their halo lines, measured slower.)
+    const int tile = blockIdx.x;
+    const int tq = tile / n_tt;
+    const int bi = tq / n_ot;
+    const int t0 = (tile - tq * n_tt) * TT;
+    const int o0 = (tq - bi * n_ot) * Cfg::OT + wave * 16 * OB;  // this wave's first output channel
+    const float* xb = x + (size_t)bi * C * T;
 
     // 1. staging: per row two LDS-direct loads of 64 consecutive steps; rows
     //    >= C get an empty resource and load 0
@@ -339,11 +347,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
                                                          0);
         }
         if constexpr (Cfg::KC == 9) {
-            // the chunk's taps w_dw[c0 .. c0+CC-1][0..8] are contiguous: 9 runs
-            // of 64 floats (0 past channel C-1)
+            // the chunk's taps w_dw[c0 .. c0+CC-1][0..8] are contiguous: runs of
+            // 64 floats (0 past channel C-1; the ws region is whole runs)
             const int n = min(CC, C - c0) * 9;
             const buf_rsrc rt = make_rsrc(w_dw + (size_t)c0 * 9, n * 4);
-            for (int q = wave; q < 9 * CC / 64; q += NW)
+            for (int q = wave; q < (9 * CC + 63) / 64; q += NW)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, ws3 + 64 * q, 4, (64 * q + lane) * 4, 0, 0, 0);
         }
     };
@@ -394,8 +402,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
         // 2. depthwise -> Ds[t][c] for the wave's CPW channels (channels >= C
         //    read the zero rows staged for them, so their D is 0)
         if constexpr (Cfg::KC == 9) {
-            static_assert(CPW == 8 && 9 * CC % 64 == 0, "8 channels x 8 groups of 8 steps per wave");
-            const int dc = lane & 7, dj = lane >> 3;
+            static_assert(CPW == 8, "8 channels x 8 groups of 8 steps per wave");
+            const int dj = lane & 7, dc = lane >> 3;
             const int c = wave * CPW + dc;
             float xv[16], wv[9];
 #pragma unroll
@@ -432,28 +440,51 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
         }
         __syncthreads();
         if (c0 + CC < C) stage(c0 + CC);
-        // 3. pointwise GEMM over the chunk's 16-channel groups; block ob's
-        //    registers take the next group's weights once its products are
-        //    issued (past the last group these load 0)
+        // 3. pointwise GEMM over the chunk's 16-channel groups.  Block ob's
+        //    weight registers take the next group's weights as soon as its
+        //    16 products are issued (past the last group these load 0); the
+        //    last block runs in two halves of the time blocks, and each
+        //    half's D registers take the next group's D once used.  The
+        //    scheduling fences keep that order: without them the compiler
+        //    moves the next group's first products up against their loads.
+        auto read_d = [&](floatx4& dst, int tb, int s16) {
+            dst = *reinterpret_cast<const floatx4*>(Ds + (tb * 16 + l16) * CCP + s16 + 4 * g);
+        };
+        floatx4 bq[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) read_d(bq[tb], tb, 0);
 #pragma unroll
         for (int s16 = 0; s16 < CC; s16 += 16) {
-            floatx4 bq[TB];
+            const int cb = c0 + s16 + 16;  // first channel of the next group
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
-                bq[tb] = *reinterpret_cast<const floatx4*>(Ds + (tb * 16 + l16) * CCP + s16 + 4 * g);
-#pragma unroll
-            for (int ob = 0; ob < OB; ++ob) {
+            for (int ob = 0; ob < OB - 1; ++ob) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int tb = 0; tb < TB; ++tb) acc[ob][tb] = mfma_16x16x4(a[ob][j], bq[tb][j], acc[ob][tb]);
-                a[ob] = load_pw(ob, c0 + s16 + 16);
+                a[ob] = load_pw(ob, cb);
+                __builtin_amdgcn_sched_barrier(0);
             }
+#pragma unroll
+            for (int h = 0; h < TB; h += 2) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int tb = h; tb < h + 2; ++tb)
+                        acc[OB - 1][tb] = mfma_16x16x4(a[OB - 1][j], bq[tb][j], acc[OB - 1][tb]);
+                if (s16 + 16 < CC) {
+                    read_d(bq[h], h, s16 + 16);
+                    read_d(bq[h + 1], h + 1, s16 + 16);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            a[OB - 1] = load_pw(OB - 1, cb);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     // 4. epilogue: lane (g, l16) holds y[o0 + 16*ob + 4g + r, t0 + 16*tb + l16]
-    float* yb = y + (size_t)blockIdx.z * O * Tout;
+    float* yb = y + (size_t)bi * O * Tout;
     __syncthreads();  // every wave is done reading Ds (outside the branch: o0 differs per wave)
     if (vec_out && o0 + 16 * OB <= O && t0 + TT <= Tout) {
         float* ow = Ds + wave * 16 * OP;
@@ -493,12 +524,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
 using DwTall9 = DwsepCfg<FCONV_CFG_TALL>;
 using DwTallK = DwsepCfg<4, 4, 8, 1, 64, 0, 4>;
 
-static constexpr size_t kTallLds =
-    ((size_t)DwTall9::CC * 128 +
-     (size_t)(DwTall9::TT * DwTall9::CCP > DwTall9::NW * 16 * 68 ? DwTall9::TT * DwTall9::CCP
-                                                                 : DwTall9::NW * 16 * 68) +
-     (size_t)DwTall9::NW * 64 + (size_t)DwTall9::CC * 9) *
-    sizeof(float);
+template <class Cfg>
+static constexpr size_t tall_lds_bytes() {
+    constexpr size_t ds = (size_t)(Cfg::TT * Cfg::CCP > Cfg::NW * 16 * 68 ? Cfg::TT * Cfg::CCP : Cfg::NW * 16 * 68);
+    return ((size_t)Cfg::CC * 132 + ds + (size_t)Cfg::NW * 64 + (size_t)(9 * Cfg::CC + 63) / 64 * 64) * sizeof(float);
+}
+
 
 // ---------------------------------------------------------------- dense-fused variant
 
@@ -670,16 +701,25 @@ static hipError_t launch_dw(const DwsepShape& s, const float* x, const float* w_
     return hipGetLastError();
 }
 
+// The tall kernel's 1-D grid holds every (time tile, output tile, item).
+static bool tall_tiles_fit(const DwsepShape& s) {
+    const int ot = DwTall9::OT < DwTallK::OT ? DwTall9::OT : DwTallK::OT;
+    const long n = (long)((s.Tout + 63) / 64) * ((s.O + ot - 1) / ot) * s.B;
+    return n <= 0x7fffffffL;
+}
+
 template <class Cfg>
 static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                               const float* b_pw, float* y, hipStream_t stream) {
+    constexpr size_t lds = tall_lds_bytes<Cfg>();
     hipError_t e = hipFuncSetAttribute((const void*)dwsep_tall_kernel<Cfg>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTallLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    dim3 grid((s.Tout + Cfg::TT - 1) / Cfg::TT, (s.O + Cfg::OT - 1) / Cfg::OT, s.B);
+    const int n_tt = (s.Tout + Cfg::TT - 1) / Cfg::TT, n_ot = (s.O + Cfg::OT - 1) / Cfg::OT;
+    const int n_tiles = n_tt * n_ot * s.B;  // < 2^31: checked by tall_tiles_fit
     const int vec_out = (s.Tout % 4 == 0) && ((uintptr_t)y % 16 == 0);
-    hipLaunchKernelGGL(dwsep_tall_kernel<Cfg>, grid, dim3(Cfg::NT), kTallLds, stream, x, w_dw, w_pw, b_pw, y, s.C,
-                       s.T, s.K, s.O, s.pad, s.Tout, vec_out);
+    hipLaunchKernelGGL(dwsep_tall_kernel<Cfg>, dim3(n_tiles), dim3(Cfg::NT), lds, stream, x, w_dw, w_pw, b_pw,
+                       y, s.C, s.T, s.K, s.O, s.pad, s.Tout, n_tt, n_ot, vec_out);
     return hipGetLastError();
 }
 
@@ -690,7 +730,7 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 static int pick_dw(const DwsepShape& s, bool vec_ok) {
     const bool unit = s.stride == 1 && s.dil == 1;
 #ifndef FCONV_DW_NO_TALL
-    if (unit && vec_ok && s.O > 256 && s.K <= 65 && s.C % 4 == 0) return s.K == 9 ? 5 : 6;
+    if (unit && vec_ok && s.O > 256 && s.K <= 65 && s.C % 4 == 0 && tall_tiles_fit(s)) return s.K == 9 ? 5 : 6;
 #endif
     if (s.O > 64) {
         if (unit && s.K == 9) return 1;

@@ -59,4 +59,16 @@ __device__ __forceinline__ float block_sum(float v, float* red /* NWAVES floats 
 // saturating to 0 or 1 (never NaN) for large |a|.
 __device__ __forceinline__ float logistic(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
+// Block order for 8 XCDs.  The hardware deals consecutive block ids to the
+// XCDs round-robin; this maps a block id to a logical tile id so that each
+// XCD gets one contiguous run of tiles (neighbouring tiles then share that
+// XCD's L2).  A bijection on [0, n).
+__device__ __forceinline__ int xcd_spread(int bid, int n) {
+    // Inverse of the round-robin deal of block ids to 8 XCDs: XCD k's blocks
+    // (bid % 8 == k) get the k-th contiguous share of the logical ids.
+    const int per = n / 8, rem = n % 8;
+    const int xcd = bid % 8, idx = bid / 8;
+    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
 }  // namespace fconv
