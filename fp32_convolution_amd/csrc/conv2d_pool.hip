@@ -600,6 +600,228 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
     }
 }
 
+// ---------------------------------------------------------------- box-sum, K = 3, s = 4, one pooled column per lane
+
+// The box-sum identity above, arranged for K = 3 < s = 4.  The 6 x 6 input
+// windows of neighbouring pooled outputs overlap by two rows and columns,
+// and each pooled output needs exactly 9 box sums per channel:
+//     Sx[ic][ky][kx] at (4ph + ky, 4pw + kx), ky, kx < 3.
+// Lane l owns pooled column pw0 + l.  One 16-byte load gives it input
+// columns 4pw .. 4pw+3 of a row; the next two columns are the next lane's
+// first two, read through DPP wave_shl:1 inside the adds (lane TPW only
+// supplies them).  Per input row, 7 adds give the three horizontal 4-sums:
+//     h0 = (x0+x1) + (x2+x3),  h1 = (x1+x2) + (x3+n0),  h2 = (x2+x3) + (n0+n1);
+// per pooled row, 7-8 adds per kx give the three vertical 4-sums, pairwise
+// too.  The 9 values go to LDS as Sx[ic][ph][pw][12] (taps 0..8, 16-byte
+// aligned rows), which the contraction reads as B operands: three LDS
+// reads per 9 MFMA steps.  Compared with the general box-sum kernel this
+// computes only the box sums the pooled outputs use (9 of every 16) and
+// issues about half the vector instructions per output.
+// Workgroup: one batch item, TPH = 2 pooled rows x TPW = 48 pooled columns,
+// 64 output channels (4 waves x 16).  Wave w makes the box sums of channels
+// w, w+4, ...; k-slot g of contraction step (m, tap) is channel 4m + g at
+// tap (ky, kx) = (tap / 3, tap % 3), so lane group g reads one channel's 9
+// taps.  Requires W % 4 == 0 (a 16-byte column group is all in or all out
+// of the row); VEC selects 16-byte loads (x 16-byte aligned) or four 4-byte
+// loads.
+struct Box4 {
+    static constexpr int K = 3, S = 4, TPH = 2, TPW = 48, NW = 4, NT = 256, TP = 12;
+    static constexpr int IR = TPH * S + K - 1;  // input rows a tile reads: 10
+    static constexpr int CO_RANGE = NW * 16;
+};
+
+template <int MODE, bool VEC>
+__global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int tiles_w,
+    int tiles_per_item, int co_ranges, int nblocks) {
+    constexpr int S = Box4::S, TPH = Box4::TPH, TPW = Box4::TPW, NW = Box4::NW, TP = Box4::TP, IR = Box4::IR;
+    extern __shared__ float lds[];  // Sx [4*CINQ][TPH][TPW][TP]
+    __shared__ float red[NW];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lid = xcd_spread(blockIdx.x, nblocks);
+    const int tile = lid % tiles_per_item;
+    const int cr = (lid / tiles_per_item) % co_ranges;
+    const int b = lid / (tiles_per_item * co_ranges);
+    const int tile_y = tile / tiles_w, tile_x = tile - (tile / tiles_w) * tiles_w;
+    const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
+    const int y0 = ph0 * S, x0 = pw0 * S;
+    const int g = lane >> 4, l16 = lane & 15;
+
+    // 1. box sums of channels wave, wave + NW, ... (channels >= Cin load 0)
+    {
+        const float* xb = x + (size_t)b * Cin * H * W;
+        const int xc = x0 + 4 * lane;
+        const int coff = (lane <= TPW && xc < W) ? xc * 4 : kBufOOB;
+        auto load_rows = [&](floatx4 (&v)[IR], int ic) {
+#pragma unroll
+            for (int r = 0; r < IR; ++r) {
+                const bool ok = ic < Cin && y0 + r < H;
+                const buf_rsrc rr = make_rsrc(xb + (ok ? ((size_t)ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
+                if constexpr (VEC) {
+                    v[r] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rr, coff, 0, 0));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[r][j] = buf_load_f32(rr, coff + 4 * j);
+                }
+            }
+        };
+        // the value of lane + 1 (0 in lane 63)
+        auto next_lane = [](float v) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF,
+                                                                         true));
+        };
+        floatx4 v[IR];
+        load_rows(v, wave);
+        for (int i = 0; i < CINQ; ++i) {
+            const int ic = wave + NW * i;
+            float hs[IR][3];
+#pragma unroll
+            for (int r = 0; r < IR; ++r) {
+                const float p01 = v[r][0] + v[r][1], p23 = v[r][2] + v[r][3];
+                hs[r][0] = p01 + p23;
+                hs[r][1] = (v[r][1] + v[r][2]) + (next_lane(v[r][0]) + v[r][3]);
+                hs[r][2] = next_lane(p01) + p23;
+            }
+            if (i + 1 < CINQ) load_rows(v, ic + NW);
+            float* sp = lds + ((size_t)ic * TPH * TPW + lane) * TP;
+#pragma unroll
+            for (int ph = 0; ph < TPH; ++ph) {
+                const int R = ph * S;
+                float sx[9];
+#pragma unroll
+                for (int kx = 0; kx < 3; ++kx) {
+                    const float q23 = hs[R + 2][kx] + hs[R + 3][kx];
+                    sx[kx] = (hs[R][kx] + hs[R + 1][kx]) + q23;
+                    sx[3 + kx] = (hs[R + 1][kx] + hs[R + 2][kx]) + (hs[R + 3][kx] + hs[R + 4][kx]);
+                    sx[6 + kx] = q23 + (hs[R + 4][kx] + hs[R + 5][kx]);
+                }
+                if (lane < TPW) {
+                    float* q = sp + (size_t)ph * TPW * TP;
+                    *reinterpret_cast<floatx4*>(q) = floatx4{sx[0], sx[1], sx[2], sx[3]};
+                    *reinterpret_cast<floatx4*>(q + 4) = floatx4{sx[4], sx[5], sx[6], sx[7]};
+                    q[8] = sx[8];
+                }
+            }
+        }
+    }
+
+    // weights and bias while the box sums finish: A of step (m, tap) for lane
+    // (g, l16) is w[co][4m + g][tap], co = this wave's channel l16
+    const int co_a = cr * Box4::CO_RANGE + wave * 16 + l16;
+    const buf_rsrc rw = make_rsrc(w, Cout * Cin * 9 * 4);
+    auto load_a = [&](float (&a)[9], int m) {
+        const int ic = 4 * m + g;
+        const int base = (co_a < Cout && ic < Cin && m < CINQ) ? (co_a * Cin + ic) * 36 : kBufOOB;
+#pragma unroll
+        for (int t = 0; t < 9; ++t) a[t] = buf_load_f32(rw, base + 4 * t);
+    };
+    float a_cur[9], a_nxt[9];
+    load_a(a_cur, 0);
+    const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
+    float bco[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int co = cr * Box4::CO_RANGE + wave * 16 + 4 * g + r;
+        bco[r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
+    }
+    __syncthreads();
+
+    // 2. contraction over (channel, tap): 6 blocks of 16 positions
+    constexpr int NB = TPH * TPW / 16;
+    floatx4 acc[NB];
+#pragma unroll
+    for (int p = 0; p < NB; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < CINQ; ++m) {
+        load_a(a_nxt, m + 1);
+        const float* cb = lds + (size_t)(4 * m + g) * TPH * TPW * TP;
+#pragma unroll
+        for (int p = 0; p < NB; ++p) {
+            const float* q = cb + ((p / 3) * TPW + (p % 3) * 16 + l16) * TP;
+            const floatx4 t0 = *reinterpret_cast<const floatx4*>(q);
+            const floatx4 t1 = *reinterpret_cast<const floatx4*>(q + 4);
+            const float t8 = q[8];
+            const float t[9] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3], t8};
+#pragma unroll
+            for (int k = 0; k < 9; ++k) acc[p] = mfma_16x16x4(a_cur[k], t[k], acc[p]);
+        }
+#pragma unroll
+        for (int k = 0; k < 9; ++k) a_cur[k] = a_nxt[k];
+    }
+
+    // Epilogue: lane (g, l16) of block p holds the window sum of channel
+    // co = ... + 4g + r at pooled position (p / 3, (p % 3) * 16 + l16).
+    const float inv = 1.0f / (float)(S * S);
+    float lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int co = cr * Box4::CO_RANGE + wave * 16 + 4 * g + r;
+#pragma unroll
+        for (int p = 0; p < NB; ++p) {
+            const int ph = ph0 + p / 3, pw = pw0 + (p % 3) * 16 + l16;
+            if (co < Cout && ph < PH && pw < PW) {
+                const float avg = acc[p][r] * inv + bco[r];
+                if constexpr (MODE == OUT_MAP)
+                    dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
+                else
+                    lsum += logistic(avg);
+            }
+        }
+    }
+    if constexpr (MODE != OUT_MAP) {
+        const float sum = block_sum<NW>(lsum, red);
+        if (tid == 0) {
+            if constexpr (MODE == OUT_SUM_ATOMIC)
+                atomicAdd(dst + b, sum);
+            else
+                dst[(size_t)b * (tiles_per_item * co_ranges) + cr * tiles_per_item + tile] = sum;
+        }
+    }
+}
+
+static size_t box4_lds_bytes(int Cin) {
+    return (size_t)4 * ((Cin + 3) / 4) * Box4::TPH * Box4::TPW * Box4::TP * sizeof(float);
+}
+
+// The K = 3, s = 4 shapes the one-column-per-lane kernel takes (by shape
+// alone, so that the deterministic form's workspace size does not depend on
+// pointer alignment).
+static bool box4_fits(const Conv2dShape& s) {
+    return s.K == 3 && s.S == 4 && s.W % 4 == 0 && box4_lds_bytes(s.Cin) <= kMaxLds;
+}
+
+template <bool VEC>
+struct Box4Launch {
+    template <int MODE>
+    static constexpr auto kernel = conv2d_pool_boxsum4_kernel<MODE, VEC>;
+};
+
+static int64_t box4_parts(const Conv2dShape& s) {
+    const int tiles = ((s.PH + Box4::TPH - 1) / Box4::TPH) * ((s.PW + Box4::TPW - 1) / Box4::TPW);
+    return (int64_t)tiles * ((s.Cout + Box4::CO_RANGE - 1) / Box4::CO_RANGE);
+}
+
+static hipError_t launch_box4(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                              int mode, hipStream_t stream) {
+    const int CINQ = (s.Cin + 3) / 4;
+    const size_t lds = box4_lds_bytes(s.Cin);
+    const int tiles_w = (s.PW + Box4::TPW - 1) / Box4::TPW;
+    const int tiles = ((s.PH + Box4::TPH - 1) / Box4::TPH) * tiles_w;
+    const int co_ranges = (s.Cout + Box4::CO_RANGE - 1) / Box4::CO_RANGE;
+    const long nblocks_l = (long)tiles * co_ranges * s.B;
+    if (nblocks_l > INT32_MAX) return hipErrorInvalidValue;
+    const int nblocks = (int)nblocks_l;
+    if ((uintptr_t)x % 16 == 0) {
+        FCONV_LAUNCH_MODES(Box4Launch<true>::template kernel, dim3(nblocks), dim3(Box4::NT), lds, stream, x, w, bias,
+                           dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
+    } else {
+        FCONV_LAUNCH_MODES(Box4Launch<false>::template kernel, dim3(nblocks), dim3(Box4::NT), lds, stream, x, w,
+                           bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
+    }
+}
+
 // Instances: K3/s4 4x16 tile with 4 waves x 16 channels; K5/s3 4x12 tile
 // with 8 waves x 16 channels.
 #ifndef FCONV_CFG_BOX_K3S4
@@ -660,6 +882,9 @@ static hipError_t launch_box(const Conv2dShape& s, const float* x, const float* 
 
 hipError_t conv2d_boxsum_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
                                 float* dst, int mode, hipStream_t stream) {
+#ifndef FCONV_NO_BOX4
+    if (box4_fits(s)) return launch_box4(s, x, w, bias, dst, mode, stream);
+#endif
     if (s.K == 3 && s.S == 4) return launch_box<BoxK3S4>(s, x, w, bias, dst, mode, stream);
     if (s.K == 5 && s.S == 3) return launch_box<BoxK5S3>(s, x, w, bias, dst, mode, stream);
     if (s.K == 3 && s.S == 2) return launch_box<BoxK3S2>(s, x, w, bias, dst, mode, stream);
@@ -668,6 +893,9 @@ hipError_t conv2d_boxsum_launch(const Conv2dShape& s, const float* x, const floa
 }
 
 int64_t conv2d_boxsum_parts(const Conv2dShape& s) {
+#ifndef FCONV_NO_BOX4
+    if (box4_fits(s)) return box4_parts(s);
+#endif
     if (s.K == 3 && s.S == 4) return box_parts<BoxK3S4>(s);
     if (s.K == 5 && s.S == 3) return box_parts<BoxK5S3>(s);
     if (s.K == 3 && s.S == 2) return box_parts<BoxK3S2>(s);

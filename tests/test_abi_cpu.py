@@ -93,8 +93,10 @@ def test_det_workspace_query(lib):
 
     # direct MFMA on x[128,8,384,384], 4x16 pooled tiles of a 95x95 map: 24*6 workgroups per item
     assert fc.conv2d_det_workspace_bytes(128, 8, 384, 384, 64, 3, 4, algo=1) == 128 * 24 * 6 * 4
-    # box-sum uses the same tiles; the simple path one workgroup per 256 pooled values of an item
-    assert fc.conv2d_det_workspace_bytes(128, 8, 384, 384, 64, 3, 4, algo=3) == 128 * 24 * 6 * 4
+    # box-sum (K = 3, s = 4, W % 4 == 0) has 2 x 48 pooled tiles: 48 * 2 per item; with W % 4 != 0 it
+    # uses the direct kernel's tiles; the simple path one workgroup per 256 pooled values of an item
+    assert fc.conv2d_det_workspace_bytes(128, 8, 384, 384, 64, 3, 4, algo=3) == 128 * 48 * 2 * 4
+    assert fc.conv2d_det_workspace_bytes(128, 8, 383, 383, 64, 3, 4, algo=3) == 128 * 24 * 6 * 4
     assert fc.conv2d_det_workspace_bytes(2, 3, 16, 16, 4, 3, 4, algo=2) == 2 * 1 * 4
     assert fc.conv2d_det_workspace_bytes(3, 2, 5, 9, 4, 3, 4) == 0          # empty pooled map
     n = ctypes.c_size_t()

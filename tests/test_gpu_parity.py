@@ -91,6 +91,39 @@ def test_conv2d_small(fc, shape, algo):
     assert_close(got_out, want_out, f"out {shape}")
 
 
+BOX4_CONV = [
+    # B, Cin, H, W, Cout, K=3, s=4 with W % 4 == 0: the one-column-per-lane box-sum kernel
+    (2, 8, 70, 76, 64, 3, 4),       # odd number of pooled rows (17), one column tile
+    (1, 12, 30, 200, 20, 3, 4),     # 3 channel quads, 49 pooled columns: a 1-column second tile
+    (2, 5, 41, 100, 70, 3, 4),      # Cin not a multiple of 4, two output-channel ranges
+    (1, 8, 11, 16, 4, 3, 4),        # PH = 2, PW = 3
+    (1, 3, 6, 8, 4, 3, 4),          # PH = PW = 1: one window
+]
+
+
+@pytest.mark.parametrize("shape", BOX4_CONV)
+@pytest.mark.parametrize("aligned", [True, False])
+def test_conv2d_boxsum_one_column_per_lane(fc, shape, aligned):
+    # aligned=False starts x 4 bytes past a 16-byte boundary (4-byte loads)
+    B, Cin, H, W, Cout, K, s = shape
+    announce(f"conv2d box-sum, a pooled column per lane {shape} aligned={aligned}")
+    x, w, b = fi.conv2d_inputs(B, Cin, H, W, Cout, K, seed=21)
+    if aligned:
+        xd = dev(x)
+    else:
+        buf = torch.zeros(x.size + 1, device="cuda")
+        buf[1:] = dev(x).reshape(-1)
+        xd = buf[1:].view(*x.shape)
+    wd, bd = dev(w), dev(b)
+    want_out, want_map = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, want_pooled=True)
+    got_map = fc.conv2d_pool_map(xd, wd, bd, s, algo=3).cpu().numpy()
+    got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=3).cpu().numpy()
+    det = fc.conv2d_pool_sigmoid_sum_det(xd, wd, bd, s, algo=3).cpu().numpy()
+    assert_close(got_map, want_map, f"pooled map {shape}")
+    assert_close(got_out, want_out, f"out {shape}")
+    assert_close(det, want_out, f"deterministic out {shape}")
+
+
 @pytest.mark.parametrize("algo", [1, 3])
 def test_conv2d_no_bias(fc, algo):
     announce(f"conv2d no bias algo={algo}")
