@@ -44,7 +44,7 @@ KERNEL_SOURCES = {
                                 "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_tall_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                           "fp32_convolution_amd/csrc/fconv_device.hpp"],
-    "conv2d_pool_boxsum_kernel": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
+    "conv2d_pool_boxsum4_kernel": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
                                   "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_dense_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                            "fp32_convolution_amd/csrc/fconv_device.hpp"],
@@ -334,7 +334,7 @@ def main():
              "hbm_gbps_algorithmic": round(b_conv / (mb * 1e-3) / 1e9, 1),
              "roofline": {"bound": "hbm", "achieved": round(b_conv / (mb * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                           "unit": "GB/s", "frac": round(b_conv / (mb * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                          "traffic": measured_traffic("conv2d_pool_boxsum_kernel")},
+                          "traffic": measured_traffic("conv2d_pool_boxsum4_kernel")},
              "speedup_vs_direct": round(k_conv["ms_mean"] / mb, 2),
              "matches_direct_within_tol": bool(
                  ((out_box - out).abs() <= 1e-4 + 1e-4 * out.abs()).all().item())}

@@ -671,7 +671,7 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
         // the value of lane + 1 (0 in lane 63)
         auto next_lane = [](float v) {
             return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF,
-                                                                         true));
+                                                                         false));
         };
         floatx4 v[IR];
         load_rows(v, wave);
@@ -729,13 +729,13 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
     }
     __syncthreads();
 
-    // 2. contraction over (channel, tap): 6 blocks of 16 positions
+    // 2. contraction over (channel, tap): 6 blocks of 16 positions.  The
+    //    first channel quad starts the accumulators from 0 inside the first
+    //    MFMA, and the quads run in pairs so that the weight registers
+    //    alternate without copies.
     constexpr int NB = TPH * TPW / 16;
     floatx4 acc[NB];
-#pragma unroll
-    for (int p = 0; p < NB; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int m = 0; m < CINQ; ++m) {
-        load_a(a_nxt, m + 1);
+    auto quad = [&](const float (&a)[9], int m, bool first) {
         const float* cb = lds + (size_t)(4 * m + g) * TPH * TPW * TP;
 #pragma unroll
         for (int p = 0; p < NB; ++p) {
@@ -744,39 +744,71 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
             const floatx4 t1 = *reinterpret_cast<const floatx4*>(q + 4);
             const float t8 = q[8];
             const float t[9] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3], t8};
+            acc[p] = mfma_16x16x4(a[0], t[0], first ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[p]);
 #pragma unroll
-            for (int k = 0; k < 9; ++k) acc[p] = mfma_16x16x4(a_cur[k], t[k], acc[p]);
+            for (int k = 1; k < 9; ++k) acc[p] = mfma_16x16x4(a[k], t[k], acc[p]);
         }
-#pragma unroll
-        for (int k = 0; k < 9; ++k) a_cur[k] = a_nxt[k];
+    };
+    load_a(a_nxt, 1);
+    quad(a_cur, 0, true);
+    for (int m = 1; m < CINQ; m += 2) {
+        load_a(a_cur, m + 1);
+        quad(a_nxt, m, false);
+        if (m + 1 < CINQ) {
+            load_a(a_nxt, m + 2);
+            quad(a_cur, m + 1, false);
+        }
     }
 
     // Epilogue: lane (g, l16) of block p holds the window sum of channel
     // co = ... + 4g + r at pooled position (p / 3, (p % 3) * 16 + l16).
+    // sigma(sum / s^2 + bias) = 1 / (1 + 2^(sum * c1 + c0[r])), with the
+    // scale, the bias and -log2(e) folded into one multiply-add.
     const float inv = 1.0f / (float)(S * S);
+    constexpr float kNegLog2e = -1.4426950408889634f;
     float lsum = 0.f;
+    const int co_w = cr * Box4::CO_RANGE + wave * 16;  // this wave's first output channel
+    if constexpr (MODE != OUT_MAP) {
+        if (co_w + 16 <= Cout && ph0 + TPH <= PH && pw0 + TPW <= PW) {
+            // every output of the wave is in range
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int co = cr * Box4::CO_RANGE + wave * 16 + 4 * g + r;
+            for (int r = 0; r < 4; ++r) {
+                const float c0 = bco[r] * kNegLog2e;
 #pragma unroll
-        for (int p = 0; p < NB; ++p) {
-            const int ph = ph0 + p / 3, pw = pw0 + (p % 3) * 16 + l16;
-            if (co < Cout && ph < PH && pw < PW) {
-                const float avg = acc[p][r] * inv + bco[r];
-                if constexpr (MODE == OUT_MAP)
-                    dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
-                else
-                    lsum += logistic(avg);
+                for (int p = 0; p < NB; ++p)
+                    lsum += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(acc[p][r], inv * kNegLog2e, c0)));
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = co_w + 4 * g + r;
+                const float c0 = bco[r] * kNegLog2e;
+#pragma unroll
+                for (int p = 0; p < NB; ++p) {
+                    const int ph = ph0 + p / 3, pw = pw0 + (p % 3) * 16 + l16;
+                    const float v =
+                        __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(acc[p][r], inv * kNegLog2e, c0)));
+                    lsum += (co < Cout && ph < PH && pw < PW) ? v : 0.f;
+                }
             }
         }
-    }
-    if constexpr (MODE != OUT_MAP) {
         const float sum = block_sum<NW>(lsum, red);
         if (tid == 0) {
             if constexpr (MODE == OUT_SUM_ATOMIC)
                 atomicAdd(dst + b, sum);
             else
                 dst[(size_t)b * (tiles_per_item * co_ranges) + cr * tiles_per_item + tile] = sum;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int co = co_w + 4 * g + r;
+#pragma unroll
+            for (int p = 0; p < NB; ++p) {
+                const int ph = ph0 + p / 3, pw = pw0 + (p % 3) * 16 + l16;
+                if (co < Cout && ph < PH && pw < PW)
+                    dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = acc[p][r] * inv + bco[r];
+            }
         }
     }
 }
