@@ -409,6 +409,12 @@ def main():
         "wall_s_timed_region": round(t_wall, 3),
     }
 
+    props = torch.cuda.get_device_properties(dev)
+    result["device"] = {"name": props.name, "hip": getattr(torch.version, "hip", None),
+                        "gcn_arch": getattr(props, "gcnArchName", None),
+                        "compute_units": props.multi_processor_count,
+                        "clock_mhz": round(getattr(props, "clock_rate", 0) / 1000.0) or None}
+
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(conv_in, dw_in, out.cpu().numpy().astype(np.float64),
                                     y.cpu().numpy().astype(np.float64), args.cpu_conv_items, args.cpu_dw_items)
@@ -418,6 +424,9 @@ def main():
         result["cpu_baseline"] = None
 
     print(json.dumps(result), flush=True)
+    # the oracle leg's parity check on the timed results decides the exit status
+    if result.get("parity_sample") and not result["parity_sample"]["ok"]:
+        sys.exit(3)
 
 
 if __name__ == "__main__":
