@@ -6,6 +6,8 @@ HIP library never calls it and shares no code with it.
 """
 
 from .oracle import (  # noqa: F401
+    POOL_AVG,
+    POOL_MAX,
     conv2d_pool_sigmoid_sum,
     conv2d_pooled_at,
     conv2d_sizes,

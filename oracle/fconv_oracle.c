@@ -16,12 +16,21 @@
  *   [P7]  POPCORNBENCH reasoning trace "Kimi-K2.6 l2_p7" (depthwise-separable
  *         Conv1d): the opening problem statement (output length formula) and
  *         the per-output formula out[b,o,t] = sum_c (sum_k in*dw) * pw + bias.
+ *   [NEWS] the 新智元 article on the Stanford CRFM kernels: its list of fused
+ *         operators includes Conv2D + ReLU + MaxPool, the model for the
+ *         pooling generalisation (optional ReLU after the conv, max pooling).
  *
  * Readings taken where the pages leave a step open (listed again in the
  * design notes): AvgPool2d uses stride = kernel, padding 0 and floor mode,
  * divisor s*s; Conv2d is PyTorch's cross-correlation (no flip), stride 1, no
  * padding; sigmoid is the logistic 1/(1+exp(-a)); the depthwise stage has no
  * bias of its own; padding is zero padding; stride and dilation are 1.
+ * The pooling generalisation follows PyTorch's AvgPool2d / MaxPool2d with
+ * kernel = stride = s and no padding: ceil mode adds a last, partial window
+ * when the conv map does not divide evenly (it must start inside the map);
+ * a partial window averages over the conv outputs it covers, and takes
+ * their maximum for max pooling; ReLU, when asked for, acts on the conv
+ * outputs (bias included) before pooling.
  *
  * Every function here is a literal transcription of the definition: the
  * conv map is materialised in full, then pooled, then passed through the
@@ -107,19 +116,29 @@ static double logistic(double a) { return 1.0 / (1.0 + exp(-a)); }
 
 /* Output sizes.  [P65] opening dimension walk-through: a valid (unpadded)
  * stride-1 Conv2d of kernel K gives H-K+1; AvgPool2d(s) with its default
- * stride s and floor mode gives floor((H-K+1)/s). */
-int oracle_conv2d_sizes(long H, long W, long K, long pool, long *Hc, long *Wc, long *PH, long *PW) {
+ * stride s and floor mode gives floor((H-K+1)/s).  In ceil mode the count is
+ * rounded up instead (PyTorch's pooling output size; with no padding the
+ * last window always starts inside the conv map, so none is dropped). */
+static long pooled_len(long n, long s, int ceil_mode) { return ceil_mode ? (n + s - 1) / s : n / s; }
+
+int oracle_conv2d_sizes_ex(long H, long W, long K, long pool, int ceil_mode, long *Hc, long *Wc, long *PH,
+                           long *PW) {
     if (H < 1 || W < 1 || K < 1 || pool < 1 || H < K || W < K) return ORACLE_EINVAL;
     *Hc = H - K + 1;
     *Wc = W - K + 1;
-    *PH = *Hc / pool;
-    *PW = *Wc / pool;
+    *PH = pooled_len(*Hc, pool, ceil_mode);
+    *PW = pooled_len(*Wc, pool, ceil_mode);
     return ORACLE_OK;
+}
+
+int oracle_conv2d_sizes(long H, long W, long K, long pool, long *Hc, long *Wc, long *PH, long *PW) {
+    return oracle_conv2d_sizes_ex(H, W, K, pool, 0, Hc, Wc, PH, PW);
 }
 
 typedef struct {
     const float *x, *w, *bias;
     long B, Cin, H, W, Cout, K, pool, Hc, Wc, PH, PW;
+    int pool_mode, relu; /* pool_mode 0: average, 1: maximum */
     const long *batch_idx;
     double *part;   /* [nb*Cout] */
     double *pooled; /* [nb*Cout*PH*PW] or NULL */
@@ -153,15 +172,29 @@ static void conv2d_item(void *vctx, long item, double *M) {
             }
     }
     for (long i = 0; i < Hc * Wc; ++i) M[i] += beta;
+    if (c->relu)
+        for (long i = 0; i < Hc * Wc; ++i) M[i] = M[i] > 0.0 ? M[i] : 0.0;
 
-    /* steps 2-3: floor average pool, sigmoid, sum */
+    /* steps 2-3: pool (each window clipped to the conv map), sigmoid, sum */
     double total = 0.0;
     for (long ph = 0; ph < c->PH; ++ph)
         for (long pw = 0; pw < c->PW; ++pw) {
-            double acc = 0.0;
-            for (long dy = 0; dy < s; ++dy)
-                for (long dx = 0; dx < s; ++dx) acc += M[(ph * s + dy) * Wc + (pw * s + dx)];
-            const double a = acc / (double)(s * s);
+            const long ny = (ph * s + s <= Hc) ? s : Hc - ph * s;
+            const long nx = (pw * s + s <= Wc) ? s : Wc - pw * s;
+            double a;
+            if (c->pool_mode == 1) {
+                a = -INFINITY;
+                for (long dy = 0; dy < ny; ++dy)
+                    for (long dx = 0; dx < nx; ++dx) {
+                        const double v = M[(ph * s + dy) * Wc + (pw * s + dx)];
+                        a = v > a ? v : a;
+                    }
+            } else {
+                double acc = 0.0;
+                for (long dy = 0; dy < ny; ++dy)
+                    for (long dx = 0; dx < nx; ++dx) acc += M[(ph * s + dy) * Wc + (pw * s + dx)];
+                a = acc / (double)(ny * nx);
+            }
             if (c->pooled) c->pooled[((bi * c->Cout + co) * c->PH + ph) * c->PW + pw] = a;
             total += logistic(a);
         }
@@ -169,18 +202,26 @@ static void conv2d_item(void *vctx, long item, double *M) {
 }
 
 /*
- * out[i] = sum over co, ph, pw of sigmoid(avgpool(conv2d(x[b_i], w) + bias))
- * for the batch items b_i = batch_idx[i] (batch_idx NULL: i = 0..nb-1).
+ * out[i] = sum over co, ph, pw of sigmoid(pool(relu?(conv2d(x[b_i], w) + bias)))
+ * for the batch items b_i = batch_idx[i] (batch_idx NULL: i = 0..nb-1);
+ * pool_mode 0 averages, 1 takes the maximum; relu 1 applies ReLU to the conv
+ * outputs first; ceil_mode 1 keeps the last, partial windows.
  * part[i*Cout+co] (optional) receives the per-channel sums, pooled (optional)
  * the pre-sigmoid pooled map [nb, Cout, PH, PW].  bias may be NULL (zero).
  * The per-channel sums are added in increasing co, so out is deterministic.
  */
-int oracle_conv2d_pool_sigmoid_sum(const float *x, long B, long Cin, long H, long W, const float *w,
-                                   long Cout, long K, const float *bias, long pool, const long *batch_idx,
-                                   long nb, double *out, double *part, double *pooled, int nthreads) {
+int oracle_conv2d_pool_sigmoid_sum_ex(const float *x, long B, long Cin, long H, long W, const float *w, long Cout,
+                                      long K, const float *bias, long pool, int pool_mode, int relu, int ceil_mode,
+                                      const long *batch_idx, long nb, double *out, double *part, double *pooled,
+                                      int nthreads) {
     conv2d_ctx c;
     if (!x || !w || !out || B < 1 || Cin < 1 || Cout < 1 || nb < 0) return ORACLE_EINVAL;
-    if (oracle_conv2d_sizes(H, W, K, pool, &c.Hc, &c.Wc, &c.PH, &c.PW) != ORACLE_OK) return ORACLE_EINVAL;
+    if (pool_mode < 0 || pool_mode > 1 || relu < 0 || relu > 1 || ceil_mode < 0 || ceil_mode > 1)
+        return ORACLE_EINVAL;
+    if (oracle_conv2d_sizes_ex(H, W, K, pool, ceil_mode, &c.Hc, &c.Wc, &c.PH, &c.PW) != ORACLE_OK)
+        return ORACLE_EINVAL;
+    c.pool_mode = pool_mode;
+    c.relu = relu;
     if (batch_idx) {
         for (long i = 0; i < nb; ++i)
             if (batch_idx[i] < 0 || batch_idx[i] >= B) return ORACLE_EINVAL;
@@ -209,36 +250,56 @@ int oracle_conv2d_pool_sigmoid_sum(const float *x, long B, long Cin, long H, lon
     return rc;
 }
 
+int oracle_conv2d_pool_sigmoid_sum(const float *x, long B, long Cin, long H, long W, const float *w,
+                                   long Cout, long K, const float *bias, long pool, const long *batch_idx,
+                                   long nb, double *out, double *part, double *pooled, int nthreads) {
+    return oracle_conv2d_pool_sigmoid_sum_ex(x, B, Cin, H, W, w, Cout, K, bias, pool, 0, 0, 0, batch_idx, nb, out,
+                                             part, pooled, nthreads);
+}
+
 /*
  * Pre-sigmoid pooled values at n chosen positions idx[4*i..4*i+3] =
  * (b, co, ph, pw): avg = (1/s^2) * sum over the s x s window of the conv map,
  * each conv output computed from its definition.  [P65] fused
  * per-pooled-output formula.
  */
-int oracle_conv2d_pooled_at(const float *x, long B, long Cin, long H, long W, const float *w, long Cout,
-                            long K, const float *bias, long pool, const long *idx, long n, double *avg) {
+int oracle_conv2d_pooled_at_ex(const float *x, long B, long Cin, long H, long W, const float *w, long Cout, long K,
+                               const float *bias, long pool, int pool_mode, int relu, int ceil_mode, const long *idx,
+                               long n, double *val) {
     long Hc, Wc, PH, PW;
-    if (!x || !w || !avg || (n > 0 && !idx)) return ORACLE_EINVAL;
-    if (oracle_conv2d_sizes(H, W, K, pool, &Hc, &Wc, &PH, &PW) != ORACLE_OK) return ORACLE_EINVAL;
+    if (!x || !w || !val || (n > 0 && !idx)) return ORACLE_EINVAL;
+    if (pool_mode < 0 || pool_mode > 1 || relu < 0 || relu > 1 || ceil_mode < 0 || ceil_mode > 1)
+        return ORACLE_EINVAL;
+    if (oracle_conv2d_sizes_ex(H, W, K, pool, ceil_mode, &Hc, &Wc, &PH, &PW) != ORACLE_OK) return ORACLE_EINVAL;
     for (long i = 0; i < n; ++i) {
         const long b = idx[4 * i], co = idx[4 * i + 1], ph = idx[4 * i + 2], pw = idx[4 * i + 3];
         if (b < 0 || b >= B || co < 0 || co >= Cout || ph < 0 || ph >= PH || pw < 0 || pw >= PW)
             return ORACLE_EINVAL;
-        double acc = 0.0;
+        double acc = 0.0, mx = -INFINITY;
+        long count = 0;
         for (long dy = 0; dy < pool; ++dy)
             for (long dx = 0; dx < pool; ++dx) {
                 const long y = ph * pool + dy, xx = pw * pool + dx;
+                if (y >= Hc || xx >= Wc) continue; /* outside a partial (ceil-mode) window */
                 double conv = bias ? (double)bias[co] : 0.0;
                 for (long ic = 0; ic < Cin; ++ic)
                     for (long ky = 0; ky < K; ++ky)
                         for (long kx = 0; kx < K; ++kx)
                             conv += (double)x[((b * Cin + ic) * H + y + ky) * W + xx + kx] *
                                     (double)w[((co * Cin + ic) * K + ky) * K + kx];
+                if (relu && conv < 0.0) conv = 0.0;
                 acc += conv;
+                mx = conv > mx ? conv : mx;
+                ++count;
             }
-        avg[i] = acc / (double)(pool * pool);
+        val[i] = pool_mode == 1 ? mx : acc / (double)count;
     }
     return ORACLE_OK;
+}
+
+int oracle_conv2d_pooled_at(const float *x, long B, long Cin, long H, long W, const float *w, long Cout,
+                            long K, const float *bias, long pool, const long *idx, long n, double *avg) {
+    return oracle_conv2d_pooled_at_ex(x, B, Cin, H, W, w, Cout, K, bias, pool, 0, 0, 0, idx, n, avg);
 }
 
 /* ------------------------------------ depthwise Conv1d -> pointwise 1x1 Conv1d + bias */

@@ -32,14 +32,15 @@ def load():
 
         _build.build()
     lib = ctypes.CDLL(_LIB_PATH)
-    lib.oracle_conv2d_sizes.argtypes = [_L, _L, _L, _L, _i64p, _i64p, _i64p, _i64p]
-    lib.oracle_conv2d_sizes.restype = ctypes.c_int
-    lib.oracle_conv2d_pool_sigmoid_sum.argtypes = [
-        _f32p, _L, _L, _L, _L, _f32p, _L, _L, _f32p, _L, _i64p, _L, _f64p, _f64p, _f64p, ctypes.c_int]
-    lib.oracle_conv2d_pool_sigmoid_sum.restype = ctypes.c_int
-    lib.oracle_conv2d_pooled_at.argtypes = [
-        _f32p, _L, _L, _L, _L, _f32p, _L, _L, _f32p, _L, _i64p, _L, _f64p]
-    lib.oracle_conv2d_pooled_at.restype = ctypes.c_int
+    _I = ctypes.c_int
+    lib.oracle_conv2d_sizes_ex.argtypes = [_L, _L, _L, _L, _I, _i64p, _i64p, _i64p, _i64p]
+    lib.oracle_conv2d_sizes_ex.restype = ctypes.c_int
+    lib.oracle_conv2d_pool_sigmoid_sum_ex.argtypes = [
+        _f32p, _L, _L, _L, _L, _f32p, _L, _L, _f32p, _L, _I, _I, _I, _i64p, _L, _f64p, _f64p, _f64p, _I]
+    lib.oracle_conv2d_pool_sigmoid_sum_ex.restype = ctypes.c_int
+    lib.oracle_conv2d_pooled_at_ex.argtypes = [
+        _f32p, _L, _L, _L, _L, _f32p, _L, _L, _f32p, _L, _I, _I, _I, _i64p, _L, _f64p]
+    lib.oracle_conv2d_pooled_at_ex.restype = ctypes.c_int
     lib.oracle_dwsep_tout.argtypes = [_L, _L, _L]
     lib.oracle_dwsep_tout.restype = _L
     lib.oracle_dwsep_tout_ex.argtypes = [_L, _L, _L, _L, _L]
@@ -82,16 +83,21 @@ def _check(rc, what):
         raise ValueError(f"oracle {what} failed with code {rc}")
 
 
-def conv2d_sizes(H, W, K, pool):
-    """(Hc, Wc, PH, PW) for a valid stride-1 conv of kernel K then a floor pool of size pool."""
+POOL_AVG, POOL_MAX = 0, 1
+
+
+def conv2d_sizes(H, W, K, pool, ceil_mode=False):
+    """(Hc, Wc, PH, PW) for a valid stride-1 conv of kernel K then a pool of size pool (floor or ceil mode)."""
     lib = load()
     out = [ctypes.c_long() for _ in range(4)]
-    _check(lib.oracle_conv2d_sizes(H, W, K, pool, *[ctypes.byref(o) for o in out]), "conv2d_sizes")
+    _check(lib.oracle_conv2d_sizes_ex(H, W, K, pool, int(bool(ceil_mode)), *[ctypes.byref(o) for o in out]),
+           "conv2d_sizes")
     return tuple(o.value for o in out)
 
 
-def conv2d_pool_sigmoid_sum(x, w, b, pool, batch_idx=None, want_part=False, want_pooled=False, nthreads=None):
-    """Literal Conv2d -> AvgPool2d(pool) -> sigmoid -> sum over (C, H, W).
+def conv2d_pool_sigmoid_sum(x, w, b, pool, batch_idx=None, want_part=False, want_pooled=False, nthreads=None,
+                            pool_mode=POOL_AVG, relu=False, ceil_mode=False):
+    """Literal Conv2d -> [ReLU] -> AvgPool2d or MaxPool2d(pool) -> sigmoid -> sum over (C, H, W).
 
     x [B,Cin,H,W], w [Cout,Cin,K,K], b [Cout] or None.  Returns out [nb]
     (float64), plus part [nb,Cout] and/or the pre-sigmoid pooled map
@@ -104,7 +110,7 @@ def conv2d_pool_sigmoid_sum(x, w, b, pool, batch_idx=None, want_part=False, want
     Cout, Cin2, K, K2 = w.shape
     if Cin2 != Cin or K2 != K or (b is not None and b.shape != (Cout,)):
         raise ValueError("shape mismatch")
-    _, _, PH, PW = conv2d_sizes(H, W, K, pool)
+    _, _, PH, PW = conv2d_sizes(H, W, K, pool, ceil_mode)
     if batch_idx is None:
         idx = None
         nb = B
@@ -114,8 +120,8 @@ def conv2d_pool_sigmoid_sum(x, w, b, pool, batch_idx=None, want_part=False, want
     out = np.zeros(nb, dtype=np.float64)
     part = np.zeros((nb, Cout), dtype=np.float64) if want_part else None
     pooled = np.zeros((nb, Cout, PH, PW), dtype=np.float64) if want_pooled else None
-    rc = lib.oracle_conv2d_pool_sigmoid_sum(
-        _fp(x), B, Cin, H, W, _fp(w), Cout, K, _fp(b), pool,
+    rc = lib.oracle_conv2d_pool_sigmoid_sum_ex(
+        _fp(x), B, Cin, H, W, _fp(w), Cout, K, _fp(b), pool, int(pool_mode), int(bool(relu)), int(bool(ceil_mode)),
         None if idx is None else idx.ctypes.data_as(_i64p), nb,
         out.ctypes.data_as(_f64p),
         None if part is None else part.ctypes.data_as(_f64p),
@@ -130,7 +136,7 @@ def conv2d_pool_sigmoid_sum(x, w, b, pool, batch_idx=None, want_part=False, want
     return res[0] if len(res) == 1 else tuple(res)
 
 
-def conv2d_pooled_at(x, w, b, pool, idx):
+def conv2d_pooled_at(x, w, b, pool, idx, pool_mode=POOL_AVG, relu=False, ceil_mode=False):
     """Pre-sigmoid pooled values at positions idx [n,4] = (b, co, ph, pw)."""
     lib = load()
     x, w = _f32(x), _f32(w)
@@ -139,8 +145,9 @@ def conv2d_pooled_at(x, w, b, pool, idx):
     Cout, _, K, _ = w.shape
     idx = np.ascontiguousarray(idx, dtype=np.int64).reshape(-1, 4)
     out = np.zeros(idx.shape[0], dtype=np.float64)
-    rc = lib.oracle_conv2d_pooled_at(_fp(x), B, Cin, H, W, _fp(w), Cout, K, _fp(b), pool,
-                                     idx.ctypes.data_as(_i64p), idx.shape[0], out.ctypes.data_as(_f64p))
+    rc = lib.oracle_conv2d_pooled_at_ex(_fp(x), B, Cin, H, W, _fp(w), Cout, K, _fp(b), pool, int(pool_mode),
+                                        int(bool(relu)), int(bool(ceil_mode)), idx.ctypes.data_as(_i64p),
+                                        idx.shape[0], out.ctypes.data_as(_f64p))
     _check(rc, "conv2d_pooled_at")
     return out
 
