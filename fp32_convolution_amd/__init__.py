@@ -27,6 +27,11 @@ ALGO_DIRECT_MFMA = 1
 ALGO_DIRECT_SIMPLE = 2
 ALGO_BOXSUM = 3
 
+POOL_AVG = 0
+POOL_MAX = 1
+RELU = 1
+CEIL_MODE = 2
+
 DWSEP_AUTO = 0
 DWSEP_SEPARABLE = 1
 DWSEP_DENSE = 2
@@ -52,6 +57,13 @@ _SIGS = {
     "fconv2d_pool_sigmoid_sum_det_workspace": (
         [_i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "fconv2d_pool_out_size": ([_i64, _i64, _i64, _i64, _i64p, _i64p], ctypes.c_int),
+    "fconv2d_pool_sigmoid_sum_ex": (
+        [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp],
+        ctypes.c_int),
+    "fconv2d_pool_map_ex": (
+        [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp],
+        ctypes.c_int),
+    "fconv2d_pool_out_size_ex": ([_i64, _i64, _i64, _i64, ctypes.c_int, _i64p, _i64p], ctypes.c_int),
     "fconv2d_select_algo": ([_i64, _i64, _i64, _i64], ctypes.c_int),
     "dwsep_conv1d": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp], ctypes.c_int),
     "dwsep_conv1d_out_len": ([_i64, _i64, _i64], ctypes.c_int64),
@@ -104,9 +116,17 @@ def version() -> int:
     return lib.fconv_version()
 
 
-def conv2d_out_size(H: int, W: int, K: int, pool: int):
+def _pool_flags(relu: bool, ceil_mode: bool) -> int:
+    return (RELU if relu else 0) | (CEIL_MODE if ceil_mode else 0)
+
+
+def conv2d_out_size(H: int, W: int, K: int, pool: int, ceil_mode: bool = False):
     ph, pw = ctypes.c_int64(), ctypes.c_int64()
-    _check(lib.fconv2d_pool_out_size(H, W, K, pool, ctypes.byref(ph), ctypes.byref(pw)), "fconv2d_pool_out_size")
+    if ceil_mode:
+        _check(lib.fconv2d_pool_out_size_ex(H, W, K, pool, CEIL_MODE, ctypes.byref(ph), ctypes.byref(pw)),
+               "fconv2d_pool_out_size_ex")
+    else:
+        _check(lib.fconv2d_pool_out_size(H, W, K, pool, ctypes.byref(ph), ctypes.byref(pw)), "fconv2d_pool_out_size")
     return ph.value, pw.value
 
 
@@ -127,8 +147,10 @@ def _conv2d_args(x, w, b):
         raise ValueError("x, w and bias must be on the same device")
 
 
-def conv2d_pool_sigmoid_sum(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO):
-    """Conv2d(stride 1, no pad) -> AvgPool2d(pool, floor) -> sigmoid -> sum over (C,H,W): out[B]."""
+def conv2d_pool_sigmoid_sum(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO, pool_mode: int = POOL_AVG,
+                            relu: bool = False, ceil_mode: bool = False):
+    """Conv2d(stride 1, no pad) -> [ReLU] -> AvgPool2d or MaxPool2d(pool, floor or ceil) -> sigmoid -> sum
+    over (C,H,W): out[B].  The defaults are the plain chain (average pool, no ReLU, floor)."""
     _conv2d_args(x, w, b)
     B, Cin, H, W = x.shape
     Cout, _, K, _ = w.shape
@@ -138,8 +160,13 @@ def conv2d_pool_sigmoid_sum(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO)
         _dev_f32(out, "out")
         if tuple(out.shape) != (B,) or out.device != x.device:
             raise ValueError("out must be [B] on x's device")
-    rc = lib.fconv2d_pool_sigmoid_sum_algo(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
-                                           _ptr(out), _stream(x))
+    flags = _pool_flags(relu, ceil_mode)
+    if pool_mode == POOL_AVG and flags == 0:
+        rc = lib.fconv2d_pool_sigmoid_sum_algo(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
+                                               _ptr(out), _stream(x))
+    else:
+        rc = lib.fconv2d_pool_sigmoid_sum_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode,
+                                             flags, algo, _ptr(out), _stream(x))
     _check(rc, "fconv2d_pool_sigmoid_sum")
     return out
 
@@ -178,19 +205,26 @@ def conv2d_pool_sigmoid_sum_det(x, w, b, pool: int, out=None, algo: int = ALGO_A
     return out
 
 
-def conv2d_pool_map(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO):
+def conv2d_pool_map(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO, pool_mode: int = POOL_AVG,
+                    relu: bool = False, ceil_mode: bool = False):
     """Pre-sigmoid pooled map [B,Cout,PH,PW] of the same fused computation."""
     _conv2d_args(x, w, b)
     B, Cin, H, W = x.shape
     Cout, _, K, _ = w.shape
-    PH, PW = conv2d_out_size(H, W, K, pool)
+    PH, PW = conv2d_out_size(H, W, K, pool, ceil_mode)
     if out is None:
         out = torch.empty((B, Cout, PH, PW), dtype=torch.float32, device=x.device)
     else:
         _dev_f32(out, "out")
         if tuple(out.shape) != (B, Cout, PH, PW) or out.device != x.device:
             raise ValueError("out must be [B,Cout,PH,PW] on x's device")
-    rc = lib.fconv2d_pool_map(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo, _ptr(out), _stream(x))
+    flags = _pool_flags(relu, ceil_mode)
+    if pool_mode == POOL_AVG and flags == 0:
+        rc = lib.fconv2d_pool_map(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo, _ptr(out),
+                                  _stream(x))
+    else:
+        rc = lib.fconv2d_pool_map_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode, flags, algo,
+                                     _ptr(out), _stream(x))
     _check(rc, "fconv2d_pool_map")
     return out
 

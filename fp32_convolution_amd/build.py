@@ -21,7 +21,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfconv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["fconv_api.hip", "conv2d_pool.hip", "dwsep_conv1d.hip"]
+SOURCES = ["fconv_api.hip", "conv2d_pool.hip", "conv2d_pool_ex.hip", "dwsep_conv1d.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

@@ -1,0 +1,420 @@
+// conv2d_pool_ex.hip -- the Conv2d path with the pool generalised: average or
+// max pooling, an optional ReLU between the convolution and the pool, and
+// PyTorch's floor or ceil output size.
+//
+//   pooled[co,ph,pw] = POOL_{y,x in window(ph,pw)} act(conv[co,y,x])
+//   conv[co,y,x]     = bias[co] + sum_{ic,ky,kx} x[ic,y+ky,x+kx] * w[co,ic,ky,kx]
+//   act              = ReLU or identity;  POOL = mean or max
+//   window(ph,pw)    = rows [ph*s, min(ph*s+s, Hc)) x columns [pw*s, min(pw*s+s, Wc))
+//   out[b]           = sum_{co,ph,pw} sigmoid(pooled[co,ph,pw])
+//
+// Sources: the base chain is the one of POPCORNBENCH reasoning trace
+// "Kimi-K2.6 l2_p65" (Conv2d -> AvgPool2d -> Sigmoid -> Sum); the 新智元
+// article on the same benchmark lists a fused Conv2D + ReLU + MaxPool
+// operator, which is where the ReLU-before-the-pool order and the max pool
+// come from.  Ceil mode follows PyTorch's pooling: ceil(Hc/s) rows, the last
+// window clipped to the map, a partial window averaging over its valid
+// elements only (there is no padding, so every window starts inside the map).
+//
+// Neither ReLU nor max is linear, so the pool can no longer be folded into
+// the contraction (as the AvgPool kernels do): each conv output must exist
+// on its own, if only in a register.  Two kernels:
+//  * conv2d_pool_elem_kernel (K = 3, s = 4, fp32 matrix cores): the MFMA N
+//    dimension runs over 16 consecutive conv columns (four windows) of one
+//    conv row, and each wave keeps four accumulator blocks, one per window
+//    row dy, for each of its 16-column blocks.  The bias is the
+//    accumulators' starting value, so every accumulator element is a finished
+//    conv output.  The pool then reduces over dy inside each lane's
+//    registers and over dx across the 4 lanes of a window with two DPP quad
+//    steps, arranged as a transposing reduction that leaves lane dx holding
+//    the pooled value of output channel 4g+dx: one sigmoid per lane per
+//    block, none wasted.  The multiply-adds are those of the direct AvgPool
+//    kernel (s^2*Cin*K*K per pooled output), only grouped by conv output.
+//  * conv2d_pool_general_kernel: one thread per pooled output, any shape.
+#include <math.h>
+
+#include "fconv_device.hpp"
+#include "fconv_internal.hpp"
+
+namespace fconv {
+
+// ---------------------------------------------------------------- any shape
+
+template <int MODE>
+__global__ __launch_bounds__(256) void conv2d_pool_general_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ dst, int Cin, int H, int W, int Cout, int K, int S, int PH, int PW, int pool_max,
+    int relu) {
+    __shared__ float red[4];
+    const int b = blockIdx.y;
+    const int n = Cout * PH * PW;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int Hc = H - K + 1, Wc = W - K + 1;
+    float v = 0.f;
+    if (idx < n) {
+        const int co = idx / (PH * PW);
+        const int rem = idx - co * (PH * PW);
+        const int ph = rem / PW, pw = rem - (rem / PW) * PW;
+        const int ny = min(S, Hc - ph * S), nx = min(S, Wc - pw * S);
+        const float* xb = x + (size_t)b * Cin * H * W;
+        const float* wc = w + (size_t)co * Cin * K * K;
+        const float bc = bias ? bias[co] : 0.f;
+        float pooled = pool_max ? -INFINITY : 0.f;
+        for (int dy = 0; dy < ny; ++dy)
+            for (int dx = 0; dx < nx; ++dx) {
+                float c = 0.f;
+                for (int ic = 0; ic < Cin; ++ic)
+                    for (int ky = 0; ky < K; ++ky) {
+                        const float* xr = xb + (ic * H + ph * S + dy + ky) * W + pw * S + dx;
+                        const float* wr = wc + (ic * K + ky) * K;
+                        for (int kx = 0; kx < K; ++kx) c += xr[kx] * wr[kx];
+                    }
+                c += bc;
+                if (relu) c = fmaxf(c, 0.f);
+                pooled = pool_max ? fmaxf(pooled, c) : pooled + c;
+            }
+        if (!pool_max) pooled /= (float)(ny * nx);
+        if constexpr (MODE == OUT_MAP)
+            dst[(size_t)b * n + idx] = pooled;
+        else
+            v = logistic(pooled);
+    }
+    if constexpr (MODE != OUT_MAP) {
+        const float s = block_sum<4>(v, red);
+        if (threadIdx.x == 0) {
+            if constexpr (MODE == OUT_SUM_ATOMIC)
+                atomicAdd(dst + b, s);
+            else
+                dst[(size_t)b * gridDim.x + blockIdx.x] = s;
+        }
+    }
+}
+
+int64_t conv2d_general_parts(const Conv2dShape& s) { return ((int64_t)s.Cout * s.PH * s.PW + 255) / 256; }
+
+// ---------------------------------------------------------------- K = 3, s = 4 on matrix cores
+
+// Tiling: a workgroup of 4 waves covers 64 output channels (16 per wave) and
+// a TPH x TPW pooled tile; each wave walks the tile's pooled rows one at a
+// time, holding NCB 16-column blocks x S window rows of accumulators.
+struct ElemK3S4 {
+    static constexpr int K = 3, S = 4;
+    static constexpr int NCB = 4;                 // 16-column blocks per wave
+    static constexpr int TPW = NCB * 16 / S;      // 16 pooled columns
+    static constexpr int TPH = 4;                 // pooled rows
+    static constexpr int NW = 4, NT = 64 * NW;
+    static constexpr int CO_RANGE = 16 * NW;
+    static constexpr int IH = TPH * S + K - 1;    // 18 input rows per tile
+    static constexpr int IW = TPW * S + K - 1;    // 66 input columns per tile
+    static constexpr int RP = IW;                 // LDS floats per row
+    static constexpr int NR = S + K - 1;          // input rows one pooled row reads
+};
+
+template <int POOL_MAX, int MODE>
+__global__ __launch_bounds__(ElemK3S4::NT) void conv2d_pool_elem_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane, int tiles_w,
+    int relu, int ceil_mode) {
+    using C = ElemK3S4;
+    constexpr int K = C::K, S = C::S, NCB = C::NCB, TPH = C::TPH, TPW = C::TPW;
+    constexpr int IH = C::IH, IW = C::IW, RP = C::RP, NR = C::NR;
+
+    extern __shared__ float lds[];
+    __shared__ float red[C::NW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;    // MFMA k-slot: channel group
+    const int l16 = lane & 15;  // row of A / column of B
+    const int tile_y = blockIdx.x / tiles_w;
+    const int tile_x = blockIdx.x - tile_y * tiles_w;
+    const int b = blockIdx.z;
+    const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
+    const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
+    const int co0 = blockIdx.y * C::CO_RANGE + wave * 16;
+    const int Hc = H - K + 1, Wc = W - K + 1;
+
+    // Weights of channel quad q: a[ky][kx] = w[co0 + l16, g*CINQ + q, ky, kx]
+    // (0 where co or ic is out of range).
+    const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
+    auto load_a = [&](float (&a)[K][K], int q) {
+        const int ic = g * CINQ + q;
+        const int co = co0 + l16;
+        const bool ok = (co < Cout) && (ic < Cin) && (q < CINQ);
+        const int base = ok ? (co * Cin + ic) * (K * K * 4) : kBufOOB;
+#pragma unroll
+        for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+            for (int kx = 0; kx < K; ++kx) a[ky][kx] = buf_load_f32(rw, base + (ky * K + kx) * 4);
+    };
+    float a_cur[K][K], a_nxt[K][K];
+    load_a(a_cur, 0);
+
+    // Bias of the channels this lane's accumulator elements hold: co0 + 4g + r.
+    const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
+    floatx4 bco;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int co = co0 + 4 * g + r;
+        bco[r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
+    }
+
+    // Stage the input tile: channel ic at ic*plane, row r at r*RP, column c at
+    // c.  Whole rows per wave through a per-row buffer resource (empty for
+    // rows outside the image and channels >= Cin, which therefore read 0).
+    {
+        constexpr int NCH = (IW + 63) / 64;
+        constexpr int UR = 4;
+        int voff[NCH];
+        bool inr[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int c = lane + 64 * k;
+            inr[k] = c < IW;
+            voff[k] = (c < IW && x0 + c < W) ? (x0 + c) * 4 : kBufOOB;
+        }
+        const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+        const int nrows = 4 * CINQ * IH;
+        const float* xb = x + (size_t)b * Cin * H * W;
+        for (int row0 = wave_s; row0 < nrows; row0 += C::NW * UR) {
+            float v[UR][NCH];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int row = row0 + u * C::NW;
+                const int ic = row / IH, r = row - (row / IH) * IH;
+                const bool ok = (row < nrows) && (ic < Cin) && (y0 + r < H);
+                const buf_rsrc rrow = make_rsrc(xb + (ok ? (ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) v[u][k] = buf_load_f32(rrow, voff[k]);
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int row = row0 + u * C::NW;
+                if (row < nrows) {
+                    const int ic = row / IH, r = row - (row / IH) * IH;
+                    float* lrow = lds + ic * plane + r * RP;
+#pragma unroll
+                    for (int k = 0; k < NCH; ++k)
+                        if (inr[k]) lrow[lane + 64 * k] = v[u][k];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const int bbase = g * CINQ * plane + l16;
+    // A column block's lanes read 16 consecutive words; the 4 channel groups
+    // sit plane*CINQ words apart (padded onto different banks).
+    auto load_row = [&](float (&bv)[NCB][K], int off) {
+#pragma unroll
+        for (int nb = 0; nb < NCB; ++nb)
+#pragma unroll
+            for (int kx = 0; kx < K; ++kx) bv[nb][kx] = lds[bbase + off + nb * 16 + kx];
+    };
+
+    // Lane roles in the pool: dx = l16 & 3 is the column inside a window and,
+    // after the transposing reduction, the channel r the lane finishes.
+    const bool odd1 = (l16 & 1) != 0, odd2 = (l16 & 2) != 0;
+    const int co_fin = co0 + 4 * g + (l16 & 3);
+    auto pool2 = [](float a, float c) { return POOL_MAX ? fmaxf(a, c) : a + c; };
+
+    float lsum = 0.f;
+    const int nrow_tile = min(TPH, PH - ph0);
+    for (int pr = 0; pr < nrow_tile; ++pr) {
+        floatx4 acc[NCB][S];
+#pragma unroll
+        for (int nb = 0; nb < NCB; ++nb)
+#pragma unroll
+            for (int dy = 0; dy < S; ++dy) acc[nb][dy] = bco;
+
+        for (int q = 0; q < CINQ; ++q) {
+            // The next quad's weights (quad 0 again after the last: the next
+            // pooled row starts there) load under this quad's MFMAs.
+            load_a(a_nxt, q + 1 < CINQ ? q + 1 : 0);
+            const int off0 = q * plane + pr * S * RP;
+            float bcur[NCB][K], bnxt[NCB][K];
+            load_row(bcur, off0);
+#pragma unroll
+            for (int rr = 0; rr < NR; ++rr) {
+                if (rr + 1 < NR) load_row(bnxt, off0 + (rr + 1) * RP);
+#pragma unroll
+                for (int ky = 0; ky < K; ++ky) {
+                    const int dy = rr - ky;
+                    if (dy < 0 || dy >= S) continue;
+#pragma unroll
+                    for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+                        for (int nb = 0; nb < NCB; ++nb)
+                            acc[nb][dy] = mfma_16x16x4(a_cur[ky][kx], bcur[nb][kx], acc[nb][dy]);
+                }
+                if (rr + 1 < NR) {
+#pragma unroll
+                    for (int nb = 0; nb < NCB; ++nb)
+#pragma unroll
+                        for (int kx = 0; kx < K; ++kx) bcur[nb][kx] = bnxt[nb][kx];
+                }
+            }
+#pragma unroll
+            for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+                for (int kx = 0; kx < K; ++kx) a_cur[ky][kx] = a_nxt[ky][kx];
+        }
+
+        // Epilogue of pooled row ph.  Lane (g, l16) holds in acc[nb][dy][r]
+        // the conv output of channel co0 + 4g + r at conv row ph*S + dy,
+        // column x0 + nb*16 + l16.
+        const int ph = ph0 + pr;
+        const int yr = y0 + pr * S;
+        // Conv outputs outside the map exist only in partial (ceil-mode)
+        // windows at the bottom and right edges; they are masked there.
+        const bool edge = ceil_mode && (yr + S > Hc || x0 + TPW * S > Wc);
+        const float fill = POOL_MAX ? -INFINITY : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NCB; ++nb) {
+            if (!POOL_MAX && relu) {
+#pragma unroll
+                for (int dy = 0; dy < S; ++dy)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[nb][dy][r] = fmaxf(acc[nb][dy][r], 0.f);
+            }
+            if (edge) {
+                const bool col_ok = x0 + nb * 16 + l16 < Wc;
+#pragma unroll
+                for (int dy = 0; dy < S; ++dy) {
+                    const bool ok = col_ok && (yr + dy < Hc);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[nb][dy][r] = ok ? acc[nb][dy][r] : fill;
+                }
+            }
+            // Over the window's rows, inside the lane.
+            floatx4 m = acc[nb][0];
+#pragma unroll
+            for (int dy = 1; dy < S; ++dy)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[r] = pool2(m[r], acc[nb][dy][r]);
+            // Over the window's 4 columns (lanes 4j..4j+3 of the 16-lane row).
+            // Step 1 pairs lanes l, l^1: the even lane keeps channels r = 0, 2
+            // and sends r = 1, 3; the odd lane the reverse.  Step 2 pairs
+            // l, l^2 the same way over the two kept values.  Lane dx ends with
+            // channel r = dx over all four columns.
+            const float k01 = odd1 ? m[1] : m[0], s01 = odd1 ? m[0] : m[1];
+            const float k23 = odd1 ? m[3] : m[2], s23 = odd1 ? m[2] : m[3];
+            const float p01 = pool2(k01, quad_xor1(s01));
+            const float p23 = pool2(k23, quad_xor1(s23));
+            const float kk = odd2 ? p23 : p01, ss = odd2 ? p01 : p23;
+            float pv = pool2(kk, quad_xor2(ss));
+
+            const int pw = pw0 + nb * 4 + (l16 >> 2);
+            if (co_fin < Cout && pw < PW) {
+                if (POOL_MAX) {
+                    if (relu) pv = fmaxf(pv, 0.f);  // ReLU commutes with max
+                } else {
+                    const int cnt = edge ? min(S, Hc - ph * S) * min(S, Wc - pw * S) : S * S;
+                    pv = edge ? pv / (float)cnt : pv * (1.0f / (S * S));
+                }
+                if constexpr (MODE == OUT_MAP)
+                    dst[(((size_t)b * Cout + co_fin) * PH + ph) * PW + pw] = pv;
+                else
+                    lsum += logistic(pv);
+            }
+        }
+    }
+
+    if constexpr (MODE != OUT_MAP) {
+        const float s = block_sum<C::NW>(lsum, red);
+        if (tid == 0) {
+            if constexpr (MODE == OUT_SUM_ATOMIC)
+                atomicAdd(dst + b, s);
+            else
+                dst[(size_t)b * (gridDim.x * gridDim.y) + blockIdx.y * gridDim.x + blockIdx.x] = s;
+        }
+    }
+}
+
+namespace {
+
+constexpr size_t kMaxLdsEx = 160 * 1024 - 256;
+
+// Channel planes padded so that the 4 channel groups (plane*CINQ words
+// apart) start 16 banks apart.
+int elem_plane(int CINQ) {
+    const int base = ElemK3S4::IH * ElemK3S4::RP;
+    for (int pad = 0; pad < 64; ++pad)
+        if (((long)CINQ * (base + pad)) % 64 == 16) return base + pad;
+    for (int pad = 0; pad < 32; ++pad)
+        if (((long)CINQ * (base + pad)) % 32 == 16) return base + pad;
+    return base;
+}
+
+size_t elem_lds_bytes(int Cin) {
+    const int CINQ = (Cin + 3) / 4;
+    return (size_t)4 * CINQ * elem_plane(CINQ) * sizeof(float);
+}
+
+dim3 elem_grid(const Conv2dShape& s) {
+    using C = ElemK3S4;
+    const int tiles_h = (s.PH + C::TPH - 1) / C::TPH;
+    const int tiles_w = (s.PW + C::TPW - 1) / C::TPW;
+    return dim3(tiles_h * tiles_w, (s.Cout + C::CO_RANGE - 1) / C::CO_RANGE, s.B);
+}
+
+template <int POOL_MAX, int MODE>
+hipError_t launch_elem_as(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                          const PoolOpts& o, hipStream_t stream) {
+    const int CINQ = (s.Cin + 3) / 4;
+    const int plane = elem_plane(CINQ);
+    const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
+    const int tiles_w = (s.PW + ElemK3S4::TPW - 1) / ElemK3S4::TPW;
+    const void* fn = (const void*)conv2d_pool_elem_kernel<POOL_MAX, MODE>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((conv2d_pool_elem_kernel<POOL_MAX, MODE>), elem_grid(s), dim3(ElemK3S4::NT), lds, stream, x,
+                       w, bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, tiles_w, o.relu ? 1 : 0,
+                       o.ceil_mode ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <int POOL_MAX>
+hipError_t launch_elem_pool(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                            int mode, const PoolOpts& o, hipStream_t stream) {
+    if (mode == OUT_MAP) return launch_elem_as<POOL_MAX, OUT_MAP>(s, x, w, bias, dst, o, stream);
+    if (mode == OUT_PARTIAL) return launch_elem_as<POOL_MAX, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
+    return launch_elem_as<POOL_MAX, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+}
+
+}  // namespace
+
+bool conv2d_elem_supported(int Cin, int K, int S) {
+    return K == ElemK3S4::K && S == ElemK3S4::S && elem_lds_bytes(Cin) <= kMaxLdsEx;
+}
+
+int64_t conv2d_elem_parts(const Conv2dShape& s) {
+    const dim3 g = elem_grid(s);
+    return (int64_t)g.x * g.y;
+}
+
+hipError_t conv2d_elem_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                              int mode, const PoolOpts& o, hipStream_t stream) {
+    if (!conv2d_elem_supported(s.Cin, s.K, s.S)) return hipErrorInvalidValue;
+    return o.pool_max ? launch_elem_pool<1>(s, x, w, bias, dst, mode, o, stream)
+                      : launch_elem_pool<0>(s, x, w, bias, dst, mode, o, stream);
+}
+
+hipError_t conv2d_general_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
+                                 float* dst, int mode, const PoolOpts& o, hipStream_t stream) {
+    const dim3 grid((unsigned)conv2d_general_parts(s), s.B);
+    const int pm = o.pool_max ? 1 : 0, rl = o.relu ? 1 : 0;
+    if (mode == OUT_MAP)
+        hipLaunchKernelGGL(conv2d_pool_general_kernel<OUT_MAP>, grid, dim3(256), 0, stream, x, w, bias, dst, s.Cin,
+                           s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl);
+    else if (mode == OUT_PARTIAL)
+        hipLaunchKernelGGL(conv2d_pool_general_kernel<OUT_PARTIAL>, grid, dim3(256), 0, stream, x, w, bias, dst,
+                           s.Cin, s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl);
+    else
+        hipLaunchKernelGGL(conv2d_pool_general_kernel<OUT_SUM_ATOMIC>, grid, dim3(256), 0, stream, x, w, bias,
+                           dst, s.Cin, s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl);
+    return hipGetLastError();
+}
+
+}  // namespace fconv

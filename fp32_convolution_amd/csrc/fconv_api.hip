@@ -39,14 +39,16 @@ int status_of(hipError_t e) { return e == hipSuccess ? FCONV_OK : FCONV_EHIP; }
 // Element counts per batch item must fit int32 (kernel offsets are 32-bit
 // inside one batch item); larger shapes are FCONV_EUNSUPPORTED.
 int check_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
-                 int64_t K, int64_t pool, const void* dst, Conv2dShape* s) {
+                 int64_t K, int64_t pool, const void* dst, Conv2dShape* s, bool ceil_mode = false) {
     if (!x || !w || !dst) return FCONV_EINVAL;
     if (B < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || K < 1 || pool < 1) return FCONV_EINVAL;
     if (H < K || W < K) return FCONV_EINVAL;
     int64_t t, per_item_x, nx, nw;
     if (!mul_ok(Cin, H, &t) || !mul_ok(t, W, &per_item_x) || !mul_ok(per_item_x, B, &nx)) return FCONV_EINVAL;
     if (!mul_ok(Cout, Cin, &t) || !mul_ok(t, K, &t) || !mul_ok(t, K, &nw)) return FCONV_EINVAL;
-    const int64_t PH = (H - K + 1) / pool, PW = (W - K + 1) / pool;
+    const int64_t Hc = H - K + 1, Wc = W - K + 1;
+    const int64_t PH = ceil_mode ? (Hc + pool - 1) / pool : Hc / pool;
+    const int64_t PW = ceil_mode ? (Wc + pool - 1) / pool : Wc / pool;
     int64_t per_item_map, nmap;
     if (!mul_ok(Cout, PH, &t) || !mul_ok(t, PW, &per_item_map) || !mul_ok(per_item_map, B, &nmap))
         return FCONV_EINVAL;
@@ -89,11 +91,18 @@ int64_t conv2d_parts(int algo, const Conv2dShape& s) {
     return fconv::conv2d_simple_parts(s);
 }
 
+// Stands in for a NULL pooled-map pointer during the argument checks.
+const float kEmptyMapStorage = 0.f;
+const void* const kEmptyMap = &kEmptyMapStorage;
+
 int run_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
                int64_t K, const float* bias, int64_t pool, int algo, float* dst, bool map, void* stream) {
     Conv2dShape s;
-    int rc = check_conv2d(x, B, Cin, H, W, w, Cout, K, pool, dst, &s);
+    // A map with no elements may come as a NULL pointer.
+    const bool null_map = map && !dst;
+    int rc = check_conv2d(x, B, Cin, H, W, w, Cout, K, pool, null_map ? kEmptyMap : dst, &s);
     if (rc != FCONV_OK) return rc;
+    if (null_map && s.PH > 0 && s.PW > 0) return FCONV_EINVAL;
     const int a = pick_conv2d_algo(s, algo);
     if (a < 0) return a;
     hipStream_t st = (hipStream_t)stream;
@@ -109,6 +118,47 @@ int run_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, con
         if (e != hipSuccess) return FCONV_EHIP;
     }
     return status_of(launch_conv2d(a, s, x, w, bias, dst, map ? fconv::OUT_MAP : fconv::OUT_SUM_ATOMIC, st));
+}
+
+constexpr int kPoolFlags = FCONV_RELU | FCONV_CEIL_MODE;
+
+// The generalised pool.  The plain average pool (no flags) is the base
+// operation and takes its algorithms; everything else runs on the
+// per-conv-output matrix-core kernel where it has an instance, else on the
+// one-thread-per-output kernel.
+int run_conv2d_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
+                  int64_t K, const float* bias, int64_t pool, int pool_mode, int flags, int algo, float* dst, bool map,
+                  void* stream) {
+    if (pool_mode != FCONV_POOL_AVG && pool_mode != FCONV_POOL_MAX) return FCONV_EINVAL;
+    if ((flags & ~kPoolFlags) != 0) return FCONV_EINVAL;
+    if (algo != FCONV_ALGO_AUTO && algo != FCONV_ALGO_DIRECT_MFMA && algo != FCONV_ALGO_DIRECT_SIMPLE &&
+        algo != FCONV_ALGO_BOXSUM)
+        return FCONV_EINVAL;
+    if (pool_mode == FCONV_POOL_AVG && flags == 0)
+        return run_conv2d(x, B, Cin, H, W, w, Cout, K, bias, pool, algo, dst, map, stream);
+    const fconv::PoolOpts o{pool_mode == FCONV_POOL_MAX, (flags & FCONV_RELU) != 0, (flags & FCONV_CEIL_MODE) != 0};
+    Conv2dShape s;
+    const bool null_map = map && !dst;
+    int rc = check_conv2d(x, B, Cin, H, W, w, Cout, K, pool, null_map ? kEmptyMap : dst, &s, o.ceil_mode);
+    if (rc != FCONV_OK) return rc;
+    if (null_map && s.PH > 0 && s.PW > 0) return FCONV_EINVAL;
+    const bool mfma_ok = fconv::conv2d_elem_supported(s.Cin, s.K, s.S);
+    int a = algo;
+    if (a == FCONV_ALGO_AUTO) a = mfma_ok ? FCONV_ALGO_DIRECT_MFMA : FCONV_ALGO_DIRECT_SIMPLE;
+    if (a == FCONV_ALGO_BOXSUM || (a == FCONV_ALGO_DIRECT_MFMA && !mfma_ok)) return FCONV_EUNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    if (log_enabled())
+        fprintf(stderr, "[fconv] conv2d_ex%s B=%d Cin=%d H=%d W=%d Cout=%d K=%d pool=%d max=%d relu=%d ceil=%d -> algo %d\n",
+                map ? "_map" : "", s.B, s.Cin, s.H, s.W, s.Cout, s.K, s.S, (int)o.pool_max, (int)o.relu,
+                (int)o.ceil_mode, a);
+    if (s.PH == 0 || s.PW == 0) return map ? FCONV_OK : status_of(fconv::fill_zero(dst, s.B, st));
+    if (!map) {
+        hipError_t e = fconv::fill_zero(dst, s.B, st);
+        if (e != hipSuccess) return FCONV_EHIP;
+    }
+    const int mode = map ? fconv::OUT_MAP : fconv::OUT_SUM_ATOMIC;
+    return status_of(a == FCONV_ALGO_DIRECT_MFMA ? fconv::conv2d_elem_launch(s, x, w, bias, dst, mode, o, st)
+                                                 : fconv::conv2d_general_launch(s, x, w, bias, dst, mode, o, st));
 }
 
 // Shape/algorithm checks shared by the deterministic entry point and its
@@ -142,6 +192,29 @@ int fconv2d_pool_sigmoid_sum_algo(const float* x, int64_t B, int64_t Cin, int64_
 int fconv2d_pool_map(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
                      int64_t K, const float* bias, int64_t pool, int algo, float* pooled, void* stream) {
     return run_conv2d(x, B, Cin, H, W, w, Cout, K, bias, pool, algo, pooled, true, stream);
+}
+
+int fconv2d_pool_sigmoid_sum_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w,
+                                int64_t Cout, int64_t K, const float* bias, int64_t pool, int pool_mode, int flags,
+                                int algo, float* out, void* stream) {
+    return run_conv2d_ex(x, B, Cin, H, W, w, Cout, K, bias, pool, pool_mode, flags, algo, out, false, stream);
+}
+
+int fconv2d_pool_map_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
+                        int64_t K, const float* bias, int64_t pool, int pool_mode, int flags, int algo, float* pooled,
+                        void* stream) {
+    return run_conv2d_ex(x, B, Cin, H, W, w, Cout, K, bias, pool, pool_mode, flags, algo, pooled, true, stream);
+}
+
+int fconv2d_pool_out_size_ex(int64_t H, int64_t W, int64_t K, int64_t pool, int flags, int64_t* PH,
+                             int64_t* PW) {
+    if (!PH || !PW || H < 1 || W < 1 || K < 1 || pool < 1 || H < K || W < K) return FCONV_EINVAL;
+    if ((flags & ~kPoolFlags) != 0) return FCONV_EINVAL;
+    const int64_t Hc = H - K + 1, Wc = W - K + 1;
+    const bool c = (flags & FCONV_CEIL_MODE) != 0;
+    *PH = c ? (Hc + pool - 1) / pool : Hc / pool;
+    *PW = c ? (Wc + pool - 1) / pool : Wc / pool;
+    return FCONV_OK;
 }
 
 int fconv2d_pool_sigmoid_sum_det_workspace(int64_t B, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t K,

@@ -54,6 +54,15 @@ __device__ __forceinline__ float block_sum(float v, float* red /* NWAVES floats 
     return s;
 }
 
+// DPP quad permutations: lane l reads lane l^1 (quad_perm 1,0,3,2) or lane
+// l^2 (quad_perm 2,3,0,1) of its aligned group of 4 lanes.
+__device__ __forceinline__ float quad_xor1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+
 // Logistic sigmoid 1/(1+e^-a) with the hardware exp2 (v_exp_f32) and
 // reciprocal: relative error a few ulp for |a| < 80, exactly 1/2 at a = 0,
 // saturating to 0 or 1 (never NaN) for large |a|.

@@ -20,6 +20,12 @@ struct DwsepShape {
 // workgroup into ws[b * parts_per_item + part] for a fixed-order reduction.
 enum OutMode { OUT_SUM_ATOMIC = 0, OUT_MAP = 1, OUT_PARTIAL = 2 };
 
+// The generalised pool: max instead of mean, a ReLU between the conv and the
+// pool, PyTorch's ceil output size (partial windows at the bottom/right).
+struct PoolOpts {
+    bool pool_max, relu, ceil_mode;
+};
+
 // Returns true (and fills lds_bytes) if the MFMA direct-conv kernel has an
 // instance for (K, S) and its LDS tile for Cin channels fits one workgroup.
 bool conv2d_mfma_supported(int Cin, int K, int S, size_t* lds_bytes);
@@ -38,6 +44,16 @@ hipError_t conv2d_simple_launch(const Conv2dShape& s, const float* x, const floa
 int64_t conv2d_mfma_parts(const Conv2dShape& s);
 int64_t conv2d_boxsum_parts(const Conv2dShape& s);
 int64_t conv2d_simple_parts(const Conv2dShape& s);
+// Generalised-pool kernels (conv2d_pool_ex.hip).  `s.PH`, `s.PW` are the
+// pooled sizes under o.ceil_mode.  The matrix-core kernel has one instance
+// (K = 3, s = 4); the general kernel takes any shape.
+bool conv2d_elem_supported(int Cin, int K, int S);
+int64_t conv2d_elem_parts(const Conv2dShape& s);
+int64_t conv2d_general_parts(const Conv2dShape& s);
+hipError_t conv2d_elem_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                              int mode, const PoolOpts& o, hipStream_t stream);
+hipError_t conv2d_general_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
+                                 float* dst, int mode, const PoolOpts& o, hipStream_t stream);
 // out[b] = sum of ws[b*parts .. b*parts+parts-1], in a fixed order.
 hipError_t reduce_partials(const float* ws, int64_t parts, int B, float* out, hipStream_t stream);
 hipError_t fill_zero(float* p, int64_t n, hipStream_t stream);

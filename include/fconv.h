@@ -138,7 +138,7 @@ int fconv2d_pool_sigmoid_sum_det_workspace(int64_t B, int64_t Cin, int64_t H, in
  * This is the elementwise view the fused scalar hides; it exists for
  * verification and costs an extra HBM write of B*Cout*PH*PW floats.
  * Errors as fconv2d_pool_sigmoid_sum_algo; with PH or PW = 0 nothing is
- * written.
+ * written and `pooled` may be NULL (it must not be NULL otherwise).
  */
 int fconv2d_pool_map(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
                      const float* w, int64_t Cout, int64_t K, const float* bias, int64_t pool,
@@ -151,6 +151,65 @@ int fconv2d_pool_out_size(int64_t H, int64_t W, int64_t K, int64_t pool, int64_t
 /* The algorithm FCONV_ALGO_AUTO would run for this shape (a FCONV_ALGO_*
  * value), or FCONV_EINVAL.  Pure host logic, no device access. */
 int fconv2d_select_algo(int64_t Cin, int64_t Cout, int64_t K, int64_t pool);
+
+/*
+ * Generalised pool (the Conv2D + ReLU + MaxPool fused operator that the
+ * 新智元 article on the KernelBench / POPCORNBENCH results lists, on top of
+ * the l2_p65 chain):
+ *
+ *   out[b] = sum_{co,ph,pw} sigmoid( POOL_{(y,x) in window(ph,pw)} act(conv[b,co,y,x]) )
+ *   conv   as in fconv2d_pool_sigmoid_sum (bias included before act)
+ *   act    = max(., 0) with FCONV_RELU, else the identity
+ *   POOL   = mean over the window's elements (FCONV_POOL_AVG) or their
+ *            maximum (FCONV_POOL_MAX)
+ *   window(ph,pw) = rows [ph*pool, min(ph*pool+pool, Hc)) x columns
+ *            [pw*pool, min(pw*pool+pool, Wc))
+ *   PH = floor(Hc/pool), or ceil(Hc/pool) with FCONV_CEIL_MODE (PW alike).
+ *
+ * This is PyTorch's AvgPool2d / MaxPool2d with kernel = stride = pool, no
+ * padding, ceil_mode as flagged: in ceil mode the last window of a row or
+ * column is clipped to the map and a clipped window averages over its
+ * valid elements only (no padding means every window starts inside the map).
+ * FCONV_POOL_AVG with flags 0 is exactly fconv2d_pool_sigmoid_sum.
+ * NaN inputs: the maximum of a window that holds a NaN is unspecified.
+ */
+#define FCONV_POOL_AVG 0
+#define FCONV_POOL_MAX 1
+#define FCONV_RELU 1      /* flag: ReLU after the conv + bias, before the pool */
+#define FCONV_CEIL_MODE 2 /* flag: ceil output size, clipped last windows      */
+
+/*
+ * fconv2d_pool_sigmoid_sum_ex -- the fused sum with the generalised pool.
+ *   pool_mode  FCONV_POOL_AVG or FCONV_POOL_MAX
+ *   flags      0 or an OR of FCONV_RELU, FCONV_CEIL_MODE
+ *   algo       FCONV_ALGO_AUTO, DIRECT_MFMA (one instance: K = 3, pool = 4,
+ *              Cin up to about 220), DIRECT_SIMPLE (any shape) or, only for
+ *              FCONV_POOL_AVG with flags 0, BOXSUM.  AUTO picks DIRECT_MFMA
+ *              where it has an instance, else DIRECT_SIMPLE (for the plain
+ *              average pool it picks as fconv2d_pool_sigmoid_sum does).
+ * Other arguments, layouts and errors as fconv2d_pool_sigmoid_sum_algo;
+ * additionally FCONV_EINVAL for an unknown pool_mode or flag bit, and
+ * FCONV_EUNSUPPORTED for BOXSUM with a max pool, ReLU or ceil mode (the
+ * box-sum identity needs a linear pool over full windows).
+ */
+int fconv2d_pool_sigmoid_sum_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
+                                const float* w, int64_t Cout, int64_t K, const float* bias,
+                                int64_t pool, int pool_mode, int flags, int algo, float* out,
+                                void* stream);
+
+/* The pre-sigmoid pooled map [B, Cout, PH, PW] of fconv2d_pool_sigmoid_sum_ex
+ * (PH, PW as fconv2d_pool_out_size_ex reports), computed by the same kernels.
+ * Arguments and errors as fconv2d_pool_sigmoid_sum_ex; `pooled` may be NULL
+ * when the map has no elements. */
+int fconv2d_pool_map_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
+                        const float* w, int64_t Cout, int64_t K, const float* bias, int64_t pool,
+                        int pool_mode, int flags, int algo, float* pooled, void* stream);
+
+/* PH, PW of the generalised pool (FCONV_CEIL_MODE in flags selects ceil;
+ * FCONV_RELU is accepted and ignored).  Host only.  FCONV_EINVAL on sizes
+ * < 1, H < K, W < K or an unknown flag bit. */
+int fconv2d_pool_out_size_ex(int64_t H, int64_t W, int64_t K, int64_t pool, int flags, int64_t* PH,
+                             int64_t* PW);
 
 /*
  * dwsep_conv1d

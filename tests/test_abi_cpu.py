@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ["fconv2d_pool_sigmoid_sum", "dwsep_conv1d", "fconv2d_pool_map", "fconv_strerror",
                  "fconv_version", "fconv2d_pool_sigmoid_sum_algo", "fconv2d_pool_out_size",
-                 "fconv2d_select_algo", "dwsep_conv1d_out_len"]:
+                 "fconv2d_select_algo", "dwsep_conv1d_out_len", "fconv2d_pool_sigmoid_sum_ex",
+                 "fconv2d_pool_map_ex", "fconv2d_pool_out_size_ex"]:
         assert must in names, must
 
 
@@ -139,6 +140,72 @@ def test_conv2d_entry_points_share_checks(lib):
     assert lib.fconv2d_pool_sigmoid_sum(None, 1, 1, 8, 8, FAKE, 1, 3, None, 2, FAKE, None) == EINVAL
     assert lib.fconv2d_pool_map(FAKE, 1, 1, 8, 8, FAKE, 1, 3, None, 0, 0, FAKE, None) == EINVAL
     assert lib.fconv2d_pool_map(FAKE, 1, 1, 8, 8, FAKE, 1, 9, None, 2, 1, FAKE, None) == EINVAL  # H < K
+
+
+def conv_ex(lib, x=FAKE, B=1, Cin=1, H=8, W=8, w=FAKE, Cout=1, K=3, b=None, pool=2, pool_mode=1, flags=0, algo=0,
+            out=FAKE, fn="fconv2d_pool_sigmoid_sum_ex"):
+    return getattr(lib, fn)(x, B, Cin, H, W, w, Cout, K, b, pool, pool_mode, flags, algo, out, None)
+
+
+@pytest.mark.parametrize("fn", ["fconv2d_pool_sigmoid_sum_ex", "fconv2d_pool_map_ex"])
+@pytest.mark.parametrize("kw", [
+    dict(pool_mode=2), dict(pool_mode=-1),   # unknown pool
+    dict(flags=4), dict(flags=-1),           # unknown flag bits
+    dict(algo=4), dict(algo=-1),             # unknown algorithm
+    dict(x=None), dict(out=None), dict(pool=0), dict(H=2, K=3),
+    dict(pool_mode=0, flags=0, x=None),      # the plain average pool takes the base checks
+])
+def test_conv2d_ex_einval(lib, fn, kw):
+    assert conv_ex(lib, fn=fn, **kw) == EINVAL
+
+
+def test_empty_map_may_be_null(lib):
+    # 3 x 7 conv map, pool 4: no pooled rows in floor mode -> nothing to write, NULL accepted
+    assert lib.fconv2d_pool_map(FAKE, 1, 2, 5, 9, FAKE, 3, 3, None, 4, 0, None, None) == 0
+    assert conv_ex(lib, H=5, W=9, pool=4, out=None, fn="fconv2d_pool_map_ex") == 0
+    # ceil mode has one pooled row there, so NULL is an error
+    assert conv_ex(lib, H=5, W=9, pool=4, flags=2, out=None, fn="fconv2d_pool_map_ex") == EINVAL
+    assert lib.fconv2d_pool_map(FAKE, 1, 2, 8, 9, FAKE, 3, 3, None, 4, 0, None, None) == EINVAL
+
+
+def test_conv2d_ex_unsupported(lib):
+    assert conv_ex(lib, algo=3) == EUNSUP                          # box-sum needs a linear pool
+    assert conv_ex(lib, pool_mode=0, flags=1, algo=3) == EUNSUP    # ... without ReLU
+    assert conv_ex(lib, pool_mode=0, flags=2, algo=3) == EUNSUP    # ... over full windows
+    assert conv_ex(lib, K=5, pool=4, algo=1, H=16, W=16) == EUNSUP  # matrix-core instance: K = 3, s = 4 only
+    assert conv_ex(lib, K=3, pool=2, algo=1) == EUNSUP
+    assert conv_ex(lib, Cin=300, pool=4, algo=1, H=16, W=16) == EUNSUP  # its LDS tile does not fit
+    assert conv_ex(lib, B=70000) == EUNSUP
+
+
+def test_out_size_ex_matches_torch_pooling():
+    import torch
+
+    import fp32_convolution_amd as fc
+
+    F = torch.nn.functional
+    for n in range(3, 30):
+        for K, s in [(3, 4), (3, 2), (5, 3), (1, 7)]:
+            if n < K:
+                continue
+            for ceil_mode in (False, True):
+                ph, pw = fc.conv2d_out_size(n, n + 2, K, s, ceil_mode=ceil_mode)
+                if n - K + 1 < s and not ceil_mode:
+                    assert ph == 0
+                    continue
+                shape = F.max_pool2d(torch.zeros(1, 1, n - K + 1, n + 2 - K + 1), s, s, ceil_mode=ceil_mode).shape
+                assert (ph, pw) == (shape[2], shape[3]), (n, K, s, ceil_mode)
+
+
+def test_out_size_ex_checks(lib):
+    ph, pw = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.fconv2d_pool_out_size_ex(16, 16, 3, 4, 3, ctypes.byref(ph), ctypes.byref(pw)) == 0
+    assert (ph.value, pw.value) == (4, 4)
+    assert lib.fconv2d_pool_out_size_ex(16, 16, 3, 4, 1, ctypes.byref(ph), ctypes.byref(pw)) == 0
+    assert (ph.value, pw.value) == (3, 3)
+    assert lib.fconv2d_pool_out_size_ex(16, 16, 3, 4, 4, ctypes.byref(ph), ctypes.byref(pw)) == EINVAL
+    assert lib.fconv2d_pool_out_size_ex(2, 16, 3, 4, 0, ctypes.byref(ph), ctypes.byref(pw)) == EINVAL
+    assert lib.fconv2d_pool_out_size_ex(16, 16, 3, 4, 0, None, ctypes.byref(pw)) == EINVAL
 
 
 def dw(lib, x=FAKE, B=1, C=4, T=16, wd=FAKE, K=3, wp=FAKE, O=4, b=None, pad=1, y=FAKE):

@@ -1,0 +1,226 @@
+"""GPU parity of the generalised pool (max pooling, ReLU before the pool, ceil
+mode) against the CPU oracle, through the C ABI's _ex entry points.
+
+Bar as for the base chain: |gpu - oracle| <= 1e-4 + 1e-4*|oracle| element by
+element on the pre-sigmoid pooled map and on the fused sums, oracle in
+float64.  The shapes give several tiles of the matrix-core kernel (16 x 64
+conv outputs per tile), ragged tiles, partial ceil-mode windows of every
+width 1..3 at the bottom and right, Cin not a multiple of 4 and Cout above 64
+and not a multiple of 16.
+"""
+
+import itertools
+import sys
+
+import numpy as np
+import pytest
+
+import fconv_inputs as fi
+import oracle
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+RTOL = ATOL = 1e-4
+CANARY = 12345.678
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp32_convolution_amd as fc
+
+    return fc
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def assert_close(got, want, what):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    err = np.abs(got - want)
+    bound = ATOL + RTOL * np.abs(want)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst at {i}: "
+                             f"gpu={got[i]!r} oracle={want[i]!r}")
+
+
+AVG, MAX = oracle.POOL_AVG, oracle.POOL_MAX
+COMBOS = list(itertools.product([AVG, MAX], [False, True], [False, True]))  # pool, relu, ceil
+
+
+def combo_id(c):
+    return f"{'max' if c[0] == MAX else 'avg'}{'-relu' if c[1] else ''}{'-ceil' if c[2] else ''}"
+
+
+SHAPES = [
+    # B, Cin, H, W, Cout, K, s                   conv map -> floor / ceil pooled sizes
+    (2, 3, 16, 16, 4, 3, 4),        # 14x14 -> 3x3 / 4x4 (2-wide last windows)
+    (2, 8, 70, 75, 64, 3, 4),       # 68x73 -> 17x18 / 17x19 (1-wide last column)
+    (1, 5, 83, 150, 70, 3, 4),      # 81x148 -> 20x37 / 21x37 (1-row last), two channel ranges
+    (2, 12, 40, 131, 20, 3, 4),     # 38x129 -> 9x32 / 10x33 (2-row, 1-column last), 3 quads
+    (1, 8, 6, 8, 4, 3, 4),          # 4x6 -> 1x1 / 1x2
+    (1, 2, 5, 9, 3, 3, 4),          # 3x7 -> 0x1 (empty) / 1x2 (3-row window)
+    (1, 3, 20, 17, 5, 5, 3),        # K5/s3: one-thread-per-output kernel only
+    (1, 2, 11, 13, 4, 3, 2),        # K3/s2: likewise
+    (1, 4, 12, 12, 6, 1, 5),        # K = 1: likewise
+]
+
+
+def has_mfma(shape):
+    return shape[5] == 3 and shape[6] == 4
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("combo", COMBOS, ids=combo_id)
+@pytest.mark.parametrize("algo", [0, 1, 2])
+def test_pool_small(fc, shape, combo, algo):
+    B, Cin, H, W, Cout, K, s = shape
+    pool_mode, relu, ceil_mode = combo
+    announce(f"pool ex {shape} {combo_id(combo)} algo={algo}")
+    x, w, b = fi.conv2d_inputs(B, Cin, H, W, Cout, K, seed=51)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    kw = dict(algo=algo, pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+    plain = pool_mode == AVG and not relu and not ceil_mode
+    if algo == 1 and not has_mfma(shape) and not (plain and fc.conv2d_select_algo(Cin, Cout, K, s) != 2):
+        with pytest.raises(fc.FconvError) as err:
+            fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, **kw)
+        assert err.value.status == fc.FCONV_EUNSUPPORTED
+        return
+    want_out, want_map = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, want_pooled=True, pool_mode=pool_mode,
+                                                        relu=relu, ceil_mode=ceil_mode)
+    got_map = fc.conv2d_pool_map(xd, wd, bd, s, **kw).cpu().numpy()
+    got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, **kw).cpu().numpy()
+    assert_close(got_map, want_map, f"pooled map {shape} {combo_id(combo)}")
+    assert_close(got_out, want_out, f"out {shape} {combo_id(combo)}")
+
+
+@pytest.mark.parametrize("combo", COMBOS[1:], ids=combo_id)
+def test_pool_boxsum_refused(fc, combo):
+    pool_mode, relu, ceil_mode = combo
+    announce(f"pool ex box-sum refused {combo_id(combo)}")
+    x, w, b = fi.conv2d_inputs(1, 3, 16, 16, 4, 3, seed=52)
+    with pytest.raises(fc.FconvError) as err:
+        fc.conv2d_pool_sigmoid_sum(dev(x), dev(w), dev(b), 4, algo=3, pool_mode=pool_mode, relu=relu,
+                                   ceil_mode=ceil_mode)
+    assert err.value.status == fc.FCONV_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("algo", [1, 2])
+def test_pool_no_bias(fc, algo):
+    announce(f"pool ex no bias algo={algo}")
+    x, w, _ = fi.conv2d_inputs(2, 8, 41, 70, 20, 3, seed=53)
+    for pool_mode, relu, ceil_mode in COMBOS[1:]:
+        want = oracle.conv2d_pool_sigmoid_sum(x, w, None, 4, pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+        got = fc.conv2d_pool_sigmoid_sum(dev(x), dev(w), None, 4, algo=algo, pool_mode=pool_mode, relu=relu,
+                                         ceil_mode=ceil_mode).cpu().numpy()
+        assert_close(got, want, f"out, bias=None, {combo_id((pool_mode, relu, ceil_mode))}")
+
+
+def test_pool_relu_of_negative_map(fc):
+    # every conv output below zero: ReLU gives 0, sigma(0) = 1/2, out = Cout*PH*PW/2 exactly
+    announce("pool ex relu of a negative map")
+    x, w, _ = fi.conv2d_inputs(2, 8, 70, 75, 64, 3, seed=54)
+    b = np.full(64, -100.0, dtype=np.float32)
+    for pool_mode, ceil_mode, algo in itertools.product([AVG, MAX], [False, True], [1, 2]):
+        PH, PW = fc.conv2d_out_size(70, 75, 3, 4, ceil_mode=ceil_mode)
+        got = fc.conv2d_pool_sigmoid_sum(dev(x), dev(w), dev(b), 4, algo=algo, pool_mode=pool_mode, relu=True,
+                                         ceil_mode=ceil_mode).cpu().numpy()
+        assert (got == 64 * PH * PW / 2.0).all(), (pool_mode, ceil_mode, algo, got)
+
+
+def test_pool_ceil_equals_floor_when_windows_fit(fc):
+    announce("pool ex ceil == floor on a 68x72 map")
+    x, w, b = fi.conv2d_inputs(2, 8, 70, 74, 64, 3, seed=55)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    for pool_mode, relu in itertools.product([AVG, MAX], [False, True]):
+        f = fc.conv2d_pool_map(xd, wd, bd, 4, algo=1, pool_mode=pool_mode, relu=relu, ceil_mode=False)
+        c = fc.conv2d_pool_map(xd, wd, bd, 4, algo=1, pool_mode=pool_mode, relu=relu, ceil_mode=True)
+        if pool_mode == AVG and not relu:
+            # floor mode is the base chain (its own kernel, another summation order)
+            assert_close(c.cpu().numpy(), f.cpu().numpy(), "ceil vs floor, plain average")
+        else:
+            assert torch.equal(f, c)
+
+
+def padded(n, pad=1024):
+    whole = torch.full((n + 2 * pad,), CANARY, device="cuda")
+    return whole, whole[pad:pad + n]
+
+
+def canaries_intact(whole, n, pad=1024):
+    h = whole.cpu().numpy()
+    return bool((h[:pad] == np.float32(CANARY)).all() and (h[pad + n:] == np.float32(CANARY)).all())
+
+
+@pytest.mark.parametrize("algo", [1, 2])
+def test_pool_writes_only_its_outputs(fc, algo):
+    B, Cin, H, W, Cout, K, s = 2, 5, 41, 70, 70, 3, 4
+    announce(f"pool ex canaries algo={algo}")
+    x, w, b = fi.conv2d_inputs(B, Cin, H, W, Cout, K, seed=56)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    for pool_mode, relu, ceil_mode in COMBOS[1:]:
+        PH, PW = fc.conv2d_out_size(H, W, K, s, ceil_mode=ceil_mode)
+        n = B * Cout * PH * PW
+        whole, inner = padded(n)
+        fc.conv2d_pool_map(xd, wd, bd, s, out=inner.view(B, Cout, PH, PW), algo=algo, pool_mode=pool_mode,
+                           relu=relu, ceil_mode=ceil_mode)
+        torch.cuda.synchronize()
+        assert canaries_intact(whole, n)
+        assert not torch.isnan(inner).any() and (inner != np.float32(CANARY)).all()
+        wo, io = padded(B)
+        fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, out=io, algo=algo, pool_mode=pool_mode, relu=relu,
+                                   ceil_mode=ceil_mode)
+        torch.cuda.synchronize()
+        assert canaries_intact(wo, B)
+
+
+FULL_COMBOS = [(MAX, True, False), (MAX, True, True), (AVG, True, True), (MAX, False, True)]
+
+
+@pytest.fixture(scope="module")
+def full_inputs():
+    return fi.make("conv2d_full", seed=0)
+
+
+@pytest.mark.parametrize("combo", FULL_COMBOS, ids=combo_id)
+def test_pool_full_size(fc, full_inputs, combo):
+    # x[128,8,384,384], 8 -> 64, K 3, s 4: the matrix-core kernel in the launch the benchmark times
+    pool_mode, relu, ceil_mode = combo
+    announce(f"pool ex full size {combo_id(combo)}")
+    x, w, b = full_inputs
+    s = 4
+    kw = dict(algo=0, pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, **kw).cpu().numpy()
+    got_map = fc.conv2d_pool_map(xd, wd, bd, s, **kw).cpu().numpy()
+    idx = [0, 127]
+    want_out = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, batch_idx=idx, pool_mode=pool_mode, relu=relu,
+                                              ceil_mode=ceil_mode)
+    assert_close(got_out[idx], want_out, f"out[{idx}]")
+    sig = (1.0 / (1.0 + np.exp(-got_map.astype(np.float64)))).sum(axis=(1, 2, 3))
+    assert_close(got_out, sig, "fused sum vs sigmoid(map) sum")
+    B, Cout, PH, PW = got_map.shape
+    assert (PH, PW) == ((96, 96) if ceil_mode else (95, 95))
+    rng = np.random.default_rng(57)
+    n = 20000
+    samp = np.stack([rng.integers(0, B, n), rng.integers(0, Cout, n), rng.integers(0, PH, n),
+                     rng.integers(0, PW, n)], axis=1)
+    edge = [0, 1, 3, 4, 15, 16, 31, 32, PH - 2, PH - 1]
+    extra = [(bb, co, ph, pw) for bb in (0, B - 1) for co in (0, 15, 16, Cout - 1)
+             for ph in edge for pw in edge]
+    samp = np.concatenate([samp, np.array(extra)], axis=0)
+    want = oracle.conv2d_pooled_at(x, w, b, s, samp, pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+    assert_close(got_map[tuple(samp.T)], want, "sampled pooled map")
