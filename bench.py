@@ -48,6 +48,8 @@ KERNEL_SOURCES = {
                                   "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_dense_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                            "fp32_convolution_amd/csrc/fconv_device.hpp"],
+    "conv2d_pool_elem_kernel": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
+                                "fp32_convolution_amd/csrc/fconv_device.hpp"],
 }
 
 
@@ -310,6 +312,11 @@ def main():
                                                        cc["pool"], fc.ALGO_DIRECT_MFMA) // 4, device=dev)
     ms_det = time_calls(lambda: fc.conv2d_pool_sigmoid_sum_det(x, w, b, cc["pool"], out=out_det,
                                                                algo=fc.ALGO_DIRECT_MFMA, workspace=ws_det))
+    # Conv2D + ReLU + MaxPool (floor): the per-conv-output matrix-core kernel,
+    # the same multiply-adds as the direct average-pool kernel.
+    out_mx = torch.empty_like(out)
+    ms_mx = time_calls(lambda: fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=out_mx, algo=fc.ALGO_DIRECT_MFMA,
+                                                          pool_mode=fc.POOL_MAX, relu=True))
     y_dense = torch.empty_like(y)
     ms_dense = time_calls(lambda: fc.dwsep_conv1d(xd, wdw, wpw, bpw, dc["pad"], out=y_dense, algo=fc.DWSEP_DENSE))
 
@@ -368,6 +375,12 @@ def main():
     k_det = kstats(ms_det, f_conv, b_conv)
     k_det["algorithm"] = "direct MFMA, deterministic (partials + fixed-order reduction)"
     k_det["matches_atomic_within_tol"] = bool(((out_det - out).abs() <= 1e-4 + 1e-4 * out.abs()).all().item())
+    k_mx = kstats(ms_mx, f_conv, b_conv)
+    k_mx["algorithm"] = "Conv2d -> ReLU -> MaxPool2d 4 (floor) -> sigmoid -> sum, per-conv-output MFMA kernel"
+    am = f_conv / (k_mx["ms_mean"] * 1e-3) / 1e12
+    k_mx["roofline"] = {"bound": "mfma", "achieved": round(am, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(am / PEAK_FP32_TFLOPS, 4),
+                        "traffic": measured_traffic("conv2d_pool_elem_kernel")}
     f_dense = dwsep_dense_flops(dc)
     k_dense = kstats(ms_dense, f_dense, b_dw)
     k_dense["algorithm"] = "dense-fused combined weight (FCONV_DWSEP_DENSE), own FLOPs C*K*O per step"
@@ -395,7 +408,7 @@ def main():
         },
         "kernels": {"fconv2d_pool_sigmoid_sum": k_conv, "dwsep_conv1d": k_dw},
         "variants": {"fconv2d_pool_sigmoid_sum_boxsum": k_box, "fconv2d_pool_sigmoid_sum_det": k_det,
-                     "dwsep_conv1d_dense": k_dense},
+                     "fconv2d_pool_sigmoid_sum_ex_relu_maxpool": k_mx, "dwsep_conv1d_dense": k_dense},
         "roofline": {
             "kernel": "fconv2d_pool_sigmoid_sum (conv2d_pool_mfma_kernel) on " + CONV,
             "bound": "mfma",

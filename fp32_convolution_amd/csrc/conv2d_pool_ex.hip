@@ -33,6 +33,8 @@
 //  * conv2d_pool_general_kernel: one thread per pooled output, any shape.
 #include <math.h>
 
+#include <type_traits>
+
 #include "fconv_device.hpp"
 #include "fconv_internal.hpp"
 
@@ -111,7 +113,7 @@ struct ElemK3S4 {
 };
 
 template <int POOL_MAX, int MODE>
-__global__ __launch_bounds__(ElemK3S4::NT) void conv2d_pool_elem_kernel(
+__global__ __launch_bounds__(ElemK3S4::NT, 3) void conv2d_pool_elem_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane, int tiles_w,
     int relu, int ceil_mode) {
@@ -219,80 +221,79 @@ __global__ __launch_bounds__(ElemK3S4::NT) void conv2d_pool_elem_kernel(
     const int co_fin = co0 + 4 * g + (l16 & 3);
     auto pool2 = [](float a, float c) { return POOL_MAX ? fmaxf(a, c) : a + c; };
 
-    float lsum = 0.f;
-    const int nrow_tile = min(TPH, PH - ph0);
-    for (int pr = 0; pr < nrow_tile; ++pr) {
-        floatx4 acc[NCB][S];
+    // One channel quad of one pooled row.  In the first quad the first MFMA
+    // into each accumulator block takes the bias as its C operand, so the
+    // accumulators never need a separate initialisation.
+    floatx4 acc[NCB][S];
+    auto quad = [&](int q, int pr, auto first_tag) {
+        constexpr bool FIRST = decltype(first_tag)::value;
+        // The next quad's weights (quad 0 again after the last: the next
+        // pooled row starts there) load under this quad's MFMAs.
+        load_a(a_nxt, q + 1 < CINQ ? q + 1 : 0);
+        const int off0 = q * plane + pr * S * RP;
+        float bcur[NCB][K], bnxt[NCB][K];
+        load_row(bcur, off0);
 #pragma unroll
-        for (int nb = 0; nb < NCB; ++nb)
+        for (int rr = 0; rr < NR; ++rr) {
+            if (rr + 1 < NR) load_row(bnxt, off0 + (rr + 1) * RP);
 #pragma unroll
-            for (int dy = 0; dy < S; ++dy) acc[nb][dy] = bco;
-
-        for (int q = 0; q < CINQ; ++q) {
-            // The next quad's weights (quad 0 again after the last: the next
-            // pooled row starts there) load under this quad's MFMAs.
-            load_a(a_nxt, q + 1 < CINQ ? q + 1 : 0);
-            const int off0 = q * plane + pr * S * RP;
-            float bcur[NCB][K], bnxt[NCB][K];
-            load_row(bcur, off0);
+            for (int ky = 0; ky < K; ++ky) {
+                const int dy = rr - ky;
+                if (dy < 0 || dy >= S) continue;
 #pragma unroll
-            for (int rr = 0; rr < NR; ++rr) {
-                if (rr + 1 < NR) load_row(bnxt, off0 + (rr + 1) * RP);
-#pragma unroll
-                for (int ky = 0; ky < K; ++ky) {
-                    const int dy = rr - ky;
-                    if (dy < 0 || dy >= S) continue;
-#pragma unroll
-                    for (int kx = 0; kx < K; ++kx)
-#pragma unroll
-                        for (int nb = 0; nb < NCB; ++nb)
-                            acc[nb][dy] = mfma_16x16x4(a_cur[ky][kx], bcur[nb][kx], acc[nb][dy]);
-                }
-                if (rr + 1 < NR) {
+                for (int kx = 0; kx < K; ++kx)
 #pragma unroll
                     for (int nb = 0; nb < NCB; ++nb)
-#pragma unroll
-                        for (int kx = 0; kx < K; ++kx) bcur[nb][kx] = bnxt[nb][kx];
-                }
+                        acc[nb][dy] = mfma_16x16x4(a_cur[ky][kx], bcur[nb][kx],
+                                                   (FIRST && ky == 0 && kx == 0) ? bco : acc[nb][dy]);
             }
+            if (rr + 1 < NR) {
 #pragma unroll
-            for (int ky = 0; ky < K; ++ky)
+                for (int nb = 0; nb < NCB; ++nb)
 #pragma unroll
-                for (int kx = 0; kx < K; ++kx) a_cur[ky][kx] = a_nxt[ky][kx];
+                    for (int kx = 0; kx < K; ++kx) bcur[nb][kx] = bnxt[nb][kx];
+            }
         }
+#pragma unroll
+        for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+            for (int kx = 0; kx < K; ++kx) a_cur[ky][kx] = a_nxt[ky][kx];
+    };
 
-        // Epilogue of pooled row ph.  Lane (g, l16) holds in acc[nb][dy][r]
-        // the conv output of channel co0 + 4g + r at conv row ph*S + dy,
-        // column x0 + nb*16 + l16.
-        const int ph = ph0 + pr;
-        const int yr = y0 + pr * S;
-        // Conv outputs outside the map exist only in partial (ceil-mode)
-        // windows at the bottom and right edges; they are masked there.
-        const bool edge = ceil_mode && (yr + S > Hc || x0 + TPW * S > Wc);
+    float lsum = 0.f;
+    auto pool_row = [&](const floatx4 (&ac)[NCB][S], int ph, int yr, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
         const float fill = POOL_MAX ? -INFINITY : 0.f;
 #pragma unroll
         for (int nb = 0; nb < NCB; ++nb) {
+            float v[S][4];
+#pragma unroll
+            for (int dy = 0; dy < S; ++dy)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[dy][r] = ac[nb][dy][r];
             if (!POOL_MAX && relu) {
 #pragma unroll
                 for (int dy = 0; dy < S; ++dy)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[nb][dy][r] = fmaxf(acc[nb][dy][r], 0.f);
+                    for (int r = 0; r < 4; ++r) v[dy][r] = fmaxf(v[dy][r], 0.f);
             }
-            if (edge) {
+            if constexpr (EDGE) {
                 const bool col_ok = x0 + nb * 16 + l16 < Wc;
 #pragma unroll
                 for (int dy = 0; dy < S; ++dy) {
                     const bool ok = col_ok && (yr + dy < Hc);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[nb][dy][r] = ok ? acc[nb][dy][r] : fill;
+                    for (int r = 0; r < 4; ++r) v[dy][r] = ok ? v[dy][r] : fill;
                 }
             }
             // Over the window's rows, inside the lane.
-            floatx4 m = acc[nb][0];
+            float m[4];
 #pragma unroll
-            for (int dy = 1; dy < S; ++dy)
+            for (int r = 0; r < 4; ++r) {
+                m[r] = v[0][r];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) m[r] = pool2(m[r], acc[nb][dy][r]);
+                for (int dy = 1; dy < S; ++dy) m[r] = pool2(m[r], v[dy][r]);
+            }
             // Over the window's 4 columns (lanes 4j..4j+3 of the 16-lane row).
             // Step 1 pairs lanes l, l^1: the even lane keeps channels r = 0, 2
             // and sends r = 1, 3; the odd lane the reverse.  Step 2 pairs
@@ -309,9 +310,10 @@ __global__ __launch_bounds__(ElemK3S4::NT) void conv2d_pool_elem_kernel(
             if (co_fin < Cout && pw < PW) {
                 if (POOL_MAX) {
                     if (relu) pv = fmaxf(pv, 0.f);  // ReLU commutes with max
+                } else if (EDGE) {
+                    pv = pv / (float)(min(S, Hc - ph * S) * min(S, Wc - pw * S));
                 } else {
-                    const int cnt = edge ? min(S, Hc - ph * S) * min(S, Wc - pw * S) : S * S;
-                    pv = edge ? pv / (float)cnt : pv * (1.0f / (S * S));
+                    pv = pv * (1.0f / (S * S));
                 }
                 if constexpr (MODE == OUT_MAP)
                     dst[(((size_t)b * Cout + co_fin) * PH + ph) * PW + pw] = pv;
@@ -319,6 +321,25 @@ __global__ __launch_bounds__(ElemK3S4::NT) void conv2d_pool_elem_kernel(
                     lsum += logistic(pv);
             }
         }
+    };
+
+    const int nrow_tile = min(TPH, PH - ph0);
+    for (int pr = 0; pr < nrow_tile; ++pr) {
+        quad(0, pr, std::true_type{});
+        for (int q = 1; q < CINQ; ++q) quad(q, pr, std::false_type{});
+
+        // Epilogue of pooled row ph.  Lane (g, l16) holds in acc[nb][dy][r]
+        // the conv output of channel co0 + 4g + r at conv row ph*S + dy,
+        // column x0 + nb*16 + l16.  The pool works on register copies.
+        // Conv outputs outside the map exist only in partial (ceil-mode)
+        // windows at the bottom and right edges; those rows take a separate
+        // copy of the epilogue that masks them.
+        const int ph = ph0 + pr;
+        const int yr = y0 + pr * S;
+        if (ceil_mode && (yr + S > Hc || x0 + TPW * S > Wc))
+            pool_row(acc, ph, yr, std::true_type{});
+        else
+            pool_row(acc, ph, yr, std::false_type{});
     }
 
     if constexpr (MODE != OUT_MAP) {
