@@ -28,6 +28,9 @@
 //  * Weights stream from L2/L1 straight into registers (they are 18-200 KB).
 //  * Epilogue: scale by 1/s^2, add bias, sigmoid, lane sum, wave + LDS
 //    reduction, one float atomic per workgroup into out[b].
+// Instances: K5/s3, K3/s2, K3/s3.  K3/s4 runs on conv2d_pool_elem_kernel
+// (conv2d_pool_ex.hip), which keeps each conv output in an accumulator and
+// pools in registers: the same multiply-adds, measured slightly faster there.
 #include "fconv_device.hpp"
 #include "fconv_internal.hpp"
 
@@ -256,18 +259,17 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
     }
 }
 
-// Instances (tilings measured on MI355X).  K3/s4 and the other K3 pools: a
-// 4x16 pooled tile, 4 waves each owning 16 output channels of a 64-channel
-// range and all 64 positions.  K5/s3: a 4x12 tile (84 = 21*4 = 7*12, so an
-// 84x84 map has no ragged tiles), 8 waves of 16 channels each.
+// Instances (tilings measured on MI355X).  K3/s2 and K3/s3: a 4x16 pooled
+// tile, 4 waves each owning 16 output channels of a 64-channel range and all
+// 64 positions.  K5/s3: a 4x12 tile (84 = 21*4 = 7*12, so an 84x84 map has no
+// ragged tiles), 8 waves of 16 channels each.  K3/s4 runs on the
+// per-conv-output kernel of conv2d_pool_ex.hip (same multiply-adds; it
+// measured 4 % faster than this kernel's 4x16 instance: it skips the padded
+// pooled rows of a ragged tile and its row-major tile has no bank conflicts).
 // The FCONV_CFG_* macros let a build override an instance's tiling.
-#ifndef FCONV_CFG_K3S4
-#define FCONV_CFG_K3S4 3, 4, 1, 4, 4, 1, 4, 16
-#endif
 #ifndef FCONV_CFG_K5S3
 #define FCONV_CFG_K5S3 5, 3, 1, 3, 8, 1, 4, 12
 #endif
-using CfgK3S4 = DirectCfg<FCONV_CFG_K3S4>;
 using CfgK5S3 = DirectCfg<FCONV_CFG_K5S3>;
 using CfgK3S2 = DirectCfg<3, 2, 1, 4, 4, 1, 4, 16>;
 using CfgK3S3 = DirectCfg<3, 3, 1, 4, 4, 1, 4, 16>;
@@ -290,14 +292,13 @@ static size_t lds_bytes_for(int Cin) {
 
 static constexpr size_t kMaxLds = 160 * 1024 - 256;  // dynamic share; the rest holds the reduction slots
 
-bool conv2d_mfma_supported(int Cin, int K, int S, size_t* lds_bytes) {
+bool conv2d_mfma_supported(int Cin, int K, int S) {
     size_t bytes = 0;
-    if (K == 3 && S == 4) bytes = lds_bytes_for<CfgK3S4>(Cin);
-    else if (K == 5 && S == 3) bytes = lds_bytes_for<CfgK5S3>(Cin);
+    if (K == 3 && S == 4) return conv2d_elem_supported(Cin, K, S);
+    if (K == 5 && S == 3) bytes = lds_bytes_for<CfgK5S3>(Cin);
     else if (K == 3 && S == 2) bytes = lds_bytes_for<CfgK3S2>(Cin);
     else if (K == 3 && S == 3) bytes = lds_bytes_for<CfgK3S3>(Cin);
     else return false;
-    if (lds_bytes) *lds_bytes = bytes;
     return bytes <= kMaxLds;
 }
 
@@ -349,7 +350,7 @@ static hipError_t launch_direct(const Conv2dShape& s, const float* x, const floa
 
 hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
                               float* dst, int mode, hipStream_t stream) {
-    if (s.K == 3 && s.S == 4) return launch_direct<CfgK3S4>(s, x, w, bias, dst, mode, stream);
+    if (s.K == 3 && s.S == 4) return conv2d_elem_launch(s, x, w, bias, dst, mode, PoolOpts{false, false, false}, stream);
     if (s.K == 5 && s.S == 3) return launch_direct<CfgK5S3>(s, x, w, bias, dst, mode, stream);
     if (s.K == 3 && s.S == 2) return launch_direct<CfgK3S2>(s, x, w, bias, dst, mode, stream);
     if (s.K == 3 && s.S == 3) return launch_direct<CfgK3S3>(s, x, w, bias, dst, mode, stream);
@@ -358,8 +359,8 @@ hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float*
 
 int64_t conv2d_mfma_parts(const Conv2dShape& s) {
     dim3 g;
-    if (s.K == 3 && s.S == 4) g = direct_grid<CfgK3S4>(s);
-    else if (s.K == 5 && s.S == 3) g = direct_grid<CfgK5S3>(s);
+    if (s.K == 3 && s.S == 4) return conv2d_elem_parts(s);
+    if (s.K == 5 && s.S == 3) g = direct_grid<CfgK5S3>(s);
     else if (s.K == 3 && s.S == 2) g = direct_grid<CfgK3S2>(s);
     else if (s.K == 3 && s.S == 3) g = direct_grid<CfgK3S3>(s);
     else return -1;

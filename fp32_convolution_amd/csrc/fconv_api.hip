@@ -64,14 +64,14 @@ int check_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, c
 
 int auto_conv2d_algo(int Cin, int K, int S) {
     if (fconv::conv2d_boxsum_supported(Cin, K, S)) return FCONV_ALGO_BOXSUM;
-    if (fconv::conv2d_mfma_supported(Cin, K, S, nullptr)) return FCONV_ALGO_DIRECT_MFMA;
+    if (fconv::conv2d_mfma_supported(Cin, K, S)) return FCONV_ALGO_DIRECT_MFMA;
     return FCONV_ALGO_DIRECT_SIMPLE;
 }
 
 int pick_conv2d_algo(const Conv2dShape& s, int algo) {
     if (algo == FCONV_ALGO_AUTO) return auto_conv2d_algo(s.Cin, s.K, s.S);
     if (algo == FCONV_ALGO_DIRECT_MFMA)
-        return fconv::conv2d_mfma_supported(s.Cin, s.K, s.S, nullptr) ? algo : FCONV_EUNSUPPORTED;
+        return fconv::conv2d_mfma_supported(s.Cin, s.K, s.S) ? algo : FCONV_EUNSUPPORTED;
     if (algo == FCONV_ALGO_BOXSUM)
         return fconv::conv2d_boxsum_supported(s.Cin, s.K, s.S) ? algo : FCONV_EUNSUPPORTED;
     if (algo == FCONV_ALGO_DIRECT_SIMPLE) return algo;

@@ -26,9 +26,9 @@ struct PoolOpts {
     bool pool_max, relu, ceil_mode;
 };
 
-// Returns true (and fills lds_bytes) if the MFMA direct-conv kernel has an
-// instance for (K, S) and its LDS tile for Cin channels fits one workgroup.
-bool conv2d_mfma_supported(int Cin, int K, int S, size_t* lds_bytes);
+// Returns true if the MFMA direct-conv path has an instance for (K, S) and
+// its LDS tile for Cin channels fits one workgroup.
+bool conv2d_mfma_supported(int Cin, int K, int S);
 
 // Enqueue kernels; return hipSuccess or the launch error.  `mode` is an
 // OutMode; dst is out[B], pooled[B,Cout,PH,PW] or ws[B * parts_per_item].
