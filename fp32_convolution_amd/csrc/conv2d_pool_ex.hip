@@ -31,6 +31,7 @@
 //    block, none wasted.  The multiply-adds are those of the direct AvgPool
 //    kernel (s^2*Cin*K*K per pooled output), only grouped by conv output.
 //  * conv2d_pool_general_kernel: one thread per pooled output, any shape.
+#include <limits.h>
 #include <math.h>
 
 #include <type_traits>
@@ -116,7 +117,7 @@ template <int POOL_MAX, int MODE>
 __global__ __launch_bounds__(ElemK3S4::NT, 3) void conv2d_pool_elem_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane, int tiles_w,
-    int relu, int ceil_mode) {
+    int tiles, int co_ranges, int nblocks, int relu, int ceil_mode) {
     using C = ElemK3S4;
     constexpr int K = C::K, S = C::S, NCB = C::NCB, TPH = C::TPH, TPW = C::TPW;
     constexpr int IH = C::IH, IW = C::IW, RP = C::RP, NR = C::NR;
@@ -129,12 +130,22 @@ __global__ __launch_bounds__(ElemK3S4::NT, 3) void conv2d_pool_elem_kernel(
     const int wave = tid >> 6;
     const int g = lane >> 4;    // MFMA k-slot: channel group
     const int l16 = lane & 15;  // row of A / column of B
-    const int tile_y = blockIdx.x / tiles_w;
-    const int tile_x = blockIdx.x - tile_y * tiles_w;
-    const int b = blockIdx.z;
+    // Block order: the hardware deals block ids to the 8 XCDs round-robin;
+    // xcd_spread gives each XCD one contiguous run of logical ids, ordered
+    // (batch item, tile row, tile column, channel range) with the channel
+    // range fastest.  Tiles that share input (the channel ranges of one tile,
+    // its right and lower neighbours with their halo lines) then run close
+    // together in time on one XCD and find that input in its L2.
+    const int lid = xcd_spread(blockIdx.x, nblocks);
+    const int cor = lid % co_ranges;
+    const int rest = lid / co_ranges;
+    const int tile = rest % tiles;
+    const int b = rest / tiles;
+    const int tile_y = tile / tiles_w;
+    const int tile_x = tile - tile_y * tiles_w;
     const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
     const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
-    const int co0 = blockIdx.y * C::CO_RANGE + wave * 16;
+    const int co0 = cor * C::CO_RANGE + wave * 16;
     const int Hc = H - K + 1, Wc = W - K + 1;
 
     // Weights of channel quad q: a[ky][kx] = w[co0 + l16, g*CINQ + q, ky, kx]
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(ElemK3S4::NT, 3) void conv2d_pool_elem_kernel(
             if constexpr (MODE == OUT_SUM_ATOMIC)
                 atomicAdd(dst + b, s);
             else
-                dst[(size_t)b * (gridDim.x * gridDim.y) + blockIdx.y * gridDim.x + blockIdx.x] = s;
+                dst[(size_t)b * (tiles * co_ranges) + tile * co_ranges + cor] = s;
         }
     }
 }
@@ -373,11 +384,17 @@ size_t elem_lds_bytes(int Cin) {
     return (size_t)4 * CINQ * elem_plane(CINQ) * sizeof(float);
 }
 
-dim3 elem_grid(const Conv2dShape& s) {
+struct ElemGrid {
+    int tiles_w, tiles, co_ranges;
+    int64_t nblocks;
+};
+
+ElemGrid elem_grid(const Conv2dShape& s) {
     using C = ElemK3S4;
     const int tiles_h = (s.PH + C::TPH - 1) / C::TPH;
     const int tiles_w = (s.PW + C::TPW - 1) / C::TPW;
-    return dim3(tiles_h * tiles_w, (s.Cout + C::CO_RANGE - 1) / C::CO_RANGE, s.B);
+    const int co_ranges = (s.Cout + C::CO_RANGE - 1) / C::CO_RANGE;
+    return {tiles_w, tiles_h * tiles_w, co_ranges, (int64_t)tiles_h * tiles_w * co_ranges * s.B};
 }
 
 template <int POOL_MAX, int MODE>
@@ -386,13 +403,14 @@ hipError_t launch_elem_as(const Conv2dShape& s, const float* x, const float* w, 
     const int CINQ = (s.Cin + 3) / 4;
     const int plane = elem_plane(CINQ);
     const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
-    const int tiles_w = (s.PW + ElemK3S4::TPW - 1) / ElemK3S4::TPW;
+    const ElemGrid g = elem_grid(s);
+    if (g.nblocks > INT32_MAX) return hipErrorInvalidValue;
     const void* fn = (const void*)conv2d_pool_elem_kernel<POOL_MAX, MODE>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((conv2d_pool_elem_kernel<POOL_MAX, MODE>), elem_grid(s), dim3(ElemK3S4::NT), lds, stream, x,
-                       w, bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, tiles_w, o.relu ? 1 : 0,
-                       o.ceil_mode ? 1 : 0);
+    hipLaunchKernelGGL((conv2d_pool_elem_kernel<POOL_MAX, MODE>), dim3((unsigned)g.nblocks), dim3(ElemK3S4::NT), lds,
+                       stream, x, w, bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, g.tiles_w, g.tiles,
+                       g.co_ranges, (int)g.nblocks, o.relu ? 1 : 0, o.ceil_mode ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -411,8 +429,8 @@ bool conv2d_elem_supported(int Cin, int K, int S) {
 }
 
 int64_t conv2d_elem_parts(const Conv2dShape& s) {
-    const dim3 g = elem_grid(s);
-    return (int64_t)g.x * g.y;
+    const ElemGrid g = elem_grid(s);
+    return (int64_t)g.tiles * g.co_ranges;
 }
 
 hipError_t conv2d_elem_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
