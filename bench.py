@@ -36,25 +36,31 @@ PEAK_FP32_TFLOPS = 157.3  # MI355X dense fp32 (matrix cores), published
 PEAK_HBM_GBPS = 8000.0
 
 CONV = "conv2d_full"
+TAIL = "conv2d_tail"
 DW = "dwsep_full"
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # Sources that define the timed kernels; measured HBM traffic is reported
 # only while their hash matches the one recorded with the counters.
-# Keys are kernel-name prefixes as rocprofv3 prints them; the template
-# arguments of conv2d_pool_elem_kernel are <max pool, output mode>.
+# Keys are kernel-name parts as rocprofv3 prints them; the template arguments
+# of conv2d_pool_elem_kernel are <tiling <K, s, column blocks, pooled rows>,
+# max pool, output mode>.
 KERNEL_SOURCES = {
-    "conv2d_pool_elem_kernel<0, 0>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
-                                      "fp32_convolution_amd/csrc/fconv_device.hpp"],
+    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 0, 0>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
+                                                                  "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_tall_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                           "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "conv2d_pool_boxsum4_kernel": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
                                   "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_dense_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                            "fp32_convolution_amd/csrc/fconv_device.hpp"],
-    "conv2d_pool_elem_kernel<1, 0>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
-                                      "fp32_convolution_amd/csrc/fconv_device.hpp"],
+    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 1, 0>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
+                                                                  "fp32_convolution_amd/csrc/fconv_device.hpp"],
 }
+
+
+ELEM_AVG = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 0, 0>"
+ELEM_MAX = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 1, 0>"
 
 
 def sources_sha256(kernel):
@@ -337,6 +343,14 @@ def main():
     out_mx = torch.empty_like(out)
     ms_mx = time_calls(lambda: fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=out_mx, algo=fc.ALGO_DIRECT_MFMA,
                                                           pool_mode=fc.POOL_MAX, relu=True))
+    # The same on the K = 5, s = 3 workload (x[64,16,257,257], 16 -> 128).
+    tc = fi.WORKLOADS[TAIL]
+    xt, wt, bt = (torch.from_numpy(a).to(dev) for a in fi.make(TAIL, seed=args.seed))
+    out_tmx = torch.empty(tc["B"], device=dev)
+    ms_tmx = time_calls(lambda: fc.conv2d_pool_sigmoid_sum(xt, wt, bt, tc["pool"], out=out_tmx,
+                                                           algo=fc.ALGO_DIRECT_MFMA, pool_mode=fc.POOL_MAX,
+                                                           relu=True))
+    del xt
     y_dense = torch.empty_like(y)
     ms_dense = time_calls(lambda: fc.dwsep_conv1d(xd, wdw, wpw, bpw, dc["pad"], out=y_dense, algo=fc.DWSEP_DENSE))
 
@@ -375,7 +389,7 @@ def main():
 
     k_conv = kstats(ms_conv, f_conv, b_conv)
     k_dw = kstats(ms_dw, f_dw, b_dw)
-    k_conv["hbm_bytes_measured"] = measured_traffic("conv2d_pool_elem_kernel<0, 0>")
+    k_conv["hbm_bytes_measured"] = measured_traffic(ELEM_AVG)
     k_dw["hbm_bytes_measured"] = measured_traffic("dwsep_tall_kernel")
     k_dw["cold_ms_median"] = round(float(np.median(ms_cold)), 4)
     k_dw["cold_note"] = "each call after a 512 MB overwrite (inputs not in the 256 MB Infinity Cache)"
@@ -400,7 +414,11 @@ def main():
     am = f_conv / (k_mx["ms_mean"] * 1e-3) / 1e12
     k_mx["roofline"] = {"bound": "mfma", "achieved": round(am, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(am / PEAK_FP32_TFLOPS, 4),
-                        "traffic": measured_traffic("conv2d_pool_elem_kernel<1, 0>")}
+                        "traffic": measured_traffic(ELEM_MAX)}
+    f_tail = conv2d_flops(tc)
+    k_tmx = kstats(ms_tmx, f_tail, conv2d_bytes(tc))
+    k_tmx["algorithm"] = ("Conv2d k5 -> ReLU -> MaxPool2d 3 (floor) -> sigmoid -> sum on x[64,16,257,257], "
+                          "per-conv-output MFMA kernel (K = 5, s = 3 instance)")
     f_dense = dwsep_dense_flops(dc)
     k_dense = kstats(ms_dense, f_dense, b_dw)
     k_dense["algorithm"] = "dense-fused combined weight (FCONV_DWSEP_DENSE), own FLOPs C*K*O per step"
@@ -428,15 +446,16 @@ def main():
         },
         "kernels": {"fconv2d_pool_sigmoid_sum": k_conv, "dwsep_conv1d": k_dw},
         "variants": {"fconv2d_pool_sigmoid_sum_boxsum": k_box, "fconv2d_pool_sigmoid_sum_det": k_det,
-                     "fconv2d_pool_sigmoid_sum_ex_relu_maxpool": k_mx, "dwsep_conv1d_dense": k_dense},
+                     "fconv2d_pool_sigmoid_sum_ex_relu_maxpool": k_mx,
+                     "fconv2d_pool_sigmoid_sum_ex_relu_maxpool_k5s3": k_tmx, "dwsep_conv1d_dense": k_dense},
         "roofline": {
-            "kernel": "fconv2d_pool_sigmoid_sum, direct MFMA (conv2d_pool_elem_kernel<0, 0>) on " + CONV,
+            "kernel": f"fconv2d_pool_sigmoid_sum, direct MFMA ({ELEM_AVG}) on " + CONV,
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_FP32_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-            "traffic": measured_traffic("conv2d_pool_elem_kernel<0, 0>"),
+            "traffic": measured_traffic(ELEM_AVG),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         },
         "wall_s_timed_region": round(t_wall, 3),

@@ -95,32 +95,42 @@ __global__ __launch_bounds__(256) void conv2d_pool_general_kernel(
 
 int64_t conv2d_general_parts(const Conv2dShape& s) { return ((int64_t)s.Cout * s.PH * s.PW + 255) / 256; }
 
-// ---------------------------------------------------------------- K = 3, s = 4 on matrix cores
+// ---------------------------------------------------------------- on matrix cores
 
 // Tiling: a workgroup of 4 waves covers 64 output channels (16 per wave) and
 // a TPH x TPW pooled tile; each wave walks the tile's pooled rows one at a
-// time, holding NCB 16-column blocks x S window rows of accumulators.
-struct ElemK3S4 {
-    static constexpr int K = 3, S = 4;
-    static constexpr int NCB = 4;                 // 16-column blocks per wave
-    static constexpr int TPW = NCB * 16 / S;      // 16 pooled columns
-    static constexpr int TPH = 4;                 // pooled rows
+// time, holding NCB column blocks x S window rows of accumulators.  A column
+// block is the MFMA's 16 lanes of N: WPB = 16/S whole windows, CPB = WPB*S
+// conv columns (for s = 3 the 16th lane's column belongs to no window of its
+// block and is ignored).
+template <int K_, int S_, int NCB_, int TPH_>
+struct ElemCfg {
+    static constexpr int K = K_, S = S_, NCB = NCB_, TPH = TPH_;
+    static constexpr int WPB = 16 / S;                 // windows per column block
+    static constexpr int CPB = WPB * S;                // conv columns per column block
+    static constexpr int TPW = NCB * WPB;              // pooled columns per tile
     static constexpr int NW = 4, NT = 64 * NW;
     static constexpr int CO_RANGE = 16 * NW;
-    static constexpr int IH = TPH * S + K - 1;    // 18 input rows per tile
-    static constexpr int IW = TPW * S + K - 1;    // 66 input columns per tile
-    static constexpr int RP = IW;                 // LDS floats per row
-    static constexpr int NR = S + K - 1;          // input rows one pooled row reads
+    static constexpr int IH = TPH * S + K - 1;         // input rows per tile
+    static constexpr int IW = (NCB - 1) * CPB + 16 + K - 1;  // input columns the lanes read
+    static constexpr int RP = IW;                      // LDS floats per row
+    static constexpr int NR = S + K - 1;               // input rows one pooled row reads
+    static_assert(S == 2 || S == 3 || S == 4, "window reduction implemented for s = 2, 3, 4");
 };
 
-template <int POOL_MAX, int MODE>
-__global__ __launch_bounds__(ElemK3S4::NT, 3) void conv2d_pool_elem_kernel(
+// Instances: K = 3 with s = 2, 3, 4; K = 5 with s = 3.
+using ElemK3S4 = ElemCfg<3, 4, 4, 4>;  // 4 x 16 pooled tile, 18 x 66 input
+using ElemK3S2 = ElemCfg<3, 2, 4, 4>;  // 4 x 32 pooled tile, 10 x 66 input
+using ElemK3S3 = ElemCfg<3, 3, 4, 4>;  // 4 x 20 pooled tile, 14 x 63 input
+using ElemK5S3 = ElemCfg<5, 3, 2, 4>;  // 4 x 10 pooled tile, 16 x 35 input
+
+template <class C, int POOL_MAX, int MODE>
+__global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane, int tiles_w,
     int tiles, int co_ranges, int nblocks, int relu, int ceil_mode) {
-    using C = ElemK3S4;
     constexpr int K = C::K, S = C::S, NCB = C::NCB, TPH = C::TPH, TPW = C::TPW;
-    constexpr int IH = C::IH, IW = C::IW, RP = C::RP, NR = C::NR;
+    constexpr int IH = C::IH, IW = C::IW, RP = C::RP, NR = C::NR, WPB = C::WPB, CPB = C::CPB;
 
     extern __shared__ float lds[];
     __shared__ float red[C::NW];
@@ -223,13 +233,10 @@ __global__ __launch_bounds__(ElemK3S4::NT, 3) void conv2d_pool_elem_kernel(
 #pragma unroll
         for (int nb = 0; nb < NCB; ++nb)
 #pragma unroll
-            for (int kx = 0; kx < K; ++kx) bv[nb][kx] = lds[bbase + off + nb * 16 + kx];
+            for (int kx = 0; kx < K; ++kx) bv[nb][kx] = lds[bbase + off + nb * CPB + kx];
     };
 
-    // Lane roles in the pool: dx = l16 & 3 is the column inside a window and,
-    // after the transposing reduction, the channel r the lane finishes.
     const bool odd1 = (l16 & 1) != 0, odd2 = (l16 & 2) != 0;
-    const int co_fin = co0 + 4 * g + (l16 & 3);
     auto pool2 = [](float a, float c) { return POOL_MAX ? fmaxf(a, c) : a + c; };
 
     // One channel quad of one pooled row.  In the first quad the first MFMA
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(ElemK3S4::NT, 3) void conv2d_pool_elem_kernel(
                     for (int r = 0; r < 4; ++r) v[dy][r] = fmaxf(v[dy][r], 0.f);
             }
             if constexpr (EDGE) {
-                const bool col_ok = x0 + nb * 16 + l16 < Wc;
+                const bool col_ok = x0 + nb * CPB + l16 < Wc;
 #pragma unroll
                 for (int dy = 0; dy < S; ++dy) {
                     const bool ok = col_ok && (yr + dy < Hc);
@@ -305,31 +312,74 @@ __global__ __launch_bounds__(ElemK3S4::NT, 3) void conv2d_pool_elem_kernel(
 #pragma unroll
                 for (int dy = 1; dy < S; ++dy) m[r] = pool2(m[r], v[dy][r]);
             }
-            // Over the window's 4 columns (lanes 4j..4j+3 of the 16-lane row).
-            // Step 1 pairs lanes l, l^1: the even lane keeps channels r = 0, 2
-            // and sends r = 1, 3; the odd lane the reverse.  Step 2 pairs
-            // l, l^2 the same way over the two kept values.  Lane dx ends with
-            // channel r = dx over all four columns.
-            const float k01 = odd1 ? m[1] : m[0], s01 = odd1 ? m[0] : m[1];
-            const float k23 = odd1 ? m[3] : m[2], s23 = odd1 ? m[2] : m[3];
-            const float p01 = pool2(k01, quad_xor1(s01));
-            const float p23 = pool2(k23, quad_xor1(s23));
-            const float kk = odd2 ? p23 : p01, ss = odd2 ? p01 : p23;
-            float pv = pool2(kk, quad_xor2(ss));
-
-            const int pw = pw0 + nb * 4 + (l16 >> 2);
-            if (co_fin < Cout && pw < PW) {
-                if (POOL_MAX) {
-                    if (relu) pv = fmaxf(pv, 0.f);  // ReLU commutes with max
-                } else if (EDGE) {
-                    pv = pv / (float)(min(S, Hc - ph * S) * min(S, Wc - pw * S));
-                } else {
-                    pv = pv * (1.0f / (S * S));
+            // Over the window's columns, across lanes.  Each case leaves NV
+            // finished pooled values per lane, value i for channel
+            // co0 + 4g + chan[i] at window win of the block, valid where the
+            // lane finishes a window (fin).
+            constexpr int NV = S == 4 ? 1 : S == 2 ? 2 : 4;
+            float pv[NV];
+            int chan[NV];
+            int win;
+            bool fin;
+            if constexpr (S == 4) {
+                // Lanes 4j..4j+3 hold window j.  Step 1 pairs lanes l, l^1:
+                // the even lane keeps channels r = 0, 2 and sends r = 1, 3;
+                // the odd lane the reverse.  Step 2 pairs l, l^2 the same way
+                // over the two kept values.  Lane dx ends with channel r = dx
+                // over all four columns.
+                const float k01 = odd1 ? m[1] : m[0], s01 = odd1 ? m[0] : m[1];
+                const float k23 = odd1 ? m[3] : m[2], s23 = odd1 ? m[2] : m[3];
+                const float p01 = pool2(k01, quad_xor1(s01));
+                const float p23 = pool2(k23, quad_xor1(s23));
+                const float kk = odd2 ? p23 : p01, ss = odd2 ? p01 : p23;
+                pv[0] = pool2(kk, quad_xor2(ss));
+                chan[0] = l16 & 3;
+                win = l16 >> 2;
+                fin = true;
+            } else if constexpr (S == 2) {
+                // Lanes 2j, 2j+1 hold window j.  One pairing step as above:
+                // lane dx ends with channels dx and 2 + dx.
+                const float k01 = odd1 ? m[1] : m[0], s01 = odd1 ? m[0] : m[1];
+                const float k23 = odd1 ? m[3] : m[2], s23 = odd1 ? m[2] : m[3];
+                pv[0] = pool2(k01, quad_xor1(s01));
+                pv[1] = pool2(k23, quad_xor1(s23));
+                chan[0] = l16 & 1;
+                chan[1] = 2 + (l16 & 1);
+                win = l16 >> 1;
+                fin = true;
+            } else {
+                // Lanes 3j..3j+2 (j < 5) hold window j: the window's last lane
+                // gathers its two left neighbours (DPP row shifts) and
+                // finishes all four channels.
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pv[r] = pool2(pool2(m[r], row_shr1(m[r])), row_shr2(m[r]));
+                    chan[r] = r;
                 }
-                if constexpr (MODE == OUT_MAP)
-                    dst[(((size_t)b * Cout + co_fin) * PH + ph) * PW + pw] = pv;
-                else
-                    lsum += logistic(pv);
+                win = l16 / 3;
+                fin = (l16 % 3 == 2) && l16 < 15;
+            }
+
+            const int pw = pw0 + nb * WPB + win;
+            if (fin && pw < PW) {
+                const float inv = EDGE ? 1.0f / (float)(min(S, Hc - ph * S) * min(S, Wc - pw * S))
+                                       : 1.0f / (float)(S * S);
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const int co = co0 + 4 * g + chan[i];
+                    if (co < Cout) {
+                        float o = pv[i];
+                        if (POOL_MAX) {
+                            if (relu) o = fmaxf(o, 0.f);  // ReLU commutes with max
+                        } else {
+                            o = o * inv;
+                        }
+                        if constexpr (MODE == OUT_MAP)
+                            dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = o;
+                        else
+                            lsum += logistic(o);
+                    }
+                }
             }
         }
     };
@@ -370,8 +420,9 @@ constexpr size_t kMaxLdsEx = 160 * 1024 - 256;
 
 // Channel planes padded so that the 4 channel groups (plane*CINQ words
 // apart) start 16 banks apart.
+template <class C>
 int elem_plane(int CINQ) {
-    const int base = ElemK3S4::IH * ElemK3S4::RP;
+    const int base = C::IH * C::RP;
     for (int pad = 0; pad < 64; ++pad)
         if (((long)CINQ * (base + pad)) % 64 == 16) return base + pad;
     for (int pad = 0; pad < 32; ++pad)
@@ -379,9 +430,10 @@ int elem_plane(int CINQ) {
     return base;
 }
 
+template <class C>
 size_t elem_lds_bytes(int Cin) {
     const int CINQ = (Cin + 3) / 4;
-    return (size_t)4 * CINQ * elem_plane(CINQ) * sizeof(float);
+    return (size_t)4 * CINQ * elem_plane<C>(CINQ) * sizeof(float);
 }
 
 struct ElemGrid {
@@ -389,55 +441,79 @@ struct ElemGrid {
     int64_t nblocks;
 };
 
+template <class C>
 ElemGrid elem_grid(const Conv2dShape& s) {
-    using C = ElemK3S4;
     const int tiles_h = (s.PH + C::TPH - 1) / C::TPH;
     const int tiles_w = (s.PW + C::TPW - 1) / C::TPW;
     const int co_ranges = (s.Cout + C::CO_RANGE - 1) / C::CO_RANGE;
     return {tiles_w, tiles_h * tiles_w, co_ranges, (int64_t)tiles_h * tiles_w * co_ranges * s.B};
 }
 
-template <int POOL_MAX, int MODE>
+template <class C, int POOL_MAX, int MODE>
 hipError_t launch_elem_as(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
                           const PoolOpts& o, hipStream_t stream) {
     const int CINQ = (s.Cin + 3) / 4;
-    const int plane = elem_plane(CINQ);
+    const int plane = elem_plane<C>(CINQ);
     const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
-    const ElemGrid g = elem_grid(s);
+    const ElemGrid g = elem_grid<C>(s);
     if (g.nblocks > INT32_MAX) return hipErrorInvalidValue;
-    const void* fn = (const void*)conv2d_pool_elem_kernel<POOL_MAX, MODE>;
+    const void* fn = (const void*)conv2d_pool_elem_kernel<C, POOL_MAX, MODE>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((conv2d_pool_elem_kernel<POOL_MAX, MODE>), dim3((unsigned)g.nblocks), dim3(ElemK3S4::NT), lds,
+    hipLaunchKernelGGL((conv2d_pool_elem_kernel<C, POOL_MAX, MODE>), dim3((unsigned)g.nblocks), dim3(C::NT), lds,
                        stream, x, w, bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, g.tiles_w, g.tiles,
                        g.co_ranges, (int)g.nblocks, o.relu ? 1 : 0, o.ceil_mode ? 1 : 0);
     return hipGetLastError();
 }
 
-template <int POOL_MAX>
-hipError_t launch_elem_pool(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
-                            int mode, const PoolOpts& o, hipStream_t stream) {
-    if (mode == OUT_MAP) return launch_elem_as<POOL_MAX, OUT_MAP>(s, x, w, bias, dst, o, stream);
-    if (mode == OUT_PARTIAL) return launch_elem_as<POOL_MAX, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
-    return launch_elem_as<POOL_MAX, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+template <class C>
+hipError_t launch_elem_cfg(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                           int mode, const PoolOpts& o, hipStream_t stream) {
+    if (o.pool_max) {
+        if (mode == OUT_MAP) return launch_elem_as<C, 1, OUT_MAP>(s, x, w, bias, dst, o, stream);
+        if (mode == OUT_PARTIAL) return launch_elem_as<C, 1, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
+        return launch_elem_as<C, 1, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+    }
+    if (mode == OUT_MAP) return launch_elem_as<C, 0, OUT_MAP>(s, x, w, bias, dst, o, stream);
+    if (mode == OUT_PARTIAL) return launch_elem_as<C, 0, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
+    return launch_elem_as<C, 0, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+}
+
+// Calls f with a value of the instance's config type for (K, S); returns
+// false if there is no instance.
+template <class F>
+bool with_elem_cfg(int K, int S, F&& f) {
+    if (K == 3 && S == 4) return f(ElemK3S4{}), true;
+    if (K == 3 && S == 2) return f(ElemK3S2{}), true;
+    if (K == 3 && S == 3) return f(ElemK3S3{}), true;
+    if (K == 5 && S == 3) return f(ElemK5S3{}), true;
+    return false;
 }
 
 }  // namespace
 
 bool conv2d_elem_supported(int Cin, int K, int S) {
-    return K == ElemK3S4::K && S == ElemK3S4::S && elem_lds_bytes(Cin) <= kMaxLdsEx;
+    size_t bytes = 0;
+    if (!with_elem_cfg(K, S, [&](auto c) { bytes = elem_lds_bytes<decltype(c)>(Cin); })) return false;
+    return bytes <= kMaxLdsEx;
 }
 
 int64_t conv2d_elem_parts(const Conv2dShape& s) {
-    const ElemGrid g = elem_grid(s);
-    return (int64_t)g.tiles * g.co_ranges;
+    int64_t parts = -1;
+    with_elem_cfg(s.K, s.S, [&](auto c) {
+        const ElemGrid g = elem_grid<decltype(c)>(s);
+        parts = (int64_t)g.tiles * g.co_ranges;
+    });
+    return parts;
 }
 
 hipError_t conv2d_elem_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
                               int mode, const PoolOpts& o, hipStream_t stream) {
     if (!conv2d_elem_supported(s.Cin, s.K, s.S)) return hipErrorInvalidValue;
-    return o.pool_max ? launch_elem_pool<1>(s, x, w, bias, dst, mode, o, stream)
-                      : launch_elem_pool<0>(s, x, w, bias, dst, mode, o, stream);
+    hipError_t e = hipErrorInvalidValue;
+    with_elem_cfg(s.K, s.S,
+                  [&](auto c) { e = launch_elem_cfg<decltype(c)>(s, x, w, bias, dst, mode, o, stream); });
+    return e;
 }
 
 hipError_t conv2d_general_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,

@@ -319,7 +319,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     const int l16 = lane & 15;
     // tile = (b * n_ot + ot) * n_tt + tt in launch order.  (Dealing the
     // tiles to the XCDs in contiguous runs, so that neighbouring time tiles
-    // share an L2 for their halo lines, measured slower.)
+    // share an L2 for their halo lines, read 160 MB instead of 292 MB of x
+    // for x[32,256,4096] but ran 2 % slower.)
     const int tile = blockIdx.x;
     const int tq = tile / n_tt;
     const int bi = tq / n_ot;

@@ -63,6 +63,15 @@ __device__ __forceinline__ float quad_xor2(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
 }
 
+// DPP row shifts: lane l reads lane l-1 (row_shr:1) or l-2 (row_shr:2) of its
+// row of 16 lanes; the first one or two lanes of each row read 0.
+__device__ __forceinline__ float row_shr1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_shr2(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, false));
+}
+
 // Logistic sigmoid 1/(1+e^-a) with the hardware exp2 (v_exp_f32) and
 // reciprocal: relative error a few ulp for |a| < 80, exactly 1/2 at a = 0,
 // saturating to 0 or 1 (never NaN) for large |a|.

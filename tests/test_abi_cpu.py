@@ -172,8 +172,8 @@ def test_conv2d_ex_unsupported(lib):
     assert conv_ex(lib, algo=3) == EUNSUP                          # box-sum needs a linear pool
     assert conv_ex(lib, pool_mode=0, flags=1, algo=3) == EUNSUP    # ... without ReLU
     assert conv_ex(lib, pool_mode=0, flags=2, algo=3) == EUNSUP    # ... over full windows
-    assert conv_ex(lib, K=5, pool=4, algo=1, H=16, W=16) == EUNSUP  # matrix-core instance: K = 3, s = 4 only
-    assert conv_ex(lib, K=3, pool=2, algo=1) == EUNSUP
+    assert conv_ex(lib, K=5, pool=4, algo=1, H=16, W=16) == EUNSUP  # matrix-core instances: K3 s2-4, K5 s3
+    assert conv_ex(lib, K=7, pool=2, algo=1, H=16, W=16) == EUNSUP
     assert conv_ex(lib, Cin=300, pool=4, algo=1, H=16, W=16) == EUNSUP  # its LDS tile does not fit
     assert conv_ex(lib, B=70000) == EUNSUP
 

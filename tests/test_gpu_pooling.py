@@ -3,10 +3,10 @@ mode) against the CPU oracle, through the C ABI's _ex entry points.
 
 Bar as for the base chain: |gpu - oracle| <= 1e-4 + 1e-4*|oracle| element by
 element on the pre-sigmoid pooled map and on the fused sums, oracle in
-float64.  The shapes give several tiles of the matrix-core kernel (16 x 64
-conv outputs per tile), ragged tiles, partial ceil-mode windows of every
-width 1..3 at the bottom and right, Cin not a multiple of 4 and Cout above 64
-and not a multiple of 16.
+float64.  The shapes give several tiles of each matrix-core instance (K = 3 with
+s = 2, 3, 4; K = 5 with s = 3), ragged tiles, partial ceil-mode windows of
+every width at the bottom and right, Cin not a multiple of 4 and Cout above
+64 and not a multiple of 16.
 """
 
 import itertools
@@ -73,14 +73,20 @@ SHAPES = [
     (2, 12, 40, 131, 20, 3, 4),     # 38x129 -> 9x32 / 10x33 (2-row, 1-column last), 3 quads
     (1, 8, 6, 8, 4, 3, 4),          # 4x6 -> 1x1 / 1x2
     (1, 2, 5, 9, 3, 3, 4),          # 3x7 -> 0x1 (empty) / 1x2 (3-row window)
-    (1, 3, 20, 17, 5, 5, 3),        # K5/s3: one-thread-per-output kernel only
-    (1, 2, 11, 13, 4, 3, 2),        # K3/s2: likewise
-    (1, 4, 12, 12, 6, 1, 5),        # K = 1: likewise
+    (1, 3, 20, 17, 5, 5, 3),        # K5/s3: 16x13 -> 5x4 / 6x5
+    (1, 16, 40, 45, 70, 5, 3),      # K5/s3: 36x41 -> 12x13 / 12x14, 4 quads, two channel ranges, 2 tile columns
+    (1, 4, 7, 9, 3, 5, 3),          # K5/s3: 3x5 -> 1x1 / 1x2
+    (1, 2, 11, 13, 4, 3, 2),        # K3/s2: 9x11 -> 4x5 / 5x6
+    (2, 6, 37, 70, 20, 3, 2),       # K3/s2: 35x68 -> 17x34 / 18x34, 3 tile columns
+    (1, 5, 40, 50, 20, 3, 3),       # K3/s3: 38x48 -> 12x16 / 13x16
+    (1, 4, 12, 12, 6, 1, 5),        # K = 1, s = 5: one-thread-per-output kernel only
 ]
+
+MFMA_INSTANCES = {(3, 4), (3, 2), (3, 3), (5, 3)}   # (K, s) of the per-conv-output matrix-core kernel
 
 
 def has_mfma(shape):
-    return shape[5] == 3 and shape[6] == 4
+    return (shape[5], shape[6]) in MFMA_INSTANCES
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -193,6 +199,40 @@ FULL_COMBOS = [(MAX, True, False), (MAX, True, True), (AVG, True, True), (MAX, F
 @pytest.fixture(scope="module")
 def full_inputs():
     return fi.make("conv2d_full", seed=0)
+
+
+@pytest.fixture(scope="module")
+def tail_inputs():
+    return fi.make("conv2d_tail", seed=0)
+
+
+@pytest.mark.parametrize("combo", [(MAX, True, False), (MAX, True, True), (AVG, True, True)], ids=combo_id)
+def test_pool_tail_size(fc, tail_inputs, combo):
+    # x[64,16,257,257], 16 -> 128, K 5, s 3: the K5/s3 instance, two channel ranges
+    pool_mode, relu, ceil_mode = combo
+    announce(f"pool ex tail size {combo_id(combo)}")
+    x, w, b = tail_inputs
+    s = 3
+    kw = dict(algo=1, pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, **kw).cpu().numpy()
+    got_map = fc.conv2d_pool_map(xd, wd, bd, s, **kw).cpu().numpy()
+    want_out = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, batch_idx=[63], pool_mode=pool_mode, relu=relu,
+                                              ceil_mode=ceil_mode)
+    assert_close(got_out[[63]], want_out, "out[63]")
+    sig = (1.0 / (1.0 + np.exp(-got_map.astype(np.float64)))).sum(axis=(1, 2, 3))
+    assert_close(got_out, sig, "fused sum vs sigmoid(map) sum")
+    B, Cout, PH, PW = got_map.shape
+    assert (PH, PW) == ((85, 85) if ceil_mode else (84, 84))
+    rng = np.random.default_rng(58)
+    n = 10000
+    samp = np.stack([rng.integers(0, B, n), rng.integers(0, Cout, n), rng.integers(0, PH, n),
+                     rng.integers(0, PW, n)], axis=1)
+    edge = [0, 1, 3, 4, 9, 10, 19, 20, PH - 2, PH - 1]
+    extra = [(bb, co, ph, pw) for bb in (0, B - 1) for co in (0, 63, 64, Cout - 1) for ph in edge for pw in edge]
+    samp = np.concatenate([samp, np.array(extra)], axis=0)
+    want = oracle.conv2d_pooled_at(x, w, b, s, samp, pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+    assert_close(got_map[tuple(samp.T)], want, "sampled pooled map")
 
 
 @pytest.mark.parametrize("combo", FULL_COMBOS, ids=combo_id)
