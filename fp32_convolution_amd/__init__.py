@@ -64,6 +64,12 @@ _SIGS = {
         [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp],
         ctypes.c_int),
     "fconv2d_pool_out_size_ex": ([_i64, _i64, _i64, _i64, ctypes.c_int, _i64p, _i64p], ctypes.c_int),
+    "fconv2d_pool_sigmoid_sum_det_ex": (
+        [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp,
+         ctypes.c_size_t, _vp, _vp], ctypes.c_int),
+    "fconv2d_pool_sigmoid_sum_det_workspace_ex": (
+        [_i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+         ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "fconv2d_select_algo": ([_i64, _i64, _i64, _i64], ctypes.c_int),
     "dwsep_conv1d": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp], ctypes.c_int),
     "dwsep_conv1d_out_len": ([_i64, _i64, _i64], ctypes.c_int64),
@@ -171,14 +177,22 @@ def conv2d_pool_sigmoid_sum(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO,
     return out
 
 
-def conv2d_det_workspace_bytes(B, Cin, H, W, Cout, K, pool, algo: int = ALGO_AUTO) -> int:
+def conv2d_det_workspace_bytes(B, Cin, H, W, Cout, K, pool, algo: int = ALGO_AUTO, pool_mode: int = POOL_AVG,
+                               relu: bool = False, ceil_mode: bool = False) -> int:
     n = ctypes.c_size_t()
-    _check(lib.fconv2d_pool_sigmoid_sum_det_workspace(B, Cin, H, W, Cout, K, pool, algo, ctypes.byref(n)),
-           "fconv2d_pool_sigmoid_sum_det_workspace")
+    flags = _pool_flags(relu, ceil_mode)
+    if pool_mode == POOL_AVG and flags == 0:
+        _check(lib.fconv2d_pool_sigmoid_sum_det_workspace(B, Cin, H, W, Cout, K, pool, algo, ctypes.byref(n)),
+               "fconv2d_pool_sigmoid_sum_det_workspace")
+    else:
+        _check(lib.fconv2d_pool_sigmoid_sum_det_workspace_ex(B, Cin, H, W, Cout, K, pool, pool_mode, flags, algo,
+                                                             ctypes.byref(n)),
+               "fconv2d_pool_sigmoid_sum_det_workspace_ex")
     return n.value
 
 
-def conv2d_pool_sigmoid_sum_det(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO, workspace=None):
+def conv2d_pool_sigmoid_sum_det(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO, workspace=None,
+                                pool_mode: int = POOL_AVG, relu: bool = False, ceil_mode: bool = False):
     """Bitwise-reproducible form of conv2d_pool_sigmoid_sum (partials + fixed-order reduction).
 
     workspace: a device tensor of at least conv2d_det_workspace_bytes() bytes,
@@ -193,14 +207,19 @@ def conv2d_pool_sigmoid_sum_det(x, w, b, pool: int, out=None, algo: int = ALGO_A
         _dev_f32(out, "out")
         if tuple(out.shape) != (B,) or out.device != x.device:
             raise ValueError("out must be [B] on x's device")
-    need = conv2d_det_workspace_bytes(B, Cin, H, W, Cout, K, pool, algo)
+    need = conv2d_det_workspace_bytes(B, Cin, H, W, Cout, K, pool, algo, pool_mode, relu, ceil_mode)
     if workspace is None:
         workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=x.device)
     if workspace.device != x.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on x's device")
     nbytes = workspace.numel() * workspace.element_size()
-    rc = lib.fconv2d_pool_sigmoid_sum_det(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
-                                          _ptr(workspace), nbytes, _ptr(out), _stream(x))
+    flags = _pool_flags(relu, ceil_mode)
+    if pool_mode == POOL_AVG and flags == 0:
+        rc = lib.fconv2d_pool_sigmoid_sum_det(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
+                                              _ptr(workspace), nbytes, _ptr(out), _stream(x))
+    else:
+        rc = lib.fconv2d_pool_sigmoid_sum_det_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode,
+                                                 flags, algo, _ptr(workspace), nbytes, _ptr(out), _stream(x))
     _check(rc, "fconv2d_pool_sigmoid_sum_det")
     return out
 

@@ -122,43 +122,74 @@ int run_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, con
 
 constexpr int kPoolFlags = FCONV_RELU | FCONV_CEIL_MODE;
 
-// The generalised pool.  The plain average pool (no flags) is the base
-// operation and takes its algorithms; everything else runs on the
-// per-conv-output matrix-core kernel where it has an instance, else on the
+// The generalised pool, validated: shape, options and the resolved
+// algorithm.  The plain average pool (no flags) is the base operation and
+// takes its algorithms; everything else runs on the per-conv-output
+// matrix-core kernel where it has an instance, else on the
 // one-thread-per-output kernel.
-int run_conv2d_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
-                  int64_t K, const float* bias, int64_t pool, int pool_mode, int flags, int algo, float* dst, bool map,
-                  void* stream) {
+struct ExPlan {
+    Conv2dShape s;
+    fconv::PoolOpts o;
+    int algo;    // FCONV_ALGO_*, never AUTO
+    bool plain;  // average pool, no flags
+};
+
+int plan_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout, int64_t K,
+            int64_t pool, int pool_mode, int flags, int algo, const void* dst, ExPlan* p) {
     if (pool_mode != FCONV_POOL_AVG && pool_mode != FCONV_POOL_MAX) return FCONV_EINVAL;
     if ((flags & ~kPoolFlags) != 0) return FCONV_EINVAL;
     if (algo != FCONV_ALGO_AUTO && algo != FCONV_ALGO_DIRECT_MFMA && algo != FCONV_ALGO_DIRECT_SIMPLE &&
         algo != FCONV_ALGO_BOXSUM)
         return FCONV_EINVAL;
-    if (pool_mode == FCONV_POOL_AVG && flags == 0)
-        return run_conv2d(x, B, Cin, H, W, w, Cout, K, bias, pool, algo, dst, map, stream);
-    const fconv::PoolOpts o{pool_mode == FCONV_POOL_MAX, (flags & FCONV_RELU) != 0, (flags & FCONV_CEIL_MODE) != 0};
-    Conv2dShape s;
-    const bool null_map = map && !dst;
-    int rc = check_conv2d(x, B, Cin, H, W, w, Cout, K, pool, null_map ? kEmptyMap : dst, &s, o.ceil_mode);
+    p->plain = pool_mode == FCONV_POOL_AVG && flags == 0;
+    p->o = {pool_mode == FCONV_POOL_MAX, (flags & FCONV_RELU) != 0, (flags & FCONV_CEIL_MODE) != 0};
+    int rc = check_conv2d(x, B, Cin, H, W, w, Cout, K, pool, dst, &p->s, p->o.ceil_mode);
     if (rc != FCONV_OK) return rc;
-    if (null_map && s.PH > 0 && s.PW > 0) return FCONV_EINVAL;
-    const bool mfma_ok = fconv::conv2d_elem_supported(s.Cin, s.K, s.S);
+    if (p->plain) {
+        p->algo = pick_conv2d_algo(p->s, algo);
+        return p->algo < 0 ? p->algo : FCONV_OK;
+    }
+    const bool mfma_ok = fconv::conv2d_elem_supported(p->s.Cin, p->s.K, p->s.S);
     int a = algo;
     if (a == FCONV_ALGO_AUTO) a = mfma_ok ? FCONV_ALGO_DIRECT_MFMA : FCONV_ALGO_DIRECT_SIMPLE;
     if (a == FCONV_ALGO_BOXSUM || (a == FCONV_ALGO_DIRECT_MFMA && !mfma_ok)) return FCONV_EUNSUPPORTED;
+    p->algo = a;
+    return FCONV_OK;
+}
+
+hipError_t launch_ex(const ExPlan& p, const float* x, const float* w, const float* bias, float* dst, int mode,
+                     hipStream_t st) {
+    if (p.plain) return launch_conv2d(p.algo, p.s, x, w, bias, dst, mode, st);
+    return p.algo == FCONV_ALGO_DIRECT_MFMA ? fconv::conv2d_elem_launch(p.s, x, w, bias, dst, mode, p.o, st)
+                                            : fconv::conv2d_general_launch(p.s, x, w, bias, dst, mode, p.o, st);
+}
+
+// Workgroups (= partial sums) per batch item of the planned launch.
+int64_t parts_ex(const ExPlan& p) {
+    if (p.s.PH == 0 || p.s.PW == 0) return 0;
+    if (p.plain) return conv2d_parts(p.algo, p.s);
+    return p.algo == FCONV_ALGO_DIRECT_MFMA ? fconv::conv2d_elem_parts(p.s) : fconv::conv2d_general_parts(p.s);
+}
+
+int run_conv2d_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,
+                  int64_t K, const float* bias, int64_t pool, int pool_mode, int flags, int algo, float* dst, bool map,
+                  void* stream) {
+    ExPlan p;
+    const bool null_map = map && !dst;
+    int rc = plan_ex(x, B, Cin, H, W, w, Cout, K, pool, pool_mode, flags, algo, null_map ? kEmptyMap : dst, &p);
+    if (rc != FCONV_OK) return rc;
+    if (null_map && p.s.PH > 0 && p.s.PW > 0) return FCONV_EINVAL;
     hipStream_t st = (hipStream_t)stream;
     if (log_enabled())
         fprintf(stderr, "[fconv] conv2d_ex%s B=%d Cin=%d H=%d W=%d Cout=%d K=%d pool=%d max=%d relu=%d ceil=%d -> algo %d\n",
-                map ? "_map" : "", s.B, s.Cin, s.H, s.W, s.Cout, s.K, s.S, (int)o.pool_max, (int)o.relu,
-                (int)o.ceil_mode, a);
-    if (s.PH == 0 || s.PW == 0) return map ? FCONV_OK : status_of(fconv::fill_zero(dst, s.B, st));
+                map ? "_map" : "", p.s.B, p.s.Cin, p.s.H, p.s.W, p.s.Cout, p.s.K, p.s.S, (int)p.o.pool_max,
+                (int)p.o.relu, (int)p.o.ceil_mode, p.algo);
+    if (p.s.PH == 0 || p.s.PW == 0) return map ? FCONV_OK : status_of(fconv::fill_zero(dst, p.s.B, st));
     if (!map) {
-        hipError_t e = fconv::fill_zero(dst, s.B, st);
+        hipError_t e = fconv::fill_zero(dst, p.s.B, st);
         if (e != hipSuccess) return FCONV_EHIP;
     }
-    const int mode = map ? fconv::OUT_MAP : fconv::OUT_SUM_ATOMIC;
-    return status_of(a == FCONV_ALGO_DIRECT_MFMA ? fconv::conv2d_elem_launch(s, x, w, bias, dst, mode, o, st)
-                                                 : fconv::conv2d_general_launch(s, x, w, bias, dst, mode, o, st));
+    return status_of(launch_ex(p, x, w, bias, dst, map ? fconv::OUT_MAP : fconv::OUT_SUM_ATOMIC, st));
 }
 
 // Shape/algorithm checks shared by the deterministic entry point and its
@@ -204,6 +235,36 @@ int fconv2d_pool_map_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64
                         int64_t K, const float* bias, int64_t pool, int pool_mode, int flags, int algo, float* pooled,
                         void* stream) {
     return run_conv2d_ex(x, B, Cin, H, W, w, Cout, K, bias, pool, pool_mode, flags, algo, pooled, true, stream);
+}
+
+int fconv2d_pool_sigmoid_sum_det_workspace_ex(int64_t B, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                                               int64_t K, int64_t pool, int pool_mode, int flags, int algo,
+                                               size_t* bytes) {
+    if (!bytes) return FCONV_EINVAL;
+    static const float placeholder = 0.f;
+    ExPlan p;
+    int rc = plan_ex(&placeholder, B, Cin, H, W, &placeholder, Cout, K, pool, pool_mode, flags, algo, &placeholder,
+                     &p);
+    if (rc != FCONV_OK) return rc;
+    *bytes = (size_t)parts_ex(p) * (size_t)p.s.B * sizeof(float);
+    return FCONV_OK;
+}
+
+int fconv2d_pool_sigmoid_sum_det_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w,
+                                    int64_t Cout, int64_t K, const float* bias, int64_t pool, int pool_mode,
+                                    int flags, int algo, void* workspace, size_t workspace_bytes, float* out,
+                                    void* stream) {
+    ExPlan p;
+    int rc = plan_ex(x, B, Cin, H, W, w, Cout, K, pool, pool_mode, flags, algo, out, &p);
+    if (rc != FCONV_OK) return rc;
+    const int64_t parts = parts_ex(p);
+    hipStream_t st = (hipStream_t)stream;
+    if (parts == 0) return status_of(fconv::fill_zero(out, p.s.B, st));
+    if (!workspace || workspace_bytes < (size_t)parts * (size_t)p.s.B * sizeof(float)) return FCONV_EINVAL;
+    float* ws = (float*)workspace;
+    hipError_t e = launch_ex(p, x, w, bias, ws, fconv::OUT_PARTIAL, st);
+    if (e != hipSuccess) return FCONV_EHIP;
+    return status_of(fconv::reduce_partials(ws, parts, p.s.B, out, st));
 }
 
 int fconv2d_pool_out_size_ex(int64_t H, int64_t W, int64_t K, int64_t pool, int flags, int64_t* PH,

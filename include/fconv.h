@@ -182,8 +182,10 @@ int fconv2d_select_algo(int64_t Cin, int64_t Cout, int64_t K, int64_t pool);
  * fconv2d_pool_sigmoid_sum_ex -- the fused sum with the generalised pool.
  *   pool_mode  FCONV_POOL_AVG or FCONV_POOL_MAX
  *   flags      0 or an OR of FCONV_RELU, FCONV_CEIL_MODE
- *   algo       FCONV_ALGO_AUTO, DIRECT_MFMA (one instance: K = 3, pool = 4,
- *              Cin up to about 220), DIRECT_SIMPLE (any shape) or, only for
+ *   algo       FCONV_ALGO_AUTO, DIRECT_MFMA (instances where the LDS tile
+ *              fits: K = 3 with pool 4 (Cin <= 32), pool 2 (Cin <= 56) and
+ *              pool 3 (Cin <= 40); K = 5 with pool 3 (Cin <= 68)),
+ *              DIRECT_SIMPLE (any shape) or, only for
  *              FCONV_POOL_AVG with flags 0, BOXSUM.  AUTO picks DIRECT_MFMA
  *              where it has an instance, else DIRECT_SIMPLE (for the plain
  *              average pool it picks as fconv2d_pool_sigmoid_sum does).
@@ -204,6 +206,23 @@ int fconv2d_pool_sigmoid_sum_ex(const float* x, int64_t B, int64_t Cin, int64_t 
 int fconv2d_pool_map_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
                         const float* w, int64_t Cout, int64_t K, const float* bias, int64_t pool,
                         int pool_mode, int flags, int algo, float* pooled, void* stream);
+
+/* The bitwise-reproducible form of fconv2d_pool_sigmoid_sum_ex: per-workgroup
+ * partial sums into `workspace`, then a fixed-order reduction, as
+ * fconv2d_pool_sigmoid_sum_det (same workspace rules; its size from
+ * fconv2d_pool_sigmoid_sum_det_workspace_ex).  Arguments and errors as
+ * fconv2d_pool_sigmoid_sum_ex, plus FCONV_EINVAL for a workspace that is too
+ * small (or NULL with a non-empty pooled map). */
+int fconv2d_pool_sigmoid_sum_det_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
+                                    const float* w, int64_t Cout, int64_t K, const float* bias,
+                                    int64_t pool, int pool_mode, int flags, int algo, void* workspace,
+                                    size_t workspace_bytes, float* out, void* stream);
+
+/* Workspace bytes fconv2d_pool_sigmoid_sum_det_ex needs (0 for an empty
+ * pooled map).  Host only; errors as the call itself (NULL bytes: EINVAL). */
+int fconv2d_pool_sigmoid_sum_det_workspace_ex(int64_t B, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                                              int64_t K, int64_t pool, int pool_mode, int flags, int algo,
+                                              size_t* bytes);
 
 /* PH, PW of the generalised pool (FCONV_CEIL_MODE in flags selects ceil;
  * FCONV_RELU is accepted and ignored).  Host only.  FCONV_EINVAL on sizes

@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
     for must in ["fconv2d_pool_sigmoid_sum", "dwsep_conv1d", "fconv2d_pool_map", "fconv_strerror",
                  "fconv_version", "fconv2d_pool_sigmoid_sum_algo", "fconv2d_pool_out_size",
                  "fconv2d_select_algo", "dwsep_conv1d_out_len", "fconv2d_pool_sigmoid_sum_ex",
-                 "fconv2d_pool_map_ex", "fconv2d_pool_out_size_ex"]:
+                 "fconv2d_pool_map_ex", "fconv2d_pool_out_size_ex", "fconv2d_pool_sigmoid_sum_det_ex",
+                 "fconv2d_pool_sigmoid_sum_det_workspace_ex"]:
         assert must in names, must
 
 
@@ -176,6 +177,48 @@ def test_conv2d_ex_unsupported(lib):
     assert conv_ex(lib, K=7, pool=2, algo=1, H=16, W=16) == EUNSUP
     assert conv_ex(lib, Cin=300, pool=4, algo=1, H=16, W=16) == EUNSUP  # its LDS tile does not fit
     assert conv_ex(lib, B=70000) == EUNSUP
+
+
+def test_det_ex_workspace_query(lib):
+    import fp32_convolution_amd as fc
+
+    # the per-conv-output kernel on x[128,8,384,384] (K3/s4): 24 x 6 tiles of 4 x 16 pooled outputs per item;
+    # ceil mode (96 x 96) has the same tile count
+    for relu, ceil_mode in [(True, False), (False, True), (True, True)]:
+        assert fc.conv2d_det_workspace_bytes(128, 8, 384, 384, 64, 3, 4, algo=1, pool_mode=fc.POOL_MAX, relu=relu,
+                                             ceil_mode=ceil_mode) == 128 * 24 * 6 * 4
+    # K5/s3 on x[64,16,257,257]: 21 x 9 tiles of 4 x 10, two channel ranges
+    assert fc.conv2d_det_workspace_bytes(64, 16, 257, 257, 128, 5, 3, algo=1, pool_mode=fc.POOL_MAX) == \
+        64 * 21 * 9 * 2 * 4
+    # one-thread-per-output kernel: one workgroup per 256 pooled values of an item
+    assert fc.conv2d_det_workspace_bytes(2, 3, 16, 16, 4, 3, 4, algo=2, pool_mode=fc.POOL_MAX) == 2 * 1 * 4
+    # floor mode, empty map -> 0; ceil mode has one pooled row there
+    assert fc.conv2d_det_workspace_bytes(3, 2, 5, 9, 4, 3, 4, pool_mode=fc.POOL_MAX) == 0
+    assert fc.conv2d_det_workspace_bytes(3, 2, 5, 9, 4, 3, 4, pool_mode=fc.POOL_MAX, ceil_mode=True) > 0
+    # the plain average pool is the base call's workspace
+    assert fc.conv2d_det_workspace_bytes(128, 8, 384, 384, 64, 3, 4, algo=3, pool_mode=fc.POOL_AVG) == \
+        lib_det_bytes(lib, 128, 8, 384, 384, 64, 3, 4, 3)
+    n = ctypes.c_size_t()
+    q = lib.fconv2d_pool_sigmoid_sum_det_workspace_ex
+    assert q(1, 1, 8, 8, 1, 3, 2, 1, 0, 0, None) == EINVAL
+    assert q(1, 1, 8, 8, 1, 3, 2, 2, 0, 0, ctypes.byref(n)) == EINVAL     # unknown pool
+    assert q(1, 1, 8, 8, 1, 3, 2, 1, 8, 0, ctypes.byref(n)) == EINVAL     # unknown flag
+    assert q(1, 1, 8, 8, 1, 3, 2, 1, 0, 3, ctypes.byref(n)) == EUNSUP     # box-sum with a max pool
+    assert q(1, 1, 8, 8, 1, 7, 2, 1, 0, 1, ctypes.byref(n)) == EUNSUP     # no matrix-core instance for K = 7
+
+
+def lib_det_bytes(lib, *args):
+    n = ctypes.c_size_t()
+    assert lib.fconv2d_pool_sigmoid_sum_det_workspace(*args, ctypes.byref(n)) == 0
+    return n.value
+
+
+def test_det_ex_rejects_small_workspace(lib):
+    args = (FAKE, 2, 3, 16, 16, FAKE, 4, 3, None, 4, 1, 1, 2)   # max pool, ReLU, one-thread-per-output
+    assert lib.fconv2d_pool_sigmoid_sum_det_ex(*args, FAKE, 7, FAKE, None) == EINVAL
+    assert lib.fconv2d_pool_sigmoid_sum_det_ex(*args, None, 8, FAKE, None) == EINVAL
+    assert lib.fconv2d_pool_sigmoid_sum_det_ex(None, *args[1:], FAKE, 8, FAKE, None) == EINVAL
+    assert lib.fconv2d_pool_sigmoid_sum_det_ex(*args[:-3], 2, 1, 2, FAKE, 8, FAKE, None) == EINVAL  # pool mode 2
 
 
 def test_out_size_ex_matches_torch_pooling():

@@ -161,6 +161,28 @@ def test_pool_ceil_equals_floor_when_windows_fit(fc):
             assert torch.equal(f, c)
 
 
+@pytest.mark.parametrize("shape", [(3, 8, 70, 75, 64, 3, 4), (2, 16, 40, 45, 70, 5, 3), (2, 3, 20, 17, 5, 7, 2)])
+@pytest.mark.parametrize("algo", [0, 2])
+def test_pool_deterministic(fc, shape, algo):
+    # partial sums + fixed-order reduction: repeated calls give identical bits, within tolerance of the oracle
+    B, Cin, H, W, Cout, K, s = shape
+    announce(f"pool ex deterministic {shape} algo={algo}")
+    x, w, b = fi.conv2d_inputs(B, Cin, H, W, Cout, K, seed=59)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    for pool_mode, relu, ceil_mode in [(MAX, True, False), (MAX, False, True), (AVG, True, True)]:
+        kw = dict(algo=algo, pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+        want = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+        first = fc.conv2d_pool_sigmoid_sum_det(xd, wd, bd, s, **kw).cpu().numpy()
+        nbytes = fc.conv2d_det_workspace_bytes(B, Cin, H, W, Cout, K, s, algo, pool_mode, relu, ceil_mode)
+        ws = torch.full((max(nbytes, 4) // 4,), float("nan"), device="cuda")
+        for _ in range(3):
+            again = fc.conv2d_pool_sigmoid_sum_det(xd, wd, bd, s, workspace=ws, **kw).cpu().numpy()
+            assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+        assert_close(first, want, f"deterministic out {shape} {combo_id((pool_mode, relu, ceil_mode))}")
+        atomic = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, **kw).cpu().numpy()
+        assert_close(atomic, first.astype(np.float64), "atomic vs deterministic")
+
+
 def padded(n, pad=1024):
     whole = torch.full((n + 2 * pad,), CANARY, device="cuda")
     return whole, whole[pad:pad + n]
