@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fconv {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -33,10 +35,23 @@ __device__ __forceinline__ float buf_load_f32(buf_rsrc r, int byte_off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 
+// Sum over the 64 lanes, valid in every lane; the order is fixed.  Within
+// each row of 16 lanes with DPP (pairs, quads, half-row mirror, row mirror:
+// every lane then holds its row's sum), then the four row sums read out of
+// lanes 0, 16, 32, 48.  Needs all 64 lanes active.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    auto dpp = [](float x, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                     decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm 1,0,3,2
+    v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm 2,3,0,1
+    v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    v += dpp(v, std::integral_constant<int, 0x140>{});  // row_mirror
+    auto lane = [](float x, int l) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+    };
+    return (lane(v, 0) + lane(v, 16)) + (lane(v, 32) + lane(v, 48));
 }
 
 // Sums v over the workgroup; the result is valid in thread 0 only.
