@@ -133,6 +133,62 @@ def ingest_counters(fetch_csv, write_csv, copy_mb, command):
     print(json.dumps(out, indent=1))
 
 
+PROBE_LIB = os.path.join(ROOT, "fp32_convolution_amd", "libfconv_probe.so")
+
+
+def measured_ceilings(torch, dev, stream):
+    """What the GPU sustains for each bound, measured here: the fp32 matrix-core
+    rate and the non-packed fp32 vector FMA rate (libfconv_probe.so: eight
+    independent chains of one instruction per wave, best of 1, 2 and 4 waves
+    per SIMD), and a 1 GiB device-to-device copy (read + write bytes).  Each
+    timing is the median of 5 launches after 2 untimed ones."""
+    import ctypes
+
+    res = {}
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    if os.path.exists(PROBE_LIB):
+        lib = ctypes.CDLL(PROBE_LIB)
+        out = torch.empty(cus * 4 * 256, device=dev)
+        st = ctypes.c_void_p(stream.cuda_stream)
+        for name, fn, flop_per_inst, iters, peak in (
+                ("mfma_f32_16x16x4", lib.fconv_probe_mfma_f32, 2 * 16 * 16 * 4, 4000, PEAK_FP32_TFLOPS),
+                ("valu_fma_f32", lib.fconv_probe_fma_f32, 2 * 64, 40000, PEAK_FP32_TFLOPS / 2)):
+            fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+            best = 0.0
+            for wps in (1, 2, 4):
+                blocks = cus * wps
+                ms = []
+                for i in range(7):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    if fn(blocks, iters, ctypes.c_void_p(out.data_ptr()), st) != 0:
+                        raise RuntimeError(f"probe {name} failed to launch")
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    if i >= 2:
+                        ms.append(e0.elapsed_time(e1))
+                flops = flop_per_inst * 8 * iters * blocks * 4
+                best = max(best, flops / (float(np.median(ms)) * 1e-3) / 1e12)
+            res[name] = {"tflops": round(best, 1), "peak": peak, "frac_of_peak": round(best / peak, 4)}
+        del out
+    n = (1 << 30) // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty_like(src)
+    ms = []
+    for i in range(7):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ms.append(e0.elapsed_time(e1))
+    gbps = 2 * n * 4 / (float(np.median(ms)) * 1e-3) / 1e9
+    res["hbm_copy"] = {"gbps": round(gbps, 1), "peak": PEAK_HBM_GBPS, "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+    del src, dst
+    return res
+
+
 def conv2d_flops(cfg):
     Hc, Wc = cfg["H"] - cfg["K"] + 1, cfg["W"] - cfg["K"] + 1
     s = cfg["pool"]
@@ -371,6 +427,8 @@ def main():
     ms_cold = np.array([e0.elapsed_time(e1) for e0, e1 in cold])
     del flush
 
+    ceilings = measured_ceilings(torch, dev, stream)
+
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
     ms_conv = np.array([e[0].elapsed_time(e[1]) for e in ev])
@@ -389,6 +447,10 @@ def main():
 
     k_conv = kstats(ms_conv, f_conv, b_conv)
     k_dw = kstats(ms_dw, f_dw, b_dw)
+    if "mfma_f32_16x16x4" in ceilings:
+        ceil_tf = ceilings["mfma_f32_16x16x4"]["tflops"]
+        for k, f in ((k_conv, f_conv), (k_dw, f_dw)):
+            k["frac_of_measured_mfma_ceiling"] = round(f / (k["ms_mean"] * 1e-3) / 1e12 / ceil_tf, 4)
     k_conv["hbm_bytes_measured"] = measured_traffic(ELEM_AVG)
     k_dw["hbm_bytes_measured"] = measured_traffic("dwsep_tall_kernel")
     k_dw["cold_ms_median"] = round(float(np.median(ms_cold)), 4)
@@ -457,7 +519,10 @@ def main():
             "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
             "traffic": measured_traffic(ELEM_AVG),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "frac_of_measured_ceiling": (round(achieved / ceilings["mfma_f32_16x16x4"]["tflops"], 4)
+                                         if "mfma_f32_16x16x4" in ceilings else None),
         },
+        "ceilings": ceilings,
         "wall_s_timed_region": round(t_wall, 3),
         "settle": {"steps": settle_steps, "wall_s": round(t_settle, 3),
                    "note": "untimed whole steps before the warm-up, until the clocks leave their idle state"},

@@ -56,17 +56,31 @@ def _compile(src: str, verbose: bool, build_dir: str = BUILD, defines=()) -> str
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD, defines=()) -> str:
-    """Compiles every source and links `out`.  `defines` (NAME=VALUE strings)
-    override compile-time tiling macros for a variant build."""
-    os.makedirs(build_dir, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), SOURCES))
+PROBE_SOURCES = ["ceiling_probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libfconv_probe.so")
+
+
+def _link(objs, out: str, verbose: bool) -> None:
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD, defines=()) -> str:
+    """Compiles every source and links `out` (libfconv.so), then the
+    benchmark's ceiling probes (libfconv_probe.so, default build only).
+    `defines` (NAME=VALUE strings) override compile-time tiling macros for a
+    variant build."""
+    os.makedirs(build_dir, exist_ok=True)
+    probes = out == LIB and not defines
+    srcs = SOURCES + (PROBE_SOURCES if probes else [])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), srcs))
+    _link(objs[:len(SOURCES)], out, verbose)
+    if probes:
+        _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return out
 
 

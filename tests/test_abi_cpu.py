@@ -50,6 +50,19 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), f"{name} declared in fconv.h but not exported"
 
 
+def test_ceiling_probe_library():
+    # benchmark-only probes (not part of fconv.h): exported, argument checks on the host
+    path = os.path.join(ROOT, "fp32_convolution_amd", "libfconv_probe.so")
+    assert os.path.exists(path), "libfconv_probe.so is not built"
+    probe = ctypes.CDLL(path)
+    for name in ("fconv_probe_mfma_f32", "fconv_probe_fma_f32"):
+        fn = getattr(probe, name)
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        assert fn(0, 10, FAKE, None) == -1
+        assert fn(4, 0, FAKE, None) == -1
+        assert fn(4, 10, None, None) == -1
+
+
 def test_version_and_strerror(lib):
     assert lib.fconv_version() >= 100
     for code in [0, -1, -2, -3, 7]:
