@@ -124,13 +124,22 @@ using ElemK3S2 = ElemCfg<3, 2, 4, 4>;  // 4 x 32 pooled tile, 10 x 66 input
 using ElemK3S3 = ElemCfg<3, 3, 4, 4>;  // 4 x 20 pooled tile, 14 x 63 input
 using ElemK5S3 = ElemCfg<5, 3, 2, 4>;  // 4 x 10 pooled tile, 16 x 35 input
 
-template <class C, int POOL_MAX, int MODE>
+// POOL: kPoolMean (each conv output kept, then averaged), kPoolMax, or
+// kPoolMeanFolded: the average pool of a plain conv (no ReLU, floor mode),
+// where the pool's linearity lets the MFMAs add a window's rows into one
+// accumulator block per column block (which starts at s * bias), so only the
+// window's columns are summed afterwards.
+constexpr int kPoolMean = 0, kPoolMax = 1, kPoolMeanFolded = 2;
+
+template <class C, int POOL, int MODE>
 __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane, int tiles_w,
     int tiles, int co_ranges, int nblocks, int relu, int ceil_mode) {
     constexpr int K = C::K, S = C::S, NCB = C::NCB, TPH = C::TPH, TPW = C::TPW;
     constexpr int IH = C::IH, IW = C::IW, RP = C::RP, NR = C::NR, WPB = C::WPB, CPB = C::CPB;
+    constexpr bool POOL_MAX = POOL == kPoolMax, FOLD = POOL == kPoolMeanFolded;
+    constexpr int NACC = FOLD ? 1 : S;  // accumulator blocks per column block
 
     extern __shared__ float lds[];
     __shared__ float red[C::NW];
@@ -242,7 +251,10 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     // One channel quad of one pooled row.  In the first quad the first MFMA
     // into each accumulator block takes the bias as its C operand, so the
     // accumulators never need a separate initialisation.
-    floatx4 acc[NCB][S];
+    // Folded rows: each column accumulator sums S conv outputs, so it starts
+    // at S * bias.
+    if constexpr (FOLD) bco = bco * (float)S;
+    floatx4 acc[NCB][NACC];
     auto quad = [&](int q, int pr, auto first_tag) {
         constexpr bool FIRST = decltype(first_tag)::value;
         // The next quad's weights (quad 0 again after the last: the next
@@ -262,8 +274,9 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
                 for (int kx = 0; kx < K; ++kx)
 #pragma unroll
                     for (int nb = 0; nb < NCB; ++nb)
-                        acc[nb][dy] = mfma_16x16x4(a_cur[ky][kx], bcur[nb][kx],
-                                                   (FIRST && ky == 0 && kx == 0) ? bco : acc[nb][dy]);
+                        acc[nb][FOLD ? 0 : dy] = mfma_16x16x4(
+                            a_cur[ky][kx], bcur[nb][kx],
+                            (FIRST && ky == 0 && kx == 0 && (!FOLD || dy == 0)) ? bco : acc[nb][FOLD ? 0 : dy]);
             }
             if (rr + 1 < NR) {
 #pragma unroll
@@ -279,38 +292,43 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     };
 
     float lsum = 0.f;
-    auto pool_row = [&](const floatx4 (&ac)[NCB][S], int ph, int yr, auto edge_tag) {
+    auto pool_row = [&](const floatx4 (&ac)[NCB][NACC], int ph, int yr, auto edge_tag) {
         constexpr bool EDGE = decltype(edge_tag)::value;
         const float fill = POOL_MAX ? -INFINITY : 0.f;
 #pragma unroll
         for (int nb = 0; nb < NCB; ++nb) {
-            float v[S][4];
+            float m[4];
+            if constexpr (FOLD) {
 #pragma unroll
-            for (int dy = 0; dy < S; ++dy)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v[dy][r] = ac[nb][dy][r];
-            if (!POOL_MAX && relu) {
+                for (int r = 0; r < 4; ++r) m[r] = ac[nb][0][r];
+            } else {
+                float v[S][4];
 #pragma unroll
                 for (int dy = 0; dy < S; ++dy)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) v[dy][r] = fmaxf(v[dy][r], 0.f);
-            }
-            if constexpr (EDGE) {
-                const bool col_ok = x0 + nb * CPB + l16 < Wc;
+                    for (int r = 0; r < 4; ++r) v[dy][r] = ac[nb][dy][r];
+                if (!POOL_MAX && relu) {
 #pragma unroll
-                for (int dy = 0; dy < S; ++dy) {
-                    const bool ok = col_ok && (yr + dy < Hc);
+                    for (int dy = 0; dy < S; ++dy)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) v[dy][r] = ok ? v[dy][r] : fill;
+                        for (int r = 0; r < 4; ++r) v[dy][r] = fmaxf(v[dy][r], 0.f);
                 }
-            }
-            // Over the window's rows, inside the lane.
-            float m[4];
+                if constexpr (EDGE) {
+                    const bool col_ok = x0 + nb * CPB + l16 < Wc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                m[r] = v[0][r];
+                    for (int dy = 0; dy < S; ++dy) {
+                        const bool ok = col_ok && (yr + dy < Hc);
 #pragma unroll
-                for (int dy = 1; dy < S; ++dy) m[r] = pool2(m[r], v[dy][r]);
+                        for (int r = 0; r < 4; ++r) v[dy][r] = ok ? v[dy][r] : fill;
+                    }
+                }
+                // Over the window's rows, inside the lane.
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    m[r] = v[0][r];
+#pragma unroll
+                    for (int dy = 1; dy < S; ++dy) m[r] = pool2(m[r], v[dy][r]);
+                }
             }
             // Over the window's columns, across lanes.  Each case leaves NV
             // finished pooled values per lane, value i for channel
@@ -397,10 +415,14 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
         // copy of the epilogue that masks them.
         const int ph = ph0 + pr;
         const int yr = y0 + pr * S;
-        if (ceil_mode && (yr + S > Hc || x0 + TPW * S > Wc))
-            pool_row(acc, ph, yr, std::true_type{});
-        else
-            pool_row(acc, ph, yr, std::false_type{});
+        if constexpr (FOLD) {
+            pool_row(acc, ph, yr, std::false_type{});  // floor mode only: no partial windows
+        } else {
+            if (ceil_mode && (yr + S > Hc || x0 + TPW * S > Wc))
+                pool_row(acc, ph, yr, std::true_type{});
+            else
+                pool_row(acc, ph, yr, std::false_type{});
+        }
     }
 
     if constexpr (MODE != OUT_MAP) {
@@ -449,7 +471,7 @@ ElemGrid elem_grid(const Conv2dShape& s) {
     return {tiles_w, tiles_h * tiles_w, co_ranges, (int64_t)tiles_h * tiles_w * co_ranges * s.B};
 }
 
-template <class C, int POOL_MAX, int MODE>
+template <class C, int POOL, int MODE>
 hipError_t launch_elem_as(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
                           const PoolOpts& o, hipStream_t stream) {
     const int CINQ = (s.Cin + 3) / 4;
@@ -457,10 +479,10 @@ hipError_t launch_elem_as(const Conv2dShape& s, const float* x, const float* w, 
     const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
     const ElemGrid g = elem_grid<C>(s);
     if (g.nblocks > INT32_MAX) return hipErrorInvalidValue;
-    const void* fn = (const void*)conv2d_pool_elem_kernel<C, POOL_MAX, MODE>;
+    const void* fn = (const void*)conv2d_pool_elem_kernel<C, POOL, MODE>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((conv2d_pool_elem_kernel<C, POOL_MAX, MODE>), dim3((unsigned)g.nblocks), dim3(C::NT), lds,
+    hipLaunchKernelGGL((conv2d_pool_elem_kernel<C, POOL, MODE>), dim3((unsigned)g.nblocks), dim3(C::NT), lds,
                        stream, x, w, bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, g.tiles_w, g.tiles,
                        g.co_ranges, (int)g.nblocks, o.relu ? 1 : 0, o.ceil_mode ? 1 : 0);
     return hipGetLastError();
@@ -470,13 +492,19 @@ template <class C>
 hipError_t launch_elem_cfg(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
                            int mode, const PoolOpts& o, hipStream_t stream) {
     if (o.pool_max) {
-        if (mode == OUT_MAP) return launch_elem_as<C, 1, OUT_MAP>(s, x, w, bias, dst, o, stream);
-        if (mode == OUT_PARTIAL) return launch_elem_as<C, 1, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
-        return launch_elem_as<C, 1, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+        if (mode == OUT_MAP) return launch_elem_as<C, kPoolMax, OUT_MAP>(s, x, w, bias, dst, o, stream);
+        if (mode == OUT_PARTIAL) return launch_elem_as<C, kPoolMax, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
+        return launch_elem_as<C, kPoolMax, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
     }
-    if (mode == OUT_MAP) return launch_elem_as<C, 0, OUT_MAP>(s, x, w, bias, dst, o, stream);
-    if (mode == OUT_PARTIAL) return launch_elem_as<C, 0, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
-    return launch_elem_as<C, 0, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+    if (!o.relu && !o.ceil_mode) {
+        if (mode == OUT_MAP) return launch_elem_as<C, kPoolMeanFolded, OUT_MAP>(s, x, w, bias, dst, o, stream);
+        if (mode == OUT_PARTIAL)
+            return launch_elem_as<C, kPoolMeanFolded, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
+        return launch_elem_as<C, kPoolMeanFolded, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+    }
+    if (mode == OUT_MAP) return launch_elem_as<C, kPoolMean, OUT_MAP>(s, x, w, bias, dst, o, stream);
+    if (mode == OUT_PARTIAL) return launch_elem_as<C, kPoolMean, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
+    return launch_elem_as<C, kPoolMean, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
 }
 
 // Calls f with a value of the instance's config type for (K, S); returns
