@@ -46,7 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # of conv2d_pool_elem_kernel are <tiling <K, s, column blocks, pooled rows>,
 # pool (0 mean, 1 max, 2 mean with the rows folded into the MFMAs), output mode>.
 KERNEL_SOURCES = {
-    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 2, 0>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
+    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3>, 2, 0>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
                                                                   "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_tall_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                           "fp32_convolution_amd/csrc/fconv_device.hpp"],
@@ -59,7 +59,7 @@ KERNEL_SOURCES = {
 }
 
 
-ELEM_AVG = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 2, 0>"
+ELEM_AVG = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3>, 2, 0>"
 ELEM_MAX = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 1, 0>"
 
 

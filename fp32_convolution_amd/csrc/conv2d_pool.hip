@@ -359,7 +359,7 @@ hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float*
 
 int64_t conv2d_mfma_parts(const Conv2dShape& s) {
     dim3 g;
-    if (s.K == 3 && s.S == 4) return conv2d_elem_parts(s);
+    if (s.K == 3 && s.S == 4) return conv2d_elem_parts(s, PoolOpts{false, false, false});
     if (s.K == 5 && s.S == 3) g = direct_grid<CfgK5S3>(s);
     else if (s.K == 3 && s.S == 2) g = direct_grid<CfgK3S2>(s);
     else if (s.K == 3 && s.S == 3) g = direct_grid<CfgK3S3>(s);

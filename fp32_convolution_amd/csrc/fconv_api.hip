@@ -168,7 +168,7 @@ hipError_t launch_ex(const ExPlan& p, const float* x, const float* w, const floa
 int64_t parts_ex(const ExPlan& p) {
     if (p.s.PH == 0 || p.s.PW == 0) return 0;
     if (p.plain) return conv2d_parts(p.algo, p.s);
-    return p.algo == FCONV_ALGO_DIRECT_MFMA ? fconv::conv2d_elem_parts(p.s) : fconv::conv2d_general_parts(p.s);
+    return p.algo == FCONV_ALGO_DIRECT_MFMA ? fconv::conv2d_elem_parts(p.s, p.o) : fconv::conv2d_general_parts(p.s);
 }
 
 int run_conv2d_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w, int64_t Cout,

@@ -48,7 +48,7 @@ int64_t conv2d_simple_parts(const Conv2dShape& s);
 // pooled sizes under o.ceil_mode.  The matrix-core kernel has one instance
 // (K = 3, s = 4); the general kernel takes any shape.
 bool conv2d_elem_supported(int Cin, int K, int S);
-int64_t conv2d_elem_parts(const Conv2dShape& s);
+int64_t conv2d_elem_parts(const Conv2dShape& s, const PoolOpts& o);
 int64_t conv2d_general_parts(const Conv2dShape& s);
 hipError_t conv2d_elem_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
                               int mode, const PoolOpts& o, hipStream_t stream);

@@ -106,8 +106,8 @@ def test_select_algo(lib):
 def test_det_workspace_query(lib):
     import fp32_convolution_amd as fc
 
-    # direct MFMA on x[128,8,384,384], 4x16 pooled tiles of a 95x95 map: 24*6 workgroups per item
-    assert fc.conv2d_det_workspace_bytes(128, 8, 384, 384, 64, 3, 4, algo=1) == 128 * 24 * 6 * 4
+    # direct MFMA on x[128,8,384,384] (folded average pool), 3x16 pooled tiles of a 95x95 map: 32*6 per item
+    assert fc.conv2d_det_workspace_bytes(128, 8, 384, 384, 64, 3, 4, algo=1) == 128 * 32 * 6 * 4
     # box-sum (K = 3, s = 4, W % 4 == 0) has 2 x 48 pooled tiles: 48 * 2 per item; with W % 4 != 0 it
     # uses the direct kernel's tiles; the simple path one workgroup per 256 pooled values of an item
     assert fc.conv2d_det_workspace_bytes(128, 8, 384, 384, 64, 3, 4, algo=3) == 128 * 48 * 2 * 4
