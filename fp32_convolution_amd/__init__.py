@@ -114,6 +114,8 @@ def _dev_f32(t, name):
     return t
 
 
+# Every call runs with the tensors' device current and enqueues on that
+# device's current torch stream.
 def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -167,12 +169,13 @@ def conv2d_pool_sigmoid_sum(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO,
         if tuple(out.shape) != (B,) or out.device != x.device:
             raise ValueError("out must be [B] on x's device")
     flags = _pool_flags(relu, ceil_mode)
-    if pool_mode == POOL_AVG and flags == 0:
-        rc = lib.fconv2d_pool_sigmoid_sum_algo(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
-                                               _ptr(out), _stream(x))
-    else:
-        rc = lib.fconv2d_pool_sigmoid_sum_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode,
-                                             flags, algo, _ptr(out), _stream(x))
+    with torch.cuda.device(x.device):
+        if pool_mode == POOL_AVG and flags == 0:
+            rc = lib.fconv2d_pool_sigmoid_sum_algo(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
+                                                   _ptr(out), _stream(x))
+        else:
+            rc = lib.fconv2d_pool_sigmoid_sum_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode,
+                                                 flags, algo, _ptr(out), _stream(x))
     _check(rc, "fconv2d_pool_sigmoid_sum")
     return out
 
@@ -214,12 +217,13 @@ def conv2d_pool_sigmoid_sum_det(x, w, b, pool: int, out=None, algo: int = ALGO_A
         raise ValueError("workspace must be a contiguous tensor on x's device")
     nbytes = workspace.numel() * workspace.element_size()
     flags = _pool_flags(relu, ceil_mode)
-    if pool_mode == POOL_AVG and flags == 0:
-        rc = lib.fconv2d_pool_sigmoid_sum_det(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
-                                              _ptr(workspace), nbytes, _ptr(out), _stream(x))
-    else:
-        rc = lib.fconv2d_pool_sigmoid_sum_det_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode,
-                                                 flags, algo, _ptr(workspace), nbytes, _ptr(out), _stream(x))
+    with torch.cuda.device(x.device):
+        if pool_mode == POOL_AVG and flags == 0:
+            rc = lib.fconv2d_pool_sigmoid_sum_det(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
+                                                  _ptr(workspace), nbytes, _ptr(out), _stream(x))
+        else:
+            rc = lib.fconv2d_pool_sigmoid_sum_det_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode,
+                                                     flags, algo, _ptr(workspace), nbytes, _ptr(out), _stream(x))
     _check(rc, "fconv2d_pool_sigmoid_sum_det")
     return out
 
@@ -238,12 +242,13 @@ def conv2d_pool_map(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO, pool_mo
         if tuple(out.shape) != (B, Cout, PH, PW) or out.device != x.device:
             raise ValueError("out must be [B,Cout,PH,PW] on x's device")
     flags = _pool_flags(relu, ceil_mode)
-    if pool_mode == POOL_AVG and flags == 0:
-        rc = lib.fconv2d_pool_map(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo, _ptr(out),
-                                  _stream(x))
-    else:
-        rc = lib.fconv2d_pool_map_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode, flags, algo,
-                                     _ptr(out), _stream(x))
+    with torch.cuda.device(x.device):
+        if pool_mode == POOL_AVG and flags == 0:
+            rc = lib.fconv2d_pool_map(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo, _ptr(out),
+                                      _stream(x))
+        else:
+            rc = lib.fconv2d_pool_map_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode, flags, algo,
+                                         _ptr(out), _stream(x))
     _check(rc, "fconv2d_pool_map")
     return out
 
@@ -288,7 +293,8 @@ def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None, stride: int = 1, dilat
         _dev_f32(out, "out")
         if tuple(out.shape) != (B, O, Tout):
             raise ValueError(f"out must be [B,O,Tout]=({B},{O},{Tout})")
-    rc = lib.dwsep_conv1d_algo(_ptr(x), B, C, T, _ptr(w_dw), K, _ptr(w_pw), O, _ptr(b_pw), pad, stride, dilation,
-                               algo, _ptr(out), _stream(x))
+    with torch.cuda.device(x.device):
+        rc = lib.dwsep_conv1d_algo(_ptr(x), B, C, T, _ptr(w_dw), K, _ptr(w_pw), O, _ptr(b_pw), pad, stride, dilation,
+                                   algo, _ptr(out), _stream(x))
     _check(rc, "dwsep_conv1d")
     return out
