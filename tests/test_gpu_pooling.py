@@ -113,6 +113,41 @@ def test_pool_small(fc, shape, combo, algo):
     assert_close(got_out, want_out, f"out {shape} {combo_id(combo)}")
 
 
+LDS_LIMITS = [(3, 4, 32), (3, 2, 56), (3, 3, 40), (5, 3, 68)]   # (K, s, largest Cin whose LDS tile fits)
+
+
+@pytest.mark.parametrize("K,s,cin_max", LDS_LIMITS)
+def test_pool_largest_lds_tile(fc, K, s, cin_max):
+    # the matrix-core instance at its largest channel count (a full LDS tile: staging, plane padding and
+    # reads at the end of LDS), and one channel more, where AUTO falls back and DIRECT_MFMA is refused
+    H, W = 4 * s + K + 3, 17 * s + K + 1
+    announce(f"pool ex largest LDS tile K={K} s={s} Cin={cin_max}")
+    for Cin in (cin_max, cin_max + 1):
+        x, w, b = fi.conv2d_inputs(1, Cin, H, W, 20, K, seed=60 + Cin)
+        xd, wd, bd = dev(x), dev(w), dev(b)
+        for pool_mode, relu, ceil_mode in [(MAX, True, True), (AVG, False, False), (AVG, True, False)]:
+            kw = dict(pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+            want_out, want_map = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, want_pooled=True, **kw)
+            plain = pool_mode == AVG and not relu and not ceil_mode
+            try:  # host-side support query of DIRECT_MFMA (the plain average pool uses the base kernels' limits)
+                fc.conv2d_det_workspace_bytes(1, Cin, H, W, 20, K, s, 1, pool_mode, relu, ceil_mode)
+                mfma = True
+            except fc.FconvError as e:
+                assert e.status == fc.FCONV_EUNSUPPORTED
+                mfma = False
+            if not plain:  # the generalised pool's instances: exactly up to cin_max
+                assert mfma == (Cin == cin_max)
+            if mfma:
+                got = fc.conv2d_pool_map(xd, wd, bd, s, algo=1, **kw).cpu().numpy()
+                assert_close(got, want_map, f"K{K} s{s} Cin {Cin} {combo_id((pool_mode, relu, ceil_mode))}")
+            else:
+                with pytest.raises(fc.FconvError) as err:
+                    fc.conv2d_pool_map(xd, wd, bd, s, algo=1, **kw)
+                assert err.value.status == fc.FCONV_EUNSUPPORTED
+            got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=0, **kw).cpu().numpy()
+            assert_close(got_out, want_out, f"AUTO out K{K} s{s} Cin {Cin}")
+
+
 @pytest.mark.parametrize("combo", COMBOS[1:], ids=combo_id)
 def test_pool_boxsum_refused(fc, combo):
     pool_mode, relu, ceil_mode = combo
