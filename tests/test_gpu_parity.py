@@ -124,6 +124,40 @@ def test_conv2d_boxsum_one_column_per_lane(fc, shape, aligned):
     assert_close(det, want_out, f"deterministic out {shape}")
 
 
+def largest_supported_cin(fc, K, s, H, W, algo):
+    """Largest Cin (up to 256) for which the algorithm has an instance, by the host-side query."""
+    best = 0
+    for cin in range(1, 257):
+        try:
+            fc.conv2d_det_workspace_bytes(1, cin, H, W, 8, K, s, algo)
+            best = cin
+        except fc.FconvError as e:
+            assert e.status == fc.FCONV_EUNSUPPORTED
+    return best
+
+
+@pytest.mark.parametrize("K,s,wx", [(3, 4, 3), (3, 4, 1), (5, 3, 3), (3, 2, 3), (3, 3, 3)])
+@pytest.mark.parametrize("algo", [1, 3])
+def test_conv2d_largest_lds_tile(fc, K, s, wx, algo):
+    # each algorithm at the largest channel count its LDS tile takes (support is contiguous in Cin:
+    # nothing larger is accepted), checked against the oracle; one channel more is refused.  K3/s4
+    # with wx = 1 has W % 4 == 0, which box-sum runs on its one-column-per-lane kernel.
+    H, W = 5 * s + K + 2, 33 * s + K + wx
+    cin = largest_supported_cin(fc, K, s, H, W, algo)
+    announce(f"conv2d largest LDS tile K={K} s={s} algo={algo} Cin={cin}")
+    assert cin >= 8
+    x, w, b = fi.conv2d_inputs(2, cin, H, W, 70, K, seed=24)
+    want_out, want_map = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, want_pooled=True)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    assert_close(fc.conv2d_pool_map(xd, wd, bd, s, algo=algo).cpu().numpy(), want_map, f"map Cin={cin}")
+    assert_close(fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=algo).cpu().numpy(), want_out, f"out Cin={cin}")
+    if cin < 256:
+        x1, w1, b1 = fi.conv2d_inputs(1, cin + 1, H, W, 8, K, seed=25)
+        with pytest.raises(fc.FconvError) as err:
+            fc.conv2d_pool_sigmoid_sum(dev(x1), dev(w1), dev(b1), s, algo=algo)
+        assert err.value.status == fc.FCONV_EUNSUPPORTED
+
+
 @pytest.mark.parametrize("algo", [1, 3])
 def test_conv2d_no_bias(fc, algo):
     announce(f"conv2d no bias algo={algo}")
@@ -270,6 +304,26 @@ TALL_DW = [
     (1, 32, 70, 300, 1, 0),      # 1-tap depthwise
     (1, 44, 200, 1100, 3, 1),    # three output tiles, C not a multiple of 16
 ]
+
+
+def test_dwsep_widest_windows(fc):
+    # the runtime-K kernels up to the widest depthwise window their LDS tile stages, then refusal:
+    # every supported K is checked against the oracle, and support ends at one K (no gaps)
+    announce("dwsep widest windows")
+    supported = []
+    for K in (66, 129, 257, 400, 480, 500, 520, 600, 1000, 4000):
+        B, C, T, O, pad = 1, 8, K + 40, 300, K // 2
+        x, wd, wp, bp = fi.dwsep_inputs(B, C, T, O, K, seed=26)
+        try:
+            got = fc.dwsep_conv1d(dev(x), dev(wd), dev(wp), dev(bp), pad).cpu().numpy()
+        except fc.FconvError as e:
+            assert e.status == fc.FCONV_EUNSUPPORTED, K
+            continue
+        supported.append(K)
+        assert_close(got, oracle.dwsep_conv1d(x, wd, wp, bp, pad), f"dwsep K={K}")
+    assert supported and supported[0] == 66 and 400 in supported, supported
+    assert supported == [k for k in (66, 129, 257, 400, 480, 500, 520, 600, 1000, 4000) if k <= supported[-1]]
+    assert 4000 not in supported
 
 
 @pytest.mark.parametrize("shape", TALL_DW)
