@@ -422,7 +422,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
                 float s = 0.f;
 #pragma unroll
                 for (int k = 0; k < 9; ++k) s += wv[k] * xv[i + k];
-                Ds[(8 * dj + i) * CCP + c] = s;
+                Ds[(8 * dj + i) * CCP + (c ^ ((dj >> 1) << 2))] = s;  // swizzled: see read_d
             }
         } else {
             float d[CPW];
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
             }
 #pragma unroll
             for (int c4 = 0; c4 < CPW; c4 += 4)
-                *reinterpret_cast<floatx4*>(Ds + lane * CCP + wave * CPW + c4) =
+                *reinterpret_cast<floatx4*>(Ds + lane * CCP + ((wave * CPW + c4) ^ ((lane >> 4) << 2))) =
                     floatx4{d[c4], d[c4 + 1], d[c4 + 2], d[c4 + 3]};
         }
         __syncthreads();
@@ -448,8 +448,14 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
         //    half's D registers take the next group's D once used.  The
         //    scheduling fences keep that order: without them the compiler
         //    moves the next group's first products up against their loads.
+        // D[t][c] sits at column c ^ 4*(t >> 4) of row t: the 4-channel groups
+        // stay whole for these 16-byte reads (all lanes of one read share
+        // t >> 4 = tb, so they remain conflict-free), while the depthwise
+        // stage's writes, whose lanes cover 8 rows 8 apart (row pitch 68:
+        // every other row lands on the same banks), spread over 32 banks
+        // instead of 8.  This halved the kernel's LDS bank-conflict cycles.
         auto read_d = [&](floatx4& dst, int tb, int s16) {
-            dst = *reinterpret_cast<const floatx4*>(Ds + (tb * 16 + l16) * CCP + s16 + 4 * g);
+            dst = *reinterpret_cast<const floatx4*>(Ds + (tb * 16 + l16) * CCP + ((s16 + 4 * g) ^ (tb << 2)));
         };
         floatx4 bq[TB];
 #pragma unroll
