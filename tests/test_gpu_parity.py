@@ -158,6 +158,53 @@ def test_conv2d_largest_lds_tile(fc, K, s, wx, algo):
         assert err.value.status == fc.FCONV_EUNSUPPORTED
 
 
+@pytest.fixture(scope="module")
+def largest_item():
+    # x[2,2,16384,16383]: 536,838,144 elements per batch item, just under the 2^29 the ABI accepts
+    # (in-item offsets are 32-bit), 4.3 GB in all (batch offsets past 2^31 bytes)
+    B, Cin, H, W, Cout, K = 2, 2, 16384, 16383, 16, 3
+    x, w, b = fi.conv2d_inputs(B, Cin, H, W, Cout, K, seed=27)
+    return x, w, b
+
+
+@pytest.mark.parametrize("algo,pool_mode,relu,ceil_mode", [(0, 0, False, False), (1, 0, False, False),
+                                                          (3, 0, False, False), (0, 1, True, True)])
+def test_conv2d_largest_batch_item(fc, largest_item, algo, pool_mode, relu, ceil_mode):
+    x, w, b = largest_item
+    B, Cin, H, W = x.shape
+    assert Cin * H * W < 2 ** 29 and B * Cin * H * W * 4 > 2 ** 31
+    announce(f"conv2d largest batch item x{list(x.shape)} algo={algo} pool_mode={pool_mode} relu={relu} "
+             f"ceil={ceil_mode}")
+    kw = dict(pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, 4, algo=algo, **kw).cpu().numpy()
+    got_map = fc.conv2d_pool_map(xd, wd, bd, 4, algo=algo, **kw)
+    del xd
+    Bq, Cout, PH, PW = got_map.shape
+    rng = np.random.default_rng(28)
+    n = 3000
+    samp = np.stack([rng.integers(0, Bq, n), rng.integers(0, Cout, n), rng.integers(0, PH, n),
+                     rng.integers(0, PW, n)], axis=1)
+    corners = [(bb, co, ph, pw) for bb in (0, Bq - 1) for co in (0, Cout - 1) for ph in (0, PH - 1)
+               for pw in (0, PW - 1)]
+    samp = np.concatenate([samp, np.array(corners)], axis=0)
+    want = oracle.conv2d_pooled_at(x, w, b, 4, samp, **kw)
+    got = got_map[tuple(torch.from_numpy(samp.T).cuda())].cpu().numpy()
+    assert_close(got, want, "sampled pooled map")
+    # the literal oracle keeps one full conv map (2.1 GB in double) per thread: 8 threads
+    want_out = oracle.conv2d_pool_sigmoid_sum(x, w, b, 4, batch_idx=[1], nthreads=8, **kw)
+    # The deterministic form adds the per-workgroup partials in a fixed order from small values up:
+    # within the 1e-4 bar of the oracle.
+    det = fc.conv2d_pool_sigmoid_sum_det(dev(x), wd, bd, 4, algo=algo, **kw).cpu().numpy()
+    assert_close(det[[1]], want_out, "deterministic out[1] (second batch item, past 2^31 bytes)")
+    # The atomic form adds each workgroup's partial into one fp32 total: every add rounds by up to half
+    # an ulp of the total, so its error bound grows with the number of workgroups per item (about 350 K
+    # here, against 144 for x[128,8,384,384]).
+    parts = fc.conv2d_det_workspace_bytes(B, Cin, H, W, Cout, w.shape[2], 4, algo, **kw) // (4 * B)
+    bound = parts * 0.5 * 2.0 ** (np.floor(np.log2(np.abs(want_out))) - 23)
+    assert np.abs(got_out[[1]] - want_out) <= bound + 1e-4 * np.abs(want_out), (got_out[1], want_out, bound)
+
+
 @pytest.mark.parametrize("algo", [1, 3])
 def test_conv2d_no_bias(fc, algo):
     announce(f"conv2d no bias algo={algo}")
