@@ -44,9 +44,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # only while their hash matches the one recorded with the counters.
 # Keys are kernel-name parts as rocprofv3 prints them; the template arguments
 # of conv2d_pool_elem_kernel are <tiling <K, s, column blocks, pooled rows>,
-# pool (0 mean, 1 max, 2 mean with the rows folded into the MFMAs), output mode>.
+# pool (0 mean, 1 max, 2 mean with the rows folded into the MFMAs), output mode,
+# channel quads with weights resident in registers (0: streamed)>.
 KERNEL_SOURCES = {
-    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3>, 2, 0>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
+    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3>, 2, 0, 2>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
                                                                   "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_tall_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                           "fp32_convolution_amd/csrc/fconv_device.hpp"],
@@ -54,13 +55,13 @@ KERNEL_SOURCES = {
                                   "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_dense_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                            "fp32_convolution_amd/csrc/fconv_device.hpp"],
-    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 1, 0>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
+    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 1, 0, 2>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
                                                                   "fp32_convolution_amd/csrc/fconv_device.hpp"],
 }
 
 
-ELEM_AVG = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3>, 2, 0>"
-ELEM_MAX = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 1, 0>"
+ELEM_AVG = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3>, 2, 0, 2>"
+ELEM_MAX = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 1, 0, 2>"
 
 
 def sources_sha256(kernel):

@@ -135,7 +135,10 @@ using ElemK5S3 = ElemCfg<5, 3, 2, 4>;  // 4 x 10 pooled tile, 16 x 35 input
 // window's columns are summed afterwards.
 constexpr int kPoolMean = 0, kPoolMax = 1, kPoolMeanFolded = 2;
 
-template <class C, int POOL, int MODE>
+// NQ: 0, or the number of channel quads CINQ (1 or 2) when all of them fit
+// in registers.  Then the block's weights load once; otherwise quad q's
+// weights stream in under quad q-1's matrix instructions.
+template <class C, int POOL, int MODE, int NQ>
 __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane, int tiles_w,
@@ -144,6 +147,7 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     constexpr int IH = C::IH, IW = C::IW, RP = C::RP, NR = C::NR, WPB = C::WPB, CPB = C::CPB;
     constexpr bool POOL_MAX = POOL == kPoolMax, FOLD = POOL == kPoolMeanFolded;
     constexpr int NACC = FOLD ? 1 : S;  // accumulator blocks per column block
+    static_assert(NQ >= 0 && NQ <= 2, "resident weights for one or two channel quads");
 
     extern __shared__ float lds[];
     __shared__ float red[C::NW];
@@ -184,8 +188,11 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
 #pragma unroll
             for (int kx = 0; kx < K; ++kx) a[ky][kx] = buf_load_f32(rw, base + (ky * K + kx) * 4);
     };
-    float a_cur[K][K], a_nxt[K][K];
-    load_a(a_cur, 0);
+    // Streaming: a[0] holds the current quad's weights, a[1] the next one's.
+    // Resident: a[q] holds quad q's.
+    float a[2][K][K];
+    load_a(a[0], 0);
+    if constexpr (NQ == 2) load_a(a[1], 1);
 
     // Bias of the channels this lane's accumulator elements hold: co0 + 4g + r.
     const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     // rows outside the image and channels >= Cin, which therefore read 0).
     {
         constexpr int NCH = (IW + 63) / 64;
-        constexpr int UR = 4;
+        constexpr int UR = 14;  // rows in flight per wave
         int voff[NCH];
         bool inr[NCH];
 #pragma unroll
@@ -239,37 +246,41 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     }
     __syncthreads();
 
-    const int bbase = g * CINQ * plane + l16;
     // A column block's lanes read 16 consecutive words; the 4 channel groups
-    // sit plane*CINQ words apart (padded onto different banks).
-    auto load_row = [&](float (&bv)[NCB][K], int off) {
+    // sit plane*CINQ words apart (padded onto different banks).  Rows of one
+    // pooled row read from two base registers: rows 0 .. RG-1 from the
+    // first, the rest from a second one RG rows further on, so that every
+    // read keeps within the 8-bit dword offsets of paired LDS reads.
+    constexpr int RG = (255 - (NCB - 1) * CPB - (K - 1)) / RP + 1;
+    static_assert(RG >= 1 && NR <= 2 * RG, "two base registers reach every row");
+    const lds_fptr lbase = (lds_fptr)lds + g * CINQ * plane + l16;
+    auto load_row = [&](float (&bv)[NCB][K], lds_fptr row) {
 #pragma unroll
         for (int nb = 0; nb < NCB; ++nb)
 #pragma unroll
-            for (int kx = 0; kx < K; ++kx) bv[nb][kx] = lds[bbase + off + nb * CPB + kx];
+            for (int kx = 0; kx < K; ++kx) bv[nb][kx] = row[nb * CPB + kx];
     };
 
     const bool odd1 = (l16 & 1) != 0, odd2 = (l16 & 2) != 0;
     auto pool2 = [](float a, float c) { return POOL_MAX ? fmaxf(a, c) : a + c; };
 
-    // One channel quad of one pooled row.  In the first quad the first MFMA
-    // into each accumulator block takes the bias as its C operand, so the
-    // accumulators never need a separate initialisation.
+    // One channel quad of one pooled row with weights aq.  In the first quad
+    // the first MFMA into each accumulator block takes the bias as its C
+    // operand, so the accumulators never need a separate initialisation.
     // Folded rows: each column accumulator sums S conv outputs, so it starts
     // at S * bias.
     if constexpr (FOLD) bco = bco * (float)S;
     floatx4 acc[NCB][NACC];
-    auto quad = [&](int q, int pr, auto first_tag) {
+    auto mma_quad = [&](const float (&aq)[K][K], int q, int pr, auto first_tag) {
         constexpr bool FIRST = decltype(first_tag)::value;
-        // The next quad's weights (quad 0 again after the last: the next
-        // pooled row starts there) load under this quad's MFMAs.
-        load_a(a_nxt, q + 1 < CINQ ? q + 1 : 0);
-        const int off0 = q * plane + pr * S * RP;
+        const lds_fptr p0 = lbase + q * plane + pr * S * RP;
+        const lds_fptr p1 = NR > RG ? lds_opaque(p0 + RG * RP) : p0;
+        auto row = [&](int rr) { return rr < RG ? p0 + rr * RP : p1 + (rr - RG) * RP; };
         float bcur[NCB][K], bnxt[NCB][K];
-        load_row(bcur, off0);
+        load_row(bcur, row(0));
 #pragma unroll
         for (int rr = 0; rr < NR; ++rr) {
-            if (rr + 1 < NR) load_row(bnxt, off0 + (rr + 1) * RP);
+            if (rr + 1 < NR) load_row(bnxt, row(rr + 1));
 #pragma unroll
             for (int ky = 0; ky < K; ++ky) {
                 const int dy = rr - ky;
@@ -279,7 +290,7 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
 #pragma unroll
                     for (int nb = 0; nb < NCB; ++nb)
                         acc[nb][FOLD ? 0 : dy] = mfma_16x16x4(
-                            a_cur[ky][kx], bcur[nb][kx],
+                            aq[ky][kx], bcur[nb][kx],
                             (FIRST && ky == 0 && kx == 0 && (!FOLD || dy == 0)) ? bco : acc[nb][FOLD ? 0 : dy]);
             }
             if (rr + 1 < NR) {
@@ -289,15 +300,23 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
                     for (int kx = 0; kx < K; ++kx) bcur[nb][kx] = bnxt[nb][kx];
             }
         }
+    };
+    // Streaming weights: the next quad's (quad 0 again after the last: the
+    // next pooled row starts there) load under this quad's MFMAs.
+    auto quad_stream = [&](int q, int pr, auto first_tag) {
+        load_a(a[1], q + 1 < CINQ ? q + 1 : 0);
+        mma_quad(a[0], q, pr, first_tag);
 #pragma unroll
         for (int ky = 0; ky < K; ++ky)
 #pragma unroll
-            for (int kx = 0; kx < K; ++kx) a_cur[ky][kx] = a_nxt[ky][kx];
+            for (int kx = 0; kx < K; ++kx) a[0][ky][kx] = a[1][ky][kx];
     };
 
     float lsum = 0.f;
-    auto pool_row = [&](const floatx4 (&ac)[NCB][NACC], int ph, int yr, auto edge_tag) {
-        constexpr bool EDGE = decltype(edge_tag)::value;
+    // FULL: every column of the tile and every channel of the wave lies
+    // inside the pooled map, so no lane needs a range check.
+    auto pool_row = [&](const floatx4 (&ac)[NCB][NACC], int ph, int yr, auto edge_tag, auto full_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value, FULL = decltype(full_tag)::value;
         const float fill = POOL_MAX ? -INFINITY : 0.f;
 #pragma unroll
         for (int nb = 0; nb < NCB; ++nb) {
@@ -383,23 +402,25 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
             }
 
             const int pw = pw0 + nb * WPB + win;
-            if (fin && pw < PW) {
+            if (fin && (FULL || pw < PW)) {
                 const float inv = EDGE ? 1.0f / (float)(min(S, Hc - ph * S) * min(S, Wc - pw * S))
                                        : 1.0f / (float)(S * S);
 #pragma unroll
                 for (int i = 0; i < NV; ++i) {
                     const int co = co0 + 4 * g + chan[i];
-                    if (co < Cout) {
+                    if (FULL || co < Cout) {
                         float o = pv[i];
                         if (POOL_MAX) {
                             if (relu) o = fmaxf(o, 0.f);  // ReLU commutes with max
-                        } else {
+                        } else if (EDGE || MODE == OUT_MAP) {
                             o = o * inv;
                         }
                         if constexpr (MODE == OUT_MAP)
                             dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = o;
-                        else
+                        else if (POOL_MAX || EDGE)
                             lsum += logistic(o);
+                        else
+                            lsum += logistic_scaled(o, inv);
                     }
                 }
             }
@@ -407,9 +428,15 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     };
 
     const int nrow_tile = min(TPH, PH - ph0);
+    const bool full = pw0 + TPW <= PW && co0 + 16 <= Cout;
     for (int pr = 0; pr < nrow_tile; ++pr) {
-        quad(0, pr, std::true_type{});
-        for (int q = 1; q < CINQ; ++q) quad(q, pr, std::false_type{});
+        if constexpr (NQ > 0) {
+            mma_quad(a[0], 0, pr, std::true_type{});
+            if constexpr (NQ == 2) mma_quad(a[1], 1, pr, std::false_type{});
+        } else {
+            quad_stream(0, pr, std::true_type{});
+            for (int q = 1; q < CINQ; ++q) quad_stream(q, pr, std::false_type{});
+        }
 
         // Epilogue of pooled row ph.  Lane (g, l16) holds in acc[nb][dy][r]
         // the conv output of channel co0 + 4g + r at conv row ph*S + dy,
@@ -419,14 +446,12 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
         // copy of the epilogue that masks them.
         const int ph = ph0 + pr;
         const int yr = y0 + pr * S;
-        if constexpr (FOLD) {
-            pool_row(acc, ph, yr, std::false_type{});  // floor mode only: no partial windows
-        } else {
-            if (ceil_mode && (yr + S > Hc || x0 + TPW * S > Wc))
-                pool_row(acc, ph, yr, std::true_type{});
-            else
-                pool_row(acc, ph, yr, std::false_type{});
-        }
+        if (!FOLD && ceil_mode && (yr + S > Hc || x0 + TPW * S > Wc))
+            pool_row(acc, ph, yr, std::true_type{}, std::false_type{});  // (the folded pool has floor mode only)
+        else if (full)
+            pool_row(acc, ph, yr, std::false_type{}, std::true_type{});
+        else
+            pool_row(acc, ph, yr, std::false_type{}, std::false_type{});
     }
 
     if constexpr (MODE != OUT_MAP) {
@@ -462,6 +487,9 @@ size_t elem_lds_bytes(int Cin) {
     return (size_t)4 * CINQ * elem_plane<C>(CINQ) * sizeof(float);
 }
 
+// The plain average pool (no ReLU, floor mode) runs folded.
+bool folds(const PoolOpts& o) { return !o.pool_max && !o.relu && !o.ceil_mode; }
+
 struct ElemGrid {
     int tiles_w, tiles, co_ranges;
     int64_t nblocks;
@@ -475,45 +503,64 @@ ElemGrid elem_grid(const Conv2dShape& s) {
     return {tiles_w, tiles_h * tiles_w, co_ranges, (int64_t)tiles_h * tiles_w * co_ranges * s.B};
 }
 
-template <class C, int POOL, int MODE>
-hipError_t launch_elem_as(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+template <class C, int POOL, int MODE, int NQ>
+hipError_t launch_elem_nq(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
                           const PoolOpts& o, hipStream_t stream) {
     const int CINQ = (s.Cin + 3) / 4;
     const int plane = elem_plane<C>(CINQ);
     const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
     const ElemGrid g = elem_grid<C>(s);
     if (g.nblocks > INT32_MAX) return hipErrorInvalidValue;
-    const void* fn = (const void*)conv2d_pool_elem_kernel<C, POOL, MODE>;
+    const void* fn = (const void*)conv2d_pool_elem_kernel<C, POOL, MODE, NQ>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((conv2d_pool_elem_kernel<C, POOL, MODE>), dim3((unsigned)g.nblocks), dim3(C::NT), lds,
+    hipLaunchKernelGGL((conv2d_pool_elem_kernel<C, POOL, MODE, NQ>), dim3((unsigned)g.nblocks), dim3(C::NT), lds,
                        stream, x, w, bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, g.tiles_w, g.tiles,
                        g.co_ranges, (int)g.nblocks, o.relu ? 1 : 0, o.ceil_mode ? 1 : 0);
     return hipGetLastError();
 }
 
+// One or two channel quads keep their weights in registers.
+template <class C, int POOL, int MODE>
+hipError_t launch_elem_as(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                          const PoolOpts& o, hipStream_t stream) {
+    const int CINQ = (s.Cin + 3) / 4;
+    if (CINQ == 1) return launch_elem_nq<C, POOL, MODE, 1>(s, x, w, bias, dst, o, stream);
+    if (CINQ == 2) return launch_elem_nq<C, POOL, MODE, 2>(s, x, w, bias, dst, o, stream);
+    return launch_elem_nq<C, POOL, MODE, 0>(s, x, w, bias, dst, o, stream);
+}
+
+// The K = 3, s = 4 tiling has a folded-pool config and one for the other
+// pools; each is only launched for its own.
 template <class C>
 hipError_t launch_elem_cfg(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
                            int mode, const PoolOpts& o, hipStream_t stream) {
-    if (o.pool_max) {
-        if (mode == OUT_MAP) return launch_elem_as<C, kPoolMax, OUT_MAP>(s, x, w, bias, dst, o, stream);
-        if (mode == OUT_PARTIAL) return launch_elem_as<C, kPoolMax, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
-        return launch_elem_as<C, kPoolMax, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+    constexpr bool fold_only = std::is_same<C, ElemK3S4Fold>::value, no_fold = std::is_same<C, ElemK3S4>::value;
+    if constexpr (!fold_only) {
+        if (o.pool_max) {
+            if (mode == OUT_MAP) return launch_elem_as<C, kPoolMax, OUT_MAP>(s, x, w, bias, dst, o, stream);
+            if (mode == OUT_PARTIAL) return launch_elem_as<C, kPoolMax, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
+            return launch_elem_as<C, kPoolMax, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+        }
     }
-    if (!o.relu && !o.ceil_mode) {
-        if (mode == OUT_MAP) return launch_elem_as<C, kPoolMeanFolded, OUT_MAP>(s, x, w, bias, dst, o, stream);
-        if (mode == OUT_PARTIAL)
-            return launch_elem_as<C, kPoolMeanFolded, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
-        return launch_elem_as<C, kPoolMeanFolded, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+    if constexpr (!no_fold) {
+        if (folds(o)) {
+            if (mode == OUT_MAP) return launch_elem_as<C, kPoolMeanFolded, OUT_MAP>(s, x, w, bias, dst, o, stream);
+            if (mode == OUT_PARTIAL)
+                return launch_elem_as<C, kPoolMeanFolded, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
+            return launch_elem_as<C, kPoolMeanFolded, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+        }
     }
-    if (mode == OUT_MAP) return launch_elem_as<C, kPoolMean, OUT_MAP>(s, x, w, bias, dst, o, stream);
-    if (mode == OUT_PARTIAL) return launch_elem_as<C, kPoolMean, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
-    return launch_elem_as<C, kPoolMean, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+    if constexpr (!fold_only) {
+        if (mode == OUT_MAP) return launch_elem_as<C, kPoolMean, OUT_MAP>(s, x, w, bias, dst, o, stream);
+        if (mode == OUT_PARTIAL) return launch_elem_as<C, kPoolMean, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
+        return launch_elem_as<C, kPoolMean, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 // Calls f with a value of the instance's config type for (K, S) and the
 // pool variant; returns false if there is no instance.
-bool folds(const PoolOpts& o) { return !o.pool_max && !o.relu && !o.ceil_mode; }
 
 template <class F>
 bool with_elem_cfg(int K, int S, bool fold, F&& f) {

@@ -70,27 +70,47 @@ __device__ __forceinline__ float block_sum(float v, float* red /* NWAVES floats 
 }
 
 // DPP quad permutations: lane l reads lane l^1 (quad_perm 1,0,3,2) or lane
-// l^2 (quad_perm 2,3,0,1) of its aligned group of 4 lanes.
+// l^2 (quad_perm 2,3,0,1) of its aligned group of 4 lanes.  Every lane has a
+// valid source, so the move needs no old value and can fuse into the
+// instruction that uses it.
 __device__ __forceinline__ float quad_xor1(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float quad_xor2(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
 }
 
 // DPP row shifts: lane l reads lane l-1 (row_shr:1) or l-2 (row_shr:2) of its
 // row of 16 lanes; the first one or two lanes of each row read 0.
 __device__ __forceinline__ float row_shr1(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x111, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float row_shr2(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x112, 0xF, 0xF, true));
 }
 
 // Logistic sigmoid 1/(1+e^-a) with the hardware exp2 (v_exp_f32) and
 // reciprocal: relative error a few ulp for |a| < 80, exactly 1/2 at a = 0,
 // saturating to 0 or 1 (never NaN) for large |a|.
 __device__ __forceinline__ float logistic(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+
+// logistic(a * scale), the scale (an average pool's 1/s^2) joined to the
+// exponent's constant -log2(e): one multiply instead of two.  For a
+// power-of-two scale the product rounds exactly as (a * scale) * -log2(e)
+// does; otherwise it may differ in the last bit of the exponent's argument.
+__device__ __forceinline__ float logistic_scaled(float a, float scale) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * (scale * -1.44269504f)));
+}
+
+// An LDS address the compiler cannot relate to others.  Reads off one base
+// pair into ds_read2 instructions with 8-bit dword offsets; for rows past
+// that reach the compiler otherwise derives a new base register for every
+// pair.  A second base made opaque here keeps those rows on one register.
+typedef __attribute__((address_space(3))) float* lds_fptr;
+__device__ __forceinline__ lds_fptr lds_opaque(lds_fptr p) {
+    asm("" : "+v"(p));
+    return p;
+}
 
 // Block order for 8 XCDs.  The hardware deals consecutive block ids to the
 // XCDs round-robin; this maps a block id to a logical tile id so that each
