@@ -79,6 +79,12 @@ SHAPES = [
     (1, 2, 11, 13, 4, 3, 2),        # K3/s2: 9x11 -> 4x5 / 5x6
     (2, 6, 37, 70, 20, 3, 2),       # K3/s2: 35x68 -> 17x34 / 18x34, 3 tile columns
     (1, 5, 40, 50, 20, 3, 3),       # K3/s3: 38x48 -> 12x16 / 13x16
+    # one channel quad (weights resident), two (resident) and more (streamed)
+    # for every matrix-core instance
+    (1, 7, 30, 40, 20, 5, 3),       # K5/s3, 2 quads: 26x36 -> 8x12 / 9x12
+    (1, 10, 21, 75, 24, 3, 2),      # K3/s2, 3 quads: 19x73 -> 9x36 / 10x37, 2 tile columns
+    (2, 13, 29, 44, 18, 3, 3),      # K3/s3, 4 quads: 27x42 -> 9x14 (ceil = floor)
+    (1, 3, 25, 47, 8, 3, 3),        # K3/s3, 1 quad: 23x45 -> 7x15 / 8x15
     (1, 4, 12, 12, 6, 1, 5),        # K = 1, s = 5: one-thread-per-output kernel only
 ]
 
