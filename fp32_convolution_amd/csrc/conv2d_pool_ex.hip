@@ -254,9 +254,10 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     constexpr int RG = (255 - (NCB - 1) * CPB - (K - 1)) / RP + 1;
     static_assert(RG >= 1 && NR <= 2 * RG, "two base registers reach every row");
     const lds_fptr lbase = (lds_fptr)lds + g * CINQ * plane + l16;
-    auto load_row = [&](float (&bv)[NCB][K], lds_fptr row) {
+    // NBA (a compile-time tag): the column blocks the tile computes.
+    auto load_row = [&](float (&bv)[NCB][K], lds_fptr row, auto nba) {
 #pragma unroll
-        for (int nb = 0; nb < NCB; ++nb)
+        for (int nb = 0; nb < decltype(nba)::value; ++nb)
 #pragma unroll
             for (int kx = 0; kx < K; ++kx) bv[nb][kx] = row[nb * CPB + kx];
     };
@@ -271,16 +272,17 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     // at S * bias.
     if constexpr (FOLD) bco = bco * (float)S;
     floatx4 acc[NCB][NACC];
-    auto mma_quad = [&](const float (&aq)[K][K], int q, int pr, auto first_tag) {
+    auto mma_quad = [&](const float (&aq)[K][K], int q, int pr, auto first_tag, auto nba) {
         constexpr bool FIRST = decltype(first_tag)::value;
+        constexpr int NBA = decltype(nba)::value;
         const lds_fptr p0 = lbase + q * plane + pr * S * RP;
         const lds_fptr p1 = NR > RG ? lds_opaque(p0 + RG * RP) : p0;
         auto row = [&](int rr) { return rr < RG ? p0 + rr * RP : p1 + (rr - RG) * RP; };
         float bcur[NCB][K], bnxt[NCB][K];
-        load_row(bcur, row(0));
+        load_row(bcur, row(0), nba);
 #pragma unroll
         for (int rr = 0; rr < NR; ++rr) {
-            if (rr + 1 < NR) load_row(bnxt, row(rr + 1));
+            if (rr + 1 < NR) load_row(bnxt, row(rr + 1), nba);
 #pragma unroll
             for (int ky = 0; ky < K; ++ky) {
                 const int dy = rr - ky;
@@ -288,14 +290,14 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
 #pragma unroll
                 for (int kx = 0; kx < K; ++kx)
 #pragma unroll
-                    for (int nb = 0; nb < NCB; ++nb)
+                    for (int nb = 0; nb < NBA; ++nb)
                         acc[nb][FOLD ? 0 : dy] = mfma_16x16x4(
                             aq[ky][kx], bcur[nb][kx],
                             (FIRST && ky == 0 && kx == 0 && (!FOLD || dy == 0)) ? bco : acc[nb][FOLD ? 0 : dy]);
             }
             if (rr + 1 < NR) {
 #pragma unroll
-                for (int nb = 0; nb < NCB; ++nb)
+                for (int nb = 0; nb < NBA; ++nb)
 #pragma unroll
                     for (int kx = 0; kx < K; ++kx) bcur[nb][kx] = bnxt[nb][kx];
             }
@@ -303,9 +305,9 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     };
     // Streaming weights: the next quad's (quad 0 again after the last: the
     // next pooled row starts there) load under this quad's MFMAs.
-    auto quad_stream = [&](int q, int pr, auto first_tag) {
+    auto quad_stream = [&](int q, int pr, auto first_tag, auto nba) {
         load_a(a[1], q + 1 < CINQ ? q + 1 : 0);
-        mma_quad(a[0], q, pr, first_tag);
+        mma_quad(a[0], q, pr, first_tag, nba);
 #pragma unroll
         for (int ky = 0; ky < K; ++ky)
 #pragma unroll
@@ -315,11 +317,11 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     float lsum = 0.f;
     // FULL: every column of the tile and every channel of the wave lies
     // inside the pooled map, so no lane needs a range check.
-    auto pool_row = [&](const floatx4 (&ac)[NCB][NACC], int ph, int yr, auto edge_tag, auto full_tag) {
+    auto pool_row = [&](const floatx4 (&ac)[NCB][NACC], int ph, int yr, auto edge_tag, auto full_tag, auto nba) {
         constexpr bool EDGE = decltype(edge_tag)::value, FULL = decltype(full_tag)::value;
         const float fill = POOL_MAX ? -INFINITY : 0.f;
 #pragma unroll
-        for (int nb = 0; nb < NCB; ++nb) {
+        for (int nb = 0; nb < decltype(nba)::value; ++nb) {
             float m[4];
             if constexpr (FOLD) {
 #pragma unroll
@@ -429,13 +431,13 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
 
     const int nrow_tile = min(TPH, PH - ph0);
     const bool full = pw0 + TPW <= PW && co0 + 16 <= Cout;
-    for (int pr = 0; pr < nrow_tile; ++pr) {
+    auto row_pass = [&](int pr, auto nba) {
         if constexpr (NQ > 0) {
-            mma_quad(a[0], 0, pr, std::true_type{});
-            if constexpr (NQ == 2) mma_quad(a[1], 1, pr, std::false_type{});
+            mma_quad(a[0], 0, pr, std::true_type{}, nba);
+            if constexpr (NQ == 2) mma_quad(a[1], 1, pr, std::false_type{}, nba);
         } else {
-            quad_stream(0, pr, std::true_type{});
-            for (int q = 1; q < CINQ; ++q) quad_stream(q, pr, std::false_type{});
+            quad_stream(0, pr, std::true_type{}, nba);
+            for (int q = 1; q < CINQ; ++q) quad_stream(q, pr, std::false_type{}, nba);
         }
 
         // Epilogue of pooled row ph.  Lane (g, l16) holds in acc[nb][dy][r]
@@ -447,11 +449,25 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
         const int ph = ph0 + pr;
         const int yr = y0 + pr * S;
         if (!FOLD && ceil_mode && (yr + S > Hc || x0 + TPW * S > Wc))
-            pool_row(acc, ph, yr, std::true_type{}, std::false_type{});  // (the folded pool has floor mode only)
+            pool_row(acc, ph, yr, std::true_type{}, std::false_type{}, nba);  // (the folded pool has floor mode only)
         else if (full)
-            pool_row(acc, ph, yr, std::false_type{}, std::true_type{});
+            pool_row(acc, ph, yr, std::false_type{}, std::true_type{}, nba);
         else
-            pool_row(acc, ph, yr, std::false_type{}, std::false_type{});
+            pool_row(acc, ph, yr, std::false_type{}, std::false_type{}, nba);
+    };
+    // A tile of two column blocks whose second block lies wholly past the
+    // map (the last tile column when the map's width is not a multiple of
+    // the tile's) computes the first block only.
+    const int nbv = min(NCB, (PW - pw0 + WPB - 1) / WPB);
+    for (int pr = 0; pr < nrow_tile; ++pr) {
+        if constexpr (NCB == 2) {
+            if (nbv == 1)
+                row_pass(pr, std::integral_constant<int, 1>{});
+            else
+                row_pass(pr, std::integral_constant<int, 2>{});
+        } else {
+            row_pass(pr, std::integral_constant<int, NCB>{});
+        }
     }
 
     if constexpr (MODE != OUT_MAP) {
