@@ -631,7 +631,7 @@ struct Box4 {
     static constexpr int CO_RANGE = NW * 16;
 };
 
-template <int MODE, bool VEC>
+template <int MODE, bool VEC, int NQ>
 __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int tiles_w,
@@ -669,14 +669,22 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
                 }
             }
         };
-        // the value of lane + 1 (0 in lane 63)
+        // the value of lane + 1 (wave_shl:1; lane 63, whose value no stored
+        // sum uses, reads 0 through the bound control, so the move needs no
+        // zeroed old value)
         auto next_lane = [](float v) {
-            return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF,
-                                                                         false));
+            return __builtin_bit_cast(float,
+                                      __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x130, 0xF, 0xF, true));
         };
+        // NQ > 0: CINQ == NQ at compile time, so the loop unrolls and each
+        // channel's rows load into registers of their own (a run-time loop
+        // copies the prefetched rows back into the loop's registers: 40
+        // moves per channel)
         floatx4 v[IR];
         load_rows(v, wave);
-        for (int i = 0; i < CINQ; ++i) {
+        const int nq = NQ > 0 ? NQ : CINQ;
+#pragma unroll(NQ > 0 ? NQ : 1)
+        for (int i = 0; i < nq; ++i) {
             const int ic = wave + NW * i;
             float hs[IR][3];
 #pragma unroll
@@ -686,7 +694,7 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
                 hs[r][1] = (v[r][1] + v[r][2]) + (next_lane(v[r][0]) + v[r][3]);
                 hs[r][2] = next_lane(p01) + p23;
             }
-            if (i + 1 < CINQ) load_rows(v, ic + NW);
+            if (i + 1 < nq) load_rows(v, ic + NW);
             float* sp = lds + ((size_t)ic * TPH * TPW + lane) * TP;
 #pragma unroll
             for (int ph = 0; ph < TPH; ++ph) {
@@ -779,6 +787,24 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
                 for (int p = 0; p < NB; ++p)
                     lsum += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(acc[p][r], inv * kNegLog2e, c0)));
             }
+        } else if (co_w + 16 <= Cout) {
+            // a tile at the bottom or right edge: every channel of the wave is
+            // in range, so one select per position block adds the block's
+            // four sums or nothing (positions past the map hold finite values
+            // of the zero-padded or dropped input, but a select keeps a
+            // non-finite one out of the sum too)
+            bool colok[3];
+#pragma unroll
+            for (int c = 0; c < 3; ++c) colok[c] = pw0 + c * 16 + l16 < PW;
+#pragma unroll
+            for (int p = 0; p < NB; ++p) {
+                float sp = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sp += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(
+                                                           __builtin_fmaf(acc[p][r], inv * kNegLog2e, bco[r] * kNegLog2e)));
+                lsum += (ph0 + p / 3 < PH && colok[p % 3]) ? sp : 0.f;
+            }
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -825,10 +851,10 @@ static bool box4_fits(const Conv2dShape& s) {
     return s.K == 3 && s.S == 4 && s.W % 4 == 0 && box4_lds_bytes(s.Cin) <= kMaxLds;
 }
 
-template <bool VEC>
+template <bool VEC, int NQ>
 struct Box4Launch {
     template <int MODE>
-    static constexpr auto kernel = conv2d_pool_boxsum4_kernel<MODE, VEC>;
+    static constexpr auto kernel = conv2d_pool_boxsum4_kernel<MODE, VEC, NQ>;
 };
 
 static int64_t box4_parts(const Conv2dShape& s) {
@@ -836,8 +862,9 @@ static int64_t box4_parts(const Conv2dShape& s) {
     return (int64_t)tiles * ((s.Cout + Box4::CO_RANGE - 1) / Box4::CO_RANGE);
 }
 
-static hipError_t launch_box4(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
-                              int mode, hipStream_t stream) {
+template <bool VEC, int NQ>
+static hipError_t launch_box4_q(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                                int mode, hipStream_t stream) {
     const int CINQ = (s.Cin + 3) / 4;
     const size_t lds = box4_lds_bytes(s.Cin);
     const int tiles_w = (s.PW + Box4::TPW - 1) / Box4::TPW;
@@ -846,13 +873,25 @@ static hipError_t launch_box4(const Conv2dShape& s, const float* x, const float*
     const long nblocks_l = (long)tiles * co_ranges * s.B;
     if (nblocks_l > INT32_MAX) return hipErrorInvalidValue;
     const int nblocks = (int)nblocks_l;
-    if ((uintptr_t)x % 16 == 0) {
-        FCONV_LAUNCH_MODES(Box4Launch<true>::template kernel, dim3(nblocks), dim3(Box4::NT), lds, stream, x, w, bias,
-                           dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
-    } else {
-        FCONV_LAUNCH_MODES(Box4Launch<false>::template kernel, dim3(nblocks), dim3(Box4::NT), lds, stream, x, w,
-                           bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
-    }
+    using L = Box4Launch<VEC, NQ>;
+    FCONV_LAUNCH_MODES(L::template kernel, dim3(nblocks), dim3(Box4::NT), lds, stream, x, w, bias, dst, s.Cin, s.H,
+                       s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
+}
+
+// One or two channels per wave at compile time, more at run time.
+template <bool VEC>
+static hipError_t launch_box4_v(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                                int mode, hipStream_t stream) {
+    const int CINQ = (s.Cin + 3) / 4;
+    if (CINQ == 1) return launch_box4_q<VEC, 1>(s, x, w, bias, dst, mode, stream);
+    if (CINQ == 2) return launch_box4_q<VEC, 2>(s, x, w, bias, dst, mode, stream);
+    return launch_box4_q<VEC, 0>(s, x, w, bias, dst, mode, stream);
+}
+
+static hipError_t launch_box4(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                              int mode, hipStream_t stream) {
+    if ((uintptr_t)x % 16 == 0) return launch_box4_v<true>(s, x, w, bias, dst, mode, stream);
+    return launch_box4_v<false>(s, x, w, bias, dst, mode, stream);
 }
 
 // Instances: K3/s4 4x16 tile with 4 waves x 16 channels; K5/s3 4x12 tile
