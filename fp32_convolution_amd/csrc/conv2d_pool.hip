@@ -609,13 +609,15 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
 //     Sx[ic][ky][kx] at (4ph + ky, 4pw + kx), ky, kx < 3.
 // Lane l owns pooled column pw0 + l.  One 16-byte load gives it input
 // columns 4pw .. 4pw+3 of a row; the next two columns are the next lane's
-// first two, read through DPP wave_shl:1 inside the adds (lane TPW only
-// supplies them).  Per input row, 7 adds give the three horizontal 4-sums:
-//     h0 = (x0+x1) + (x2+x3),  h1 = (x1+x2) + (x3+n0),  h2 = (x2+x3) + (n0+n1);
-// per pooled row, 7-8 adds per kx give the three vertical 4-sums, pairwise
-// too.  The 9 values go to LDS as Sx[ic][ph][pw][12] (taps 0..8, 16-byte
-// aligned rows), which the contraction reads as B operands: three LDS
-// reads per 9 MFMA steps.  Compared with the general box-sum kernel this
+// first two, read through DPP wave_shl:1 (lane TPW only supplies them).
+// The vertical 4-sums come first, per column: 9 sums of adjacent rows, then
+// each window of rows 4ph+ky .. +3 as two of them (15 adds per column for
+// both pooled rows).  Then per (ph, ky) 7 adds give the horizontal 4-sums:
+//     h0 = (u0+u1) + (u2+u3),  h1 = (u1+u2) + (u3+n0),  h2 = (u2+u3) + (n0+n1).
+// That is 114 adds and 12 lane moves per channel; summing each row across
+// first took 138 and 20.  The 9 values go to LDS as Sx[ic][ph][pw][12]
+// (taps 0..8, 16-byte aligned rows), which the contraction reads as B
+// operands: three LDS reads per 9 MFMA steps.  Compared with the general box-sum kernel this
 // computes only the box sums the pooled outputs use (9 of every 16) and
 // issues about half the vector instructions per output.
 // Workgroup: one batch item, TPH = 2 pooled rows x TPW = 48 pooled columns,
@@ -686,26 +688,33 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
 #pragma unroll(NQ > 0 ? NQ : 1)
         for (int i = 0; i < nq; ++i) {
             const int ic = wave + NW * i;
-            float hs[IR][3];
+            // vertical 4-sums first: column c of the lane's four, window rows
+            // 4ph+ky .. 4ph+ky+3 = pair (4ph+ky, +1) + pair (4ph+ky+2, +3)
+            float vs[TPH][3][4];
 #pragma unroll
-            for (int r = 0; r < IR; ++r) {
-                const float p01 = v[r][0] + v[r][1], p23 = v[r][2] + v[r][3];
-                hs[r][0] = p01 + p23;
-                hs[r][1] = (v[r][1] + v[r][2]) + (next_lane(v[r][0]) + v[r][3]);
-                hs[r][2] = next_lane(p01) + p23;
+            for (int c = 0; c < 4; ++c) {
+                float a[IR - 1];
+#pragma unroll
+                for (int r = 0; r + 1 < IR; ++r) a[r] = v[r][c] + v[r + 1][c];
+#pragma unroll
+                for (int ph = 0; ph < TPH; ++ph)
+#pragma unroll
+                    for (int ky = 0; ky < 3; ++ky) vs[ph][ky][c] = a[ph * S + ky] + a[ph * S + ky + 2];
             }
             if (i + 1 < nq) load_rows(v, ic + NW);
             float* sp = lds + ((size_t)ic * TPH * TPW + lane) * TP;
 #pragma unroll
             for (int ph = 0; ph < TPH; ++ph) {
-                const int R = ph * S;
+                // then the horizontal 4-sums at kx = 0, 1, 2 (columns 4 and 5
+                // are the next lane's 0 and 1)
                 float sx[9];
 #pragma unroll
-                for (int kx = 0; kx < 3; ++kx) {
-                    const float q23 = hs[R + 2][kx] + hs[R + 3][kx];
-                    sx[kx] = (hs[R][kx] + hs[R + 1][kx]) + q23;
-                    sx[3 + kx] = (hs[R + 1][kx] + hs[R + 2][kx]) + (hs[R + 3][kx] + hs[R + 4][kx]);
-                    sx[6 + kx] = q23 + (hs[R + 4][kx] + hs[R + 5][kx]);
+                for (int ky = 0; ky < 3; ++ky) {
+                    const float* u = vs[ph][ky];
+                    const float p01 = u[0] + u[1], p23 = u[2] + u[3];
+                    sx[3 * ky] = p01 + p23;
+                    sx[3 * ky + 1] = (u[1] + u[2]) + (next_lane(u[0]) + u[3]);
+                    sx[3 * ky + 2] = next_lane(p01) + p23;
                 }
                 if (lane < TPW) {
                     float* q = sp + (size_t)ph * TPW * TP;
