@@ -615,9 +615,13 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
 // both pooled rows).  Then per (ph, ky) 7 adds give the horizontal 4-sums:
 //     h0 = (u0+u1) + (u2+u3),  h1 = (u1+u2) + (u3+n0),  h2 = (u2+u3) + (n0+n1).
 // That is 114 adds and 12 lane moves per channel; summing each row across
-// first took 138 and 20.  The 9 values go to LDS as Sx[ic][ph][pw][12]
-// (taps 0..8, 16-byte aligned rows), which the contraction reads as B
-// operands: three LDS reads per 9 MFMA steps.  Compared with the general box-sum kernel this
+// first took 138 and 20.  The 9 values go to LDS tap-major, Sx[ic][ph][tap][pw]
+// (consecutive lanes write and read consecutive words), which the
+// contraction reads as B operands, one word per MFMA step.  Each channel's
+// plane is padded by 16 words so that the four lane groups, which read four
+// channels, start 16 banks apart.  Unpadded it is 28 KB per workgroup, and 5
+// workgroups fit a CU; a position-major [pw][12] layout (three 16-byte reads
+// per 9 steps) took 37 KB, 4 per CU, and ran 2 % slower.  Compared with the general box-sum kernel this
 // computes only the box sums the pooled outputs use (9 of every 16) and
 // issues about half the vector instructions per output.
 // Workgroup: one batch item, TPH = 2 pooled rows x TPW = 48 pooled columns,
@@ -628,9 +632,12 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
 // of the row); VEC selects 16-byte loads (x 16-byte aligned) or four 4-byte
 // loads.
 struct Box4 {
-    static constexpr int K = 3, S = 4, TPH = 2, TPW = 48, NW = 4, NT = 256, TP = 12;
+    static constexpr int K = 3, S = 4, TPH = 2, TPW = 48, NW = 4, NT = 256;
     static constexpr int IR = TPH * S + K - 1;  // input rows a tile reads: 10
     static constexpr int CO_RANGE = NW * 16;
+    // tap-major layout: a channel's [TPH][9][TPW] values plus 16 floats, so
+    // that the four lane groups' channels start 16 banks apart
+    static constexpr int CPLANE = TPH * 9 * TPW + 16;
 };
 
 template <int MODE, bool VEC, int NQ>
@@ -638,8 +645,8 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int tiles_w,
     int tiles_per_item, int co_ranges, int nblocks) {
-    constexpr int S = Box4::S, TPH = Box4::TPH, TPW = Box4::TPW, NW = Box4::NW, TP = Box4::TP, IR = Box4::IR;
-    extern __shared__ float lds[];  // Sx [4*CINQ][TPH][TPW][TP]
+    constexpr int S = Box4::S, TPH = Box4::TPH, TPW = Box4::TPW, NW = Box4::NW, IR = Box4::IR;
+    extern __shared__ float lds[];  // Sx [4*CINQ][CPLANE]: [TPH][9][TPW] + 16 per channel
     __shared__ float red[NW];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -702,7 +709,7 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
                     for (int ky = 0; ky < 3; ++ky) vs[ph][ky][c] = a[ph * S + ky] + a[ph * S + ky + 2];
             }
             if (i + 1 < nq) load_rows(v, ic + NW);
-            float* sp = lds + ((size_t)ic * TPH * TPW + lane) * TP;
+            float* sp = lds + (size_t)ic * Box4::CPLANE + lane;
 #pragma unroll
             for (int ph = 0; ph < TPH; ++ph) {
                 // then the horizontal 4-sums at kx = 0, 1, 2 (columns 4 and 5
@@ -717,10 +724,9 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
                     sx[3 * ky + 2] = next_lane(p01) + p23;
                 }
                 if (lane < TPW) {
-                    float* q = sp + (size_t)ph * TPW * TP;
-                    *reinterpret_cast<floatx4*>(q) = floatx4{sx[0], sx[1], sx[2], sx[3]};
-                    *reinterpret_cast<floatx4*>(q + 4) = floatx4{sx[4], sx[5], sx[6], sx[7]};
-                    q[8] = sx[8];
+                    float* q = sp + ph * 9 * TPW;
+#pragma unroll
+                    for (int k = 0; k < 9; ++k) q[k * TPW] = sx[k];
                 }
             }
         }
@@ -754,14 +760,13 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
     constexpr int NB = TPH * TPW / 16;
     floatx4 acc[NB];
     auto quad = [&](const float (&a)[9], int m, bool first) {
-        const float* cb = lds + (size_t)(4 * m + g) * TPH * TPW * TP;
+        const float* cb = lds + (size_t)(4 * m + g) * Box4::CPLANE;
 #pragma unroll
         for (int p = 0; p < NB; ++p) {
-            const float* q = cb + ((p / 3) * TPW + (p % 3) * 16 + l16) * TP;
-            const floatx4 t0 = *reinterpret_cast<const floatx4*>(q);
-            const floatx4 t1 = *reinterpret_cast<const floatx4*>(q + 4);
-            const float t8 = q[8];
-            const float t[9] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3], t8};
+            const float* q = cb + (p / 3) * 9 * TPW + (p % 3) * 16 + l16;
+            float t[9];
+#pragma unroll
+            for (int k = 0; k < 9; ++k) t[k] = q[k * TPW];
             acc[p] = mfma_16x16x4(a[0], t[0], first ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[p]);
 #pragma unroll
             for (int k = 1; k < 9; ++k) acc[p] = mfma_16x16x4(a[k], t[k], acc[p]);
@@ -850,7 +855,7 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
 }
 
 static size_t box4_lds_bytes(int Cin) {
-    return (size_t)4 * ((Cin + 3) / 4) * Box4::TPH * Box4::TPW * Box4::TP * sizeof(float);
+    return (size_t)4 * ((Cin + 3) / 4) * Box4::CPLANE * sizeof(float);
 }
 
 // The K = 3, s = 4 shapes the one-column-per-lane kernel takes (by shape
