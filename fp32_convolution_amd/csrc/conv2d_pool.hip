@@ -619,11 +619,12 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
 // (consecutive lanes write and read consecutive words), which the
 // contraction reads as B operands, one word per MFMA step.  Each channel's
 // plane is padded by 16 words so that the four lane groups, which read four
-// channels, start 16 banks apart.  Unpadded it is 28 KB per workgroup, and 5
-// workgroups fit a CU; a position-major [pw][12] layout (three 16-byte reads
-// per 9 steps) took 37 KB, 4 per CU, and ran 2 % slower.  Compared with the general box-sum kernel this
-// computes only the box sums the pooled outputs use (9 of every 16) and
-// issues about half the vector instructions per output.
+// channels, start 16 banks apart.  For Cin = 8 that is 28 KB per workgroup,
+// and 5 workgroups fit a CU; a position-major [pw][12] layout (three 16-byte
+// reads per 9 steps) took 37 KB, 4 per CU, and ran 2 % slower.  Compared
+// with the general box-sum kernel this computes only the box sums the pooled
+// outputs use (9 of every 16) and issues about half the vector instructions
+// per output.
 // Workgroup: one batch item, TPH = 2 pooled rows x TPW = 48 pooled columns,
 // 64 output channels (4 waves x 16).  Wave w makes the box sums of channels
 // w, w+4, ...; k-slot g of contraction step (m, tap) is channel 4m + g at
