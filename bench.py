@@ -410,6 +410,11 @@ def main():
     ms_tmx = time_calls(lambda: fc.conv2d_pool_sigmoid_sum(xt, wt, bt, tc["pool"], out=out_tmx,
                                                            algo=fc.ALGO_DIRECT_MFMA, pool_mode=fc.POOL_MAX,
                                                            relu=True))
+    # The K = 5, s = 3 workload's default algorithm: box-sum (the general
+    # box-sum kernel), 400 MACs per (co, pooled output) instead of 3600.
+    out_tbox = torch.empty(tc["B"], device=dev)
+    ms_tbox = time_calls(lambda: fc.conv2d_pool_sigmoid_sum(xt, wt, bt, tc["pool"], out=out_tbox,
+                                                            algo=fc.ALGO_BOXSUM))
     del xt
     y_dense = torch.empty_like(y)
     ms_dense = time_calls(lambda: fc.dwsep_conv1d(xd, wdw, wpw, bpw, dc["pad"], out=y_dense, algo=fc.DWSEP_DENSE))
@@ -485,6 +490,16 @@ def main():
     k_tail = kstats(ms_tail, f_tail, conv2d_bytes(tc))
     k_tail["algorithm"] = ("Conv2d k5 -> AvgPool2d 3 -> sigmoid -> sum on x[64,16,257,257] (the K5/s3 workload), "
                            "direct MFMA (pool folded into the contraction)")
+    f_tbox = conv2d_boxsum_flops(tc)
+    k_tbox = kstats(ms_tbox, f_tbox, conv2d_bytes(tc))
+    k_tbox["algorithm"] = ("box-sum (FCONV_ALGO_BOXSUM, the default for this shape) on x[64,16,257,257], "
+                           "own FLOPs Cin*K*K per (co, pooled output)")
+    at = f_tbox / (k_tbox["ms_mean"] * 1e-3) / 1e12
+    k_tbox["roofline"] = {"bound": "mfma", "achieved": round(at, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(at / PEAK_FP32_TFLOPS, 4), "traffic": None}
+    k_tbox["speedup_vs_direct"] = round(float(ms_tail.mean()) / k_tbox["ms_mean"], 2)
+    k_tbox["matches_direct_within_tol"] = bool(
+        ((out_tbox - out_tail).abs() <= 1e-4 + 1e-4 * out_tail.abs()).all().item())
     k_tmx = kstats(ms_tmx, f_tail, conv2d_bytes(tc))
     k_tmx["algorithm"] = ("Conv2d k5 -> ReLU -> MaxPool2d 3 (floor) -> sigmoid -> sum on x[64,16,257,257], "
                           "per-conv-output MFMA kernel (K = 5, s = 3 instance)")
@@ -517,7 +532,8 @@ def main():
         "variants": {"fconv2d_pool_sigmoid_sum_boxsum": k_box, "fconv2d_pool_sigmoid_sum_det": k_det,
                      "fconv2d_pool_sigmoid_sum_ex_relu_maxpool": k_mx,
                      "fconv2d_pool_sigmoid_sum_k5s3": k_tail,
-                     "fconv2d_pool_sigmoid_sum_ex_relu_maxpool_k5s3": k_tmx, "dwsep_conv1d_dense": k_dense},
+                     "fconv2d_pool_sigmoid_sum_ex_relu_maxpool_k5s3": k_tmx,
+                     "fconv2d_pool_sigmoid_sum_boxsum_k5s3": k_tbox, "dwsep_conv1d_dense": k_dense},
         "roofline": {
             "kernel": f"fconv2d_pool_sigmoid_sum, direct MFMA ({ELEM_AVG}) on " + CONV,
             "bound": "mfma",
