@@ -403,8 +403,18 @@ struct BoxLayout {
     static_assert(Cfg::WPOS == 1, "box-sum waves split output channels only");
 };
 
+// Waves per SIMD the register budget must allow.  The K = 5, s = 3 instance
+// (8-wave workgroups, 37 KB of LDS) is held to 80 VGPRs so that 3 workgroups
+// fit a CU instead of 2: 0.398 against 0.434 ms on x[64,16,257,257] (0.412
+// with 73 VGPRs when its weight buffers were copied rather than alternated);
+// at 64 VGPRs (4 workgroups) its spills made it 0.467 ms.
+template <class Cfg>
+constexpr int box_min_waves() {
+    return Cfg::K == 5 && Cfg::S == 3 ? 6 : 1;
+}
+
 template <class Cfg, int MODE>
-__global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
+__global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_boxsum_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int tiles_w,
     int tiles_per_item, int co_ranges, int nblocks) {
@@ -546,9 +556,8 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int p = 0; p < P; ++p) acc[cb][p] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < CINQ; ++q) {
+    auto contract = [&](const float (&a)[K * K][CB], int q) {
         const int lq = q * L::SPLANE;
-        load_a(a_nxt, q + 1);
 #pragma unroll
         for (int ky = 0; ky < K; ++ky)
 #pragma unroll
@@ -559,12 +568,18 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_boxsum_kernel(
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                    for (int p = 0; p < P; ++p) acc[cb][p] = mfma_16x16x4(a_cur[ky * K + kx][cb], bv[p], acc[cb][p]);
+                    for (int p = 0; p < P; ++p) acc[cb][p] = mfma_16x16x4(a[ky * K + kx][cb], bv[p], acc[cb][p]);
             }
-#pragma unroll
-        for (int kk = 0; kk < K * K; ++kk)
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) a_cur[kk][cb] = a_nxt[kk][cb];
+    };
+    // channel groups in pairs, so that the two weight buffers alternate
+    // without copies (one copy per weight and group cost 25 moves per group)
+    for (int q = 0; q < CINQ; q += 2) {
+        load_a(a_nxt, q + 1);
+        contract(a_cur, q);
+        if (q + 1 < CINQ) {
+            load_a(a_cur, q + 2);
+            contract(a_nxt, q + 1);
+        }
     }
 
     // Epilogue (as the direct kernel): window sum / s^2 + bias.
