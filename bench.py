@@ -53,6 +53,8 @@ KERNEL_SOURCES = {
                           "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "conv2d_pool_boxsum4_kernel": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
                                   "fp32_convolution_amd/csrc/fconv_device.hpp"],
+    "conv2d_pool_boxsum_kernel": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
+                                 "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_dense_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                            "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 1, 0, 2>": ["fp32_convolution_amd/csrc/conv2d_pool_ex.hip",
@@ -496,7 +498,8 @@ def main():
                            "own FLOPs Cin*K*K per (co, pooled output)")
     at = f_tbox / (k_tbox["ms_mean"] * 1e-3) / 1e12
     k_tbox["roofline"] = {"bound": "mfma", "achieved": round(at, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(at / PEAK_FP32_TFLOPS, 4), "traffic": None}
+                          "frac": round(at / PEAK_FP32_TFLOPS, 4),
+                          "traffic": measured_traffic("conv2d_pool_boxsum_kernel")}
     k_tbox["speedup_vs_direct"] = round(float(ms_tail.mean()) / k_tbox["ms_mean"], 2)
     k_tbox["matches_direct_within_tol"] = bool(
         ((out_tbox - out_tail).abs() <= 1e-4 + 1e-4 * out_tail.abs()).all().item())
