@@ -66,6 +66,10 @@ SMALL_CONV = [
     (2, 4, 30, 28, 9, 3, 3),        # K3/s3 instance
     (1, 2, 23, 19, 5, 7, 2),        # no MFMA instance (K=7): simple path
     (1, 3, 9, 9, 4, 5, 3),          # PH = PW = 1
+    # box-sum K3/s4 kernel (W % 4 == 0): one, two and streamed channel quads
+    (3, 1, 20, 200, 16, 3, 4),      # Cin 1; a 1-column second tile; 3 of 4 waves' channels past Cout
+    (1, 6, 38, 100, 64, 3, 4),      # Cin 6 (two quads, two zero channels); one partial tile column
+    (2, 12, 45, 52, 40, 3, 4),      # Cin 12 (channel loop at run time); Cout 40; ragged rows
 ]
 
 
