@@ -586,25 +586,42 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
     const float inv = 1.0f / (float)(S * S);
     const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
     float lsum = 0.f;
+    static_assert(P * 16 == TPH * TPW, "every lane of every block holds a tile position");
+    if (MODE != OUT_MAP && co0 + 16 * CB <= Cout && ph0 + TPH <= PH && pw0 + TPW <= PW) {
+        // the whole tile is in range: no per-output tests, and the scale, the
+        // bias and -log2(e) of the sigmoid's argument in one multiply-add
+        constexpr float kNegLog2e = -1.4426950408889634f;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int co = co0 + cb * 16 + 4 * g + r;
-            const bool cok = co < Cout;
+            for (int r = 0; r < 4; ++r) {
+                const float c0 = bco[cb][r] * kNegLog2e;
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int j = p * 16 + l16;
-                const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
-                if (cok && ph < PH && pw < PW) {
-                    const float avg = acc[cb][p][r] * inv + bco[cb][r];
-                    if constexpr (MODE == OUT_MAP)
-                        dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
-                    else
-                        lsum += logistic(avg);
+                for (int p = 0; p < P; ++p)
+                    lsum += __builtin_amdgcn_rcpf(
+                        1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(acc[cb][p][r], inv * kNegLog2e, c0)));
+            }
+    } else {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = co0 + cb * 16 + 4 * g + r;
+                const bool cok = co < Cout;
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    const int j = p * 16 + l16;
+                    const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
+                    if (cok && ph < PH && pw < PW) {
+                        const float avg = acc[cb][p][r] * inv + bco[cb][r];
+                        if constexpr (MODE == OUT_MAP)
+                            dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
+                        else
+                            lsum += logistic(avg);
+                    }
                 }
             }
-        }
+    }
     if constexpr (MODE != OUT_MAP) {
         const float s = block_sum<NW>(lsum, red);
         if (tid == 0) {
