@@ -725,7 +725,8 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
         floatx4 v[IR];
         load_rows(v, wave);
         const int nq = NQ > 0 ? NQ : CINQ;
-#pragma unroll(NQ > 0 ? NQ : 1)
+        constexpr int kUnroll = NQ > 0 ? NQ : 1;
+#pragma unroll kUnroll
         for (int i = 0; i < nq; ++i) {
             const int ic = wave + NW * i;
             // vertical 4-sums first: column c of the lane's four, window rows
