@@ -58,11 +58,11 @@ struct DirectCfg {
     static_assert(TPH * TPW == 16 * P * WPOS, "tile must hold the waves' position blocks");
 };
 
-template <class Cfg, int MODE>
+template <class Cfg, int MODE, bool WALK>
 __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane,
-    int tiles_w) {
+    int tiles_w, int tiles, int units, int parts) {
     constexpr int K = Cfg::K, S = Cfg::S, CB = Cfg::CB, P = Cfg::P, WCO = Cfg::WCO;
     constexpr int TPH = Cfg::TPH, TPW = Cfg::TPW, IH = Cfg::IH, IW = Cfg::IW;
     constexpr int QP = Cfg::QP, RP = Cfg::RP, NBV = Cfg::NBV;
@@ -76,185 +76,196 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
     const int wave = tid >> 6;
     const int wco = wave % WCO;
     const int wpos = wave / WCO;
-    const int tile_y = blockIdx.x / tiles_w;
-    const int tile_x = blockIdx.x - tile_y * tiles_w;
-    const int b = blockIdx.z;
-    const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
     const int g = lane >> 4;   // k-slot of the MFMA: channel group
     const int l16 = lane & 15; // row of A / column of B
-    const int co0 = blockIdx.y * Cfg::CO_RANGE + wco * 16 * CB;
+    // Workgroup `part` of batch item b walks units part, part + parts, ...
+    // of the item (unit = channel range * tiles + tile), so that a fused sum
+    // adds at most `parts` partials into out[b].
+    const int b = blockIdx.x / parts;
+    const int part = blockIdx.x - b * parts;
+    walk_sum_t<WALK> dsum = 0;  // this lane's sigmoids over all its units
+    for (int u = part;; u += parts) {
+        if (WALK && u != part) __syncthreads();  // every wave is done with the last unit's tile
+        const int cr = u / tiles, tile = u - (u / tiles) * tiles;
+        const int tile_y = tile / tiles_w;
+        const int tile_x = tile - tile_y * tiles_w;
+        const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
+        const int co0 = cr * Cfg::CO_RANGE + wco * 16 * CB;
 
-    const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
+        const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
 
-    // Weights of channel quad q for this lane: a[ky][cb][kx] =
-    // w[co0 + cb*16 + l16, g*CINQ + q, ky, kx], 0 where co or ic is out of range.
-    auto load_a = [&](float (&a)[K][CB][K], int q) {
-        const int ic = g * CINQ + q;
+        // Weights of channel quad q for this lane: a[ky][cb][kx] =
+        // w[co0 + cb*16 + l16, g*CINQ + q, ky, kx], 0 where co or ic is out of range.
+        auto load_a = [&](float (&a)[K][CB][K], int q) {
+            const int ic = g * CINQ + q;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int co = co0 + cb * 16 + l16;
-            const bool ok = (co < Cout) && (ic < Cin) && (q < CINQ);
-            const int base = ok ? (co * Cin + ic) * (K * K * 4) : kBufOOB;
+            for (int cb = 0; cb < CB; ++cb) {
+                const int co = co0 + cb * 16 + l16;
+                const bool ok = (co < Cout) && (ic < Cin) && (q < CINQ);
+                const int base = ok ? (co * Cin + ic) * (K * K * 4) : kBufOOB;
+#pragma unroll
+                for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+                    for (int kx = 0; kx < K; ++kx) a[ky][cb][kx] = buf_load_f32(rw, base + (ky * K + kx) * 4);
+            }
+        };
+        float a_cur[K][CB][K], a_nxt[K][CB][K];
+        load_a(a_cur, 0);  // in flight while the tile is staged
+
+        // Biases of this lane's output channels co0 + cb*16 + 4g + r (0 where
+        // co >= Cout or bias is NULL: the resource is then empty).
+        const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
+        float bco[CB][4];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = co0 + cb * 16 + 4 * g + r;
+                bco[cb][r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
+            }
+
+        // Stage the input tile: channel ic at ic*plane, row r at r*RP, column c at
+        // phase (c % S)*QP + slot c/S.  Each wave copies whole rows: the row's
+        // address and bounds live in a buffer resource built in scalar registers
+        // (empty for rows outside the image and channels >= Cin, so they load
+        // as 0), and each lane's column offset is fixed for the whole tile, so a
+        // row costs its loads, one address add and its LDS writes.
+        {
+            constexpr int NCH = (IW + 63) / 64;  // 64-column chunks per row
+            constexpr int UR = 4;                // rows in flight per wave
+            int voff[NCH], loff[NCH];
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                const int c = lane + 64 * k;
+                voff[k] = (c < IW && x0 + c < W) ? (x0 + c) * 4 : kBufOOB;
+                loff[k] = (c < IW) ? (c % S) * QP + c / S : -1;
+            }
+            const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+            const int nrows = 4 * CINQ * IH;
+            const float* xb = x + (size_t)b * Cin * H * W;
+            for (int row0 = wave_s; row0 < nrows; row0 += Cfg::NW * UR) {
+                float v[UR][NCH];
+#pragma unroll
+                for (int u = 0; u < UR; ++u) {
+                    const int row = row0 + u * Cfg::NW;
+                    const int ic = row / IH, r = row - (row / IH) * IH;
+                    const bool ok = (row < nrows) && (ic < Cin) && (y0 + r < H);
+                    const buf_rsrc rrow = make_rsrc(xb + (ok ? (ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
+#pragma unroll
+                    for (int k = 0; k < NCH; ++k) v[u][k] = buf_load_f32(rrow, voff[k]);
+                }
+#pragma unroll
+                for (int u = 0; u < UR; ++u) {
+                    const int row = row0 + u * Cfg::NW;
+                    if (row < nrows) {
+                        const int ic = row / IH, r = row - (row / IH) * IH;
+                        float* lrow = lds + ic * plane + r * RP;
+#pragma unroll
+                        for (int k = 0; k < NCH; ++k)
+                            if (loff[k] >= 0) lrow[loff[k]] = v[u][k];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        int pbase[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int j = (wpos * P + p) * 16 + l16;
+            const int py = j / TPW, px = j - (j / TPW) * TPW;
+            pbase[p] = g * CINQ * plane + py * S * RP + px;
+        }
+
+        floatx4 acc[CB][P];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int p = 0; p < P; ++p) acc[cb][p] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+        // Input row rr of a window (0 <= rr < S+K-1) is shared by every (ky, dy)
+        // with ky + dy = rr: it is read from LDS once and multiplied by each of
+        // those weight rows.  The next row (and the next quad's weights) load
+        // while the current row's matrix instructions run.
+        auto load_row = [&](float (&bv)[P][NBV], int lq, int rr) {
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int cc = 0; cc < NBV; ++cc) bv[p][cc] = lds[pbase[p] + lq + rr * RP + (cc % S) * QP + cc / S];
+        };
+
+        for (int q = 0; q < CINQ; ++q) {
+            const int lq = q * plane;
+            load_a(a_nxt, q + 1);  // zeros past the last quad
+            float bcur[P][NBV], bnxt[P][NBV];
+            load_row(bcur, lq, 0);
+#pragma unroll
+            for (int rr = 0; rr < NR; ++rr) {
+                if (rr + 1 < NR) load_row(bnxt, lq, rr + 1);
+#pragma unroll
+                for (int ky = 0; ky < K; ++ky) {
+                    const int dy = rr - ky;
+                    if (dy < 0 || dy >= S) continue;
+#pragma unroll
+                    for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+                        for (int dx = 0; dx < S; ++dx)
+#pragma unroll
+                            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                                for (int p = 0; p < P; ++p)
+                                    acc[cb][p] = mfma_16x16x4(a_cur[ky][cb][kx], bcur[p][dx + kx], acc[cb][p]);
+                }
+                if (rr + 1 < NR) {
+#pragma unroll
+                    for (int p = 0; p < P; ++p)
+#pragma unroll
+                        for (int cc = 0; cc < NBV; ++cc) bcur[p][cc] = bnxt[p][cc];
+                }
+            }
 #pragma unroll
             for (int ky = 0; ky < K; ++ky)
 #pragma unroll
-                for (int kx = 0; kx < K; ++kx) a[ky][cb][kx] = buf_load_f32(rw, base + (ky * K + kx) * 4);
-        }
-    };
-    float a_cur[K][CB][K], a_nxt[K][CB][K];
-    load_a(a_cur, 0);  // in flight while the tile is staged
-
-    // Biases of this lane's output channels co0 + cb*16 + 4g + r (0 where
-    // co >= Cout or bias is NULL: the resource is then empty).
-    const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
-    float bco[CB][4];
+                for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int co = co0 + cb * 16 + 4 * g + r;
-            bco[cb][r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
+                    for (int kx = 0; kx < K; ++kx) a_cur[ky][cb][kx] = a_nxt[ky][cb][kx];
         }
 
-    // Stage the input tile: channel ic at ic*plane, row r at r*RP, column c at
-    // phase (c % S)*QP + slot c/S.  Each wave copies whole rows: the row's
-    // address and bounds live in a buffer resource built in scalar registers
-    // (empty for rows outside the image and channels >= Cin, so they load
-    // as 0), and each lane's column offset is fixed for the whole tile, so a
-    // row costs its loads, one address add and its LDS writes.
-    {
-        constexpr int NCH = (IW + 63) / 64;  // 64-column chunks per row
-        constexpr int UR = 4;                // rows in flight per wave
-        int voff[NCH], loff[NCH];
+        // Epilogue.  Lane (g, l16) holds, for block (cb, p) and r = 0..3, the
+        // window sum of output channel co0 + cb*16 + 4g + r at pooled position
+        // j = (wpos*P + p)*16 + l16 of the tile.
+        const float inv = 1.0f / (float)(S * S);
+        const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
+        float lsum = 0.f;
 #pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int c = lane + 64 * k;
-            voff[k] = (c < IW && x0 + c < W) ? (x0 + c) * 4 : kBufOOB;
-            loff[k] = (c < IW) ? (c % S) * QP + c / S : -1;
-        }
-        const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-        const int nrows = 4 * CINQ * IH;
-        const float* xb = x + (size_t)b * Cin * H * W;
-        for (int row0 = wave_s; row0 < nrows; row0 += Cfg::NW * UR) {
-            float v[UR][NCH];
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int row = row0 + u * Cfg::NW;
-                const int ic = row / IH, r = row - (row / IH) * IH;
-                const bool ok = (row < nrows) && (ic < Cin) && (y0 + r < H);
-                const buf_rsrc rrow = make_rsrc(xb + (ok ? (ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
+            for (int r = 0; r < 4; ++r) {
+                const int co = co0 + cb * 16 + 4 * g + r;
+                const bool cok = co < Cout;
 #pragma unroll
-                for (int k = 0; k < NCH; ++k) v[u][k] = buf_load_f32(rrow, voff[k]);
-            }
-#pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int row = row0 + u * Cfg::NW;
-                if (row < nrows) {
-                    const int ic = row / IH, r = row - (row / IH) * IH;
-                    float* lrow = lds + ic * plane + r * RP;
-#pragma unroll
-                    for (int k = 0; k < NCH; ++k)
-                        if (loff[k] >= 0) lrow[loff[k]] = v[u][k];
+                for (int p = 0; p < P; ++p) {
+                    const int j = (wpos * P + p) * 16 + l16;
+                    const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
+                    if (cok && ph < PH && pw < PW) {
+                        const float avg = acc[cb][p][r] * inv + bco[cb][r];
+                        if constexpr (MODE == OUT_MAP)
+                            dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
+                        else
+                            lsum += logistic(avg);
+                    }
                 }
             }
-        }
-    }
-    __syncthreads();
-
-    int pbase[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int j = (wpos * P + p) * 16 + l16;
-        const int py = j / TPW, px = j - (j / TPW) * TPW;
-        pbase[p] = g * CINQ * plane + py * S * RP + px;
-    }
-
-    floatx4 acc[CB][P];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int p = 0; p < P; ++p) acc[cb][p] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    // Input row rr of a window (0 <= rr < S+K-1) is shared by every (ky, dy)
-    // with ky + dy = rr: it is read from LDS once and multiplied by each of
-    // those weight rows.  The next row (and the next quad's weights) load
-    // while the current row's matrix instructions run.
-    auto load_row = [&](float (&bv)[P][NBV], int lq, int rr) {
-#pragma unroll
-        for (int p = 0; p < P; ++p)
-#pragma unroll
-            for (int cc = 0; cc < NBV; ++cc) bv[p][cc] = lds[pbase[p] + lq + rr * RP + (cc % S) * QP + cc / S];
-    };
-
-    for (int q = 0; q < CINQ; ++q) {
-        const int lq = q * plane;
-        load_a(a_nxt, q + 1);  // zeros past the last quad
-        float bcur[P][NBV], bnxt[P][NBV];
-        load_row(bcur, lq, 0);
-#pragma unroll
-        for (int rr = 0; rr < NR; ++rr) {
-            if (rr + 1 < NR) load_row(bnxt, lq, rr + 1);
-#pragma unroll
-            for (int ky = 0; ky < K; ++ky) {
-                const int dy = rr - ky;
-                if (dy < 0 || dy >= S) continue;
-#pragma unroll
-                for (int kx = 0; kx < K; ++kx)
-#pragma unroll
-                    for (int dx = 0; dx < S; ++dx)
-#pragma unroll
-                        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                            for (int p = 0; p < P; ++p)
-                                acc[cb][p] = mfma_16x16x4(a_cur[ky][cb][kx], bcur[p][dx + kx], acc[cb][p]);
-            }
-            if (rr + 1 < NR) {
-#pragma unroll
-                for (int p = 0; p < P; ++p)
-#pragma unroll
-                    for (int cc = 0; cc < NBV; ++cc) bcur[p][cc] = bnxt[p][cc];
-            }
-        }
-#pragma unroll
-        for (int ky = 0; ky < K; ++ky)
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                for (int kx = 0; kx < K; ++kx) a_cur[ky][cb][kx] = a_nxt[ky][cb][kx];
-    }
-
-    // Epilogue.  Lane (g, l16) holds, for block (cb, p) and r = 0..3, the
-    // window sum of output channel co0 + cb*16 + 4g + r at pooled position
-    // j = (wpos*P + p)*16 + l16 of the tile.
-    const float inv = 1.0f / (float)(S * S);
-    const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
-    float lsum = 0.f;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int co = co0 + cb * 16 + 4 * g + r;
-            const bool cok = co < Cout;
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int j = (wpos * P + p) * 16 + l16;
-                const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
-                if (cok && ph < PH && pw < PW) {
-                    const float avg = acc[cb][p][r] * inv + bco[cb][r];
-                    if constexpr (MODE == OUT_MAP)
-                        dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
-                    else
-                        lsum += logistic(avg);
-                }
-            }
-        }
+        dsum += lsum;
+        if (!WALK || u + parts >= units) break;
+    }  // units
     if constexpr (MODE != OUT_MAP) {
-        const float s = block_sum<Cfg::NW>(lsum, red);
+        const float s = block_sum<Cfg::NW>((float)dsum, red);
         if (tid == 0) {
             if constexpr (MODE == OUT_SUM_ATOMIC)
                 atomicAdd(dst + b, s);
             else
-                dst[(size_t)b * (gridDim.x * gridDim.y) + blockIdx.y * gridDim.x + blockIdx.x] = s;
+                dst[(size_t)b * parts + part] = s;
         }
     }
 }
@@ -322,18 +333,46 @@ bool conv2d_mfma_supported(int Cin, int K, int S) {
         return hipGetLastError();                                                                        \
     } while (0)
 
+// The same for a kernel template KERNEL<MODE, WALK>: the WALK instance (each
+// workgroup walks several units) when there are more units than workgroups.
+#define FCONV_LAUNCH_WALK(KERNEL, WALK, GRID, BLOCK, LDS, STREAM, ...)                                      \
+    do {                                                                                                 \
+        if (WALK) {                                                                                      \
+            FCONV_LAUNCH_MODES(KERNEL##_walk, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                    \
+        } else {                                                                                         \
+            FCONV_LAUNCH_MODES(KERNEL##_once, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                    \
+        }                                                                                                \
+    } while (0)
+
 template <class Cfg>
 struct DirectLaunch {
     template <int MODE>
-    static constexpr auto kernel = conv2d_pool_mfma_kernel<Cfg, MODE>;
+    static constexpr auto kernel_once = conv2d_pool_mfma_kernel<Cfg, MODE, false>;
+    template <int MODE>
+    static constexpr auto kernel_walk = conv2d_pool_mfma_kernel<Cfg, MODE, true>;
 };
 
+// Units of work of one batch item: pooled tiles x output-channel ranges.
+// A tile's pooled count fits int32 and so does the item's pooled map, which
+// holds at least one output per unit.
+struct Walk {
+    int tiles_w, tiles, co_ranges, units, parts;
+};
+
+template <int TPH, int TPW, int CO_RANGE>
+static Walk make_walk(const Conv2dShape& s) {
+    Walk k;
+    k.tiles_w = (s.PW + TPW - 1) / TPW;
+    k.tiles = ((s.PH + TPH - 1) / TPH) * k.tiles_w;
+    k.co_ranges = (s.Cout + CO_RANGE - 1) / CO_RANGE;
+    k.units = k.tiles * k.co_ranges;
+    k.parts = walk_parts(k.units);
+    return k;
+}
+
 template <class Cfg>
-static dim3 direct_grid(const Conv2dShape& s) {
-    const int tiles_h = (s.PH + Cfg::TPH - 1) / Cfg::TPH;
-    const int tiles_w = (s.PW + Cfg::TPW - 1) / Cfg::TPW;
-    const int co_ranges = (s.Cout + Cfg::CO_RANGE - 1) / Cfg::CO_RANGE;
-    return dim3(tiles_h * tiles_w, co_ranges, s.B);
+static Walk direct_walk(const Conv2dShape& s) {
+    return make_walk<Cfg::TPH, Cfg::TPW, Cfg::CO_RANGE>(s);
 }
 
 template <class Cfg>
@@ -342,10 +381,11 @@ static hipError_t launch_direct(const Conv2dShape& s, const float* x, const floa
     const int CINQ = (s.Cin + 3) / 4;
     const int plane = plane_floats<Cfg>(CINQ);
     const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
-    const int tiles_w = (s.PW + Cfg::TPW - 1) / Cfg::TPW;
-    const dim3 grid = direct_grid<Cfg>(s);
-    FCONV_LAUNCH_MODES(DirectLaunch<Cfg>::template kernel, grid, dim3(Cfg::NT), lds, stream, x, w, bias, dst, s.Cin,
-                       s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, tiles_w);
+    const Walk k = direct_walk<Cfg>(s);
+    // at most 65535 * 1024 workgroups
+    const dim3 grid((unsigned)k.parts * (unsigned)s.B);
+    FCONV_LAUNCH_WALK(DirectLaunch<Cfg>::template kernel, k.units > k.parts, grid, dim3(Cfg::NT), lds, stream, x, w, bias, dst, s.Cin,
+                       s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, k.tiles_w, k.tiles, k.units, k.parts);
 }
 
 hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
@@ -358,13 +398,11 @@ hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float*
 }
 
 int64_t conv2d_mfma_parts(const Conv2dShape& s) {
-    dim3 g;
     if (s.K == 3 && s.S == 4) return conv2d_elem_parts(s, PoolOpts{false, false, false});
-    if (s.K == 5 && s.S == 3) g = direct_grid<CfgK5S3>(s);
-    else if (s.K == 3 && s.S == 2) g = direct_grid<CfgK3S2>(s);
-    else if (s.K == 3 && s.S == 3) g = direct_grid<CfgK3S3>(s);
-    else return -1;
-    return (int64_t)g.x * g.y;
+    if (s.K == 5 && s.S == 3) return direct_walk<CfgK5S3>(s).parts;
+    if (s.K == 3 && s.S == 2) return direct_walk<CfgK3S2>(s).parts;
+    if (s.K == 3 && s.S == 3) return direct_walk<CfgK3S3>(s).parts;
+    return -1;
 }
 
 // ---------------------------------------------------------------- box-sum variant
@@ -400,7 +438,10 @@ struct BoxLayout {
     static constexpr int RSS = S * QS;                  // Sx floats per row
     static constexpr int SPLANE = RS * RSS;
     static constexpr int SCRATCH = NCH * 64;            // one vertical-sum row per wave
+    static constexpr int CC = 2 * Cfg::NW;              // channels per LDS chunk: two per wave
+    static constexpr int QC = CC / 4;                   // channel quads per chunk
     static_assert(Cfg::WPOS == 1, "box-sum waves split output channels only");
+    static_assert(QC % 2 == 0, "a chunk's quads run in weight-buffer pairs");
 };
 
 // Waves per SIMD the register budget must allow.  The K = 5, s = 3 instance
@@ -413,66 +454,74 @@ constexpr int box_min_waves() {
     return Cfg::K == 5 && Cfg::S == 3 ? 6 : 1;
 }
 
-template <class Cfg, int MODE>
+template <class Cfg, int MODE, bool WALK>
 __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_boxsum_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int tiles_w,
-    int tiles_per_item, int co_ranges, int nblocks) {
+    int tiles, int units, int parts, int nblocks) {
     using L = BoxLayout<Cfg>;
     constexpr int K = Cfg::K, S = Cfg::S, CB = Cfg::CB, P = Cfg::P, NW = Cfg::NW;
     constexpr int TPH = Cfg::TPH, TPW = Cfg::TPW, IH = Cfg::IH, IW = Cfg::IW;
     constexpr int RS = L::RS, CS = L::CS, QS = L::QS, RSS = L::RSS;
 
+    constexpr int CC = L::CC, QC = L::QC;
     extern __shared__ float lds[];
     __shared__ float red[NW];
-    const int CinP = 4 * CINQ;
-    float* Sb = lds;                                        // [CinP][RS][RSS] phase-split
-    float* scratch = lds + CinP * L::SPLANE;                // [NW][SCRATCH]
+    float* Sb = lds;                                        // [CC][RS][RSS] phase-split
+    float* scratch = lds + CC * L::SPLANE;                  // [NW][SCRATCH]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lid = xcd_spread(blockIdx.x, nblocks);
-    const int tile = lid % tiles_per_item;
-    const int cr = (lid / tiles_per_item) % co_ranges;
-    const int b = lid / (tiles_per_item * co_ranges);
-    const int tile_y = tile / tiles_w, tile_x = tile - (tile / tiles_w) * tiles_w;
-    const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
     const int g = lane >> 4, l16 = lane & 15;
-    const int co0 = cr * Cfg::CO_RANGE + wave * 16 * CB;
+    // Workgroup `part` of batch item b walks units part, part + parts, ...
+    // (unit = channel range * tiles + tile).
+    const int lid = xcd_spread(blockIdx.x, nblocks);
+    const int b = lid / parts;
+    const int part = lid - b * parts;
+    walk_sum_t<WALK> dsum = 0;  // this lane's sigmoids over all its units
+    for (int u = part;; u += parts) {
+        if (WALK && u != part) __syncthreads();  // every wave is done with the last unit's box sums
+        const int cr = u / tiles, tile = u - (u / tiles) * tiles;
+        const int tile_y = tile / tiles_w, tile_x = tile - (tile / tiles_w) * tiles_w;
+        const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
+        const int co0 = cr * Cfg::CO_RANGE + wave * 16 * CB;
 
-    const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
-    auto load_a = [&](float (&a)[K * K][CB], int q) {
-        const int ic = g * CINQ + q;
+        const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
+        // Weights of quad q for lane (g, l16): channel 4q + g (0 past Cin,
+        // Cout and CINQ).
+        auto load_a = [&](float (&a)[K * K][CB], int q) {
+            const int ic = 4 * q + g;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int co = co0 + cb * 16 + l16;
-            const bool ok = (co < Cout) && (ic < Cin) && (q < CINQ);
-            const int base = ok ? (co * Cin + ic) * (K * K * 4) : kBufOOB;
+            for (int cb = 0; cb < CB; ++cb) {
+                const int co = co0 + cb * 16 + l16;
+                const bool ok = (co < Cout) && (ic < Cin) && (q < CINQ);
+                const int base = ok ? (co * Cin + ic) * (K * K * 4) : kBufOOB;
 #pragma unroll
-            for (int kk = 0; kk < K * K; ++kk) a[kk][cb] = buf_load_f32(rw, base + kk * 4);
-        }
-    };
-    float a_cur[K * K][CB], a_nxt[K * K][CB];
-    load_a(a_cur, 0);
-    const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
-    float bco[CB][4];
+                for (int kk = 0; kk < K * K; ++kk) a[kk][cb] = buf_load_f32(rw, base + kk * 4);
+            }
+        };
+        float a_cur[K * K][CB], a_nxt[K * K][CB];
+        load_a(a_cur, 0);
+        const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
+        float bco[CB][4];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int co = co0 + cb * 16 + 4 * g + r;
-            bco[cb][r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
-        }
+            for (int r = 0; r < 4; ++r) {
+                const int co = co0 + cb * 16 + 4 * g + r;
+                bco[cb][r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
+            }
 
-    // 1-2. Box sums, one channel per wave at a time.  All IH rows of the
-    //      channel's tile are loaded into registers (the next channel's rows
-    //      load while this one is summed); s rows are added in registers;
-    //      each vertical-sum row goes through the wave's own LDS scratch row
-    //      and comes back shifted by 0..s-1 columns for the horizontal sum.
-    //      LDS operations of one wave complete in order, so the scratch row
-    //      needs no workgroup barrier, only compiler fences.
-    {
+        // 1-2. Box sums, one channel per wave at a time, CC = 2*NW channels
+        //      (QC quads) per LDS chunk: wave w makes those of the chunk's
+        //      channels w and w + NW.  All IH rows of the channel's tile are
+        //      loaded into registers (the second channel's rows load while the
+        //      first one is summed); s rows are added in registers; each
+        //      vertical-sum row goes through the wave's own LDS scratch row and
+        //      comes back shifted by 0..s-1 columns for the horizontal sum.
+        //      LDS operations of one wave complete in order, so the scratch row
+        //      needs no workgroup barrier, only compiler fences.
         constexpr int NCH = L::NCH, NCS = L::NCS;
         int voff[NCH];
 #pragma unroll
@@ -497,8 +546,9 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
                 for (int k = 0; k < NCH; ++k) vv[r][k] = buf_load_f32(rrow, voff[k]);
             }
         };
-        auto sum_rows = [&](float (&vv)[IH][NCH], int ic) {
-            float* splane = Sb + ic * L::SPLANE;
+        // into LDS slot `slot` of the chunk
+        auto sum_rows = [&](float (&vv)[IH][NCH], int slot) {
+            float* splane = Sb + slot * L::SPLANE;
 #pragma unroll
             for (int r = 0; r < RS; ++r) {
                 // The fences keep the compiler from moving this row's reads
@@ -525,110 +575,129 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
                 }
             }
         };
-        // Channels wave, wave+NW, ...; two register buffers alternate (the
-        // loop is unrolled by two so that neither is indexed at run time).
-        const int nmine = (CinP - wave + NW - 1) / NW;
+
+        // 3. contraction: B for lane (g, l16), block p, tap (ky, kx) and the
+        //    chunk's quad j is Sx[slot 4j + g][py*S + ky][px*S + kx] for
+        //    position j = p*16 + l16.
+        int pbase[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int j = p * 16 + l16;
+            const int py = j / TPW, px = j - (j / TPW) * TPW;
+            pbase[p] = g * L::SPLANE + py * S * RSS + px;
+        }
+        floatx4 acc[CB][P];
+        auto contract = [&](const float (&a)[K * K][CB], int jq) {
+            const int lq = 4 * jq * L::SPLANE;
+#pragma unroll
+            for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+                for (int kx = 0; kx < K; ++kx) {
+                    float bv[P];
+#pragma unroll
+                    for (int p = 0; p < P; ++p) bv[p] = Sb[pbase[p] + lq + ky * RSS + (kx % S) * QS + kx / S];
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                        for (int p = 0; p < P; ++p) acc[cb][p] = mfma_16x16x4(a[ky * K + kx][cb], bv[p], acc[cb][p]);
+                }
+        };
+
         float va[IH][NCH], vb[IH][NCH];
-        if (nmine > 0) load_rows(va, wave);
-        for (int m = 0; m < nmine; m += 2) {
-            const int ic = wave + m * NW;
-            if (m + 1 < nmine) load_rows(vb, ic + NW);
-            sum_rows(va, ic);
-            if (m + 1 < nmine) {
-                if (m + 2 < nmine) load_rows(va, ic + 2 * NW);
-                sum_rows(vb, ic + NW);
-            }
-        }
-    }
-    __syncthreads();
-
-    // 3. contraction: B for lane (g, l16), block p, tap (ky, kx) is
-    //    Sx[g*CINQ + q][py*S + ky][px*S + kx] for position j = p*16 + l16.
-    int pbase[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int j = p * 16 + l16;
-        const int py = j / TPW, px = j - (j / TPW) * TPW;
-        pbase[p] = g * CINQ * L::SPLANE + py * S * RSS + px;
-    }
-    floatx4 acc[CB][P];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int p = 0; p < P; ++p) acc[cb][p] = floatx4{0.f, 0.f, 0.f, 0.f};
-    auto contract = [&](const float (&a)[K * K][CB], int q) {
-        const int lq = q * L::SPLANE;
-#pragma unroll
-        for (int ky = 0; ky < K; ++ky)
-#pragma unroll
-            for (int kx = 0; kx < K; ++kx) {
-                float bv[P];
-#pragma unroll
-                for (int p = 0; p < P; ++p) bv[p] = Sb[pbase[p] + lq + ky * RSS + (kx % S) * QS + kx / S];
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int p = 0; p < P; ++p) acc[cb][p] = mfma_16x16x4(a[ky * K + kx][cb], bv[p], acc[cb][p]);
-            }
-    };
-    // channel groups in pairs, so that the two weight buffers alternate
-    // without copies (one copy per weight and group cost 25 moves per group)
-    for (int q = 0; q < CINQ; q += 2) {
-        load_a(a_nxt, q + 1);
-        contract(a_cur, q);
-        if (q + 1 < CINQ) {
-            load_a(a_cur, q + 2);
-            contract(a_nxt, q + 1);
-        }
-    }
-
-    // Epilogue (as the direct kernel): window sum / s^2 + bias.
-    const float inv = 1.0f / (float)(S * S);
-    const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
-    float lsum = 0.f;
-    static_assert(P * 16 == TPH * TPW, "every lane of every block holds a tile position");
-    if (MODE != OUT_MAP && co0 + 16 * CB <= Cout && ph0 + TPH <= PH && pw0 + TPW <= PW) {
-        // the whole tile is in range: no per-output tests, and the scale, the
-        // bias and -log2(e) of the sigmoid's argument in one multiply-add
-        constexpr float kNegLog2e = -1.4426950408889634f;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float c0 = bco[cb][r] * kNegLog2e;
-#pragma unroll
-                for (int p = 0; p < P; ++p)
-                    lsum += __builtin_amdgcn_rcpf(
-                        1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(acc[cb][p][r], inv * kNegLog2e, c0)));
-            }
-    } else {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int co = co0 + cb * 16 + 4 * g + r;
-                const bool cok = co < Cout;
-#pragma unroll
-                for (int p = 0; p < P; ++p) {
-                    const int j = p * 16 + l16;
-                    const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
-                    if (cok && ph < PH && pw < PW) {
-                        const float avg = acc[cb][p][r] * inv + bco[cb][r];
-                        if constexpr (MODE == OUT_MAP)
-                            dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
-                        else
-                            lsum += logistic(avg);
-                    }
+        // box sums of chunk c (va holds the rows of its first channel)
+        auto box_chunk = [&](int c) {
+            load_rows(vb, c * CC + wave + NW);
+            sum_rows(va, wave);
+            sum_rows(vb, wave + NW);
+            __syncthreads();
+        };
+        // the chunk's quads in pairs, so that the two weight buffers
+        // alternate without copies (one copy per weight and group cost 25
+        // moves per group); a_cur holds the chunk's first quad on entry and
+        // the next chunk's on exit (QC is even)
+        auto contract_chunk = [&](int c) {
+            const int q0 = c * QC, qend = min(q0 + QC, CINQ);
+            for (int q = q0; q < qend; q += 2) {
+                load_a(a_nxt, q + 1);
+                contract(a_cur, q - q0);
+                if (q + 1 < qend) {
+                    load_a(a_cur, q + 2);
+                    contract(a_nxt, q + 1 - q0);
                 }
             }
-    }
+        };
+        // the first chunk on its own, so that the accumulators start after
+        // its box sums
+        load_rows(va, wave);
+        box_chunk(0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int p = 0; p < P; ++p) acc[cb][p] = floatx4{0.f, 0.f, 0.f, 0.f};
+        contract_chunk(0);
+        // Further chunks: the accumulators stay live through the box sums,
+        // so those use one row buffer (no prefetch of the second channel).
+        const int nchunks = (CINQ + QC - 1) / QC;
+        for (int c = 1; c < nchunks; ++c) {
+            __syncthreads();  // the last chunk's box sums are read
+            load_rows(va, c * CC + wave);
+            sum_rows(va, wave);
+            load_rows(va, c * CC + wave + NW);
+            sum_rows(va, wave + NW);
+            __syncthreads();
+            contract_chunk(c);
+        }
+
+        // Epilogue (as the direct kernel): window sum / s^2 + bias.
+        const float inv = 1.0f / (float)(S * S);
+        const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
+        float lsum = 0.f;
+        static_assert(P * 16 == TPH * TPW, "every lane of every block holds a tile position");
+        if (MODE != OUT_MAP && co0 + 16 * CB <= Cout && ph0 + TPH <= PH && pw0 + TPW <= PW) {
+            // the whole tile is in range: no per-output tests, and the scale, the
+            // bias and -log2(e) of the sigmoid's argument in one multiply-add
+            constexpr float kNegLog2e = -1.4426950408889634f;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float c0 = bco[cb][r] * kNegLog2e;
+#pragma unroll
+                    for (int p = 0; p < P; ++p)
+                        lsum += __builtin_amdgcn_rcpf(
+                            1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(acc[cb][p][r], inv * kNegLog2e, c0)));
+                }
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int co = co0 + cb * 16 + 4 * g + r;
+                    const bool cok = co < Cout;
+#pragma unroll
+                    for (int p = 0; p < P; ++p) {
+                        const int j = p * 16 + l16;
+                        const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
+                        if (cok && ph < PH && pw < PW) {
+                            const float avg = acc[cb][p][r] * inv + bco[cb][r];
+                            if constexpr (MODE == OUT_MAP)
+                                dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = avg;
+                            else
+                                lsum += logistic(avg);
+                        }
+                    }
+                }
+        }
+        dsum += lsum;
+        if (!WALK || u + parts >= units) break;
+    }  // units
     if constexpr (MODE != OUT_MAP) {
-        const float s = block_sum<NW>(lsum, red);
+        const float s = block_sum<NW>((float)dsum, red);
         if (tid == 0) {
             if constexpr (MODE == OUT_SUM_ATOMIC)
                 atomicAdd(dst + b, s);
             else
-                dst[(size_t)b * (tiles_per_item * co_ranges) + cr * tiles_per_item + tile] = s;
+                dst[(size_t)b * parts + part] = s;
         }
     }
 }
@@ -658,12 +727,16 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
 // outputs use (9 of every 16) and issues about half the vector instructions
 // per output.
 // Workgroup: one batch item, TPH = 2 pooled rows x TPW = 48 pooled columns,
-// 64 output channels (4 waves x 16).  Wave w makes the box sums of channels
-// w, w+4, ...; k-slot g of contraction step (m, tap) is channel 4m + g at
-// tap (ky, kx) = (tap / 3, tap % 3), so lane group g reads one channel's 9
-// taps.  Requires W % 4 == 0 (a 16-byte column group is all in or all out
-// of the row); VEC selects 16-byte loads (x 16-byte aligned) or four 4-byte
-// loads.
+// 64 output channels (4 waves x 16).  k-slot g of contraction step (m, tap)
+// is channel 4m + g at tap (ky, kx) = (tap / 3, tap % 3), so lane group g
+// reads one channel's 9 taps.  The channels go through LDS in chunks of CQ
+// quads (4*CQ channels: 28 KB for CQ = 2), so any channel count fits: wave w
+// makes the box sums of channel 4m + w of each quad m of the chunk, then the
+// workgroup contracts the chunk's quads, then the next chunk's box sums
+// overwrite them.  The next channel's rows load during the current one's
+// sums and, across a chunk boundary, during the contraction.  Requires
+// W % 4 == 0 (a 16-byte column group is all in or all out of the row); VEC
+// selects 16-byte loads (x 16-byte aligned) or four 4-byte loads.
 struct Box4 {
     static constexpr int K = 3, S = 4, TPH = 2, TPW = 48, NW = 4, NT = 256;
     static constexpr int IR = TPH * S + K - 1;  // input rows a tile reads: 10
@@ -673,29 +746,52 @@ struct Box4 {
     static constexpr int CPLANE = TPH * 9 * TPW + 16;
 };
 
-template <int MODE, bool VEC, int NQ>
+// Channel quads per LDS chunk: one for a single-quad input, else two.
+constexpr int box4_chunk_quads(int NQ) { return NQ == 1 ? 1 : 2; }
+
+// NQ: CINQ when it is 1 or 2 (one chunk, the channel loop unrolled, each
+// channel's rows in registers of their own), else 0 (chunks in a run-time
+// loop).
+template <int MODE, bool VEC, int NQ, bool WALK>
 __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int tiles_w,
-    int tiles_per_item, int co_ranges, int nblocks) {
+    int tiles, int units, int parts, int nblocks) {
     constexpr int S = Box4::S, TPH = Box4::TPH, TPW = Box4::TPW, NW = Box4::NW, IR = Box4::IR;
-    extern __shared__ float lds[];  // Sx [4*CINQ][CPLANE]: [TPH][9][TPW] + 16 per channel
+    constexpr int CQ = box4_chunk_quads(NQ);
+    constexpr int NB = TPH * TPW / 16;  // 16-position blocks of the tile
+    extern __shared__ float lds[];      // Sx [4*CQ][CPLANE]: [TPH][9][TPW] + 16 per channel
     __shared__ float red[NW];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lid = xcd_spread(blockIdx.x, nblocks);
-    const int tile = lid % tiles_per_item;
-    const int cr = (lid / tiles_per_item) % co_ranges;
-    const int b = lid / (tiles_per_item * co_ranges);
-    const int tile_y = tile / tiles_w, tile_x = tile - (tile / tiles_w) * tiles_w;
-    const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
-    const int y0 = ph0 * S, x0 = pw0 * S;
     const int g = lane >> 4, l16 = lane & 15;
+    // Workgroup `part` of batch item b walks units part, part + parts, ...
+    // (unit = channel range * tiles + tile).
+    const int lid = xcd_spread(blockIdx.x, nblocks);
+    const int b = lid / parts;
+    const int part = lid - b * parts;
+    const float* xb = x + (size_t)b * Cin * H * W;
+    const buf_rsrc rw = make_rsrc(w, Cout * Cin * 9 * 4);
+    const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
+    const int nq = NQ > 0 ? NQ : CINQ;
+    walk_sum_t<WALK> dsum = 0;  // this lane's sigmoids over all its units
 
-    // 1. box sums of channels wave, wave + NW, ... (channels >= Cin load 0)
-    {
-        const float* xb = x + (size_t)b * Cin * H * W;
+    for (int u = part;; u += parts) {
+        if (WALK && u != part) __syncthreads();  // every wave is done with the last unit's box sums
+        const int cr = u / tiles, tile = u - (u / tiles) * tiles;
+        const int tile_y = tile / tiles_w, tile_x = tile - (tile / tiles_w) * tiles_w;
+        const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
+        const int y0 = ph0 * S, x0 = pw0 * S;
+        const int co_w = cr * Box4::CO_RANGE + wave * 16;  // this wave's first output channel
+
+        float bco[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int co = co_w + 4 * g + r;
+            bco[r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
+        }
+
         const int xc = x0 + 4 * lane;
         const int coff = (lane <= TPW && xc < W) ? xc * 4 : kBufOOB;
         auto load_rows = [&](floatx4 (&v)[IR], int ic) {
@@ -718,32 +814,50 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
             return __builtin_bit_cast(float,
                                       __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x130, 0xF, 0xF, true));
         };
-        // NQ > 0: CINQ == NQ at compile time, so the loop unrolls and each
-        // channel's rows load into registers of their own (a run-time loop
-        // copies the prefetched rows back into the loop's registers: 40
-        // moves per channel)
+        // A of step (m, tap) for lane (g, l16) is w[co][4m + g][tap], co = this
+        // wave's channel l16; 0 past Cin, past Cout and for m >= CINQ.
+        const int co_a = co_w + l16;
+        auto load_a = [&](float (&a)[9], int m) {
+            const int ic = 4 * m + g;
+            const int base = (co_a < Cout && ic < Cin && m < CINQ) ? (co_a * Cin + ic) * 36 : kBufOOB;
+#pragma unroll
+            for (int t = 0; t < 9; ++t) a[t] = buf_load_f32(rw, base + 4 * t);
+        };
+
         floatx4 v[IR];
         load_rows(v, wave);
-        const int nq = NQ > 0 ? NQ : CINQ;
-        constexpr int kUnroll = NQ > 0 ? NQ : 1;
-#pragma unroll kUnroll
-        for (int i = 0; i < nq; ++i) {
-            const int ic = wave + NW * i;
+        float a[CQ][9];
+        floatx4 acc[NB];
+
+        // Box sums of this wave's channel of quad c*CQ + j into LDS slot
+        // 4j + wave.  Loads return in issue order, so when the next chunk's
+        // rows are prefetched, the chunk's weights load before them (at the
+        // chunk's last quad); in the last chunk they load after the sums.
+        auto load_chunk_a = [&](int c) {
+#pragma unroll
+            for (int jj = 0; jj < CQ; ++jj) load_a(a[jj], c * CQ + jj);
+        };
+        auto box_sums = [&](int c, int j) {
+            const int i = c * CQ + j;
+            const int ic = 4 * i + wave;
             // vertical 4-sums first: column c of the lane's four, window rows
             // 4ph+ky .. 4ph+ky+3 = pair (4ph+ky, +1) + pair (4ph+ky+2, +3)
             float vs[TPH][3][4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float a[IR - 1];
+            for (int cc = 0; cc < 4; ++cc) {
+                float p[IR - 1];
 #pragma unroll
-                for (int r = 0; r + 1 < IR; ++r) a[r] = v[r][c] + v[r + 1][c];
+                for (int r = 0; r + 1 < IR; ++r) p[r] = v[r][cc] + v[r + 1][cc];
 #pragma unroll
                 for (int ph = 0; ph < TPH; ++ph)
 #pragma unroll
-                    for (int ky = 0; ky < 3; ++ky) vs[ph][ky][c] = a[ph * S + ky] + a[ph * S + ky + 2];
+                    for (int ky = 0; ky < 3; ++ky) vs[ph][ky][cc] = p[ph * S + ky] + p[ph * S + ky + 2];
             }
-            if (i + 1 < nq) load_rows(v, ic + NW);
-            float* sp = lds + (size_t)ic * Box4::CPLANE + lane;
+            if (i + 1 < nq) {
+                if (j == CQ - 1) load_chunk_a(c);
+                load_rows(v, ic + NW);
+            }
+            float* sp = lds + (size_t)(4 * j + wave) * Box4::CPLANE + lane;
 #pragma unroll
             for (int ph = 0; ph < TPH; ++ph) {
                 // then the horizontal 4-sums at kx = 0, 1, 2 (columns 4 and 5
@@ -751,10 +865,10 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
                 float sx[9];
 #pragma unroll
                 for (int ky = 0; ky < 3; ++ky) {
-                    const float* u = vs[ph][ky];
-                    const float p01 = u[0] + u[1], p23 = u[2] + u[3];
+                    const float* uu = vs[ph][ky];
+                    const float p01 = uu[0] + uu[1], p23 = uu[2] + uu[3];
                     sx[3 * ky] = p01 + p23;
-                    sx[3 * ky + 1] = (u[1] + u[2]) + (next_lane(u[0]) + u[3]);
+                    sx[3 * ky + 1] = (uu[1] + uu[2]) + (next_lane(uu[0]) + uu[3]);
                     sx[3 * ky + 2] = next_lane(p01) + p23;
                 }
                 if (lane < TPW) {
@@ -763,167 +877,151 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
                     for (int k = 0; k < 9; ++k) q[k * TPW] = sx[k];
                 }
             }
-        }
-    }
-
-    // weights and bias while the box sums finish: A of step (m, tap) for lane
-    // (g, l16) is w[co][4m + g][tap], co = this wave's channel l16
-    const int co_a = cr * Box4::CO_RANGE + wave * 16 + l16;
-    const buf_rsrc rw = make_rsrc(w, Cout * Cin * 9 * 4);
-    auto load_a = [&](float (&a)[9], int m) {
-        const int ic = 4 * m + g;
-        const int base = (co_a < Cout && ic < Cin && m < CINQ) ? (co_a * Cin + ic) * 36 : kBufOOB;
-#pragma unroll
-        for (int t = 0; t < 9; ++t) a[t] = buf_load_f32(rw, base + 4 * t);
-    };
-    float a_cur[9], a_nxt[9];
-    load_a(a_cur, 0);
-    const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
-    float bco[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int co = cr * Box4::CO_RANGE + wave * 16 + 4 * g + r;
-        bco[r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
-    }
-    __syncthreads();
-
-    // 2. contraction over (channel, tap): 6 blocks of 16 positions.  The
-    //    first channel quad starts the accumulators from 0 inside the first
-    //    MFMA, and the quads run in pairs so that the weight registers
-    //    alternate without copies.
-    constexpr int NB = TPH * TPW / 16;
-    floatx4 acc[NB];
-    auto quad = [&](const float (&a)[9], int m, bool first) {
-        const float* cb = lds + (size_t)(4 * m + g) * Box4::CPLANE;
-#pragma unroll
-        for (int p = 0; p < NB; ++p) {
-            const float* q = cb + (p / 3) * 9 * TPW + (p % 3) * 16 + l16;
-            float t[9];
-#pragma unroll
-            for (int k = 0; k < 9; ++k) t[k] = q[k * TPW];
-            acc[p] = mfma_16x16x4(a[0], t[0], first ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[p]);
-#pragma unroll
-            for (int k = 1; k < 9; ++k) acc[p] = mfma_16x16x4(a[k], t[k], acc[p]);
-        }
-    };
-    load_a(a_nxt, 1);
-    quad(a_cur, 0, true);
-    for (int m = 1; m < CINQ; m += 2) {
-        load_a(a_cur, m + 1);
-        quad(a_nxt, m, false);
-        if (m + 1 < CINQ) {
-            load_a(a_nxt, m + 2);
-            quad(a_cur, m + 1, false);
-        }
-    }
-
-    // Epilogue: lane (g, l16) of block p holds the window sum of channel
-    // co = ... + 4g + r at pooled position (p / 3, (p % 3) * 16 + l16).
-    // sigma(sum / s^2 + bias) = 1 / (1 + 2^(sum * c1 + c0[r])), with the
-    // scale, the bias and -log2(e) folded into one multiply-add.
-    const float inv = 1.0f / (float)(S * S);
-    constexpr float kNegLog2e = -1.4426950408889634f;
-    float lsum = 0.f;
-    const int co_w = cr * Box4::CO_RANGE + wave * 16;  // this wave's first output channel
-    if constexpr (MODE != OUT_MAP) {
-        if (co_w + 16 <= Cout && ph0 + TPH <= PH && pw0 + TPW <= PW) {
-            // every output of the wave is in range
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float c0 = bco[r] * kNegLog2e;
-#pragma unroll
-                for (int p = 0; p < NB; ++p)
-                    lsum += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(acc[p][r], inv * kNegLog2e, c0)));
-            }
-        } else if (co_w + 16 <= Cout) {
-            // a tile at the bottom or right edge: every channel of the wave is
-            // in range, so one select per position block adds the block's
-            // four sums or nothing (positions past the map hold finite values
-            // of the zero-padded or dropped input, but a select keeps a
-            // non-finite one out of the sum too)
-            bool colok[3];
-#pragma unroll
-            for (int c = 0; c < 3; ++c) colok[c] = pw0 + c * 16 + l16 < PW;
+        };
+        // Contraction of LDS slot quad j (channels 4j .. 4j+3) with weights aq:
+        // 6 blocks of 16 positions x 9 taps.  The unit's first quad starts the
+        // accumulators from 0 inside its first MFMA.
+        auto quad = [&](const float (&aq)[9], int j, auto first_tag) {
+            constexpr bool FIRST = decltype(first_tag)::value;
+            const float* cb = lds + (size_t)(4 * j + g) * Box4::CPLANE;
 #pragma unroll
             for (int p = 0; p < NB; ++p) {
-                float sp = 0.f;
+                const float* q = cb + (p / 3) * 9 * TPW + (p % 3) * 16 + l16;
+                float t[9];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sp += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(
-                                                           __builtin_fmaf(acc[p][r], inv * kNegLog2e, bco[r] * kNegLog2e)));
-                lsum += (ph0 + p / 3 < PH && colok[p % 3]) ? sp : 0.f;
+                for (int k = 0; k < 9; ++k) t[k] = q[k * TPW];
+                acc[p] = mfma_16x16x4(aq[0], t[0], FIRST ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[p]);
+#pragma unroll
+                for (int k = 1; k < 9; ++k) acc[p] = mfma_16x16x4(aq[k], t[k], acc[p]);
             }
+        };
+        auto chunk = [&](int c, auto first_tag) {
+#pragma unroll
+            for (int j = 0; j < CQ; ++j) box_sums(c, j);
+            if ((c + 1) * CQ >= nq) load_chunk_a(c);
+            __syncthreads();
+            quad(a[0], 0, first_tag);
+#pragma unroll
+            for (int j = 1; j < CQ; ++j)
+                if (c * CQ + j < nq) quad(a[j], j, std::false_type{});
+        };
+        chunk(0, std::true_type{});
+        if constexpr (NQ == 0) {
+            const int nchunks = (nq + CQ - 1) / CQ;
+            for (int c = 1; c < nchunks; ++c) {
+                __syncthreads();  // the last chunk's box sums are read
+                chunk(c, std::false_type{});
+            }
+        }
+
+        // Epilogue: lane (g, l16) of block p holds the window sum of channel
+        // co = ... + 4g + r at pooled position (p / 3, (p % 3) * 16 + l16).
+        // sigma(sum / s^2 + bias) = 1 / (1 + 2^(sum * c1 + c0[r])), with the
+        // scale, the bias and -log2(e) folded into one multiply-add.
+        const float inv = 1.0f / (float)(S * S);
+        constexpr float kNegLog2e = -1.4426950408889634f;
+        float lsum = 0.f;
+        if constexpr (MODE != OUT_MAP) {
+            if (co_w + 16 <= Cout && ph0 + TPH <= PH && pw0 + TPW <= PW) {
+                // every output of the wave is in range
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float c0 = bco[r] * kNegLog2e;
+#pragma unroll
+                    for (int p = 0; p < NB; ++p)
+                        lsum += __builtin_amdgcn_rcpf(
+                            1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(acc[p][r], inv * kNegLog2e, c0)));
+                }
+            } else if (co_w + 16 <= Cout) {
+                // a tile at the bottom or right edge: every channel of the wave
+                // is in range, so one select per position block adds the
+                // block's four sums or nothing (positions past the map hold
+                // finite values of the zero-padded or dropped input, but a
+                // select keeps a non-finite one out of the sum too)
+                bool colok[3];
+#pragma unroll
+                for (int c = 0; c < 3; ++c) colok[c] = pw0 + c * 16 + l16 < PW;
+#pragma unroll
+                for (int p = 0; p < NB; ++p) {
+                    float sp = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sp += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(
+                                                               acc[p][r], inv * kNegLog2e, bco[r] * kNegLog2e)));
+                    lsum += (ph0 + p / 3 < PH && colok[p % 3]) ? sp : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int co = co_w + 4 * g + r;
+                    const float c0 = bco[r] * kNegLog2e;
+#pragma unroll
+                    for (int p = 0; p < NB; ++p) {
+                        const int ph = ph0 + p / 3, pw = pw0 + (p % 3) * 16 + l16;
+                        const float v =
+                            __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(acc[p][r], inv * kNegLog2e, c0)));
+                        lsum += (co < Cout && ph < PH && pw < PW) ? v : 0.f;
+                    }
+                }
+            }
+            dsum += lsum;
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int co = co_w + 4 * g + r;
-                const float c0 = bco[r] * kNegLog2e;
 #pragma unroll
                 for (int p = 0; p < NB; ++p) {
                     const int ph = ph0 + p / 3, pw = pw0 + (p % 3) * 16 + l16;
-                    const float v =
-                        __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(acc[p][r], inv * kNegLog2e, c0)));
-                    lsum += (co < Cout && ph < PH && pw < PW) ? v : 0.f;
+                    if (co < Cout && ph < PH && pw < PW)
+                        dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = acc[p][r] * inv + bco[r];
                 }
             }
         }
-        const float sum = block_sum<NW>(lsum, red);
+        if (!WALK || u + parts >= units) break;
+    }  // units
+    if constexpr (MODE != OUT_MAP) {
+        const float sum = block_sum<NW>((float)dsum, red);
         if (tid == 0) {
             if constexpr (MODE == OUT_SUM_ATOMIC)
                 atomicAdd(dst + b, sum);
             else
-                dst[(size_t)b * (tiles_per_item * co_ranges) + cr * tiles_per_item + tile] = sum;
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int co = co_w + 4 * g + r;
-#pragma unroll
-            for (int p = 0; p < NB; ++p) {
-                const int ph = ph0 + p / 3, pw = pw0 + (p % 3) * 16 + l16;
-                if (co < Cout && ph < PH && pw < PW)
-                    dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = acc[p][r] * inv + bco[r];
-            }
+                dst[(size_t)b * parts + part] = sum;
         }
     }
 }
 
-static size_t box4_lds_bytes(int Cin) {
-    return (size_t)4 * ((Cin + 3) / 4) * Box4::CPLANE * sizeof(float);
+static size_t box4_lds_bytes(int NQ) {
+    return (size_t)4 * box4_chunk_quads(NQ) * Box4::CPLANE * sizeof(float);
 }
 
 // The K = 3, s = 4 shapes the one-column-per-lane kernel takes (by shape
 // alone, so that the deterministic form's workspace size does not depend on
-// pointer alignment).
-static bool box4_fits(const Conv2dShape& s) {
-    return s.K == 3 && s.S == 4 && s.W % 4 == 0 && box4_lds_bytes(s.Cin) <= kMaxLds;
-}
+// pointer alignment).  Any channel count: the box sums go through LDS in
+// chunks of at most 8 channels.
+static bool box4_fits(const Conv2dShape& s) { return s.K == 3 && s.S == 4 && s.W % 4 == 0; }
 
 template <bool VEC, int NQ>
 struct Box4Launch {
     template <int MODE>
-    static constexpr auto kernel = conv2d_pool_boxsum4_kernel<MODE, VEC, NQ>;
+    static constexpr auto kernel_once = conv2d_pool_boxsum4_kernel<MODE, VEC, NQ, false>;
+    template <int MODE>
+    static constexpr auto kernel_walk = conv2d_pool_boxsum4_kernel<MODE, VEC, NQ, true>;
 };
 
-static int64_t box4_parts(const Conv2dShape& s) {
-    const int tiles = ((s.PH + Box4::TPH - 1) / Box4::TPH) * ((s.PW + Box4::TPW - 1) / Box4::TPW);
-    return (int64_t)tiles * ((s.Cout + Box4::CO_RANGE - 1) / Box4::CO_RANGE);
-}
+static Walk box4_walk(const Conv2dShape& s) { return make_walk<Box4::TPH, Box4::TPW, Box4::CO_RANGE>(s); }
+
+static int64_t box4_parts(const Conv2dShape& s) { return box4_walk(s).parts; }
 
 template <bool VEC, int NQ>
 static hipError_t launch_box4_q(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
                                 int mode, hipStream_t stream) {
     const int CINQ = (s.Cin + 3) / 4;
-    const size_t lds = box4_lds_bytes(s.Cin);
-    const int tiles_w = (s.PW + Box4::TPW - 1) / Box4::TPW;
-    const int tiles = ((s.PH + Box4::TPH - 1) / Box4::TPH) * tiles_w;
-    const int co_ranges = (s.Cout + Box4::CO_RANGE - 1) / Box4::CO_RANGE;
-    const long nblocks_l = (long)tiles * co_ranges * s.B;
-    if (nblocks_l > INT32_MAX) return hipErrorInvalidValue;
-    const int nblocks = (int)nblocks_l;
+    const size_t lds = box4_lds_bytes(NQ);
+    const Walk k = box4_walk(s);
+    const int nblocks = k.parts * s.B;  // at most 1024 * 65535
     using L = Box4Launch<VEC, NQ>;
-    FCONV_LAUNCH_MODES(L::template kernel, dim3(nblocks), dim3(Box4::NT), lds, stream, x, w, bias, dst, s.Cin, s.H,
-                       s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
+    FCONV_LAUNCH_WALK(L::template kernel, k.units > k.parts, dim3(nblocks), dim3(Box4::NT), lds, stream, x, w, bias, dst, s.Cin, s.H,
+                       s.W, s.Cout, s.PH, s.PW, CINQ, k.tiles_w, k.tiles, k.units, k.parts, nblocks);
 }
 
 // One or two channels per wave at compile time, more at run time.
@@ -955,49 +1053,42 @@ using BoxK5S3 = DirectCfg<FCONV_CFG_BOX_K5S3>;
 using BoxK3S2 = DirectCfg<3, 2, 1, 4, 4, 1, 4, 16>;
 using BoxK3S3 = DirectCfg<3, 3, 1, 4, 4, 1, 4, 16>;
 
+// LDS of one workgroup: a chunk of CC channels' box sums plus the waves'
+// scratch rows, whatever Cin is.
 template <class Cfg>
-static size_t box_lds_bytes(int Cin) {
+static constexpr size_t box_lds_bytes() {
     using L = BoxLayout<Cfg>;
-    const int CinP = 4 * ((Cin + 3) / 4);
-    return ((size_t)CinP * L::SPLANE + (size_t)Cfg::NW * L::SCRATCH) * sizeof(float);
+    return ((size_t)L::CC * L::SPLANE + (size_t)Cfg::NW * L::SCRATCH) * sizeof(float);
 }
 
+// Every channel count: the box sums go through LDS in chunks.
 bool conv2d_boxsum_supported(int Cin, int K, int S) {
-    size_t bytes = 0;
-    if (K == 3 && S == 4) bytes = box_lds_bytes<BoxK3S4>(Cin);
-    else if (K == 5 && S == 3) bytes = box_lds_bytes<BoxK5S3>(Cin);
-    else if (K == 3 && S == 2) bytes = box_lds_bytes<BoxK3S2>(Cin);
-    else if (K == 3 && S == 3) bytes = box_lds_bytes<BoxK3S3>(Cin);
-    else return false;
-    return bytes <= kMaxLds;
+    return Cin >= 1 && ((K == 3 && (S == 2 || S == 3 || S == 4)) || (K == 5 && S == 3));
 }
 
 template <class Cfg>
 struct BoxLaunch {
     template <int MODE>
-    static constexpr auto kernel = conv2d_pool_boxsum_kernel<Cfg, MODE>;
+    static constexpr auto kernel_once = conv2d_pool_boxsum_kernel<Cfg, MODE, false>;
+    template <int MODE>
+    static constexpr auto kernel_walk = conv2d_pool_boxsum_kernel<Cfg, MODE, true>;
 };
 
 template <class Cfg>
 static int64_t box_parts(const Conv2dShape& s) {
-    const int tiles = ((s.PH + Cfg::TPH - 1) / Cfg::TPH) * ((s.PW + Cfg::TPW - 1) / Cfg::TPW);
-    const int co_ranges = (s.Cout + Cfg::CO_RANGE - 1) / Cfg::CO_RANGE;
-    return (int64_t)tiles * co_ranges;
+    return direct_walk<Cfg>(s).parts;
 }
 
 template <class Cfg>
 static hipError_t launch_box(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
                              int mode, hipStream_t stream) {
     const int CINQ = (s.Cin + 3) / 4;
-    const size_t lds = box_lds_bytes<Cfg>(s.Cin);
-    const int tiles_w = (s.PW + Cfg::TPW - 1) / Cfg::TPW;
-    const int tiles = ((s.PH + Cfg::TPH - 1) / Cfg::TPH) * tiles_w;
-    const int co_ranges = (s.Cout + Cfg::CO_RANGE - 1) / Cfg::CO_RANGE;
-    const long nblocks_l = (long)tiles * co_ranges * s.B;
-    if (nblocks_l > INT32_MAX) return hipErrorInvalidValue;
-    const int nblocks = (int)nblocks_l;
-    FCONV_LAUNCH_MODES(BoxLaunch<Cfg>::template kernel, dim3(nblocks), dim3(Cfg::NT), lds, stream, x, w, bias, dst,
-                       s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, tiles_w, tiles, co_ranges, nblocks);
+    constexpr size_t lds = box_lds_bytes<Cfg>();
+    static_assert(lds <= kMaxLds, "box-sum chunk fits LDS");
+    const Walk k = direct_walk<Cfg>(s);
+    const int nblocks = k.parts * s.B;  // at most 1024 * 65535
+    FCONV_LAUNCH_WALK(BoxLaunch<Cfg>::template kernel, k.units > k.parts, dim3(nblocks), dim3(Cfg::NT), lds, stream, x, w, bias, dst,
+                       s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, k.tiles_w, k.tiles, k.units, k.parts, nblocks);
 }
 
 hipError_t conv2d_boxsum_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
@@ -1027,43 +1118,49 @@ int64_t conv2d_boxsum_parts(const Conv2dShape& s) {
 
 // One thread per (co, ph, pw) of one batch item: the window's s*s conv
 // outputs are summed straight from global memory.  The general fallback.
+// Workgroup (part, b) walks the item's 256-output blocks part, part + parts,
+// ... (parts = gridDim.x).
 template <int MODE>
 __global__ __launch_bounds__(256) void conv2d_pool_simple_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
-    float* __restrict__ dst, int Cin, int H, int W, int Cout, int K, int S, int PH, int PW) {
+    float* __restrict__ dst, int Cin, int H, int W, int Cout, int K, int S, int PH, int PW, int units) {
     __shared__ float red[4];
     const int b = blockIdx.y;
+    const int parts = gridDim.x;
     const int n = Cout * PH * PW;
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    float v = 0.f;
-    if (idx < n) {
-        const int co = idx / (PH * PW);
-        const int rem = idx - co * (PH * PW);
-        const int ph = rem / PW, pw = rem - (rem / PW) * PW;
-        const float* xb = x + (size_t)b * Cin * H * W;
-        const float* wc = w + (size_t)co * Cin * K * K;
-        float acc = 0.f;
-        for (int dy = 0; dy < S; ++dy)
-            for (int dx = 0; dx < S; ++dx)
-                for (int ic = 0; ic < Cin; ++ic)
-                    for (int ky = 0; ky < K; ++ky) {
-                        const float* xr = xb + (ic * H + ph * S + dy + ky) * W + pw * S + dx;
-                        const float* wr = wc + (ic * K + ky) * K;
-                        for (int kx = 0; kx < K; ++kx) acc += xr[kx] * wr[kx];
-                    }
-        const float avg = acc / (float)(S * S) + (bias ? bias[co] : 0.f);
-        if constexpr (MODE == OUT_MAP)
-            dst[(size_t)b * n + idx] = avg;
-        else
-            v = logistic(avg);
+    double dsum = 0.0;
+    for (int blk = blockIdx.x; blk < units; blk += parts) {
+        const int64_t idx64 = (int64_t)blk * 256 + threadIdx.x;
+        if (idx64 < n) {
+            const int idx = (int)idx64;
+            const int co = idx / (PH * PW);
+            const int rem = idx - co * (PH * PW);
+            const int ph = rem / PW, pw = rem - (rem / PW) * PW;
+            const float* xb = x + (size_t)b * Cin * H * W;
+            const float* wc = w + (size_t)co * Cin * K * K;
+            float acc = 0.f;
+            for (int dy = 0; dy < S; ++dy)
+                for (int dx = 0; dx < S; ++dx)
+                    for (int ic = 0; ic < Cin; ++ic)
+                        for (int ky = 0; ky < K; ++ky) {
+                            const float* xr = xb + ((size_t)ic * H + ph * S + dy + ky) * W + pw * S + dx;
+                            const float* wr = wc + (ic * K + ky) * K;
+                            for (int kx = 0; kx < K; ++kx) acc += xr[kx] * wr[kx];
+                        }
+            const float avg = acc / (float)(S * S) + (bias ? bias[co] : 0.f);
+            if constexpr (MODE == OUT_MAP)
+                dst[(size_t)b * n + idx] = avg;
+            else
+                dsum += (double)logistic(avg);
+        }
     }
     if constexpr (MODE != OUT_MAP) {
-        const float s = block_sum<4>(v, red);
+        const float s = block_sum<4>((float)dsum, red);
         if (threadIdx.x == 0) {
             if constexpr (MODE == OUT_SUM_ATOMIC)
                 atomicAdd(dst + b, s);
             else
-                dst[(size_t)b * gridDim.x + blockIdx.x] = s;
+                dst[(size_t)b * parts + blockIdx.x] = s;
         }
     }
 }
@@ -1073,13 +1170,15 @@ struct SimpleLaunch {
     static constexpr auto kernel = conv2d_pool_simple_kernel<MODE>;
 };
 
-int64_t conv2d_simple_parts(const Conv2dShape& s) { return ((int64_t)s.Cout * s.PH * s.PW + 255) / 256; }
+static int simple_units(const Conv2dShape& s) { return (int)(((int64_t)s.Cout * s.PH * s.PW + 255) / 256); }
+
+int64_t conv2d_simple_parts(const Conv2dShape& s) { return walk_parts(simple_units(s)); }
 
 hipError_t conv2d_simple_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
                                 float* dst, int mode, hipStream_t stream) {
     const dim3 grid((unsigned)conv2d_simple_parts(s), s.B);
     FCONV_LAUNCH_MODES(SimpleLaunch::template kernel, grid, dim3(256), 0, stream, x, w, bias, dst, s.Cin, s.H, s.W,
-                       s.Cout, s.K, s.S, s.PH, s.PW);
+                       s.Cout, s.K, s.S, s.PH, s.PW, simple_units(s));
 }
 
 // ---------------------------------------------------------------- fixed-order reduction of partial sums

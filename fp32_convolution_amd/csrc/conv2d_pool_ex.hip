@@ -43,57 +43,65 @@ namespace fconv {
 
 // ---------------------------------------------------------------- any shape
 
+// One thread per pooled output; workgroup (part, b) walks the item's
+// 256-output blocks part, part + parts, ... (parts = gridDim.x).
 template <int MODE>
 __global__ __launch_bounds__(256) void conv2d_pool_general_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int K, int S, int PH, int PW, int pool_max,
-    int relu) {
+    int relu, int units) {
     __shared__ float red[4];
     const int b = blockIdx.y;
+    const int parts = gridDim.x;
     const int n = Cout * PH * PW;
-    const int idx = blockIdx.x * 256 + threadIdx.x;
     const int Hc = H - K + 1, Wc = W - K + 1;
-    float v = 0.f;
-    if (idx < n) {
-        const int co = idx / (PH * PW);
-        const int rem = idx - co * (PH * PW);
-        const int ph = rem / PW, pw = rem - (rem / PW) * PW;
-        const int ny = min(S, Hc - ph * S), nx = min(S, Wc - pw * S);
-        const float* xb = x + (size_t)b * Cin * H * W;
-        const float* wc = w + (size_t)co * Cin * K * K;
-        const float bc = bias ? bias[co] : 0.f;
-        float pooled = pool_max ? -INFINITY : 0.f;
-        for (int dy = 0; dy < ny; ++dy)
-            for (int dx = 0; dx < nx; ++dx) {
-                float c = 0.f;
-                for (int ic = 0; ic < Cin; ++ic)
-                    for (int ky = 0; ky < K; ++ky) {
-                        const float* xr = xb + (ic * H + ph * S + dy + ky) * W + pw * S + dx;
-                        const float* wr = wc + (ic * K + ky) * K;
-                        for (int kx = 0; kx < K; ++kx) c += xr[kx] * wr[kx];
-                    }
-                c += bc;
-                if (relu) c = fmaxf(c, 0.f);
-                pooled = pool_max ? fmaxf(pooled, c) : pooled + c;
-            }
-        if (!pool_max) pooled /= (float)(ny * nx);
-        if constexpr (MODE == OUT_MAP)
-            dst[(size_t)b * n + idx] = pooled;
-        else
-            v = logistic(pooled);
+    double dsum = 0.0;
+    for (int blk = blockIdx.x; blk < units; blk += parts) {
+        const int64_t idx64 = (int64_t)blk * 256 + threadIdx.x;
+        if (idx64 < n) {
+            const int idx = (int)idx64;
+            const int co = idx / (PH * PW);
+            const int rem = idx - co * (PH * PW);
+            const int ph = rem / PW, pw = rem - (rem / PW) * PW;
+            const int ny = min(S, Hc - ph * S), nx = min(S, Wc - pw * S);
+            const float* xb = x + (size_t)b * Cin * H * W;
+            const float* wc = w + (size_t)co * Cin * K * K;
+            const float bc = bias ? bias[co] : 0.f;
+            float pooled = pool_max ? -INFINITY : 0.f;
+            for (int dy = 0; dy < ny; ++dy)
+                for (int dx = 0; dx < nx; ++dx) {
+                    float c = 0.f;
+                    for (int ic = 0; ic < Cin; ++ic)
+                        for (int ky = 0; ky < K; ++ky) {
+                            const float* xr = xb + ((size_t)ic * H + ph * S + dy + ky) * W + pw * S + dx;
+                            const float* wr = wc + (ic * K + ky) * K;
+                            for (int kx = 0; kx < K; ++kx) c += xr[kx] * wr[kx];
+                        }
+                    c += bc;
+                    if (relu) c = fmaxf(c, 0.f);
+                    pooled = pool_max ? fmaxf(pooled, c) : pooled + c;
+                }
+            if (!pool_max) pooled /= (float)(ny * nx);
+            if constexpr (MODE == OUT_MAP)
+                dst[(size_t)b * n + idx] = pooled;
+            else
+                dsum += (double)logistic(pooled);
+        }
     }
     if constexpr (MODE != OUT_MAP) {
-        const float s = block_sum<4>(v, red);
+        const float s = block_sum<4>((float)dsum, red);
         if (threadIdx.x == 0) {
             if constexpr (MODE == OUT_SUM_ATOMIC)
                 atomicAdd(dst + b, s);
             else
-                dst[(size_t)b * gridDim.x + blockIdx.x] = s;
+                dst[(size_t)b * parts + blockIdx.x] = s;
         }
     }
 }
 
-int64_t conv2d_general_parts(const Conv2dShape& s) { return ((int64_t)s.Cout * s.PH * s.PW + 255) / 256; }
+static int general_units(const Conv2dShape& s) { return (int)(((int64_t)s.Cout * s.PH * s.PW + 255) / 256); }
+
+int64_t conv2d_general_parts(const Conv2dShape& s) { return walk_parts(general_units(s)); }
 
 // ---------------------------------------------------------------- on matrix cores
 
@@ -138,11 +146,11 @@ constexpr int kPoolMean = 0, kPoolMax = 1, kPoolMeanFolded = 2;
 // NQ: 0, or the number of channel quads CINQ (1 or 2) when all of them fit
 // in registers.  Then the block's weights load once; otherwise quad q's
 // weights stream in under quad q-1's matrix instructions.
-template <class C, int POOL, int MODE, int NQ>
+template <class C, int POOL, int MODE, int NQ, bool WALK>
 __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane, int tiles_w,
-    int tiles, int co_ranges, int nblocks, int relu, int ceil_mode) {
+    int tiles, int co_ranges, int units, int parts, int nblocks, int relu, int ceil_mode) {
     constexpr int K = C::K, S = C::S, NCB = C::NCB, TPH = C::TPH, TPW = C::TPW;
     constexpr int IH = C::IH, IW = C::IW, RP = C::RP, NR = C::NR, WPB = C::WPB, CPB = C::CPB;
     constexpr bool POOL_MAX = POOL == kPoolMax, FOLD = POOL == kPoolMeanFolded;
@@ -157,326 +165,334 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     const int wave = tid >> 6;
     const int g = lane >> 4;    // MFMA k-slot: channel group
     const int l16 = lane & 15;  // row of A / column of B
+    const int Hc = H - K + 1, Wc = W - K + 1;
     // Block order: the hardware deals block ids to the 8 XCDs round-robin;
     // xcd_spread gives each XCD one contiguous run of logical ids, ordered
     // (batch item, tile row, tile column, channel range) with the channel
     // range fastest.  Tiles that share input (the channel ranges of one tile,
     // its right and lower neighbours with their halo lines) then run close
-    // together in time on one XCD and find that input in its L2.
+    // together in time on one XCD and find that input in its L2.  Workgroup
+    // `part` of batch item b walks the item's units part, part + parts, ...
+    // (unit = tile * co_ranges + channel range).
     const int lid = xcd_spread(blockIdx.x, nblocks);
-    const int cor = lid % co_ranges;
-    const int rest = lid / co_ranges;
-    const int tile = rest % tiles;
-    const int b = rest / tiles;
-    const int tile_y = tile / tiles_w;
-    const int tile_x = tile - tile_y * tiles_w;
-    const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
-    const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
-    const int co0 = cor * C::CO_RANGE + wave * 16;
-    const int Hc = H - K + 1, Wc = W - K + 1;
+    const int b = lid / parts;
+    const int part = lid - b * parts;
+    walk_sum_t<WALK> dsum = 0;  // this lane's sigmoids over all its units
+    for (int u = part;; u += parts) {
+        if (WALK && u != part) __syncthreads();  // every wave is done with the last unit's tile
+        const int cor = u % co_ranges;
+        const int tile = u / co_ranges;
+        const int tile_y = tile / tiles_w;
+        const int tile_x = tile - tile_y * tiles_w;
+        const int y0 = tile_y * TPH * S, x0 = tile_x * TPW * S;
+        const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
+        const int co0 = cor * C::CO_RANGE + wave * 16;
 
-    // Weights of channel quad q: a[ky][kx] = w[co0 + l16, g*CINQ + q, ky, kx]
-    // (0 where co or ic is out of range).
-    const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
-    auto load_a = [&](float (&a)[K][K], int q) {
-        const int ic = g * CINQ + q;
-        const int co = co0 + l16;
-        const bool ok = (co < Cout) && (ic < Cin) && (q < CINQ);
-        const int base = ok ? (co * Cin + ic) * (K * K * 4) : kBufOOB;
+        // Weights of channel quad q: a[ky][kx] = w[co0 + l16, g*CINQ + q, ky, kx]
+        // (0 where co or ic is out of range).
+        const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
+        auto load_a = [&](float (&a)[K][K], int q) {
+            const int ic = g * CINQ + q;
+            const int co = co0 + l16;
+            const bool ok = (co < Cout) && (ic < Cin) && (q < CINQ);
+            const int base = ok ? (co * Cin + ic) * (K * K * 4) : kBufOOB;
 #pragma unroll
-        for (int ky = 0; ky < K; ++ky)
+            for (int ky = 0; ky < K; ++ky)
 #pragma unroll
-            for (int kx = 0; kx < K; ++kx) a[ky][kx] = buf_load_f32(rw, base + (ky * K + kx) * 4);
-    };
-    // Streaming: a[0] holds the current quad's weights, a[1] the next one's.
-    // Resident: a[q] holds quad q's.
-    float a[2][K][K];
-    load_a(a[0], 0);
-    if constexpr (NQ == 2) load_a(a[1], 1);
+                for (int kx = 0; kx < K; ++kx) a[ky][kx] = buf_load_f32(rw, base + (ky * K + kx) * 4);
+        };
+        // Streaming: a[0] holds the current quad's weights, a[1] the next one's.
+        // Resident: a[q] holds quad q's.
+        float a[2][K][K];
+        load_a(a[0], 0);
+        if constexpr (NQ == 2) load_a(a[1], 1);
 
-    // Bias of the channels this lane's accumulator elements hold: co0 + 4g + r.
-    const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
-    floatx4 bco;
+        // Bias of the channels this lane's accumulator elements hold: co0 + 4g + r.
+        const buf_rsrc rb = make_rsrc(bias, bias ? Cout * 4 : 0);
+        floatx4 bco;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int co = co0 + 4 * g + r;
-        bco[r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
-    }
-
-    // Stage the input tile: channel ic at ic*plane, row r at r*RP, column c at
-    // c.  Whole rows per wave through a per-row buffer resource (empty for
-    // rows outside the image and channels >= Cin, which therefore read 0).
-    {
-        constexpr int NCH = (IW + 63) / 64;
-        constexpr int UR = 14;  // rows in flight per wave
-        int voff[NCH];
-        bool inr[NCH];
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int c = lane + 64 * k;
-            inr[k] = c < IW;
-            voff[k] = (c < IW && x0 + c < W) ? (x0 + c) * 4 : kBufOOB;
+        for (int r = 0; r < 4; ++r) {
+            const int co = co0 + 4 * g + r;
+            bco[r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
         }
-        const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-        const int nrows = 4 * CINQ * IH;
-        const float* xb = x + (size_t)b * Cin * H * W;
-        for (int row0 = wave_s; row0 < nrows; row0 += C::NW * UR) {
-            float v[UR][NCH];
+
+        // Stage the input tile: channel ic at ic*plane, row r at r*RP, column c at
+        // c.  Whole rows per wave through a per-row buffer resource (empty for
+        // rows outside the image and channels >= Cin, which therefore read 0).
+        {
+            constexpr int NCH = (IW + 63) / 64;
+            constexpr int UR = 14;  // rows in flight per wave
+            int voff[NCH];
+            bool inr[NCH];
 #pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int row = row0 + u * C::NW;
-                const int ic = row / IH, r = row - (row / IH) * IH;
-                const bool ok = (row < nrows) && (ic < Cin) && (y0 + r < H);
-                const buf_rsrc rrow = make_rsrc(xb + (ok ? (ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
-#pragma unroll
-                for (int k = 0; k < NCH; ++k) v[u][k] = buf_load_f32(rrow, voff[k]);
+            for (int k = 0; k < NCH; ++k) {
+                const int c = lane + 64 * k;
+                inr[k] = c < IW;
+                voff[k] = (c < IW && x0 + c < W) ? (x0 + c) * 4 : kBufOOB;
             }
+            const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+            const int nrows = 4 * CINQ * IH;
+            const float* xb = x + (size_t)b * Cin * H * W;
+            for (int row0 = wave_s; row0 < nrows; row0 += C::NW * UR) {
+                float v[UR][NCH];
 #pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int row = row0 + u * C::NW;
-                if (row < nrows) {
+                for (int u = 0; u < UR; ++u) {
+                    const int row = row0 + u * C::NW;
                     const int ic = row / IH, r = row - (row / IH) * IH;
-                    float* lrow = lds + ic * plane + r * RP;
+                    const bool ok = (row < nrows) && (ic < Cin) && (y0 + r < H);
+                    const buf_rsrc rrow = make_rsrc(xb + (ok ? (ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
 #pragma unroll
-                    for (int k = 0; k < NCH; ++k)
-                        if (inr[k]) lrow[lane + 64 * k] = v[u][k];
+                    for (int k = 0; k < NCH; ++k) v[u][k] = buf_load_f32(rrow, voff[k]);
+                }
+#pragma unroll
+                for (int u = 0; u < UR; ++u) {
+                    const int row = row0 + u * C::NW;
+                    if (row < nrows) {
+                        const int ic = row / IH, r = row - (row / IH) * IH;
+                        float* lrow = lds + ic * plane + r * RP;
+#pragma unroll
+                        for (int k = 0; k < NCH; ++k)
+                            if (inr[k]) lrow[lane + 64 * k] = v[u][k];
+                    }
                 }
             }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // A column block's lanes read 16 consecutive words; the 4 channel groups
-    // sit plane*CINQ words apart (padded onto different banks).  Rows of one
-    // pooled row read from two base registers: rows 0 .. RG-1 from the
-    // first, the rest from a second one RG rows further on, so that every
-    // read keeps within the 8-bit dword offsets of paired LDS reads.
-    constexpr int RG = (255 - (NCB - 1) * CPB - (K - 1)) / RP + 1;
-    static_assert(RG >= 1 && NR <= 2 * RG, "two base registers reach every row");
-    const lds_fptr lbase = (lds_fptr)lds + g * CINQ * plane + l16;
-    // NBA (a compile-time tag): the column blocks the tile computes.
-    auto load_row = [&](float (&bv)[NCB][K], lds_fptr row, auto nba) {
+        // A column block's lanes read 16 consecutive words; the 4 channel groups
+        // sit plane*CINQ words apart (padded onto different banks).  Rows of one
+        // pooled row read from two base registers: rows 0 .. RG-1 from the
+        // first, the rest from a second one RG rows further on, so that every
+        // read keeps within the 8-bit dword offsets of paired LDS reads.
+        constexpr int RG = (255 - (NCB - 1) * CPB - (K - 1)) / RP + 1;
+        static_assert(RG >= 1 && NR <= 2 * RG, "two base registers reach every row");
+        const lds_fptr lbase = (lds_fptr)lds + g * CINQ * plane + l16;
+        // NBA (a compile-time tag): the column blocks the tile computes.
+        auto load_row = [&](float (&bv)[NCB][K], lds_fptr row, auto nba) {
 #pragma unroll
-        for (int nb = 0; nb < decltype(nba)::value; ++nb)
+            for (int nb = 0; nb < decltype(nba)::value; ++nb)
 #pragma unroll
-            for (int kx = 0; kx < K; ++kx) bv[nb][kx] = row[nb * CPB + kx];
-    };
+                for (int kx = 0; kx < K; ++kx) bv[nb][kx] = row[nb * CPB + kx];
+        };
 
-    const bool odd1 = (l16 & 1) != 0, odd2 = (l16 & 2) != 0;
-    auto pool2 = [](float a, float c) { return POOL_MAX ? fmaxf(a, c) : a + c; };
+        const bool odd1 = (l16 & 1) != 0, odd2 = (l16 & 2) != 0;
+        auto pool2 = [](float a, float c) { return POOL_MAX ? fmaxf(a, c) : a + c; };
 
-    // One channel quad of one pooled row with weights aq.  In the first quad
-    // the first MFMA into each accumulator block takes the bias as its C
-    // operand, so the accumulators never need a separate initialisation.
-    // Folded rows: each column accumulator sums S conv outputs, so it starts
-    // at S * bias.
-    if constexpr (FOLD) bco = bco * (float)S;
-    floatx4 acc[NCB][NACC];
-    auto mma_quad = [&](const float (&aq)[K][K], int q, int pr, auto first_tag, auto nba) {
-        constexpr bool FIRST = decltype(first_tag)::value;
-        constexpr int NBA = decltype(nba)::value;
-        const lds_fptr p0 = lbase + q * plane + pr * S * RP;
-        const lds_fptr p1 = NR > RG ? lds_opaque(p0 + RG * RP) : p0;
-        auto row = [&](int rr) { return rr < RG ? p0 + rr * RP : p1 + (rr - RG) * RP; };
-        float bcur[NCB][K], bnxt[NCB][K];
-        load_row(bcur, row(0), nba);
+        // One channel quad of one pooled row with weights aq.  In the first quad
+        // the first MFMA into each accumulator block takes the bias as its C
+        // operand, so the accumulators never need a separate initialisation.
+        // Folded rows: each column accumulator sums S conv outputs, so it starts
+        // at S * bias.
+        if constexpr (FOLD) bco = bco * (float)S;
+        floatx4 acc[NCB][NACC];
+        auto mma_quad = [&](const float (&aq)[K][K], int q, int pr, auto first_tag, auto nba) {
+            constexpr bool FIRST = decltype(first_tag)::value;
+            constexpr int NBA = decltype(nba)::value;
+            const lds_fptr p0 = lbase + q * plane + pr * S * RP;
+            const lds_fptr p1 = NR > RG ? lds_opaque(p0 + RG * RP) : p0;
+            auto row = [&](int rr) { return rr < RG ? p0 + rr * RP : p1 + (rr - RG) * RP; };
+            float bcur[NCB][K], bnxt[NCB][K];
+            load_row(bcur, row(0), nba);
 #pragma unroll
-        for (int rr = 0; rr < NR; ++rr) {
-            if (rr + 1 < NR) load_row(bnxt, row(rr + 1), nba);
+            for (int rr = 0; rr < NR; ++rr) {
+                if (rr + 1 < NR) load_row(bnxt, row(rr + 1), nba);
 #pragma unroll
-            for (int ky = 0; ky < K; ++ky) {
-                const int dy = rr - ky;
-                if (dy < 0 || dy >= S) continue;
+                for (int ky = 0; ky < K; ++ky) {
+                    const int dy = rr - ky;
+                    if (dy < 0 || dy >= S) continue;
 #pragma unroll
-                for (int kx = 0; kx < K; ++kx)
+                    for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+                        for (int nb = 0; nb < NBA; ++nb)
+                            acc[nb][FOLD ? 0 : dy] = mfma_16x16x4(
+                                aq[ky][kx], bcur[nb][kx],
+                                (FIRST && ky == 0 && kx == 0 && (!FOLD || dy == 0)) ? bco : acc[nb][FOLD ? 0 : dy]);
+                }
+                if (rr + 1 < NR) {
 #pragma unroll
                     for (int nb = 0; nb < NBA; ++nb)
-                        acc[nb][FOLD ? 0 : dy] = mfma_16x16x4(
-                            aq[ky][kx], bcur[nb][kx],
-                            (FIRST && ky == 0 && kx == 0 && (!FOLD || dy == 0)) ? bco : acc[nb][FOLD ? 0 : dy]);
+#pragma unroll
+                        for (int kx = 0; kx < K; ++kx) bcur[nb][kx] = bnxt[nb][kx];
+                }
             }
-            if (rr + 1 < NR) {
+        };
+        // Streaming weights: the next quad's (quad 0 again after the last: the
+        // next pooled row starts there) load under this quad's MFMAs.
+        auto quad_stream = [&](int q, int pr, auto first_tag, auto nba) {
+            load_a(a[1], q + 1 < CINQ ? q + 1 : 0);
+            mma_quad(a[0], q, pr, first_tag, nba);
 #pragma unroll
-                for (int nb = 0; nb < NBA; ++nb)
+            for (int ky = 0; ky < K; ++ky)
 #pragma unroll
-                    for (int kx = 0; kx < K; ++kx) bcur[nb][kx] = bnxt[nb][kx];
-            }
-        }
-    };
-    // Streaming weights: the next quad's (quad 0 again after the last: the
-    // next pooled row starts there) load under this quad's MFMAs.
-    auto quad_stream = [&](int q, int pr, auto first_tag, auto nba) {
-        load_a(a[1], q + 1 < CINQ ? q + 1 : 0);
-        mma_quad(a[0], q, pr, first_tag, nba);
-#pragma unroll
-        for (int ky = 0; ky < K; ++ky)
-#pragma unroll
-            for (int kx = 0; kx < K; ++kx) a[0][ky][kx] = a[1][ky][kx];
-    };
+                for (int kx = 0; kx < K; ++kx) a[0][ky][kx] = a[1][ky][kx];
+        };
 
-    float lsum = 0.f;
-    // FULL: every column of the tile and every channel of the wave lies
-    // inside the pooled map, so no lane needs a range check.
-    auto pool_row = [&](const floatx4 (&ac)[NCB][NACC], int ph, int yr, auto edge_tag, auto full_tag, auto nba) {
-        constexpr bool EDGE = decltype(edge_tag)::value, FULL = decltype(full_tag)::value;
-        const float fill = POOL_MAX ? -INFINITY : 0.f;
+        float lsum = 0.f;
+        // FULL: every column of the tile and every channel of the wave lies
+        // inside the pooled map, so no lane needs a range check.
+        auto pool_row = [&](const floatx4 (&ac)[NCB][NACC], int ph, int yr, auto edge_tag, auto full_tag, auto nba) {
+            constexpr bool EDGE = decltype(edge_tag)::value, FULL = decltype(full_tag)::value;
+            const float fill = POOL_MAX ? -INFINITY : 0.f;
 #pragma unroll
-        for (int nb = 0; nb < decltype(nba)::value; ++nb) {
-            float m[4];
-            if constexpr (FOLD) {
+            for (int nb = 0; nb < decltype(nba)::value; ++nb) {
+                float m[4];
+                if constexpr (FOLD) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) m[r] = ac[nb][0][r];
-            } else {
-                float v[S][4];
-#pragma unroll
-                for (int dy = 0; dy < S; ++dy)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) v[dy][r] = ac[nb][dy][r];
-                if (!POOL_MAX && relu) {
+                    for (int r = 0; r < 4; ++r) m[r] = ac[nb][0][r];
+                } else {
+                    float v[S][4];
 #pragma unroll
                     for (int dy = 0; dy < S; ++dy)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) v[dy][r] = fmaxf(v[dy][r], 0.f);
-                }
-                if constexpr (EDGE) {
-                    const bool col_ok = x0 + nb * CPB + l16 < Wc;
+                        for (int r = 0; r < 4; ++r) v[dy][r] = ac[nb][dy][r];
+                    if (!POOL_MAX && relu) {
 #pragma unroll
-                    for (int dy = 0; dy < S; ++dy) {
-                        const bool ok = col_ok && (yr + dy < Hc);
+                        for (int dy = 0; dy < S; ++dy)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) v[dy][r] = ok ? v[dy][r] : fill;
+                            for (int r = 0; r < 4; ++r) v[dy][r] = fmaxf(v[dy][r], 0.f);
                     }
-                }
-                // Over the window's rows, inside the lane.
+                    if constexpr (EDGE) {
+                        const bool col_ok = x0 + nb * CPB + l16 < Wc;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    m[r] = v[0][r];
+                        for (int dy = 0; dy < S; ++dy) {
+                            const bool ok = col_ok && (yr + dy < Hc);
 #pragma unroll
-                    for (int dy = 1; dy < S; ++dy) m[r] = pool2(m[r], v[dy][r]);
-                }
-            }
-            // Over the window's columns, across lanes.  Each case leaves NV
-            // finished pooled values per lane, value i for channel
-            // co0 + 4g + chan[i] at window win of the block, valid where the
-            // lane finishes a window (fin).
-            constexpr int NV = S == 4 ? 1 : S == 2 ? 2 : 4;
-            float pv[NV];
-            int chan[NV];
-            int win;
-            bool fin;
-            if constexpr (S == 4) {
-                // Lanes 4j..4j+3 hold window j.  Step 1 pairs lanes l, l^1:
-                // the even lane keeps channels r = 0, 2 and sends r = 1, 3;
-                // the odd lane the reverse.  Step 2 pairs l, l^2 the same way
-                // over the two kept values.  Lane dx ends with channel r = dx
-                // over all four columns.
-                const float k01 = odd1 ? m[1] : m[0], s01 = odd1 ? m[0] : m[1];
-                const float k23 = odd1 ? m[3] : m[2], s23 = odd1 ? m[2] : m[3];
-                const float p01 = pool2(k01, quad_xor1(s01));
-                const float p23 = pool2(k23, quad_xor1(s23));
-                const float kk = odd2 ? p23 : p01, ss = odd2 ? p01 : p23;
-                pv[0] = pool2(kk, quad_xor2(ss));
-                chan[0] = l16 & 3;
-                win = l16 >> 2;
-                fin = true;
-            } else if constexpr (S == 2) {
-                // Lanes 2j, 2j+1 hold window j.  One pairing step as above:
-                // lane dx ends with channels dx and 2 + dx.
-                const float k01 = odd1 ? m[1] : m[0], s01 = odd1 ? m[0] : m[1];
-                const float k23 = odd1 ? m[3] : m[2], s23 = odd1 ? m[2] : m[3];
-                pv[0] = pool2(k01, quad_xor1(s01));
-                pv[1] = pool2(k23, quad_xor1(s23));
-                chan[0] = l16 & 1;
-                chan[1] = 2 + (l16 & 1);
-                win = l16 >> 1;
-                fin = true;
-            } else {
-                // Lanes 3j..3j+2 (j < 5) hold window j: the window's last lane
-                // gathers its two left neighbours (DPP row shifts) and
-                // finishes all four channels.
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pv[r] = pool2(pool2(m[r], row_shr1(m[r])), row_shr2(m[r]));
-                    chan[r] = r;
-                }
-                win = l16 / 3;
-                fin = (l16 % 3 == 2) && l16 < 15;
-            }
-
-            const int pw = pw0 + nb * WPB + win;
-            if (fin && (FULL || pw < PW)) {
-                const float inv = EDGE ? 1.0f / (float)(min(S, Hc - ph * S) * min(S, Wc - pw * S))
-                                       : 1.0f / (float)(S * S);
-#pragma unroll
-                for (int i = 0; i < NV; ++i) {
-                    const int co = co0 + 4 * g + chan[i];
-                    if (FULL || co < Cout) {
-                        float o = pv[i];
-                        if (POOL_MAX) {
-                            if (relu) o = fmaxf(o, 0.f);  // ReLU commutes with max
-                        } else if (EDGE || MODE == OUT_MAP) {
-                            o = o * inv;
+                            for (int r = 0; r < 4; ++r) v[dy][r] = ok ? v[dy][r] : fill;
                         }
-                        if constexpr (MODE == OUT_MAP)
-                            dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = o;
-                        else if (POOL_MAX || EDGE)
-                            lsum += logistic(o);
-                        else
-                            lsum += logistic_scaled(o, inv);
+                    }
+                    // Over the window's rows, inside the lane.
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        m[r] = v[0][r];
+#pragma unroll
+                        for (int dy = 1; dy < S; ++dy) m[r] = pool2(m[r], v[dy][r]);
+                    }
+                }
+                // Over the window's columns, across lanes.  Each case leaves NV
+                // finished pooled values per lane, value i for channel
+                // co0 + 4g + chan[i] at window win of the block, valid where the
+                // lane finishes a window (fin).
+                constexpr int NV = S == 4 ? 1 : S == 2 ? 2 : 4;
+                float pv[NV];
+                int chan[NV];
+                int win;
+                bool fin;
+                if constexpr (S == 4) {
+                    // Lanes 4j..4j+3 hold window j.  Step 1 pairs lanes l, l^1:
+                    // the even lane keeps channels r = 0, 2 and sends r = 1, 3;
+                    // the odd lane the reverse.  Step 2 pairs l, l^2 the same way
+                    // over the two kept values.  Lane dx ends with channel r = dx
+                    // over all four columns.
+                    const float k01 = odd1 ? m[1] : m[0], s01 = odd1 ? m[0] : m[1];
+                    const float k23 = odd1 ? m[3] : m[2], s23 = odd1 ? m[2] : m[3];
+                    const float p01 = pool2(k01, quad_xor1(s01));
+                    const float p23 = pool2(k23, quad_xor1(s23));
+                    const float kk = odd2 ? p23 : p01, ss = odd2 ? p01 : p23;
+                    pv[0] = pool2(kk, quad_xor2(ss));
+                    chan[0] = l16 & 3;
+                    win = l16 >> 2;
+                    fin = true;
+                } else if constexpr (S == 2) {
+                    // Lanes 2j, 2j+1 hold window j.  One pairing step as above:
+                    // lane dx ends with channels dx and 2 + dx.
+                    const float k01 = odd1 ? m[1] : m[0], s01 = odd1 ? m[0] : m[1];
+                    const float k23 = odd1 ? m[3] : m[2], s23 = odd1 ? m[2] : m[3];
+                    pv[0] = pool2(k01, quad_xor1(s01));
+                    pv[1] = pool2(k23, quad_xor1(s23));
+                    chan[0] = l16 & 1;
+                    chan[1] = 2 + (l16 & 1);
+                    win = l16 >> 1;
+                    fin = true;
+                } else {
+                    // Lanes 3j..3j+2 (j < 5) hold window j: the window's last lane
+                    // gathers its two left neighbours (DPP row shifts) and
+                    // finishes all four channels.
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pv[r] = pool2(pool2(m[r], row_shr1(m[r])), row_shr2(m[r]));
+                        chan[r] = r;
+                    }
+                    win = l16 / 3;
+                    fin = (l16 % 3 == 2) && l16 < 15;
+                }
+
+                const int pw = pw0 + nb * WPB + win;
+                if (fin && (FULL || pw < PW)) {
+                    const float inv = EDGE ? 1.0f / (float)(min(S, Hc - ph * S) * min(S, Wc - pw * S))
+                                           : 1.0f / (float)(S * S);
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) {
+                        const int co = co0 + 4 * g + chan[i];
+                        if (FULL || co < Cout) {
+                            float o = pv[i];
+                            if (POOL_MAX) {
+                                if (relu) o = fmaxf(o, 0.f);  // ReLU commutes with max
+                            } else if (EDGE || MODE == OUT_MAP) {
+                                o = o * inv;
+                            }
+                            if constexpr (MODE == OUT_MAP)
+                                dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = o;
+                            else if (POOL_MAX || EDGE)
+                                lsum += logistic(o);
+                            else
+                                lsum += logistic_scaled(o, inv);
+                        }
                     }
                 }
             }
-        }
-    };
+        };
 
-    const int nrow_tile = min(TPH, PH - ph0);
-    const bool full = pw0 + TPW <= PW && co0 + 16 <= Cout;
-    auto row_pass = [&](int pr, auto nba) {
-        if constexpr (NQ > 0) {
-            mma_quad(a[0], 0, pr, std::true_type{}, nba);
-            if constexpr (NQ == 2) mma_quad(a[1], 1, pr, std::false_type{}, nba);
-        } else {
-            quad_stream(0, pr, std::true_type{}, nba);
-            for (int q = 1; q < CINQ; ++q) quad_stream(q, pr, std::false_type{}, nba);
-        }
+        const int nrow_tile = min(TPH, PH - ph0);
+        const bool full = pw0 + TPW <= PW && co0 + 16 <= Cout;
+        auto row_pass = [&](int pr, auto nba) {
+            if constexpr (NQ > 0) {
+                mma_quad(a[0], 0, pr, std::true_type{}, nba);
+                if constexpr (NQ == 2) mma_quad(a[1], 1, pr, std::false_type{}, nba);
+            } else {
+                quad_stream(0, pr, std::true_type{}, nba);
+                for (int q = 1; q < CINQ; ++q) quad_stream(q, pr, std::false_type{}, nba);
+            }
 
-        // Epilogue of pooled row ph.  Lane (g, l16) holds in acc[nb][dy][r]
-        // the conv output of channel co0 + 4g + r at conv row ph*S + dy,
-        // column x0 + nb*16 + l16.  The pool works on register copies.
-        // Conv outputs outside the map exist only in partial (ceil-mode)
-        // windows at the bottom and right edges; those rows take a separate
-        // copy of the epilogue that masks them.
-        const int ph = ph0 + pr;
-        const int yr = y0 + pr * S;
-        if (!FOLD && ceil_mode && (yr + S > Hc || x0 + TPW * S > Wc))
-            pool_row(acc, ph, yr, std::true_type{}, std::false_type{}, nba);  // (the folded pool has floor mode only)
-        else if (full)
-            pool_row(acc, ph, yr, std::false_type{}, std::true_type{}, nba);
-        else
-            pool_row(acc, ph, yr, std::false_type{}, std::false_type{}, nba);
-    };
-    // A tile of two column blocks whose second block lies wholly past the
-    // map (the last tile column when the map's width is not a multiple of
-    // the tile's) computes the first block only.
-    const int nbv = min(NCB, (PW - pw0 + WPB - 1) / WPB);
-    for (int pr = 0; pr < nrow_tile; ++pr) {
-        if constexpr (NCB == 2) {
-            if (nbv == 1)
-                row_pass(pr, std::integral_constant<int, 1>{});
+            // Epilogue of pooled row ph.  Lane (g, l16) holds in acc[nb][dy][r]
+            // the conv output of channel co0 + 4g + r at conv row ph*S + dy,
+            // column x0 + nb*16 + l16.  The pool works on register copies.
+            // Conv outputs outside the map exist only in partial (ceil-mode)
+            // windows at the bottom and right edges; those rows take a separate
+            // copy of the epilogue that masks them.
+            const int ph = ph0 + pr;
+            const int yr = y0 + pr * S;
+            if (!FOLD && ceil_mode && (yr + S > Hc || x0 + TPW * S > Wc))
+                pool_row(acc, ph, yr, std::true_type{}, std::false_type{}, nba);  // (the folded pool has floor mode only)
+            else if (full)
+                pool_row(acc, ph, yr, std::false_type{}, std::true_type{}, nba);
             else
-                row_pass(pr, std::integral_constant<int, 2>{});
-        } else {
-            row_pass(pr, std::integral_constant<int, NCB>{});
+                pool_row(acc, ph, yr, std::false_type{}, std::false_type{}, nba);
+        };
+        // A tile of two column blocks whose second block lies wholly past the
+        // map (the last tile column when the map's width is not a multiple of
+        // the tile's) computes the first block only.
+        const int nbv = min(NCB, (PW - pw0 + WPB - 1) / WPB);
+        for (int pr = 0; pr < nrow_tile; ++pr) {
+            if constexpr (NCB == 2) {
+                if (nbv == 1)
+                    row_pass(pr, std::integral_constant<int, 1>{});
+                else
+                    row_pass(pr, std::integral_constant<int, 2>{});
+            } else {
+                row_pass(pr, std::integral_constant<int, NCB>{});
+            }
         }
-    }
 
+        dsum += lsum;
+        if (!WALK || u + parts >= units) break;
+    }  // units
     if constexpr (MODE != OUT_MAP) {
-        const float s = block_sum<C::NW>(lsum, red);
+        const float s = block_sum<C::NW>((float)dsum, red);
         if (tid == 0) {
             if constexpr (MODE == OUT_SUM_ATOMIC)
                 atomicAdd(dst + b, s);
             else
-                dst[(size_t)b * (tiles * co_ranges) + tile * co_ranges + cor] = s;
+                dst[(size_t)b * parts + part] = s;
         }
     }
 }
@@ -506,9 +522,10 @@ size_t elem_lds_bytes(int Cin) {
 // The plain average pool (no ReLU, floor mode) runs folded.
 bool folds(const PoolOpts& o) { return !o.pool_max && !o.relu && !o.ceil_mode; }
 
+// Units of one batch item (tiles x channel ranges: at most its pooled-map
+// size, which fits int32) and workgroups per item.
 struct ElemGrid {
-    int tiles_w, tiles, co_ranges;
-    int64_t nblocks;
+    int tiles_w, tiles, co_ranges, units, parts;
 };
 
 template <class C>
@@ -516,24 +533,34 @@ ElemGrid elem_grid(const Conv2dShape& s) {
     const int tiles_h = (s.PH + C::TPH - 1) / C::TPH;
     const int tiles_w = (s.PW + C::TPW - 1) / C::TPW;
     const int co_ranges = (s.Cout + C::CO_RANGE - 1) / C::CO_RANGE;
-    return {tiles_w, tiles_h * tiles_w, co_ranges, (int64_t)tiles_h * tiles_w * co_ranges * s.B};
+    const int units = tiles_h * tiles_w * co_ranges;
+    return {tiles_w, tiles_h * tiles_w, co_ranges, units, walk_parts(units)};
 }
 
-template <class C, int POOL, int MODE, int NQ>
-hipError_t launch_elem_nq(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
-                          const PoolOpts& o, hipStream_t stream) {
+template <class C, int POOL, int MODE, int NQ, bool WALK>
+hipError_t launch_elem_w(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                         const PoolOpts& o, hipStream_t stream) {
     const int CINQ = (s.Cin + 3) / 4;
     const int plane = elem_plane<C>(CINQ);
     const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
     const ElemGrid g = elem_grid<C>(s);
-    if (g.nblocks > INT32_MAX) return hipErrorInvalidValue;
-    const void* fn = (const void*)conv2d_pool_elem_kernel<C, POOL, MODE, NQ>;
+    const int nblocks = g.parts * s.B;  // at most 1024 * 65535
+    const void* fn = (const void*)conv2d_pool_elem_kernel<C, POOL, MODE, NQ, WALK>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((conv2d_pool_elem_kernel<C, POOL, MODE, NQ>), dim3((unsigned)g.nblocks), dim3(C::NT), lds,
+    hipLaunchKernelGGL((conv2d_pool_elem_kernel<C, POOL, MODE, NQ, WALK>), dim3((unsigned)nblocks), dim3(C::NT), lds,
                        stream, x, w, bias, dst, s.Cin, s.H, s.W, s.Cout, s.PH, s.PW, CINQ, plane, g.tiles_w, g.tiles,
-                       g.co_ranges, (int)g.nblocks, o.relu ? 1 : 0, o.ceil_mode ? 1 : 0);
+                       g.co_ranges, g.units, g.parts, nblocks, o.relu ? 1 : 0, o.ceil_mode ? 1 : 0);
     return hipGetLastError();
+}
+
+// The walking instance when there are more units than workgroups.
+template <class C, int POOL, int MODE, int NQ>
+hipError_t launch_elem_nq(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
+                          const PoolOpts& o, hipStream_t stream) {
+    const ElemGrid g = elem_grid<C>(s);
+    if (g.units > g.parts) return launch_elem_w<C, POOL, MODE, NQ, true>(s, x, w, bias, dst, o, stream);
+    return launch_elem_w<C, POOL, MODE, NQ, false>(s, x, w, bias, dst, o, stream);
 }
 
 // One or two channel quads keep their weights in registers.
@@ -599,8 +626,7 @@ bool conv2d_elem_supported(int Cin, int K, int S) {
 int64_t conv2d_elem_parts(const Conv2dShape& s, const PoolOpts& o) {
     int64_t parts = -1;
     with_elem_cfg(s.K, s.S, folds(o), [&](auto c) {
-        const ElemGrid g = elem_grid<decltype(c)>(s);
-        parts = (int64_t)g.tiles * g.co_ranges;
+        parts = elem_grid<decltype(c)>(s).parts;
     });
     return parts;
 }
@@ -618,15 +644,16 @@ hipError_t conv2d_general_launch(const Conv2dShape& s, const float* x, const flo
                                  float* dst, int mode, const PoolOpts& o, hipStream_t stream) {
     const dim3 grid((unsigned)conv2d_general_parts(s), s.B);
     const int pm = o.pool_max ? 1 : 0, rl = o.relu ? 1 : 0;
+    const int units = general_units(s);
     if (mode == OUT_MAP)
         hipLaunchKernelGGL(conv2d_pool_general_kernel<OUT_MAP>, grid, dim3(256), 0, stream, x, w, bias, dst, s.Cin,
-                           s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl);
+                           s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl, units);
     else if (mode == OUT_PARTIAL)
         hipLaunchKernelGGL(conv2d_pool_general_kernel<OUT_PARTIAL>, grid, dim3(256), 0, stream, x, w, bias, dst,
-                           s.Cin, s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl);
+                           s.Cin, s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl, units);
     else
         hipLaunchKernelGGL(conv2d_pool_general_kernel<OUT_SUM_ATOMIC>, grid, dim3(256), 0, stream, x, w, bias,
-                           dst, s.Cin, s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl);
+                           dst, s.Cin, s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl, units);
     return hipGetLastError();
 }
 

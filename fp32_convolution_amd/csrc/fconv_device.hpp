@@ -35,6 +35,12 @@ __device__ __forceinline__ float buf_load_f32(buf_rsrc r, int byte_off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 
+// A lane's running sum of sigmoids across the units of work a workgroup
+// walks: fp64 when it walks several (its rounding then stays far below the
+// fp32 rounding of the final sums), fp32 for a single unit.
+template <bool WALK>
+using walk_sum_t = typename std::conditional<WALK, double, float>::type;
+
 // Sum over the 64 lanes, valid in every lane; the order is fixed.  Within
 // each row of 16 lanes with DPP (pairs, quads, half-row mirror, row mirror:
 // every lane then holds its row's sum), then the four row sums read out of

@@ -15,9 +15,21 @@ struct DwsepShape {
     int B, C, T, K, O, pad, Tout, stride, dil;
 };
 
+// Workgroups per batch item of a Conv2d launch.  A fused sum adds one fp32
+// partial per workgroup into out[b] with an atomic add.  Every partial is
+// positive (a sum of sigmoids), so each add rounds by at most half an ulp of
+// the final out[b], i.e. by at most 2^-24 |out[b]|; with at most
+// kMaxPartsPerItem partials that rounding stays within 1024 * 2^-24 = 6.1e-5
+// of |out[b]|, whatever the map size.  A map with more units of work (tiles x
+// output-channel ranges) than that has each workgroup walk several units,
+// part, part + parts, ..., summing its lanes' sigmoids in fp64 between units.
+constexpr int kMaxPartsPerItem = 1024;
+inline int walk_parts(int64_t units) { return units < kMaxPartsPerItem ? (int)units : kMaxPartsPerItem; }
+
 // What a Conv2d kernel writes: the fused sums (one float atomic per
 // workgroup into out[b]), the pre-sigmoid pooled map, or one partial sum per
 // workgroup into ws[b * parts_per_item + part] for a fixed-order reduction.
+// parts_per_item = walk_parts(units per item) for every mode.
 enum OutMode { OUT_SUM_ATOMIC = 0, OUT_MAP = 1, OUT_PARTIAL = 2 };
 
 // The generalised pool: max instead of mean, a ReLU between the conv and the

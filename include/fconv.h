@@ -36,15 +36,16 @@
  *     device work; a failed check returns FCONV_EINVAL and enqueues nothing.
  *   - A HIP launch error is returned as FCONV_EHIP (from hipGetLastError).
  *   - The sums inside a call are fp32.  fconv2d_pool_sigmoid_sum combines
- *     partial sums with floating-point atomics, so its last bits may differ
- *     from call to call.  Each atomic add rounds by up to half an ulp of the
- *     running total, so that error grows with the number of workgroups per
- *     batch item (bound: parts x ulp(out[b]) / 2, parts as reported by the
- *     deterministic form's workspace query / 4 / B).  It is about 1e-5
- *     relative for x[128,8,384,384] but reaches about 1e-3 relative for a
- *     single item of 5e8 input elements; the deterministic form sums the
- *     partials in a fixed order from small values up and stays within 1e-4
- *     there as well.
+ *     per-workgroup partial sums with floating-point atomics, so its last
+ *     bits may differ from call to call.  Every partial is positive (a sum
+ *     of sigmoids), so each atomic add rounds by at most half an ulp of the
+ *     final out[b], i.e. by at most 2^-24 |out[b]|.  A call never uses more
+ *     than 1024 workgroups per batch item (larger maps have each workgroup
+ *     walk several tiles, summing in fp64 between them), so the atomic
+ *     rounding stays within 1024 x 2^-24 = 6.1e-5 |out[b]| at every shape
+ *     the ABI accepts: 96 partials per item for x[128,8,384,384] (box-sum),
+ *     1024 for an item of 5e8 input elements.  The deterministic form adds
+ *     the same partials in a fixed order.
  */
 #ifndef FCONV_H
 #define FCONV_H
@@ -68,13 +69,15 @@ extern "C" {
 #define FCONV_ALGO_AUTO 0
 #define FCONV_ALGO_DIRECT_MFMA 1   /* direct conv on fp32 matrix cores: s*s*Cin*K*K MACs per
                                       (co, pooled output); instances for K=3 with pool 2,3,4
-                                      and K=5 with pool 3 */
+                                      and K=5 with pool 3, where one workgroup's input tile
+                                      for all Cin fits LDS (K=3 pool 4: Cin <= 32) */
 #define FCONV_ALGO_DIRECT_SIMPLE 2 /* direct conv, one thread per pooled output, any shape */
 #define FCONV_ALGO_BOXSUM 3        /* pool-then-convolve: s x s box sums of the input, then
                                       Cin*K*K MACs per (co, pooled output) on matrix cores;
-                                      same instances as DIRECT_MFMA.  Pooling commutes with the
-                                      convolution (both are linear), so the result is the
-                                      same function of the inputs. */
+                                      K=3 with pool 2,3,4 and K=5 with pool 3, any Cin (the box
+                                      sums pass through LDS 8 or 16 channels at a time).
+                                      Pooling commutes with the convolution (both are linear),
+                                      so the result is the same function of the inputs. */
 
 /*
  * fconv2d_pool_sigmoid_sum
@@ -132,8 +135,9 @@ int fconv2d_pool_sigmoid_sum_det(const float* x, int64_t B, int64_t Cin, int64_t
                                  float* out, void* stream);
 
 /* Workspace bytes fconv2d_pool_sigmoid_sum_det needs for this shape and
- * algorithm (B * workgroups per batch item * 4; 0 if the pooled map is
- * empty).  Host only.  Errors as the call itself (NULL bytes: EINVAL). */
+ * algorithm (B * workgroups per batch item * 4, with at most 1024 workgroups
+ * per item: at most 4 KiB per batch item; 0 if the pooled map is empty).
+ * Host only.  Errors as the call itself (NULL bytes: EINVAL). */
 int fconv2d_pool_sigmoid_sum_det_workspace(int64_t B, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
                                            int64_t K, int64_t pool, int algo, size_t* bytes);
 
