@@ -21,6 +21,8 @@ FCONV_OK = 0
 FCONV_EINVAL = -1
 FCONV_EUNSUPPORTED = -2
 FCONV_EHIP = -3
+FCONV_ESCRATCH = -4
+NOALLOC_MAX_PARTIALS = 1 << 18
 
 ALGO_AUTO = 0
 ALGO_DIRECT_MFMA = 1
@@ -54,6 +56,8 @@ _SIGS = {
     "fconv2d_pool_sigmoid_sum_det": (
         [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, ctypes.c_size_t, _vp, _vp],
         ctypes.c_int),
+    "fconv2d_pool_sigmoid_sum_det_noalloc": (
+        [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
     "fconv2d_pool_sigmoid_sum_det_workspace": (
         [_i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "fconv2d_pool_out_size": ([_i64, _i64, _i64, _i64, _i64p, _i64p], ctypes.c_int),
@@ -225,6 +229,23 @@ def conv2d_pool_sigmoid_sum_det(x, w, b, pool: int, out=None, algo: int = ALGO_A
             rc = lib.fconv2d_pool_sigmoid_sum_det_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode,
                                                      flags, algo, _ptr(workspace), nbytes, _ptr(out), _stream(x))
     _check(rc, "fconv2d_pool_sigmoid_sum_det")
+    return out
+
+
+def conv2d_pool_sigmoid_sum_det_noalloc(x, w, b, pool: int, out, algo: int = ALGO_AUTO):
+    """The bitwise-reproducible sum with its partials in the library's fixed per-GPU array: no
+    allocation anywhere in the call (`out` must be given).  Calls that overlap in time on one GPU
+    race; see include/fconv.h."""
+    _conv2d_args(x, w, b)
+    B, Cin, H, W = x.shape
+    Cout, _, K, _ = w.shape
+    _dev_f32(out, "out")
+    if tuple(out.shape) != (B,) or out.device != x.device:
+        raise ValueError("out must be [B] on x's device")
+    with torch.cuda.device(x.device):
+        rc = lib.fconv2d_pool_sigmoid_sum_det_noalloc(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
+                                                      _ptr(out), _stream(x))
+    _check(rc, "fconv2d_pool_sigmoid_sum_det_noalloc")
     return out
 
 

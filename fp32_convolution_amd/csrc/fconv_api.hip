@@ -5,8 +5,16 @@
 #include <stdlib.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/fconv.h"
 #include "fconv_internal.hpp"
+
+// Partial sums of fconv2d_pool_sigmoid_sum_det_noalloc: a fixed device
+// array, one copy per GPU the library runs on, held until the process ends.
+// In host code `scratch` names a host-side stand-in; its device address comes
+// from hipGetSymbolAddress (scratch_ptr below), never from the name.
+static __device__ __align__(256) float scratch[FCONV_NOALLOC_MAX_PARTIALS];
 
 namespace {
 
@@ -205,6 +213,25 @@ int det_plan(int64_t B, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t
     return *parts < 0 ? FCONV_EUNSUPPORTED : FCONV_OK;
 }
 
+// The device address of `scratch` on the current device: looked up once per
+// device (with that device current) and kept.  nullptr if the lookup failed.
+constexpr int kMaxDevices = 64;
+float* scratch_ptr() {
+    static std::mutex mu;
+    static float* ptrs[kMaxDevices] = {};
+    static bool looked[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!looked[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        ptrs[dev] = (float*)p;
+        looked[dev] = true;
+    }
+    return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -308,6 +335,27 @@ int fconv2d_pool_sigmoid_sum_det(const float* x, int64_t B, int64_t Cin, int64_t
     return status_of(fconv::reduce_partials(ws, parts, s.B, out, st));
 }
 
+int fconv2d_pool_sigmoid_sum_det_noalloc(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
+                                         const float* w, int64_t Cout, int64_t K, const float* bias, int64_t pool,
+                                         int algo, float* out, void* stream) {
+    if (!x || !w || !out) return FCONV_EINVAL;
+    Conv2dShape s;
+    int a;
+    int64_t parts;
+    int rc = det_plan(B, Cin, H, W, Cout, K, pool, algo, &s, &a, &parts);
+    if (rc != FCONV_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (parts == 0) return status_of(fconv::fill_zero(out, s.B, st));
+    if (parts * s.B > FCONV_NOALLOC_MAX_PARTIALS) return FCONV_ESCRATCH;
+    float* ws = scratch_ptr();
+    if (!ws) return FCONV_EHIP;
+    // Every slot ws[0 .. B*parts) is written by the first kernel before the
+    // second reads it, so nothing needs clearing between calls.
+    hipError_t e = launch_conv2d(a, s, x, w, bias, ws, fconv::OUT_PARTIAL, st);
+    if (e != hipSuccess) return FCONV_EHIP;
+    return status_of(fconv::reduce_partials(ws, parts, s.B, out, st));
+}
+
 int fconv2d_pool_out_size(int64_t H, int64_t W, int64_t K, int64_t pool, int64_t* PH, int64_t* PW) {
     if (!PH || !PW || H < 1 || W < 1 || K < 1 || pool < 1 || H < K || W < K) return FCONV_EINVAL;
     *PH = (H - K + 1) / pool;
@@ -378,6 +426,7 @@ const char* fconv_strerror(int status) {
         case FCONV_EINVAL: return "invalid argument";
         case FCONV_EUNSUPPORTED: return "shape not supported by the requested algorithm";
         case FCONV_EHIP: return "HIP runtime error";
+        case FCONV_ESCRATCH: return "more partial sums than the fixed scratch array holds";
         default: return "unknown status";
     }
 }

@@ -62,6 +62,8 @@ extern "C" {
 #define FCONV_EINVAL (-1)      /* an argument failed a check; nothing was enqueued */
 #define FCONV_EUNSUPPORTED (-2) /* the requested algorithm cannot run this shape   */
 #define FCONV_EHIP (-3)        /* the HIP runtime reported an error              */
+#define FCONV_ESCRATCH (-4)    /* more partial sums than the fixed scratch holds (see
+                                  fconv2d_pool_sigmoid_sum_det_noalloc); nothing was enqueued */
 
 /* Algorithms for the Conv2d path.  All compute the same result up to fp32
  * rounding.  AUTO picks the fastest one that supports the shape: BOXSUM,
@@ -133,6 +135,31 @@ int fconv2d_pool_sigmoid_sum_det(const float* x, int64_t B, int64_t Cin, int64_t
                                  const float* w, int64_t Cout, int64_t K, const float* bias,
                                  int64_t pool, int algo, void* workspace, size_t workspace_bytes,
                                  float* out, void* stream);
+
+/*
+ * fconv2d_pool_sigmoid_sum_det_noalloc -- fconv2d_pool_sigmoid_sum_det with no
+ *   workspace argument, for callers that cannot allocate device memory: code
+ *   under HIP graph capture, tight serving loops, harnesses that forbid
+ *   hipMalloc.  The call allocates nothing (no hipMalloc, no allocating
+ *   library routine); its partial sums go to a fixed device array of
+ *   FCONV_NOALLOC_MAX_PARTIALS floats (1 MiB) inside the library, one per GPU,
+ *   held until the process ends.  Same kernels, same fixed-order reduction
+ *   and so the same bits as fconv2d_pool_sigmoid_sum_det.
+ *   Limit: B * (workgroups per batch item) <= FCONV_NOALLOC_MAX_PARTIALS
+ *   (the workspace query of fconv2d_pool_sigmoid_sum_det / 4 gives that
+ *   product; at most 1024 workgroups per item, so any shape with B <= 256
+ *   fits); beyond it the call returns FCONV_ESCRATCH and enqueues nothing.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in
+ *   time on one GPU (different streams, or different host threads without
+ *   ordering) race and give undefined results.  Calls ordered on one stream
+ *   are safe.  `stream` must belong to the current device.
+ *   FCONV_EHIP also if the array's device address cannot be obtained.
+ * Other arguments and errors as fconv2d_pool_sigmoid_sum_det.
+ */
+#define FCONV_NOALLOC_MAX_PARTIALS (1 << 18)
+int fconv2d_pool_sigmoid_sum_det_noalloc(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
+                                         const float* w, int64_t Cout, int64_t K, const float* bias,
+                                         int64_t pool, int algo, float* out, void* stream);
 
 /* Workspace bytes fconv2d_pool_sigmoid_sum_det needs for this shape and
  * algorithm (B * workgroups per batch item * 4, with at most 1024 workgroups
