@@ -16,6 +16,13 @@
 // per thread to out[blocks*256] so that no chain is dead code.  Inline
 // assembly pins the instruction (the compiler may neither fuse, pack nor
 // reorder the chains into something else).  Return 0 or -3 (launch error).
+//
+// HBM streaming rates, for kernels that only read (the box-sum Conv2d) or
+// mostly write (the depthwise-separable Conv1d's output):
+//   fconv_probe_read_f32: `blocks` workgroups of 256 threads read n4 16-byte
+//     words of `in` (grid-stride, coalesced) and write one sum per thread to
+//     out[blocks*256];
+//   fconv_probe_write_f32: the same grid writes n4 16-byte words to `dst`.
 #include <hip/hip_runtime.h>
 
 namespace {
@@ -52,9 +59,42 @@ __global__ __launch_bounds__(256) void fma_f32_rate_kernel(float* __restrict__ o
     out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+__global__ __launch_bounds__(256) void read_f32_rate_kernel(const float4* __restrict__ in, long n4,
+                                                             float* __restrict__ out) {
+    const long stride = (long)gridDim.x * 256;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        const float4 v = in[i];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    out[blockIdx.x * 256 + threadIdx.x] = (acc.x + acc.y) + (acc.z + acc.w);
+}
+
+__global__ __launch_bounds__(256) void write_f32_rate_kernel(float4* __restrict__ dst, long n4, float v) {
+    const long stride = (long)gridDim.x * 256;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) dst[i] = make_float4(v, v, v, v);
+}
+
 }  // namespace
 
 extern "C" {
+
+int fconv_probe_read_f32(int blocks, long n4, const float* in, float* out, void* stream) {
+    if (blocks < 1 || n4 < 1 || !in || !out) return -1;
+    hipLaunchKernelGGL(read_f32_rate_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const float4*)in, n4,
+                       out);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int fconv_probe_write_f32(int blocks, long n4, float* dst, void* stream) {
+    if (blocks < 1 || n4 < 1 || !dst) return -1;
+    hipLaunchKernelGGL(write_f32_rate_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (float4*)dst, n4,
+                       1.0f);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 int fconv_probe_mfma_f32(int blocks, int iters, float* out, void* stream) {
     if (blocks < 1 || iters < 1 || !out) return -1;

@@ -75,6 +75,14 @@ def test_ceiling_probe_library():
         assert fn(0, 10, FAKE, None) == -1
         assert fn(4, 0, FAKE, None) == -1
         assert fn(4, 10, None, None) == -1
+    probe.fconv_probe_read_f32.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+    probe.fconv_probe_write_f32.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p]
+    assert probe.fconv_probe_read_f32(0, 16, FAKE, FAKE, None) == -1
+    assert probe.fconv_probe_read_f32(4, 0, FAKE, FAKE, None) == -1
+    assert probe.fconv_probe_read_f32(4, 16, None, FAKE, None) == -1
+    assert probe.fconv_probe_write_f32(0, 16, FAKE, None) == -1
+    assert probe.fconv_probe_write_f32(4, 16, None, None) == -1
 
 
 def test_version_and_strerror(lib):
