@@ -435,8 +435,22 @@ struct BoxLayout {
     static constexpr int NCH = (Cfg::IW + 63) / 64;     // 64-column chunks of an input row
     static constexpr int NCS = (CS + 63) / 64;          // 64-column chunks of an Sx row
     static constexpr int QS = (CS + S - 1) / S;         // Sx slots per phase
-    static constexpr int RSS = S * QS;                  // Sx floats per row
-    static constexpr int SPLANE = RS * RSS;
+    // Lanes and banks.  With PATCH, block p's 16 lanes (l = 0..15) read the
+    // 4 x 4 patch of pooled positions (l / 4, 4p + l % 4) of the 4-row tile,
+    // and the Sx row stride RSS satisfies S * RSS = 4 (mod 64): the 16 lanes
+    // then read 16 consecutive LDS banks, and channel planes padded to 16
+    // (mod 64) put the four lane groups (four channels) on disjoint banks.
+    // PATCH needs a 4-row tile, a width that is a multiple of 4, and at most
+    // 16 floats of row padding; otherwise block p holds positions
+    // 16p .. 16p+15 in row order and RSS = S * QS.
+    static constexpr int rss_patch() {
+        for (int r = S * QS; r < S * QS + 64; ++r)
+            if ((S * r) % 64 == 4) return r;
+        return -1;
+    }
+    static constexpr bool PATCH = Cfg::TPH == 4 && Cfg::TPW % 4 == 0 && rss_patch() >= 0 && rss_patch() - S * QS <= 16;
+    static constexpr int RSS = PATCH ? rss_patch() : S * QS;  // Sx floats per row
+    static constexpr int SPLANE = PATCH ? RS * RSS + (80 - (RS * RSS) % 64) % 64 : RS * RSS;
     static constexpr int SCRATCH = NCH * 64;            // one vertical-sum row per wave
     static constexpr int CC = 2 * Cfg::NW;              // channels per LDS chunk: two per wave
     static constexpr int QC = CC / 4;                   // channel quads per chunk
@@ -474,6 +488,17 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
+    // The tile position (row py, column px) lane l16 holds in block p.
+    auto tile_pos = [&](int p, int& py, int& px) {
+        if constexpr (L::PATCH) {
+            py = l16 >> 2;
+            px = 4 * p + (l16 & 3);
+        } else {
+            const int j = p * 16 + l16;
+            py = j / TPW;
+            px = j - (j / TPW) * TPW;
+        }
+    };
     // Workgroup `part` of batch item b walks units part, part + parts, ...
     // (unit = channel range * tiles + tile).
     const int lid = xcd_spread(blockIdx.x, nblocks);
@@ -577,13 +602,13 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
         };
 
         // 3. contraction: B for lane (g, l16), block p, tap (ky, kx) and the
-        //    chunk's quad j is Sx[slot 4j + g][py*S + ky][px*S + kx] for
-        //    position j = p*16 + l16.
+        //    chunk's quad j is Sx[slot 4j + g][py*S + ky][px*S + kx] for the
+        //    lane's position (py, px) of block p.
         int pbase[P];
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            const int j = p * 16 + l16;
-            const int py = j / TPW, px = j - (j / TPW) * TPW;
+            int py, px;
+            tile_pos(p, py, px);
             pbase[p] = g * L::SPLANE + py * S * RSS + px;
         }
         floatx4 acc[CB][P];
@@ -676,8 +701,9 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
                     const bool cok = co < Cout;
 #pragma unroll
                     for (int p = 0; p < P; ++p) {
-                        const int j = p * 16 + l16;
-                        const int ph = ph0 + j / TPW, pw = pw0 + (j - (j / TPW) * TPW);
+                        int py, px;
+                        tile_pos(p, py, px);
+                        const int ph = ph0 + py, pw = pw0 + px;
                         if (cok && ph < PH && pw < PW) {
                             const float avg = acc[cb][p][r] * inv + bco[cb][r];
                             if constexpr (MODE == OUT_MAP)
