@@ -562,18 +562,39 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
         }
         const float* xb = x + (size_t)b * Cin * H * W;
         float* srow = scratch + wave * L::SCRATCH;
+        // Row r of channel ic: rows past the image and channels past Cin get
+        // an empty resource (their loads return 0 and touch no memory), so
+        // the row pointer needs no condition: one scalar add per row.
         auto load_rows = [&](float (&vv)[IH][NCH], int ic) {
+            const bool cok = ic < Cin;
+            const float* prow = xb + ((size_t)(cok ? ic : 0) * H + y0) * W;
 #pragma unroll
-            for (int r = 0; r < IH; ++r) {
-                const bool ok = (ic < Cin) && (y0 + r < H);
-                const buf_rsrc rrow = make_rsrc(xb + (ok ? (ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
+            for (int r = 0; r < IH; ++r, prow += W) {
+                const bool ok = cok && (y0 + r < H);
+                const buf_rsrc rrow = make_rsrc(prow, ok ? W * 4 : 0);
 #pragma unroll
                 for (int k = 0; k < NCH; ++k) vv[r][k] = buf_load_f32(rrow, voff[k]);
             }
         };
         // into LDS slot `slot` of the chunk
+        // With one 64-column chunk per row (NCH = 1) and s = 2 or 3, lane c
+        // takes its neighbours' vertical sums with DPP wave shifts, which fold
+        // into the adds: h = v + shl(v) for s = 2, h = v + shl(v + shl(v))
+        // for s = 3.  Otherwise they go through the wave's LDS scratch row.
+        constexpr bool DPP_H = NCH == 1 && (S == 2 || S == 3);
         auto sum_rows = [&](float (&vv)[IH][NCH], int slot) {
             float* splane = Sb + slot * L::SPLANE;
+            if constexpr (DPP_H) {
+#pragma unroll
+                for (int r = 0; r < RS; ++r) {
+                    float v = vv[r][0];
+#pragma unroll
+                    for (int dy = 1; dy < S; ++dy) v += vv[r + dy][0];
+                    const float h = S == 2 ? v + wave_shl1(v) : v + wave_shl1(v + wave_shl1(v));
+                    if (lane < CS) splane[r * RSS + soff[0]] = h;
+                }
+                return;
+            }
 #pragma unroll
             for (int r = 0; r < RS; ++r) {
                 // The fences keep the compiler from moving this row's reads
@@ -612,15 +633,25 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
             pbase[p] = g * L::SPLANE + py * S * RSS + px;
         }
         floatx4 acc[CB][P];
+        // Each quad's reads come off base registers the compiler cannot
+        // relate to one another, so that paired LDS reads take their taps
+        // and blocks as immediate offsets (with PATCH one base: block p is 4p
+        // words on, and a quad's reads span under 256 words) instead of an
+        // address add per pair.
         auto contract = [&](const float (&a)[K * K][CB], int jq) {
             const int lq = 4 * jq * L::SPLANE;
+            lds_fptr qb[P];
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                qb[p] = L::PATCH ? (p == 0 ? lds_opaque((lds_fptr)lds + pbase[0] + lq) : qb[0] + 4 * p)
+                                 : lds_opaque((lds_fptr)lds + pbase[p] + lq);
 #pragma unroll
             for (int ky = 0; ky < K; ++ky)
 #pragma unroll
                 for (int kx = 0; kx < K; ++kx) {
                     float bv[P];
 #pragma unroll
-                    for (int p = 0; p < P; ++p) bv[p] = Sb[pbase[p] + lq + ky * RSS + (kx % S) * QS + kx / S];
+                    for (int p = 0; p < P; ++p) bv[p] = qb[p][ky * RSS + (kx % S) * QS + kx / S];
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -820,11 +851,15 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
 
         const int xc = x0 + 4 * lane;
         const int coff = (lane <= TPW && xc < W) ? xc * 4 : kBufOOB;
+        // rows past the image and channels past Cin get an empty resource
+        // (their loads return 0), so the row pointer needs no condition
         auto load_rows = [&](floatx4 (&v)[IR], int ic) {
+            const bool cok = ic < Cin;
+            const float* prow = xb + ((size_t)(cok ? ic : 0) * H + y0) * W;
 #pragma unroll
-            for (int r = 0; r < IR; ++r) {
-                const bool ok = ic < Cin && y0 + r < H;
-                const buf_rsrc rr = make_rsrc(xb + (ok ? ((size_t)ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
+            for (int r = 0; r < IR; ++r, prow += W) {
+                const bool ok = cok && y0 + r < H;
+                const buf_rsrc rr = make_rsrc(prow, ok ? W * 4 : 0);
                 if constexpr (VEC) {
                     v[r] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rr, coff, 0, 0));
                 } else {
@@ -833,13 +868,9 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
                 }
             }
         };
-        // the value of lane + 1 (wave_shl:1; lane 63, whose value no stored
-        // sum uses, reads 0 through the bound control, so the move needs no
-        // zeroed old value)
-        auto next_lane = [](float v) {
-            return __builtin_bit_cast(float,
-                                      __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x130, 0xF, 0xF, true));
-        };
+        // the value of lane + 1 (lane 63, whose value no stored sum uses,
+        // reads 0)
+        auto next_lane = [](float v) { return wave_shl1(v); };
         // A of step (m, tap) for lane (g, l16) is w[co][4m + g][tap], co = this
         // wave's channel l16; 0 past Cin, past Cout and for m >= CINQ.
         const int co_a = co_w + l16;
@@ -856,9 +887,7 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
         floatx4 acc[NB];
 
         // Box sums of this wave's channel of quad c*CQ + j into LDS slot
-        // 4j + wave.  Loads return in issue order, so when the next chunk's
-        // rows are prefetched, the chunk's weights load before them (at the
-        // chunk's last quad); in the last chunk they load after the sums.
+        // 4j + wave.  The chunk's weights load after its box sums.
         auto load_chunk_a = [&](int c) {
 #pragma unroll
             for (int jj = 0; jj < CQ; ++jj) load_a(a[jj], c * CQ + jj);
@@ -879,10 +908,11 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
 #pragma unroll
                     for (int ky = 0; ky < 3; ++ky) vs[ph][ky][cc] = p[ph * S + ky] + p[ph * S + ky + 2];
             }
-            if (i + 1 < nq) {
-                if (j == CQ - 1) load_chunk_a(c);
-                load_rows(v, ic + NW);
-            }
+            // within a chunk the next channel's rows load now, under this
+            // channel's sums; the next chunk's first rows load when that chunk
+            // starts (a prefetch across the contraction kept them live
+            // together with the accumulators and spilled registers)
+            if (j < CQ - 1 && i + 1 < nq) load_rows(v, ic + NW);
             float* sp = lds + (size_t)(4 * j + wave) * Box4::CPLANE + lane;
 #pragma unroll
             for (int ph = 0; ph < TPH; ++ph) {
@@ -924,7 +954,7 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
         auto chunk = [&](int c, auto first_tag) {
 #pragma unroll
             for (int j = 0; j < CQ; ++j) box_sums(c, j);
-            if ((c + 1) * CQ >= nq) load_chunk_a(c);
+            load_chunk_a(c);
             __syncthreads();
             quad(a[0], 0, first_tag);
 #pragma unroll
@@ -936,6 +966,7 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
             const int nchunks = (nq + CQ - 1) / CQ;
             for (int c = 1; c < nchunks; ++c) {
                 __syncthreads();  // the last chunk's box sums are read
+                load_rows(v, 4 * c * CQ + wave);
                 chunk(c, std::false_type{});
             }
         }

@@ -95,6 +95,12 @@ __device__ __forceinline__ float row_shr2(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x112, 0xF, 0xF, true));
 }
 
+// DPP wave shift: lane l reads lane l+1 of the wave (wave_shl:1); lane 63
+// reads 0 through the bound control, so the move needs no zeroed old value.
+__device__ __forceinline__ float wave_shl1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x130, 0xF, 0xF, true));
+}
+
 // Logistic sigmoid 1/(1+e^-a) with the hardware exp2 (v_exp_f32) and
 // reciprocal: relative error a few ulp for |a| < 80, exactly 1/2 at a = 0,
 // saturating to 0 or 1 (never NaN) for large |a|.

@@ -23,7 +23,10 @@ struct DwsepShape {
 // of |out[b]|, whatever the map size.  A map with more units of work (tiles x
 // output-channel ranges) than that has each workgroup walk several units,
 // part, part + parts, ..., summing its lanes' sigmoids in fp64 between units.
-constexpr int kMaxPartsPerItem = 1024;
+#ifndef FCONV_MAX_PARTS_PER_ITEM
+#define FCONV_MAX_PARTS_PER_ITEM 1024
+#endif
+constexpr int kMaxPartsPerItem = FCONV_MAX_PARTS_PER_ITEM;
 inline int walk_parts(int64_t units) { return units < kMaxPartsPerItem ? (int)units : kMaxPartsPerItem; }
 
 // What a Conv2d kernel writes: the fused sums (one float atomic per
