@@ -56,7 +56,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # channel quads with weights resident in registers (0: streamed), whether
 # each workgroup walks several tiles>.
 KERNEL_SOURCES = {
-    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3>, 2, 0, 2, false>": [
+    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3, false>, 2, 0, 2, false>": [
         "fp32_convolution_amd/csrc/conv2d_pool_ex.hip", "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_tall_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                           "fp32_convolution_amd/csrc/fconv_device.hpp"],
@@ -66,15 +66,15 @@ KERNEL_SOURCES = {
         "fp32_convolution_amd/csrc/conv2d_pool.hip", "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_dense_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                            "fp32_convolution_amd/csrc/fconv_device.hpp"],
-    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 1, 0, 2, false>": [
+    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4, false>, 1, 0, 2, false>": [
         "fp32_convolution_amd/csrc/conv2d_pool_ex.hip", "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "conv2d_pool_mfma_kernel<fconv::DirectCfg<5, 3, 1, 3, 8, 1, 4, 12>, 0, false>": [
         "fp32_convolution_amd/csrc/conv2d_pool.hip", "fp32_convolution_amd/csrc/fconv_device.hpp"],
 }
 
 
-ELEM_AVG = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3>, 2, 0, 2, false>"
-ELEM_MAX = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4>, 1, 0, 2, false>"
+ELEM_AVG = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3, false>, 2, 0, 2, false>"
+ELEM_MAX = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4, false>, 1, 0, 2, false>"
 TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace.json")
 
 
@@ -561,6 +561,32 @@ def main():
             f_tail, b_tail, "Conv2d k5 -> ReLU -> MaxPool2d 3 (floor) -> sigmoid -> sum on " + TAIL
             + ", per-conv-output MFMA kernel (K = 5, s = 3 instance)"),
     }
+    # Cin 64: past the whole-tile LDS budget of the direct kernels, so DIRECT_MFMA runs the per-conv-output
+    # kernel's channel-chunked tiling; AUTO runs box-sum (8-channel LDS chunks)
+    wc = dict(B=16, Cin=64, H=384, W=384, Cout=64, K=3, pool=4)
+    wide_host = fi.conv2d_inputs(wc["B"], wc["Cin"], wc["H"], wc["W"], wc["Cout"], wc["K"], seed=11)
+    xw, ww, bw = (torch.from_numpy(a).to(dev) for a in wide_host)
+    ow = {k: torch.empty(wc["B"], device=dev) for k in ("auto", "direct", "max")}
+    wide_desc = "x[16,64,384,384] Conv2d 64->64 k3 -> "
+    f_wide, b_wide = conv2d_flops(wc), conv2d_bytes(wc)
+    bw_bound = "mfma" if conv2d_boxsum_flops(wc) / b_wide > PEAK_FP32_TFLOPS * 1e3 / PEAK_HBM_GBPS else "hbm"
+    variants["fconv2d_pool_sigmoid_sum_cin64"] = variant(
+        lambda: fc.conv2d_pool_sigmoid_sum(xw, ww, bw, wc["pool"], out=ow["auto"]),
+        conv2d_boxsum_flops(wc), b_wide, "AUTO (box-sum, 8-channel LDS chunks) on " + wide_desc
+        + "AvgPool2d 4 -> sigmoid -> sum, own FLOPs Cin*K*K per (co, pooled output)", bound=bw_bound)
+    variants["fconv2d_pool_sigmoid_sum_cin64_direct"] = variant(
+        lambda: fc.conv2d_pool_sigmoid_sum(xw, ww, bw, wc["pool"], out=ow["direct"], algo=fc.ALGO_DIRECT_MFMA),
+        f_wide, b_wide, "direct MFMA, channel-chunked per-conv-output kernel (folded average pool) on "
+        + wide_desc + "AvgPool2d 4 -> sigmoid -> sum")
+    variants["fconv2d_pool_sigmoid_sum_ex_relu_maxpool_cin64"] = variant(
+        lambda: fc.conv2d_pool_sigmoid_sum(xw, ww, bw, wc["pool"], out=ow["max"], algo=fc.ALGO_DIRECT_MFMA,
+                                           pool_mode=fc.POOL_MAX, relu=True),
+        f_wide, b_wide, "channel-chunked per-conv-output kernel on " + wide_desc
+        + "ReLU -> MaxPool2d 4 (floor) -> sigmoid -> sum")
+    torch.cuda.synchronize()
+    wide_out = {k: v.cpu().numpy().astype(np.float64) for k, v in ow.items()}
+    del xw, ww, bw, ow
+
     y_dense = torch.empty_like(y)
     variants["dwsep_conv1d_dense"] = variant(
         lambda: fc.dwsep_conv1d(xd, wdw, wpw, bpw, dc["pad"], out=y_dense, algo=fc.DWSEP_DENSE),
@@ -715,6 +741,20 @@ def main():
                     parity_ok &= r <= 1.0
             par["oracle_gflops"] = round(configs[name]["algorithmic_gflop"] / t, 3)
             configs[name]["parity"] = par
+        # the Cin-64 variants on their first and last batch items
+        items = [0, wc["B"] - 1]
+        t0 = time.perf_counter()
+        want_avg = oracle.conv2d_pool_sigmoid_sum(*wide_host, wc["pool"], batch_idx=items, nthreads=threads)
+        want_max = oracle.conv2d_pool_sigmoid_sum(*wide_host, wc["pool"], batch_idx=items, nthreads=threads,
+                                                  pool_mode=oracle.POOL_MAX, relu=True)
+        t_wide = time.perf_counter() - t0
+        for key, got, want in (("fconv2d_pool_sigmoid_sum_cin64", "auto", want_avg),
+                               ("fconv2d_pool_sigmoid_sum_cin64_direct", "direct", want_avg),
+                               ("fconv2d_pool_sigmoid_sum_ex_relu_maxpool_cin64", "max", want_max)):
+            r = err_over_tol(wide_out[got][items], want)
+            variants[key]["parity"] = {"max_err_over_tol": r, "checked": f"batch items {items}, every output",
+                                       "oracle_s_both_pools": round(t_wide, 3)}
+            parity_ok &= r <= 1.0
         t_sample = t_base[CONV] + t_base[DW]
         result["cpu_baseline"] = {
             "value": round((f_conv + f_dw) / t_sample / 1e9, 3),
@@ -729,7 +769,8 @@ def main():
         }
         result["parity_sample"] = {"ok": bool(parity_ok),
                                    "what": "every workload's default call (and direct call for the Conv2d ones) "
-                                           "against the oracle on all batch items, |err| / (1e-4 + 1e-4 |oracle|)"}
+                                           "against the oracle on all batch items, and the Cin-64 variants on two, "
+                                           "|err| / (1e-4 + 1e-4 |oracle|)"}
     else:
         result["cpu_baseline"] = None
 

@@ -303,14 +303,22 @@ static size_t lds_bytes_for(int Cin) {
 
 static constexpr size_t kMaxLds = 160 * 1024 - 256;  // dynamic share; the rest holds the reduction slots
 
-bool conv2d_mfma_supported(int Cin, int K, int S) {
+// The pool-folded direct kernel takes (Cin, K, S): its instance exists and
+// one workgroup's tile of all Cin channels fits LDS.
+static bool direct_fits(int Cin, int K, int S) {
     size_t bytes = 0;
-    if (K == 3 && S == 4) return conv2d_elem_supported(Cin, K, S);
     if (K == 5 && S == 3) bytes = lds_bytes_for<CfgK5S3>(Cin);
     else if (K == 3 && S == 2) bytes = lds_bytes_for<CfgK3S2>(Cin);
     else if (K == 3 && S == 3) bytes = lds_bytes_for<CfgK3S3>(Cin);
     else return false;
     return bytes <= kMaxLds;
+}
+
+// Direct MFMA: K3/s4 runs on the per-conv-output kernel; K5/s3, K3/s2 and
+// K3/s3 on the pool-folded kernel while its tile fits, else on the
+// per-conv-output kernel's channel-chunked tiling (any Cin).
+bool conv2d_mfma_supported(int Cin, int K, int S) {
+    return direct_fits(Cin, K, S) || conv2d_elem_supported(Cin, K, S);
 }
 
 // Instantiates a kernel template for the three output modes and launches
@@ -390,7 +398,8 @@ static hipError_t launch_direct(const Conv2dShape& s, const float* x, const floa
 
 hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float* w, const float* bias,
                               float* dst, int mode, hipStream_t stream) {
-    if (s.K == 3 && s.S == 4) return conv2d_elem_launch(s, x, w, bias, dst, mode, PoolOpts{false, false, false}, stream);
+    if (!direct_fits(s.Cin, s.K, s.S))
+        return conv2d_elem_launch(s, x, w, bias, dst, mode, PoolOpts{false, false, false}, stream);
     if (s.K == 5 && s.S == 3) return launch_direct<CfgK5S3>(s, x, w, bias, dst, mode, stream);
     if (s.K == 3 && s.S == 2) return launch_direct<CfgK3S2>(s, x, w, bias, dst, mode, stream);
     if (s.K == 3 && s.S == 3) return launch_direct<CfgK3S3>(s, x, w, bias, dst, mode, stream);
@@ -398,7 +407,7 @@ hipError_t conv2d_mfma_launch(const Conv2dShape& s, const float* x, const float*
 }
 
 int64_t conv2d_mfma_parts(const Conv2dShape& s) {
-    if (s.K == 3 && s.S == 4) return conv2d_elem_parts(s, PoolOpts{false, false, false});
+    if (!direct_fits(s.Cin, s.K, s.S)) return conv2d_elem_parts(s, PoolOpts{false, false, false});
     if (s.K == 5 && s.S == 3) return direct_walk<CfgK5S3>(s).parts;
     if (s.K == 3 && s.S == 2) return direct_walk<CfgK3S2>(s).parts;
     if (s.K == 3 && s.S == 3) return direct_walk<CfgK3S3>(s).parts;
@@ -450,8 +459,16 @@ struct BoxLayout {
     }
     static constexpr bool PATCH = Cfg::TPH == 4 && Cfg::TPW % 4 == 0 && rss_patch() >= 0 && rss_patch() - S * QS <= 16;
     static constexpr int RSS = PATCH ? rss_patch() : S * QS;  // Sx floats per row
-    static constexpr int SPLANE = PATCH ? RS * RSS + (80 - (RS * RSS) % 64) % 64 : RS * RSS;
-    static constexpr int SCRATCH = NCH * 64;            // one vertical-sum row per wave
+    // channel planes 16 or 48 (mod 64) apart: either puts the four lane
+    // groups on four disjoint 16-bank sets; the nearer one is taken
+    static constexpr int pad_to(int n, int m) { return (m - n % 64 + 64) % 64; }
+    static constexpr int SPLANE =
+        PATCH ? RS * RSS + (pad_to(RS * RSS, 16) < pad_to(RS * RSS, 48) ? pad_to(RS * RSS, 16) : pad_to(RS * RSS, 48))
+              : RS * RSS;
+    // horizontal sums by DPP wave shifts (one 64-column chunk per row, s = 2
+    // or 3), else through one vertical-sum row of LDS per wave
+    static constexpr bool DPP_H = NCH == 1 && (S == 2 || S == 3);
+    static constexpr int SCRATCH = DPP_H ? 0 : NCH * 64;
     static constexpr int CC = 2 * Cfg::NW;              // channels per LDS chunk: two per wave
     static constexpr int QC = CC / 4;                   // channel quads per chunk
     static_assert(Cfg::WPOS == 1, "box-sum waves split output channels only");
@@ -463,9 +480,12 @@ struct BoxLayout {
 // fit a CU instead of 2: 0.398 against 0.434 ms on x[64,16,257,257] (0.412
 // with 73 VGPRs when its weight buffers were copied rather than alternated);
 // at 64 VGPRs (4 workgroups) its spills made it 0.467 ms.
+#ifndef FCONV_BOX_K5S3_MIN_WAVES
+#define FCONV_BOX_K5S3_MIN_WAVES 6
+#endif
 template <class Cfg>
 constexpr int box_min_waves() {
-    return Cfg::K == 5 && Cfg::S == 3 ? 6 : 1;
+    return Cfg::K == 5 && Cfg::S == 3 ? FCONV_BOX_K5S3_MIN_WAVES : 1;
 }
 
 template <class Cfg, int MODE, bool WALK>
@@ -581,7 +601,7 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
         // takes its neighbours' vertical sums with DPP wave shifts, which fold
         // into the adds: h = v + shl(v) for s = 2, h = v + shl(v + shl(v))
         // for s = 3.  Otherwise they go through the wave's LDS scratch row.
-        constexpr bool DPP_H = NCH == 1 && (S == 2 || S == 3);
+        constexpr bool DPP_H = L::DPP_H;
         auto sum_rows = [&](float (&vv)[IH][NCH], int slot) {
             float* splane = Sb + slot * L::SPLANE;
             if constexpr (DPP_H) {

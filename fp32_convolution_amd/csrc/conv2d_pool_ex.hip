@@ -111,9 +111,13 @@ int64_t conv2d_general_parts(const Conv2dShape& s) { return walk_parts(general_u
 // block is the MFMA's 16 lanes of N: WPB = 16/S whole windows, CPB = WPB*S
 // conv columns (for s = 3 the 16th lane's column belongs to no window of its
 // block and is ignored).
-template <int K_, int S_, int NCB_, int TPH_>
+template <int K_, int S_, int NCB_, int TPH_, bool CHUNK_ = false>
 struct ElemCfg {
     static constexpr int K = K_, S = S_, NCB = NCB_, TPH = TPH_;
+    // CHUNK: the channels pass through LDS CQ quads at a time (any Cin);
+    // otherwise all of a tile's channels are staged at once
+    static constexpr bool CHUNK = CHUNK_;
+    static constexpr int CQ = 4;
     static constexpr int WPB = 16 / S;                 // windows per column block
     static constexpr int CPB = WPB * S;                // conv columns per column block
     static constexpr int TPW = NCB * WPB;              // pooled columns per tile
@@ -135,6 +139,13 @@ using ElemK3S4Fold = ElemCfg<3, 4, 4, 3>;  // 3 x 16 pooled tile, 14 x 66 input
 using ElemK3S2 = ElemCfg<3, 2, 4, 4>;  // 4 x 32 pooled tile, 10 x 66 input
 using ElemK3S3 = ElemCfg<3, 3, 4, 4>;  // 4 x 20 pooled tile, 14 x 63 input
 using ElemK5S3 = ElemCfg<5, 3, 2, 4>;  // 4 x 10 pooled tile, 16 x 35 input
+// Channel-chunked instances for Cin beyond the staged tiles above: one pooled
+// row per tile, so that one row's accumulators carry over the chunks, and 16
+// channels per LDS chunk (17-26 KB).
+using ElemK3S4C = ElemCfg<3, 4, 4, 1, true>;
+using ElemK3S2C = ElemCfg<3, 2, 4, 1, true>;
+using ElemK3S3C = ElemCfg<3, 3, 4, 1, true>;
+using ElemK5S3C = ElemCfg<5, 3, 2, 1, true>;
 
 // POOL: kPoolMean (each conv output kept, then averaged), kPoolMax, or
 // kPoolMeanFolded: the average pool of a plain conv (no ReLU, floor mode),
@@ -188,11 +199,13 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
         const int ph0 = tile_y * TPH, pw0 = tile_x * TPW;
         const int co0 = cor * C::CO_RANGE + wave * 16;
 
-        // Weights of channel quad q: a[ky][kx] = w[co0 + l16, g*CINQ + q, ky, kx]
-        // (0 where co or ic is out of range).
+        // Weights of channel quad q: a[ky][kx] = w[co0 + l16, ic, ky, kx] with
+        // ic = g*CINQ + q (whole tiles staged: lane group g walks its own
+        // channel range) or ic = 4q + g (chunked: a quad is 4 consecutive
+        // channels); 0 where co or ic is out of range.
         const buf_rsrc rw = make_rsrc(w, Cout * Cin * K * K * 4);
         auto load_a = [&](float (&a)[K][K], int q) {
-            const int ic = g * CINQ + q;
+            const int ic = C::CHUNK ? 4 * q + g : g * CINQ + q;
             const int co = co0 + l16;
             const bool ok = (co < Cout) && (ic < Cin) && (q < CINQ);
             const int base = ok ? (co * Cin + ic) * (K * K * 4) : kBufOOB;
@@ -216,12 +229,13 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
             bco[r] = buf_load_f32(rb, co < Cout ? co * 4 : kBufOOB);
         }
 
-        // Stage the input tile: channel ic at ic*plane, row r at r*RP, column c at
-        // c.  Whole rows per wave through a per-row buffer resource (empty for
-        // rows outside the image and channels >= Cin, which therefore read 0).
-        {
+        // Stage the input tile: channels chan0 .. chan0+nchan-1 (slot s =
+        // ic - chan0 at s*plane), row r at r*RP, column c at c.  Whole rows per
+        // wave through a per-row buffer resource (empty for rows outside the
+        // image and channels >= Cin, which therefore read 0).
+        auto stage = [&](int chan0, int nchan) {
             constexpr int NCH = (IW + 63) / 64;
-            constexpr int UR = 14;  // rows in flight per wave
+            constexpr int UR = C::CHUNK ? 6 : 14;  // rows in flight per wave
             int voff[NCH];
             bool inr[NCH];
 #pragma unroll
@@ -231,42 +245,47 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
                 voff[k] = (c < IW && x0 + c < W) ? (x0 + c) * 4 : kBufOOB;
             }
             const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-            const int nrows = 4 * CINQ * IH;
+            const int nrows = nchan * IH;
             const float* xb = x + (size_t)b * Cin * H * W;
             for (int row0 = wave_s; row0 < nrows; row0 += C::NW * UR) {
                 float v[UR][NCH];
 #pragma unroll
-                for (int u = 0; u < UR; ++u) {
-                    const int row = row0 + u * C::NW;
-                    const int ic = row / IH, r = row - (row / IH) * IH;
+                for (int uu = 0; uu < UR; ++uu) {
+                    const int row = row0 + uu * C::NW;
+                    const int ic = chan0 + row / IH, r = row - (row / IH) * IH;
                     const bool ok = (row < nrows) && (ic < Cin) && (y0 + r < H);
                     const buf_rsrc rrow = make_rsrc(xb + (ok ? (ic * H + y0 + r) * W : 0), ok ? W * 4 : 0);
 #pragma unroll
-                    for (int k = 0; k < NCH; ++k) v[u][k] = buf_load_f32(rrow, voff[k]);
+                    for (int k = 0; k < NCH; ++k) v[uu][k] = buf_load_f32(rrow, voff[k]);
                 }
 #pragma unroll
-                for (int u = 0; u < UR; ++u) {
-                    const int row = row0 + u * C::NW;
+                for (int uu = 0; uu < UR; ++uu) {
+                    const int row = row0 + uu * C::NW;
                     if (row < nrows) {
-                        const int ic = row / IH, r = row - (row / IH) * IH;
-                        float* lrow = lds + ic * plane + r * RP;
+                        const int sl = row / IH, r = row - (row / IH) * IH;
+                        float* lrow = lds + sl * plane + r * RP;
 #pragma unroll
                         for (int k = 0; k < NCH; ++k)
-                            if (inr[k]) lrow[lane + 64 * k] = v[u][k];
+                            if (inr[k]) lrow[lane + 64 * k] = v[uu][k];
                     }
                 }
             }
-        }
+        };
+        if constexpr (C::CHUNK)
+            stage(0, 4 * min(C::CQ, CINQ));
+        else
+            stage(0, 4 * CINQ);
         __syncthreads();
 
         // A column block's lanes read 16 consecutive words; the 4 channel groups
-        // sit plane*CINQ words apart (padded onto different banks).  Rows of one
+        // sit plane*CINQ (chunked: plane) words apart (padded onto different
+        // banks).  Rows of one
         // pooled row read from two base registers: rows 0 .. RG-1 from the
         // first, the rest from a second one RG rows further on, so that every
         // read keeps within the 8-bit dword offsets of paired LDS reads.
         constexpr int RG = (255 - (NCB - 1) * CPB - (K - 1)) / RP + 1;
         static_assert(RG >= 1 && NR <= 2 * RG, "two base registers reach every row");
-        const lds_fptr lbase = (lds_fptr)lds + g * CINQ * plane + l16;
+        const lds_fptr lbase = (lds_fptr)lds + g * (C::CHUNK ? 1 : CINQ) * plane + l16;
         // NBA (a compile-time tag): the column blocks the tile computes.
         auto load_row = [&](float (&bv)[NCB][K], lds_fptr row, auto nba) {
 #pragma unroll
@@ -288,7 +307,8 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
         auto mma_quad = [&](const float (&aq)[K][K], int q, int pr, auto first_tag, auto nba) {
             constexpr bool FIRST = decltype(first_tag)::value;
             constexpr int NBA = decltype(nba)::value;
-            const lds_fptr p0 = lbase + q * plane + pr * S * RP;
+            // quad q's channels: slot q (whole tile) or 4 (q % CQ) (chunked)
+            const lds_fptr p0 = lbase + (C::CHUNK ? 4 * (q % C::CQ) : q) * plane + pr * S * RP;
             const lds_fptr p1 = NR > RG ? lds_opaque(p0 + RG * RP) : p0;
             auto row = [&](int rr) { return rr < RG ? p0 + rr * RP : p1 + (rr - RG) * RP; };
             float bcur[NCB][K], bnxt[NCB][K];
@@ -448,6 +468,19 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
             if constexpr (NQ > 0) {
                 mma_quad(a[0], 0, pr, std::true_type{}, nba);
                 if constexpr (NQ == 2) mma_quad(a[1], 1, pr, std::false_type{}, nba);
+            } else if constexpr (C::CHUNK) {
+                // one pooled row per tile: every CQ quads, the next chunk of
+                // channels replaces the last one in LDS
+                static_assert(TPH == 1, "a chunked tile is one pooled row");
+                quad_stream(0, pr, std::true_type{}, nba);
+                for (int q = 1; q < CINQ; ++q) {
+                    if (q % C::CQ == 0) {
+                        __syncthreads();  // every wave is done with the last chunk
+                        stage(4 * q, 4 * min(C::CQ, CINQ - q));
+                        __syncthreads();
+                    }
+                    quad_stream(q, pr, std::false_type{}, nba);
+                }
             } else {
                 quad_stream(0, pr, std::true_type{}, nba);
                 for (int q = 1; q < CINQ; ++q) quad_stream(q, pr, std::false_type{}, nba);
@@ -502,9 +535,10 @@ namespace {
 constexpr size_t kMaxLdsEx = 160 * 1024 - 256;
 
 // Channel planes padded so that the 4 channel groups (plane*CINQ words
-// apart) start 16 banks apart.
+// apart; chunked: plane words) start 16 banks apart.
 template <class C>
 int elem_plane(int CINQ) {
+    if (C::CHUNK) CINQ = 1;
     const int base = C::IH * C::RP;
     for (int pad = 0; pad < 64; ++pad)
         if (((long)CINQ * (base + pad)) % 64 == 16) return base + pad;
@@ -513,10 +547,16 @@ int elem_plane(int CINQ) {
     return base;
 }
 
+// The channel slots a workgroup stages at once: all quads, or one chunk.
+template <class C>
+int elem_slots(int CINQ) {
+    return 4 * (C::CHUNK ? (CINQ < C::CQ ? CINQ : C::CQ) : CINQ);
+}
+
 template <class C>
 size_t elem_lds_bytes(int Cin) {
     const int CINQ = (Cin + 3) / 4;
-    return (size_t)4 * CINQ * elem_plane<C>(CINQ) * sizeof(float);
+    return (size_t)elem_slots<C>(CINQ) * elem_plane<C>(CINQ) * sizeof(float);
 }
 
 // The plain average pool (no ReLU, floor mode) runs folded.
@@ -542,7 +582,7 @@ hipError_t launch_elem_w(const Conv2dShape& s, const float* x, const float* w, c
                          const PoolOpts& o, hipStream_t stream) {
     const int CINQ = (s.Cin + 3) / 4;
     const int plane = elem_plane<C>(CINQ);
-    const size_t lds = (size_t)4 * CINQ * plane * sizeof(float);
+    const size_t lds = (size_t)elem_slots<C>(CINQ) * plane * sizeof(float);
     const ElemGrid g = elem_grid<C>(s);
     const int nblocks = g.parts * s.B;  // at most 1024 * 65535
     const void* fn = (const void*)conv2d_pool_elem_kernel<C, POOL, MODE, NQ, WALK>;
@@ -568,8 +608,10 @@ template <class C, int POOL, int MODE>
 hipError_t launch_elem_as(const Conv2dShape& s, const float* x, const float* w, const float* bias, float* dst,
                           const PoolOpts& o, hipStream_t stream) {
     const int CINQ = (s.Cin + 3) / 4;
-    if (CINQ == 1) return launch_elem_nq<C, POOL, MODE, 1>(s, x, w, bias, dst, o, stream);
-    if (CINQ == 2) return launch_elem_nq<C, POOL, MODE, 2>(s, x, w, bias, dst, o, stream);
+    if constexpr (!C::CHUNK) {
+        if (CINQ == 1) return launch_elem_nq<C, POOL, MODE, 1>(s, x, w, bias, dst, o, stream);
+        if (CINQ == 2) return launch_elem_nq<C, POOL, MODE, 2>(s, x, w, bias, dst, o, stream);
+    }
     return launch_elem_nq<C, POOL, MODE, 0>(s, x, w, bias, dst, o, stream);
 }
 
@@ -602,32 +644,36 @@ hipError_t launch_elem_cfg(const Conv2dShape& s, const float* x, const float* w,
     return hipErrorInvalidValue;
 }
 
-// Calls f with a value of the instance's config type for (K, S) and the
-// pool variant; returns false if there is no instance.
+// Calls f with a value of the instance's config type for (K, S), the pool
+// variant and Cin: the whole-tile tiling where its LDS tile fits, else the
+// channel-chunked one; returns false if there is no instance.
+template <class Whole, class Chunked, class F>
+bool pick_elem(int Cin, F&& f) {
+    if (elem_lds_bytes<Whole>(Cin) <= kMaxLdsEx) return f(Whole{}), true;
+    return f(Chunked{}), true;
+}
 
 template <class F>
-bool with_elem_cfg(int K, int S, bool fold, F&& f) {
-    if (K == 3 && S == 4) return fold ? (f(ElemK3S4Fold{}), true) : (f(ElemK3S4{}), true);
-    if (K == 3 && S == 2) return f(ElemK3S2{}), true;
-    if (K == 3 && S == 3) return f(ElemK3S3{}), true;
-    if (K == 5 && S == 3) return f(ElemK5S3{}), true;
+bool with_elem_cfg(int K, int S, bool fold, int Cin, F&& f) {
+    if (K == 3 && S == 4)
+        return fold ? pick_elem<ElemK3S4Fold, ElemK3S4C>(Cin, f) : pick_elem<ElemK3S4, ElemK3S4C>(Cin, f);
+    if (K == 3 && S == 2) return pick_elem<ElemK3S2, ElemK3S2C>(Cin, f);
+    if (K == 3 && S == 3) return pick_elem<ElemK3S3, ElemK3S3C>(Cin, f);
+    if (K == 5 && S == 3) return pick_elem<ElemK5S3, ElemK5S3C>(Cin, f);
     return false;
 }
 
 }  // namespace
 
+// Every channel count: past the whole-tile LDS budget the chunked tiling runs.
 bool conv2d_elem_supported(int Cin, int K, int S) {
-    // the non-folded tiling is the larger one
-    size_t bytes = 0;
-    if (!with_elem_cfg(K, S, false, [&](auto c) { bytes = elem_lds_bytes<decltype(c)>(Cin); })) return false;
-    return bytes <= kMaxLdsEx;
+    return Cin >= 1 && ((K == 3 && (S == 2 || S == 3 || S == 4)) || (K == 5 && S == 3));
 }
+
 
 int64_t conv2d_elem_parts(const Conv2dShape& s, const PoolOpts& o) {
     int64_t parts = -1;
-    with_elem_cfg(s.K, s.S, folds(o), [&](auto c) {
-        parts = elem_grid<decltype(c)>(s).parts;
-    });
+    with_elem_cfg(s.K, s.S, folds(o), s.Cin, [&](auto c) { parts = elem_grid<decltype(c)>(s).parts; });
     return parts;
 }
 
@@ -635,7 +681,7 @@ hipError_t conv2d_elem_launch(const Conv2dShape& s, const float* x, const float*
                               int mode, const PoolOpts& o, hipStream_t stream) {
     if (!conv2d_elem_supported(s.Cin, s.K, s.S)) return hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
-    with_elem_cfg(s.K, s.S, folds(o),
+    with_elem_cfg(s.K, s.S, folds(o), s.Cin,
                   [&](auto c) { e = launch_elem_cfg<decltype(c)>(s, x, w, bias, dst, mode, o, stream); });
     return e;
 }

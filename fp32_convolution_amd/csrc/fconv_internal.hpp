@@ -60,8 +60,9 @@ int64_t conv2d_mfma_parts(const Conv2dShape& s);
 int64_t conv2d_boxsum_parts(const Conv2dShape& s);
 int64_t conv2d_simple_parts(const Conv2dShape& s);
 // Generalised-pool kernels (conv2d_pool_ex.hip).  `s.PH`, `s.PW` are the
-// pooled sizes under o.ceil_mode.  The matrix-core kernel has one instance
-// (K = 3, s = 4); the general kernel takes any shape.
+// pooled sizes under o.ceil_mode.  The matrix-core kernel has instances for
+// K = 3 with s = 2, 3, 4 and K = 5 with s = 3, any Cin (channel-chunked past
+// its whole-tile LDS budget); the general kernel takes any shape.
 bool conv2d_elem_supported(int Cin, int K, int S);
 int64_t conv2d_elem_parts(const Conv2dShape& s, const PoolOpts& o);
 int64_t conv2d_general_parts(const Conv2dShape& s);

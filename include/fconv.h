@@ -70,9 +70,10 @@ extern "C" {
  * else DIRECT_MFMA, else DIRECT_SIMPLE. */
 #define FCONV_ALGO_AUTO 0
 #define FCONV_ALGO_DIRECT_MFMA 1   /* direct conv on fp32 matrix cores: s*s*Cin*K*K MACs per
-                                      (co, pooled output); instances for K=3 with pool 2,3,4
-                                      and K=5 with pool 3, where one workgroup's input tile
-                                      for all Cin fits LDS (K=3 pool 4: Cin <= 32) */
+                                      (co, pooled output); K=3 with pool 2,3,4 and K=5 with
+                                      pool 3, any Cin: a workgroup stages all of its tile's
+                                      channels in LDS while they fit (up to Cin 32-68 by
+                                      shape), else 16 channels at a time */
 #define FCONV_ALGO_DIRECT_SIMPLE 2 /* direct conv, one thread per pooled output, any shape */
 #define FCONV_ALGO_BOXSUM 3        /* pool-then-convolve: s x s box sums of the input, then
                                       Cin*K*K MACs per (co, pooled output) on matrix cores;
@@ -220,9 +221,10 @@ int fconv2d_select_algo(int64_t Cin, int64_t Cout, int64_t K, int64_t pool);
  * fconv2d_pool_sigmoid_sum_ex -- the fused sum with the generalised pool.
  *   pool_mode  FCONV_POOL_AVG or FCONV_POOL_MAX
  *   flags      0 or an OR of FCONV_RELU, FCONV_CEIL_MODE
- *   algo       FCONV_ALGO_AUTO, DIRECT_MFMA (instances where the LDS tile
- *              fits: K = 3 with pool 4 (Cin <= 32), pool 2 (Cin <= 56) and
- *              pool 3 (Cin <= 40); K = 5 with pool 3 (Cin <= 68)),
+ *   algo       FCONV_ALGO_AUTO, DIRECT_MFMA (K = 3 with pool 2, 3, 4 and
+ *              K = 5 with pool 3, any Cin; whole-tile LDS staging up to
+ *              Cin 32 (K3, pool 4), 56 (pool 2), 40 (pool 3), 68 (K5,
+ *              pool 3), 16 channels at a time beyond),
  *              DIRECT_SIMPLE (any shape) or, only for
  *              FCONV_POOL_AVG with flags 0, BOXSUM.  AUTO picks DIRECT_MFMA
  *              where it has an instance, else DIRECT_SIMPLE (for the plain

@@ -226,8 +226,6 @@ def test_conv2d_ex_unsupported(lib):
     assert conv_ex(lib, pool_mode=0, flags=2, algo=3) == EUNSUP    # ... over full windows
     assert conv_ex(lib, K=5, pool=4, algo=1, H=16, W=16) == EUNSUP  # matrix-core instances: K3 s2-4, K5 s3
     assert conv_ex(lib, K=7, pool=2, algo=1, H=16, W=16) == EUNSUP
-    assert conv_ex(lib, Cin=300, pool=4, algo=1, H=16, W=16) == EUNSUP  # its LDS tile does not fit
-    assert conv(lib, Cin=300, pool=4, algo=1, H=16, W=16) == EUNSUP     # (the direct average-pool form too)
     assert conv_ex(lib, B=70000) == EUNSUP
 
 
@@ -244,6 +242,15 @@ def test_det_ex_workspace_query(lib):
         64 * 21 * 9 * 2 * 4
     # one-thread-per-output kernel: one workgroup per 256 pooled values of an item
     assert fc.conv2d_det_workspace_bytes(2, 3, 16, 16, 4, 3, 4, algo=2, pool_mode=fc.POOL_MAX) == 2 * 1 * 4
+    # past the whole-tile LDS budget (Cin 300) the channel-chunked tiling runs, 1 x 16 pooled tiles: a
+    # 3 x 3 map is 3 tiles per item, for every pool form and for the direct average-pool call
+    for pool_mode, relu in [(fc.POOL_MAX, False), (fc.POOL_AVG, True), (fc.POOL_AVG, False)]:
+        assert fc.conv2d_det_workspace_bytes(2, 300, 16, 16, 4, 3, 4, algo=1, pool_mode=pool_mode,
+                                             relu=relu) == 2 * 3 * 4
+    assert lib_det_bytes(lib, 2, 300, 16, 16, 4, 3, 4, 1) == 2 * 3 * 4
+    # K5/s3 at Cin 100 leaves the pool-folded kernel (largest whole tile: Cin 68) for the chunked tiling:
+    # 1 x 10 pooled tiles of a 4 x 4 map, 4 x 1 tiles and two channel ranges
+    assert lib_det_bytes(lib, 1, 100, 16, 16, 100, 5, 3, 1) == 1 * 4 * 2 * 4
     # floor mode, empty map -> 0; ceil mode has one pooled row there
     assert fc.conv2d_det_workspace_bytes(3, 2, 5, 9, 4, 3, 4, pool_mode=fc.POOL_MAX) == 0
     assert fc.conv2d_det_workspace_bytes(3, 2, 5, 9, 4, 3, 4, pool_mode=fc.POOL_MAX, ceil_mode=True) > 0

@@ -143,31 +143,25 @@ def largest_supported_cin(fc, K, s, H, W, algo):
 @pytest.mark.parametrize("K,s,wx", [(3, 4, 3), (3, 4, 1), (5, 3, 3), (3, 2, 3), (3, 3, 3)])
 @pytest.mark.parametrize("algo", [1, 3])
 def test_conv2d_largest_lds_tile(fc, K, s, wx, algo):
-    # each algorithm at the largest channel count it takes (support is contiguous in Cin: nothing larger is
-    # accepted), checked against the oracle; one channel more is refused.  The direct kernels hold every
-    # channel of a tile in LDS; box-sum stages 8 or 16 channels at a time and takes every channel count
-    # (here the query's upper end, 256, that is 32 or 16 chunks).  K3/s4 with wx = 1 has W % 4 == 0, which
-    # box-sum runs on its one-column-per-lane kernel.
+    # each algorithm at the largest channel count the query probes (256), checked against the oracle.
+    # Box-sum stages 8 or 16 channels at a time (32 or 16 chunks here); the direct kernels hold a whole
+    # tile's channels in LDS up to Cin 32-68 and past that run the per-conv-output kernel's channel-
+    # chunked tiling (16 channels per chunk).  K3/s4 with wx = 1 has W % 4 == 0, which box-sum runs on
+    # its one-column-per-lane kernel.
     H, W = 5 * s + K + 2, 33 * s + K + wx
     cin = largest_supported_cin(fc, K, s, H, W, algo)
     announce(f"conv2d largest LDS tile K={K} s={s} algo={algo} Cin={cin}")
-    assert cin >= 8
-    assert algo != 3 or cin == 256
+    assert cin == 256
     x, w, b = fi.conv2d_inputs(2, cin, H, W, 70, K, seed=24)
     want_out, want_map = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, want_pooled=True)
     xd, wd, bd = dev(x), dev(w), dev(b)
     assert_close(fc.conv2d_pool_map(xd, wd, bd, s, algo=algo).cpu().numpy(), want_map, f"map Cin={cin}")
     assert_close(fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=algo).cpu().numpy(), want_out, f"out Cin={cin}")
-    if cin < 256:
-        x1, w1, b1 = fi.conv2d_inputs(1, cin + 1, H, W, 8, K, seed=25)
-        with pytest.raises(fc.FconvError) as err:
-            fc.conv2d_pool_sigmoid_sum(dev(x1), dev(w1), dev(b1), s, algo=algo)
-        assert err.value.status == fc.FCONV_EUNSUPPORTED
 
 
 MANY_CHANNELS = [
     # B, Cin, H, W, Cout, K, s: box-sum with several LDS chunks of channels (8 per chunk for K = 3,
-    # 16 for K = 5), a partial last chunk, and Cin = 64 and 128 on the matrix cores
+    # 16 for K = 5), a partial last chunk, and Cin = 64 and 128 on the matrix cores; the direct path too
     (2, 12, 30, 104, 64, 3, 4),     # one-column-per-lane kernel: chunks of 2 + 1 quads
     (1, 20, 37, 101, 70, 3, 4),     # W % 4 != 0: general kernel, chunks of 2 + 2 + 1 quads, two channel ranges
     (2, 64, 22, 200, 64, 3, 4),     # Cin 64: 8 chunks
@@ -192,6 +186,8 @@ def test_conv2d_many_channels(fc, shape):
     assert_close(fc.conv2d_pool_map(xd, wd, bd, s, algo=3).cpu().numpy(), want_map, f"map {shape}")
     assert_close(fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s).cpu().numpy(), want_out, f"out (auto) {shape}")
     assert_close(fc.conv2d_pool_sigmoid_sum_det(xd, wd, bd, s, algo=3).cpu().numpy(), want_out, f"det {shape}")
+    # and on the direct matrix-core path (whole tiles up to Cin 32-68, channel-chunked past that)
+    assert_close(fc.conv2d_pool_map(xd, wd, bd, s, algo=1).cpu().numpy(), want_map, f"direct map {shape}")
 
 
 WALK_CONV = [
@@ -233,6 +229,8 @@ WALK_POOL = [
     (1, 2, 266, 6340, 4, 3, 4, 1, 1, True, True),    # per-conv-output kernel, 17 x 99 tiles of 4 x 16
     (1, 2, 400, 1204, 8, 5, 3, 1, 1, False, True),   # its K5/s3 instance, 33 x 41 tiles of 4 x 10
     (1, 2, 266, 1100, 16, 3, 4, 2, 0, True, True),   # one thread per output
+    (1, 33, 134, 2050, 4, 3, 4, 1, 1, True, False),  # channel-chunked per-conv-output tiling, 33 x 32 tiles of 1 x 16
+    (1, 70, 154, 634, 8, 5, 3, 1, 0, True, False),   # its K5/s3 instance, 50 x 21 tiles of 1 x 10
 ]
 
 

@@ -119,39 +119,62 @@ def test_pool_small(fc, shape, combo, algo):
     assert_close(got_out, want_out, f"out {shape} {combo_id(combo)}")
 
 
-LDS_LIMITS = [(3, 4, 32), (3, 2, 56), (3, 3, 40), (5, 3, 68)]   # (K, s, largest Cin whose LDS tile fits)
+# (K, s, largest Cin whose whole tile fits LDS, for the max / ReLU / ceil forms and for the folded
+# average pool): past it the per-conv-output kernel stages CQ = 4 channel quads at a time
+LDS_LIMITS = [(3, 4, 32, 40), (3, 2, 56, 56), (3, 3, 40, 40), (5, 3, 68, 68)]
 
 
-@pytest.mark.parametrize("K,s,cin_max", LDS_LIMITS)
-def test_pool_largest_lds_tile(fc, K, s, cin_max):
-    # the matrix-core instance at its largest channel count (a full LDS tile: staging, plane padding and
-    # reads at the end of LDS), and one channel more, where AUTO falls back and DIRECT_MFMA is refused
+@pytest.mark.parametrize("K,s,cin_max,cin_fold", LDS_LIMITS)
+def test_pool_whole_and_chunked_tiles(fc, K, s, cin_max, cin_fold):
+    # the matrix-core kernel at its largest whole tile (staging, plane padding and reads at the end of
+    # LDS), one channel more (the first chunked case: a partial last quad), and a count that needs
+    # several chunks plus a partial one; every pool form stays on the matrix cores
     H, W = 4 * s + K + 3, 17 * s + K + 1
-    announce(f"pool ex largest LDS tile K={K} s={s} Cin={cin_max}")
-    for Cin in (cin_max, cin_max + 1):
+    cins = sorted({cin_max, cin_max + 1, cin_fold, cin_fold + 1, 2 * cin_max + 19})
+    for Cin in cins:
+        announce(f"pool ex whole/chunked tile K={K} s={s} Cin={Cin}")
         x, w, b = fi.conv2d_inputs(1, Cin, H, W, 20, K, seed=60 + Cin)
         xd, wd, bd = dev(x), dev(w), dev(b)
-        for pool_mode, relu, ceil_mode in [(MAX, True, True), (AVG, False, False), (AVG, True, False)]:
+        for pool_mode, relu, ceil_mode in [(MAX, True, True), (AVG, False, False), (AVG, True, False),
+                                           (MAX, False, False)]:
             kw = dict(pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
             want_out, want_map = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, want_pooled=True, **kw)
-            plain = pool_mode == AVG and not relu and not ceil_mode
-            try:  # host-side support query of DIRECT_MFMA (the plain average pool uses the base kernels' limits)
-                fc.conv2d_det_workspace_bytes(1, Cin, H, W, 20, K, s, 1, pool_mode, relu, ceil_mode)
-                mfma = True
-            except fc.FconvError as e:
-                assert e.status == fc.FCONV_EUNSUPPORTED
-                mfma = False
-            if not plain:  # the generalised pool's instances: exactly up to cin_max
-                assert mfma == (Cin == cin_max)
-            if mfma:
-                got = fc.conv2d_pool_map(xd, wd, bd, s, algo=1, **kw).cpu().numpy()
-                assert_close(got, want_map, f"K{K} s{s} Cin {Cin} {combo_id((pool_mode, relu, ceil_mode))}")
-            else:
-                with pytest.raises(fc.FconvError) as err:
-                    fc.conv2d_pool_map(xd, wd, bd, s, algo=1, **kw)
-                assert err.value.status == fc.FCONV_EUNSUPPORTED
+            assert fc.conv2d_det_workspace_bytes(1, Cin, H, W, 20, K, s, 1, pool_mode, relu, ceil_mode) > 0
+            got = fc.conv2d_pool_map(xd, wd, bd, s, algo=1, **kw).cpu().numpy()
+            what = f"K{K} s{s} Cin {Cin} {combo_id((pool_mode, relu, ceil_mode))}"
+            assert_close(got, want_map, what)
+            det = fc.conv2d_pool_sigmoid_sum_det(xd, wd, bd, s, algo=1, **kw).cpu().numpy()
+            assert_close(det, want_out, f"det {what}")
             got_out = fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=0, **kw).cpu().numpy()
-            assert_close(got_out, want_out, f"AUTO out K{K} s{s} Cin {Cin}")
+            assert_close(got_out, want_out, f"AUTO out {what}")
+
+
+CHUNKED = [
+    # B, Cin, H, W, Cout, K, s: the channel-chunked per-conv-output tiling on larger maps: several tiles
+    # in both directions, ragged edges, two output-channel ranges, Cin 64 and 128
+    (2, 64, 38, 70, 64, 3, 4),
+    (1, 128, 27, 101, 70, 3, 4),
+    (1, 64, 30, 68, 40, 3, 2),
+    (1, 128, 25, 64, 20, 3, 3),
+    (2, 64, 31, 44, 128, 5, 3),
+    (1, 130, 26, 35, 24, 5, 3),
+]
+
+
+@pytest.mark.parametrize("shape", CHUNKED)
+@pytest.mark.parametrize("combo", COMBOS, ids=combo_id)
+def test_pool_chunked_many_channels(fc, shape, combo):
+    B, Cin, H, W, Cout, K, s = shape
+    pool_mode, relu, ceil_mode = combo
+    announce(f"pool ex chunked {shape} {combo_id(combo)}")
+    x, w, b = fi.conv2d_inputs(B, Cin, H, W, Cout, K, seed=61)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    kw = dict(pool_mode=pool_mode, relu=relu, ceil_mode=ceil_mode)
+    want_out, want_map = oracle.conv2d_pool_sigmoid_sum(x, w, b, s, want_pooled=True, **kw)
+    assert_close(fc.conv2d_pool_map(xd, wd, bd, s, algo=1, **kw).cpu().numpy(), want_map,
+                 f"map {shape} {combo_id(combo)}")
+    assert_close(fc.conv2d_pool_sigmoid_sum(xd, wd, bd, s, algo=1, **kw).cpu().numpy(), want_out,
+                 f"out {shape} {combo_id(combo)}")
 
 
 @pytest.mark.parametrize("combo", COMBOS[1:], ids=combo_id)
