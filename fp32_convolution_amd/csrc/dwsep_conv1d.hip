@@ -354,10 +354,13 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
         if constexpr (Cfg::KC == 9) {
             // the chunk's taps w_dw[c0 .. c0+CC-1][0..8] are contiguous: runs of
             // 64 floats (0 past channel C-1; the ws region is whole runs)
+            // (each run's resource starts at the run, so every load takes the
+            // lane's own offset: no per-run offset register to keep live)
             const int n = min(CC, C - c0) * 9;
-            const buf_rsrc rt = make_rsrc(w_dw + (size_t)c0 * 9, n * 4);
-            for (int q = wave; q < (9 * CC + 63) / 64; q += NW)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, ws3 + 64 * q, 4, (64 * q + lane) * 4, 0, 0, 0);
+            for (int q = wave; q < (9 * CC + 63) / 64; q += NW) {
+                const buf_rsrc rt = make_rsrc(w_dw + (size_t)c0 * 9 + 64 * q, max(n - 64 * q, 0) * 4);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, ws3 + 64 * q, 4, lane * 4, 0, 0, 0);
+            }
         }
     };
 
