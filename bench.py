@@ -56,25 +56,25 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # channel quads with weights resident in registers (0: streamed), whether
 # each workgroup walks several tiles>.
 KERNEL_SOURCES = {
-    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3, false>, 2, 0, 2, false>": [
+    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3, false>, 2, 2, 2, false>": [
         "fp32_convolution_amd/csrc/conv2d_pool_ex.hip", "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_tall_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                           "fp32_convolution_amd/csrc/fconv_device.hpp"],
-    "conv2d_pool_boxsum4_kernel<0, true, 2, false>": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
+    "conv2d_pool_boxsum4_kernel<2, true, 2, false>": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
                                                       "fp32_convolution_amd/csrc/fconv_device.hpp"],
-    "conv2d_pool_boxsum_kernel<fconv::DirectCfg<5, 3, 1, 3, 8, 1, 4, 12>, 0, false>": [
+    "conv2d_pool_boxsum_kernel<fconv::DirectCfg<5, 3, 1, 3, 8, 1, 4, 12>, 2, false>": [
         "fp32_convolution_amd/csrc/conv2d_pool.hip", "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "dwsep_dense_kernel": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                            "fp32_convolution_amd/csrc/fconv_device.hpp"],
-    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4, false>, 1, 0, 2, false>": [
+    "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4, false>, 1, 2, 2, false>": [
         "fp32_convolution_amd/csrc/conv2d_pool_ex.hip", "fp32_convolution_amd/csrc/fconv_device.hpp"],
-    "conv2d_pool_mfma_kernel<fconv::DirectCfg<5, 3, 1, 3, 8, 1, 4, 12>, 0, false>": [
+    "conv2d_pool_mfma_kernel<fconv::DirectCfg<5, 3, 1, 3, 8, 1, 4, 12>, 2, false>": [
         "fp32_convolution_amd/csrc/conv2d_pool.hip", "fp32_convolution_amd/csrc/fconv_device.hpp"],
 }
 
 
-ELEM_AVG = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3, false>, 2, 0, 2, false>"
-ELEM_MAX = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4, false>, 1, 0, 2, false>"
+ELEM_AVG = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3, false>, 2, 2, 2, false>"
+ELEM_MAX = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4, false>, 1, 2, 2, false>"
 TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace.json")
 
 
@@ -531,12 +531,12 @@ def main():
         "fconv2d_pool_sigmoid_sum_boxsum": variant(
             lambda: fc.conv2d_pool_sigmoid_sum(x, w, b, cc["pool"], out=o1, algo=fc.ALGO_BOXSUM),
             conv2d_boxsum_flops(cc), b_conv, "box-sum (FCONV_ALGO_BOXSUM, the default for this shape) on " + CONV
-            + ": zero fill + conv2d_pool_boxsum4_kernel, HBM-bound", bound="hbm",
-            traffic_key="conv2d_pool_boxsum4_kernel<0, true, 2, false>"),
+            + ": conv2d_pool_boxsum4_kernel (partial sums) + fixed-order reduction, HBM-bound", bound="hbm",
+            traffic_key="conv2d_pool_boxsum4_kernel<2, true, 2, false>"),
         "fconv2d_pool_sigmoid_sum_det": variant(
             lambda: fc.conv2d_pool_sigmoid_sum_det(x, w, b, cc["pool"], out=o1, algo=fc.ALGO_DIRECT_MFMA,
                                                    workspace=ws_det),
-            f_conv, b_conv, "direct MFMA, deterministic (partials + fixed-order reduction) on " + CONV),
+            f_conv, b_conv, "direct MFMA with a caller-owned workspace for the partial sums (the default call takes it from the library pool) on " + CONV),
         "fconv2d_pool_sigmoid_sum_det_noalloc": variant(
             lambda: fc.conv2d_pool_sigmoid_sum_det_noalloc(x, w, b, cc["pool"], o1),
             conv2d_boxsum_flops(cc), b_conv, "allocation-free deterministic call (AUTO: box-sum partials in the "
@@ -549,12 +549,12 @@ def main():
         "fconv2d_pool_sigmoid_sum_k5s3_direct": variant(
             lambda: fc.conv2d_pool_sigmoid_sum(xt, wt, bt, tc["pool"], out=o2, algo=fc.ALGO_DIRECT_MFMA),
             f_tail, b_tail, "direct MFMA (pool folded into the contraction) on " + TAIL,
-            traffic_key="conv2d_pool_mfma_kernel<fconv::DirectCfg<5, 3, 1, 3, 8, 1, 4, 12>, 0, false>"),
+            traffic_key="conv2d_pool_mfma_kernel<fconv::DirectCfg<5, 3, 1, 3, 8, 1, 4, 12>, 2, false>"),
         "fconv2d_pool_sigmoid_sum_boxsum_k5s3": variant(
             lambda: fc.conv2d_pool_sigmoid_sum(xt, wt, bt, tc["pool"], out=o2, algo=fc.ALGO_BOXSUM),
             conv2d_boxsum_flops(tc), b_tail, "box-sum (the default for this shape) on " + TAIL
             + ", own FLOPs Cin*K*K per (co, pooled output)",
-            traffic_key="conv2d_pool_boxsum_kernel<fconv::DirectCfg<5, 3, 1, 3, 8, 1, 4, 12>, 0, false>"),
+            traffic_key="conv2d_pool_boxsum_kernel<fconv::DirectCfg<5, 3, 1, 3, 8, 1, 4, 12>, 2, false>"),
         "fconv2d_pool_sigmoid_sum_ex_relu_maxpool_k5s3": variant(
             lambda: fc.conv2d_pool_sigmoid_sum(xt, wt, bt, tc["pool"], out=o2, algo=fc.ALGO_DIRECT_MFMA,
                                                pool_mode=fc.POOL_MAX, relu=True),
@@ -648,7 +648,7 @@ def main():
     k_dw["cold_note"] = "each call after a 512 MB overwrite (inputs not in the 256 MB Infinity Cache)"
     # the box-sum call against the measured streaming-read rate too
     box = variants["fconv2d_pool_sigmoid_sum_boxsum"]
-    box["trace_kernel_ms"] = trace_kernel_ms("conv2d_pool_boxsum4_kernel<0, true, 2, false>")
+    box["trace_kernel_ms"] = trace_kernel_ms("conv2d_pool_boxsum4_kernel<2, true, 2, false>")
     if "hbm_read" in ceilings:
         box["roofline"]["frac_of_measured_read"] = round(box["roofline"]["achieved"] / ceilings["hbm_read"]["gbps"], 4)
         configs[CONV]["default"]["roofline"]["frac_of_measured_read"] = round(

@@ -27,7 +27,8 @@
 //    (stride s in x) hit 16 consecutive LDS words.
 //  * Weights stream from L2/L1 straight into registers (they are 18-200 KB).
 //  * Epilogue: scale by 1/s^2, add bias, sigmoid, lane sum, wave + LDS
-//    reduction, one float atomic per workgroup into out[b].
+//    reduction, one partial sum per workgroup (added in a fixed order into
+//    out[b] by reduce_partials).
 // Instances: K5/s3, K3/s2, K3/s3.  K3/s4 runs on conv2d_pool_elem_kernel
 // (conv2d_pool_ex.hip), which keeps each conv output in an accumulator and
 // pools in registers: the same multiply-adds, measured slightly faster there.
@@ -261,12 +262,7 @@ __global__ __launch_bounds__(Cfg::NT) void conv2d_pool_mfma_kernel(
     }  // units
     if constexpr (MODE != OUT_MAP) {
         const float s = block_sum<Cfg::NW>((float)dsum, red);
-        if (tid == 0) {
-            if constexpr (MODE == OUT_SUM_ATOMIC)
-                atomicAdd(dst + b, s);
-            else
-                dst[(size_t)b * parts + part] = s;
-        }
+        if (tid == 0) dst[(size_t)b * parts + part] = s;
     }
 }
 
@@ -325,19 +321,15 @@ bool conv2d_mfma_supported(int Cin, int K, int S) {
 // the one `mode` asks for, raising the dynamic LDS limit first.
 #define FCONV_LAUNCH_MODES(KERNEL, GRID, BLOCK, LDS, STREAM, ...)                                            \
     do {                                                                                                 \
-        const void* fn = mode == OUT_MAP       ? (const void*)KERNEL<OUT_MAP>                            \
-                         : mode == OUT_PARTIAL ? (const void*)KERNEL<OUT_PARTIAL>                        \
-                                               : (const void*)KERNEL<OUT_SUM_ATOMIC>;                    \
+        const void* fn = mode == OUT_MAP ? (const void*)KERNEL<OUT_MAP> : (const void*)KERNEL<OUT_PARTIAL>; \
         if ((LDS) > 0) {                                                                                 \
             hipError_t ea = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(LDS)); \
             if (ea != hipSuccess) return ea;                                                             \
         }                                                                                                \
         if (mode == OUT_MAP)                                                                             \
             hipLaunchKernelGGL((KERNEL<OUT_MAP>), GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                \
-        else if (mode == OUT_PARTIAL)                                                                    \
-            hipLaunchKernelGGL((KERNEL<OUT_PARTIAL>), GRID, BLOCK, LDS, STREAM, __VA_ARGS__);            \
         else                                                                                             \
-            hipLaunchKernelGGL((KERNEL<OUT_SUM_ATOMIC>), GRID, BLOCK, LDS, STREAM, __VA_ARGS__);         \
+            hipLaunchKernelGGL((KERNEL<OUT_PARTIAL>), GRID, BLOCK, LDS, STREAM, __VA_ARGS__);            \
         return hipGetLastError();                                                                        \
     } while (0)
 
@@ -770,12 +762,7 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
     }  // units
     if constexpr (MODE != OUT_MAP) {
         const float s = block_sum<NW>((float)dsum, red);
-        if (tid == 0) {
-            if constexpr (MODE == OUT_SUM_ATOMIC)
-                atomicAdd(dst + b, s);
-            else
-                dst[(size_t)b * parts + part] = s;
-        }
+        if (tid == 0) dst[(size_t)b * parts + part] = s;
     }
 }
 
@@ -1058,12 +1045,7 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
     }  // units
     if constexpr (MODE != OUT_MAP) {
         const float sum = block_sum<NW>((float)dsum, red);
-        if (tid == 0) {
-            if constexpr (MODE == OUT_SUM_ATOMIC)
-                atomicAdd(dst + b, sum);
-            else
-                dst[(size_t)b * parts + part] = sum;
-        }
+        if (tid == 0) dst[(size_t)b * parts + part] = sum;
     }
 }
 
@@ -1233,12 +1215,7 @@ __global__ __launch_bounds__(256) void conv2d_pool_simple_kernel(
     }
     if constexpr (MODE != OUT_MAP) {
         const float s = block_sum<4>((float)dsum, red);
-        if (threadIdx.x == 0) {
-            if constexpr (MODE == OUT_SUM_ATOMIC)
-                atomicAdd(dst + b, s);
-            else
-                dst[(size_t)b * parts + blockIdx.x] = s;
-        }
+        if (threadIdx.x == 0) dst[(size_t)b * parts + blockIdx.x] = s;
     }
 }
 

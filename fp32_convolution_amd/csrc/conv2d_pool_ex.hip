@@ -90,12 +90,7 @@ __global__ __launch_bounds__(256) void conv2d_pool_general_kernel(
     }
     if constexpr (MODE != OUT_MAP) {
         const float s = block_sum<4>((float)dsum, red);
-        if (threadIdx.x == 0) {
-            if constexpr (MODE == OUT_SUM_ATOMIC)
-                atomicAdd(dst + b, s);
-            else
-                dst[(size_t)b * parts + blockIdx.x] = s;
-        }
+        if (threadIdx.x == 0) dst[(size_t)b * parts + blockIdx.x] = s;
     }
 }
 
@@ -521,12 +516,7 @@ __global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
     }  // units
     if constexpr (MODE != OUT_MAP) {
         const float s = block_sum<C::NW>((float)dsum, red);
-        if (tid == 0) {
-            if constexpr (MODE == OUT_SUM_ATOMIC)
-                atomicAdd(dst + b, s);
-            else
-                dst[(size_t)b * parts + part] = s;
-        }
+        if (tid == 0) dst[(size_t)b * parts + part] = s;
     }
 }
 
@@ -624,22 +614,18 @@ hipError_t launch_elem_cfg(const Conv2dShape& s, const float* x, const float* w,
     if constexpr (!fold_only) {
         if (o.pool_max) {
             if (mode == OUT_MAP) return launch_elem_as<C, kPoolMax, OUT_MAP>(s, x, w, bias, dst, o, stream);
-            if (mode == OUT_PARTIAL) return launch_elem_as<C, kPoolMax, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
-            return launch_elem_as<C, kPoolMax, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+            return launch_elem_as<C, kPoolMax, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
         }
     }
     if constexpr (!no_fold) {
         if (folds(o)) {
             if (mode == OUT_MAP) return launch_elem_as<C, kPoolMeanFolded, OUT_MAP>(s, x, w, bias, dst, o, stream);
-            if (mode == OUT_PARTIAL)
-                return launch_elem_as<C, kPoolMeanFolded, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
-            return launch_elem_as<C, kPoolMeanFolded, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+            return launch_elem_as<C, kPoolMeanFolded, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
         }
     }
     if constexpr (!fold_only) {
         if (mode == OUT_MAP) return launch_elem_as<C, kPoolMean, OUT_MAP>(s, x, w, bias, dst, o, stream);
-        if (mode == OUT_PARTIAL) return launch_elem_as<C, kPoolMean, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
-        return launch_elem_as<C, kPoolMean, OUT_SUM_ATOMIC>(s, x, w, bias, dst, o, stream);
+        return launch_elem_as<C, kPoolMean, OUT_PARTIAL>(s, x, w, bias, dst, o, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -694,12 +680,9 @@ hipError_t conv2d_general_launch(const Conv2dShape& s, const float* x, const flo
     if (mode == OUT_MAP)
         hipLaunchKernelGGL(conv2d_pool_general_kernel<OUT_MAP>, grid, dim3(256), 0, stream, x, w, bias, dst, s.Cin,
                            s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl, units);
-    else if (mode == OUT_PARTIAL)
+    else
         hipLaunchKernelGGL(conv2d_pool_general_kernel<OUT_PARTIAL>, grid, dim3(256), 0, stream, x, w, bias, dst,
                            s.Cin, s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl, units);
-    else
-        hipLaunchKernelGGL(conv2d_pool_general_kernel<OUT_SUM_ATOMIC>, grid, dim3(256), 0, stream, x, w, bias,
-                           dst, s.Cin, s.H, s.W, s.Cout, s.K, s.S, s.PH, s.PW, pm, rl, units);
     return hipGetLastError();
 }
 

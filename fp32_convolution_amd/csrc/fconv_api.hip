@@ -99,6 +99,52 @@ int64_t conv2d_parts(int algo, const Conv2dShape& s) {
     return fconv::conv2d_simple_parts(s);
 }
 
+constexpr int kMaxDevices = 64;
+
+// The memory pool of the fused-sum entry points' partial sums on the current
+// device: created on first use (with that device current) and kept, with an
+// unlimited release threshold, so that freed blocks stay with the pool for
+// the next call instead of going back to the driver.  nullptr on failure.
+hipMemPool_t partials_pool() {
+    static std::mutex mu;
+    static hipMemPool_t pools[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t p = nullptr;
+        if (hipMemPoolCreate(&p, &props) != hipSuccess) return nullptr;
+        uint64_t keep = UINT64_MAX;
+        if (hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) {
+            (void)hipMemPoolDestroy(p);
+            return nullptr;
+        }
+        pools[dev] = p;
+    }
+    return pools[dev];
+}
+
+// A fused sum: `launch(ws)` writes B * parts partial sums to ws, taken from
+// the pool in stream order on `st`; reduce_partials adds each item's partials
+// in a fixed order into out[b]; ws goes back to the pool in stream order.
+// Calls on different streams therefore never share scratch.
+template <class Launch>
+int sum_through_partials(int64_t parts, int B, float* out, hipStream_t st, Launch&& launch) {
+    hipMemPool_t pool = partials_pool();
+    if (!pool) return FCONV_EHIP;
+    void* ws = nullptr;
+    if (hipMallocFromPoolAsync(&ws, (size_t)parts * (size_t)B * sizeof(float), pool, st) != hipSuccess)
+        return FCONV_EHIP;
+    hipError_t e = launch((float*)ws);
+    if (e == hipSuccess) e = fconv::reduce_partials((float*)ws, parts, B, out, st);
+    const hipError_t ef = hipFreeAsync(ws, st);
+    return (e == hipSuccess && ef == hipSuccess) ? FCONV_OK : FCONV_EHIP;
+}
+
 // Stands in for a NULL pooled-map pointer during the argument checks.
 const float kEmptyMapStorage = 0.f;
 const void* const kEmptyMap = &kEmptyMapStorage;
@@ -121,11 +167,10 @@ int run_conv2d(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, con
         // Empty pooled map: the sum is 0 and the map has no elements.
         return map ? FCONV_OK : status_of(fconv::fill_zero(dst, s.B, st));
     }
-    if (!map) {
-        hipError_t e = fconv::fill_zero(dst, s.B, st);
-        if (e != hipSuccess) return FCONV_EHIP;
-    }
-    return status_of(launch_conv2d(a, s, x, w, bias, dst, map ? fconv::OUT_MAP : fconv::OUT_SUM_ATOMIC, st));
+    if (map) return status_of(launch_conv2d(a, s, x, w, bias, dst, fconv::OUT_MAP, st));
+    return sum_through_partials(conv2d_parts(a, s), s.B, dst, st, [&](float* ws) {
+        return launch_conv2d(a, s, x, w, bias, ws, fconv::OUT_PARTIAL, st);
+    });
 }
 
 constexpr int kPoolFlags = FCONV_RELU | FCONV_CEIL_MODE;
@@ -193,11 +238,9 @@ int run_conv2d_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, 
                 map ? "_map" : "", p.s.B, p.s.Cin, p.s.H, p.s.W, p.s.Cout, p.s.K, p.s.S, (int)p.o.pool_max,
                 (int)p.o.relu, (int)p.o.ceil_mode, p.algo);
     if (p.s.PH == 0 || p.s.PW == 0) return map ? FCONV_OK : status_of(fconv::fill_zero(dst, p.s.B, st));
-    if (!map) {
-        hipError_t e = fconv::fill_zero(dst, p.s.B, st);
-        if (e != hipSuccess) return FCONV_EHIP;
-    }
-    return status_of(launch_ex(p, x, w, bias, dst, map ? fconv::OUT_MAP : fconv::OUT_SUM_ATOMIC, st));
+    if (map) return status_of(launch_ex(p, x, w, bias, dst, fconv::OUT_MAP, st));
+    return sum_through_partials(parts_ex(p), p.s.B, dst, st,
+                                [&](float* ws) { return launch_ex(p, x, w, bias, ws, fconv::OUT_PARTIAL, st); });
 }
 
 // Shape/algorithm checks shared by the deterministic entry point and its
@@ -215,7 +258,6 @@ int det_plan(int64_t B, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t
 
 // The device address of `scratch` on the current device: looked up once per
 // device (with that device current) and kept.  nullptr if the lookup failed.
-constexpr int kMaxDevices = 64;
 float* scratch_ptr() {
     static std::mutex mu;
     static float* ptrs[kMaxDevices] = {};

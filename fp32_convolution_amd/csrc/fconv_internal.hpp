@@ -15,25 +15,27 @@ struct DwsepShape {
     int B, C, T, K, O, pad, Tout, stride, dil;
 };
 
-// Workgroups per batch item of a Conv2d launch.  A fused sum adds one fp32
-// partial per workgroup into out[b] with an atomic add.  Every partial is
-// positive (a sum of sigmoids), so each add rounds by at most half an ulp of
-// the final out[b], i.e. by at most 2^-24 |out[b]|; with at most
-// kMaxPartsPerItem partials that rounding stays within 1024 * 2^-24 = 6.1e-5
-// of |out[b]|, whatever the map size.  A map with more units of work (tiles x
-// output-channel ranges) than that has each workgroup walk several units,
-// part, part + parts, ..., summing its lanes' sigmoids in fp64 between units.
+// Workgroups per batch item of a Conv2d launch.  A fused sum writes one fp32
+// partial per workgroup and reduce_partials adds an item's partials in a
+// fixed order: each thread adds at most 4 of them (1024 / 256) in sequence,
+// then a 256-thread tree adds the threads' sums, so no chain of additions is
+// longer than 12.  Every partial is positive (a sum of sigmoids), so each
+// addition rounds by at most 2^-24 of the final out[b], and the reduction by
+// at most 12 * 2^-24 = 7.2e-7 |out[b]|, whatever the map size.  A map with
+// more units of work (tiles x output-channel ranges) than kMaxPartsPerItem
+// has each workgroup walk several units, part, part + parts, ..., summing its
+// lanes' sigmoids in fp64 between units.
 #ifndef FCONV_MAX_PARTS_PER_ITEM
 #define FCONV_MAX_PARTS_PER_ITEM 1024
 #endif
 constexpr int kMaxPartsPerItem = FCONV_MAX_PARTS_PER_ITEM;
 inline int walk_parts(int64_t units) { return units < kMaxPartsPerItem ? (int)units : kMaxPartsPerItem; }
 
-// What a Conv2d kernel writes: the fused sums (one float atomic per
-// workgroup into out[b]), the pre-sigmoid pooled map, or one partial sum per
-// workgroup into ws[b * parts_per_item + part] for a fixed-order reduction.
-// parts_per_item = walk_parts(units per item) for every mode.
-enum OutMode { OUT_SUM_ATOMIC = 0, OUT_MAP = 1, OUT_PARTIAL = 2 };
+// What a Conv2d kernel writes: the pre-sigmoid pooled map, or one partial
+// sum per workgroup into ws[b * parts_per_item + part], which
+// reduce_partials then adds in a fixed order into out[b].
+// parts_per_item = walk_parts(units per item).
+enum OutMode { OUT_MAP = 1, OUT_PARTIAL = 2 };
 
 // The generalised pool: max instead of mean, a ReLU between the conv and the
 // pool, PyTorch's ceil output size (partial windows at the bottom/right).

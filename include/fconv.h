@@ -25,9 +25,15 @@
  *   - Tensors are dense, contiguous, row-major fp32 in DEVICE memory
  *     (hipMalloc'd or equivalent), owned by the caller.  Only 4-byte
  *     alignment is required.  Input buffers are never written.
- *   - The library allocates no memory and keeps no state between calls; it
- *     is reentrant.  Calls on different streams may run concurrently as
- *     long as their output buffers do not overlap.
+ *   - The library is reentrant.  Calls on different streams may run
+ *     concurrently as long as their output buffers do not overlap.  The
+ *     fused sums (fconv2d_pool_sigmoid_sum, _algo, _ex) take their partial
+ *     sums' scratch (at most 4 KiB per batch item) from a memory pool the
+ *     library creates per device on first use and keeps until the process
+ *     ends: allocated and freed in stream order on the call's stream
+ *     (hipMallocFromPoolAsync / hipFreeAsync), so concurrent calls never
+ *     share it, and `stream` must belong to the current device.  No other
+ *     entry point allocates device memory.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *     Every call is asynchronous with respect to the host: it enqueues its
  *     kernels on `stream` and returns.  Outputs are valid once the stream
@@ -35,17 +41,16 @@
  *   - Sizes are int64_t.  Argument checks happen on the host before any
  *     device work; a failed check returns FCONV_EINVAL and enqueues nothing.
  *   - A HIP launch error is returned as FCONV_EHIP (from hipGetLastError).
- *   - The sums inside a call are fp32.  fconv2d_pool_sigmoid_sum combines
- *     per-workgroup partial sums with floating-point atomics, so its last
- *     bits may differ from call to call.  Every partial is positive (a sum
- *     of sigmoids), so each atomic add rounds by at most half an ulp of the
- *     final out[b], i.e. by at most 2^-24 |out[b]|.  A call never uses more
- *     than 1024 workgroups per batch item (larger maps have each workgroup
- *     walk several tiles, summing in fp64 between them), so the atomic
- *     rounding stays within 1024 x 2^-24 = 6.1e-5 |out[b]| at every shape
- *     the ABI accepts: 96 partials per item for x[128,8,384,384] (box-sum),
- *     1024 for an item of 5e8 input elements.  The deterministic form adds
- *     the same partials in a fixed order.
+ *   - The sums inside a call are fp32.  Every fused sum writes one partial
+ *     sum per workgroup and a second kernel adds each batch item's partials
+ *     in a fixed order, so repeated calls with the same inputs, algorithm
+ *     and device give identical bits.  A call never uses more than 1024
+ *     workgroups per batch item (larger maps have each workgroup walk
+ *     several tiles, summing in fp64 between them): 96 partials per item
+ *     for x[128,8,384,384] (box-sum), 1024 for an item of 5e8 input
+ *     elements.  Every partial is positive (a sum of sigmoids) and no chain
+ *     of additions in that reduction is longer than 12, so it rounds by at
+ *     most 12 x 2^-24 = 7.2e-7 |out[b]| at every shape the ABI accepts.
  */
 #ifndef FCONV_H
 #define FCONV_H
@@ -95,7 +100,7 @@ extern "C" {
  *   x    [B, Cin, H, W]
  *   w    [Cout, Cin, K, K]   (cross-correlation, as PyTorch's Conv2d)
  *   bias [Cout], or NULL for no bias
- *   out  [B], fully overwritten (the call zeroes it on `stream` first)
+ *   out  [B], fully overwritten
  *
  * FCONV_EINVAL when: x, w or out is NULL; any of B, Cin, Cout, H, W, K, pool
  * is < 1; H < K or W < K; an element count overflows int64.  A shape with
@@ -104,6 +109,7 @@ extern "C" {
  * (Cout*Cin*K*K) has 2^29 elements or more, one batch item's pooled map
  * (Cout*PH*PW) exceeds 2^31-1 elements, B > 65535, Cout > 2^20, or K or
  * pool > 4096.
+ * FCONV_EHIP also if the partial sums' scratch cannot be allocated.
  */
 int fconv2d_pool_sigmoid_sum(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
                              const float* w, int64_t Cout, int64_t K, const float* bias,
@@ -116,13 +122,15 @@ int fconv2d_pool_sigmoid_sum_algo(const float* x, int64_t B, int64_t Cin, int64_
                                   int64_t pool, int algo, float* out, void* stream);
 
 /*
- * fconv2d_pool_sigmoid_sum_det -- the same result, bitwise reproducible.
- *   Each workgroup writes its partial sum to its own slot of `workspace`
- *   (no atomics); a second kernel then adds each batch item's slots in a
- *   fixed order into out[b].  Repeated calls with the same inputs, algorithm
- *   and device give identical bits.  This is the two-pass alternative to the
- *   per-block atomics that the l2_p65 trace weighs in its atomic-contention
- *   discussion.
+ * fconv2d_pool_sigmoid_sum_det -- fconv2d_pool_sigmoid_sum_algo with the
+ *   partial sums in a caller-owned workspace instead of the library's pool:
+ *   each workgroup writes its partial sum to its own slot of `workspace`; a
+ *   second kernel then adds each batch item's slots in a fixed order into
+ *   out[b].  Same kernels, so the same bits as the pooled call with the same
+ *   algorithm.  This is the workspace two-pass that the l2_p65 trace weighs
+ *   against per-block atomics in its atomic-contention discussion; on
+ *   MI355X it is also the faster of the two (12,288 same-address float
+ *   atomics for x[128,8,384,384] cost 13 % of the kernel's time).
  *   workspace        device memory of at least the size that
  *                    fconv2d_pool_sigmoid_sum_det_workspace reports, owned by
  *                    the caller; its contents on entry are ignored and on
