@@ -162,7 +162,8 @@ def _conv2d_args(x, w, b):
 def conv2d_pool_sigmoid_sum(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO, pool_mode: int = POOL_AVG,
                             relu: bool = False, ceil_mode: bool = False):
     """Conv2d(stride 1, no pad) -> [ReLU] -> AvgPool2d or MaxPool2d(pool, floor or ceil) -> sigmoid -> sum
-    over (C,H,W): out[B].  The defaults are the plain chain (average pool, no ReLU, floor)."""
+    over (C,H,W): out[B].  The defaults are the plain chain (average pool, no ReLU, floor).  The sum's
+    partials take scratch from the library's stream-ordered pool; repeated calls give identical bits."""
     _conv2d_args(x, w, b)
     B, Cin, H, W = x.shape
     Cout, _, K, _ = w.shape
@@ -200,7 +201,8 @@ def conv2d_det_workspace_bytes(B, Cin, H, W, Cout, K, pool, algo: int = ALGO_AUT
 
 def conv2d_pool_sigmoid_sum_det(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO, workspace=None,
                                 pool_mode: int = POOL_AVG, relu: bool = False, ceil_mode: bool = False):
-    """Bitwise-reproducible form of conv2d_pool_sigmoid_sum (partials + fixed-order reduction).
+    """conv2d_pool_sigmoid_sum with a caller-owned workspace for its partial sums (same kernels, same
+    fixed-order reduction, same bits).
 
     workspace: a device tensor of at least conv2d_det_workspace_bytes() bytes,
     or None to allocate one here.
@@ -233,7 +235,7 @@ def conv2d_pool_sigmoid_sum_det(x, w, b, pool: int, out=None, algo: int = ALGO_A
 
 
 def conv2d_pool_sigmoid_sum_det_noalloc(x, w, b, pool: int, out, algo: int = ALGO_AUTO):
-    """The bitwise-reproducible sum with its partials in the library's fixed per-GPU array: no
+    """conv2d_pool_sigmoid_sum_det with its partials in the library's fixed per-GPU array: no
     allocation anywhere in the call (`out` must be given).  Calls that overlap in time on one GPU
     race; see include/fconv.h."""
     _conv2d_args(x, w, b)
