@@ -152,8 +152,12 @@ constexpr int kPoolMean = 0, kPoolMax = 1, kPoolMeanFolded = 2;
 // NQ: 0, or the number of channel quads CINQ (1 or 2) when all of them fit
 // in registers.  Then the block's weights load once; otherwise quad q's
 // weights stream in under quad q-1's matrix instructions.
+// Occupancy: the whole-tile instances are held to 3 workgroups per CU (up
+// to 170 VGPRs); the channel-chunked ones to 4, which fits the max-pool
+// instance's 64 accumulators in 128 VGPRs without spills in its sum path
+// (x[16,64,384,384], ReLU + max pool: 1.316 -> 1.260 ms).
 template <class C, int POOL, int MODE, int NQ, bool WALK>
-__global__ __launch_bounds__(C::NT, 3) void conv2d_pool_elem_kernel(
+__global__ __launch_bounds__(C::NT, C::CHUNK ? 4 : 3) void conv2d_pool_elem_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int PH, int PW, int CINQ, int plane, int tiles_w,
     int tiles, int co_ranges, int units, int parts, int nblocks, int relu, int ceil_mode) {
