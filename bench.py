@@ -667,7 +667,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded: x ~ N(0,1), weights and biases ~ U(+-1/sqrt(fan_in)))",
+        "data": ("synthetic: numpy PCG64 seeded with SeedSequence([seed, tensor id]), seed 0; x ~ N(0,1), "
+                 "weights and biases ~ U(+-1/sqrt(fan_in)) (fconv_inputs.py); the same bytes feed the oracle"),
         "config": {
             "workload": f"{CONV} + {DW} (one call each per step)",
             CONV: "x[128,8,384,384] Conv2d 8->64 k3 -> AvgPool2d 4 -> sigmoid -> sum, direct convolution",
