@@ -238,6 +238,22 @@ def measured_ceilings(torch, dev, stream):
         res["valu_fma_f32"].update({
             "nominal_non_packed_tflops": 78.6,
             "implied_cycles_per_wave64_fma_at_2400MHz": round(cus * 4 * 2.4e9 * 128 / (v * 1e12), 2)})
+        # vector work beside matrix work on one SIMD: overlapped or in turn
+        fn = lib.fconv_probe_mfma_valu_f32
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        ov = torch.empty(cus * 512, device=dev)
+        t_mode = {}
+        for mode in (1, 2, 3):
+            def launch_ov(mode=mode):
+                if fn(cus, mode, 4000, 15000, ctypes.c_void_p(ov.data_ptr()), st) != 0:
+                    raise RuntimeError("probe mfma_valu failed to launch")
+            t_mode[mode] = med_ms(launch_ov)
+        res["mfma_beside_valu"] = {
+            "mfma_waves_ms": round(t_mode[1], 4), "valu_waves_ms": round(t_mode[2], 4), "both_ms": round(t_mode[3], 4),
+            "overlap": round((t_mode[1] + t_mode[2] - t_mode[3]) / min(t_mode[1], t_mode[2]), 3),
+            "what": "one wave of v_mfma_f32_16x16x4_f32 chains and one of v_fma_f32 chains per SIMD; overlap 1 = "
+                    "both-mode time is the longer of the two, 0 = their sum (the SIMD runs them in turn)"}
+        del ov
         src = torch.ones(n, device=dev)
         red = torch.empty(cus * 8 * 256, device=dev)
         lib.fconv_probe_read_f32.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p,

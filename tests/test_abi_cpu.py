@@ -83,6 +83,14 @@ def test_ceiling_probe_library():
     assert probe.fconv_probe_read_f32(4, 16, None, FAKE, None) == -1
     assert probe.fconv_probe_write_f32(0, 16, FAKE, None) == -1
     assert probe.fconv_probe_write_f32(4, 16, None, None) == -1
+    ov = probe.fconv_probe_mfma_valu_f32
+    ov.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert ov(0, 3, 10, 10, FAKE, None) == -1
+    assert ov(4, 0, 10, 10, FAKE, None) == -1
+    assert ov(4, 4, 10, 10, FAKE, None) == -1
+    assert ov(4, 3, 0, 10, FAKE, None) == -1
+    assert ov(4, 3, 10, 0, FAKE, None) == -1
+    assert ov(4, 3, 10, 10, None, None) == -1
 
 
 def test_version_and_strerror(lib):
