@@ -277,17 +277,19 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 // The accumulators start at the bias.  Epilogue: each wave transposes its
 // 64 x 64 block through LDS, 16 rows at a time, and writes rows of 64 steps
 // with 16-byte stores; ragged tiles store element by element.
-// Depthwise (K = 9 instance): lane (dc, dj) = (lane/8, lane%8) makes steps
-// 8dj .. 8dj+7 of the wave's channel dc from 16 staged steps (four 16-byte LDS reads) and the
-// channel's 9 taps (staged in LDS too, so the stage needs no scalar loads,
+// Depthwise: lane (dc, dj) = (lane/8, lane%8) makes steps 8dj .. 8dj+7 of
+// the wave's channel dc from staged steps (16-byte LDS reads) and the
+// channel's K taps (staged in LDS too, so the stage needs no scalar loads,
 // whose out-of-order return would serialize the LDS reads): 8 independent
-// multiply-add chains per lane.  The runtime-K instance has lane t make
-// step t of each of the wave's channels.
+// multiply-add chains per lane.  The K = 9 instance reads 16 steps and 9
+// taps once; the runtime-K instance goes over the taps in blocks of 8, 16
+// steps per block.
 // LDS: xs [CC][132], then Ds: [64][CC+4] for the GEMM operand and
-// 8 x [16][68] in the epilogue, then the bias [512] and the taps [CC][9]
-// (72.9 KB, two workgroups per CU).  Row r of xs holds input steps
-// t0-pad .. t0-pad+127 (two 64-lane runs; steps past the K-1 halo or
-// outside [0, T) load as 0), so K <= 65.
+// 8 x [16][68] in the epilogue, then the bias [512] and the taps [CC][K]
+// (72.9 KB for K = 9, two workgroups per CU up to K = 30).  Row r of xs
+// holds input steps t0-pad .. t0-pad+127 (two 64-lane runs; steps past the
+// K-1 halo or outside [0, T) load as 0); the runtime-K blocks read up to
+// step 8*7 + 8*floor((K-1)/8) + 15, so K <= 64.
 // Pointwise weights: lane (g, l16) of block ob keeps channels 4g..4g+3 of
 // the current group; the registers of block ob are refilled with the next
 // group's weights as soon as its 16 matrix instructions are issued.
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     float* xs = lds;            // [CC][XP]
     float* Ds = lds + CC * XP;  // [TT][CCP]; epilogue: [NW][16][OP]
     float* bs = Ds + DSF;       // [NW][64]: each wave's 64 bias values
-    float* ws = bs + NW * 64;   // [CC][9], rounded up to whole 64-float runs: the chunk's taps (K = 9)
+    float* ws = bs + NW * 64;   // [CC][K], rounded up to whole 64-float runs: the chunk's taps
     auto* xs3 = (__attribute__((address_space(3))) float*)xs;
     auto* bs3 = (__attribute__((address_space(3))) float*)bs;
     auto* ws3 = (__attribute__((address_space(3))) float*)ws;
@@ -351,16 +353,14 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, xs3 + (wave + i * NW) * XP + 64 * r, 4, voff[r], 0, 0,
                                                          0);
         }
-        if constexpr (Cfg::KC == 9) {
-            // the chunk's taps w_dw[c0 .. c0+CC-1][0..8] are contiguous: runs of
-            // 64 floats (0 past channel C-1; the ws region is whole runs)
-            // (each run's resource starts at the run, so every load takes the
-            // lane's own offset: no per-run offset register to keep live)
-            const int n = min(CC, C - c0) * 9;
-            for (int q = wave; q < (9 * CC + 63) / 64; q += NW) {
-                const buf_rsrc rt = make_rsrc(w_dw + (size_t)c0 * 9 + 64 * q, max(n - 64 * q, 0) * 4);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, ws3 + 64 * q, 4, lane * 4, 0, 0, 0);
-            }
+        // the chunk's taps w_dw[c0 .. c0+CC-1][0..K-1] are contiguous: runs of
+        // 64 floats (0 past channel C-1; the ws region is whole runs)
+        // (each run's resource starts at the run, so every load takes the
+        // lane's own offset: no per-run offset register to keep live)
+        const int n = min(CC, C - c0) * K;
+        for (int q = wave; q < (K * CC + 63) / 64; q += NW) {
+            const buf_rsrc rt = make_rsrc(w_dw + (size_t)c0 * K + 64 * q, max(n - 64 * q, 0) * 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, ws3 + 64 * q, 4, lane * 4, 0, 0, 0);
         }
     };
 
@@ -432,19 +432,37 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
                 Ds[(8 * dj + i) * CCP + (c ^ ((dj >> 1) << 2))] = s;  // swizzled: see read_d
             }
         } else {
-            float d[CPW];
+            // runtime K: the same lanes and chains, over blocks of 8 taps;
+            // block kb reads 16 staged steps from 8dj + kb (16-byte aligned:
+            // kb is a multiple of 8), and K <= 64 keeps them inside the
+            // row's 128 staged steps
+            static_assert(CPW == 8, "8 channels x 8 groups of 8 steps per wave");
+            const int dj = lane & 7, dc = lane >> 3;
+            const int c = wave * CPW + dc;
+            float sacc[8];
 #pragma unroll
-            for (int cc = 0; cc < CPW; ++cc) {
-                const float* wr = w_dw + (size_t)min(c0 + wave * CPW + cc, C - 1) * K;
-                const float* xr = xs + (wave * CPW + cc) * XP + lane;
-                float s = 0.f;
-                for (int k = 0; k < K; ++k) s += wr[k] * xr[k];
-                d[cc] = s;
+            for (int i = 0; i < 8; ++i) sacc[i] = 0.f;
+            for (int kb = 0; kb < K; kb += 8) {
+                float xv[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const floatx4 v = *reinterpret_cast<const floatx4*>(xs + c * XP + 8 * dj + kb + 4 * q);
+                    xv[4 * q] = v[0];
+                    xv[4 * q + 1] = v[1];
+                    xv[4 * q + 2] = v[2];
+                    xv[4 * q + 3] = v[3];
+                }
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    if (kb + kk < K) {
+                        const float wk = ws[c * K + kb + kk];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) sacc[i] += wk * xv[i + kk];
+                    }
+                }
             }
 #pragma unroll
-            for (int c4 = 0; c4 < CPW; c4 += 4)
-                *reinterpret_cast<floatx4*>(Ds + lane * CCP + ((wave * CPW + c4) ^ ((lane >> 4) << 2))) =
-                    floatx4{d[c4], d[c4 + 1], d[c4 + 2], d[c4 + 3]};
+            for (int i = 0; i < 8; ++i) Ds[(8 * dj + i) * CCP + (c ^ ((dj >> 1) << 2))] = sacc[i];
         }
         __syncthreads();
         if (c0 + CC < C) stage(c0 + CC);
@@ -540,9 +558,9 @@ using DwTall9 = DwsepCfg<FCONV_CFG_TALL>;
 using DwTallK = DwsepCfg<4, 4, 8, 1, 64, 0, 4>;
 
 template <class Cfg>
-static constexpr size_t tall_lds_bytes() {
+static constexpr size_t tall_lds_bytes(int K) {
     constexpr size_t ds = (size_t)(Cfg::TT * Cfg::CCP > Cfg::NW * 16 * 68 ? Cfg::TT * Cfg::CCP : Cfg::NW * 16 * 68);
-    return ((size_t)Cfg::CC * 132 + ds + (size_t)Cfg::NW * 64 + (size_t)(9 * Cfg::CC + 63) / 64 * 64) * sizeof(float);
+    return ((size_t)Cfg::CC * 132 + ds + (size_t)Cfg::NW * 64 + (size_t)(K * Cfg::CC + 63) / 64 * 64) * sizeof(float);
 }
 
 
@@ -726,7 +744,7 @@ static bool tall_tiles_fit(const DwsepShape& s) {
 template <class Cfg>
 static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                               const float* b_pw, float* y, hipStream_t stream) {
-    constexpr size_t lds = tall_lds_bytes<Cfg>();
+    const size_t lds = tall_lds_bytes<Cfg>(s.K);
     hipError_t e = hipFuncSetAttribute((const void*)dwsep_tall_kernel<Cfg>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -745,7 +763,7 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 static int pick_dw(const DwsepShape& s, bool vec_ok) {
     const bool unit = s.stride == 1 && s.dil == 1;
 #ifndef FCONV_DW_NO_TALL
-    if (unit && vec_ok && s.O > 256 && s.K <= 65 && s.C % 4 == 0 && tall_tiles_fit(s)) return s.K == 9 ? 5 : 6;
+    if (unit && vec_ok && s.O > 256 && s.K <= 64 && s.C % 4 == 0 && tall_tiles_fit(s)) return s.K == 9 ? 5 : 6;
 #endif
     if (s.O > 64) {
         if (unit && s.K == 9) return 1;

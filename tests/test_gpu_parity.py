@@ -461,7 +461,11 @@ TALL_DW = [
     # B, C, T, O, K, pad: O > 256 at stride 1 runs the 512 x 64 tile
     (2, 200, 130, 520, 9, 4),    # 3 full chunks + an 8-channel chunk (half a group), 2 output tiles
     (1, 68, 64, 257, 33, 16),    # runtime K, a 4-channel last chunk, one valid row in the 2nd block
-    (1, 64, 100, 300, 65, 32),   # the widest window the tile stages (K = 65)
+    (1, 64, 100, 300, 64, 32),   # the widest window the tile takes (K = 64: 8 full blocks of 8 taps)
+    (1, 64, 100, 300, 65, 32),   # one wider: the 256-row runtime-K kernel
+    (2, 36, 130, 512, 5, 2),     # runtime K inside one block of 8 taps
+    (1, 40, 96, 300, 8, 3),      # exactly one block, even K (asymmetric padding)
+    (1, 24, 80, 384, 17, 8),     # a last block with one tap
     (2, 16, 50, 512, 9, 0),      # a single partial chunk, T < 64, no padding
     (1, 32, 70, 300, 1, 0),      # 1-tap depthwise
     (1, 44, 200, 1100, 3, 1),    # three output tiles, C not a multiple of 16
