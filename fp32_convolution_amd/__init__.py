@@ -53,6 +53,7 @@ _SIGS = {
         [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
     "fconv2d_pool_map": (
         [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
+    "fconv2d_pool_debug_map": ([_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _vp], ctypes.c_int),
     "fconv2d_pool_sigmoid_sum_det": (
         [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, ctypes.c_size_t, _vp, _vp],
         ctypes.c_int),

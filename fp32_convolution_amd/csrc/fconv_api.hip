@@ -294,6 +294,11 @@ int fconv2d_pool_map(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t 
     return run_conv2d(x, B, Cin, H, W, w, Cout, K, bias, pool, algo, pooled, true, stream);
 }
 
+int fconv2d_pool_debug_map(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w,
+                           int64_t Cout, int64_t K, const float* bias, int64_t pool, float* pooled, void* stream) {
+    return run_conv2d(x, B, Cin, H, W, w, Cout, K, bias, pool, FCONV_ALGO_AUTO, pooled, true, stream);
+}
+
 int fconv2d_pool_sigmoid_sum_ex(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W, const float* w,
                                 int64_t Cout, int64_t K, const float* bias, int64_t pool, int pool_mode, int flags,
                                 int algo, float* out, void* stream) {

@@ -62,13 +62,15 @@
 extern "C" {
 #endif
 
-/* Status codes returned by every entry point. */
-#define FCONV_OK 0
-#define FCONV_EINVAL (-1)      /* an argument failed a check; nothing was enqueued */
-#define FCONV_EUNSUPPORTED (-2) /* the requested algorithm cannot run this shape   */
-#define FCONV_EHIP (-3)        /* the HIP runtime reported an error              */
-#define FCONV_ESCRATCH (-4)    /* more partial sums than the fixed scratch holds (see
-                                  fconv2d_pool_sigmoid_sum_det_noalloc); nothing was enqueued */
+/* Status codes returned (as int) by every entry point. */
+typedef enum fconv_status {
+    FCONV_OK = 0,
+    FCONV_EINVAL = -1,       /* an argument failed a check; nothing was enqueued */
+    FCONV_EUNSUPPORTED = -2, /* the requested algorithm cannot run this shape   */
+    FCONV_EHIP = -3,         /* the HIP runtime reported an error              */
+    FCONV_ESCRATCH = -4      /* more partial sums than the fixed scratch holds (see
+                                fconv2d_pool_sigmoid_sum_det_noalloc); nothing was enqueued */
+} fconv_status;
 
 /* Algorithms for the Conv2d path.  All compute the same result up to fp32
  * rounding.  AUTO picks the fastest one that supports the shape: BOXSUM,
@@ -190,6 +192,13 @@ int fconv2d_pool_sigmoid_sum_det_workspace(int64_t B, int64_t Cin, int64_t H, in
 int fconv2d_pool_map(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
                      const float* w, int64_t Cout, int64_t K, const float* bias, int64_t pool,
                      int algo, float* pooled, void* stream);
+
+/* fconv2d_pool_debug_map -- fconv2d_pool_map with algo = FCONV_ALGO_AUTO:
+ * the pooled map the default fconv2d_pool_sigmoid_sum call sums, with that
+ * call's arguments (pooled [B, Cout, PH, PW] in place of out).  Same errors. */
+int fconv2d_pool_debug_map(const float* x, int64_t B, int64_t Cin, int64_t H, int64_t W,
+                           const float* w, int64_t Cout, int64_t K, const float* bias, int64_t pool,
+                           float* pooled, void* stream);
 
 /* Output size of the pooled map: PH, PW (either may be 0).  Pure host
  * arithmetic, no device access.  FCONV_EINVAL on sizes < 1, H < K, W < K. */

@@ -50,7 +50,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for must in ["fconv2d_pool_sigmoid_sum", "dwsep_conv1d", "fconv2d_pool_map", "fconv_strerror",
+    for must in ["fconv2d_pool_sigmoid_sum", "dwsep_conv1d", "fconv2d_pool_map", "fconv2d_pool_debug_map",
+                 "fconv_strerror",
                  "fconv_version", "fconv2d_pool_sigmoid_sum_algo", "fconv2d_pool_out_size",
                  "fconv2d_select_algo", "dwsep_conv1d_out_len", "fconv2d_pool_sigmoid_sum_ex",
                  "fconv2d_pool_map_ex", "fconv2d_pool_out_size_ex", "fconv2d_pool_sigmoid_sum_det_ex",
@@ -197,6 +198,9 @@ def test_conv2d_entry_points_share_checks(lib):
     assert lib.fconv2d_pool_sigmoid_sum(None, 1, 1, 8, 8, FAKE, 1, 3, None, 2, FAKE, None) == EINVAL
     assert lib.fconv2d_pool_map(FAKE, 1, 1, 8, 8, FAKE, 1, 3, None, 0, 0, FAKE, None) == EINVAL
     assert lib.fconv2d_pool_map(FAKE, 1, 1, 8, 8, FAKE, 1, 9, None, 2, 1, FAKE, None) == EINVAL  # H < K
+    assert lib.fconv2d_pool_debug_map(FAKE, 1, 1, 8, 8, FAKE, 1, 3, None, 0, FAKE, None) == EINVAL
+    assert lib.fconv2d_pool_debug_map(FAKE, 1, 1, 8, 8, FAKE, 1, 9, None, 2, FAKE, None) == EINVAL  # H < K
+    assert lib.fconv2d_pool_debug_map(None, 1, 1, 8, 8, FAKE, 1, 3, None, 2, FAKE, None) == EINVAL
 
 
 def conv_ex(lib, x=FAKE, B=1, Cin=1, H=8, W=8, w=FAKE, Cout=1, K=3, b=None, pool=2, pool_mode=1, flags=0, algo=0,

@@ -129,6 +129,45 @@ def test_dwsep_conv1d_symbol(fc, name, side_stream):
     assert np.isfinite(got).all()
 
 
+@pytest.mark.parametrize("name", list(CONV_ITEMS))
+def test_fconv2d_pool_debug_map_symbol(fc, name):
+    # the pre-sigmoid pooled map of the default call: the oracle's map element by element (whole map
+    # for the tiny workload, whole items plus sampled outputs at full size), and bit for bit what
+    # fconv2d_pool_map returns with algo AUTO
+    cfg = fi.WORKLOADS[name]
+    announce(f"fconv2d_pool_debug_map (C ABI) on {name}")
+    x, w, b = fi.make(name, seed=0)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    B, Cin, H, W = x.shape
+    Cout, _, K, _ = w.shape
+    pool = cfg["pool"]
+    PH, PW = (H - K + 1) // pool, (W - K + 1) // pool
+    pooled = torch.full((B, Cout, PH, PW), float("nan"), device="cuda")
+    ref = torch.full_like(pooled, float("nan"))
+    st = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    rc = fc.lib.fconv2d_pool_debug_map(ptr(xd), B, Cin, H, W, ptr(wd), Cout, K, ptr(bd), pool, ptr(pooled),
+                                       ctypes.c_void_p(st.cuda_stream))
+    assert rc == 0, fc.lib.fconv_strerror(rc)
+    rc = fc.lib.fconv2d_pool_map(ptr(xd), B, Cin, H, W, ptr(wd), Cout, K, ptr(bd), pool, 0, ptr(ref),
+                                 ctypes.c_void_p(st.cuda_stream))
+    assert rc == 0, fc.lib.fconv_strerror(rc)
+    torch.cuda.synchronize()
+    got = pooled.cpu().numpy()
+    assert np.array_equal(got, ref.cpu().numpy())
+    if name == "conv2d_tiny":
+        _, want = oracle.conv2d_pool_sigmoid_sum(x, w, b, pool, want_pooled=True)
+        assert_close(got, want, f"{name} pooled map")
+        return
+    rng = np.random.default_rng(33)
+    n = 20000
+    samp = np.stack([rng.integers(0, B, n), rng.integers(0, Cout, n), rng.integers(0, PH, n),
+                     rng.integers(0, PW, n)], axis=1)
+    want = oracle.conv2d_pooled_at(x, w, b, pool, samp)
+    assert_close(got[tuple(samp.T)], want, f"{name} pooled sampled")
+    assert np.isfinite(got).all()
+
+
 def test_symbols_refuse_bad_arguments_before_launch(fc):
     # host checks on real buffers: nothing is enqueued and the output keeps its contents
     announce("C ABI argument checks with real buffers")
