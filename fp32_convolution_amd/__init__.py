@@ -164,7 +164,7 @@ def conv2d_pool_sigmoid_sum(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO,
                             relu: bool = False, ceil_mode: bool = False):
     """Conv2d(stride 1, no pad) -> [ReLU] -> AvgPool2d or MaxPool2d(pool, floor or ceil) -> sigmoid -> sum
     over (C,H,W): out[B].  The defaults are the plain chain (average pool, no ReLU, floor).  The sum's
-    partials take scratch from the library's stream-ordered pool; repeated calls give identical bits."""
+    partials take scratch the library keeps per stream (else from its stream-ordered pool); repeated calls give identical bits."""
     _conv2d_args(x, w, b)
     B, Cin, H, W = x.shape
     Cout, _, K, _ = w.shape

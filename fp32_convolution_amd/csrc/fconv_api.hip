@@ -128,20 +128,100 @@ hipMemPool_t partials_pool() {
     return pools[dev];
 }
 
-// A fused sum: `launch(ws)` writes B * parts partial sums to ws, taken from
-// the pool in stream order on `st`; reduce_partials adds each item's partials
-// in a fixed order into out[b]; ws goes back to the pool in stream order.
-// Calls on different streams therefore never share scratch.
+// Scratch kept per (device, stream).  A stream's partial sums go to a buffer
+// that only calls on that stream use, so a call makes no allocation (the
+// pool's stream-ordered allocate and free cost about 8 us of host time per
+// call).  Stream handles are reused (a destroyed stream's handle comes back
+// for the next stream created, possibly while the old stream's work still
+// runs), so each slot carries an event recorded after every use: a call
+// waits on it (on the GPU) before it touches the buffer, and a buffer is
+// freed only in stream order after it.  kStreamSlots streams per device hold
+// a slot (the least recently used one passes to a new stream), each buffer at
+// most kSlotMaxBytes, kept until the process ends; larger requests and
+// streams being captured into a graph allocate per call from the pool.
+constexpr int kStreamSlots = 8;
+constexpr size_t kSlotMaxBytes = (size_t)1 << 20;
+constexpr size_t kSlotMinBytes = (size_t)64 << 10;
+
+struct StreamSlot {
+    hipStream_t stream;
+    void* buf;         // from the partials pool, allocated in stream order
+    size_t bytes;
+    hipEvent_t done;   // recorded after the last call that used the slot
+    uint64_t last;     // use counter, for eviction
+};
+
+std::mutex g_slot_mu;
+StreamSlot g_slots[kMaxDevices][kStreamSlots] = {};
+uint64_t g_slot_clock = 0;
+
+// The slot of stream `st` with a buffer of at least `bytes`, ready to use on
+// st (st already waits for the slot's previous use); nullptr when the call
+// should allocate per call (*err says whether that is because of an error).
+StreamSlot* stream_scratch(hipStream_t st, size_t bytes, hipMemPool_t pool, hipError_t* err) {
+    *err = hipSuccess;
+    if (bytes > kSlotMaxBytes) return nullptr;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_slot_mu);
+    StreamSlot* e = nullptr;
+    StreamSlot* lru = &g_slots[dev][0];
+    for (StreamSlot& t : g_slots[dev]) {
+        if (t.buf && t.stream == st) e = &t;
+        if (!t.buf ? (lru->buf != nullptr) : (lru->buf && t.last < lru->last)) lru = &t;
+    }
+    if (!e) {
+        // an empty slot, else the least recently used one, whose buffer
+        // passes to this stream
+        e = lru;
+        if (!e->done && (*err = hipEventCreateWithFlags(&e->done, hipEventDisableTiming)) != hipSuccess) {
+            e->done = nullptr;
+            return nullptr;
+        }
+    }
+    // the slot's previous use (this stream's, an earlier stream's that had
+    // this handle, or an evicted stream's) before anything below touches or
+    // frees its buffer
+    if ((*err = hipStreamWaitEvent(st, e->done, 0)) != hipSuccess) return nullptr;
+    e->stream = st;
+    if (e->bytes < bytes) {
+        size_t nb = e->bytes ? 2 * e->bytes : kSlotMinBytes;
+        while (nb < bytes) nb *= 2;
+        if (nb > kSlotMaxBytes) nb = kSlotMaxBytes;
+        void* buf = nullptr;
+        if ((*err = hipMallocFromPoolAsync(&buf, nb, pool, st)) != hipSuccess) return nullptr;
+        if (e->buf && (*err = hipFreeAsync(e->buf, st)) != hipSuccess) {
+            (void)hipFreeAsync(buf, st);
+            return nullptr;
+        }
+        e->buf = buf;
+        e->bytes = nb;
+    }
+    e->last = ++g_slot_clock;
+    return e;
+}
+
+// A fused sum: `launch(ws)` writes B * parts partial sums to ws (the
+// stream's slot, else a block taken from the pool in stream order on `st`
+// and returned after the call); reduce_partials adds each item's partials
+// in a fixed order into out[b].  Calls on different streams never share
+// scratch at the same time.
 template <class Launch>
 int sum_through_partials(int64_t parts, int B, float* out, hipStream_t st, Launch&& launch) {
     hipMemPool_t pool = partials_pool();
     if (!pool) return FCONV_EHIP;
-    void* ws = nullptr;
-    if (hipMallocFromPoolAsync(&ws, (size_t)parts * (size_t)B * sizeof(float), pool, st) != hipSuccess)
-        return FCONV_EHIP;
-    hipError_t e = launch((float*)ws);
+    const size_t bytes = (size_t)parts * (size_t)B * sizeof(float);
+    hipError_t e = hipSuccess;
+    StreamSlot* slot = stream_scratch(st, bytes, pool, &e);
+    if (e != hipSuccess) return FCONV_EHIP;
+    void* ws = slot ? slot->buf : nullptr;
+    if (!slot && hipMallocFromPoolAsync(&ws, bytes, pool, st) != hipSuccess) return FCONV_EHIP;
+    e = launch((float*)ws);
     if (e == hipSuccess) e = fconv::reduce_partials((float*)ws, parts, B, out, st);
-    const hipError_t ef = hipFreeAsync(ws, st);
+    // mark the slot's use (also after a failed launch: what was enqueued may still run)
+    const hipError_t ef = slot ? hipEventRecord(slot->done, st) : hipFreeAsync(ws, st);
     return (e == hipSuccess && ef == hipSuccess) ? FCONV_OK : FCONV_EHIP;
 }
 

@@ -30,9 +30,13 @@
  *     fused sums (fconv2d_pool_sigmoid_sum, _algo, _ex) take their partial
  *     sums' scratch (at most 4 KiB per batch item) from a memory pool the
  *     library creates per device on first use and keeps until the process
- *     ends: allocated and freed in stream order on the call's stream
- *     (hipMallocFromPoolAsync / hipFreeAsync), so concurrent calls never
- *     share it, and `stream` must belong to the current device.  No other
+ *     ends, allocated in stream order on the call's stream
+ *     (hipMallocFromPoolAsync).  Up to 8 streams per device keep a buffer
+ *     of up to 1 MiB between calls, guarded by an event the library records
+ *     after each use and waits on (on the GPU) before the next; other calls,
+ *     and calls on a stream being captured into a graph, allocate per call
+ *     and free in stream order (hipFreeAsync).  Concurrent calls never share
+ *     scratch, and `stream` must belong to the current device.  No other
  *     entry point allocates device memory.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *     Every call is asynchronous with respect to the host: it enqueues its

@@ -7,6 +7,7 @@ write; the scalar sums are checked as well.  Full-size workloads compare
 sampled outputs that the oracle computes one by one, plus whole batch items.
 """
 
+import ctypes
 import sys
 
 import numpy as np
@@ -361,6 +362,76 @@ def test_conv2d_default_sum_scratch(fc, algo):
     torch.cuda.synchronize()
     for i in range(2):
         assert np.array_equal(outs[i].cpu().numpy().view(np.uint32), ref[i].view(np.uint32)), shapes[i]
+
+
+def _hip_runtime():
+    # the HIP runtime this process already runs on (torch's and the library's)
+    import re
+
+    paths = sorted(set(re.findall(r"(/\S*libamdhip64\.so\S*)", open("/proc/self/maps").read())))
+    assert paths, "no HIP runtime mapped"
+    hip = ctypes.CDLL(paths[0])
+    hip.hipStreamCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def test_conv2d_default_sum_many_streams(fc):
+    # more streams than the library keeps scratch slots for: every call on every stream, three rounds, gives
+    # the caller-workspace call's bits (streams past the slots evict the least recently used one)
+    announce("conv2d default-call scratch on 12 streams")
+    n = 12
+    shapes = [(2 + i % 3, 3 + i % 5, 40 + 3 * i, 44 + 2 * i, 8 + 4 * i, 3) for i in range(n)]
+    devs = [tuple(dev(a) for a in fi.conv2d_inputs(*sh, seed=60 + i)) for i, sh in enumerate(shapes)]
+    ref = [fc.conv2d_pool_sigmoid_sum_det(*d, 4).cpu().numpy() for d in devs]
+    streams = [torch.cuda.Stream() for _ in range(n)]
+    outs = [[torch.full((sh[0],), float("nan"), device="cuda") for sh in shapes] for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in range(3):
+        for d, o, st in zip(devs, outs[r], streams):
+            with torch.cuda.stream(st):
+                fc.conv2d_pool_sigmoid_sum(*d, 4, out=o)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for i in range(n):
+            assert np.array_equal(outs[r][i].cpu().numpy().view(np.uint32), ref[i].view(np.uint32)), (r, shapes[i])
+
+
+def test_conv2d_default_sum_reused_stream_handle(fc):
+    # a stream destroyed with calls still queued, and a new stream that gets the same handle: the new
+    # stream's call must not overlap the old stream's use of that handle's scratch
+    announce("conv2d default-call scratch across a destroyed and re-created stream handle")
+    hip = _hip_runtime()
+    sh1, sh2 = (16, 8, 256, 256, 64, 3), (6, 5, 120, 90, 24, 3)
+    d1 = tuple(dev(a) for a in fi.conv2d_inputs(*sh1, seed=70))
+    d2 = tuple(dev(a) for a in fi.conv2d_inputs(*sh2, seed=71))
+    ref1 = fc.conv2d_pool_sigmoid_sum_det(*d1, 4).cpu().numpy()
+    ref2 = fc.conv2d_pool_sigmoid_sum_det(*d2, 4).cpu().numpy()
+    outs1 = [torch.full((sh1[0],), float("nan"), device="cuda") for _ in range(4)]
+    out2 = torch.full((sh2[0],), float("nan"), device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    call = lambda d, sh, o, st: fc.lib.fconv2d_pool_sigmoid_sum(P(d[0]), sh[0], sh[1], sh[2], sh[3], P(d[1]), sh[4],
+                                                               sh[5], P(d[2]), 4, P(o), st)
+    torch.cuda.synchronize()
+    handles = []
+    for rep in range(3):
+        a = ctypes.c_void_p()
+        assert hip.hipStreamCreate(ctypes.byref(a)) == 0
+        for o in outs1:
+            assert call(d1, sh1, o, a) == 0
+        assert hip.hipStreamDestroy(a) == 0  # calls may still be queued
+        b = ctypes.c_void_p()
+        assert hip.hipStreamCreate(ctypes.byref(b)) == 0
+        handles.append((a.value, b.value))
+        assert call(d2, sh2, out2, b) == 0
+        torch.cuda.synchronize()
+        assert hip.hipStreamDestroy(b) == 0
+        for o in outs1:
+            assert np.array_equal(o.cpu().numpy().view(np.uint32), ref1.view(np.uint32)), rep
+        assert np.array_equal(out2.cpu().numpy().view(np.uint32), ref2.view(np.uint32)), rep
+        for o in outs1 + [out2]:
+            o.fill_(float("nan"))
+    print(f"[gpu-case] stream handles (destroyed, new): {handles}", flush=True)
 
 
 FULL_CONV = {
