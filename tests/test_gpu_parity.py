@@ -397,6 +397,44 @@ def test_conv2d_default_sum_many_streams(fc):
             assert np.array_equal(outs[r][i].cpu().numpy().view(np.uint32), ref[i].view(np.uint32)), (r, shapes[i])
 
 
+def test_conv2d_default_sum_host_threads(fc):
+    # four host threads, each with its own stream, issuing default calls at once through the C ABI (ctypes
+    # releases the GIL during a call, so the library's slot table is entered concurrently): every output
+    # matches the caller-workspace call's bits
+    import threading
+
+    announce("conv2d default-call scratch from 4 host threads")
+    shapes = [(3, 4, 50, 60, 24, 3), (2, 8, 70, 72, 64, 3), (4, 3, 41, 44, 16, 3), (1, 16, 60, 50, 128, 5)]
+    pools = [4, 4, 4, 3]
+    devs = [tuple(dev(a) for a in fi.conv2d_inputs(*sh, seed=80 + i)) for i, sh in enumerate(shapes)]
+    ref = [fc.conv2d_pool_sigmoid_sum_det(*d, pl).cpu().numpy() for d, pl in zip(devs, pools)]
+    streams = [torch.cuda.Stream() for _ in shapes]
+    rounds = 25
+    outs = [[torch.full((sh[0],), float("nan"), device="cuda") for _ in range(rounds)] for sh in shapes]
+    torch.cuda.synchronize()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    errors = []
+
+    def worker(i):
+        sh, d, st = shapes[i], devs[i], ctypes.c_void_p(streams[i].cuda_stream)
+        for r in range(rounds):
+            rc = fc.lib.fconv2d_pool_sigmoid_sum(P(d[0]), sh[0], sh[1], sh[2], sh[3], P(d[1]), sh[4], sh[5],
+                                                 P(d[2]), pools[i], P(outs[i][r]), st)
+            if rc != 0:
+                errors.append((i, r, rc))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(len(shapes)):
+        for r in range(rounds):
+            assert np.array_equal(outs[i][r].cpu().numpy().view(np.uint32), ref[i].view(np.uint32)), (i, r)
+
+
 def test_conv2d_default_sum_reused_stream_handle(fc):
     # a stream destroyed with calls still queued, and a new stream that gets the same handle: the new
     # stream's call must not overlap the old stream's use of that handle's scratch
