@@ -112,17 +112,28 @@ def _dev_f32(t, name):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32, got {t.dtype}")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU device, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
 
 
-# Every call runs with the tensors' device current and enqueues on that
-# device's current torch stream.
-def _stream(t):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+# torch's current stream on a device as a raw handle: the private accessor
+# skips building a Stream object (a few microseconds a call, which is most
+# of a small call's cost); the public one is the fallback.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _call(t, fn, *args):
+    """Calls fn(*args, stream) with t's device current (switching only when
+    another one is) and that device's current torch stream."""
+    idx = t.get_device()
+    st = ctypes.c_void_p(_raw_stream(idx) if _raw_stream is not None else torch.cuda.current_stream(idx).cuda_stream)
+    if idx == torch.cuda.current_device():
+        return fn(*args, st)
+    with torch.cuda.device(idx):
+        return fn(*args, st)
 
 
 def version() -> int:
@@ -156,7 +167,8 @@ def _conv2d_args(x, w, b):
         raise ValueError(f"expected x[B,Cin,H,W] and w[Cout,Cin,K,K], got {tuple(x.shape)} and {tuple(w.shape)}")
     if b is not None and tuple(b.shape) != (w.shape[0],):
         raise ValueError(f"bias must be [Cout]={w.shape[0]}, got {tuple(b.shape)}")
-    if x.device != w.device or (b is not None and b.device != x.device):
+    d = x.get_device()
+    if w.get_device() != d or (b is not None and b.get_device() != d):
         raise ValueError("x, w and bias must be on the same device")
 
 
@@ -172,16 +184,15 @@ def conv2d_pool_sigmoid_sum(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO,
         out = torch.empty(B, dtype=torch.float32, device=x.device)
     else:
         _dev_f32(out, "out")
-        if tuple(out.shape) != (B,) or out.device != x.device:
+        if tuple(out.shape) != (B,) or out.get_device() != x.get_device():
             raise ValueError("out must be [B] on x's device")
     flags = _pool_flags(relu, ceil_mode)
-    with torch.cuda.device(x.device):
-        if pool_mode == POOL_AVG and flags == 0:
-            rc = lib.fconv2d_pool_sigmoid_sum_algo(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
-                                                   _ptr(out), _stream(x))
-        else:
-            rc = lib.fconv2d_pool_sigmoid_sum_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode,
-                                                 flags, algo, _ptr(out), _stream(x))
+    if pool_mode == POOL_AVG and flags == 0:
+        rc = _call(x, lib.fconv2d_pool_sigmoid_sum_algo, _ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
+                   _ptr(out))
+    else:
+        rc = _call(x, lib.fconv2d_pool_sigmoid_sum_ex, _ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool,
+                   pool_mode, flags, algo, _ptr(out))
     _check(rc, "fconv2d_pool_sigmoid_sum")
     return out
 
@@ -215,22 +226,21 @@ def conv2d_pool_sigmoid_sum_det(x, w, b, pool: int, out=None, algo: int = ALGO_A
         out = torch.empty(B, dtype=torch.float32, device=x.device)
     else:
         _dev_f32(out, "out")
-        if tuple(out.shape) != (B,) or out.device != x.device:
+        if tuple(out.shape) != (B,) or out.get_device() != x.get_device():
             raise ValueError("out must be [B] on x's device")
     need = conv2d_det_workspace_bytes(B, Cin, H, W, Cout, K, pool, algo, pool_mode, relu, ceil_mode)
     if workspace is None:
         workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=x.device)
-    if workspace.device != x.device or not workspace.is_contiguous():
+    if not workspace.is_cuda or workspace.get_device() != x.get_device() or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on x's device")
     nbytes = workspace.numel() * workspace.element_size()
     flags = _pool_flags(relu, ceil_mode)
-    with torch.cuda.device(x.device):
-        if pool_mode == POOL_AVG and flags == 0:
-            rc = lib.fconv2d_pool_sigmoid_sum_det(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
-                                                  _ptr(workspace), nbytes, _ptr(out), _stream(x))
-        else:
-            rc = lib.fconv2d_pool_sigmoid_sum_det_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode,
-                                                     flags, algo, _ptr(workspace), nbytes, _ptr(out), _stream(x))
+    if pool_mode == POOL_AVG and flags == 0:
+        rc = _call(x, lib.fconv2d_pool_sigmoid_sum_det, _ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
+                   _ptr(workspace), nbytes, _ptr(out))
+    else:
+        rc = _call(x, lib.fconv2d_pool_sigmoid_sum_det_ex, _ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool,
+                   pool_mode, flags, algo, _ptr(workspace), nbytes, _ptr(out))
     _check(rc, "fconv2d_pool_sigmoid_sum_det")
     return out
 
@@ -243,11 +253,10 @@ def conv2d_pool_sigmoid_sum_det_noalloc(x, w, b, pool: int, out, algo: int = ALG
     B, Cin, H, W = x.shape
     Cout, _, K, _ = w.shape
     _dev_f32(out, "out")
-    if tuple(out.shape) != (B,) or out.device != x.device:
+    if tuple(out.shape) != (B,) or out.get_device() != x.get_device():
         raise ValueError("out must be [B] on x's device")
-    with torch.cuda.device(x.device):
-        rc = lib.fconv2d_pool_sigmoid_sum_det_noalloc(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo,
-                                                      _ptr(out), _stream(x))
+    rc = _call(x, lib.fconv2d_pool_sigmoid_sum_det_noalloc, _ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool,
+               algo, _ptr(out))
     _check(rc, "fconv2d_pool_sigmoid_sum_det_noalloc")
     return out
 
@@ -263,16 +272,14 @@ def conv2d_pool_map(x, w, b, pool: int, out=None, algo: int = ALGO_AUTO, pool_mo
         out = torch.empty((B, Cout, PH, PW), dtype=torch.float32, device=x.device)
     else:
         _dev_f32(out, "out")
-        if tuple(out.shape) != (B, Cout, PH, PW) or out.device != x.device:
+        if tuple(out.shape) != (B, Cout, PH, PW) or out.get_device() != x.get_device():
             raise ValueError("out must be [B,Cout,PH,PW] on x's device")
     flags = _pool_flags(relu, ceil_mode)
-    with torch.cuda.device(x.device):
-        if pool_mode == POOL_AVG and flags == 0:
-            rc = lib.fconv2d_pool_map(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo, _ptr(out),
-                                      _stream(x))
-        else:
-            rc = lib.fconv2d_pool_map_ex(_ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode, flags, algo,
-                                         _ptr(out), _stream(x))
+    if pool_mode == POOL_AVG and flags == 0:
+        rc = _call(x, lib.fconv2d_pool_map, _ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, algo, _ptr(out))
+    else:
+        rc = _call(x, lib.fconv2d_pool_map_ex, _ptr(x), B, Cin, H, W, _ptr(w), Cout, K, _ptr(b), pool, pool_mode,
+                   flags, algo, _ptr(out))
     _check(rc, "fconv2d_pool_map")
     return out
 
@@ -305,8 +312,9 @@ def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None, stride: int = 1, dilat
     O = w_pw.shape[0]
     if b_pw is not None and tuple(b_pw.shape) != (O,):
         raise ValueError(f"b_pw must be [O]={O}")
+    d = x.get_device()
     for t in (w_dw, w_pw, b_pw, out):
-        if t is not None and t.device != x.device:
+        if t is not None and t.get_device() != d:
             raise ValueError("all tensors must be on x's device")
     Tout = dwsep_out_len(T, K, pad, stride, dilation)
     if Tout < 1:
@@ -317,8 +325,7 @@ def dwsep_conv1d(x, w_dw, w_pw, b_pw, pad: int, out=None, stride: int = 1, dilat
         _dev_f32(out, "out")
         if tuple(out.shape) != (B, O, Tout):
             raise ValueError(f"out must be [B,O,Tout]=({B},{O},{Tout})")
-    with torch.cuda.device(x.device):
-        rc = lib.dwsep_conv1d_algo(_ptr(x), B, C, T, _ptr(w_dw), K, _ptr(w_pw), O, _ptr(b_pw), pad, stride, dilation,
-                                   algo, _ptr(out), _stream(x))
+    rc = _call(x, lib.dwsep_conv1d_algo, _ptr(x), B, C, T, _ptr(w_dw), K, _ptr(w_pw), O, _ptr(b_pw), pad, stride,
+               dilation, algo, _ptr(out))
     _check(rc, "dwsep_conv1d")
     return out
