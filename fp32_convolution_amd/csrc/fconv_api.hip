@@ -136,9 +136,12 @@ hipMemPool_t partials_pool() {
 // runs), so each slot carries an event recorded after every use: a call
 // waits on it (on the GPU) before it touches the buffer, and a buffer is
 // freed only in stream order after it.  kStreamSlots streams per device hold
-// a slot (the least recently used one passes to a new stream), each buffer at
-// most kSlotMaxBytes, kept until the process ends; larger requests and
-// streams being captured into a graph allocate per call from the pool.
+// a slot (the least recently used idle one passes to a new stream), each
+// buffer at most kSlotMaxBytes, kept until the process ends.  A slot counts
+// the calls between taking it and recording its event (other host threads
+// may be inside one): a slot so in use is neither handed to another stream
+// nor regrown.  Larger requests, streams being captured into a graph, and
+// calls that find no idle slot allocate per call from the pool.
 constexpr int kStreamSlots = 8;
 constexpr size_t kSlotMaxBytes = (size_t)1 << 20;
 constexpr size_t kSlotMinBytes = (size_t)64 << 10;
@@ -149,6 +152,7 @@ struct StreamSlot {
     size_t bytes;
     hipEvent_t done;   // recorded after the last call that used the slot
     uint64_t last;     // use counter, for eviction
+    int busy;          // calls between stream_scratch and their event record
 };
 
 std::mutex g_slot_mu;
@@ -156,8 +160,9 @@ StreamSlot g_slots[kMaxDevices][kStreamSlots] = {};
 uint64_t g_slot_clock = 0;
 
 // The slot of stream `st` with a buffer of at least `bytes`, ready to use on
-// st (st already waits for the slot's previous use); nullptr when the call
-// should allocate per call (*err says whether that is because of an error).
+// st (st already waits for the slot's previous use) and counted busy until
+// release_slot; nullptr when the call should allocate per call (*err says
+// whether that is because of an error).
 StreamSlot* stream_scratch(hipStream_t st, size_t bytes, hipMemPool_t pool, hipError_t* err) {
     *err = hipSuccess;
     if (bytes > kSlotMaxBytes) return nullptr;
@@ -167,14 +172,16 @@ StreamSlot* stream_scratch(hipStream_t st, size_t bytes, hipMemPool_t pool, hipE
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
     std::lock_guard<std::mutex> lock(g_slot_mu);
     StreamSlot* e = nullptr;
-    StreamSlot* lru = &g_slots[dev][0];
+    StreamSlot* lru = nullptr;  // idle slots only: empty first, else least recently used
     for (StreamSlot& t : g_slots[dev]) {
         if (t.buf && t.stream == st) e = &t;
-        if (!t.buf ? (lru->buf != nullptr) : (lru->buf && t.last < lru->last)) lru = &t;
+        if (t.busy == 0 && (!lru || (!t.buf ? lru->buf != nullptr : (lru->buf && t.last < lru->last)))) lru = &t;
     }
+    if (e && e->busy > 0 && e->bytes < bytes) return nullptr;  // in use by another call: not regrown
     if (!e) {
-        // an empty slot, else the least recently used one, whose buffer
+        // an empty slot, else the least recently used idle one, whose buffer
         // passes to this stream
+        if (!lru) return nullptr;
         e = lru;
         if (!e->done && (*err = hipEventCreateWithFlags(&e->done, hipEventDisableTiming)) != hipSuccess) {
             e->done = nullptr;
@@ -200,7 +207,14 @@ StreamSlot* stream_scratch(hipStream_t st, size_t bytes, hipMemPool_t pool, hipE
         e->bytes = nb;
     }
     e->last = ++g_slot_clock;
+    ++e->busy;
     return e;
+}
+
+// Ends a call's use of its slot (after its event is recorded).
+void release_slot(StreamSlot* e) {
+    std::lock_guard<std::mutex> lock(g_slot_mu);
+    --e->busy;
 }
 
 // A fused sum: `launch(ws)` writes B * parts partial sums to ws (the
@@ -221,7 +235,13 @@ int sum_through_partials(int64_t parts, int B, float* out, hipStream_t st, Launc
     e = launch((float*)ws);
     if (e == hipSuccess) e = fconv::reduce_partials((float*)ws, parts, B, out, st);
     // mark the slot's use (also after a failed launch: what was enqueued may still run)
-    const hipError_t ef = slot ? hipEventRecord(slot->done, st) : hipFreeAsync(ws, st);
+    hipError_t ef;
+    if (slot) {
+        ef = hipEventRecord(slot->done, st);
+        release_slot(slot);
+    } else {
+        ef = hipFreeAsync(ws, st);
+    }
     return (e == hipSuccess && ef == hipSuccess) ? FCONV_OK : FCONV_EHIP;
 }
 

@@ -397,15 +397,18 @@ def test_conv2d_default_sum_many_streams(fc):
             assert np.array_equal(outs[r][i].cpu().numpy().view(np.uint32), ref[i].view(np.uint32)), (r, shapes[i])
 
 
-def test_conv2d_default_sum_host_threads(fc):
-    # four host threads, each with its own stream, issuing default calls at once through the C ABI (ctypes
-    # releases the GIL during a call, so the library's slot table is entered concurrently): every output
-    # matches the caller-workspace call's bits
+@pytest.mark.parametrize("nthreads", [4, 12])
+def test_conv2d_default_sum_host_threads(fc, nthreads):
+    # host threads, each with its own stream, issuing default calls at once through the C ABI (ctypes
+    # releases the GIL during a call, so the library's slot table is entered concurrently; with 12 threads
+    # there are more streams than slots, so slots pass between streams while others are in use): every
+    # output matches the caller-workspace call's bits
     import threading
 
-    announce("conv2d default-call scratch from 4 host threads")
-    shapes = [(3, 4, 50, 60, 24, 3), (2, 8, 70, 72, 64, 3), (4, 3, 41, 44, 16, 3), (1, 16, 60, 50, 128, 5)]
-    pools = [4, 4, 4, 3]
+    announce(f"conv2d default-call scratch from {nthreads} host threads")
+    base = [(3, 4, 50, 60, 24, 3), (2, 8, 70, 72, 64, 3), (4, 3, 41, 44, 16, 3), (1, 16, 60, 50, 128, 5)]
+    shapes = [base[i % 4][:2] + (base[i % 4][2] + i, base[i % 4][3] + 2 * i) + base[i % 4][4:] for i in range(nthreads)]
+    pools = [3 if sh[5] == 5 else 4 for sh in shapes]
     devs = [tuple(dev(a) for a in fi.conv2d_inputs(*sh, seed=80 + i)) for i, sh in enumerate(shapes)]
     ref = [fc.conv2d_pool_sigmoid_sum_det(*d, pl).cpu().numpy() for d, pl in zip(devs, pools)]
     streams = [torch.cuda.Stream() for _ in shapes]
