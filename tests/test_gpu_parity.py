@@ -614,6 +614,20 @@ def test_dwsep_tall_tile(fc, shape):
     assert_close(got, want, f"y {shape}")
 
 
+def test_dwsep_tall_tile_every_k(fc):
+    # every depthwise width the tall tile takes (K = 1 .. 64; K = 9 is its compiled instance, the rest run
+    # the runtime-K stage over blocks of 8 taps), with odd and even padding and a partial channel chunk,
+    # against the oracle; K = 65 goes to the 256-row kernel and is checked the same way
+    announce("dwsep tall tile, K = 1 .. 65")
+    B, C, T, O = 1, 36, 100, 300
+    for K in range(1, 66):
+        pad = K // 2 if K % 3 else (K - 1) // 2
+        x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=300 + K)
+        want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad)
+        got = fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad).cpu().numpy()
+        assert_close(got, want, f"y K={K} pad={pad}")
+
+
 def test_dwsep_tall_tile_inf_in_next_row(fc):
     # Padded channels of a partial group must form no product: an infinite
     # weight in row o+1 may not reach row o.
