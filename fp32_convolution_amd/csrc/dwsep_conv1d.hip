@@ -286,10 +286,10 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 // steps per block.
 // LDS: xs [CC][132], then Ds: [64][CC+4] for the GEMM operand and
 // 8 x [16][68] in the epilogue, then the bias [512] and the taps [CC][K]
-// (72.9 KB for K = 9, two workgroups per CU up to K = 30).  Row r of xs
-// holds input steps t0-pad .. t0-pad+127 (two 64-lane runs; steps past the
-// K-1 halo or outside [0, T) load as 0); the runtime-K blocks read up to
-// step 8*7 + 8*floor((K-1)/8) + 15, so K <= 64.
+// (70,656 + 256 K bytes: 72,960 for K = 9, two workgroups per CU up to
+// K = 44).  Row r of xs holds input steps t0-pad .. t0-pad+127 (two 64-lane
+// runs; steps past the K-1 halo or outside [0, T) load as 0); the runtime-K
+// blocks read up to step 8*7 + 8*floor((K-1)/8) + 15, so K <= 64.
 // Pointwise weights: lane (g, l16) of block ob keeps channels 4g..4g+3 of
 // the current group; the registers of block ob are refilled with the next
 // group's weights as soon as its 16 matrix instructions are issued.
