@@ -333,6 +333,16 @@ def err_over_tol(got, want):
     return float((np.abs(got - want) / (1e-4 + 1e-4 * np.abs(want))).max())
 
 
+def abs_rel_err(got, want):
+    """Largest |gpu - oracle|, and largest |gpu - oracle| / |oracle| over the outputs with
+    |oracle| >= 1e-4 (below that the tolerance's absolute term governs)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    d = np.abs(got - want)
+    big = np.abs(want) >= 1e-4
+    return float(d.max()), (float((d[big] / np.abs(want[big])).max()) if big.any() else 0.0)
+
+
 ALGO_NAMES = {0: "FCONV_ALGO_AUTO", 1: "FCONV_ALGO_DIRECT_MFMA", 2: "FCONV_ALGO_DIRECT_SIMPLE", 3: "FCONV_ALGO_BOXSUM"}
 
 
@@ -737,12 +747,15 @@ def main():
             t = time.perf_counter() - t0
             t_base[name] = t
             par = {"oracle_s": round(t, 3), "oracle_threads": threads,
-                   "checked": "every output of every batch item"}
+                   "checked": "every output of every batch item",
+                   "rel_err_over": "outputs with |oracle| >= 1e-4"}
             if cfg["kind"] == "conv2d":
                 for call_algo, key in ((0, "default"), (fc.ALGO_DIRECT_MFMA, "direct_mfma")):
                     if (name, call_algo) in conv_outputs:
                         r = err_over_tol(conv_outputs[(name, call_algo)], want)
                         par[f"{key}_max_err_over_tol"] = r
+                        par[f"{key}_max_abs_err"], par[f"{key}_max_rel_err"] = abs_rel_err(
+                            conv_outputs[(name, call_algo)], want)
                         parity_ok &= r <= 1.0
                 if name == CONV:
                     r = err_over_tol(out.cpu().numpy(), want)   # the timed step's own results
@@ -751,6 +764,7 @@ def main():
             else:
                 r = err_over_tol(dw_outputs[name], want)
                 par["default_max_err_over_tol"] = r
+                par["default_max_abs_err"], par["default_max_rel_err"] = abs_rel_err(dw_outputs[name], want)
                 parity_ok &= r <= 1.0
                 if name == DW:
                     r = err_over_tol(y.cpu().numpy(), want)
