@@ -716,6 +716,23 @@ def test_dwsep_unaligned_weights(fc, O):
     assert_close(got, want, "y unaligned")
 
 
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_dwsep_unaligned_output(fc, offset):
+    # y starting 4, 8 or 12 bytes past a 16-byte boundary (Tout a multiple of 4): the tall tile stores
+    # element by element instead of in 16-byte rows; the elements around y stay untouched
+    announce(f"dwsep unaligned y, offset {offset} floats")
+    B, C, T, O, K, pad = 2, 40, 128, 300, 9, 4
+    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=10 + offset)
+    want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad)
+    n = B * O * T
+    buf = torch.full((n + 8,), 7.0, device="cuda")
+    y = buf[offset:offset + n].view(B, O, T)
+    fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad, out=y)
+    assert_close(y.cpu().numpy(), want, f"y offset {offset}")
+    rest = torch.cat([buf[:offset], buf[offset + n:]]).cpu().numpy()
+    assert (rest == 7.0).all()
+
+
 def test_dwsep_full_size(fc):
     name = "dwsep_full"
     cfg = fi.WORKLOADS[name]
