@@ -355,6 +355,9 @@ def main():
                     help="untimed whole steps run first for this long, so that the clocks have left their idle state")
     ap.add_argument("--reps", type=int, default=20, help="timed repetitions per call in `configs` and `variants`")
     ap.add_argument("--per-rep", type=int, default=10, help="back-to-back calls between one event pair")
+    ap.add_argument("--call-warm-s", type=float, default=0.05,
+                    help="untimed calls of the same call for at least this long before its timed runs in `configs` "
+                         "and `variants`, so that the clocks leave the state the previous (lighter or idle) work left")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity legs")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -451,9 +454,18 @@ def main():
     def time_calls(fn):
         """ms per call: `reps` runs of `per_rep` back-to-back calls, each run
         between one event pair (so host time between calls is hidden as it
-        is in a stream of calls), after `per_rep` untimed calls."""
+        is in a stream of calls), after untimed runs of the same call for at
+        least `call_warm_s` seconds (after the host-side oracle or a few
+        microsecond-long calls, 10 calls left the box-sum call on
+        x[128,8,384,384] 4-8 % slower than in a steady stream)."""
         for _ in range(args.per_rep):
             fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.call_warm_s:
+            for _ in range(args.per_rep):
+                fn()
+            torch.cuda.synchronize()
         evs = []
         for _ in range(args.reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -719,7 +731,8 @@ def main():
         "ceilings": ceilings,
         "timing": {"step": "one event triple per step around its two calls, on torch's current stream",
                    "configs_variants": f"median/p10/p90 over {args.reps} runs of {args.per_rep} back-to-back calls, "
-                                       "one event pair per run"},
+                                       f"one event pair per run, after at least {args.call_warm_s} s of untimed "
+                                       "runs of the same call"},
         "wall_s_timed_region": round(t_wall, 3),
         "settle": {"steps": settle_steps, "wall_s": round(t_settle, 3),
                    "note": "untimed whole steps before the warm-up, until the clocks leave their idle state"},

@@ -452,11 +452,12 @@ struct BoxLayout {
     static constexpr bool PATCH = Cfg::TPH == 4 && Cfg::TPW % 4 == 0 && rss_patch() >= 0 && rss_patch() - S * QS <= 16;
     static constexpr int RSS = PATCH ? rss_patch() : S * QS;  // Sx floats per row
     // channel planes 16 or 48 (mod 64) apart: either puts the four lane
-    // groups on four disjoint 16-bank sets; the nearer one is taken
+    // groups on four disjoint 16-bank sets; the nearer one is taken (in row
+    // order too, where a block's 16 lanes read 16 consecutive words: K3/s3's
+    // unpadded 576-word planes put all four groups on the same banks)
     static constexpr int pad_to(int n, int m) { return (m - n % 64 + 64) % 64; }
     static constexpr int SPLANE =
-        PATCH ? RS * RSS + (pad_to(RS * RSS, 16) < pad_to(RS * RSS, 48) ? pad_to(RS * RSS, 16) : pad_to(RS * RSS, 48))
-              : RS * RSS;
+        RS * RSS + (pad_to(RS * RSS, 16) < pad_to(RS * RSS, 48) ? pad_to(RS * RSS, 16) : pad_to(RS * RSS, 48));
     // horizontal sums by DPP wave shifts (one 64-column chunk per row, s = 2
     // or 3), else through one vertical-sum row of LDS per wave
     static constexpr bool DPP_H = NCH == 1 && (S == 2 || S == 3);
@@ -475,8 +476,16 @@ struct BoxLayout {
 #ifndef FCONV_BOX_K5S3_MIN_WAVES
 #define FCONV_BOX_K5S3_MIN_WAVES 6
 #endif
+// The 4-wave K3/s2 and K3/s3 instances are held to 8 waves per SIMD (64
+// VGPRs: 57-61 used, no VGPR spills): unbounded, the compiler took 100
+// registers (accumulators in AGPRs) and 4 waves per SIMD, and these short
+// workgroups (36 MFMAs per channel quad and wave) had too few waves to hide
+// their loads and barriers: 0.4384 against 0.4538 ms for K3/s2 and 0.2422
+// against 0.2517 ms for K3/s3 on x[128,8,384,384] -> 64 channels, 0.0998
+// against 0.1081 ms for K3/s3 on x[32,32,256,256] (interleaved A/B).
 template <class Cfg>
 constexpr int box_min_waves() {
+    if (Cfg::K == 3 && (Cfg::S == 2 || Cfg::S == 3) && Cfg::NW == 4) return 8;
     return Cfg::K == 5 && Cfg::S == 3 ? FCONV_BOX_K5S3_MIN_WAVES : 1;
 }
 
@@ -597,13 +606,25 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
         auto sum_rows = [&](float (&vv)[IH][NCH], int slot) {
             float* splane = Sb + slot * L::SPLANE;
             if constexpr (DPP_H) {
+                // All rows first, then one store branch: with a branch per
+                // row the compiler sank each row's last add into it, where
+                // the shift's source lane may be inactive, so every shift
+                // stayed a move of its own (with its hazard wait) and every
+                // row paid an exec-mask save and restore.  The empty register
+                // constraint keeps the sums ahead of the branch.
+                float hv[RS];
 #pragma unroll
                 for (int r = 0; r < RS; ++r) {
                     float v = vv[r][0];
 #pragma unroll
                     for (int dy = 1; dy < S; ++dy) v += vv[r + dy][0];
-                    const float h = S == 2 ? v + wave_shl1(v) : v + wave_shl1(v + wave_shl1(v));
-                    if (lane < CS) splane[r * RSS + soff[0]] = h;
+                    hv[r] = S == 2 ? v + wave_shl1(v) : v + wave_shl1(v + wave_shl1(v));
+                }
+#pragma unroll
+                for (int r = 0; r < RS; ++r) asm volatile("" : "+v"(hv[r]));
+                if (lane < CS) {
+#pragma unroll
+                    for (int r = 0; r < RS; ++r) splane[r * RSS + soff[0]] = hv[r];
                 }
                 return;
             }
@@ -779,8 +800,9 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
 // each window of rows 4ph+ky .. +3 as two of them (15 adds per column for
 // both pooled rows).  Then per (ph, ky) 7 adds give the horizontal 4-sums:
 //     h0 = (u0+u1) + (u2+u3),  h1 = (u1+u2) + (u3+n0),  h2 = (u2+u3) + (n0+n1).
-// That is 114 adds and 12 lane moves per channel; summing each row across
-// first took 138 and 20.  The 9 values go to LDS tap-major, Sx[ic][ph][tap][pw]
+// That is 114 adds per channel, 12 of which read the next lane's operand
+// through a DPP modifier (no move of their own); summing each row across
+// first took 138 adds and 20 moves.  The 9 values go to LDS tap-major, Sx[ic][ph][tap][pw]
 // (consecutive lanes write and read consecutive words), which the
 // contraction reads as B operands, one word per MFMA step.  Each channel's
 // plane is padded by 16 words so that the four lane groups, which read four
@@ -934,6 +956,12 @@ __global__ __launch_bounds__(Box4::NT, 4) void conv2d_pool_boxsum4_kernel(
                     sx[3 * ky + 1] = (uu[1] + uu[2]) + (next_lane(uu[0]) + uu[3]);
                     sx[3 * ky + 2] = next_lane(p01) + p23;
                 }
+                // The sums stay ahead of the store branch: sunk into it, an add
+                // whose operand comes from lane TPW (inactive there) cannot
+                // take its DPP move as a modifier, and each of the 12 moves
+                // became an instruction of its own.
+#pragma unroll
+                for (int k = 0; k < 9; ++k) asm volatile("" : "+v"(sx[k]));
                 if (lane < TPW) {
                     float* q = sp + ph * 9 * TPW;
 #pragma unroll
@@ -1100,7 +1128,11 @@ static hipError_t launch_box4(const Conv2dShape& s, const float* x, const float*
 }
 
 // Instances: K3/s4 4x16 tile with 4 waves x 16 channels; K5/s3 4x12 tile
-// with 8 waves x 16 channels.
+// with 8 waves x 16 channels; K3/s2 and K3/s3 4x16 tiles with 4 waves x 16
+// channels, or 8 waves x 16 where Cout > 64: with 64-channel ranges two
+// workgroups made the same box sums for each tile of a 128-channel map
+// (x[64,16,257,257] -> 128: 0.1875 against 0.2045 ms for K3/s3, 0.3411
+// against 0.3481 ms for K3/s2, interleaved A/B).
 #ifndef FCONV_CFG_BOX_K3S4
 #define FCONV_CFG_BOX_K3S4 3, 4, 1, 4, 4, 1, 4, 16
 #endif
@@ -1111,6 +1143,8 @@ using BoxK3S4 = DirectCfg<FCONV_CFG_BOX_K3S4>;
 using BoxK5S3 = DirectCfg<FCONV_CFG_BOX_K5S3>;
 using BoxK3S2 = DirectCfg<3, 2, 1, 4, 4, 1, 4, 16>;
 using BoxK3S3 = DirectCfg<3, 3, 1, 4, 4, 1, 4, 16>;
+using BoxK3S2W8 = DirectCfg<3, 2, 1, 4, 8, 1, 4, 16>;
+using BoxK3S3W8 = DirectCfg<3, 3, 1, 4, 8, 1, 4, 16>;
 
 // LDS of one workgroup: a chunk of CC channels' box sums plus the waves'
 // scratch rows, whatever Cin is.
@@ -1157,8 +1191,12 @@ hipError_t conv2d_boxsum_launch(const Conv2dShape& s, const float* x, const floa
 #endif
     if (s.K == 3 && s.S == 4) return launch_box<BoxK3S4>(s, x, w, bias, dst, mode, stream);
     if (s.K == 5 && s.S == 3) return launch_box<BoxK5S3>(s, x, w, bias, dst, mode, stream);
-    if (s.K == 3 && s.S == 2) return launch_box<BoxK3S2>(s, x, w, bias, dst, mode, stream);
-    if (s.K == 3 && s.S == 3) return launch_box<BoxK3S3>(s, x, w, bias, dst, mode, stream);
+    if (s.K == 3 && s.S == 2)
+        return s.Cout > 64 ? launch_box<BoxK3S2W8>(s, x, w, bias, dst, mode, stream)
+                           : launch_box<BoxK3S2>(s, x, w, bias, dst, mode, stream);
+    if (s.K == 3 && s.S == 3)
+        return s.Cout > 64 ? launch_box<BoxK3S3W8>(s, x, w, bias, dst, mode, stream)
+                           : launch_box<BoxK3S3>(s, x, w, bias, dst, mode, stream);
     return hipErrorInvalidValue;
 }
 
@@ -1168,8 +1206,8 @@ int64_t conv2d_boxsum_parts(const Conv2dShape& s) {
 #endif
     if (s.K == 3 && s.S == 4) return box_parts<BoxK3S4>(s);
     if (s.K == 5 && s.S == 3) return box_parts<BoxK5S3>(s);
-    if (s.K == 3 && s.S == 2) return box_parts<BoxK3S2>(s);
-    if (s.K == 3 && s.S == 3) return box_parts<BoxK3S3>(s);
+    if (s.K == 3 && s.S == 2) return s.Cout > 64 ? box_parts<BoxK3S2W8>(s) : box_parts<BoxK3S2>(s);
+    if (s.K == 3 && s.S == 3) return s.Cout > 64 ? box_parts<BoxK3S3W8>(s) : box_parts<BoxK3S3>(s);
     return -1;
 }
 

@@ -65,6 +65,8 @@ SMALL_CONV = [
     (1, 8, 40, 40, 70, 3, 4),       # Cout > 64: two channel ranges
     (1, 3, 37, 41, 7, 3, 2),        # K3/s2 instance
     (2, 4, 30, 28, 9, 3, 3),        # K3/s3 instance
+    (1, 8, 37, 70, 100, 3, 2),      # K3/s2, Cout > 64: 8-wave box-sum instance, Cout not a multiple of 16
+    (2, 16, 45, 50, 128, 3, 3),     # K3/s3, Cout > 64: 8-wave box-sum instance, one 128-channel range
     (1, 2, 23, 19, 5, 7, 2),        # no MFMA instance (K=7): simple path
     (1, 3, 9, 9, 4, 5, 3),          # PH = PW = 1
     # box-sum K3/s4 kernel (W % 4 == 0): one, two and streamed channel quads
@@ -173,6 +175,8 @@ MANY_CHANNELS = [
     (1, 128, 20, 47, 40, 5, 3),     # K5/s3, Cin 128
     (1, 36, 40, 66, 30, 3, 2),      # K3/s2: 4 + 4 + 1 quads
     (1, 64, 31, 70, 64, 3, 3),      # K3/s3, Cin 64
+    (1, 20, 40, 41, 200, 3, 3),     # K3/s3, 8-wave instance: chunks of 16 + 4 channels, two ranges (128 + 72)
+    (1, 36, 34, 40, 130, 3, 2),     # K3/s2, 8-wave instance: chunks of 16 + 16 + 4, a 2-channel second range
 ]
 
 
@@ -202,6 +206,7 @@ WALK_CONV = [
     (1, 2, 400, 1204, 8, 5, 3, 1),     # direct K5/s3 (pool folded into the contraction)
     (1, 20, 266, 1026, 4, 3, 2, 3),    # general box-sum K3/s2, 3 chunks of channels
     (1, 3, 398, 1538, 4, 3, 3, 1),     # direct K3/s3
+    (1, 2, 266, 3100, 72, 3, 3, 3),    # 8-wave general box-sum K3/s3 (Cout > 64): 22 x 65 tiles of 4 x 16
 ]
 
 
