@@ -574,11 +574,14 @@ static constexpr size_t tall_lds_bytes(int K) {
 //   (as in the separable kernel); A = w_pw[o, c] * w_dw[c, k] is formed in
 //   registers (one multiply per weight fragment and tap), B is the staged
 //   input x[c, t*stride + k*dilation - pad] read straight from LDS.
+//   Epilogue: each wave's 32 x 64 block goes out 16 rows at a time through
+//   LDS, as whole 256-byte row segments (16-byte stores); ragged tiles, an
+//   unaligned y or Tout % 4 != 0 store element by element.
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_dense_kernel(
     const float* __restrict__ x, const float* __restrict__ w_dw, const float* __restrict__ w_pw,
     const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int K, int O, int pad, int Tout,
-    int stride, int dil) {
+    int stride, int dil, int vec_out) {
     constexpr int OB = Cfg::OB, TB = Cfg::TB, WO = Cfg::WO, CC = Cfg::CC, TT = Cfg::TT, NW = Cfg::NW, NT = Cfg::NT;
     static_assert(Cfg::KC == 0, "the dense kernel takes K at run time");
 
@@ -667,26 +670,60 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_dense_kernel(
 
     const buf_rsrc rb = make_rsrc(b_pw, b_pw ? O * 4 : 0);
     float* yb = y + (size_t)b * O * Tout;
+    float bo[OB][4];
 #pragma unroll
     for (int ob = 0; ob < OB; ++ob)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int o = o0 + ob * 16 + 4 * g + r;
-            const float bo = buf_load_f32(rb, o < O ? o * 4 : kBufOOB);
-            if (o >= O) continue;
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const int t = t0 + (wt * TB + tb) * 16 + l16;
-                if (t < Tout) __builtin_nontemporal_store(acc[ob][tb][r] + bo, yb + (size_t)o * Tout + t);
-            }
+            bo[ob][r] = buf_load_f32(rb, o < O ? o * 4 : kBufOOB);
         }
+    // A wave's row segment is TB * 16 steps; with WT = 1 that is the tile.
+    static_assert(Cfg::WT == 1 && TB * 16 == 64, "the staged store writes 64-step rows");
+    constexpr int OP = 68;  // LDS row pitch: the four lane groups' rows start 16 banks apart
+    __syncthreads();  // every wave is done reading xs and wsm (outside the branch: o0 differs per wave)
+    if (vec_out && o0 + 16 * OB <= O && t0 + TT <= Tout) {
+        float* ow = lds + wave * 16 * OP;
+#pragma unroll
+        for (int ob = 0; ob < OB; ++ob) {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ow[(4 * g + r) * OP + 16 * tb + l16] = acc[ob][tb][r] + bo[ob][r];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const floatx4 v = *reinterpret_cast<const floatx4*>(ow + (4 * i + g) * OP + 4 * l16);
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<floatx4*>(yb + (size_t)(o0 + 16 * ob + 4 * i + g) * Tout + t0 + 4 * l16));
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    } else {
+#pragma unroll
+        for (int ob = 0; ob < OB; ++ob)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = o0 + ob * 16 + 4 * g + r;
+                if (o >= O) continue;
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const int t = t0 + (wt * TB + tb) * 16 + l16;
+                    if (t < Tout) __builtin_nontemporal_store(acc[ob][tb][r] + bo[ob][r], yb + (size_t)o * Tout + t);
+                }
+            }
+    }
 }
 
 using DwDense = DwsepCfg<2, 4, 8, 1, 64, 0, 4>;
 
+// The staged input and taps, or (after the last chunk) the waves' 16-row
+// output staging, whichever is larger.
 static size_t dense_lds_bytes(const DwsepShape& s) {
     const long xw = (long)(DwDense::TT - 1) * s.stride + (long)(s.K - 1) * s.dil + 1;
-    return ((size_t)DwDense::CC * xw + (size_t)DwDense::CC * s.K) * sizeof(float);
+    const size_t in = ((size_t)DwDense::CC * xw + (size_t)DwDense::CC * s.K) * sizeof(float);
+    const size_t out = (size_t)DwDense::NW * 16 * 68 * sizeof(float);
+    return in > out ? in : out;
 }
 
 bool dwsep_dense_supported(const DwsepShape& s) { return dense_lds_bytes(s) <= 160 * 1024; }
@@ -698,8 +735,9 @@ hipError_t dwsep_dense_launch(const DwsepShape& s, const float* x, const float* 
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     dim3 grid((s.Tout + DwDense::TT - 1) / DwDense::TT, (s.O + DwDense::OT - 1) / DwDense::OT, s.B);
+    const int vec_out = (s.Tout % 4 == 0) && ((uintptr_t)y % 16 == 0);
     hipLaunchKernelGGL(dwsep_dense_kernel<DwDense>, grid, dim3(DwDense::NT), lds, stream, x, w_dw, w_pw, b_pw, y, s.C,
-                       s.T, s.K, s.O, s.pad, s.Tout, s.stride, s.dil);
+                       s.T, s.K, s.O, s.pad, s.Tout, s.stride, s.dil, vec_out);
     return hipGetLastError();
 }
 

@@ -673,6 +673,7 @@ DENSE_DW = [
     (4, 16, 256, 32, 9, 4, 1, 1),      # the small workload
     (2, 100, 150, 70, 9, 4, 1, 1),     # C not a multiple of 16, O ragged
     (1, 64, 200, 300, 5, 2, 2, 2),     # strided and dilated
+    (2, 48, 260, 520, 9, 4, 1, 1),     # whole tiles through the staged 16-byte stores; ragged last time and O tiles
 ]
 
 
@@ -721,18 +722,21 @@ def test_dwsep_unaligned_weights(fc, O):
     assert_close(got, want, "y unaligned")
 
 
+@pytest.mark.parametrize("dense", [False, True])
 @pytest.mark.parametrize("offset", [1, 2, 3])
-def test_dwsep_unaligned_output(fc, offset):
-    # y starting 4, 8 or 12 bytes past a 16-byte boundary (Tout a multiple of 4): the tall tile stores
-    # element by element instead of in 16-byte rows; the elements around y stay untouched
-    announce(f"dwsep unaligned y, offset {offset} floats")
+def test_dwsep_unaligned_output(fc, offset, dense):
+    # y starting 4, 8 or 12 bytes past a 16-byte boundary (Tout a multiple of 4): the tall tile (and the
+    # dense-fused kernel's) stores element by element instead of in 16-byte rows; the elements around y
+    # stay untouched
+    announce(f"dwsep unaligned y, offset {offset} floats, dense {dense}")
     B, C, T, O, K, pad = 2, 40, 128, 300, 9, 4
     x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=10 + offset)
     want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad)
     n = B * O * T
     buf = torch.full((n + 8,), 7.0, device="cuda")
     y = buf[offset:offset + n].view(B, O, T)
-    fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad, out=y)
+    fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad, out=y,
+                    algo=fc.DWSEP_DENSE if dense else fc.DWSEP_SEPARABLE)
     assert_close(y.cpu().numpy(), want, f"y offset {offset}")
     rest = torch.cat([buf[:offset], buf[offset + n:]]).cpu().numpy()
     assert (rest == 7.0).all()
