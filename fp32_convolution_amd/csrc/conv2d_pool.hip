@@ -29,9 +29,10 @@
 //  * Epilogue: scale by 1/s^2, add bias, sigmoid, lane sum, wave + LDS
 //    reduction, one partial sum per workgroup (added in a fixed order into
 //    out[b] by reduce_partials).
-// Instances: K5/s3, K3/s2, K3/s3.  K3/s4 runs on conv2d_pool_elem_kernel
-// (conv2d_pool_ex.hip), which keeps each conv output in an accumulator and
-// pools in registers: the same multiply-adds, measured slightly faster there.
+// Instances: K5/s3, K3/s2, K3/s3.  K3/s4, and K3/s2 up to 16 channels, run
+// on conv2d_pool_elem_kernel (conv2d_pool_ex.hip), which keeps each conv
+// output in an accumulator and pools in registers: the same multiply-adds,
+// measured faster there.
 #include "fconv_device.hpp"
 #include "fconv_internal.hpp"
 
@@ -299,20 +300,29 @@ static size_t lds_bytes_for(int Cin) {
 
 static constexpr size_t kMaxLds = 160 * 1024 - 256;  // dynamic share; the rest holds the reduction slots
 
-// The pool-folded direct kernel takes (Cin, K, S): its instance exists and
-// one workgroup's tile of all Cin channels fits LDS.
+// The pool-folded direct kernel takes (Cin, K, S): its instance exists, one
+// workgroup's tile of all Cin channels fits LDS, and it is the faster of the
+// two direct kernels there.  For K3/s2 up to 16 channels the per-conv-output
+// kernel's 4 x 32 tiles (its own folded average pool) ran faster: 1.2552
+// against 1.4481 ms on x[128,8,384,384] -> 64 and 1.1337 against 1.2006 ms on
+// x[64,16,257,257] -> 128, but 0.7845 against 0.6578 ms with Cin = 32
+// (interleaved A/B); for K3/s3 it was slower at every Cin tried.
 static bool direct_fits(int Cin, int K, int S) {
     size_t bytes = 0;
     if (K == 5 && S == 3) bytes = lds_bytes_for<CfgK5S3>(Cin);
-    else if (K == 3 && S == 2) bytes = lds_bytes_for<CfgK3S2>(Cin);
+    else if (K == 3 && S == 2) {
+        if (Cin <= 16) return false;
+        bytes = lds_bytes_for<CfgK3S2>(Cin);
+    }
     else if (K == 3 && S == 3) bytes = lds_bytes_for<CfgK3S3>(Cin);
     else return false;
     return bytes <= kMaxLds;
 }
 
-// Direct MFMA: K3/s4 runs on the per-conv-output kernel; K5/s3, K3/s2 and
-// K3/s3 on the pool-folded kernel while its tile fits, else on the
-// per-conv-output kernel's channel-chunked tiling (any Cin).
+// Direct MFMA: K3/s4, and K3/s2 up to 16 channels, run on the
+// per-conv-output kernel; K5/s3, K3/s2 and K3/s3 otherwise on the pool-folded
+// kernel while its tile fits, else on the per-conv-output kernel's
+// channel-chunked tiling (any Cin).
 bool conv2d_mfma_supported(int Cin, int K, int S) {
     return direct_fits(Cin, K, S) || conv2d_elem_supported(Cin, K, S);
 }
