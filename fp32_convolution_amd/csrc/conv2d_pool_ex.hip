@@ -165,14 +165,18 @@ __global__ __launch_bounds__(C::NT, C::CHUNK ? 4 : 3) void conv2d_pool_elem_kern
     constexpr int IH = C::IH, IW = C::IW, RP = C::RP, NR = C::NR, WPB = C::WPB, CPB = C::CPB;
     constexpr bool POOL_MAX = POOL == kPoolMax, FOLD = POOL == kPoolMeanFolded;
     constexpr int NACC = FOLD ? 1 : S;  // accumulator blocks per column block
-    // TF: the folded pool with s = 4 or 2 swaps the MFMA operands (input as
-    // A, weights as B), so a lane's four accumulator elements are four
-    // adjacent conv columns of one channel, and a window's column sum stays
-    // inside the lane: 3 adds per window instead of the cross-lane exchange
-    // (6 selects and 3 DPP adds per 16-column block).  x[128,8,384,384] -> 64:
-    // 1.1966 against 1.2090 ms; K3/s2: 1.2467 against 1.2646 ms (interleaved
-    // A/B).  s = 3 windows do not align with a lane's four columns.
-    constexpr bool TF = FOLD && (S == 4 || S == 2);
+    // TF: with s = 4 or 2 the MFMA operands are swapped (input as A,
+    // weights as B), so a lane's four accumulator elements are four adjacent
+    // conv columns of one channel, and a window's columns pool inside the
+    // lane instead of through the cross-lane exchange (6 selects and 3 DPP
+    // operations per 16-column block).  Interleaved A/B on x[128,8,384,384]
+    // -> 64, ms: folded average pool 1.1966 against 1.2090 (K3/s2: 1.2467
+    // against 1.2646); ReLU + max pool 1.2159 against 1.2286 (K3/s2: 1.2659
+    // against 1.2910; ceil mode 1.2497 against 1.2556).  The unfolded average
+    // pool (ReLU before it) measured 1.2745 against 1.2554 and keeps the
+    // exchange; so do s = 3 windows, which do not align with a lane's four
+    // columns.
+    constexpr bool TF = (S == 4 || S == 2) && POOL != kPoolMean;
     static_assert(NQ >= 0 && NQ <= 2, "resident weights for one or two channel quads");
 
     extern __shared__ float lds[];
@@ -370,22 +374,54 @@ __global__ __launch_bounds__(C::NT, C::CHUNK ? 4 : 3) void conv2d_pool_elem_kern
             constexpr bool EDGE = decltype(edge_tag)::value, FULL = decltype(full_tag)::value;
             const float fill = POOL_MAX ? -INFINITY : 0.f;
             if constexpr (TF) {
-                // Lane (g, l16) holds, for channel co0 + l16, the window-row
-                // sums of conv columns x0 + nb*16 + 4g + r (r = 0..3): its
-                // 4 / S windows are sums of its own elements.
+                // Lane (g, l16) holds, for channel co0 + l16, conv columns
+                // x0 + nb*16 + 4g + r (r = 0..3) of each conv row dy of the
+                // window (folded: the rows' sum), so its 4 / S windows pool
+                // over its own elements.
                 constexpr int NV = 4 / S;
                 const int co = co0 + l16;
-                const float inv = 1.0f / (float)(S * S);
 #pragma unroll
                 for (int nb = 0; nb < decltype(nba)::value; ++nb)
 #pragma unroll
                     for (int i = 0; i < NV; ++i) {
-                        const floatx4 v = ac[nb][0];
-                        const float o = S == 4 ? (v[0] + v[1]) + (v[2] + v[3]) : v[2 * i] + v[2 * i + 1];
+                        float o;
+                        if constexpr (FOLD) {
+                            const floatx4 v = ac[nb][0];
+                            o = S == 4 ? (v[0] + v[1]) + (v[2] + v[3]) : v[2 * i] + v[2 * i + 1];
+                        } else {
+                            float e[S * S];
+#pragma unroll
+                            for (int dy = 0; dy < S; ++dy)
+#pragma unroll
+                                for (int j = 0; j < S; ++j) {
+                                    float t = ac[nb][dy][S * i + j];
+                                    if (!POOL_MAX && relu) t = fmaxf(t, 0.f);
+                                    if constexpr (EDGE) {
+                                        const bool ok = (yr + dy < Hc) && (x0 + nb * CPB + 4 * g + S * i + j < Wc);
+                                        t = ok ? t : fill;
+                                    }
+                                    e[dy * S + j] = t;
+                                }
+                            // pairwise over the window's S*S conv outputs
+#pragma unroll
+                            for (int w2 = S * S / 2; w2 >= 1; w2 /= 2)
+#pragma unroll
+                                for (int k = 0; k < w2; ++k) e[k] = pool2(e[k], e[k + w2]);
+                            o = e[0];
+                        }
                         const int pw = pw0 + nb * WPB + NV * g + i;
                         if (FULL || (pw < PW && co < Cout)) {
+                            const float inv = EDGE ? 1.0f / (float)(min(S, Hc - ph * S) * min(S, Wc - pw * S))
+                                                   : 1.0f / (float)(S * S);
+                            if (POOL_MAX) {
+                                if (relu) o = fmaxf(o, 0.f);  // ReLU commutes with max
+                            } else if (EDGE || MODE == OUT_MAP) {
+                                o = o * inv;
+                            }
                             if constexpr (MODE == OUT_MAP)
-                                dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = o * inv;
+                                dst[(((size_t)b * Cout + co) * PH + ph) * PW + pw] = o;
+                            else if (POOL_MAX || EDGE)
+                                lsum += logistic(o);
                             else
                                 lsum += logistic_scaled(o, inv);
                         }
