@@ -261,7 +261,8 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 // Stride 1, dilation 1, O > 256: a 512 x 64 tile (8 waves of 64 x 64), so
 // each depthwise value is made once per time tile instead of once per 256
 // output channels, and the matrix cores see twice the work per depthwise
-// instruction.  The extra accumulator registers are paid for by staging x,
+// instruction.  64 < O <= 256 takes the same kernel with 256- or 128-row
+// tiles (8 waves of 32 x 64 or 16 x 64).  The extra accumulator registers are paid for by staging x,
 // the depthwise taps and the bias with LDS-direct buffer loads
 // (buffer_load_dword ... lds: memory to LDS with no register round trip),
 // which also lets the next chunk's rows stream in while the current chunk's
@@ -303,7 +304,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     // channels start 16 bytes apart on the LDS banks
     constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = 132, OP = 68;
     constexpr int DSF = TT * CCP > NW * 16 * OP ? TT * CCP : NW * 16 * OP;
-    static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && OB == 4 && TB == 4, "waves of 64 x 64 along o");
+    static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && (OB == 4 || OB == 2 || OB == 1) && TB == 4,
+                  "waves of 16 OB x 64 along o");
     static_assert(CC % NW == 0 && CC % 16 == 0, "whole rows per wave, whole groups per chunk");
     const int K = Cfg::KC > 0 ? Cfg::KC : Kr;
     const int XW = TT + K - 1;  // input steps the tile reads (<= XP)
@@ -556,6 +558,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
 #endif
 using DwTall9 = DwsepCfg<FCONV_CFG_TALL>;
 using DwTallK = DwsepCfg<4, 4, 8, 1, 64, 0, 4>;
+// The same tile for 64 < O <= 256: waves of 32 x 64 (256 rows) or 16 x 64
+// (128 rows), so no wave computes rows past O.
+using DwTall9M = DwsepCfg<2, 4, 8, 1, 64, 9, 4>;
+using DwTallKM = DwsepCfg<2, 4, 8, 1, 64, 0, 4>;
+using DwTall9S = DwsepCfg<1, 4, 8, 1, 64, 9, 4>;
+using DwTallKS = DwsepCfg<1, 4, 8, 1, 64, 0, 4>;
 
 template <class Cfg>
 static constexpr size_t tall_lds_bytes(int K) {
@@ -774,7 +782,7 @@ static hipError_t launch_dw(const DwsepShape& s, const float* x, const float* w_
 
 // The tall kernel's 1-D grid holds every (time tile, output tile, item).
 static bool tall_tiles_fit(const DwsepShape& s) {
-    const int ot = DwTall9::OT < DwTallK::OT ? DwTall9::OT : DwTallK::OT;
+    const int ot = DwTall9S::OT;  // the smallest tile height of the instances
     const long n = (long)((s.Tout + 63) / 64) * ((s.O + ot - 1) / ot) * s.B;
     return n <= 0x7fffffffL;
 }
@@ -795,13 +803,18 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 }
 
 // The instance a shape runs on: 0 = none fits, 1 = wide K=9, 2 = wide
-// runtime-K, 3 = narrow runtime-K, 4 = small runtime-K, 5 = tall K=9,
-// 6 = tall runtime-K.  The tall tile needs 16-byte weight loads (C a
-// multiple of 4 and an aligned w_pw), which the caller states in vec_ok.
+// runtime-K, 3 = narrow runtime-K, 4 = small runtime-K, 5/6 = tall K=9 /
+// runtime-K (512 rows), 7/8 = the same with 256 rows, 9/10 with 128 rows.
+// The tall tile needs 16-byte weight loads (C a multiple of 4 and an aligned
+// w_pw), which the caller states in vec_ok.
 static int pick_dw(const DwsepShape& s, bool vec_ok) {
     const bool unit = s.stride == 1 && s.dil == 1;
 #ifndef FCONV_DW_NO_TALL
-    if (unit && vec_ok && s.O > 256 && s.K <= 64 && s.C % 4 == 0 && tall_tiles_fit(s)) return s.K == 9 ? 5 : 6;
+    if (unit && vec_ok && s.O > 64 && s.K <= 64 && s.C % 4 == 0 && tall_tiles_fit(s)) {
+        if (s.O > 256) return s.K == 9 ? 5 : 6;
+        if (s.O > 128) return s.K == 9 ? 7 : 8;
+        return s.K == 9 ? 9 : 10;
+    }
 #endif
     if (s.O > 64) {
         if (unit && s.K == 9) return 1;
@@ -825,6 +838,10 @@ hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, 
         case 4: return launch_dw<DwSmallK>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 5: return launch_tall<DwTall9>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 6: return launch_tall<DwTallK>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 7: return launch_tall<DwTall9M>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 8: return launch_tall<DwTallKM>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 9: return launch_tall<DwTall9S>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 10: return launch_tall<DwTallKS>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

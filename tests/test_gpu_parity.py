@@ -586,6 +586,13 @@ TALL_DW = [
     (2, 16, 50, 512, 9, 0),      # a single partial chunk, T < 64, no padding
     (1, 32, 70, 300, 1, 0),      # 1-tap depthwise
     (1, 44, 200, 1100, 3, 1),    # three output tiles, C not a multiple of 16
+    # 64 < O <= 256: the same kernel with 256-row (waves of 32 x 64) and 128-row (16 x 64) tiles
+    (2, 200, 130, 256, 9, 4),    # 256 rows exactly, 3 full chunks + an 8-channel chunk, a ragged time tile
+    (1, 68, 100, 129, 9, 4),     # 256-row tile with one valid row in its fifth wave, a 4-channel chunk
+    (1, 64, 100, 200, 64, 32),   # 256-row tile, the widest window
+    (1, 36, 64, 128, 5, 2),      # 128 rows exactly, runtime K
+    (2, 44, 150, 65, 9, 4),      # 128-row tile with one valid row in its fifth wave
+    (1, 100, 80, 100, 17, 8),    # 128-row tile, runtime K, chunks of 64 + 36 channels
 ]
 
 
@@ -619,12 +626,14 @@ def test_dwsep_tall_tile(fc, shape):
     assert_close(got, want, f"y {shape}")
 
 
-def test_dwsep_tall_tile_every_k(fc):
+@pytest.mark.parametrize("O", [300, 200, 100])
+def test_dwsep_tall_tile_every_k(fc, O):
     # every depthwise width the tall tile takes (K = 1 .. 64; K = 9 is its compiled instance, the rest run
     # the runtime-K stage over blocks of 8 taps), with odd and even padding and a partial channel chunk,
-    # against the oracle; K = 65 goes to the 256-row kernel and is checked the same way
-    announce("dwsep tall tile, K = 1 .. 65")
-    B, C, T, O = 1, 36, 100, 300
+    # against the oracle, for its 512-, 256- and 128-row tiles; K = 65 goes to the 256-row kernel and is
+    # checked the same way
+    announce(f"dwsep tall tile, K = 1 .. 65, O = {O}")
+    B, C, T = 1, 36, 100
     for K in range(1, 66):
         pad = K // 2 if K % 3 else (K - 1) // 2
         x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=300 + K)
