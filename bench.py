@@ -633,7 +633,38 @@ def main():
     torch.cuda.synchronize()
     variants["dwsep_conv1d_dense"]["matches_separable_within_tol"] = bool(
         ((y_dense - y).abs() <= 1e-4 + 1e-4 * y.abs()).all().item())
+
+    # the conv1d generalisations at the dwsep_full scale: stride 2 (over twice the steps, so Tout is the
+    # same), dilation 2, and 256 output channels (the tall tile's 256-row instance); parity for these
+    # forms is in tests/test_gpu_parity.py and tests/test_gpu_random_shapes.py
+    def dw_gen(B, C, T, O, K, pad, stride, dil, seed):
+        xg = torch.from_numpy(fi.dwsep_inputs(B, C, T, O, K, seed=seed)[0]).to(dev)
+        To = (T + 2 * pad - dil * (K - 1) - 1) // stride + 1
+        flops = 2 * B * To * C * (K + O)
+        nbytes = 4 * (B * C * T + C * K + O * C + O + B * O * To)
+        return xg, To, flops, nbytes
+    x2, To2, f2, b2 = dw_gen(dc["B"], dc["C"], 2 * dc["T"], dc["O"], dc["K"], dc["pad"], 2, 1, seed=41)
+    variants["dwsep_conv1d_stride2"] = variant(
+        lambda: fc.dwsep_conv1d(x2, wdw, wpw, bpw, dc["pad"], out=y_dense, stride=2),
+        f2, b2, f"stride 2 on x[{dc['B']},{dc['C']},{2 * dc['T']}] -> {dc['O']} channels (Tout {To2}), "
+        "K 9, pad 4: the 256-row kernel (dwsep_mfma_kernel), own separable FLOPs")
+    del x2
+    xg = torch.from_numpy(fi.dwsep_inputs(dc["B"], dc["C"], dc["T"], dc["O"], dc["K"], seed=42)[0]).to(dev)
+    f3 = 2 * dc["B"] * dc["T"] * dc["C"] * (dc["K"] + dc["O"])
+    variants["dwsep_conv1d_dilation2"] = variant(
+        lambda: fc.dwsep_conv1d(xg, wdw, wpw, bpw, 2 * dc["pad"], out=y_dense, dilation=2),
+        f3, b_dw, f"dilation 2, pad 8 on {DW}: the 256-row kernel (dwsep_mfma_kernel), own separable FLOPs")
     del y_dense
+    O4 = dc["O"] // 2
+    y4 = torch.empty(dc["B"], O4, dc["T"], device=dev)
+    w4, b4 = wpw[:O4].contiguous(), bpw[:O4].contiguous()
+    f4 = 2 * dc["B"] * dc["T"] * dc["C"] * (dc["K"] + O4)
+    b4b = 4 * (dc["B"] * dc["C"] * dc["T"] + dc["C"] * dc["K"] + O4 * dc["C"] + O4 + dc["B"] * O4 * dc["T"])
+    variants["dwsep_conv1d_o256"] = variant(
+        lambda: fc.dwsep_conv1d(xg, wdw, w4, b4, dc["pad"], out=y4),
+        f4, b4b, f"x[{dc['B']},{dc['C']},{dc['T']}] -> {O4} channels, K 9, pad 4: the tall tile's 256-row "
+        "instance, own separable FLOPs")
+    del xg, y4, w4, b4
 
     # dwsep "cold": x and the weights (135 MB) fit in the 256 MB Infinity
     # Cache, so each timed call follows an overwrite of a 512 MB buffer; the
