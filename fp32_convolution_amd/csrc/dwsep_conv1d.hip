@@ -41,7 +41,8 @@
 namespace fconv {
 
 // OB, TB: 16x16 output blocks per wave along o and t; WO, WT: waves along o
-// and t; CC: channel chunk; KC: compile-time depthwise taps (0 = runtime K);
+// and t; CC: channel chunk; KC: compile-time depthwise taps (0 = runtime K;
+// -1 = runtime K with dilation 2, 4 or 8, tall tile only);
 // MINW: waves per SIMD the register budget must allow.
 template <int OB_, int TB_, int WO_, int WT_, int CC_, int KC_, int MINW_>
 struct DwsepCfg {
@@ -258,7 +259,7 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 
 // ---------------------------------------------------------------- tall-tile variant
 
-// Stride 1, dilation 1, O > 256: a 512 x 64 tile (8 waves of 64 x 64), so
+// Stride 1, dilation 1 (or 2, 4, 8), O > 256: a 512 x 64 tile (8 waves of 64 x 64), so
 // each depthwise value is made once per time tile instead of once per 256
 // output channels, and the matrix cores see twice the work per depthwise
 // instruction.  64 < O <= 256 takes the same kernel with 256- or 128-row
@@ -289,8 +290,9 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 // 8 x [16][68] in the epilogue, then the bias [512] and the taps [CC][K]
 // (70,656 + 256 K bytes: 72,960 for K = 9, two workgroups per CU up to
 // K = 44).  Row r of xs holds input steps t0-pad .. t0-pad+127 (two 64-lane
-// runs; steps past the K-1 halo or outside [0, T) load as 0); the runtime-K
-// blocks read up to step 8*7 + 8*floor((K-1)/8) + 15, so K <= 64.
+// runs; steps past the (K-1)*dil halo or outside [0, T) load as 0); the
+// runtime-K blocks read up to step 8*7 + 8*floor((K-1)*dil/8) + 15, so
+// (K-1)*dil <= 63.  Dilation 2, 4 or 8 runs on the runtime-K instance.
 // Pointwise weights: lane (g, l16) of block ob keeps channels 4g..4g+3 of
 // the current group; the registers of block ob are refilled with the next
 // group's weights as soon as its 16 matrix instructions are issued.
@@ -298,7 +300,7 @@ template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     const float* __restrict__ x, const float* __restrict__ w_dw, const float* __restrict__ w_pw,
     const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int Kr, int O, int pad, int Tout, int n_tt,
-    int n_ot, int vec_out) {
+    int n_ot, int vec_out, int dil) {
     constexpr int OB = Cfg::OB, TB = Cfg::TB, CC = Cfg::CC, CCP = Cfg::CCP, CPW = Cfg::CPW;
     // xs row pitch: 128 staged steps + 4, so that rows of consecutive
     // channels start 16 bytes apart on the LDS banks
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
                   "waves of 16 OB x 64 along o");
     static_assert(CC % NW == 0 && CC % 16 == 0, "whole rows per wave, whole groups per chunk");
     const int K = Cfg::KC > 0 ? Cfg::KC : Kr;
-    const int XW = TT + K - 1;  // input steps the tile reads (<= XP)
+    const int XW = TT + (K - 1) * dil;  // input steps the tile reads (<= 128)
 
     // xs first: the depthwise reads then fit the short LDS offset fields
     extern __shared__ float lds[];
@@ -434,34 +436,50 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
                 Ds[(8 * dj + i) * CCP + (c ^ ((dj >> 1) << 2))] = s;  // swizzled: see read_d
             }
         } else {
-            // runtime K: the same lanes and chains, over blocks of 8 taps;
-            // block kb reads 16 staged steps from 8dj + kb (16-byte aligned:
-            // kb is a multiple of 8), and K <= 64 keeps them inside the
-            // row's 128 staged steps
+            // runtime K: the same lanes and chains, over blocks of 8 / dil
+            // taps (KC = 0: dilation 1; KC = -1: dilation 2, 4 or 8, a
+            // compile-time copy each, in instances of their own so that the
+            // undilated ones keep their registers); block kb
+            // reads 16 staged steps from 8dj + kb*dil (16-byte aligned: kb*dil
+            // is a multiple of 8), tap kb + kk at step i + kk*dil of them, and
+            // (K - 1) * dil <= 63 keeps them inside the row's 128 staged steps
             static_assert(CPW == 8, "8 channels x 8 groups of 8 steps per wave");
             const int dj = lane & 7, dc = lane >> 3;
             const int c = wave * CPW + dc;
             float sacc[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) sacc[i] = 0.f;
-            for (int kb = 0; kb < K; kb += 8) {
-                float xv[16];
+            auto taps = [&](auto dil_tag) {
+                constexpr int D = decltype(dil_tag)::value, TPB = 8 / D;
+                for (int kb = 0; kb < K; kb += TPB) {
+                    float xv[16];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const floatx4 v = *reinterpret_cast<const floatx4*>(xs + c * XP + 8 * dj + kb + 4 * q);
-                    xv[4 * q] = v[0];
-                    xv[4 * q + 1] = v[1];
-                    xv[4 * q + 2] = v[2];
-                    xv[4 * q + 3] = v[3];
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const floatx4 v = *reinterpret_cast<const floatx4*>(xs + c * XP + 8 * dj + kb * D + 4 * q);
+                        xv[4 * q] = v[0];
+                        xv[4 * q + 1] = v[1];
+                        xv[4 * q + 2] = v[2];
+                        xv[4 * q + 3] = v[3];
+                    }
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    if (kb + kk < K) {
-                        const float wk = ws[c * K + kb + kk];
+                    for (int kk = 0; kk < TPB; ++kk) {
+                        if (kb + kk < K) {
+                            const float wk = ws[c * K + kb + kk];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) sacc[i] += wk * xv[i + kk];
+                            for (int i = 0; i < 8; ++i) sacc[i] += wk * xv[i + kk * D];
+                        }
                     }
                 }
+            };
+            if constexpr (Cfg::KC < 0) {
+                if (dil == 2)
+                    taps(std::integral_constant<int, 2>{});
+                else if (dil == 4)
+                    taps(std::integral_constant<int, 4>{});
+                else
+                    taps(std::integral_constant<int, 8>{});
+            } else {
+                taps(std::integral_constant<int, 1>{});
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) Ds[(8 * dj + i) * CCP + (c ^ ((dj >> 1) << 2))] = sacc[i];
@@ -564,6 +582,10 @@ using DwTall9M = DwsepCfg<2, 4, 8, 1, 64, 9, 4>;
 using DwTallKM = DwsepCfg<2, 4, 8, 1, 64, 0, 4>;
 using DwTall9S = DwsepCfg<1, 4, 8, 1, 64, 9, 4>;
 using DwTallKS = DwsepCfg<1, 4, 8, 1, 64, 0, 4>;
+// Dilation 2, 4 or 8 (KC = -1: runtime K).
+using DwTallKD = DwsepCfg<4, 4, 8, 1, 64, -1, 4>;
+using DwTallKMD = DwsepCfg<2, 4, 8, 1, 64, -1, 4>;
+using DwTallKSD = DwsepCfg<1, 4, 8, 1, 64, -1, 4>;
 
 template <class Cfg>
 static constexpr size_t tall_lds_bytes(int K) {
@@ -798,19 +820,24 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
     const int n_tiles = n_tt * n_ot * s.B;  // < 2^31: checked by tall_tiles_fit
     const int vec_out = (s.Tout % 4 == 0) && ((uintptr_t)y % 16 == 0);
     hipLaunchKernelGGL(dwsep_tall_kernel<Cfg>, dim3(n_tiles), dim3(Cfg::NT), lds, stream, x, w_dw, w_pw, b_pw,
-                       y, s.C, s.T, s.K, s.O, s.pad, s.Tout, n_tt, n_ot, vec_out);
+                       y, s.C, s.T, s.K, s.O, s.pad, s.Tout, n_tt, n_ot, vec_out, s.dil);
     return hipGetLastError();
 }
 
 // The instance a shape runs on: 0 = none fits, 1 = wide K=9, 2 = wide
 // runtime-K, 3 = narrow runtime-K, 4 = small runtime-K, 5/6 = tall K=9 /
-// runtime-K (512 rows), 7/8 = the same with 256 rows, 9/10 with 128 rows.
+// runtime-K (512 rows), 7/8 = the same with 256 rows, 9/10 with 128 rows,
+// 11/12/13 = dilation 2, 4 or 8 with 512, 256 or 128 rows.
 // The tall tile needs 16-byte weight loads (C a multiple of 4 and an aligned
 // w_pw), which the caller states in vec_ok.
 static int pick_dw(const DwsepShape& s, bool vec_ok) {
     const bool unit = s.stride == 1 && s.dil == 1;
 #ifndef FCONV_DW_NO_TALL
-    if (unit && vec_ok && s.O > 64 && s.K <= 64 && s.C % 4 == 0 && tall_tiles_fit(s)) {
+    // the tall tile: stride 1, dilation 1, 2, 4 or 8, a window of at most 64 steps
+    const bool tall_dil = s.dil == 1 || s.dil == 2 || s.dil == 4 || s.dil == 8;
+    if (s.stride == 1 && tall_dil && (int64_t)(s.K - 1) * s.dil <= 63 && vec_ok && s.O > 64 && s.C % 4 == 0 &&
+        tall_tiles_fit(s)) {
+        if (s.dil > 1) return s.O > 256 ? 11 : s.O > 128 ? 12 : 13;
         if (s.O > 256) return s.K == 9 ? 5 : 6;
         if (s.O > 128) return s.K == 9 ? 7 : 8;
         return s.K == 9 ? 9 : 10;
@@ -842,6 +869,9 @@ hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, 
         case 8: return launch_tall<DwTallKM>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 9: return launch_tall<DwTall9S>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 10: return launch_tall<DwTallKS>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 11: return launch_tall<DwTallKD>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 12: return launch_tall<DwTallKMD>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 13: return launch_tall<DwTallKSD>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

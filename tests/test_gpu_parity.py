@@ -660,10 +660,18 @@ def test_dwsep_tall_tile_inf_in_next_row(fc):
 STRIDED_DW = [
     # B, C, T, O, K, pad, stride, dilation
     (2, 64, 300, 300, 9, 4, 2, 1),     # wide runtime-K instance, stride 2
-    (1, 48, 257, 512, 9, 8, 1, 2),     # dilation 2
+    (1, 48, 257, 512, 9, 8, 1, 2),     # dilation 2: the tall tile's dilated instance, 512 rows
     (2, 20, 100, 40, 5, 3, 3, 2),      # small instance
     (1, 16, 2000, 128, 9, 4, 16, 1),   # window too wide for 64 steps: narrow instance
     (1, 32, 40, 64, 3, 0, 5, 4),       # few output steps
+    # the tall tile's dilated instances: dilation 2, 4 and 8 on 512-, 256- and 128-row tiles, up to the
+    # widest window it stages ((K - 1) * dilation = 63), and one past it (the 256-row kernel)
+    (2, 36, 150, 300, 5, 8, 1, 4),     # dilation 4, blocks of 2 taps, a ragged time tile, a partial chunk
+    (1, 64, 130, 200, 8, 28, 1, 8),    # dilation 8, one tap per block, 256 rows
+    (1, 100, 120, 100, 32, 31, 1, 2),  # dilation 2, (K - 1) * dil = 62, 128 rows, chunks of 64 + 36
+    (1, 40, 140, 300, 16, 30, 1, 4),   # dilation 4, (K - 1) * dil = 60
+    (1, 40, 140, 300, 17, 32, 1, 4),   # (K - 1) * dil = 64: past the tall tile, the 256-row kernel
+    (1, 32, 90, 300, 9, 12, 1, 3),     # dilation 3: the 256-row kernel
 ]
 
 
