@@ -635,7 +635,7 @@ def main():
         ((y_dense - y).abs() <= 1e-4 + 1e-4 * y.abs()).all().item())
 
     # the conv1d generalisations at the dwsep_full scale: stride 2 (over twice the steps, so Tout is the
-    # same), dilation 2, and 256 output channels (the tall tile's 256-row instance); parity for these
+    # same; the 256-row kernel), dilation 2 and 256 output channels (the tall tile); parity for these
     # forms is in tests/test_gpu_parity.py and tests/test_gpu_random_shapes.py
     def dw_gen(B, C, T, O, K, pad, stride, dil, seed):
         xg = torch.from_numpy(fi.dwsep_inputs(B, C, T, O, K, seed=seed)[0]).to(dev)
@@ -653,7 +653,7 @@ def main():
     f3 = 2 * dc["B"] * dc["T"] * dc["C"] * (dc["K"] + dc["O"])
     variants["dwsep_conv1d_dilation2"] = variant(
         lambda: fc.dwsep_conv1d(xg, wdw, wpw, bpw, 2 * dc["pad"], out=y_dense, dilation=2),
-        f3, b_dw, f"dilation 2, pad 8 on {DW}: the 256-row kernel (dwsep_mfma_kernel), own separable FLOPs")
+        f3, b_dw, f"dilation 2, pad 8 on {DW}: the tall tile's dilated instance, own separable FLOPs")
     del y_dense
     O4 = dc["O"] // 2
     y4 = torch.empty(dc["B"], O4, dc["T"], device=dev)
