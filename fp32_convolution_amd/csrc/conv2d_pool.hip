@@ -487,7 +487,8 @@ struct BoxLayout {
 #define FCONV_BOX_K5S3_MIN_WAVES 6
 #endif
 // The 4-wave K3/s2 and K3/s3 instances are held to 8 waves per SIMD (64
-// VGPRs: 57-61 used, no VGPR spills): unbounded, the compiler took 100
+// VGPRs: 58-61 used, no VGPR spills; 5-9 SGPRs kept in VGPR lanes):
+// unbounded, the compiler took 100
 // registers (accumulators in AGPRs) and 4 waves per SIMD, and these short
 // workgroups (36 MFMAs per channel quad and wave) had too few waves to hide
 // their loads and barriers: 0.4384 against 0.4538 ms for K3/s2 and 0.2422
@@ -812,8 +813,8 @@ __global__ __launch_bounds__(Cfg::NT, box_min_waves<Cfg>()) void conv2d_pool_box
 //     h0 = (u0+u1) + (u2+u3),  h1 = (u1+u2) + (u3+n0),  h2 = (u2+u3) + (n0+n1).
 // That is 114 adds per channel, 12 of which read the next lane's operand
 // through a DPP modifier (no move of their own); summing each row across
-// first took 138 adds and 20 moves.  The 9 values go to LDS tap-major, Sx[ic][ph][tap][pw]
-// (consecutive lanes write and read consecutive words), which the
+// first took 138 adds and 20 moves.  The 9 values go to LDS tap-major,
+// Sx[ic][ph][tap][pw] (consecutive lanes write and read consecutive words), which the
 // contraction reads as B operands, one word per MFMA step.  Each channel's
 // plane is padded by 16 words so that the four lane groups, which read four
 // channels, start 16 banks apart.  For Cin = 8 that is 28 KB per workgroup,

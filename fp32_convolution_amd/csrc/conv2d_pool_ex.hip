@@ -564,8 +564,8 @@ __global__ __launch_bounds__(C::NT, C::CHUNK ? 4 : 3) void conv2d_pool_elem_kern
             // Epilogue of pooled row ph.  Lane (g, l16) holds in acc[nb][dy][r]
             // the conv output of channel co0 + 4g + r at conv row ph*S + dy,
             // column x0 + nb*16 + l16 (TF: channel co0 + l16, column
-            // x0 + nb*16 + 4g + r, rows summed).  The pool works on register
-            // copies.
+            // x0 + nb*16 + 4g + r; folded: the window's rows summed in
+            // acc[nb][0]).  The pool works on register copies.
             // Conv outputs outside the map exist only in partial (ceil-mode)
             // windows at the bottom and right edges; those rows take a separate
             // copy of the epilogue that masks them.
