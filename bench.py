@@ -635,7 +635,7 @@ def main():
         ((y_dense - y).abs() <= 1e-4 + 1e-4 * y.abs()).all().item())
 
     # the conv1d generalisations at the dwsep_full scale: stride 2 (over twice the steps, so Tout is the
-    # same; the 256-row kernel), dilation 2 and 256 output channels (the tall tile); parity for these
+    # same), dilation 2 and 256 output channels, all on the tall tile; parity for these
     # forms is in tests/test_gpu_parity.py and tests/test_gpu_random_shapes.py
     def dw_gen(B, C, T, O, K, pad, stride, dil, seed):
         xg = torch.from_numpy(fi.dwsep_inputs(B, C, T, O, K, seed=seed)[0]).to(dev)
@@ -647,7 +647,7 @@ def main():
     variants["dwsep_conv1d_stride2"] = variant(
         lambda: fc.dwsep_conv1d(x2, wdw, wpw, bpw, dc["pad"], out=y_dense, stride=2),
         f2, b2, f"stride 2 on x[{dc['B']},{dc['C']},{2 * dc['T']}] -> {dc['O']} channels (Tout {To2}), "
-        "K 9, pad 4: the 256-row kernel (dwsep_mfma_kernel), own separable FLOPs")
+        "K 9, pad 4: the tall tile's stride-2 instance, own separable FLOPs")
     del x2
     xg = torch.from_numpy(fi.dwsep_inputs(dc["B"], dc["C"], dc["T"], dc["O"], dc["K"], seed=42)[0]).to(dev)
     f3 = 2 * dc["B"] * dc["T"] * dc["C"] * (dc["K"] + dc["O"])

@@ -259,7 +259,7 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 
 // ---------------------------------------------------------------- tall-tile variant
 
-// Stride 1, dilation 1 (or 2, 4, 8), O > 256: a 512 x 64 tile (8 waves of 64 x 64), so
+// Stride 1, dilation 1 (or 2, 4, 8), or stride 2, O > 256: a 512 x 64 tile (8 waves of 64 x 64), so
 // each depthwise value is made once per time tile instead of once per 256
 // output channels, and the matrix cores see twice the work per depthwise
 // instruction.  64 < O <= 256 takes the same kernel with 256- or 128-row
@@ -289,28 +289,48 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 // LDS: xs [CC][132], then Ds: [64][CC+4] for the GEMM operand and
 // 8 x [16][68] in the epilogue, then the bias [512] and the taps [CC][K]
 // (70,656 + 256 K bytes: 72,960 for K = 9, two workgroups per CU up to
-// K = 44).  Row r of xs holds input steps t0-pad .. t0-pad+127 (two 64-lane
+// K = 44).  Stride 2: 64 outputs read 127 + K steps, staged as three runs
+// (xs [CC][196]); the epilogue then stages through xs and Ds, so the total
+// is 69,632 + 256 K bytes (71,936 for K = 9).  Row r of xs holds input steps t0-pad .. t0-pad+127 (two 64-lane
 // runs; steps past the (K-1)*dil halo or outside [0, T) load as 0); the
 // runtime-K blocks read up to step 8*7 + 8*floor((K-1)*dil/8) + 15, so
 // (K-1)*dil <= 63.  Dilation 2, 4 or 8 runs on the runtime-K instance.
 // Pointwise weights: lane (g, l16) of block ob keeps channels 4g..4g+3 of
 // the current group; the registers of block ob are refilled with the next
 // group's weights as soon as its 16 matrix instructions are issued.
-template <class Cfg>
+// Tall-tile LDS geometry for stride ST: NRUN 64-step runs staged per input
+// row (64 outputs read (TT - 1) * ST + (K - 1) * dil + 1 steps), a row pitch
+// of the runs + 4 (rows of consecutive channels start 16 bytes apart on the
+// banks), and the float count of the region after xs.  With stride 1 the
+// epilogue's [NW][16][68] staging gets a region of its own beside Ds; with
+// stride 2 the wider xs rows leave no room for it, so the epilogue stages
+// through xs and Ds together (both free by then: the last chunk stages no
+// next chunk) and the region after xs is Ds alone.
+template <class Cfg, int ST>
+struct TallGeom {
+    static constexpr int NRUN = ST == 1 ? 2 : 3;
+    static constexpr int XP = 64 * NRUN + 4;
+    static constexpr int OP = 68;
+    static constexpr int EPI = Cfg::NW * 16 * OP;
+    static constexpr int DS = Cfg::TT * Cfg::CCP;
+    static constexpr int DSF = ST == 1 ? (DS > EPI ? DS : EPI) : DS;
+    static_assert(ST == 1 || Cfg::CC * XP + DS >= EPI, "the epilogue fits xs + Ds");
+};
+
+template <class Cfg, int ST>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     const float* __restrict__ x, const float* __restrict__ w_dw, const float* __restrict__ w_pw,
     const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int Kr, int O, int pad, int Tout, int n_tt,
     int n_ot, int vec_out, int dil) {
     constexpr int OB = Cfg::OB, TB = Cfg::TB, CC = Cfg::CC, CCP = Cfg::CCP, CPW = Cfg::CPW;
-    // xs row pitch: 128 staged steps + 4, so that rows of consecutive
-    // channels start 16 bytes apart on the LDS banks
-    constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = 132, OP = 68;
-    constexpr int DSF = TT * CCP > NW * 16 * OP ? TT * CCP : NW * 16 * OP;
+    using G = TallGeom<Cfg, ST>;
+    constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = G::XP, OP = G::OP, DSF = G::DSF, NRUN = G::NRUN;
+    static_assert(ST == 1 || (ST == 2 && Cfg::KC >= 0), "stride 2 with dilation 1");
     static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && (OB == 4 || OB == 2 || OB == 1) && TB == 4,
                   "waves of 16 OB x 64 along o");
     static_assert(CC % NW == 0 && CC % 16 == 0, "whole rows per wave, whole groups per chunk");
     const int K = Cfg::KC > 0 ? Cfg::KC : Kr;
-    const int XW = TT + (K - 1) * dil;  // input steps the tile reads (<= 128)
+    const int XW = (TT - 1) * ST + (K - 1) * dil + 1;  // input steps the tile reads (<= 64 * NRUN)
 
     // xs first: the depthwise reads then fit the short LDS offset fields
     extern __shared__ float lds[];
@@ -334,17 +354,17 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     const int tile = blockIdx.x;
     const int tq = tile / n_tt;
     const int bi = tq / n_ot;
-    const int t0 = (tile - tq * n_tt) * TT;
+    const int t0 = (tile - tq * n_tt) * TT;  // first output step
     const int o0 = (tq - bi * n_ot) * Cfg::OT + wave * 16 * OB;  // this wave's first output channel
     const float* xb = x + (size_t)bi * C * T;
 
-    // 1. staging: per row two LDS-direct loads of 64 consecutive steps; rows
-    //    >= C get an empty resource and load 0
-    int voff[2];
+    // 1. staging: per row NRUN LDS-direct loads of 64 consecutive steps from
+    //    input step t0*ST - pad; rows >= C get an empty resource and load 0
+    int voff[NRUN];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NRUN; ++r) {
         const int u = 64 * r + lane;
-        const int src = t0 - pad + u;
+        const int src = t0 * ST - pad + u;
         voff[r] = (u < XW && src >= 0) ? src * 4 : kBufOOB;
     }
     auto stage = [&](int c0) {
@@ -353,7 +373,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
             const int row = c0 + wave + i * NW;
             const buf_rsrc rr = make_rsrc(xb + (size_t)min(row, C - 1) * T, row < C ? T * 4 : 0);
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
+            for (int r = 0; r < NRUN; ++r)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, xs3 + (wave + i * NW) * XP + 64 * r, 4, voff[r], 0, 0,
                                                          0);
         }
@@ -412,15 +432,18 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
             }
         }
         // 2. depthwise -> Ds[t][c] for the wave's CPW channels (channels >= C
-        //    read the zero rows staged for them, so their D is 0)
+        //    read the zero rows staged for them, so their D is 0).  Lane
+        //    (dc, dj) makes output steps 8dj .. 8dj+7, whose inputs start at
+        //    staged step 8*ST*dj: NX = 8*ST + 8 staged steps cover 8 taps.
+        constexpr int NX = 8 * ST + 8;
         if constexpr (Cfg::KC == 9) {
             static_assert(CPW == 8, "8 channels x 8 groups of 8 steps per wave");
             const int dj = lane & 7, dc = lane >> 3;
             const int c = wave * CPW + dc;
-            float xv[16], wv[9];
+            float xv[NX], wv[9];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const floatx4 v = *reinterpret_cast<const floatx4*>(xs + c * XP + 8 * dj + 4 * q);
+            for (int q = 0; q < NX / 4; ++q) {
+                const floatx4 v = *reinterpret_cast<const floatx4*>(xs + c * XP + 8 * ST * dj + 4 * q);
                 xv[4 * q] = v[0];
                 xv[4 * q + 1] = v[1];
                 xv[4 * q + 2] = v[2];
@@ -432,17 +455,18 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
             for (int i = 0; i < 8; ++i) {
                 float s = 0.f;
 #pragma unroll
-                for (int k = 0; k < 9; ++k) s += wv[k] * xv[i + k];
+                for (int k = 0; k < 9; ++k) s += wv[k] * xv[ST * i + k];
                 Ds[(8 * dj + i) * CCP + (c ^ ((dj >> 1) << 2))] = s;  // swizzled: see read_d
             }
         } else {
             // runtime K: the same lanes and chains, over blocks of 8 / dil
             // taps (KC = 0: dilation 1; KC = -1: dilation 2, 4 or 8, a
             // compile-time copy each, in instances of their own so that the
-            // undilated ones keep their registers); block kb
-            // reads 16 staged steps from 8dj + kb*dil (16-byte aligned: kb*dil
-            // is a multiple of 8), tap kb + kk at step i + kk*dil of them, and
-            // (K - 1) * dil <= 63 keeps them inside the row's 128 staged steps
+            // undilated ones keep their registers); block kb reads NX staged
+            // steps from 8*ST*dj + kb*dil (16-byte aligned: kb*dil is a
+            // multiple of 8), tap kb + kk at step ST*i + kk*dil of them, and
+            // (K - 1) * dil <= 63 keeps them inside the row's 64 * NRUN staged
+            // steps
             static_assert(CPW == 8, "8 channels x 8 groups of 8 steps per wave");
             const int dj = lane & 7, dc = lane >> 3;
             const int c = wave * CPW + dc;
@@ -452,10 +476,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
             auto taps = [&](auto dil_tag) {
                 constexpr int D = decltype(dil_tag)::value, TPB = 8 / D;
                 for (int kb = 0; kb < K; kb += TPB) {
-                    float xv[16];
+                    float xv[NX];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const floatx4 v = *reinterpret_cast<const floatx4*>(xs + c * XP + 8 * dj + kb * D + 4 * q);
+                    for (int q = 0; q < NX / 4; ++q) {
+                        const floatx4 v =
+                            *reinterpret_cast<const floatx4*>(xs + c * XP + 8 * ST * dj + kb * D + 4 * q);
                         xv[4 * q] = v[0];
                         xv[4 * q + 1] = v[1];
                         xv[4 * q + 2] = v[2];
@@ -466,7 +491,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
                         if (kb + kk < K) {
                             const float wk = ws[c * K + kb + kk];
 #pragma unroll
-                            for (int i = 0; i < 8; ++i) sacc[i] += wk * xv[i + kk * D];
+                            for (int i = 0; i < 8; ++i) sacc[i] += wk * xv[ST * i + kk * D];
                         }
                     }
                 }
@@ -539,7 +564,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     float* yb = y + (size_t)bi * O * Tout;
     __syncthreads();  // every wave is done reading Ds (outside the branch: o0 differs per wave)
     if (vec_out && o0 + 16 * OB <= O && t0 + TT <= Tout) {
-        float* ow = Ds + wave * 16 * OP;
+        float* ow = (ST == 1 ? Ds : lds) + wave * 16 * OP;  // see TallGeom
 #pragma unroll
         for (int ob = 0; ob < OB; ++ob) {
 #pragma unroll
@@ -587,10 +612,11 @@ using DwTallKD = DwsepCfg<4, 4, 8, 1, 64, -1, 4>;
 using DwTallKMD = DwsepCfg<2, 4, 8, 1, 64, -1, 4>;
 using DwTallKSD = DwsepCfg<1, 4, 8, 1, 64, -1, 4>;
 
-template <class Cfg>
+template <class Cfg, int ST>
 static constexpr size_t tall_lds_bytes(int K) {
-    constexpr size_t ds = (size_t)(Cfg::TT * Cfg::CCP > Cfg::NW * 16 * 68 ? Cfg::TT * Cfg::CCP : Cfg::NW * 16 * 68);
-    return ((size_t)Cfg::CC * 132 + ds + (size_t)Cfg::NW * 64 + (size_t)(K * Cfg::CC + 63) / 64 * 64) * sizeof(float);
+    using G = TallGeom<Cfg, ST>;
+    return ((size_t)Cfg::CC * G::XP + G::DSF + (size_t)Cfg::NW * 64 + (size_t)(K * Cfg::CC + 63) / 64 * 64) *
+           sizeof(float);
 }
 
 
@@ -809,17 +835,17 @@ static bool tall_tiles_fit(const DwsepShape& s) {
     return n <= 0x7fffffffL;
 }
 
-template <class Cfg>
+template <class Cfg, int ST = 1>
 static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                               const float* b_pw, float* y, hipStream_t stream) {
-    const size_t lds = tall_lds_bytes<Cfg>(s.K);
-    hipError_t e = hipFuncSetAttribute((const void*)dwsep_tall_kernel<Cfg>,
+    const size_t lds = tall_lds_bytes<Cfg, ST>(s.K);
+    hipError_t e = hipFuncSetAttribute((const void*)dwsep_tall_kernel<Cfg, ST>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int n_tt = (s.Tout + Cfg::TT - 1) / Cfg::TT, n_ot = (s.O + Cfg::OT - 1) / Cfg::OT;
     const int n_tiles = n_tt * n_ot * s.B;  // < 2^31: checked by tall_tiles_fit
     const int vec_out = (s.Tout % 4 == 0) && ((uintptr_t)y % 16 == 0);
-    hipLaunchKernelGGL(dwsep_tall_kernel<Cfg>, dim3(n_tiles), dim3(Cfg::NT), lds, stream, x, w_dw, w_pw, b_pw,
+    hipLaunchKernelGGL((dwsep_tall_kernel<Cfg, ST>), dim3(n_tiles), dim3(Cfg::NT), lds, stream, x, w_dw, w_pw, b_pw,
                        y, s.C, s.T, s.K, s.O, s.pad, s.Tout, n_tt, n_ot, vec_out, s.dil);
     return hipGetLastError();
 }
@@ -827,7 +853,8 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 // The instance a shape runs on: 0 = none fits, 1 = wide K=9, 2 = wide
 // runtime-K, 3 = narrow runtime-K, 4 = small runtime-K, 5/6 = tall K=9 /
 // runtime-K (512 rows), 7/8 = the same with 256 rows, 9/10 with 128 rows,
-// 11/12/13 = dilation 2, 4 or 8 with 512, 256 or 128 rows.
+// 11/12/13 = dilation 2, 4 or 8 with 512, 256 or 128 rows, 14..19 = 5..10
+// with stride 2.
 // The tall tile needs 16-byte weight loads (C a multiple of 4 and an aligned
 // w_pw), which the caller states in vec_ok.
 static int pick_dw(const DwsepShape& s, bool vec_ok) {
@@ -841,6 +868,12 @@ static int pick_dw(const DwsepShape& s, bool vec_ok) {
         if (s.O > 256) return s.K == 9 ? 5 : 6;
         if (s.O > 128) return s.K == 9 ? 7 : 8;
         return s.K == 9 ? 9 : 10;
+    }
+    // and stride 2 with dilation 1, K <= 64 (three staged runs per row)
+    if (s.stride == 2 && s.dil == 1 && s.K <= 64 && vec_ok && s.O > 64 && s.C % 4 == 0 && tall_tiles_fit(s)) {
+        if (s.O > 256) return s.K == 9 ? 14 : 15;
+        if (s.O > 128) return s.K == 9 ? 16 : 17;
+        return s.K == 9 ? 18 : 19;
     }
 #endif
     if (s.O > 64) {
@@ -872,6 +905,12 @@ hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, 
         case 11: return launch_tall<DwTallKD>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 12: return launch_tall<DwTallKMD>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 13: return launch_tall<DwTallKSD>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 14: return launch_tall<DwTall9, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 15: return launch_tall<DwTallK, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 16: return launch_tall<DwTall9M, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 17: return launch_tall<DwTallKM, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 18: return launch_tall<DwTall9S, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 19: return launch_tall<DwTallKS, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

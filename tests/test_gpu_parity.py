@@ -659,7 +659,7 @@ def test_dwsep_tall_tile_inf_in_next_row(fc):
 
 STRIDED_DW = [
     # B, C, T, O, K, pad, stride, dilation
-    (2, 64, 300, 300, 9, 4, 2, 1),     # wide runtime-K instance, stride 2
+    (2, 64, 300, 300, 9, 4, 2, 1),     # stride 2: the tall tile's stride-2 K = 9 instance, 512 rows
     (1, 48, 257, 512, 9, 8, 1, 2),     # dilation 2: the tall tile's dilated instance, 512 rows
     (2, 20, 100, 40, 5, 3, 3, 2),      # small instance
     (1, 16, 2000, 128, 9, 4, 16, 1),   # window too wide for 64 steps: narrow instance
@@ -672,6 +672,11 @@ STRIDED_DW = [
     (1, 40, 140, 300, 16, 30, 1, 4),   # dilation 4, (K - 1) * dil = 60
     (1, 40, 140, 300, 17, 32, 1, 4),   # (K - 1) * dil = 64: past the tall tile, the 256-row kernel
     (1, 32, 90, 300, 9, 12, 1, 3),     # dilation 3: the 256-row kernel
+    # the tall tile at stride 2 (three staged runs per row, the epilogue staged through xs and Ds)
+    (1, 36, 257, 200, 5, 2, 2, 1),     # runtime K, 256 rows, an odd T (ragged last time tile)
+    (2, 68, 131, 100, 9, 4, 2, 1),     # K = 9, 128 rows, chunks of 64 + 4 channels
+    (1, 40, 300, 520, 64, 32, 2, 1),   # the widest window it stages, two 512-row tiles
+    (1, 40, 300, 520, 65, 32, 2, 1),   # one wider: the 256-row kernel
 ]
 
 
@@ -716,6 +721,22 @@ def test_dwsep_dense_full_size_sampled(fc):
     samp = np.stack([rng.integers(0, n, 5000) for n in got.shape], axis=1)
     want = oracle.dwsep_conv1d_at(x, w_dw, w_pw, b_pw, cfg["pad"], samp)
     assert_close(got[tuple(samp.T)], want, "dense sampled")
+
+
+def test_dwsep_stride2_full_size_sampled(fc):
+    # stride 2 over x[32,256,8192] -> 512 (Tout 4096, the dwsep_full output): the tall tile's stride-2
+    # instance at full size, 5000 sampled outputs with the padded edges against the oracle
+    announce("dwsep stride 2 full size")
+    B, C, T, O, K, pad = 32, 256, 8192, 512, 9, 4
+    x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=41)
+    got = fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad, stride=2).cpu().numpy()
+    assert got.shape == (B, O, 4096)
+    rng = np.random.default_rng(9)
+    samp = np.stack([rng.integers(0, n, 5000) for n in got.shape], axis=1)
+    samp[:100, 2] = 0
+    samp[100:200, 2] = got.shape[2] - 1
+    want = oracle.dwsep_conv1d_at(x, w_dw, w_pw, b_pw, pad, samp, stride=2)
+    assert_close(got[tuple(samp.T)], want, "stride 2 sampled")
 
 
 def test_dwsep_no_bias_and_torch_shapes(fc):
