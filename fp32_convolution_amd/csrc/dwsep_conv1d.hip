@@ -607,6 +607,13 @@ using DwTall9M = DwsepCfg<2, 4, 8, 1, 64, 9, 4>;
 using DwTallKM = DwsepCfg<2, 4, 8, 1, 64, 0, 4>;
 using DwTall9S = DwsepCfg<1, 4, 8, 1, 64, 9, 4>;
 using DwTallKS = DwsepCfg<1, 4, 8, 1, 64, 0, 4>;
+// O <= 64: 64 rows as 4 waves of 16 x 64 (32-channel chunks), O <= 32: 32 rows
+// as 2 waves (16-channel chunks), so each wave still makes the depthwise
+// values of 8 channels.
+using DwTall9Q = DwsepCfg<1, 4, 4, 1, 32, 9, 4>;
+using DwTallKQ = DwsepCfg<1, 4, 4, 1, 32, 0, 4>;
+using DwTall9E = DwsepCfg<1, 4, 2, 1, 16, 9, 4>;
+using DwTallKE = DwsepCfg<1, 4, 2, 1, 16, 0, 4>;
 // Dilation 2, 4 or 8 (KC = -1: runtime K).
 using DwTallKD = DwsepCfg<4, 4, 8, 1, 64, -1, 4>;
 using DwTallKMD = DwsepCfg<2, 4, 8, 1, 64, -1, 4>;
@@ -830,7 +837,7 @@ static hipError_t launch_dw(const DwsepShape& s, const float* x, const float* w_
 
 // The tall kernel's 1-D grid holds every (time tile, output tile, item).
 static bool tall_tiles_fit(const DwsepShape& s) {
-    const int ot = DwTall9S::OT;  // the smallest tile height of the instances
+    const int ot = DwTall9E::OT;  // the smallest tile height of the instances
     const long n = (long)((s.Tout + 63) / 64) * ((s.O + ot - 1) / ot) * s.B;
     return n <= 0x7fffffffL;
 }
@@ -854,7 +861,7 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 // runtime-K, 3 = narrow runtime-K, 4 = small runtime-K, 5/6 = tall K=9 /
 // runtime-K (512 rows), 7/8 = the same with 256 rows, 9/10 with 128 rows,
 // 11/12/13 = dilation 2, 4 or 8 with 512, 256 or 128 rows, 14..19 = 5..10
-// with stride 2.
+// with stride 2, 20/21 and 22/23 = K=9 / runtime-K with 64 and 32 rows.
 // The tall tile needs 16-byte weight loads (C a multiple of 4 and an aligned
 // w_pw), which the caller states in vec_ok.
 static int pick_dw(const DwsepShape& s, bool vec_ok) {
@@ -868,6 +875,11 @@ static int pick_dw(const DwsepShape& s, bool vec_ok) {
         if (s.O > 256) return s.K == 9 ? 5 : 6;
         if (s.O > 128) return s.K == 9 ? 7 : 8;
         return s.K == 9 ? 9 : 10;
+    }
+    // O <= 64 at stride 1, dilation 1: 64- or 32-row tiles
+    if (unit && s.K <= 64 && vec_ok && s.C % 4 == 0 && tall_tiles_fit(s)) {
+        if (s.O > 32) return s.K == 9 ? 20 : 21;
+        return s.K == 9 ? 22 : 23;
     }
     // and stride 2 with dilation 1, K <= 64 (three staged runs per row)
     if (s.stride == 2 && s.dil == 1 && s.K <= 64 && vec_ok && s.O > 64 && s.C % 4 == 0 && tall_tiles_fit(s)) {
@@ -911,6 +923,10 @@ hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, 
         case 17: return launch_tall<DwTallKM, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 18: return launch_tall<DwTall9S, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 19: return launch_tall<DwTallKS, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 20: return launch_tall<DwTall9Q>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 21: return launch_tall<DwTallKQ>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 22: return launch_tall<DwTall9E>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 23: return launch_tall<DwTallKE>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -593,6 +593,12 @@ TALL_DW = [
     (1, 36, 64, 128, 5, 2),      # 128 rows exactly, runtime K
     (2, 44, 150, 65, 9, 4),      # 128-row tile with one valid row in its fifth wave
     (1, 100, 80, 100, 17, 8),    # 128-row tile, runtime K, chunks of 64 + 36 channels
+    # O <= 64: 64-row tiles (4 waves, 32-channel chunks) and 32-row tiles (2 waves, 16-channel chunks)
+    (2, 36, 130, 64, 9, 4),      # 64 rows exactly, chunks of 32 + 4 channels, a ragged time tile
+    (1, 40, 100, 33, 5, 2),      # 64-row tile with one valid row in its third wave, runtime K
+    (2, 16, 70, 32, 9, 4),       # 32 rows exactly, one chunk
+    (1, 20, 64, 1, 3, 1),        # a single output channel: 32-row tile, runtime K, chunks of 16 + 4
+    (1, 64, 100, 17, 64, 32),    # the widest window on a 32-row tile
 ]
 
 
@@ -626,12 +632,12 @@ def test_dwsep_tall_tile(fc, shape):
     assert_close(got, want, f"y {shape}")
 
 
-@pytest.mark.parametrize("O", [300, 200, 100])
+@pytest.mark.parametrize("O", [300, 200, 100, 48, 20])
 def test_dwsep_tall_tile_every_k(fc, O):
     # every depthwise width the tall tile takes (K = 1 .. 64; K = 9 is its compiled instance, the rest run
     # the runtime-K stage over blocks of 8 taps), with odd and even padding and a partial channel chunk,
-    # against the oracle, for its 512-, 256- and 128-row tiles; K = 65 goes to the 256-row kernel and is
-    # checked the same way
+    # against the oracle, for its 512-, 256-, 128-, 64- and 32-row tiles; K = 65 goes to the older
+    # kernels and is checked the same way
     announce(f"dwsep tall tile, K = 1 .. 65, O = {O}")
     B, C, T = 1, 36, 100
     for K in range(1, 66):
