@@ -393,8 +393,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     // 16*ob + l16 of it at channels cb + 4g .. +3, with the channel offset
     // cb*4 in the scalar offset field.  A lane in range stays inside its
     // row, so the loads are in bounds whether or not the scalar offset
-    // enters the hardware range check.  Lanes whose channels are all >= C
-    // (C is a multiple of 4) take an out-of-range offset and load 0.
+    // enters the hardware range check.  Only whole runs of 4 channels below C
+    // load (rows of any C are 4-byte aligned, all a 4-dword buffer load
+    // needs); a lane whose run reaches C or past it takes an out-of-range
+    // offset and loads 0.  The run that C cuts (C % 4 != 0) is added once
+    // after the last chunk (step 3b).
     const int woff = (l16 * C + 4 * g) * 4;
     buf_rsrc rw[OB];
 #pragma unroll
@@ -403,8 +406,18 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
         rw[ob] = make_rsrc(w_pw + (size_t)(rows > 0 ? o0 + 16 * ob : 0) * C, rows > 0 ? rows * C * 4 : 0);
     }
     auto load_pw = [&](int ob, int cb) {
-        const int off = cb + 4 * g < C ? woff : kBufOOB;
+        const int off = cb + 4 * g + 3 < C ? woff : kBufOOB;
         return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rw[ob], off, cb * 4, 0));
+    };
+
+    // D[t][c] sits at column c ^ 4*(t >> 4) of row t: the 4-channel groups
+    // stay whole for these 16-byte reads (all lanes of one read share
+    // t >> 4 = tb, so they remain conflict-free), while the depthwise
+    // stage's writes, whose lanes cover 8 rows 8 apart (row pitch 68:
+    // every other row lands on the same banks), spread over 32 banks
+    // instead of 8.  This halved the kernel's LDS bank-conflict cycles.
+    auto read_d = [&](floatx4& dst, int tb, int s16) {
+        dst = *reinterpret_cast<const floatx4*>(Ds + (tb * 16 + l16) * CCP + ((s16 + 4 * g) ^ (tb << 2)));
     };
 
     floatx4 acc[OB][TB];
@@ -518,15 +531,6 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
         //    half's D registers take the next group's D once used.  The
         //    scheduling fences keep that order: without them the compiler
         //    moves the next group's first products up against their loads.
-        // D[t][c] sits at column c ^ 4*(t >> 4) of row t: the 4-channel groups
-        // stay whole for these 16-byte reads (all lanes of one read share
-        // t >> 4 = tb, so they remain conflict-free), while the depthwise
-        // stage's writes, whose lanes cover 8 rows 8 apart (row pitch 68:
-        // every other row lands on the same banks), spread over 32 banks
-        // instead of 8.  This halved the kernel's LDS bank-conflict cycles.
-        auto read_d = [&](floatx4& dst, int tb, int s16) {
-            dst = *reinterpret_cast<const floatx4*>(Ds + (tb * 16 + l16) * CCP + ((s16 + 4 * g) ^ (tb << 2)));
-        };
         floatx4 bq[TB];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) read_d(bq[tb], tb, 0);
@@ -558,6 +562,34 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
             a[OB - 1] = load_pw(OB - 1, cb);
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+
+    // 3b. C % 4 != 0: channels cl .. C-1 (cl = C rounded down to a multiple
+    //     of 4) belong to the lane group g = (cl % 16) / 4 of the group at
+    //     channel cl & ~15, in the last chunk, whose D values are still in Ds
+    //     (0 past channel C-1).  That lane group loads their weights one
+    //     channel at a time (the other lanes and channels >= C load 0), and
+    //     three more matrix steps add them.
+    if (C & 3) {
+        const int cl = C & ~3, cg = cl & ~15;
+        const int s16 = cg - (C - 1) / CC * CC;
+        const bool mine = 4 * g == (cl & 15);
+        floatx4 bq[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) read_d(bq[tb], tb, s16);
+#pragma unroll
+        for (int ob = 0; ob < OB; ++ob)
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int off = mine && cl + j < C ? woff + 4 * j : kBufOOB;
+                a[ob][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw[ob], off, cg * 4, 0));
+            }
+#pragma unroll
+        for (int ob = 0; ob < OB; ++ob)
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) acc[ob][tb] = mfma_16x16x4(a[ob][j], bq[tb][j], acc[ob][tb]);
     }
 
     // 4. epilogue: lane (g, l16) holds y[o0 + 16*ob + 4g + r, t0 + 16*tb + l16]
@@ -862,27 +894,25 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 // runtime-K (512 rows), 7/8 = the same with 256 rows, 9/10 with 128 rows,
 // 11/12/13 = dilation 2, 4 or 8 with 512, 256 or 128 rows, 14..19 = 5..10
 // with stride 2, 20/21 and 22/23 = K=9 / runtime-K with 64 and 32 rows.
-// The tall tile needs 16-byte weight loads (C a multiple of 4 and an aligned
-// w_pw), which the caller states in vec_ok.
-static int pick_dw(const DwsepShape& s, bool vec_ok) {
+// The tall tile takes any C and any 4-byte aligned w_pw.
+static int pick_dw(const DwsepShape& s) {
     const bool unit = s.stride == 1 && s.dil == 1;
 #ifndef FCONV_DW_NO_TALL
     // the tall tile: stride 1, dilation 1, 2, 4 or 8, a window of at most 64 steps
     const bool tall_dil = s.dil == 1 || s.dil == 2 || s.dil == 4 || s.dil == 8;
-    if (s.stride == 1 && tall_dil && (int64_t)(s.K - 1) * s.dil <= 63 && vec_ok && s.O > 64 && s.C % 4 == 0 &&
-        tall_tiles_fit(s)) {
+    if (s.stride == 1 && tall_dil && (int64_t)(s.K - 1) * s.dil <= 63 && s.O > 64 && tall_tiles_fit(s)) {
         if (s.dil > 1) return s.O > 256 ? 11 : s.O > 128 ? 12 : 13;
         if (s.O > 256) return s.K == 9 ? 5 : 6;
         if (s.O > 128) return s.K == 9 ? 7 : 8;
         return s.K == 9 ? 9 : 10;
     }
     // O <= 64 at stride 1, dilation 1: 64- or 32-row tiles
-    if (unit && s.K <= 64 && vec_ok && s.C % 4 == 0 && tall_tiles_fit(s)) {
+    if (unit && s.K <= 64 && tall_tiles_fit(s)) {
         if (s.O > 32) return s.K == 9 ? 20 : 21;
         return s.K == 9 ? 22 : 23;
     }
     // and stride 2 with dilation 1, K <= 64 (three staged runs per row)
-    if (s.stride == 2 && s.dil == 1 && s.K <= 64 && vec_ok && s.O > 64 && s.C % 4 == 0 && tall_tiles_fit(s)) {
+    if (s.stride == 2 && s.dil == 1 && s.K <= 64 && s.O > 64 && tall_tiles_fit(s)) {
         if (s.O > 256) return s.K == 9 ? 14 : 15;
         if (s.O > 128) return s.K == 9 ? 16 : 17;
         return s.K == 9 ? 18 : 19;
@@ -899,11 +929,11 @@ static int pick_dw(const DwsepShape& s, bool vec_ok) {
     return 0;
 }
 
-bool dwsep_supported(const DwsepShape& s) { return pick_dw(s, false) != 0; }
+bool dwsep_supported(const DwsepShape& s) { return pick_dw(s) != 0; }
 
 hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                         const float* b_pw, float* y, hipStream_t stream) {
-    switch (pick_dw(s, (uintptr_t)w_pw % 16 == 0)) {
+    switch (pick_dw(s)) {
         case 1: return launch_dw<DwWide9>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 2: return launch_dw<DwWideK>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 3: return launch_dw<DwNarrowK>(s, x, w_dw, w_pw, b_pw, y, stream);

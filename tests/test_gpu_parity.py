@@ -599,6 +599,17 @@ TALL_DW = [
     (2, 16, 70, 32, 9, 4),       # 32 rows exactly, one chunk
     (1, 20, 64, 1, 3, 1),        # a single output channel: 32-row tile, runtime K, chunks of 16 + 4
     (1, 64, 100, 17, 64, 32),    # the widest window on a 32-row tile
+    # C not a multiple of 4: the runtime-K instances with 4-byte weight loads, at every tile height
+    (2, 201, 130, 520, 9, 4),    # 512 rows, chunks of 64 x 3 + 9 (a group of 9 channels)
+    (1, 67, 100, 300, 33, 16),   # 512 rows, runtime K, a 3-channel last chunk
+    (1, 63, 100, 300, 64, 32),   # 512 rows, the widest window, one chunk one channel short
+    (2, 45, 150, 256, 5, 2),     # 256 rows exactly
+    (1, 101, 80, 129, 17, 8),    # 256 rows, one valid row in the fifth wave
+    (2, 30, 70, 100, 9, 4),      # 128 rows, a 14-channel group
+    (1, 1, 64, 65, 3, 1),        # one channel
+    (1, 37, 100, 64, 9, 4),      # 64 rows exactly
+    (2, 3, 70, 20, 5, 2),        # 32 rows, three channels
+    (1, 13, 64, 1, 1, 0),        # one output channel, 1-tap depthwise
 ]
 
 
@@ -648,11 +659,13 @@ def test_dwsep_tall_tile_every_k(fc, O):
         assert_close(got, want, f"y K={K} pad={pad}")
 
 
-def test_dwsep_tall_tile_inf_in_next_row(fc):
+@pytest.mark.parametrize("C", [36, 35])
+def test_dwsep_tall_tile_inf_in_next_row(fc, C):
     # Padded channels of a partial group must form no product: an infinite
-    # weight in row o+1 may not reach row o.
-    announce("dwsep tall tile, inf weight next to a partial group")
-    B, C, T, O, K, pad = 1, 36, 64, 300, 9, 4
+    # weight in row o+1 may not reach row o (with C = 35 that weight sits
+    # right after row o's last channel).
+    announce(f"dwsep tall tile, inf weight next to a partial group, C={C}")
+    B, T, O, K, pad = 1, 64, 300, 9, 4
     x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=14)
     w_pw = w_pw.copy()
     w_pw[101, 0] = np.inf
@@ -753,9 +766,9 @@ def test_dwsep_no_bias_and_torch_shapes(fc):
     assert_close(got, want, "y no bias")
 
 
-@pytest.mark.parametrize("O", [32, 300])
+@pytest.mark.parametrize("O", [32, 48, 100, 200, 300])
 def test_dwsep_unaligned_weights(fc, O):
-    # w_pw starting 4 bytes past a 16-byte boundary takes the scalar weight path.
+    # w_pw starting 4 bytes past a 16-byte boundary takes the 4-byte weight loads.
     announce(f"dwsep unaligned w_pw, O={O}")
     x, w_dw, w_pw, b_pw = fi.dwsep_inputs(1, 32, 64, O, 9, seed=9)
     want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, 4)
