@@ -42,7 +42,8 @@ namespace fconv {
 
 // OB, TB: 16x16 output blocks per wave along o and t; WO, WT: waves along o
 // and t; CC: channel chunk; KC: compile-time depthwise taps (0 = runtime K;
-// -1 = runtime K with dilation 2, 4 or 8, tall tile only);
+// -1 = runtime K with dilation 2, 4 or 8, -2 = runtime K with any dilation,
+// tall tile only);
 // MINW: waves per SIMD the register budget must allow.
 template <int OB_, int TB_, int WO_, int WT_, int CC_, int KC_, int MINW_>
 struct DwsepCfg {
@@ -326,6 +327,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     using G = TallGeom<Cfg, ST>;
     constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = G::XP, OP = G::OP, DSF = G::DSF, NRUN = G::NRUN;
     static_assert(ST == 1 || (ST == 2 && Cfg::KC >= 0), "stride 2 with dilation 1");
+    static_assert(Cfg::KC >= -2, "KC: 9, 0, -1 or -2");
     static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && (OB == 4 || OB == 2 || OB == 1) && TB == 4,
                   "waves of 16 OB x 64 along o");
     static_assert(CC % NW == 0 && CC % 16 == 0, "whole rows per wave, whole groups per chunk");
@@ -475,7 +477,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
             // runtime K: the same lanes and chains, over blocks of 8 / dil
             // taps (KC = 0: dilation 1; KC = -1: dilation 2, 4 or 8, a
             // compile-time copy each, in instances of their own so that the
-            // undilated ones keep their registers); block kb reads NX staged
+            // undilated ones keep their registers; KC = -2: any other
+            // dilation, tap by tap, stride 1); block kb reads NX staged
             // steps from 8*ST*dj + kb*dil (16-byte aligned: kb*dil is a
             // multiple of 8), tap kb + kk at step ST*i + kk*dil of them, and
             // (K - 1) * dil <= 63 keeps them inside the row's 64 * NRUN staged
@@ -509,7 +512,17 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
                     }
                 }
             };
-            if constexpr (Cfg::KC < 0) {
+            if constexpr (Cfg::KC == -2) {
+                // any other dilation: tap k reads the 8 steps from 8*dj + k*dil
+                // one word at a time (paired reads; the start is not 16-byte
+                // aligned), the same chains
+                for (int k = 0; k < K; ++k) {
+                    const float wk = ws[c * K + k];
+                    const float* xr = xs + c * XP + 8 * dj + k * dil;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) sacc[i] += wk * xr[i];
+                }
+            } else if constexpr (Cfg::KC < 0) {
                 if (dil == 2)
                     taps(std::integral_constant<int, 2>{});
                 else if (dil == 4)
@@ -646,10 +659,13 @@ using DwTall9Q = DwsepCfg<1, 4, 4, 1, 32, 9, 4>;
 using DwTallKQ = DwsepCfg<1, 4, 4, 1, 32, 0, 4>;
 using DwTall9E = DwsepCfg<1, 4, 2, 1, 16, 9, 4>;
 using DwTallKE = DwsepCfg<1, 4, 2, 1, 16, 0, 4>;
-// Dilation 2, 4 or 8 (KC = -1: runtime K).
+// Dilation 2, 4 or 8 (KC = -1: runtime K), and any other dilation (KC = -2).
 using DwTallKD = DwsepCfg<4, 4, 8, 1, 64, -1, 4>;
 using DwTallKMD = DwsepCfg<2, 4, 8, 1, 64, -1, 4>;
 using DwTallKSD = DwsepCfg<1, 4, 8, 1, 64, -1, 4>;
+using DwTallKG = DwsepCfg<4, 4, 8, 1, 64, -2, 4>;
+using DwTallKMG = DwsepCfg<2, 4, 8, 1, 64, -2, 4>;
+using DwTallKSG = DwsepCfg<1, 4, 8, 1, 64, -2, 4>;
 
 template <class Cfg, int ST>
 static constexpr size_t tall_lds_bytes(int K) {
@@ -893,15 +909,17 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 // runtime-K, 3 = narrow runtime-K, 4 = small runtime-K, 5/6 = tall K=9 /
 // runtime-K (512 rows), 7/8 = the same with 256 rows, 9/10 with 128 rows,
 // 11/12/13 = dilation 2, 4 or 8 with 512, 256 or 128 rows, 14..19 = 5..10
-// with stride 2, 20/21 and 22/23 = K=9 / runtime-K with 64 and 32 rows.
+// with stride 2, 20/21 and 22/23 = K=9 / runtime-K with 64 and 32 rows,
+// 24/25/26 = other dilations with 512, 256 or 128 rows.
 // The tall tile takes any C and any 4-byte aligned w_pw.
 static int pick_dw(const DwsepShape& s) {
     const bool unit = s.stride == 1 && s.dil == 1;
 #ifndef FCONV_DW_NO_TALL
-    // the tall tile: stride 1, dilation 1, 2, 4 or 8, a window of at most 64 steps
-    const bool tall_dil = s.dil == 1 || s.dil == 2 || s.dil == 4 || s.dil == 8;
-    if (s.stride == 1 && tall_dil && (int64_t)(s.K - 1) * s.dil <= 63 && s.O > 64 && tall_tiles_fit(s)) {
-        if (s.dil > 1) return s.O > 256 ? 11 : s.O > 128 ? 12 : 13;
+    // the tall tile: stride 1, a window of at most 64 steps
+    const bool pow2_dil = s.dil == 2 || s.dil == 4 || s.dil == 8;
+    if (s.stride == 1 && (int64_t)(s.K - 1) * s.dil <= 63 && s.O > 64 && tall_tiles_fit(s)) {
+        if (pow2_dil) return s.O > 256 ? 11 : s.O > 128 ? 12 : 13;
+        if (s.dil > 1) return s.O > 256 ? 24 : s.O > 128 ? 25 : 26;
         if (s.O > 256) return s.K == 9 ? 5 : 6;
         if (s.O > 128) return s.K == 9 ? 7 : 8;
         return s.K == 9 ? 9 : 10;
@@ -957,6 +975,9 @@ hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, 
         case 21: return launch_tall<DwTallKQ>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 22: return launch_tall<DwTall9E>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 23: return launch_tall<DwTallKE>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 24: return launch_tall<DwTallKG>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 25: return launch_tall<DwTallKMG>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 26: return launch_tall<DwTallKSG>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

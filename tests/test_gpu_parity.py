@@ -659,6 +659,20 @@ def test_dwsep_tall_tile_every_k(fc, O):
         assert_close(got, want, f"y K={K} pad={pad}")
 
 
+@pytest.mark.parametrize("dil", [3, 5, 6])
+def test_dwsep_tall_tile_any_dilation_every_k(fc, dil):
+    # every K the tall tile's tap-by-tap instance takes at this dilation ((K - 1) * dil <= 63), and the
+    # first K past it, with odd and even padding, against the oracle
+    announce(f"dwsep tall tile, dilation {dil}, every K")
+    B, C, T, O = 1, 36, 100, 300
+    for K in range(1, 63 // dil + 3):
+        pad = (K - 1) * dil // 2 if K % 2 else (K - 2) * dil // 2
+        x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=400 + K)
+        want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad, dilation=dil)
+        got = fc.dwsep_conv1d(dev(x), dev(w_dw), dev(w_pw), dev(b_pw), pad, dilation=dil).cpu().numpy()
+        assert_close(got, want, f"y K={K} pad={pad} dil={dil}")
+
+
 @pytest.mark.parametrize("C", [36, 35])
 def test_dwsep_tall_tile_inf_in_next_row(fc, C):
     # Padded channels of a partial group must form no product: an infinite
@@ -690,7 +704,13 @@ STRIDED_DW = [
     (1, 100, 120, 100, 32, 31, 1, 2),  # dilation 2, (K - 1) * dil = 62, 128 rows, chunks of 64 + 36
     (1, 40, 140, 300, 16, 30, 1, 4),   # dilation 4, (K - 1) * dil = 60
     (1, 40, 140, 300, 17, 32, 1, 4),   # (K - 1) * dil = 64: past the tall tile, the 256-row kernel
-    (1, 32, 90, 300, 9, 12, 1, 3),     # dilation 3: the 256-row kernel
+    # any other dilation: the tall tile's tap-by-tap instances
+    (1, 32, 90, 300, 9, 12, 1, 3),     # dilation 3, 512 rows
+    (2, 35, 150, 300, 5, 6, 1, 3),     # dilation 3, a ragged time tile, C % 4 != 0
+    (1, 68, 140, 200, 10, 27, 1, 7),   # dilation 7, (K - 1) * dil = 63, 256 rows
+    (1, 30, 120, 100, 4, 10, 1, 21),   # dilation 21, (K - 1) * dil = 63, 128 rows
+    (1, 33, 100, 129, 7, 18, 1, 6),    # dilation 6, 256 rows with one valid row in the fifth wave
+    (1, 40, 140, 300, 23, 33, 1, 3),   # (K - 1) * dil = 66: past the tall tile, the 256-row kernel
     # the tall tile at stride 2 (three staged runs per row, the epilogue staged through xs and Ds)
     (1, 36, 257, 200, 5, 2, 2, 1),     # runtime K, 256 rows, an odd T (ragged last time tile)
     (2, 68, 131, 100, 9, 4, 2, 1),     # K = 9, 128 rows, chunks of 64 + 4 channels
