@@ -915,22 +915,23 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 static int pick_dw(const DwsepShape& s) {
     const bool unit = s.stride == 1 && s.dil == 1;
 #ifndef FCONV_DW_NO_TALL
-    // the tall tile: stride 1, a window of at most 64 steps
+    // the tall tile: stride 1, a window of at most 64 steps.  With a dilation
+    // (and with stride 2, below) O <= 64 takes the 128-row tile, whose waves
+    // past O multiply zero weights: still far cheaper than the 32 x 32 tile,
+    // which remakes every depthwise value per 32 outputs and 32 steps.
     const bool pow2_dil = s.dil == 2 || s.dil == 4 || s.dil == 8;
-    if (s.stride == 1 && (int64_t)(s.K - 1) * s.dil <= 63 && s.O > 64 && tall_tiles_fit(s)) {
+    if (s.stride == 1 && (int64_t)(s.K - 1) * s.dil <= 63 && tall_tiles_fit(s)) {
         if (pow2_dil) return s.O > 256 ? 11 : s.O > 128 ? 12 : 13;
         if (s.dil > 1) return s.O > 256 ? 24 : s.O > 128 ? 25 : 26;
         if (s.O > 256) return s.K == 9 ? 5 : 6;
         if (s.O > 128) return s.K == 9 ? 7 : 8;
-        return s.K == 9 ? 9 : 10;
-    }
-    // O <= 64 at stride 1, dilation 1: 64- or 32-row tiles
-    if (unit && s.K <= 64 && tall_tiles_fit(s)) {
+        if (s.O > 64) return s.K == 9 ? 9 : 10;
+        // 64- or 32-row tiles
         if (s.O > 32) return s.K == 9 ? 20 : 21;
         return s.K == 9 ? 22 : 23;
     }
     // and stride 2 with dilation 1, K <= 64 (three staged runs per row)
-    if (s.stride == 2 && s.dil == 1 && s.K <= 64 && s.O > 64 && tall_tiles_fit(s)) {
+    if (s.stride == 2 && s.dil == 1 && s.K <= 64 && tall_tiles_fit(s)) {
         if (s.O > 256) return s.K == 9 ? 14 : 15;
         if (s.O > 128) return s.K == 9 ? 16 : 17;
         return s.K == 9 ? 18 : 19;

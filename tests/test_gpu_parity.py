@@ -711,6 +711,11 @@ STRIDED_DW = [
     (1, 30, 120, 100, 4, 10, 1, 21),   # dilation 21, (K - 1) * dil = 63, 128 rows
     (1, 33, 100, 129, 7, 18, 1, 6),    # dilation 6, 256 rows with one valid row in the fifth wave
     (1, 40, 140, 300, 23, 33, 1, 3),   # (K - 1) * dil = 66: past the tall tile, the 256-row kernel
+    # O <= 64 with a dilation or stride 2: the 128-row tile, its waves past O idle
+    (2, 36, 130, 40, 9, 8, 1, 2),      # dilation 2, O = 40
+    (1, 35, 131, 64, 5, 2, 2, 1),      # stride 2, O = 64, runtime K, C % 4 != 0
+    (1, 20, 100, 7, 7, 9, 1, 3),       # dilation 3, O = 7
+    (2, 16, 200, 1, 9, 4, 2, 1),       # stride 2, K = 9, one output channel
     # the tall tile at stride 2 (three staged runs per row, the epilogue staged through xs and Ds)
     (1, 36, 257, 200, 5, 2, 2, 1),     # runtime K, 256 rows, an odd T (ragged last time tile)
     (2, 68, 131, 100, 9, 4, 2, 1),     # K = 9, 128 rows, chunks of 64 + 4 channels
