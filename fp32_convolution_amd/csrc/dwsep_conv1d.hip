@@ -260,11 +260,14 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 
 // ---------------------------------------------------------------- tall-tile variant
 
-// Stride 1, dilation 1 (or 2, 4, 8), or stride 2, O > 256: a 512 x 64 tile (8 waves of 64 x 64), so
-// each depthwise value is made once per time tile instead of once per 256
-// output channels, and the matrix cores see twice the work per depthwise
-// instruction.  64 < O <= 256 takes the same kernel with 256- or 128-row
-// tiles (8 waves of 32 x 64 or 16 x 64).  The extra accumulator registers are paid for by staging x,
+// Stride 1 (any dilation) or 2 to 4, any C, O > 256: a 512 x 64 tile (8
+// waves of 64 x 64), so each depthwise value is made once per time tile
+// instead of once per 256 output channels, and the matrix cores see twice
+// the work per depthwise instruction.  Smaller O takes the same kernel with
+// 256- or 128-row tiles (8 waves of 32 x 64 or 16 x 64) and, at stride 1
+// and dilation 1, 64- or 32-row tiles (4 or 2 waves of 16 x 64; with a
+// stride or dilation O <= 64 runs the 128-row tile, its waves past O idle).
+// The extra accumulator registers are paid for by staging x,
 // the depthwise taps and the bias with LDS-direct buffer loads
 // (buffer_load_dword ... lds: memory to LDS with no register round trip),
 // which also lets the next chunk's rows stream in while the current chunk's
@@ -286,30 +289,34 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 // whose out-of-order return would serialize the LDS reads): 8 independent
 // multiply-add chains per lane.  The K = 9 instance reads 16 steps and 9
 // taps once; the runtime-K instance goes over the taps in blocks of 8, 16
-// steps per block.
+// steps per block (8 / dil taps per block with dilation 2, 4 or 8, and tap
+// by tap with single-word reads for any other dilation).
 // LDS: xs [CC][132], then Ds: [64][CC+4] for the GEMM operand and
 // 8 x [16][68] in the epilogue, then the bias [512] and the taps [CC][K]
 // (70,656 + 256 K bytes: 72,960 for K = 9, two workgroups per CU up to
 // K = 44).  Stride 2: 64 outputs read 127 + K steps, staged as three runs
 // (xs [CC][196]); the epilogue then stages through xs and Ds, so the total
-// is 69,632 + 256 K bytes (71,936 for K = 9).  Row r of xs holds input steps t0-pad .. t0-pad+127 (two 64-lane
+// is 69,632 + 256 K bytes (71,936 for K = 9).  Strides 3 and 4 stage four
+// and five runs (86,016 and 102,400 + 256 K bytes): one workgroup per CU.
+// Row r of xs holds input steps t0-pad .. t0-pad+127 (two 64-lane
 // runs; steps past the (K-1)*dil halo or outside [0, T) load as 0); the
 // runtime-K blocks read up to step 8*7 + 8*floor((K-1)*dil/8) + 15, so
-// (K-1)*dil <= 63.  Dilation 2, 4 or 8 runs on the runtime-K instance.
+// (K-1)*dil <= 63.  Dilations other than 1 run on runtime-K instances.
 // Pointwise weights: lane (g, l16) of block ob keeps channels 4g..4g+3 of
 // the current group; the registers of block ob are refilled with the next
 // group's weights as soon as its 16 matrix instructions are issued.
 // Tall-tile LDS geometry for stride ST: NRUN 64-step runs staged per input
-// row (64 outputs read (TT - 1) * ST + (K - 1) * dil + 1 steps), a row pitch
+// row (64 outputs read (TT - 1) * ST + (K - 1) * dil + 1 steps: 2 runs at
+// stride 1, ST + 1 above, for windows of at most 64 steps), a row pitch
 // of the runs + 4 (rows of consecutive channels start 16 bytes apart on the
 // banks), and the float count of the region after xs.  With stride 1 the
 // epilogue's [NW][16][68] staging gets a region of its own beside Ds; with
-// stride 2 the wider xs rows leave no room for it, so the epilogue stages
+// larger strides the wider xs rows leave no room for it, so the epilogue stages
 // through xs and Ds together (both free by then: the last chunk stages no
 // next chunk) and the region after xs is Ds alone.
 template <class Cfg, int ST>
 struct TallGeom {
-    static constexpr int NRUN = ST == 1 ? 2 : 3;
+    static constexpr int NRUN = ST + 1 > 2 ? ST + 1 : 2;
     static constexpr int XP = 64 * NRUN + 4;
     static constexpr int OP = 68;
     static constexpr int EPI = Cfg::NW * 16 * OP;
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     constexpr int OB = Cfg::OB, TB = Cfg::TB, CC = Cfg::CC, CCP = Cfg::CCP, CPW = Cfg::CPW;
     using G = TallGeom<Cfg, ST>;
     constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = G::XP, OP = G::OP, DSF = G::DSF, NRUN = G::NRUN;
-    static_assert(ST == 1 || (ST == 2 && Cfg::KC >= 0), "stride 2 with dilation 1");
+    static_assert(ST == 1 || Cfg::KC >= 0, "strides above 1 with dilation 1");
     static_assert(Cfg::KC >= -2, "KC: 9, 0, -1 or -2");
     static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && (OB == 4 || OB == 2 || OB == 1) && TB == 4,
                   "waves of 16 OB x 64 along o");
@@ -666,6 +673,10 @@ using DwTallKSD = DwsepCfg<1, 4, 8, 1, 64, -1, 4>;
 using DwTallKG = DwsepCfg<4, 4, 8, 1, 64, -2, 4>;
 using DwTallKMG = DwsepCfg<2, 4, 8, 1, 64, -2, 4>;
 using DwTallKSG = DwsepCfg<1, 4, 8, 1, 64, -2, 4>;
+// Stride 3: the staged rows (four 64-step runs) leave LDS for one workgroup
+// per CU, so the 512-row instances may take 256 VGPRs (2 waves per SIMD).
+using DwTall9W = DwsepCfg<4, 4, 8, 1, 64, 9, 2>;
+using DwTallKW = DwsepCfg<4, 4, 8, 1, 64, 0, 2>;
 
 template <class Cfg, int ST>
 static constexpr size_t tall_lds_bytes(int K) {
@@ -910,7 +921,9 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 // runtime-K (512 rows), 7/8 = the same with 256 rows, 9/10 with 128 rows,
 // 11/12/13 = dilation 2, 4 or 8 with 512, 256 or 128 rows, 14..19 = 5..10
 // with stride 2, 20/21 and 22/23 = K=9 / runtime-K with 64 and 32 rows,
-// 24/25/26 = other dilations with 512, 256 or 128 rows.
+// 24/25/26 = other dilations with 512, 256 or 128 rows, 27..32 = 5..10 with
+// stride 3 (the 512-row ones with the 256-VGPR budget), 33..38 = the same
+// with stride 4.
 // The tall tile takes any C and any 4-byte aligned w_pw.
 static int pick_dw(const DwsepShape& s) {
     const bool unit = s.stride == 1 && s.dil == 1;
@@ -935,6 +948,13 @@ static int pick_dw(const DwsepShape& s) {
         if (s.O > 256) return s.K == 9 ? 14 : 15;
         if (s.O > 128) return s.K == 9 ? 16 : 17;
         return s.K == 9 ? 18 : 19;
+    }
+    // stride 3 or 4 (four or five staged runs, one workgroup per CU)
+    if ((s.stride == 3 || s.stride == 4) && s.dil == 1 && s.K <= 64 && tall_tiles_fit(s)) {
+        const int base = s.stride == 3 ? 27 : 33;
+        if (s.O > 256) return base + (s.K == 9 ? 0 : 1);
+        if (s.O > 128) return base + (s.K == 9 ? 2 : 3);
+        return base + (s.K == 9 ? 4 : 5);
     }
 #endif
     if (s.O > 64) {
@@ -979,6 +999,18 @@ hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, 
         case 24: return launch_tall<DwTallKG>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 25: return launch_tall<DwTallKMG>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 26: return launch_tall<DwTallKSG>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 27: return launch_tall<DwTall9W, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 28: return launch_tall<DwTallKW, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 29: return launch_tall<DwTall9M, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 30: return launch_tall<DwTallKM, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 31: return launch_tall<DwTall9S, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 32: return launch_tall<DwTallKS, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 33: return launch_tall<DwTall9W, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 34: return launch_tall<DwTallKW, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 35: return launch_tall<DwTall9M, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 36: return launch_tall<DwTallKM, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 37: return launch_tall<DwTall9S, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 38: return launch_tall<DwTallKS, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

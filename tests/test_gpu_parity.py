@@ -711,6 +711,17 @@ STRIDED_DW = [
     (1, 30, 120, 100, 4, 10, 1, 21),   # dilation 21, (K - 1) * dil = 63, 128 rows
     (1, 33, 100, 129, 7, 18, 1, 6),    # dilation 6, 256 rows with one valid row in the fifth wave
     (1, 40, 140, 300, 23, 33, 1, 3),   # (K - 1) * dil = 66: past the tall tile, the 256-row kernel
+    # stride 3: four staged runs per row, one workgroup per CU
+    (2, 36, 400, 300, 9, 4, 3, 1),     # K = 9, 512 rows, a ragged last time tile
+    (1, 35, 257, 200, 5, 2, 3, 1),     # runtime K, 256 rows, C % 4 != 0
+    (1, 68, 300, 100, 64, 32, 3, 1),   # the widest window it stages, 128 rows, chunks of 64 + 4
+    (1, 40, 300, 520, 65, 32, 3, 1),   # one wider: the 256-row kernel
+    (1, 16, 200, 40, 9, 4, 3, 1),      # O = 40 on the 128-row tile
+    # stride 4: five staged runs per row
+    (2, 36, 520, 300, 9, 4, 4, 1),     # K = 9, 512 rows, a ragged last time tile
+    (1, 33, 300, 256, 7, 3, 4, 1),     # runtime K, 256 rows exactly, C % 4 != 0
+    (1, 64, 400, 65, 64, 32, 4, 1),    # the widest window it stages, 128 rows with one valid row in the 5th wave
+    (1, 24, 400, 300, 65, 32, 4, 1),   # one wider: the 256-row kernel
     # O <= 64 with a dilation or stride 2: the 128-row tile, its waves past O idle
     (2, 36, 130, 40, 9, 8, 1, 2),      # dilation 2, O = 40
     (1, 35, 131, 64, 5, 2, 2, 1),      # stride 2, O = 64, runtime K, C % 4 != 0
