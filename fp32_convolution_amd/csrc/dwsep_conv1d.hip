@@ -333,7 +333,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     constexpr int OB = Cfg::OB, TB = Cfg::TB, CC = Cfg::CC, CCP = Cfg::CCP, CPW = Cfg::CPW;
     using G = TallGeom<Cfg, ST>;
     constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = G::XP, OP = G::OP, DSF = G::DSF, NRUN = G::NRUN;
-    static_assert(ST == 1 || Cfg::KC >= 0, "strides above 1 with dilation 1");
+    static_assert(ST == 1 || Cfg::KC >= 0 || ST == 2, "a dilation with strides 1 and 2 only");
     static_assert(Cfg::KC >= -2, "KC: 9, 0, -1 or -2");
     static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && (OB == 4 || OB == 2 || OB == 1) && TB == 4,
                   "waves of 16 OB x 64 along o");
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
             // taps (KC = 0: dilation 1; KC = -1: dilation 2, 4 or 8, a
             // compile-time copy each, in instances of their own so that the
             // undilated ones keep their registers; KC = -2: any other
-            // dilation, tap by tap, stride 1); block kb reads NX staged
+            // dilation, tap by tap); block kb reads NX staged
             // steps from 8*ST*dj + kb*dil (16-byte aligned: kb*dil is a
             // multiple of 8), tap kb + kk at step ST*i + kk*dil of them, and
             // (K - 1) * dil <= 63 keeps them inside the row's 64 * NRUN staged
@@ -520,14 +520,14 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
                 }
             };
             if constexpr (Cfg::KC == -2) {
-                // any other dilation: tap k reads the 8 steps from 8*dj + k*dil
-                // one word at a time (paired reads; the start is not 16-byte
-                // aligned), the same chains
+                // any other dilation: tap k reads the 8 steps ST apart from
+                // 8*ST*dj + k*dil one word at a time (paired reads; the start
+                // is not 16-byte aligned), the same chains
                 for (int k = 0; k < K; ++k) {
                     const float wk = ws[c * K + k];
-                    const float* xr = xs + c * XP + 8 * dj + k * dil;
+                    const float* xr = xs + c * XP + 8 * ST * dj + k * dil;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) sacc[i] += wk * xr[i];
+                    for (int i = 0; i < 8; ++i) sacc[i] += wk * xr[ST * i];
                 }
             } else if constexpr (Cfg::KC < 0) {
                 if (dil == 2)
@@ -923,7 +923,7 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 // with stride 2, 20/21 and 22/23 = K=9 / runtime-K with 64 and 32 rows,
 // 24/25/26 = other dilations with 512, 256 or 128 rows, 27..32 = 5..10 with
 // stride 3 (the 512-row ones with the 256-VGPR budget), 33..38 = the same
-// with stride 4.
+// with stride 4, 39..41 and 42..44 = 11..13 and 24..26 with stride 2.
 // The tall tile takes any C and any 4-byte aligned w_pw.
 static int pick_dw(const DwsepShape& s) {
     const bool unit = s.stride == 1 && s.dil == 1;
@@ -943,7 +943,12 @@ static int pick_dw(const DwsepShape& s) {
         if (s.O > 32) return s.K == 9 ? 20 : 21;
         return s.K == 9 ? 22 : 23;
     }
-    // and stride 2 with dilation 1, K <= 64 (three staged runs per row)
+    // and stride 2, K <= 64 (three staged runs per row), with a dilation
+    // while (K - 1) * dil <= 63
+    if (s.stride == 2 && s.dil > 1 && (int64_t)(s.K - 1) * s.dil <= 63 && tall_tiles_fit(s)) {
+        const int base = pow2_dil ? 39 : 42;
+        return base + (s.O > 256 ? 0 : s.O > 128 ? 1 : 2);
+    }
     if (s.stride == 2 && s.dil == 1 && s.K <= 64 && tall_tiles_fit(s)) {
         if (s.O > 256) return s.K == 9 ? 14 : 15;
         if (s.O > 128) return s.K == 9 ? 16 : 17;
@@ -1011,6 +1016,12 @@ hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, 
         case 36: return launch_tall<DwTallKM, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 37: return launch_tall<DwTall9S, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 38: return launch_tall<DwTallKS, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 39: return launch_tall<DwTallKD, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 40: return launch_tall<DwTallKMD, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 41: return launch_tall<DwTallKSD, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 42: return launch_tall<DwTallKG, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 43: return launch_tall<DwTallKMG, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 44: return launch_tall<DwTallKSG, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -717,6 +717,13 @@ STRIDED_DW = [
     (1, 68, 300, 100, 64, 32, 3, 1),   # the widest window it stages, 128 rows, chunks of 64 + 4
     (1, 40, 300, 520, 65, 32, 3, 1),   # one wider: the 256-row kernel
     (1, 16, 200, 40, 9, 4, 3, 1),      # O = 40 on the 128-row tile
+    # stride 2 with a dilation: the dilated stages on three staged runs
+    (2, 36, 300, 300, 9, 8, 2, 2),     # dilation 2, K = 9, 512 rows, a ragged last time tile
+    (1, 35, 260, 200, 16, 30, 2, 4),   # dilation 4, (K - 1) * dil = 60, 256 rows, C % 4 != 0
+    (1, 64, 200, 100, 8, 28, 2, 8),    # dilation 8, one tap per block, 128 rows
+    (1, 40, 300, 300, 22, 31, 2, 3),   # dilation 3, (K - 1) * dil = 63, tap by tap
+    (2, 20, 180, 40, 7, 15, 2, 5),     # dilation 5, O = 40 on the 128-row tile
+    (1, 24, 300, 300, 17, 32, 2, 4),   # (K - 1) * dil = 64: past the tall tile, the 256-row kernel
     # stride 4: five staged runs per row
     (2, 36, 520, 300, 9, 4, 4, 1),     # K = 9, 512 rows, a ragged last time tile
     (1, 33, 300, 256, 7, 3, 4, 1),     # runtime K, 256 rows exactly, C % 4 != 0
