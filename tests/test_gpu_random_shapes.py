@@ -3,7 +3,7 @@ Conv2d chain and every dwsep algorithm, against the CPU oracle.
 
 The fixed cases elsewhere pin each kernel instance at chosen edges; these
 draw (B, Cin, H, W, Cout, K, s, pool form, algorithm) and (B, C, T, O, K,
-pad, stride, dilation, algorithm) from one seeded generator, so shapes no
+pad, stride, dilation, algorithm) from seeded generators, so shapes no
 one picked (odd channel counts, maps of one pooled row, tiles cut anywhere,
 empty pooled maps) meet the same bar: |gpu - oracle| <= 1e-4 + 1e-4*|oracle|
 on the pooled map, the fused sums and y.  A combination with no kernel must
@@ -95,8 +95,26 @@ def dw_cases(n, seed):
     return cases
 
 
+def dw_cases_wide(n, seed):
+    # strides 1 to 5 and dilations 1 to 5 in every combination, windows up to past 64 steps: the tall
+    # tile's stride and dilation instances and their handover to the 256-row kernel
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        stride = int(rng.integers(1, 6))
+        dil = int(rng.integers(1, 6))
+        K = int(rng.integers(1, 80 // dil + 2))
+        pad = int(rng.integers(0, (K - 1) * dil // 2 + 2))
+        T = int(rng.integers(1, 400))
+        if oracle.dwsep_tout(T, K, pad, stride, dil) < 1:
+            continue
+        cases.append(dict(B=int(rng.integers(1, 3)), C=int(rng.integers(1, 130)), T=T,
+                          O=int(rng.integers(1, 601)), K=K, pad=pad, stride=stride, dil=dil, algo=0))
+    return cases
+
+
 CONV_CASES = conv_cases(160, seed=2024)
-DW_CASES = dw_cases(120, seed=2025)
+DW_CASES = dw_cases(120, seed=2025) + dw_cases_wide(80, seed=2026)
 
 
 def conv_id(c):
