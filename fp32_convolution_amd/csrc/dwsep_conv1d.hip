@@ -333,7 +333,6 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     constexpr int OB = Cfg::OB, TB = Cfg::TB, CC = Cfg::CC, CCP = Cfg::CCP, CPW = Cfg::CPW;
     using G = TallGeom<Cfg, ST>;
     constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = G::XP, OP = G::OP, DSF = G::DSF, NRUN = G::NRUN;
-    static_assert(ST == 1 || Cfg::KC >= 0 || ST == 2, "a dilation with strides 1 and 2 only");
     static_assert(Cfg::KC >= -2, "KC: 9, 0, -1 or -2");
     static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && (OB == 4 || OB == 2 || OB == 1) && TB == 4,
                   "waves of 16 OB x 64 along o");
@@ -673,10 +672,13 @@ using DwTallKSD = DwsepCfg<1, 4, 8, 1, 64, -1, 4>;
 using DwTallKG = DwsepCfg<4, 4, 8, 1, 64, -2, 4>;
 using DwTallKMG = DwsepCfg<2, 4, 8, 1, 64, -2, 4>;
 using DwTallKSG = DwsepCfg<1, 4, 8, 1, 64, -2, 4>;
-// Stride 3: the staged rows (four 64-step runs) leave LDS for one workgroup
-// per CU, so the 512-row instances may take 256 VGPRs (2 waves per SIMD).
+// Strides 3 and 4: the staged rows (four or five 64-step runs) leave LDS for
+// one workgroup per CU, so the 512-row instances may take 256 VGPRs (2 waves
+// per SIMD).
 using DwTall9W = DwsepCfg<4, 4, 8, 1, 64, 9, 2>;
 using DwTallKW = DwsepCfg<4, 4, 8, 1, 64, 0, 2>;
+using DwTallKDW = DwsepCfg<4, 4, 8, 1, 64, -1, 2>;
+using DwTallKGW = DwsepCfg<4, 4, 8, 1, 64, -2, 2>;
 
 template <class Cfg, int ST>
 static constexpr size_t tall_lds_bytes(int K) {
@@ -923,7 +925,9 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 // with stride 2, 20/21 and 22/23 = K=9 / runtime-K with 64 and 32 rows,
 // 24/25/26 = other dilations with 512, 256 or 128 rows, 27..32 = 5..10 with
 // stride 3 (the 512-row ones with the 256-VGPR budget), 33..38 = the same
-// with stride 4, 39..41 and 42..44 = 11..13 and 24..26 with stride 2.
+// with stride 4, 39..41 and 42..44 = 11..13 and 24..26 with stride 2,
+// 45..50 and 51..56 = the same with stride 3 and 4 (512 rows: 256-VGPR
+// budget).
 // The tall tile takes any C and any 4-byte aligned w_pw.
 static int pick_dw(const DwsepShape& s) {
     const bool unit = s.stride == 1 && s.dil == 1;
@@ -955,6 +959,10 @@ static int pick_dw(const DwsepShape& s) {
         return s.K == 9 ? 18 : 19;
     }
     // stride 3 or 4 (four or five staged runs, one workgroup per CU)
+    if ((s.stride == 3 || s.stride == 4) && s.dil > 1 && (int64_t)(s.K - 1) * s.dil <= 63 && tall_tiles_fit(s)) {
+        const int base = 45 + (s.stride == 4 ? 6 : 0) + (pow2_dil ? 0 : 3);
+        return base + (s.O > 256 ? 0 : s.O > 128 ? 1 : 2);
+    }
     if ((s.stride == 3 || s.stride == 4) && s.dil == 1 && s.K <= 64 && tall_tiles_fit(s)) {
         const int base = s.stride == 3 ? 27 : 33;
         if (s.O > 256) return base + (s.K == 9 ? 0 : 1);
@@ -1022,6 +1030,18 @@ hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, 
         case 42: return launch_tall<DwTallKG, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 43: return launch_tall<DwTallKMG, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 44: return launch_tall<DwTallKSG, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 45: return launch_tall<DwTallKDW, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 46: return launch_tall<DwTallKMD, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 47: return launch_tall<DwTallKSD, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 48: return launch_tall<DwTallKGW, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 49: return launch_tall<DwTallKMG, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 50: return launch_tall<DwTallKSG, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 51: return launch_tall<DwTallKDW, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 52: return launch_tall<DwTallKMD, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 53: return launch_tall<DwTallKSD, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 54: return launch_tall<DwTallKGW, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 55: return launch_tall<DwTallKMG, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 56: return launch_tall<DwTallKSG, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

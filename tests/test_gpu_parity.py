@@ -694,7 +694,7 @@ STRIDED_DW = [
     # B, C, T, O, K, pad, stride, dilation
     (2, 64, 300, 300, 9, 4, 2, 1),     # stride 2: the tall tile's stride-2 K = 9 instance, 512 rows
     (1, 48, 257, 512, 9, 8, 1, 2),     # dilation 2: the tall tile's dilated instance, 512 rows
-    (2, 20, 100, 40, 5, 3, 3, 2),      # small instance
+    (2, 20, 100, 40, 5, 3, 3, 2),      # stride 3, dilation 2, O = 40: the 128-row tile
     (1, 16, 2000, 128, 9, 4, 16, 1),   # window too wide for 64 steps: narrow instance
     (1, 32, 40, 64, 3, 0, 5, 4),       # few output steps
     # the tall tile's dilated instances: dilation 2, 4 and 8 on 512-, 256- and 128-row tiles, up to the
@@ -724,6 +724,12 @@ STRIDED_DW = [
     (1, 40, 300, 300, 22, 31, 2, 3),   # dilation 3, (K - 1) * dil = 63, tap by tap
     (2, 20, 180, 40, 7, 15, 2, 5),     # dilation 5, O = 40 on the 128-row tile
     (1, 24, 300, 300, 17, 32, 2, 4),   # (K - 1) * dil = 64: past the tall tile, the 256-row kernel
+    # strides 3 and 4 with a dilation
+    (2, 36, 500, 300, 9, 8, 3, 2),     # stride 3, dilation 2, 512 rows (256-VGPR budget)
+    (1, 35, 400, 200, 10, 27, 3, 7),   # stride 3, dilation 7, (K - 1) * dil = 63, tap by tap, 256 rows
+    (1, 64, 600, 300, 8, 28, 4, 8),    # stride 4, dilation 8, one tap per block, 512 rows
+    (1, 30, 500, 100, 22, 31, 4, 3),   # stride 4, dilation 3, (K - 1) * dil = 63, 128 rows
+    (1, 24, 500, 300, 17, 32, 3, 4),   # (K - 1) * dil = 64: past the tall tile, the 256-row kernel
     # stride 4: five staged runs per row
     (2, 36, 520, 300, 9, 4, 4, 1),     # K = 9, 512 rows, a ragged last time tile
     (1, 33, 300, 256, 7, 3, 4, 1),     # runtime K, 256 rows exactly, C % 4 != 0
