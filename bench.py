@@ -58,7 +58,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3, false>, 2, 2, 2, false>": [
         "fp32_convolution_amd/csrc/conv2d_pool_ex.hip", "fp32_convolution_amd/csrc/fconv_device.hpp"],
-    "dwsep_tall_kernel<fconv::DwsepCfg<4, 4, 8, 1, 64, 9, 4>, 1>": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
+    "dwsep_tall_kernel<fconv::DwsepCfg<4, 4, 8, 1, 64, 9, 4>, 1, 0>": ["fp32_convolution_amd/csrc/dwsep_conv1d.hip",
                                                                     "fp32_convolution_amd/csrc/fconv_device.hpp"],
     "conv2d_pool_boxsum4_kernel<2, true, 2, false>": ["fp32_convolution_amd/csrc/conv2d_pool.hip",
                                                       "fp32_convolution_amd/csrc/fconv_device.hpp"],
@@ -75,7 +75,7 @@ KERNEL_SOURCES = {
 
 ELEM_AVG = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 3, false>, 2, 2, 2, false>"
 # the separable dwsep kernel of the step: the 512 x 64 tile, K = 9, stride 1
-DW_TALL = "dwsep_tall_kernel<fconv::DwsepCfg<4, 4, 8, 1, 64, 9, 4>, 1>"
+DW_TALL = "dwsep_tall_kernel<fconv::DwsepCfg<4, 4, 8, 1, 64, 9, 4>, 1, 0>"
 ELEM_MAX = "conv2d_pool_elem_kernel<fconv::ElemCfg<3, 4, 4, 4, false>, 1, 2, 2, false>"
 TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace.json")
 

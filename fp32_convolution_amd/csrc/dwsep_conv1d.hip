@@ -314,25 +314,27 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 // larger strides the wider xs rows leave no room for it, so the epilogue stages
 // through xs and Ds together (both free by then: the last chunk stages no
 // next chunk) and the region after xs is Ds alone.
-template <class Cfg, int ST>
+// WX = 1 stages one more run per row, for windows of 65 to 128 steps.
+template <class Cfg, int ST, int WX>
 struct TallGeom {
-    static constexpr int NRUN = ST + 1 > 2 ? ST + 1 : 2;
+    static constexpr int NRUN = (ST + 1 > 2 ? ST + 1 : 2) + WX;
     static constexpr int XP = 64 * NRUN + 4;
     static constexpr int OP = 68;
     static constexpr int EPI = Cfg::NW * 16 * OP;
     static constexpr int DS = Cfg::TT * Cfg::CCP;
-    static constexpr int DSF = ST == 1 ? (DS > EPI ? DS : EPI) : DS;
-    static_assert(ST == 1 || Cfg::CC * XP + DS >= EPI, "the epilogue fits xs + Ds");
+    static constexpr int DSF = NRUN == 2 ? (DS > EPI ? DS : EPI) : DS;
+    static_assert(NRUN == 2 || Cfg::CC * XP + DS >= EPI, "the epilogue fits xs + Ds");
 };
 
-template <class Cfg, int ST>
+template <class Cfg, int ST, int WX>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     const float* __restrict__ x, const float* __restrict__ w_dw, const float* __restrict__ w_pw,
     const float* __restrict__ b_pw, float* __restrict__ y, int C, int T, int Kr, int O, int pad, int Tout, int n_tt,
     int n_ot, int vec_out, int dil) {
     constexpr int OB = Cfg::OB, TB = Cfg::TB, CC = Cfg::CC, CCP = Cfg::CCP, CPW = Cfg::CPW;
-    using G = TallGeom<Cfg, ST>;
+    using G = TallGeom<Cfg, ST, WX>;
     constexpr int TT = Cfg::TT, NW = Cfg::NW, XP = G::XP, OP = G::OP, DSF = G::DSF, NRUN = G::NRUN;
+    static_assert(WX == 0 || (ST == 1 && Cfg::KC <= 0), "wide windows: stride 1, runtime K");
     static_assert(Cfg::KC >= -2, "KC: 9, 0, -1 or -2");
     static_assert(Cfg::WT == 1 && TT == 64 && Cfg::WO == NW && (OB == 4 || OB == 2 || OB == 1) && TB == 4,
                   "waves of 16 OB x 64 along o");
@@ -487,8 +489,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
             // dilation, tap by tap); block kb reads NX staged
             // steps from 8*ST*dj + kb*dil (16-byte aligned: kb*dil is a
             // multiple of 8), tap kb + kk at step ST*i + kk*dil of them, and
-            // (K - 1) * dil <= 63 keeps them inside the row's 64 * NRUN staged
-            // steps
+            // (K - 1) * dil <= 63 (127 with WX = 1) keeps them inside the
+            // row's 64 * NRUN staged steps
             static_assert(CPW == 8, "8 channels x 8 groups of 8 steps per wave");
             const int dj = lane & 7, dc = lane >> 3;
             const int c = wave * CPW + dc;
@@ -615,7 +617,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     float* yb = y + (size_t)bi * O * Tout;
     __syncthreads();  // every wave is done reading Ds (outside the branch: o0 differs per wave)
     if (vec_out && o0 + 16 * OB <= O && t0 + TT <= Tout) {
-        float* ow = (ST == 1 ? Ds : lds) + wave * 16 * OP;  // see TallGeom
+        float* ow = (NRUN == 2 ? Ds : lds) + wave * 16 * OP;  // see TallGeom
 #pragma unroll
         for (int ob = 0; ob < OB; ++ob) {
 #pragma unroll
@@ -680,9 +682,9 @@ using DwTallKW = DwsepCfg<4, 4, 8, 1, 64, 0, 2>;
 using DwTallKDW = DwsepCfg<4, 4, 8, 1, 64, -1, 2>;
 using DwTallKGW = DwsepCfg<4, 4, 8, 1, 64, -2, 2>;
 
-template <class Cfg, int ST>
+template <class Cfg, int ST, int WX>
 static constexpr size_t tall_lds_bytes(int K) {
-    using G = TallGeom<Cfg, ST>;
+    using G = TallGeom<Cfg, ST, WX>;
     return ((size_t)Cfg::CC * G::XP + G::DSF + (size_t)Cfg::NW * 64 + (size_t)(K * Cfg::CC + 63) / 64 * 64) *
            sizeof(float);
 }
@@ -903,17 +905,17 @@ static bool tall_tiles_fit(const DwsepShape& s) {
     return n <= 0x7fffffffL;
 }
 
-template <class Cfg, int ST = 1>
+template <class Cfg, int ST = 1, int WX = 0>
 static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                               const float* b_pw, float* y, hipStream_t stream) {
-    const size_t lds = tall_lds_bytes<Cfg, ST>(s.K);
-    hipError_t e = hipFuncSetAttribute((const void*)dwsep_tall_kernel<Cfg, ST>,
+    const size_t lds = tall_lds_bytes<Cfg, ST, WX>(s.K);
+    hipError_t e = hipFuncSetAttribute((const void*)dwsep_tall_kernel<Cfg, ST, WX>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int n_tt = (s.Tout + Cfg::TT - 1) / Cfg::TT, n_ot = (s.O + Cfg::OT - 1) / Cfg::OT;
     const int n_tiles = n_tt * n_ot * s.B;  // < 2^31: checked by tall_tiles_fit
     const int vec_out = (s.Tout % 4 == 0) && ((uintptr_t)y % 16 == 0);
-    hipLaunchKernelGGL((dwsep_tall_kernel<Cfg, ST>), dim3(n_tiles), dim3(Cfg::NT), lds, stream, x, w_dw, w_pw, b_pw,
+    hipLaunchKernelGGL((dwsep_tall_kernel<Cfg, ST, WX>), dim3(n_tiles), dim3(Cfg::NT), lds, stream, x, w_dw, w_pw, b_pw,
                        y, s.C, s.T, s.K, s.O, s.pad, s.Tout, n_tt, n_ot, vec_out, s.dil);
     return hipGetLastError();
 }
@@ -927,7 +929,8 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 // stride 3 (the 512-row ones with the 256-VGPR budget), 33..38 = the same
 // with stride 4, 39..41 and 42..44 = 11..13 and 24..26 with stride 2,
 // 45..50 and 51..56 = the same with stride 3 and 4 (512 rows: 256-VGPR
-// budget).
+// budget), 57..65 = 6/8/10, 11..13 and 24..26 at stride 1 with a window of
+// 65 to 128 steps (one more staged run).
 // The tall tile takes any C and any 4-byte aligned w_pw.
 static int pick_dw(const DwsepShape& s) {
     const bool unit = s.stride == 1 && s.dil == 1;
@@ -957,6 +960,11 @@ static int pick_dw(const DwsepShape& s) {
         if (s.O > 256) return s.K == 9 ? 14 : 15;
         if (s.O > 128) return s.K == 9 ? 16 : 17;
         return s.K == 9 ? 18 : 19;
+    }
+    // stride 1 with a window of 65 to 128 steps: one more staged run per row
+    if (s.stride == 1 && (int64_t)(s.K - 1) * s.dil <= 127 && tall_tiles_fit(s)) {
+        const int base = s.dil == 1 ? 57 : pow2_dil ? 60 : 63;
+        return base + (s.O > 256 ? 0 : s.O > 128 ? 1 : 2);
     }
     // stride 3 or 4 (four or five staged runs, one workgroup per CU)
     if ((s.stride == 3 || s.stride == 4) && s.dil > 1 && (int64_t)(s.K - 1) * s.dil <= 63 && tall_tiles_fit(s)) {
@@ -1042,6 +1050,15 @@ hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, 
         case 54: return launch_tall<DwTallKGW, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 55: return launch_tall<DwTallKMG, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 56: return launch_tall<DwTallKSG, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 57: return launch_tall<DwTallK, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 58: return launch_tall<DwTallKM, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 59: return launch_tall<DwTallKS, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 60: return launch_tall<DwTallKD, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 61: return launch_tall<DwTallKMD, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 62: return launch_tall<DwTallKSD, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 63: return launch_tall<DwTallKG, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 64: return launch_tall<DwTallKMG, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 65: return launch_tall<DwTallKSG, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -579,7 +579,10 @@ TALL_DW = [
     (2, 200, 130, 520, 9, 4),    # 3 full chunks + an 8-channel chunk (half a group), 2 output tiles
     (1, 68, 64, 257, 33, 16),    # runtime K, a 4-channel last chunk, one valid row in the 2nd block
     (1, 64, 100, 300, 64, 32),   # the widest window the tile takes (K = 64: 8 full blocks of 8 taps)
-    (1, 64, 100, 300, 65, 32),   # one wider: the 256-row runtime-K kernel
+    (1, 64, 100, 300, 65, 32),   # one wider: the wide-window instance (three staged runs per row)
+    (1, 36, 300, 300, 128, 64),  # the widest window the wide-window instance stages
+    (1, 36, 300, 200, 129, 64),  # one wider: the 256-row runtime-K kernel
+    (2, 35, 200, 100, 100, 50),  # wide window, 128 rows, C % 4 != 0
     (2, 36, 130, 512, 5, 2),     # runtime K inside one block of 8 taps
     (1, 40, 96, 300, 8, 3),      # exactly one block, even K (asymmetric padding)
     (1, 24, 80, 384, 17, 8),     # a last block with one tap
@@ -646,12 +649,12 @@ def test_dwsep_tall_tile(fc, shape):
 @pytest.mark.parametrize("O", [300, 200, 100, 48, 20])
 def test_dwsep_tall_tile_every_k(fc, O):
     # every depthwise width the tall tile takes (K = 1 .. 64; K = 9 is its compiled instance, the rest run
-    # the runtime-K stage over blocks of 8 taps), with odd and even padding and a partial channel chunk,
-    # against the oracle, for its 512-, 256-, 128-, 64- and 32-row tiles; K = 65 goes to the older
-    # kernels and is checked the same way
-    announce(f"dwsep tall tile, K = 1 .. 65, O = {O}")
+    # the runtime-K stage over blocks of 8 taps; K = 65 .. 128 the wide-window instances with one more
+    # staged run), with odd and even padding and a partial channel chunk, against the oracle, for its
+    # 512-, 256-, 128-, 64- and 32-row tiles; K = 129 goes to the older kernels and is checked the same way
+    announce(f"dwsep tall tile, K = 1 .. 129, O = {O}")
     B, C, T = 1, 36, 100
-    for K in range(1, 66):
+    for K in range(1, 130):
         pad = K // 2 if K % 3 else (K - 1) // 2
         x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=300 + K)
         want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad)
@@ -661,11 +664,11 @@ def test_dwsep_tall_tile_every_k(fc, O):
 
 @pytest.mark.parametrize("dil", [3, 5, 6])
 def test_dwsep_tall_tile_any_dilation_every_k(fc, dil):
-    # every K the tall tile's tap-by-tap instance takes at this dilation ((K - 1) * dil <= 63), and the
-    # first K past it, with odd and even padding, against the oracle
+    # every K the tall tile's tap-by-tap instances take at this dilation ((K - 1) * dil <= 63, and up to
+    # 127 with one more staged run), and the first K past them, with odd and even padding, against the oracle
     announce(f"dwsep tall tile, dilation {dil}, every K")
     B, C, T, O = 1, 36, 100, 300
-    for K in range(1, 63 // dil + 3):
+    for K in range(1, 127 // dil + 3):
         pad = (K - 1) * dil // 2 if K % 2 else (K - 2) * dil // 2
         x, w_dw, w_pw, b_pw = fi.dwsep_inputs(B, C, T, O, K, seed=400 + K)
         want = oracle.dwsep_conv1d(x, w_dw, w_pw, b_pw, pad, dilation=dil)
@@ -703,14 +706,16 @@ STRIDED_DW = [
     (1, 64, 130, 200, 8, 28, 1, 8),    # dilation 8, one tap per block, 256 rows
     (1, 100, 120, 100, 32, 31, 1, 2),  # dilation 2, (K - 1) * dil = 62, 128 rows, chunks of 64 + 36
     (1, 40, 140, 300, 16, 30, 1, 4),   # dilation 4, (K - 1) * dil = 60
-    (1, 40, 140, 300, 17, 32, 1, 4),   # (K - 1) * dil = 64: past the tall tile, the 256-row kernel
+    (1, 40, 140, 300, 17, 32, 1, 4),   # (K - 1) * dil = 64: the wide-window instance
     # any other dilation: the tall tile's tap-by-tap instances
     (1, 32, 90, 300, 9, 12, 1, 3),     # dilation 3, 512 rows
     (2, 35, 150, 300, 5, 6, 1, 3),     # dilation 3, a ragged time tile, C % 4 != 0
     (1, 68, 140, 200, 10, 27, 1, 7),   # dilation 7, (K - 1) * dil = 63, 256 rows
     (1, 30, 120, 100, 4, 10, 1, 21),   # dilation 21, (K - 1) * dil = 63, 128 rows
     (1, 33, 100, 129, 7, 18, 1, 6),    # dilation 6, 256 rows with one valid row in the fifth wave
-    (1, 40, 140, 300, 23, 33, 1, 3),   # (K - 1) * dil = 66: past the tall tile, the 256-row kernel
+    (1, 40, 140, 300, 23, 33, 1, 3),   # (K - 1) * dil = 66: the wide-window instance, tap by tap
+    (1, 36, 300, 200, 43, 63, 1, 3),   # (K - 1) * dil = 126, 256 rows
+    (1, 36, 300, 100, 17, 64, 1, 8),   # (K - 1) * dil = 128: past the wide window, the 256-row kernel
     # stride 3: four staged runs per row, one workgroup per CU
     (2, 36, 400, 300, 9, 4, 3, 1),     # K = 9, 512 rows, a ragged last time tile
     (1, 35, 257, 200, 5, 2, 3, 1),     # runtime K, 256 rows, C % 4 != 0
