@@ -649,38 +649,22 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
     }
 }
 
-#ifndef FCONV_CFG_TALL
-#define FCONV_CFG_TALL 4, 4, 8, 1, 64, 9, 4
-#endif
-using DwTall9 = DwsepCfg<FCONV_CFG_TALL>;
-using DwTallK = DwsepCfg<4, 4, 8, 1, 64, 0, 4>;
-// The same tile for 64 < O <= 256: waves of 32 x 64 (256 rows) or 16 x 64
-// (128 rows), so no wave computes rows past O.
-using DwTall9M = DwsepCfg<2, 4, 8, 1, 64, 9, 4>;
-using DwTallKM = DwsepCfg<2, 4, 8, 1, 64, 0, 4>;
-using DwTall9S = DwsepCfg<1, 4, 8, 1, 64, 9, 4>;
-using DwTallKS = DwsepCfg<1, 4, 8, 1, 64, 0, 4>;
-// O <= 64: 64 rows as 4 waves of 16 x 64 (32-channel chunks), O <= 32: 32 rows
-// as 2 waves (16-channel chunks), so each wave still makes the depthwise
-// values of 8 channels.
-using DwTall9Q = DwsepCfg<1, 4, 4, 1, 32, 9, 4>;
-using DwTallKQ = DwsepCfg<1, 4, 4, 1, 32, 0, 4>;
-using DwTall9E = DwsepCfg<1, 4, 2, 1, 16, 9, 4>;
-using DwTallKE = DwsepCfg<1, 4, 2, 1, 16, 0, 4>;
-// Dilation 2, 4 or 8 (KC = -1: runtime K), and any other dilation (KC = -2).
-using DwTallKD = DwsepCfg<4, 4, 8, 1, 64, -1, 4>;
-using DwTallKMD = DwsepCfg<2, 4, 8, 1, 64, -1, 4>;
-using DwTallKSD = DwsepCfg<1, 4, 8, 1, 64, -1, 4>;
-using DwTallKG = DwsepCfg<4, 4, 8, 1, 64, -2, 4>;
-using DwTallKMG = DwsepCfg<2, 4, 8, 1, 64, -2, 4>;
-using DwTallKSG = DwsepCfg<1, 4, 8, 1, 64, -2, 4>;
-// Strides 3 and 4: the staged rows (four or five 64-step runs) leave LDS for
-// one workgroup per CU, so the 512-row instances may take 256 VGPRs (2 waves
-// per SIMD).
-using DwTall9W = DwsepCfg<4, 4, 8, 1, 64, 9, 2>;
-using DwTallKW = DwsepCfg<4, 4, 8, 1, 64, 0, 2>;
-using DwTallKDW = DwsepCfg<4, 4, 8, 1, 64, -1, 2>;
-using DwTallKGW = DwsepCfg<4, 4, 8, 1, 64, -2, 2>;
+// The tall tile's heights for one depthwise stage KC: 512 rows (8 waves of
+// 64 x 64) for O > 256; 256 rows (8 waves of 32 x 64) and 128 rows (16 x 64)
+// for 64 < O <= 256, so no wave computes rows past O; for O <= 64, 64 rows as
+// 4 waves of 16 x 64 (32-channel chunks) and 32 rows as 2 waves (16-channel
+// chunks), so each wave still makes the depthwise values of 8 channels.  M is
+// the 512-row tile's register budget in waves per SIMD: 2 at strides 3 and
+// 4, whose staged rows leave LDS for one workgroup per CU anyway (at 128
+// VGPRs those instances spilled 11-13 registers).
+template <int KC, int M>
+struct TallSet {
+    using H512 = DwsepCfg<4, 4, 8, 1, 64, KC, M>;
+    using H256 = DwsepCfg<2, 4, 8, 1, 64, KC, 4>;
+    using H128 = DwsepCfg<1, 4, 8, 1, 64, KC, 4>;
+    using H64 = DwsepCfg<1, 4, 4, 1, 32, KC, 4>;
+    using H32 = DwsepCfg<1, 4, 2, 1, 16, KC, 4>;
+};
 
 template <class Cfg, int ST, int WX>
 static constexpr size_t tall_lds_bytes(int K) {
@@ -900,7 +884,7 @@ static hipError_t launch_dw(const DwsepShape& s, const float* x, const float* w_
 
 // The tall kernel's 1-D grid holds every (time tile, output tile, item).
 static bool tall_tiles_fit(const DwsepShape& s) {
-    const int ot = DwTall9E::OT;  // the smallest tile height of the instances
+    const int ot = TallSet<9, 4>::H32::OT;  // the smallest tile height
     const long n = (long)((s.Tout + 63) / 64) * ((s.O + ot - 1) / ot) * s.B;
     return n <= 0x7fffffffL;
 }
@@ -920,64 +904,70 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
     return hipGetLastError();
 }
 
-// The instance a shape runs on: 0 = none fits, 1 = wide K=9, 2 = wide
-// runtime-K, 3 = narrow runtime-K, 4 = small runtime-K, 5/6 = tall K=9 /
-// runtime-K (512 rows), 7/8 = the same with 256 rows, 9/10 with 128 rows,
-// 11/12/13 = dilation 2, 4 or 8 with 512, 256 or 128 rows, 14..19 = 5..10
-// with stride 2, 20/21 and 22/23 = K=9 / runtime-K with 64 and 32 rows,
-// 24/25/26 = other dilations with 512, 256 or 128 rows, 27..32 = 5..10 with
-// stride 3 (the 512-row ones with the 256-VGPR budget), 33..38 = the same
-// with stride 4, 39..41 and 42..44 = 11..13 and 24..26 with stride 2,
-// 45..50 and 51..56 = the same with stride 3 and 4 (512 rows: 256-VGPR
-// budget), 57..65 = 6/8/10, 11..13 and 24..26 at stride 1 with a window of
-// 65 to 128 steps (one more staged run).
-// The tall tile takes any C and any 4-byte aligned w_pw.
-static int pick_dw(const DwsepShape& s) {
-    const bool unit = s.stride == 1 && s.dil == 1;
+// The tall tile's choice for a shape: its depthwise stage (9: K = 9
+// compiled, 0: runtime K, -1: dilation 2, 4 or 8, -2: any other dilation),
+// its stride (1 to 4) and its window class (wx = 1: one more staged run, for
+// windows of 65 to 128 steps at stride 1).  ok = false: no tall instance.
+struct TallPick {
+    bool ok;
+    int kc, st, wx;
+};
+
+static TallPick pick_tall(const DwsepShape& s) {
 #ifndef FCONV_DW_NO_TALL
-    // the tall tile: stride 1, a window of at most 64 steps.  With a dilation
-    // (and with stride 2, below) O <= 64 takes the 128-row tile, whose waves
-    // past O multiply zero weights: still far cheaper than the 32 x 32 tile,
-    // which remakes every depthwise value per 32 outputs and 32 steps.
-    const bool pow2_dil = s.dil == 2 || s.dil == 4 || s.dil == 8;
-    if (s.stride == 1 && (int64_t)(s.K - 1) * s.dil <= 63 && tall_tiles_fit(s)) {
-        if (pow2_dil) return s.O > 256 ? 11 : s.O > 128 ? 12 : 13;
-        if (s.dil > 1) return s.O > 256 ? 24 : s.O > 128 ? 25 : 26;
-        if (s.O > 256) return s.K == 9 ? 5 : 6;
-        if (s.O > 128) return s.K == 9 ? 7 : 8;
-        if (s.O > 64) return s.K == 9 ? 9 : 10;
-        // 64- or 32-row tiles
-        if (s.O > 32) return s.K == 9 ? 20 : 21;
-        return s.K == 9 ? 22 : 23;
-    }
-    // and stride 2, K <= 64 (three staged runs per row), with a dilation
-    // while (K - 1) * dil <= 63
-    if (s.stride == 2 && s.dil > 1 && (int64_t)(s.K - 1) * s.dil <= 63 && tall_tiles_fit(s)) {
-        const int base = pow2_dil ? 39 : 42;
-        return base + (s.O > 256 ? 0 : s.O > 128 ? 1 : 2);
-    }
-    if (s.stride == 2 && s.dil == 1 && s.K <= 64 && tall_tiles_fit(s)) {
-        if (s.O > 256) return s.K == 9 ? 14 : 15;
-        if (s.O > 128) return s.K == 9 ? 16 : 17;
-        return s.K == 9 ? 18 : 19;
-    }
-    // stride 1 with a window of 65 to 128 steps: one more staged run per row
-    if (s.stride == 1 && (int64_t)(s.K - 1) * s.dil <= 127 && tall_tiles_fit(s)) {
-        const int base = s.dil == 1 ? 57 : pow2_dil ? 60 : 63;
-        return base + (s.O > 256 ? 0 : s.O > 128 ? 1 : 2);
-    }
-    // stride 3 or 4 (four or five staged runs, one workgroup per CU)
-    if ((s.stride == 3 || s.stride == 4) && s.dil > 1 && (int64_t)(s.K - 1) * s.dil <= 63 && tall_tiles_fit(s)) {
-        const int base = 45 + (s.stride == 4 ? 6 : 0) + (pow2_dil ? 0 : 3);
-        return base + (s.O > 256 ? 0 : s.O > 128 ? 1 : 2);
-    }
-    if ((s.stride == 3 || s.stride == 4) && s.dil == 1 && s.K <= 64 && tall_tiles_fit(s)) {
-        const int base = s.stride == 3 ? 27 : 33;
-        if (s.O > 256) return base + (s.K == 9 ? 0 : 1);
-        if (s.O > 128) return base + (s.K == 9 ? 2 : 3);
-        return base + (s.K == 9 ? 4 : 5);
+    const int64_t win = (int64_t)(s.K - 1) * s.dil;
+    if (s.stride <= 4 && (win <= 63 || (win <= 127 && s.stride == 1)) && tall_tiles_fit(s)) {
+        const bool pow2 = s.dil == 2 || s.dil == 4 || s.dil == 8;
+        const int kc = s.dil == 1 ? (s.K == 9 ? 9 : 0) : pow2 ? -1 : -2;
+        return {true, kc, s.stride, win > 63 ? 1 : 0};
     }
 #endif
+    return {false, 0, 0, 0};
+}
+
+template <int KC, int ST, int WX = 0>
+static hipError_t launch_tall_o(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
+                                const float* b_pw, float* y, hipStream_t stream) {
+    using S = TallSet<KC, (ST >= 3 ? 2 : 4)>;
+    if (s.O > 256) return launch_tall<typename S::H512, ST, WX>(s, x, w_dw, w_pw, b_pw, y, stream);
+    if (s.O > 128) return launch_tall<typename S::H256, ST, WX>(s, x, w_dw, w_pw, b_pw, y, stream);
+    if (s.O > 64) return launch_tall<typename S::H128, ST, WX>(s, x, w_dw, w_pw, b_pw, y, stream);
+    if (s.O > 32) return launch_tall<typename S::H64, ST, WX>(s, x, w_dw, w_pw, b_pw, y, stream);
+    return launch_tall<typename S::H32, ST, WX>(s, x, w_dw, w_pw, b_pw, y, stream);
+}
+
+template <int ST>
+static hipError_t launch_tall_st(int kc, const DwsepShape& s, const float* x, const float* w_dw,
+                                 const float* w_pw, const float* b_pw, float* y, hipStream_t stream) {
+    switch (kc) {
+        case 9: return launch_tall_o<9, ST>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case 0: return launch_tall_o<0, ST>(s, x, w_dw, w_pw, b_pw, y, stream);
+        case -1: return launch_tall_o<-1, ST>(s, x, w_dw, w_pw, b_pw, y, stream);
+        default: return launch_tall_o<-2, ST>(s, x, w_dw, w_pw, b_pw, y, stream);
+    }
+}
+
+static hipError_t launch_tall_pick(const TallPick& t, const DwsepShape& s, const float* x, const float* w_dw,
+                                   const float* w_pw, const float* b_pw, float* y, hipStream_t stream) {
+    if (t.wx) {
+        switch (t.kc) {
+            case 0: return launch_tall_o<0, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+            case -1: return launch_tall_o<-1, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+            default: return launch_tall_o<-2, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
+        }
+    }
+    switch (t.st) {
+        case 1: return launch_tall_st<1>(t.kc, s, x, w_dw, w_pw, b_pw, y, stream);
+        case 2: return launch_tall_st<2>(t.kc, s, x, w_dw, w_pw, b_pw, y, stream);
+        case 3: return launch_tall_st<3>(t.kc, s, x, w_dw, w_pw, b_pw, y, stream);
+        default: return launch_tall_st<4>(t.kc, s, x, w_dw, w_pw, b_pw, y, stream);
+    }
+}
+
+// The older kernels (shapes the tall tile does not take): 0 = none fits,
+// 1 = wide K=9, 2 = wide runtime-K, 3 = narrow runtime-K, 4 = small runtime-K.
+static int pick_dw(const DwsepShape& s) {
+    const bool unit = s.stride == 1 && s.dil == 1;
     if (s.O > 64) {
         if (unit && s.K == 9) return 1;
         if (dw_lds_bytes<DwWideK>(s) <= kDwLdsLimit) return 2;
@@ -989,76 +979,17 @@ static int pick_dw(const DwsepShape& s) {
     return 0;
 }
 
-bool dwsep_supported(const DwsepShape& s) { return pick_dw(s) != 0; }
+bool dwsep_supported(const DwsepShape& s) { return pick_tall(s).ok || pick_dw(s) != 0; }
 
 hipError_t dwsep_launch(const DwsepShape& s, const float* x, const float* w_dw, const float* w_pw,
                         const float* b_pw, float* y, hipStream_t stream) {
+    const TallPick t = pick_tall(s);
+    if (t.ok) return launch_tall_pick(t, s, x, w_dw, w_pw, b_pw, y, stream);
     switch (pick_dw(s)) {
         case 1: return launch_dw<DwWide9>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 2: return launch_dw<DwWideK>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 3: return launch_dw<DwNarrowK>(s, x, w_dw, w_pw, b_pw, y, stream);
         case 4: return launch_dw<DwSmallK>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 5: return launch_tall<DwTall9>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 6: return launch_tall<DwTallK>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 7: return launch_tall<DwTall9M>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 8: return launch_tall<DwTallKM>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 9: return launch_tall<DwTall9S>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 10: return launch_tall<DwTallKS>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 11: return launch_tall<DwTallKD>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 12: return launch_tall<DwTallKMD>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 13: return launch_tall<DwTallKSD>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 14: return launch_tall<DwTall9, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 15: return launch_tall<DwTallK, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 16: return launch_tall<DwTall9M, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 17: return launch_tall<DwTallKM, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 18: return launch_tall<DwTall9S, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 19: return launch_tall<DwTallKS, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 20: return launch_tall<DwTall9Q>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 21: return launch_tall<DwTallKQ>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 22: return launch_tall<DwTall9E>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 23: return launch_tall<DwTallKE>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 24: return launch_tall<DwTallKG>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 25: return launch_tall<DwTallKMG>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 26: return launch_tall<DwTallKSG>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 27: return launch_tall<DwTall9W, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 28: return launch_tall<DwTallKW, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 29: return launch_tall<DwTall9M, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 30: return launch_tall<DwTallKM, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 31: return launch_tall<DwTall9S, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 32: return launch_tall<DwTallKS, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 33: return launch_tall<DwTall9W, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 34: return launch_tall<DwTallKW, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 35: return launch_tall<DwTall9M, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 36: return launch_tall<DwTallKM, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 37: return launch_tall<DwTall9S, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 38: return launch_tall<DwTallKS, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 39: return launch_tall<DwTallKD, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 40: return launch_tall<DwTallKMD, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 41: return launch_tall<DwTallKSD, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 42: return launch_tall<DwTallKG, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 43: return launch_tall<DwTallKMG, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 44: return launch_tall<DwTallKSG, 2>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 45: return launch_tall<DwTallKDW, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 46: return launch_tall<DwTallKMD, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 47: return launch_tall<DwTallKSD, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 48: return launch_tall<DwTallKGW, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 49: return launch_tall<DwTallKMG, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 50: return launch_tall<DwTallKSG, 3>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 51: return launch_tall<DwTallKDW, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 52: return launch_tall<DwTallKMD, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 53: return launch_tall<DwTallKSD, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 54: return launch_tall<DwTallKGW, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 55: return launch_tall<DwTallKMG, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 56: return launch_tall<DwTallKSG, 4>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 57: return launch_tall<DwTallK, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 58: return launch_tall<DwTallKM, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 59: return launch_tall<DwTallKS, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 60: return launch_tall<DwTallKD, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 61: return launch_tall<DwTallKMD, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 62: return launch_tall<DwTallKSD, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 63: return launch_tall<DwTallKG, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 64: return launch_tall<DwTallKMG, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
-        case 65: return launch_tall<DwTallKSG, 1, 1>(s, x, w_dw, w_pw, b_pw, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

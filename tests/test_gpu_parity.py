@@ -583,6 +583,8 @@ TALL_DW = [
     (1, 36, 300, 300, 128, 64),  # the widest window the wide-window instance stages
     (1, 36, 300, 200, 129, 64),  # one wider: the 256-row runtime-K kernel
     (2, 35, 200, 100, 100, 50),  # wide window, 128 rows, C % 4 != 0
+    (1, 36, 300, 60, 100, 50),   # wide window, 64 rows
+    (1, 13, 300, 9, 128, 64),    # the widest window on a 32-row tile
     (2, 36, 130, 512, 5, 2),     # runtime K inside one block of 8 taps
     (1, 40, 96, 300, 8, 3),      # exactly one block, even K (asymmetric padding)
     (1, 24, 80, 384, 17, 8),     # a last block with one tap
@@ -697,7 +699,7 @@ STRIDED_DW = [
     # B, C, T, O, K, pad, stride, dilation
     (2, 64, 300, 300, 9, 4, 2, 1),     # stride 2: the tall tile's stride-2 K = 9 instance, 512 rows
     (1, 48, 257, 512, 9, 8, 1, 2),     # dilation 2: the tall tile's dilated instance, 512 rows
-    (2, 20, 100, 40, 5, 3, 3, 2),      # stride 3, dilation 2, O = 40: the 128-row tile
+    (2, 20, 100, 40, 5, 3, 3, 2),      # stride 3, dilation 2, O = 40: the 64-row tile
     (1, 16, 2000, 128, 9, 4, 16, 1),   # window too wide for 64 steps: narrow instance
     (1, 32, 40, 64, 3, 0, 5, 4),       # few output steps
     # the tall tile's dilated instances: dilation 2, 4 and 8 on 512-, 256- and 128-row tiles, up to the
@@ -721,13 +723,13 @@ STRIDED_DW = [
     (1, 35, 257, 200, 5, 2, 3, 1),     # runtime K, 256 rows, C % 4 != 0
     (1, 68, 300, 100, 64, 32, 3, 1),   # the widest window it stages, 128 rows, chunks of 64 + 4
     (1, 40, 300, 520, 65, 32, 3, 1),   # one wider: the 256-row kernel
-    (1, 16, 200, 40, 9, 4, 3, 1),      # O = 40 on the 128-row tile
+    (1, 16, 200, 40, 9, 4, 3, 1),      # O = 40 on the 64-row tile
     # stride 2 with a dilation: the dilated stages on three staged runs
     (2, 36, 300, 300, 9, 8, 2, 2),     # dilation 2, K = 9, 512 rows, a ragged last time tile
     (1, 35, 260, 200, 16, 30, 2, 4),   # dilation 4, (K - 1) * dil = 60, 256 rows, C % 4 != 0
     (1, 64, 200, 100, 8, 28, 2, 8),    # dilation 8, one tap per block, 128 rows
     (1, 40, 300, 300, 22, 31, 2, 3),   # dilation 3, (K - 1) * dil = 63, tap by tap
-    (2, 20, 180, 40, 7, 15, 2, 5),     # dilation 5, O = 40 on the 128-row tile
+    (2, 20, 180, 40, 7, 15, 2, 5),     # dilation 5, O = 40 on the 64-row tile
     (1, 24, 300, 300, 17, 32, 2, 4),   # (K - 1) * dil = 64: past the tall tile, the 256-row kernel
     # strides 3 and 4 with a dilation
     (2, 36, 500, 300, 9, 8, 3, 2),     # stride 3, dilation 2, 512 rows (256-VGPR budget)
@@ -740,7 +742,11 @@ STRIDED_DW = [
     (1, 33, 300, 256, 7, 3, 4, 1),     # runtime K, 256 rows exactly, C % 4 != 0
     (1, 64, 400, 65, 64, 32, 4, 1),    # the widest window it stages, 128 rows with one valid row in the 5th wave
     (1, 24, 400, 300, 65, 32, 4, 1),   # one wider: the 256-row kernel
-    # O <= 64 with a dilation or stride 2: the 128-row tile, its waves past O idle
+    # O <= 64 with a stride, a dilation or both: the 64- and 32-row tiles of each instance
+    (1, 33, 400, 50, 9, 4, 4, 1),      # stride 4, K = 9, 64 rows
+    (2, 20, 300, 17, 5, 8, 3, 3),      # stride 3, dilation 3 (tap by tap), 32 rows
+    (1, 36, 200, 30, 17, 32, 1, 4),    # dilation 4, (K - 1) * dil = 64 (one more staged run), 32 rows
+    (1, 24, 300, 48, 9, 16, 2, 4),     # stride 2, dilation 4, 64 rows
     (2, 36, 130, 40, 9, 8, 1, 2),      # dilation 2, O = 40
     (1, 35, 131, 64, 5, 2, 2, 1),      # stride 2, O = 64, runtime K, C % 4 != 0
     (1, 20, 100, 7, 7, 9, 1, 3),       # dilation 3, O = 7
