@@ -260,7 +260,7 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 
 // ---------------------------------------------------------------- tall-tile variant
 
-// Stride 1 (any dilation) or 2 to 4, any C, O > 256: a 512 x 64 tile (8
+// Strides 1 to 5 (any dilation), any C, O > 256: a 512 x 64 tile (8
 // waves of 64 x 64), so each depthwise value is made once per time tile
 // instead of once per 256 output channels, and the matrix cores see twice
 // the work per depthwise instruction.  Smaller O takes the same kernel with
@@ -296,8 +296,9 @@ using DwSmallK = DwsepCfg<1, 1, 2, 2, 16, 0, 2>;
 // (70,656 + 256 K bytes: 72,960 for K = 9, two workgroups per CU up to
 // K = 44).  Stride 2: 64 outputs read 127 + K steps, staged as three runs
 // (xs [CC][196]); the epilogue then stages through xs and Ds, so the total
-// is 69,632 + 256 K bytes (71,936 for K = 9).  Strides 3 and 4 stage four
-// and five runs (86,016 and 102,400 + 256 K bytes): one workgroup per CU.
+// is 69,632 + 256 K bytes (71,936 for K = 9).  Strides 3, 4 and 5 stage
+// four, five and six runs (86,016, 102,400 and 118,784 + 256 K bytes): one
+// workgroup per CU.
 // Row r of xs holds input steps t0-pad .. t0-pad+127 (two 64-lane
 // runs; steps past the (K-1)*dil halo or outside [0, T) load as 0); the
 // runtime-K blocks read up to step 8*7 + 8*floor((K-1)*dil/8) + 15, so
@@ -654,8 +655,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINW) void dwsep_tall_kernel(
 // for 64 < O <= 256, so no wave computes rows past O; for O <= 64, 64 rows as
 // 4 waves of 16 x 64 (32-channel chunks) and 32 rows as 2 waves (16-channel
 // chunks), so each wave still makes the depthwise values of 8 channels.  M is
-// the 512-row tile's register budget in waves per SIMD: 2 at strides 3 and
-// 4, whose staged rows leave LDS for one workgroup per CU anyway (at 128
+// the 512-row tile's register budget in waves per SIMD: 2 at strides 3 to
+// 5, whose staged rows leave LDS for one workgroup per CU anyway (at 128
 // VGPRs those instances spilled 11-13 registers).
 template <int KC, int M>
 struct TallSet {
@@ -906,7 +907,7 @@ static hipError_t launch_tall(const DwsepShape& s, const float* x, const float* 
 
 // The tall tile's choice for a shape: its depthwise stage (9: K = 9
 // compiled, 0: runtime K, -1: dilation 2, 4 or 8, -2: any other dilation),
-// its stride (1 to 4) and its window class (wx = 1: one more staged run, for
+// its stride (1 to 5) and its window class (wx = 1: one more staged run, for
 // windows of 65 to 128 steps at stride 1).  ok = false: no tall instance.
 struct TallPick {
     bool ok;
@@ -916,7 +917,7 @@ struct TallPick {
 static TallPick pick_tall(const DwsepShape& s) {
 #ifndef FCONV_DW_NO_TALL
     const int64_t win = (int64_t)(s.K - 1) * s.dil;
-    if (s.stride <= 4 && (win <= 63 || (win <= 127 && s.stride == 1)) && tall_tiles_fit(s)) {
+    if (s.stride <= 5 && (win <= 63 || (win <= 127 && s.stride == 1)) && tall_tiles_fit(s)) {
         const bool pow2 = s.dil == 2 || s.dil == 4 || s.dil == 8;
         const int kc = s.dil == 1 ? (s.K == 9 ? 9 : 0) : pow2 ? -1 : -2;
         return {true, kc, s.stride, win > 63 ? 1 : 0};
@@ -960,7 +961,8 @@ static hipError_t launch_tall_pick(const TallPick& t, const DwsepShape& s, const
         case 1: return launch_tall_st<1>(t.kc, s, x, w_dw, w_pw, b_pw, y, stream);
         case 2: return launch_tall_st<2>(t.kc, s, x, w_dw, w_pw, b_pw, y, stream);
         case 3: return launch_tall_st<3>(t.kc, s, x, w_dw, w_pw, b_pw, y, stream);
-        default: return launch_tall_st<4>(t.kc, s, x, w_dw, w_pw, b_pw, y, stream);
+        case 4: return launch_tall_st<4>(t.kc, s, x, w_dw, w_pw, b_pw, y, stream);
+        default: return launch_tall_st<5>(t.kc, s, x, w_dw, w_pw, b_pw, y, stream);
     }
 }
 

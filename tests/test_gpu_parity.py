@@ -701,7 +701,7 @@ STRIDED_DW = [
     (1, 48, 257, 512, 9, 8, 1, 2),     # dilation 2: the tall tile's dilated instance, 512 rows
     (2, 20, 100, 40, 5, 3, 3, 2),      # stride 3, dilation 2, O = 40: the 64-row tile
     (1, 16, 2000, 128, 9, 4, 16, 1),   # window too wide for 64 steps: narrow instance
-    (1, 32, 40, 64, 3, 0, 5, 4),       # few output steps
+    (1, 32, 40, 64, 3, 0, 5, 4),       # few output steps (stride 5, dilation 4: a 64-row tile)
     # the tall tile's dilated instances: dilation 2, 4 and 8 on 512-, 256- and 128-row tiles, up to the
     # widest window it stages ((K - 1) * dilation = 63), and one past it (the 256-row kernel)
     (2, 36, 150, 300, 5, 8, 1, 4),     # dilation 4, blocks of 2 taps, a ragged time tile, a partial chunk
@@ -731,6 +731,12 @@ STRIDED_DW = [
     (1, 40, 300, 300, 22, 31, 2, 3),   # dilation 3, (K - 1) * dil = 63, tap by tap
     (2, 20, 180, 40, 7, 15, 2, 5),     # dilation 5, O = 40 on the 64-row tile
     (1, 24, 300, 300, 17, 32, 2, 4),   # (K - 1) * dil = 64: past the tall tile, the 256-row kernel
+    # stride 5: six staged runs per row; stride 6 goes to the 256-row kernel
+    (2, 36, 650, 300, 9, 4, 5, 1),     # K = 9, 512 rows, a ragged last time tile
+    (1, 35, 500, 200, 64, 32, 5, 1),   # the widest window it stages, 256 rows, C % 4 != 0
+    (1, 20, 400, 40, 7, 9, 5, 3),      # dilation 3 (tap by tap), 64 rows
+    (1, 24, 500, 300, 65, 32, 5, 1),   # one wider: the 256-row kernel
+    (1, 16, 300, 100, 9, 4, 6, 1),     # stride 6: the 256-row kernel
     # strides 3 and 4 with a dilation
     (2, 36, 500, 300, 9, 8, 3, 2),     # stride 3, dilation 2, 512 rows (256-VGPR budget)
     (1, 35, 400, 200, 10, 27, 3, 7),   # stride 3, dilation 7, (K - 1) * dil = 63, tap by tap, 256 rows
